@@ -1,0 +1,309 @@
+"""Float64 CPU oracle of the Stable LatentMoE FFN layer forward (test infrastructure only).
+
+What it computes, per token t (the K3 latent-MoE block card, "All 23 steps";
+the same order as the card's code excerpt of `KimiSparseMoeBlock.forward`):
+
+  router      z = x W_r,  s = sigmoid(z)                       (card: Router)
+  selection   I = top_k(s + b), descending, ties to the lower index
+  weights     G_j = route_scale * s_{I_j} / sum_j' s_{I_j'}     (card: G_i; K3 has no scale,
+                                                               the K2 card multiplies by 2.827)
+  latent      x^c = x W_down_latent                            (card: x^c)
+  experts     g = x^c W_gate, u = x^c W_up,
+              h = 4 tanh(g/4) sigmoid(g) * 25 tanh(u/25),      (card: Routed expert; the
+              E_j = h W_down                                    walkthrough's SituAndMul)
+  combine     u = sum_j G_j E_j                                (card: u = sum_i G_i E_i)
+  norm        u_hat = u / sqrt(mean(u^2) + eps) * gamma        (card code: routed_expert_norm
+                                                               between the sum and W_up)
+  up          y_routed = u_hat W_up_latent
+  shared      y_shared = SiTU-GLU(x) at full width (merged 2 x 3072 = 6144 hidden)
+  output      Delta = y_routed + y_shared
+
+Precision: every continuous quantity is float64 on exactly dequantised weights
+(bf16 and MXFP4 values are exact in float64).  The one place where floating
+point decides an integer, the top-k selection, is taken in float32 as the
+kernel takes it: kappa = float32(s) + float32(b).
+
+Readings of points the pages leave open are listed in the repository's design
+notes; the ones that change arithmetic are stated where they act below.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Callable
+
+import numpy as np
+
+__all__ = [
+    "bf16_to_f64", "e2m1_decode", "e8m0_decode", "dequant_mxfp4", "E2M1_GRID",
+    "sigmoid", "select_and_weight", "router_scores", "situ", "swiglu", "glu", "rmsnorm",
+    "OracleLayer", "forward", "routed_sum_dense_mask", "Result",
+]
+
+# ----------------------------------------------------------------------------------------
+# Formats.  The card states that routed experts are MXFP4 with one scale per 32 weights and
+# the port notes add "E2M1 with one E8M0 exponent per 32 columns".  The element and scale
+# encodings are those of the OCP Microscaling Formats (MX) v1.0 specification:
+#   E2M1: 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit; exponent field 0 is
+#         subnormal (value = mantissa * 0.5).
+#   E8M0: unsigned 8-bit exponent, value 2^(e - 127); 0xFF encodes NaN.
+# ----------------------------------------------------------------------------------------
+
+#: Magnitudes of the eight non-negative E2M1 codes 0..7 as printed in OCP MX v1.0.
+E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def bf16_to_f64(a: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exactly (bf16 is the top half of fp32)."""
+    return (np.asarray(a).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    """4-bit E2M1 codes (0..15) -> float64 from the field definition."""
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    mant = (c & 0x1).astype(np.float64)
+    mag = np.where(e == 0, 0.5 * mant, np.ldexp(1.0 + 0.5 * mant, (e - 1).astype(np.int64)))
+    return sign * mag
+
+
+def e8m0_decode(b: np.ndarray) -> np.ndarray:
+    """E8M0 scale bytes -> float64: 2^(b-127), NaN for 0xFF."""
+    b = np.asarray(b).astype(np.int64)
+    v = np.ldexp(1.0, b - 127)
+    return np.where(b == 0xFF, np.nan, v)
+
+
+def dequant_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP4 block [.., rows, cols/2] codes + [.., rows, cols/32] E8M0 -> float64 [.., rows, cols].
+
+    Two codes per byte, the low nibble holding the even column (storage convention of
+    the synthetic layers); one scale per 32 consecutive columns of a row (the blocks run
+    along the input axis, "one E8M0 exponent per 32 columns")."""
+    codes = np.asarray(codes)
+    lut = e2m1_decode(np.arange(16))
+    cols = codes.shape[-1] * 2
+    q = np.empty(codes.shape[:-1] + (cols,), np.float64)
+    q[..., 0::2] = lut[codes & 0xF]
+    q[..., 1::2] = lut[codes >> 4]
+    s = e8m0_decode(scales)
+    if s.shape[-1] * 32 != cols:
+        raise ValueError("scale count does not match the block size of 32")
+    q = q.reshape(q.shape[:-1] + (cols // 32, 32)) * s[..., None]
+    return q.reshape(q.shape[:-2] + (cols,))
+
+
+# ----------------------------------------------------------------------------------------
+# Router (block card: z = x W_r, s = sigmoid(z), selection by top_k(s + b), weights from the
+# raw s renormalised; toy chapter: the bias decides who is invited, not how much each
+# answer counts; port notes item (3)).
+# ----------------------------------------------------------------------------------------
+
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    """Logistic function in a form that is finite for every finite input."""
+    z = np.asarray(z, dtype=np.float64)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    out[~pos] = ez / (1.0 + ez)
+    return out
+
+
+def router_scores(x: np.ndarray, w_router: np.ndarray) -> np.ndarray:
+    """s[t, e] = sigmoid(sum_c x[t, c] W_r[e, c]), full model width (not the latent)."""
+    return sigmoid(x @ w_router.T)
+
+
+def select_and_weight(s: np.ndarray, bias: np.ndarray, k: int, route_scale: float = 1.0,
+                      forced_idx: np.ndarray | None = None):
+    """Top-k of kappa = s + b and the renormalised raw-score weights.
+
+    Returns (idx [T, k] int32 in descending kappa order, ties to the lower expert index;
+    G [T, k] float64; margin [T] = kappa_(k) - kappa_(k+1), +inf when E == k).
+    kappa is formed in float32 (float32(s) + float32(b)) because that is the precision in
+    which the kernel takes the same integer decision.  With `forced_idx` the selection
+    is taken from the caller and only the weights are computed from s."""
+    s = np.asarray(s, dtype=np.float64)
+    T, E = s.shape
+    kappa = s.astype(np.float32) + np.asarray(bias, dtype=np.float32)[None, :]
+    order = np.argsort(-kappa, axis=1, kind="stable")
+    if forced_idx is None:
+        idx = order[:, :k]
+    else:
+        idx = np.asarray(forced_idx, dtype=np.int64)
+    rows = np.arange(T)[:, None]
+    ssel = s[rows, idx]
+    G = route_scale * ssel / ssel.sum(axis=1, keepdims=True)
+    if E > k:
+        kk = kappa[rows[:, 0], order[:, k - 1]].astype(np.float64)
+        k1 = kappa[rows[:, 0], order[:, k]].astype(np.float64)
+        margin = kk - k1
+    else:
+        margin = np.full(T, np.inf)
+    return idx.astype(np.int32), G, margin
+
+
+# ----------------------------------------------------------------------------------------
+# Activations.  SiTU-GLU (walkthrough, Stable #2 and its SituAndMul excerpt; card: a, u-bar,
+# h): the Swish gate's linear factor and the up branch are each soft-capped,
+# softcap(z, beta) = beta tanh(z / beta); the sigmoid acts on the raw gate value.
+# SwiGLU (K2 card): g sigmoid(g) * u.
+# ----------------------------------------------------------------------------------------
+
+def situ(g: np.ndarray, u: np.ndarray, beta_gate: float = 4.0, beta_lin: float = 25.0) -> np.ndarray:
+    g = np.asarray(g, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    a = beta_gate * np.tanh(g / beta_gate) * sigmoid(g)
+    ubar = beta_lin * np.tanh(u / beta_lin)
+    return a * ubar
+
+
+def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    g = np.asarray(g, dtype=np.float64)
+    return g * sigmoid(g) * np.asarray(u, dtype=np.float64)
+
+
+def _act(cfg, g, u):
+    if cfg.act == "situ":
+        return situ(g, u, cfg.beta_gate, cfg.beta_lin)
+    if cfg.act == "swiglu":
+        return swiglu(g, u)
+    raise ValueError(cfg.act)
+
+
+def glu(xin: np.ndarray, w_gu: np.ndarray, w_down: np.ndarray, act: Callable) -> np.ndarray:
+    """Three-matrix gated MLP: h = act(x W_gate, x W_up), out = h W_down.
+
+    w_gu is [2m, K] with the gate rows first and the up rows second (the walkthrough's
+    SituAndMul splits the last axis in half, gate then up); w_down is [K_out, m]."""
+    m = w_gu.shape[0] // 2
+    g = xin @ w_gu[:m].T
+    u = xin @ w_gu[m:].T
+    return act(g, u) @ w_down.T
+
+
+def rmsnorm(u: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """u / sqrt(mean(u^2) + eps) * gamma over the last axis."""
+    ms = np.mean(u * u, axis=-1, keepdims=True)
+    return u / np.sqrt(ms + eps) * gamma
+
+
+# ----------------------------------------------------------------------------------------
+# The layer
+# ----------------------------------------------------------------------------------------
+
+class OracleLayer:
+    """A layer in float64, built from the canonical bytes of `synth`.
+
+    Dense weights are widened once; experts are dequantised on demand (one expert of the
+    K3 layer is 132 MB in float64, the whole set would be 118 GB)."""
+
+    def __init__(self, cfg, dense, expert_fn: Callable[[int], tuple] | None = None,
+                 experts: tuple | None = None):
+        self.cfg = cfg
+        self.router = bf16_to_f64(dense.router)
+        self.bias = np.asarray(dense.bias, dtype=np.float32)
+        self.w_down_latent = bf16_to_f64(dense.w_down_latent) if cfg.l else None
+        self.w_up_latent = bf16_to_f64(dense.w_up_latent) if cfg.l else None
+        self.gamma = bf16_to_f64(dense.norm_gamma) if cfg.l and cfg.use_norm else None
+        self.shared_gu = bf16_to_f64(dense.shared_gu) if cfg.ms else None
+        self.shared_down = bf16_to_f64(dense.shared_down) if cfg.ms else None
+        self._expert_fn = expert_fn
+        self._experts = experts   # optional fully materialised (w_gu [E,2m,K], w_down [E,K,m])
+
+    @classmethod
+    def from_synth(cls, cfg, dense=None, preload: bool | None = None):
+        import synth
+        dense = synth.dense_weights(cfg) if dense is None else dense
+        small = cfg.E * 3 * cfg.m * (cfg.l or cfg.d) <= 64 * 1024 * 1024
+        preload = small if preload is None else preload
+
+        def expert_fn(e):
+            return _expert_from_slice(synth.expert_slice(cfg, e, e + 1), 0)
+
+        experts = None
+        if preload:
+            sl = synth.expert_slice(cfg, 0, cfg.E)
+            gu, dn = _slice_to_f64(sl)
+            experts = (gu, dn)
+        return cls(cfg, dense, expert_fn, experts)
+
+    def expert(self, e: int):
+        """(w_gu [2m, K], w_down [K, m]) of expert e in float64."""
+        if self._experts is not None:
+            return self._experts[0][e], self._experts[1][e]
+        return self._expert_fn(int(e))
+
+
+def _slice_to_f64(sl):
+    if sl.fmt == "bf16":
+        return bf16_to_f64(sl.gu), bf16_to_f64(sl.down)
+    return dequant_mxfp4(sl.gu, sl.gu_scale), dequant_mxfp4(sl.down, sl.down_scale)
+
+
+def _expert_from_slice(sl, i):
+    gu, dn = _slice_to_f64(sl)
+    return gu[i], dn[i]
+
+
+@dataclass
+class Result:
+    delta: np.ndarray      # [T, d] float64
+    idx: np.ndarray        # [T, k] int32
+    G: np.ndarray          # [T, k] float64
+    margin: np.ndarray     # [T]
+    xc: np.ndarray         # [T, l] latent input of the experts
+    u: np.ndarray          # [T, l] gated sum before the norm
+    y_routed: np.ndarray   # [T, d]
+    y_shared: np.ndarray   # [T, d]
+
+
+def forward(layer: OracleLayer, x_bf16: np.ndarray, forced_idx: np.ndarray | None = None) -> Result:
+    """The layer forward for tokens x [T, d] (bf16 bit patterns or float64 values).
+
+    The routed sum is organised as the block card's `moe_infer` does it: assignments are
+    grouped by expert, each expert runs once on the tokens that chose it, and each result
+    is weighted by its G and added into its token's sum.  `forced_idx` replaces the
+    selection (used for tokens whose top-k margin is a near tie)."""
+    cfg = layer.cfg
+    x = bf16_to_f64(x_bf16) if np.asarray(x_bf16).dtype == np.uint16 else np.asarray(x_bf16, np.float64)
+    T = x.shape[0]
+    s = router_scores(x, layer.router)
+    idx, G, margin = select_and_weight(s, layer.bias, cfg.k, cfg.route_scale, forced_idx)
+
+    xc = x @ layer.w_down_latent.T if cfg.l else x
+    lat = xc.shape[1]
+    u = np.zeros((T, lat), np.float64)
+    act = lambda g, v: _act(cfg, g, v)  # noqa: E731
+    flat = idx.reshape(-1)
+    for e in np.unique(flat):
+        tj = np.nonzero(flat == e)[0]
+        t_rows, j_cols = tj // cfg.k, tj % cfg.k
+        w_gu, w_dn = layer.expert(int(e))
+        out = glu(xc[t_rows], w_gu, w_dn, act)
+        u[t_rows] += G[t_rows, j_cols][:, None] * out   # one (t, e) pair per token at most
+
+    if cfg.l:
+        u_hat = rmsnorm(u, layer.gamma, cfg.eps) if cfg.use_norm else u
+        y_r = u_hat @ layer.w_up_latent.T
+    else:
+        y_r = u
+    if cfg.ms:
+        y_s = glu(x, layer.shared_gu, layer.shared_down, act)
+    else:
+        y_s = np.zeros_like(y_r)
+    return Result(y_r + y_s, idx, G, margin, xc, u, y_r, y_s)
+
+
+def routed_sum_dense_mask(layer: OracleLayer, xc: np.ndarray, G_dense: np.ndarray) -> np.ndarray:
+    """The card's definition u = sum_{i=1}^{E} G_i E_i with G_i = 0 off the selection:
+    every expert is evaluated on every token (tiny shapes only)."""
+    cfg = layer.cfg
+    act = lambda g, v: _act(cfg, g, v)  # noqa: E731
+    u = np.zeros((xc.shape[0], xc.shape[1]), np.float64)
+    for e in range(cfg.E):
+        w_gu, w_dn = layer.expert(e)
+        u += G_dense[:, e:e + 1] * glu(xc, w_gu, w_dn, act)
+    return u
