@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Throughput of the Stable LatentMoE FFN layer forward on one MI355X.
+
+One step = one moe_layer_forward call (all steps of the layer) over one batch of
+synthetic tokens already resident in HBM.  Prints one JSON line.
+
+Default workload: the K3-shaped layer at decode batch 1 (d 7168, latent 3584, 896 MXFP4
+experts top-16, 3072-wide experts, merged 6144-wide shared expert).  Three copies of the
+dense weights (3 x 380 MB) and 64 distinct token batches rotate so that the 256 MB
+last-level cache cannot hold what a step reads.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LatentMoE layer tokens/s (decode B=1/64, prefill 8k) + % HBM / MFMA peak"
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(cfg, T, D):
+    """Compulsory HBM bytes of each step for T tokens touching D distinct experts."""
+    d, l, E, k, m, ms = cfg.d, cfg.l, cfg.E, cfg.k, cfg.m, cfg.ms
+    if cfg.expert_fmt == "mxfp4":
+        gu_w = 2 * m * (l // 2 + l // 32)
+        dn_w = l * (m // 2 + m // 32)
+    else:
+        gu_w, dn_w = 2 * m * l * 2, l * m * 2
+    tk = T * k
+    return {
+        "dense_x": T * d * 2 + (E + l + 2 * ms) * d * 2 + T * (E + l + ms) * 4,
+        "topk": T * E * 4 + E * 4 + tk * 8,
+        "dispatch": tk * 4 * 4 + E * 8,
+        "expert_gu": D * gu_w + T * l * 4 + tk * m * 4,
+        "expert_down": D * dn_w + tk * m * 4 + tk * l * 4,
+        "combine": tk * l * 4 + tk * 8 + T * l * 4,
+        "shared_down": d * ms * 2 + T * ms * 4 + T * d * 4,
+        "up": d * l * 2 + l * 2 + T * l * 4 + 2 * T * d * 4,
+    }
+
+
+def weight_bytes(cfg, D):
+    """Weights (and the fp32 bias) one call reads: the layer's algorithmic byte count."""
+    d, l, E, m, ms = cfg.d, cfg.l, cfg.E, cfg.m, cfg.ms
+    per_expert = (2 * m * (l // 2 + l // 32) + l * (m // 2 + m // 32)) if cfg.expert_fmt == "mxfp4" \
+        else 3 * m * l * 2
+    return (E * d + 2 * l * d + l + 3 * ms * d) * 2 + E * 4 + D * per_expert
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime that torch has loaded."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so.7")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.h.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def ms(self, a, b):
+        v = ctypes.c_float()
+        if self.h.hipEventElapsedTime(ctypes.byref(v), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return v.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.h.hipEventDestroy(e)
+
+
+def cpu_baseline(cfg, dense, seconds):
+    """The float64 CPU oracle, as it is, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    OL = oracle.OracleLayer.from_synth(cfg, dense)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        x = synth.tokens(cfg, batch=5000 + n)
+        oracle.forward(OL, x)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 64:
+            break
+    tps = n * cfg.tokens / el
+    return {"value": tps, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} step(s) of {cfg.tokens} token(s), {el:.1f} s, float64 numpy oracle "
+                      f"(BLAS threads {cores}), experts regenerated and dequantised per token"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="k3_latent_moe_decode_b1")
+    ap.add_argument("--rotate", type=int, default=3, help="dense weight copies rotated")
+    ap.add_argument("--batches", type=int, default=64, help="distinct token batches rotated")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_moe_layer_amd as moe
+    import synth
+
+    cfg = synth.PRESETS[args.workload]
+    dev = torch.device("cuda:0")
+    T = cfg.tokens
+    mcfg = moe.config_from(cfg)
+    log(f"[bench] workload {cfg.name}: generating and uploading the layer")
+    t0 = time.perf_counter()
+    dense0 = synth.dense_weights(cfg)
+    chunk = 64
+    staging = {}
+
+    def slice_fn(a, b):
+        if b - a == chunk and "s" in staging:
+            return synth.expert_slice(cfg, a, b, out=staging["s"])
+        sl = synth.expert_slice(cfg, a, b)
+        if b - a == chunk:
+            staging["s"] = sl
+        return sl
+    layer0 = moe.Layer.upload(mcfg, dense0, slice_fn, cfg.E, device=dev, chunk=chunk)
+    staging.clear()
+    layers = [layer0] + [layer0.with_dense(synth.dense_weights(cfg, copy=c)) for c in range(1, args.rotate)]
+    xs = [torch.from_numpy(synth.tokens(cfg, batch=1000 + b).view(np.int16)).to(dev)
+          for b in range(args.batches)]
+    torch.cuda.synchronize()
+    log(f"[bench] layer ready in {time.perf_counter() - t0:.1f} s")
+
+    delta = torch.empty((T, cfg.d), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, cfg.k), dtype=torch.int32, device=dev)
+    gw = torch.empty((T, cfg.k), dtype=torch.float32, device=dev)
+    ws = layer0.workspace(T)
+
+    # distinct experts per batch (for the byte count of the timed steps)
+    D = []
+    for b in range(args.batches):
+        layers[0].forward(xs[b], delta, idx, gw, ws)
+        D.append(len(np.unique(idx.cpu().numpy())))
+    for i in range(args.warmup):
+        layers[i % args.rotate].forward(xs[i % args.batches], delta, idx, gw, ws)
+    torch.cuda.synchronize()
+
+    # timed region: K whole forwards back to back
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(K):
+        layers[i % args.rotate].forward(xs[i % args.batches], delta, idx, gw, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / K
+    log(f"[bench] {K} steps: {ms_step * 1e3:.1f} us/step")
+
+    # per-step durations: the same forwards with in-stream events between the steps
+    hip = HipEvents()
+    nst = len(moe.STEPS)
+    evs = hip.create(K * (nst + 1))
+    for i in range(K):
+        layers[i % args.rotate].forward_timed(xs[i % args.batches], evs[i * (nst + 1):(i + 1) * (nst + 1)],
+                                              delta, idx, gw, ws)
+    torch.cuda.synchronize()
+    step_ms = np.zeros(nst)
+    for i in range(K):
+        base = i * (nst + 1)
+        for s in range(nst):
+            step_ms[s] += hip.ms(evs[base + s], evs[base + s + 1])
+    step_ms /= K
+    hip.destroy(evs)
+    steps_us = {n: round(v * 1e3, 2) for n, v in zip(moe.STEPS, step_ms)}
+    log(f"[bench] per step (us): {steps_us}")
+
+    Dm = float(np.mean([D[i % args.batches] for i in range(K)]))
+    ab = algorithmic_bytes(cfg, T, Dm)
+    dom = max(("dense_x", "expert_gu", "expert_down", "shared_down", "up"),
+              key=lambda n: step_ms[moe.STEPS.index(n)])
+    dom_s = step_ms[moe.STEPS.index(dom)] * 1e-3
+    achieved = ab[dom] / dom_s / 1e9
+    layer_bytes = weight_bytes(cfg, Dm)
+    layer_gbs = layer_bytes / (ms_step * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens_per_step": T, "d": cfg.d, "latent": cfg.l,
+                   "experts": cfg.E, "top_k": cfg.k, "expert_hidden": cfg.m,
+                   "shared_hidden": cfg.ms, "expert_weights": cfg.expert_fmt,
+                   "dense_weight_copies": args.rotate, "token_batches": args.batches,
+                   "distinct_experts_per_step": Dm},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": ab[dom], "avg_us": dom_s * 1e6},
+        "layer": {"algorithmic_bytes": layer_bytes, "achieved_GBps": layer_gbs,
+                  "hbm_frac": layer_gbs / HBM_PEAK_GBS, "steps_us": steps_us},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(cfg, dense0, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

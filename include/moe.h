@@ -1,0 +1,214 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) Stable LatentMoE FFN layer library (libmoe.so).
+ *
+ * The library computes the inference forward pass of one Kimi K3 Stable LatentMoE FFN
+ * layer, as the Kimi K3 latent mixture-of-experts block card defines it (its "All 23
+ * steps" equations and the code excerpt of KimiSparseMoeBlock.forward / moe_infer):
+ *
+ *   s = sigmoid(x W_r);  I = top_k(s + b);  G = s_I / sum(s_I)        (router)
+ *   x^c = x W_down_latent                                           (latent down, d -> l)
+ *   h_j = 4 tanh(g/4) sigmoid(g) * 25 tanh(u/25), g|u = x^c W_gate|up (routed SiTU-GLU)
+ *   E_j = h_j W_down;   u = sum_j G_j E_j                            (latent combine)
+ *   y_routed = RMSNorm(u) W_up_latent                                (norm, then l -> d)
+ *   y_shared = SiTU-GLU(x) at full width (two shared experts merged into one)
+ *   Delta = y_routed + y_shared
+ *
+ * Conventions shared by every entry point
+ *   - All pointers are device pointers unless stated otherwise.  The caller allocates
+ *     and owns every buffer; the library never allocates, frees or retains memory, and
+ *     keeps no state between calls.
+ *   - Matrices are row-major [out, in] as nn.Linear stores them.  bf16 is passed as its
+ *     16-bit pattern.  Weight, token and output buffers must be 16-byte aligned.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null stream)
+ *     and performs no host synchronisation.  Outputs are valid once the stream reaches
+ *     them.  Calls on one stream are ordered; concurrent calls on different streams
+ *     must use distinct workspaces and outputs.
+ *   - Arguments are validated before anything is launched; on any error nothing is
+ *     written and the status says why.  MOE_ERR_HIP reports a failed launch
+ *     (hipGetLastError after the launches).  NaN or Inf inside the data are not
+ *     checked: they propagate.
+ *   - Results are deterministic: the same inputs give bit-identical outputs (no
+ *     floating-point atomics; every sum has a fixed order).
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef struct ihipStream_t* moe_stream_t; /* the same type as hipStream_t */
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null or misaligned pointer, negative size, k > E, ... */
+  MOE_ERR_UNSUPPORTED = 2, /* a shape, format or precision combination not built */
+  MOE_ERR_WORKSPACE = 3,   /* workspace or packed buffer smaller than required */
+  MOE_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum moe_act {
+  MOE_ACT_SITU = 0,  /* beta_gate tanh(g/beta_gate) sigmoid(g) * beta_lin tanh(u/beta_lin) */
+  MOE_ACT_SWIGLU = 1 /* g sigmoid(g) u  (the K2 block card's expert activation) */
+} moe_act;
+
+typedef enum moe_wfmt {
+  MOE_WFMT_BF16 = 0,  /* bf16 expert weights */
+  MOE_WFMT_MXFP4 = 1  /* E2M1 codes, two per byte (low nibble = even column), plus one
+                         E8M0 scale byte per 32 consecutive input columns of a row */
+} moe_wfmt;
+
+typedef enum moe_precision {
+  MOE_PREC_FP32 = 0 /* activations kept in fp32 between all steps; Delta in fp32 */
+} moe_precision;
+
+/* Layer shape and options.  K3: d_model 7168, d_latent 3584, n_experts 896, top_k 16,
+ * d_expert 3072, d_shared 6144 (two merged 3072-wide shared experts), SiTU with
+ * beta_gate 4 and beta_lin 25, route_scale 1, use_latent_norm 1 (block card: parameter
+ * table and config fields; walkthrough: SituAndMul and the activation_situ_* fields). */
+typedef struct moe_config {
+  int32_t d_model;         /* d: token width; multiple of 8 */
+  int32_t d_latent;        /* l: latent width of the routed experts; multiple of 8 (> 0) */
+  int32_t n_experts;       /* E: routed experts, 1..1024 */
+  int32_t top_k;           /* k: experts per token, 1..min(E, 64) */
+  int32_t d_expert;        /* m: routed expert hidden width; multiple of 8 */
+  int32_t d_shared;        /* m_s: shared hidden width (0 = no shared path); multiple of 8 */
+  int32_t use_latent_norm; /* 1: RMSNorm between the latent sum and W_up_latent */
+  float rms_eps;           /* RMSNorm epsilon */
+  float route_scale;       /* multiplies the renormalised gate weights (1 for K3) */
+  float beta_gate;         /* SiTU gate cap (4) */
+  float beta_lin;          /* SiTU up-branch cap (25) */
+  int32_t act;             /* moe_act */
+  int32_t expert_wfmt;     /* moe_wfmt; MXFP4 needs d_latent and d_expert divisible by 32 */
+  int32_t precision;       /* moe_precision */
+} moe_config;
+
+/* Dense weights (canonical [out, in] bf16) and the packed routed experts. */
+typedef struct moe_weights {
+  const void* router;        /* W_r           [E, d]       bf16 */
+  const void* w_down_latent; /* W_down_latent [l, d]       bf16 */
+  const void* w_up_latent;   /* W_up_latent   [d, l]       bf16 */
+  const void* norm_gamma;    /* RMSNorm gain  [l]          bf16 (unused if no norm) */
+  const void* shared_gu;     /* shared gate rows then up rows [2 m_s, d] bf16 */
+  const void* shared_down;   /* shared down   [d, m_s]     bf16 */
+  const void* experts;       /* routed experts in the layout written by moe_pack_experts */
+} moe_weights;
+
+/* Canonical routed-expert storage for a run of consecutive experts, each pointer at
+ * the first expert of the run.  Gate/up of an expert are stacked: rows 0..m-1 gate,
+ * rows m..2m-1 up, each row l wide; down is [l, m].
+ *   BF16:  gu = [n][2m][l] bf16, down = [n][l][m] bf16, scale pointers unused.
+ *   MXFP4: gu = [n][2m][l/2] code bytes, gu_scale = [n][2m][l/32] E8M0 bytes,
+ *          down = [n][l][m/2], down_scale = [n][l][m/32]. */
+typedef struct moe_expert_src {
+  const void* gu;
+  const void* gu_scale;
+  const void* down;
+  const void* down_scale;
+} moe_expert_src;
+
+/* ABI version of the library (MOE_ABI_VERSION it was built with). */
+int moe_abi_version(void);
+
+/* Static string naming a status code. */
+const char* moe_status_str(moe_status s);
+
+/* Bytes of the packed routed-expert buffer for the whole layer (host call, no launch).
+ * Errors: MOE_ERR_INVALID_ARG (null pointer or invalid config), MOE_ERR_UNSUPPORTED. */
+moe_status moe_packed_experts_size(const moe_config* cfg, size_t* bytes);
+
+/* Rewrite canonical experts e0..e0+n-1 into the kernel-native order inside `packed`
+ * (a buffer of moe_packed_experts_size bytes for the whole layer).  The run may be any
+ * sub-range, so a layer can be packed in pieces.  MXFP4 is regrouped so that one
+ * wavefront load brings four rows' 8-column chunks and their scale bytes together; the
+ * bytes are not changed, only moved.  Errors: MOE_ERR_INVALID_ARG (null pointer, range
+ * outside 0..E), MOE_ERR_WORKSPACE (packed_bytes too small), MOE_ERR_HIP. */
+moe_status moe_pack_experts(const moe_config* cfg, const moe_expert_src* src, int32_t e0,
+                            int32_t n, void* packed, size_t packed_bytes, moe_stream_t stream);
+
+/* Bytes of workspace that moe_layer_forward needs for up to max_tokens tokens. */
+moe_status moe_workspace_size(const moe_config* cfg, int64_t max_tokens, size_t* bytes);
+
+/* Offsets (bytes) of the intermediates inside the workspace of a call with n_tokens,
+ * for inspection after moe_layer_forward (host call).  Layouts, all row-major:
+ *   [0] x^c    [T][l]   fp32     latent down-projection
+ *   [1] h_s    [T][m_s] fp32     shared SiTU-GLU hidden
+ *   [2] h      [T*k][m] fp32     routed expert hidden, rows in dispatch order
+ *   [3] E      [T*k][l] fp32     routed expert outputs, rows in dispatch order
+ *   [4] u      [T][l]   fp32     gated latent sum before the norm
+ *   [5] perm   [T*k]    int32    dispatch order -> assignment t*k+j
+ *   [6] inv    [T*k]    int32    assignment -> dispatch order
+ *   [7] counts [E]      int32    assignments per expert
+ *   [8] offsets[E+1]    int32    exclusive scan of counts
+ *   [9] z      [T][E]   fp32     router logits
+ *  [10] per-chunk expert histograms of the dispatch (internal) */
+#define MOE_WS_NUM_SLOTS 11
+moe_status moe_workspace_layout(const moe_config* cfg, int64_t n_tokens,
+                                size_t offsets[MOE_WS_NUM_SLOTS]);
+
+/* The layer forward (block card: KimiSparseMoeBlock.forward), for n_tokens tokens.
+ *   x         [T, d] bf16 tokens (batch and positions flattened, as the card's code does)
+ *   bias      [E] fp32 selection bias (e_score_correction_bias; frozen at inference)
+ *   delta     [T, d] fp32 output Delta_ffn = y_routed + y_shared
+ *   topk_idx  [T, k] int32 selected experts, in descending s + b, ties to the lower index
+ *   topk_w    [T, k] fp32 gate weights route_scale * s / sum(s) in the same order
+ *   workspace at least moe_workspace_size(cfg, n_tokens) bytes, 256-byte aligned
+ * n_tokens == 0 returns MOE_OK and launches nothing.  Errors: MOE_ERR_INVALID_ARG,
+ * MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
+moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const float* bias,
+                             const void* x, int64_t n_tokens, float* delta, int32_t* topk_idx,
+                             float* topk_w, void* workspace, size_t workspace_bytes,
+                             moe_stream_t stream);
+
+/* Steps of the forward, in launch order. */
+typedef enum moe_step {
+  MOE_STEP_DENSE_X = 0,     /* router logits, x^c = x W_down_latent, shared gate/up + SiTU */
+  MOE_STEP_TOPK = 1,        /* sigmoid, top_k(s + b), gate weights */
+  MOE_STEP_DISPATCH = 2,    /* histogram, scan, stable permutation by expert */
+  MOE_STEP_EXPERT_GU = 3,   /* routed gate/up + SiTU */
+  MOE_STEP_EXPERT_DOWN = 4, /* routed down */
+  MOE_STEP_COMBINE = 5,     /* u = sum_j G_j E_j */
+  MOE_STEP_SHARED_DOWN = 6, /* y_shared = h_s W_shared_down */
+  MOE_STEP_UP = 7,          /* Delta = RMSNorm(u) W_up_latent + y_shared */
+  MOE_NUM_STEPS = 8
+} moe_step;
+
+/* moe_layer_forward with per-step timing: identical work and results, and additionally
+ * records step_events[s] on `stream` just before step s is launched (s = 0..7) and
+ * step_events[MOE_NUM_STEPS] after the last one.  step_events holds MOE_NUM_STEPS + 1
+ * hipEvent_t handles created by the caller (with timing enabled); they are only recorded,
+ * never synchronised on.  For profilers and benchmarks; errors as moe_layer_forward. */
+moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w,
+                                   const float* bias, const void* x, int64_t n_tokens,
+                                   float* delta, int32_t* topk_idx, float* topk_w,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* const* step_events, moe_stream_t stream);
+
+/* The router step alone (block card: z = x W_r, s = sigmoid(z), top_k(s + b), and G;
+ * toy chapter: the bias selects, the raw score weights).  Same arguments and output
+ * layout as the corresponding ones of moe_layer_forward; the logits are left in the
+ * workspace slot [9]. */
+moe_status moe_route(const moe_config* cfg, const moe_weights* w, const float* bias,
+                     const void* x, int64_t n_tokens, int32_t* topk_idx, float* topk_w,
+                     void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* The dispatch step alone (block card's moe_infer: per-expert histogram, then the
+ * assignments ordered by expert).  From topk_idx [T, k] it writes counts [E], offsets
+ * [E+1] (exclusive scan, offsets[E] = T*k), perm [T*k] (dispatch order -> assignment
+ * t*k+j; within an expert, assignments in increasing t*k+j) and inv [T*k] (the inverse).
+ * workspace: at least moe_workspace_size(cfg, n_tokens) bytes.  Every index in topk_idx
+ * must lie in 0..E-1; this is not checked. */
+moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int64_t n_tokens,
+                        int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                        void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

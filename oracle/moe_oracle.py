@@ -37,7 +37,7 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "e2m1_decode", "e8m0_decode", "dequant_mxfp4", "E2M1_GRID",
     "sigmoid", "select_and_weight", "router_scores", "situ", "swiglu", "glu", "rmsnorm",
-    "OracleLayer", "forward", "routed_sum_dense_mask", "Result",
+    "OracleLayer", "forward", "routed_sum_dense_mask", "Result", "dispatch",
 ]
 
 # ----------------------------------------------------------------------------------------
@@ -307,3 +307,18 @@ def routed_sum_dense_mask(layer: OracleLayer, xc: np.ndarray, G_dense: np.ndarra
         w_gu, w_dn = layer.expert(e)
         u += G_dense[:, e:e + 1] * glu(xc, w_gu, w_dn, act)
     return u
+
+
+def dispatch(idx: np.ndarray, n_experts: int):
+    """The block card's moe_infer bookkeeping for the flattened assignments a = t*k + j:
+    tokens_per_expert (a histogram of the selected ids), the argsort of the ids (stable, so
+    assignments of one expert keep increasing a), and its inverse.
+
+    Returns (counts [E], offsets [E+1] = exclusive scan of counts, perm [T*k], inv [T*k])."""
+    flat = np.asarray(idx, dtype=np.int64).reshape(-1)
+    counts = np.bincount(flat, minlength=n_experts).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    perm = np.argsort(flat, kind="stable").astype(np.int32)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(perm.size, dtype=np.int32)
+    return counts, offsets, perm, inv

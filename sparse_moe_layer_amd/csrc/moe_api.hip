@@ -1,0 +1,304 @@
+// C ABI of libmoe.so: argument validation, workspace layout and the launch sequence of
+// the Stable LatentMoE FFN forward.  Declarations and the contract are in include/moe.h.
+#include <hip/hip_runtime.h>
+
+#include "moe.h"
+#include "moe_internal.hpp"
+
+#define MOE_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using moe::Shape;
+
+inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status make_shape(const moe_config* c, Shape* s) {
+  if (!c || !s) return MOE_ERR_INVALID_ARG;
+  if (c->d_model <= 0 || c->d_latent < 0 || c->n_experts <= 0 || c->top_k <= 0 ||
+      c->d_expert <= 0 || c->d_shared < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->top_k > c->n_experts) return MOE_ERR_INVALID_ARG;
+  if (c->act != MOE_ACT_SITU && c->act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
+  if (c->expert_wfmt != MOE_WFMT_BF16 && c->expert_wfmt != MOE_WFMT_MXFP4) return MOE_ERR_INVALID_ARG;
+  if (!(c->rms_eps >= 0.f) || !(c->route_scale == c->route_scale)) return MOE_ERR_INVALID_ARG;
+  if (c->act == MOE_ACT_SITU && !(c->beta_gate > 0.f && c->beta_lin > 0.f)) return MOE_ERR_INVALID_ARG;
+  if (c->d_model % 8 || c->d_latent % 8 || c->d_expert % 8 || c->d_shared % 8)
+    return MOE_ERR_INVALID_ARG;
+  if (c->expert_wfmt == MOE_WFMT_MXFP4 && (c->d_latent % 32 || c->d_expert % 32))
+    return MOE_ERR_INVALID_ARG;
+  if (c->precision != MOE_PREC_FP32) return MOE_ERR_UNSUPPORTED;
+  if (c->d_latent == 0) return MOE_ERR_UNSUPPORTED;  // non-latent blocks: not built yet
+  if (c->n_experts > 1024 || c->top_k > 64) return MOE_ERR_UNSUPPORTED;
+  if (c->d_model > 8192 || c->d_latent > 8192 || c->d_expert > 8192 || c->d_shared > 8192)
+    return MOE_ERR_UNSUPPORTED;
+  s->d = c->d_model;
+  s->l = c->d_latent;
+  s->E = c->n_experts;
+  s->k = c->top_k;
+  s->m = c->d_expert;
+  s->ms = c->d_shared;
+  s->use_norm = c->use_latent_norm ? 1 : 0;
+  s->eps = c->rms_eps;
+  s->route_scale = c->route_scale;
+  s->beta_gate = c->beta_gate;
+  s->beta_lin = c->beta_lin;
+  s->act = c->act;
+  s->wfmt = c->expert_wfmt;
+  s->j_gu = (int)cdiv64(s->l / 8, moe::kWave);
+  s->j_dn = (int)cdiv64(s->m / 8, moe::kWave);
+  size_t gu, dn;
+  if (s->wfmt == MOE_WFMT_MXFP4) {
+    gu = (size_t)(s->m / 2) * s->j_gu * moe::kFp4StepBytes;
+    dn = (size_t)(s->l / 4) * s->j_dn * moe::kFp4StepBytes;
+  } else {
+    gu = (size_t)2 * s->m * s->l * 2;
+    dn = (size_t)s->l * s->m * 2;
+  }
+  s->gu_bytes = gu;
+  s->expert_bytes = align256(gu + dn);
+  return MOE_OK;
+}
+
+// Workspace slots in the order of moe_workspace_layout.
+void layout(const Shape& s, int64_t T, size_t off[MOE_WS_NUM_SLOTS], size_t* total) {
+  const int64_t tk = T * s.k;
+  const int64_t nch = cdiv64(T, moe::dispatch_chunk_tokens(s.k));
+  const size_t sz[MOE_WS_NUM_SLOTS] = {
+      (size_t)T * s.l * 4,        // x^c
+      (size_t)T * s.ms * 4,       // h_s
+      (size_t)tk * s.m * 4,       // h
+      (size_t)tk * s.l * 4,       // E
+      (size_t)T * s.l * 4,        // u
+      (size_t)tk * 4,             // perm
+      (size_t)tk * 4,             // inv
+      (size_t)s.E * 4,            // counts
+      (size_t)(s.E + 1) * 4,      // offsets
+      (size_t)T * s.E * 4,        // z
+      (size_t)nch * s.E * 4,      // chunk histograms
+  };
+  size_t o = 0;
+  for (int i = 0; i < MOE_WS_NUM_SLOTS; ++i) {
+    off[i] = o;
+    o += align256(sz[i]);
+  }
+  *total = o;
+}
+
+moe::Work make_work(void* ws, const size_t off[MOE_WS_NUM_SLOTS]) {
+  char* b = static_cast<char*>(ws);
+  moe::Work w;
+  w.xc = reinterpret_cast<float*>(b + off[0]);
+  w.hs = reinterpret_cast<float*>(b + off[1]);
+  w.h = reinterpret_cast<float*>(b + off[2]);
+  w.eo = reinterpret_cast<float*>(b + off[3]);
+  w.u = reinterpret_cast<float*>(b + off[4]);
+  w.perm = reinterpret_cast<int32_t*>(b + off[5]);
+  w.inv = reinterpret_cast<int32_t*>(b + off[6]);
+  w.counts = reinterpret_cast<int32_t*>(b + off[7]);
+  w.offs = reinterpret_cast<int32_t*>(b + off[8]);
+  w.z = reinterpret_cast<float*>(b + off[9]);
+  w.chunk_hist = reinterpret_cast<int32_t*>(b + off[10]);
+  return w;
+}
+
+moe_status check_dense(const Shape& s, const moe_weights* w, bool router_only) {
+  if (!w || !w->router || !aligned(w->router, 16)) return MOE_ERR_INVALID_ARG;
+  if (router_only) return MOE_OK;
+  if (!w->w_down_latent || !w->w_up_latent || !w->experts) return MOE_ERR_INVALID_ARG;
+  if (!aligned(w->w_down_latent, 16) || !aligned(w->w_up_latent, 16) || !aligned(w->experts, 16))
+    return MOE_ERR_INVALID_ARG;
+  if (s.use_norm && (!w->norm_gamma || !aligned(w->norm_gamma, 16))) return MOE_ERR_INVALID_ARG;
+  if (s.ms > 0 && (!w->shared_gu || !w->shared_down || !aligned(w->shared_gu, 16) ||
+                   !aligned(w->shared_down, 16)))
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe::DenseW dense_of(const moe_weights* w) {
+  moe::DenseW d;
+  d.router = static_cast<const uint16_t*>(w->router);
+  d.wdn = static_cast<const uint16_t*>(w->w_down_latent);
+  d.wup = static_cast<const uint16_t*>(w->w_up_latent);
+  d.gamma = static_cast<const uint16_t*>(w->norm_gamma);
+  d.sgu = static_cast<const uint16_t*>(w->shared_gu);
+  d.sdn = static_cast<const uint16_t*>(w->shared_down);
+  d.experts = static_cast<const uint8_t*>(w->experts);
+  return d;
+}
+
+inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+MOE_EXPORT int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+MOE_EXPORT const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+MOE_EXPORT moe_status moe_packed_experts_size(const moe_config* cfg, size_t* bytes) {
+  Shape s;
+  moe_status st = make_shape(cfg, &s);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = s.expert_bytes * (size_t)s.E;
+  return MOE_OK;
+}
+
+MOE_EXPORT moe_status moe_pack_experts(const moe_config* cfg, const moe_expert_src* src,
+                                       int32_t e0, int32_t n, void* packed, size_t packed_bytes,
+                                       moe_stream_t stream) {
+  Shape s;
+  moe_status st = make_shape(cfg, &s);
+  if (st != MOE_OK) return st;
+  if (!src || !packed || !src->gu || !src->down || !aligned(packed, 16)) return MOE_ERR_INVALID_ARG;
+  if (s.wfmt == MOE_WFMT_MXFP4 &&
+      (!src->gu_scale || !src->down_scale || !aligned(src->gu, 4) || !aligned(src->down, 4)))
+    return MOE_ERR_INVALID_ARG;
+  if (e0 < 0 || n < 0 || (int64_t)e0 + n > s.E) return MOE_ERR_INVALID_ARG;
+  if (packed_bytes < s.expert_bytes * (size_t)s.E) return MOE_ERR_WORKSPACE;
+  if (n == 0) return MOE_OK;
+  return hip_status(moe::launch_pack(s, src->gu, src->gu_scale, src->down, src->down_scale, e0, n,
+                                     static_cast<uint8_t*>(packed), (hipStream_t)stream));
+}
+
+MOE_EXPORT moe_status moe_workspace_size(const moe_config* cfg, int64_t max_tokens, size_t* bytes) {
+  Shape s;
+  moe_status st = make_shape(cfg, &s);
+  if (st != MOE_OK) return st;
+  if (!bytes || max_tokens < 0) return MOE_ERR_INVALID_ARG;
+  size_t off[MOE_WS_NUM_SLOTS];
+  layout(s, max_tokens, off, bytes);
+  return MOE_OK;
+}
+
+MOE_EXPORT moe_status moe_workspace_layout(const moe_config* cfg, int64_t n_tokens,
+                                           size_t offsets[MOE_WS_NUM_SLOTS]) {
+  Shape s;
+  moe_status st = make_shape(cfg, &s);
+  if (st != MOE_OK) return st;
+  if (!offsets || n_tokens < 0) return MOE_ERR_INVALID_ARG;
+  size_t total;
+  layout(s, n_tokens, offsets, &total);
+  return MOE_OK;
+}
+
+namespace {
+
+moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const float* bias,
+                        const void* x, int64_t n_tokens, float* delta, int32_t* topk_idx,
+                        float* topk_w, void* workspace, size_t workspace_bytes,
+                        void* const* events, moe_stream_t stream) {
+  Shape s;
+  moe_status st = make_shape(cfg, &s);
+  if (st != MOE_OK) return st;
+  if (n_tokens < 0) return MOE_ERR_INVALID_ARG;
+  if ((st = check_dense(s, w, false)) != MOE_OK) return st;
+  if (!bias || !x || !delta || !topk_idx || !topk_w || !workspace) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(delta, 16) || !aligned(workspace, 256) || !aligned(bias, 4) ||
+      !aligned(topk_idx, 4) || !aligned(topk_w, 4))
+    return MOE_ERR_INVALID_ARG;
+  if (events)
+    for (int i = 0; i <= MOE_NUM_STEPS; ++i)
+      if (!events[i]) return MOE_ERR_INVALID_ARG;
+  if (n_tokens == 0) return MOE_OK;
+  size_t off[MOE_WS_NUM_SLOTS], need;
+  layout(s, n_tokens, off, &need);
+  if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  const moe::Work ws = make_work(workspace, off);
+  const moe::DenseW dw = dense_of(w);
+  hipStream_t hs = (hipStream_t)stream;
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  for (int step = 0; step < MOE_NUM_STEPS; ++step) {
+    if (events && hipEventRecord((hipEvent_t)events[step], hs) != hipSuccess) return MOE_ERR_HIP;
+    hipError_t e = hipSuccess;
+    switch (step) {
+      case MOE_STEP_DENSE_X: e = moe::launch_dense_x(s, dw, xb, n_tokens, false, ws, hs); break;
+      case MOE_STEP_TOPK: e = moe::launch_topk(s, bias, n_tokens, ws, topk_idx, topk_w, hs); break;
+      case MOE_STEP_DISPATCH:
+        e = moe::launch_dispatch(s, topk_idx, n_tokens, ws.counts, ws.offs, ws.perm, ws.inv,
+                                 ws.chunk_hist, hs);
+        break;
+      case MOE_STEP_EXPERT_GU: e = moe::launch_expert_gu(s, dw, topk_idx, n_tokens, ws, hs); break;
+      case MOE_STEP_EXPERT_DOWN: e = moe::launch_expert_down(s, dw, topk_idx, n_tokens, ws, hs); break;
+      case MOE_STEP_COMBINE: e = moe::launch_combine(s, topk_w, n_tokens, ws, hs); break;
+      case MOE_STEP_SHARED_DOWN: e = moe::launch_shared_down(s, dw, n_tokens, ws, delta, hs); break;
+      case MOE_STEP_UP: e = moe::launch_up(s, dw, n_tokens, ws, delta, hs); break;
+    }
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  if (events && hipEventRecord((hipEvent_t)events[MOE_NUM_STEPS], hs) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_EXPORT moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w,
+                                        const float* bias, const void* x, int64_t n_tokens,
+                                        float* delta, int32_t* topk_idx, float* topk_w,
+                                        void* workspace, size_t workspace_bytes,
+                                        moe_stream_t stream) {
+  return forward_impl(cfg, w, bias, x, n_tokens, delta, topk_idx, topk_w, workspace,
+                      workspace_bytes, nullptr, stream);
+}
+
+MOE_EXPORT moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w,
+                                              const float* bias, const void* x, int64_t n_tokens,
+                                              float* delta, int32_t* topk_idx, float* topk_w,
+                                              void* workspace, size_t workspace_bytes,
+                                              void* const* step_events, moe_stream_t stream) {
+  if (!step_events) return MOE_ERR_INVALID_ARG;
+  return forward_impl(cfg, w, bias, x, n_tokens, delta, topk_idx, topk_w, workspace,
+                      workspace_bytes, step_events, stream);
+}
+
+MOE_EXPORT moe_status moe_route(const moe_config* cfg, const moe_weights* w, const float* bias,
+                                const void* x, int64_t n_tokens, int32_t* topk_idx, float* topk_w,
+                                void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  Shape s;
+  moe_status st = make_shape(cfg, &s);
+  if (st != MOE_OK) return st;
+  if (n_tokens < 0) return MOE_ERR_INVALID_ARG;
+  if ((st = check_dense(s, w, true)) != MOE_OK) return st;
+  if (!bias || !x || !topk_idx || !topk_w || !workspace) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARG;
+  if (n_tokens == 0) return MOE_OK;
+  size_t off[MOE_WS_NUM_SLOTS], need;
+  layout(s, n_tokens, off, &need);
+  if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  const moe::Work ws = make_work(workspace, off);
+  const moe::DenseW dw = dense_of(w);
+  hipStream_t hs = (hipStream_t)stream;
+  if (moe::launch_dense_x(s, dw, static_cast<const uint16_t*>(x), n_tokens, true, ws, hs) != hipSuccess)
+    return MOE_ERR_HIP;
+  return hip_status(moe::launch_topk(s, bias, n_tokens, ws, topk_idx, topk_w, hs));
+}
+
+MOE_EXPORT moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int64_t n_tokens,
+                                   int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                                   void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  Shape s;
+  moe_status st = make_shape(cfg, &s);
+  if (st != MOE_OK) return st;
+  if (n_tokens < 0) return MOE_ERR_INVALID_ARG;
+  if (!topk_idx || !counts || !offsets || !perm || !inv || !workspace) return MOE_ERR_INVALID_ARG;
+  if (!aligned(workspace, 256)) return MOE_ERR_INVALID_ARG;
+  if (n_tokens == 0) return MOE_OK;
+  size_t off[MOE_WS_NUM_SLOTS], need;
+  layout(s, n_tokens, off, &need);
+  if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  const moe::Work ws = make_work(workspace, off);
+  return hip_status(moe::launch_dispatch(s, topk_idx, n_tokens, counts, offsets, perm, inv,
+                                         ws.chunk_hist, (hipStream_t)stream));
+}

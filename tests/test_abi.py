@@ -1,0 +1,124 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every declared entry
+point, sizes buffers as documented, and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_layer_amd as moe
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(moe.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return moe.lib()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 9
+    assert sorted(names) == sorted(moe.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert L.moe_abi_version() == 1
+    assert moe.status_str(0) == "MOE_OK"
+    assert moe.status_str(3) == "MOE_ERR_WORKSPACE"
+    assert moe.status_str(99) == "MOE_ERR_UNKNOWN"
+
+
+def test_packed_expert_bytes_equal_mxfp4_storage(L):
+    # MXFP4 packing moves bytes, it adds none: 4.25 bits per weight for the K3 experts
+    cfg = moe.config_from(synth.K3_DECODE_B1)
+    assert moe.packed_experts_size(cfg) == 896 * 17_547_264
+    assert 17_547_264 * 8 == 33_030_144 * 4.25
+    toy = moe.config_from(synth.TOY)    # bf16: 3 * 320 * 256 * 2 bytes per expert
+    assert moe.packed_experts_size(toy) == 64 * 491_520
+
+
+def test_workspace_layout_is_ordered_and_aligned(L):
+    cfg = moe.config_from(synth.K3_DECODE_B1)
+    for T in (1, 64, 8192):
+        off = moe.workspace_layout(cfg, T)
+        vals = [off[k] for k in moe.WS_SLOTS]
+        assert vals == sorted(vals) and all(v % 256 == 0 for v in vals)
+        assert moe.workspace_size(cfg, T) >= vals[-1]
+    assert moe.workspace_size(cfg, 64) > moe.workspace_size(cfg, 1)
+
+
+def _bad(**kw):
+    c = moe.config_from(synth.TOY)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("top_k", 65, moe.MOE_ERR_INVALID_ARG),          # k > E
+    ("top_k", 0, moe.MOE_ERR_INVALID_ARG),
+    ("d_model", 644, moe.MOE_ERR_INVALID_ARG),       # not a multiple of 8
+    ("d_model", 16384, moe.MOE_ERR_UNSUPPORTED),     # wider than the register-resident slice
+    ("n_experts", 2048, moe.MOE_ERR_UNSUPPORTED),
+    ("act", 7, moe.MOE_ERR_INVALID_ARG),
+    ("expert_wfmt", 5, moe.MOE_ERR_INVALID_ARG),
+    ("precision", 1, moe.MOE_ERR_UNSUPPORTED),
+    ("d_latent", 0, moe.MOE_ERR_UNSUPPORTED),
+    ("rms_eps", float("nan"), moe.MOE_ERR_INVALID_ARG),
+    ("beta_gate", 0.0, moe.MOE_ERR_INVALID_ARG),
+])
+def test_invalid_configs(L, field, value, status):
+    n = ctypes.c_size_t()
+    assert L.moe_workspace_size(ctypes.byref(_bad(**{field: value})), 4, ctypes.byref(n)) == status
+
+
+def test_mxfp4_needs_blocks_of_32(L):
+    n = ctypes.c_size_t()
+    c = _bad(expert_wfmt=1, d_latent=328)
+    assert L.moe_packed_experts_size(ctypes.byref(c), ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_forward_rejects_bad_arguments_before_launch(L):
+    cfg = moe.config_from(synth.TOY)
+    A = 1 << 20          # a 256-aligned non-null address; never dereferenced on error paths
+    W = moe.MoeWeights(A, A, A, A, A, A, A)
+    f = L.moe_layer_forward
+    ok = dict(bias=A, x=A, T=4, delta=A, idx=A, w=A, ws=A, wsb=1 << 40)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(ctypes.byref(cfg), ctypes.byref(a.get("W", W)), a["bias"], a["x"], a["T"],
+                 a["delta"], a["idx"], a["w"], a["ws"], a["wsb"], None)
+    assert call(x=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(delta=A + 4) == moe.MOE_ERR_INVALID_ARG          # misaligned output
+    assert call(ws=A + 64) == moe.MOE_ERR_INVALID_ARG            # workspace not 256-aligned
+    assert call(T=-1) == moe.MOE_ERR_INVALID_ARG
+    assert call(wsb=16) == moe.MOE_ERR_WORKSPACE
+    assert call(W=moe.MoeWeights(A, A, A, A, None, A, A)) == moe.MOE_ERR_INVALID_ARG
+    assert call(T=0) == moe.MOE_OK                               # nothing to do, no launch
+    assert f(None, ctypes.byref(W), A, A, 1, A, A, A, A, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_pack_and_dispatch_reject_bad_ranges(L):
+    cfg = moe.config_from(synth.TOY)
+    A = 1 << 20
+    src = moe.MoeExpertSrc(A, A, A, A)
+    size = moe.packed_experts_size(cfg)
+    assert L.moe_pack_experts(ctypes.byref(cfg), ctypes.byref(src), 60, 5, A, size, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_experts(ctypes.byref(cfg), ctypes.byref(src), 0, 4, A, size - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_pack_experts(ctypes.byref(cfg), ctypes.byref(src), 3, 0, A, size, None) == moe.MOE_OK
+    assert L.moe_dispatch(ctypes.byref(cfg), A, 8, A, A, A, A, A, 8, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_dispatch(ctypes.byref(cfg), None, 8, A, A, A, A, A, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG

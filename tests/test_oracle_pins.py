@@ -416,3 +416,18 @@ def test_generator_slices_are_independent_of_range():
     assert not np.array_equal(x0, x1)
     xf = O.bf16_to_f64(synth.tokens(synth.TOY.with_(tokens=512)))
     assert abs(xf.mean()) < 0.01 and abs(xf.std() - 1) < 0.01
+
+
+def test_dispatch_bookkeeping_brute_force():
+    rng = np.random.default_rng(8)
+    for _ in range(20):
+        E, k, T = int(rng.integers(1, 40)), 0, int(rng.integers(1, 30))
+        k = int(rng.integers(1, E + 1))
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+        counts, offs, perm, inv = O.dispatch(idx, E)
+        flat = idx.reshape(-1)
+        order = [a for e in range(E) for a in range(T * k) if flat[a] == e]
+        assert list(perm) == order
+        assert [sum(flat == e) for e in range(E)] == list(counts)
+        assert offs[0] == 0 and offs[-1] == T * k and np.all(np.diff(offs) == counts)
+        assert all(perm[inv[a]] == a for a in range(T * k))
