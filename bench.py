@@ -38,17 +38,18 @@ def algorithmic_bytes(cfg, T, D):
     else:
         gu_w, dn_w = 2 * m * l * 2, l * m * 2
     tk = T * k
+    small = T <= 4
     return {
-        "dense_x": T * d * 2 + (E + l + 2 * ms) * d * 2 + T * (E + l + ms) * 4,
-        "topk": T * E * 4 + E * 4 + tk * 8,
-        "dispatch": tk * 4 * 4 + E * 8,
+        "router": T * d * 2 + E * d * 2 + T * E * 4,
+        "dense_x": T * d * 2 + (l + 2 * ms) * d * 2 + T * (l + ms) * 4
+                   + ((T * E * 4 + E * 4 + tk * 16 + E * 8) if small else 0),
+        "route": 0 if small else T * E * 4 + E * 4 + tk * 8,
+        "dispatch": 0 if small else tk * 4 * 4 + E * 8,
         "expert_gu": D * gu_w + T * l * 4 + tk * m * 4,
         "expert_down": D * dn_w + tk * m * 4 + tk * l * 4,
         "combine": tk * l * 4 + tk * 8 + T * l * 4,
-        "shared_down": d * ms * 2 + T * ms * 4 + T * d * 4,
-        "up": d * l * 2 + l * 2 + T * l * 4 + 2 * T * d * 4,
+        "out": d * (l + ms) * 2 + l * 2 + T * (l + ms) * 4 + T * d * 4,
     }
-
 
 def weight_bytes(cfg, D):
     """Weights (and the fp32 bias) one call reads: the layer's algorithmic byte count."""
@@ -56,6 +57,40 @@ def weight_bytes(cfg, D):
     per_expert = (2 * m * (l // 2 + l // 32) + l * (m // 2 + m // 32)) if cfg.expert_fmt == "mxfp4" \
         else 3 * m * l * 2
     return (E * d + 2 * l * d + l + 3 * ms * d) * 2 + E * 4 + D * per_expert
+
+
+# rocprofv3 kernel symbol of each step's launch (its template arguments vary with shape)
+STEP_KERNELS = {"router": ("k_router",), "dense_x": ("k_dense_x",),
+                "expert_gu": ("k_expert_fp4", "true"), "expert_down": ("k_expert_fp4", "false"),
+                "combine": ("k_combine",), "out": ("k_out",)}
+
+
+def kernel_sources_sha():
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "sparse_moe_layer_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, step):
+    """HBM bytes per launch of `step` from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("traffic_json: "):
+            rec = json.loads(line[len("traffic_json: "):])
+            if rec.get("src_sha") != kernel_sources_sha():
+                return None
+            want = STEP_KERNELS.get(step, ())
+            for name, v in rec["bytes_per_launch"].items():
+                if want and all(w in name for w in want):
+                    return v
+    return None
 
 
 class HipEvents:
@@ -123,6 +158,8 @@ def main():
     ap.add_argument("--batches", type=int, default=64, help="distinct token batches rotated")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with a 1 GiB device copy (scale for HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -187,7 +224,9 @@ def main():
     ms_step = ms_total / K
     log(f"[bench] {K} steps: {ms_step * 1e3:.1f} us/step")
 
-    # per-step durations: the same forwards with in-stream events between the steps
+    # per-step durations: the same forwards with in-stream events between the steps.  An
+    # event record costs a few microseconds of GPU time, so this pass only ranks the steps;
+    # the dominant step is then timed with events around it alone.
     hip = HipEvents()
     nst = len(moe.STEPS)
     evs = hip.create(K * (nst + 1))
@@ -198,18 +237,48 @@ def main():
     step_ms = np.zeros(nst)
     for i in range(K):
         base = i * (nst + 1)
-        for s in range(nst):
-            step_ms[s] += hip.ms(evs[base + s], evs[base + s + 1])
+        for s_ in range(nst):
+            step_ms[s_] += hip.ms(evs[base + s_], evs[base + s_ + 1])
     step_ms /= K
     hip.destroy(evs)
-    steps_us = {n: round(v * 1e3, 2) for n, v in zip(moe.STEPS, step_ms)}
-    log(f"[bench] per step (us): {steps_us}")
+    steps_us = {n: round(float(v) * 1e3, 2) for n, v in zip(moe.STEPS, step_ms)}
+    log(f"[bench] per step with events at every boundary (us): {steps_us}")
+    dom = max(("dense_x", "expert_gu", "expert_down", "out"),
+              key=lambda n: step_ms[moe.STEPS.index(n)])
+    # The dominant step alone, K launches back to back between two events.  Each launch
+    # works on the buffers of an earlier full forward; R sets of buffers (different tokens,
+    # so different experts, and different dense copies) rotate past the last-level cache.
+    si = moe.STEPS.index(dom)
+    R = 8
+    sets = []
+    for r in range(R):
+        bufs = (torch.empty_like(delta), torch.empty_like(idx), torch.empty_like(gw),
+                torch.empty(ws.numel(), dtype=torch.uint8, device=dev))
+        layers[r % args.rotate].forward(xs[r % args.batches], *bufs[:3], workspace=bufs[3])
+        sets.append(bufs)
+    for r in range(R):
+        layers[r % args.rotate].forward_steps(xs[r % args.batches], si, si + 1, *sets[r])
+    torch.cuda.synchronize()
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e2.record()
+    for i in range(K):
+        r = i % R
+        layers[r % args.rotate].forward_steps(xs[r % args.batches], si, si + 1, *sets[r])
+    e3.record()
+    torch.cuda.synchronize()
+    dom_s = e2.elapsed_time(e3) / K * 1e-3
+    del sets
+    log(f"[bench] {dom}: {dom_s * 1e6:.2f} us per launch ({K} launches back to back)")
+    if args.copy_calibration:
+        # a plain device copy of known size, for scaling HBM byte counters
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 1 GiB read + 1 GiB written")
 
     Dm = float(np.mean([D[i % args.batches] for i in range(K)]))
     ab = algorithmic_bytes(cfg, T, Dm)
-    dom = max(("dense_x", "expert_gu", "expert_down", "shared_down", "up"),
-              key=lambda n: step_ms[moe.STEPS.index(n)])
-    dom_s = step_ms[moe.STEPS.index(dom)] * 1e-3
     achieved = ab[dom] / dom_s / 1e9
     layer_bytes = weight_bytes(cfg, Dm)
     layer_gbs = layer_bytes / (ms_step * 1e-3) / 1e9
@@ -233,10 +302,12 @@ def main():
                    "dense_weight_copies": args.rotate, "token_batches": args.batches,
                    "distinct_experts_per_step": Dm},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(cfg.name, dom),
                      "algorithmic_bytes": ab[dom], "avg_us": dom_s * 1e6},
         "layer": {"algorithmic_bytes": layer_bytes, "achieved_GBps": layer_gbs,
-                  "hbm_frac": layer_gbs / HBM_PEAK_GBS, "steps_us": steps_us},
+                  "hbm_frac": layer_gbs / HBM_PEAK_GBS,
+                  "steps_us_with_event_per_boundary": steps_us},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")

@@ -158,7 +158,7 @@ moe_status moe_workspace_layout(const moe_config* cfg, int64_t n_tokens,
  *   topk_idx  [T, k] int32 selected experts, in descending s + b, ties to the lower index
  *   topk_w    [T, k] fp32 gate weights route_scale * s / sum(s) in the same order
  *   workspace at least moe_workspace_size(cfg, n_tokens) bytes, 256-byte aligned
- * n_tokens == 0 returns MOE_OK and launches nothing.  Errors: MOE_ERR_INVALID_ARG,
+ * n_tokens == 0 returns MOE_OK after checking cfg, launches nothing and touches no pointer.  Errors: MOE_ERR_INVALID_ARG,
  * MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
 moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const float* bias,
                              const void* x, int64_t n_tokens, float* delta, int32_t* topk_idx,
@@ -167,27 +167,45 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const 
 
 /* Steps of the forward, in launch order. */
 typedef enum moe_step {
-  MOE_STEP_DENSE_X = 0,     /* router logits, x^c = x W_down_latent, shared gate/up + SiTU */
-  MOE_STEP_TOPK = 1,        /* sigmoid, top_k(s + b), gate weights */
-  MOE_STEP_DISPATCH = 2,    /* histogram, scan, stable permutation by expert */
-  MOE_STEP_EXPERT_GU = 3,   /* routed gate/up + SiTU */
-  MOE_STEP_EXPERT_DOWN = 4, /* routed down */
-  MOE_STEP_COMBINE = 5,     /* u = sum_j G_j E_j */
-  MOE_STEP_SHARED_DOWN = 6, /* y_shared = h_s W_shared_down */
-  MOE_STEP_UP = 7,          /* Delta = RMSNorm(u) W_up_latent + y_shared */
+  MOE_STEP_ROUTER = 0,      /* router logits z = x W_r */
+  MOE_STEP_DENSE_X = 1,     /* x^c = x W_down_latent and shared gate/up + SiTU; with at most
+                               4 tokens one workgroup of the same launch also takes the
+                               top-k, the gate weights and the dispatch */
+  MOE_STEP_ROUTE = 2,       /* sigmoid, top_k(s + b), gate weights (more than 4 tokens;
+                               launches nothing otherwise) */
+  MOE_STEP_DISPATCH = 3,    /* histogram, scan, stable permutation by expert (more than 4
+                               tokens; launches nothing otherwise) */
+  MOE_STEP_EXPERT_GU = 4,   /* routed gate/up + SiTU */
+  MOE_STEP_EXPERT_DOWN = 5, /* routed down */
+  MOE_STEP_COMBINE = 6,     /* u = sum_j G_j E_j */
+  MOE_STEP_OUT = 7,         /* Delta = RMSNorm(u) W_up_latent + h_s W_shared_down */
   MOE_NUM_STEPS = 8
 } moe_step;
 
 /* moe_layer_forward with per-step timing: identical work and results, and additionally
  * records step_events[s] on `stream` just before step s is launched (s = 0..7) and
  * step_events[MOE_NUM_STEPS] after the last one.  step_events holds MOE_NUM_STEPS + 1
- * hipEvent_t handles created by the caller (with timing enabled); they are only recorded,
- * never synchronised on.  For profilers and benchmarks; errors as moe_layer_forward. */
+ * hipEvent_t handles created by the caller (with timing enabled), or NULL entries for
+ * boundaries that need no event; they are only recorded, never synchronised on.  For
+ * profilers and benchmarks; errors as moe_layer_forward. */
 moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w,
                                    const float* bias, const void* x, int64_t n_tokens,
                                    float* delta, int32_t* topk_idx, float* topk_w,
                                    void* workspace, size_t workspace_bytes,
                                    void* const* step_events, moe_stream_t stream);
+
+/* Steps step_begin..step_end-1 of moe_layer_forward alone (0 <= begin <= end <= 8).
+ * Each step reads what the earlier steps left in `workspace`, topk_idx and topk_w, so a
+ * range that starts after step 0 is only meaningful on the buffers of an earlier call
+ * with the same config, weights, tokens and n_tokens.  Running [0, MOE_NUM_STEPS) is
+ * moe_layer_forward.  For profilers, benchmarks and callers that interleave the steps
+ * of several layers; errors as moe_layer_forward, plus MOE_ERR_INVALID_ARG for a bad
+ * range. */
+moe_status moe_layer_forward_steps(const moe_config* cfg, const moe_weights* w,
+                                   const float* bias, const void* x, int64_t n_tokens,
+                                   float* delta, int32_t* topk_idx, float* topk_w,
+                                   void* workspace, size_t workspace_bytes, int32_t step_begin,
+                                   int32_t step_end, moe_stream_t stream);
 
 /* The router step alone (block card: z = x W_r, s = sigmoid(z), top_k(s + b), and G;
  * toy chapter: the bias selects, the raw score weights).  Same arguments and output

@@ -21,8 +21,8 @@ WS_SLOTS = ("xc", "hs", "h", "eo", "u", "perm", "inv", "counts", "offsets", "z",
 
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_packed_experts_size", "moe_pack_experts",
            "moe_workspace_size", "moe_workspace_layout", "moe_layer_forward",
-           "moe_layer_forward_timed", "moe_route", "moe_dispatch")
-STEPS = ("dense_x", "topk", "dispatch", "expert_gu", "expert_down", "combine", "shared_down", "up")
+           "moe_layer_forward_timed", "moe_layer_forward_steps", "moe_route", "moe_dispatch")
+STEPS = ("router", "dense_x", "route", "dispatch", "expert_gu", "expert_down", "combine", "out")
 
 
 class MoeConfig(ctypes.Structure):
@@ -80,6 +80,8 @@ def lib():
     L.moe_layer_forward.argtypes = [P(MoeConfig), P(MoeWeights), vp, vp, i64, vp, vp, vp, vp, sz, vp]
     L.moe_layer_forward_timed.argtypes = [P(MoeConfig), P(MoeWeights), vp, vp, i64, vp, vp, vp,
                                           vp, sz, vp, vp]
+    L.moe_layer_forward_steps.argtypes = [P(MoeConfig), P(MoeWeights), vp, vp, i64, vp, vp, vp,
+                                          vp, sz, ctypes.c_int32, ctypes.c_int32, vp]
     L.moe_route.argtypes = [P(MoeConfig), P(MoeWeights), vp, vp, i64, vp, vp, vp, sz, vp]
     L.moe_dispatch.argtypes = [P(MoeConfig), vp, i64, vp, vp, vp, vp, vp, sz, vp]
     for f in EXPORTS[2:]:
@@ -246,6 +248,15 @@ class Layer:
                                              w.data_ptr(), ws.data_ptr(), ws.numel(), ev,
                                              _stream(stream)), "moe_layer_forward_timed")
         return delta, idx, w
+
+    def forward_steps(self, x, begin, end, delta, idx, w, workspace, stream=None):
+        """Steps begin..end-1 of the forward on the buffers of an earlier call."""
+        W = self.weights_struct()
+        _check(lib().moe_layer_forward_steps(ctypes.byref(self.cfg), ctypes.byref(W),
+                                             self.bias.data_ptr(), x.data_ptr(), x.shape[0],
+                                             delta.data_ptr(), idx.data_ptr(), w.data_ptr(),
+                                             workspace.data_ptr(), workspace.numel(), begin, end,
+                                             _stream(stream)), "moe_layer_forward_steps")
 
     def route(self, x, stream=None):
         import torch

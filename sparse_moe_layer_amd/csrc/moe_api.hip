@@ -198,20 +198,18 @@ namespace {
 moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const float* bias,
                         const void* x, int64_t n_tokens, float* delta, int32_t* topk_idx,
                         float* topk_w, void* workspace, size_t workspace_bytes,
-                        void* const* events, moe_stream_t stream) {
+                        void* const* events, int step_begin, int step_end, moe_stream_t stream) {
   Shape s;
   moe_status st = make_shape(cfg, &s);
   if (st != MOE_OK) return st;
   if (n_tokens < 0) return MOE_ERR_INVALID_ARG;
+  if (step_begin < 0 || step_end > MOE_NUM_STEPS || step_begin > step_end) return MOE_ERR_INVALID_ARG;
+  if (n_tokens == 0) return MOE_OK;  // nothing to read or write: buffers may be empty (null)
   if ((st = check_dense(s, w, false)) != MOE_OK) return st;
   if (!bias || !x || !delta || !topk_idx || !topk_w || !workspace) return MOE_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(delta, 16) || !aligned(workspace, 256) || !aligned(bias, 4) ||
       !aligned(topk_idx, 4) || !aligned(topk_w, 4))
     return MOE_ERR_INVALID_ARG;
-  if (events)
-    for (int i = 0; i <= MOE_NUM_STEPS; ++i)
-      if (!events[i]) return MOE_ERR_INVALID_ARG;
-  if (n_tokens == 0) return MOE_OK;
   size_t off[MOE_WS_NUM_SLOTS], need;
   layout(s, n_tokens, off, &need);
   if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
@@ -219,25 +217,33 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const float
   const moe::DenseW dw = dense_of(w);
   hipStream_t hs = (hipStream_t)stream;
   const uint16_t* xb = static_cast<const uint16_t*>(x);
-  for (int step = 0; step < MOE_NUM_STEPS; ++step) {
-    if (events && hipEventRecord((hipEvent_t)events[step], hs) != hipSuccess) return MOE_ERR_HIP;
+  for (int step = step_begin; step < step_end; ++step) {
+    if (events && events[step] && hipEventRecord((hipEvent_t)events[step], hs) != hipSuccess)
+      return MOE_ERR_HIP;
     hipError_t e = hipSuccess;
+    const bool fused = moe::route_fused(n_tokens, s.k);
     switch (step) {
-      case MOE_STEP_DENSE_X: e = moe::launch_dense_x(s, dw, xb, n_tokens, false, ws, hs); break;
-      case MOE_STEP_TOPK: e = moe::launch_topk(s, bias, n_tokens, ws, topk_idx, topk_w, hs); break;
+      case MOE_STEP_ROUTER: e = moe::launch_router(s, dw, xb, n_tokens, ws, hs); break;
+      case MOE_STEP_DENSE_X:
+        e = moe::launch_dense_x(s, dw, xb, n_tokens, bias, topk_idx, topk_w, ws, hs);
+        break;
+      case MOE_STEP_ROUTE:
+        if (!fused) e = moe::launch_route(s, bias, n_tokens, ws, topk_idx, topk_w, hs);
+        break;
       case MOE_STEP_DISPATCH:
-        e = moe::launch_dispatch(s, topk_idx, n_tokens, ws.counts, ws.offs, ws.perm, ws.inv,
-                                 ws.chunk_hist, hs);
+        if (!fused)
+          e = moe::launch_dispatch(s, topk_idx, n_tokens, ws.counts, ws.offs, ws.perm, ws.inv,
+                                   ws.chunk_hist, hs);
         break;
       case MOE_STEP_EXPERT_GU: e = moe::launch_expert_gu(s, dw, topk_idx, n_tokens, ws, hs); break;
       case MOE_STEP_EXPERT_DOWN: e = moe::launch_expert_down(s, dw, topk_idx, n_tokens, ws, hs); break;
       case MOE_STEP_COMBINE: e = moe::launch_combine(s, topk_w, n_tokens, ws, hs); break;
-      case MOE_STEP_SHARED_DOWN: e = moe::launch_shared_down(s, dw, n_tokens, ws, delta, hs); break;
-      case MOE_STEP_UP: e = moe::launch_up(s, dw, n_tokens, ws, delta, hs); break;
+      case MOE_STEP_OUT: e = moe::launch_out(s, dw, n_tokens, ws, delta, hs); break;
     }
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
-  if (events && hipEventRecord((hipEvent_t)events[MOE_NUM_STEPS], hs) != hipSuccess)
+  if (events && step_end == MOE_NUM_STEPS && events[MOE_NUM_STEPS] &&
+      hipEventRecord((hipEvent_t)events[MOE_NUM_STEPS], hs) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
 }
@@ -250,7 +256,17 @@ MOE_EXPORT moe_status moe_layer_forward(const moe_config* cfg, const moe_weights
                                         void* workspace, size_t workspace_bytes,
                                         moe_stream_t stream) {
   return forward_impl(cfg, w, bias, x, n_tokens, delta, topk_idx, topk_w, workspace,
-                      workspace_bytes, nullptr, stream);
+                      workspace_bytes, nullptr, 0, MOE_NUM_STEPS, stream);
+}
+
+MOE_EXPORT moe_status moe_layer_forward_steps(const moe_config* cfg, const moe_weights* w,
+                                              const float* bias, const void* x, int64_t n_tokens,
+                                              float* delta, int32_t* topk_idx, float* topk_w,
+                                              void* workspace, size_t workspace_bytes,
+                                              int32_t step_begin, int32_t step_end,
+                                              moe_stream_t stream) {
+  return forward_impl(cfg, w, bias, x, n_tokens, delta, topk_idx, topk_w, workspace,
+                      workspace_bytes, nullptr, step_begin, step_end, stream);
 }
 
 MOE_EXPORT moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w,
@@ -260,7 +276,7 @@ MOE_EXPORT moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_w
                                               void* const* step_events, moe_stream_t stream) {
   if (!step_events) return MOE_ERR_INVALID_ARG;
   return forward_impl(cfg, w, bias, x, n_tokens, delta, topk_idx, topk_w, workspace,
-                      workspace_bytes, step_events, stream);
+                      workspace_bytes, step_events, 0, MOE_NUM_STEPS, stream);
 }
 
 MOE_EXPORT moe_status moe_route(const moe_config* cfg, const moe_weights* w, const float* bias,
@@ -270,19 +286,19 @@ MOE_EXPORT moe_status moe_route(const moe_config* cfg, const moe_weights* w, con
   moe_status st = make_shape(cfg, &s);
   if (st != MOE_OK) return st;
   if (n_tokens < 0) return MOE_ERR_INVALID_ARG;
+  if (n_tokens == 0) return MOE_OK;
   if ((st = check_dense(s, w, true)) != MOE_OK) return st;
   if (!bias || !x || !topk_idx || !topk_w || !workspace) return MOE_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARG;
-  if (n_tokens == 0) return MOE_OK;
   size_t off[MOE_WS_NUM_SLOTS], need;
   layout(s, n_tokens, off, &need);
   if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
   const moe::Work ws = make_work(workspace, off);
   const moe::DenseW dw = dense_of(w);
   hipStream_t hs = (hipStream_t)stream;
-  if (moe::launch_dense_x(s, dw, static_cast<const uint16_t*>(x), n_tokens, true, ws, hs) != hipSuccess)
+  if (moe::launch_router(s, dw, static_cast<const uint16_t*>(x), n_tokens, ws, hs) != hipSuccess)
     return MOE_ERR_HIP;
-  return hip_status(moe::launch_topk(s, bias, n_tokens, ws, topk_idx, topk_w, hs));
+  return hip_status(moe::launch_route(s, bias, n_tokens, ws, topk_idx, topk_w, hs));
 }
 
 MOE_EXPORT moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int64_t n_tokens,
@@ -292,9 +308,9 @@ MOE_EXPORT moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_id
   moe_status st = make_shape(cfg, &s);
   if (st != MOE_OK) return st;
   if (n_tokens < 0) return MOE_ERR_INVALID_ARG;
+  if (n_tokens == 0) return MOE_OK;
   if (!topk_idx || !counts || !offsets || !perm || !inv || !workspace) return MOE_ERR_INVALID_ARG;
   if (!aligned(workspace, 256)) return MOE_ERR_INVALID_ARG;
-  if (n_tokens == 0) return MOE_OK;
   size_t off[MOE_WS_NUM_SLOTS], need;
   layout(s, n_tokens, off, &need);
   if (workspace_bytes < need) return MOE_ERR_WORKSPACE;

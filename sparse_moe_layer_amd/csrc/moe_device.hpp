@@ -10,6 +10,7 @@ namespace moe {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -23,11 +24,72 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(b), c, false);
 }
 
-// Butterfly sum over the 64 lanes; every lane receives the same, order-fixed result.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+// Streaming (non-temporal) loads for weights that are read once per call.
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld_stream32(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
+// ---- wavefront reductions through DPP row shifts and row broadcasts -----------------
+// The partial results travel lane i-1 -> i inside each 16-lane row, then row 0 -> 1,
+// row 2 -> 3 and rows 0+1 -> 2, 3; lane 63 ends with the total.  The order of the
+// additions is fixed, so the result is deterministic.
+template <int CTRL, int ROW_MASK, bool BOUND>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, BOUND);
+}
+template <int CTRL, int ROW_MASK, bool BOUND>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL, ROW_MASK, BOUND>(0u, __float_as_uint(v)));
+}
+
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114,
+              kDppRowShr8 = 0x118, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+__device__ __forceinline__ float wave_sum_to_lane63(float v) {
+  v += dpp_f32<kDppRowShr1, 0xF, true>(v);
+  v += dpp_f32<kDppRowShr2, 0xF, true>(v);
+  v += dpp_f32<kDppRowShr4, 0xF, true>(v);
+  v += dpp_f32<kDppRowShr8, 0xF, true>(v);
+  v += dpp_f32<kDppRowBcast15, 0xA, false>(v);
+  v += dpp_f32<kDppRowBcast31, 0xC, false>(v);
   return v;
+}
+
+// Sum over the 64 lanes, returned to every lane (wavefront-uniform).
+__device__ __forceinline__ float wave_sum(float v) {
+  return __uint_as_float(
+      (uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(wave_sum_to_lane63(v)), 63));
+}
+
+template <int CTRL, int ROW_MASK, bool BOUND>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = dpp_u32<CTRL, ROW_MASK, BOUND>(0u, (uint32_t)v);
+  const uint32_t hi = dpp_u32<CTRL, ROW_MASK, BOUND>(0u, (uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Maximum of an unsigned 64-bit key over the 64 lanes (0 is the identity).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = max_u64(v, dpp_u64<kDppRowShr1, 0xF, true>(v));
+  v = max_u64(v, dpp_u64<kDppRowShr2, 0xF, true>(v));
+  v = max_u64(v, dpp_u64<kDppRowShr4, 0xF, true>(v));
+  v = max_u64(v, dpp_u64<kDppRowShr8, 0xF, true>(v));
+  v = max_u64(v, dpp_u64<kDppRowBcast15, 0xA, false>(v));
+  v = max_u64(v, dpp_u64<kDppRowBcast31, 0xC, false>(v));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Unsigned key with the order of the float (after -0 -> +0).
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 // E8M0 byte -> the fp32 whose exponent field is that byte (2^(e-127) for e in 1..254).
@@ -38,7 +100,7 @@ __device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + expf
 // SiTU-GLU (act 0) or SwiGLU (act 1) of one gate/up pair.
 __device__ __forceinline__ float glu_act(float g, float u, int act, float bg, float bl) {
   if (act == 0) {
-    float a = bg * tanhf(g / bg) * sigmoidf_(g);
+    const float a = bg * tanhf(g / bg) * sigmoidf_(g);
     return a * (bl * tanhf(u / bl));
   }
   return g * sigmoidf_(g) * u;

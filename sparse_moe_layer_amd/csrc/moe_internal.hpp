@@ -55,10 +55,16 @@ struct DenseW {
 // Tokens per dispatch chunk (so that a chunk holds at most 256 assignments).
 inline int dispatch_chunk_tokens(int k) { return k >= 256 ? 1 : 256 / k; }
 
+hipError_t launch_router(const Shape& s, const DenseW& w, const uint16_t* x, int64_t T,
+                         const Work& ws, hipStream_t st);
+// latent down + shared gate/up; for route_fused batches also the route and the dispatch
 hipError_t launch_dense_x(const Shape& s, const DenseW& w, const uint16_t* x, int64_t T,
-                          bool router_only, const Work& ws, hipStream_t st);
-hipError_t launch_topk(const Shape& s, const float* bias, int64_t T, const Work& ws,
-                       int32_t* idx, float* gw, hipStream_t st);
+                          const float* bias, int32_t* idx, float* gw, const Work& ws,
+                          hipStream_t st);
+// The route step in its own launch (no dispatch).
+bool route_fused(int64_t T, int k);
+hipError_t launch_route(const Shape& s, const float* bias, int64_t T, const Work& ws,
+                        int32_t* idx, float* gw, hipStream_t st);
 hipError_t launch_dispatch(const Shape& s, const int32_t* idx, int64_t T, int32_t* counts,
                            int32_t* offs, int32_t* perm, int32_t* inv, int32_t* chunk_hist,
                            hipStream_t st);
@@ -68,10 +74,8 @@ hipError_t launch_expert_down(const Shape& s, const DenseW& w, const int32_t* id
                               const Work& ws, hipStream_t st);
 hipError_t launch_combine(const Shape& s, const float* gw, int64_t T, const Work& ws,
                           hipStream_t st);
-hipError_t launch_shared_down(const Shape& s, const DenseW& w, int64_t T, const Work& ws,
-                              float* delta, hipStream_t st);
-hipError_t launch_up(const Shape& s, const DenseW& w, int64_t T, const Work& ws, float* delta,
-                     hipStream_t st);
+hipError_t launch_out(const Shape& s, const DenseW& w, int64_t T, const Work& ws, float* delta,
+                      hipStream_t st);
 hipError_t launch_pack(const Shape& s, const void* gu, const void* gus, const void* dn,
                        const void* dns, int e0, int n, uint8_t* packed, hipStream_t st);
 

@@ -109,6 +109,7 @@ def test_forward_rejects_bad_arguments_before_launch(L):
     assert call(wsb=16) == moe.MOE_ERR_WORKSPACE
     assert call(W=moe.MoeWeights(A, A, A, A, None, A, A)) == moe.MOE_ERR_INVALID_ARG
     assert call(T=0) == moe.MOE_OK                               # nothing to do, no launch
+    assert call(T=0, x=None, delta=None, W=moe.MoeWeights()) == moe.MOE_OK
     assert f(None, ctypes.byref(W), A, A, 1, A, A, A, A, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
 
 
@@ -122,3 +123,4 @@ def test_pack_and_dispatch_reject_bad_ranges(L):
     assert L.moe_pack_experts(ctypes.byref(cfg), ctypes.byref(src), 3, 0, A, size, None) == moe.MOE_OK
     assert L.moe_dispatch(ctypes.byref(cfg), A, 8, A, A, A, A, A, 8, None) == moe.MOE_ERR_WORKSPACE
     assert L.moe_dispatch(ctypes.byref(cfg), None, 8, A, A, A, A, A, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_dispatch(ctypes.byref(cfg), None, 0, None, None, None, None, None, 0, None) == moe.MOE_OK

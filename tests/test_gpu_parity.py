@@ -203,3 +203,33 @@ def test_k3_decode_b64_sampled_tokens():
     # per-token independence: the same token alone gives the same Delta bits
     d1, i1, w1 = run(lay, x[21:22])
     assert np.array_equal(i1[0], idx[21]) and np.array_equal(d1[0], delta[21])
+
+
+def test_step_ranges_and_timed_forward_match_the_forward():
+    cfg = TINY.with_(tokens=3)
+    lay, _ = device_layer(TINY)
+    x = to_dev(synth.tokens(cfg, batch=7))
+    ref = [t.cpu().clone() for t in lay.forward(x)]
+    T = x.shape[0]
+    ws = torch.zeros(moe.workspace_size(lay.cfg, T), dtype=torch.uint8, device=DEV)
+    d = torch.empty((T, TINY.d), dtype=torch.float32, device=DEV)
+    i = torch.empty((T, TINY.k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, TINY.k), dtype=torch.float32, device=DEV)
+    lay.forward_steps(x, 0, 4, d, i, w, ws)
+    lay.forward_steps(x, 4, len(moe.STEPS), d, i, w, ws)
+    for p, q in zip(ref, (d, i, w)):
+        assert torch.equal(p, q.cpu())
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    evs = []
+    for _ in range(len(moe.STEPS) + 1):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    d2, i2, w2 = torch.empty_like(d), torch.empty_like(i), torch.empty_like(w)
+    lay.forward_timed(x, evs, d2, i2, w2)
+    torch.cuda.synchronize()
+    for p, q in zip(ref, (d2, i2, w2)):
+        assert torch.equal(p, q.cpu())
+    for e in evs:
+        hip.hipEventDestroy(ctypes.c_void_p(e))
