@@ -38,11 +38,11 @@ def algorithmic_bytes(cfg, T, D):
     else:
         gu_w, dn_w = 2 * m * l * 2, l * m * 2
     tk = T * k
-    small = T <= 4
+    small = T <= 3   # the route and the dispatch run inside the IN launch
     return {
-        "router": T * d * 2 + E * d * 2 + T * E * 4,
-        "dense_x": T * d * 2 + (l + 2 * ms) * d * 2 + T * (l + ms) * 4
-                   + ((T * E * 4 + E * 4 + tk * 16 + E * 8) if small else 0),
+        "router": T * d * 2 + E * d * 2 + T * E * 4 * 8,
+        "in": T * d * 2 + (l + 2 * ms) * d * 2 + T * (l + ms) * 4
+              + ((T * E * 4 * 8 + E * 4 + tk * 16 + E * 8) if small else 0),
         "route": 0 if small else T * E * 4 + E * 4 + tk * 8,
         "dispatch": 0 if small else tk * 4 * 4 + E * 8,
         "expert_gu": D * gu_w + T * l * 4 + tk * m * 4,
@@ -60,9 +60,8 @@ def weight_bytes(cfg, D):
 
 
 # rocprofv3 kernel symbol of each step's launch (its template arguments vary with shape)
-STEP_KERNELS = {"router": ("k_router",), "dense_x": ("k_dense_x",),
-                "expert_gu": ("k_expert_fp4", "true"), "expert_down": ("k_expert_fp4", "false"),
-                "combine": ("k_combine",), "out": ("k_out",)}
+STEP_KERNELS = {"router": ("k_router",), "in": ("k_in",), "expert_gu": ("k_exp", "true"),
+                "expert_down": ("k_exp", "false"), "combine": ("k_combine",), "out": ("k_out",)}
 
 
 def kernel_sources_sha():
@@ -243,7 +242,7 @@ def main():
     hip.destroy(evs)
     steps_us = {n: round(float(v) * 1e3, 2) for n, v in zip(moe.STEPS, step_ms)}
     log(f"[bench] per step with events at every boundary (us): {steps_us}")
-    dom = max(("dense_x", "expert_gu", "expert_down", "out"),
+    dom = max(("in", "expert_gu", "expert_down", "out"),
               key=lambda n: step_ms[moe.STEPS.index(n)])
     # The dominant step alone, K launches back to back between two events.  Each launch
     # works on the buffers of an earlier full forward; R sets of buffers (different tokens,
@@ -253,7 +252,7 @@ def main():
     sets = []
     for r in range(R):
         bufs = (torch.empty_like(delta), torch.empty_like(idx), torch.empty_like(gw),
-                torch.empty(ws.numel(), dtype=torch.uint8, device=dev))
+                moe.new_workspace(mcfg, T, dev))
         layers[r % args.rotate].forward(xs[r % args.batches], *bufs[:3], workspace=bufs[3])
         sets.append(bufs)
     for r in range(R):

@@ -15,8 +15,8 @@
  *
  * Conventions shared by every entry point
  *   - All pointers are device pointers unless stated otherwise.  The caller allocates
- *     and owns every buffer; the library never allocates, frees or retains memory, and
- *     keeps no state between calls.
+ *     and owns every buffer; the library never allocates, frees or retains memory and
+ *     keeps no state between calls outside the workspace the caller passes.
  *   - Matrices are row-major [out, in] as nn.Linear stores them.  bf16 is passed as its
  *     16-bit pattern.  Weight, token and output buffers must be 16-byte aligned.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null stream)
@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef struct ihipStream_t* moe_stream_t; /* the same type as hipStream_t */
 
@@ -88,15 +88,21 @@ typedef struct moe_config {
   int32_t precision;       /* moe_precision */
 } moe_config;
 
-/* Dense weights (canonical [out, in] bf16) and the packed routed experts. */
-typedef struct moe_weights {
+/* Canonical dense weights, bf16 [out, in] (as moe_pack_dense reads them). */
+typedef struct moe_dense_src {
   const void* router;        /* W_r           [E, d]       bf16 */
   const void* w_down_latent; /* W_down_latent [l, d]       bf16 */
   const void* w_up_latent;   /* W_up_latent   [d, l]       bf16 */
-  const void* norm_gamma;    /* RMSNorm gain  [l]          bf16 (unused if no norm) */
-  const void* shared_gu;     /* shared gate rows then up rows [2 m_s, d] bf16 */
-  const void* shared_down;   /* shared down   [d, m_s]     bf16 */
-  const void* experts;       /* routed experts in the layout written by moe_pack_experts */
+  const void* norm_gamma;    /* RMSNorm gain  [l]          bf16 (copied even without norm) */
+  const void* shared_gu;     /* shared gate rows then up rows [2 m_s, d] bf16 (m_s > 0) */
+  const void* shared_down;   /* shared down   [d, m_s]     bf16 (m_s > 0) */
+} moe_dense_src;
+
+/* The weights of a forward call: both buffers in the packed layouts written by
+ * moe_pack_dense and moe_pack_experts, 256-byte aligned. */
+typedef struct moe_weights {
+  const void* dense;
+  const void* experts;
 } moe_weights;
 
 /* Canonical routed-expert storage for a run of consecutive experts, each pointer at
@@ -118,16 +124,36 @@ int moe_abi_version(void);
 /* Static string naming a status code. */
 const char* moe_status_str(moe_status s);
 
+/* Bytes of the packed dense-weight buffer (host call, no launch).
+ * Errors: MOE_ERR_INVALID_ARG (null pointer or invalid config), MOE_ERR_UNSUPPORTED. */
+moe_status moe_packed_dense_size(const moe_config* cfg, size_t* bytes);
+
+/* Rewrite the canonical dense weights into the tiled order the kernels stream (a
+ * one-time copy per layer).  The packed buffer holds two matrices of 16-row tiles:
+ *   IN  = [W_r ; W_down_latent ; shared gate/up] over the d input columns, and
+ *   OUT = [W_up_latent | W_shared_down] over l (padded to 128) + m_s input columns,
+ * plus a copy of the norm gain.  In a tile, every 16 rows x 32 columns form 1 KiB in
+ * the operand order of the 16x16x32 bf16 matrix instruction; shared gate/up tiles carry
+ * 8 gate rows and the matching 8 up rows.  Rows and columns past the matrices are zero.
+ * packed: moe_packed_dense_size bytes, 256-byte aligned; sources 16-byte aligned.
+ * Errors: MOE_ERR_INVALID_ARG (null or misaligned pointer), MOE_ERR_WORKSPACE
+ * (packed_bytes too small), MOE_ERR_HIP. */
+moe_status moe_pack_dense(const moe_config* cfg, const moe_dense_src* src, void* packed,
+                          size_t packed_bytes, moe_stream_t stream);
+
 /* Bytes of the packed routed-expert buffer for the whole layer (host call, no launch).
  * Errors: MOE_ERR_INVALID_ARG (null pointer or invalid config), MOE_ERR_UNSUPPORTED. */
 moe_status moe_packed_experts_size(const moe_config* cfg, size_t* bytes);
 
 /* Rewrite canonical experts e0..e0+n-1 into the kernel-native order inside `packed`
- * (a buffer of moe_packed_experts_size bytes for the whole layer).  The run may be any
- * sub-range, so a layer can be packed in pieces.  MXFP4 is regrouped so that one
- * wavefront load brings four rows' 8-column chunks and their scale bytes together; the
- * bytes are not changed, only moved.  Errors: MOE_ERR_INVALID_ARG (null pointer, range
- * outside 0..E), MOE_ERR_WORKSPACE (packed_bytes too small), MOE_ERR_HIP. */
+ * (a buffer of moe_packed_experts_size bytes for the whole layer, 256-byte aligned).
+ * The run may be any sub-range, so a layer can be packed in pieces.  Each expert holds
+ * gate/up tiles (8 gate rows + the matching 8 up rows over l columns) and then down
+ * tiles (16 rows over m columns), in K-steps of 128 columns; MXFP4 K-steps are 1 KiB of
+ * codes in the operand order of the matrix instruction plus the 16 rows' four scale
+ * bytes, so one wavefront load brings both.  The code and scale bytes are moved, not
+ * changed.  Errors: MOE_ERR_INVALID_ARG (null or misaligned pointer, range outside
+ * 0..E), MOE_ERR_WORKSPACE (packed_bytes too small), MOE_ERR_HIP. */
 moe_status moe_pack_experts(const moe_config* cfg, const moe_expert_src* src, int32_t e0,
                             int32_t n, void* packed, size_t packed_bytes, moe_stream_t stream);
 
@@ -136,18 +162,21 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t max_tokens, size_t*
 
 /* Offsets (bytes) of the intermediates inside the workspace of a call with n_tokens,
  * for inspection after moe_layer_forward (host call).  Layouts, all row-major:
- *   [0] x^c    [T][l]   fp32     latent down-projection
- *   [1] h_s    [T][m_s] fp32     shared SiTU-GLU hidden
- *   [2] h      [T*k][m] fp32     routed expert hidden, rows in dispatch order
- *   [3] E      [T*k][l] fp32     routed expert outputs, rows in dispatch order
- *   [4] u      [T][l]   fp32     gated latent sum before the norm
- *   [5] perm   [T*k]    int32    dispatch order -> assignment t*k+j
- *   [6] inv    [T*k]    int32    assignment -> dispatch order
- *   [7] counts [E]      int32    assignments per expert
- *   [8] offsets[E+1]    int32    exclusive scan of counts
- *   [9] z      [T][E]   fp32     router logits
- *  [10] per-chunk expert histograms of the dispatch (internal) */
-#define MOE_WS_NUM_SLOTS 11
+ *   [0] control words (internal: [0] = number of units of the expert launches)
+ *   [1] x^c    [T][l]   fp32     latent down-projection
+ *   [2] h_s    [T][m_s] fp32     shared SiTU-GLU hidden
+ *   [3] h      [T*k][m] fp32     routed expert hidden, rows in dispatch order
+ *   [4] E      [T*k][l] fp32     routed expert outputs, rows in dispatch order
+ *   [5] u      [T][l]   fp32     gated latent sum before the norm
+ *   [6] perm   [T*k]    int32    dispatch order -> assignment t*k+j
+ *   [7] inv    [T*k]    int32    assignment -> dispatch order
+ *   [8] counts [E]      int32    assignments per expert
+ *   [9] offsets[E+1]    int32    exclusive scan of counts
+ *  [10] z      [P][T][E] fp32   router logits as P partial planes over ranges of d (their
+ *                                sum); after the route, plane 0 holds the logits
+ *  [11] per-chunk expert histograms of the dispatch (internal)
+ *  [12] unit table of the expert launches (internal) */
+#define MOE_WS_NUM_SLOTS 13
 moe_status moe_workspace_layout(const moe_config* cfg, int64_t n_tokens,
                                 size_t offsets[MOE_WS_NUM_SLOTS]);
 
@@ -167,14 +196,15 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const 
 
 /* Steps of the forward, in launch order. */
 typedef enum moe_step {
-  MOE_STEP_ROUTER = 0,      /* router logits z = x W_r */
-  MOE_STEP_DENSE_X = 1,     /* x^c = x W_down_latent and shared gate/up + SiTU; with at most
-                               4 tokens one workgroup of the same launch also takes the
-                               top-k, the gate weights and the dispatch */
-  MOE_STEP_ROUTE = 2,       /* sigmoid, top_k(s + b), gate weights (more than 4 tokens;
-                               launches nothing otherwise) */
-  MOE_STEP_DISPATCH = 3,    /* histogram, scan, stable permutation by expert (more than 4
-                               tokens; launches nothing otherwise) */
+  MOE_STEP_ROUTER = 0,      /* router logits z = x W_r (partial planes) */
+  MOE_STEP_IN = 1,          /* x^c = x W_down_latent, shared gate/up + SiTU; with few tokens
+                               (at most 4, fewer for very wide d) one workgroup of the same
+                               launch also takes the top-k, the gate weights and the
+                               dispatch */
+  MOE_STEP_ROUTE = 2,       /* sigmoid, top_k(s + b), gate weights (larger batches; launches
+                               nothing otherwise) */
+  MOE_STEP_DISPATCH = 3,    /* histogram, scan, stable permutation by expert (larger
+                               batches; launches nothing otherwise) */
   MOE_STEP_EXPERT_GU = 4,   /* routed gate/up + SiTU */
   MOE_STEP_EXPERT_DOWN = 5, /* routed down */
   MOE_STEP_COMBINE = 6,     /* u = sum_j G_j E_j */
@@ -210,7 +240,7 @@ moe_status moe_layer_forward_steps(const moe_config* cfg, const moe_weights* w,
 /* The router step alone (block card: z = x W_r, s = sigmoid(z), top_k(s + b), and G;
  * toy chapter: the bias selects, the raw score weights).  Same arguments and output
  * layout as the corresponding ones of moe_layer_forward; the logits are left in the
- * workspace slot [9]. */
+ * workspace slot [10]. */
 moe_status moe_route(const moe_config* cfg, const moe_weights* w, const float* bias,
                      const void* x, int64_t n_tokens, int32_t* topk_idx, float* topk_w,
                      void* workspace, size_t workspace_bytes, moe_stream_t stream);
@@ -219,8 +249,9 @@ moe_status moe_route(const moe_config* cfg, const moe_weights* w, const float* b
  * assignments ordered by expert).  From topk_idx [T, k] it writes counts [E], offsets
  * [E+1] (exclusive scan, offsets[E] = T*k), perm [T*k] (dispatch order -> assignment
  * t*k+j; within an expert, assignments in increasing t*k+j) and inv [T*k] (the inverse).
- * workspace: at least moe_workspace_size(cfg, n_tokens) bytes.  Every index in topk_idx
- * must lie in 0..E-1; this is not checked. */
+ * workspace: at least moe_workspace_size(cfg, n_tokens) bytes (its unit table and unit
+ * count are rewritten too).  Every index in topk_idx must lie in 0..E-1; this is not
+ * checked. */
 moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int64_t n_tokens,
                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
                         void* workspace, size_t workspace_bytes, moe_stream_t stream);

@@ -17,12 +17,15 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 ACT = {"situ": 0, "swiglu": 1}
 WFMT = {"bf16": 0, "mxfp4": 1}
-WS_SLOTS = ("xc", "hs", "h", "eo", "u", "perm", "inv", "counts", "offsets", "z", "chunk_hist")
+WS_SLOTS = ("ctrl", "xc", "hs", "h", "eo", "u", "perm", "inv", "counts", "offsets", "z",
+            "chunk_hist", "units")
 
-EXPORTS = ("moe_abi_version", "moe_status_str", "moe_packed_experts_size", "moe_pack_experts",
-           "moe_workspace_size", "moe_workspace_layout", "moe_layer_forward",
+EXPORTS = ("moe_abi_version", "moe_status_str", "moe_packed_dense_size", "moe_pack_dense",
+           "moe_packed_experts_size", "moe_pack_experts", "moe_workspace_size",
+           "moe_workspace_layout", "moe_layer_forward",
            "moe_layer_forward_timed", "moe_layer_forward_steps", "moe_route", "moe_dispatch")
-STEPS = ("router", "dense_x", "route", "dispatch", "expert_gu", "expert_down", "combine", "out")
+STEPS = ("router", "in", "route", "dispatch", "expert_gu", "expert_down", "combine", "out")
+ABI_VERSION = 2
 
 
 class MoeConfig(ctypes.Structure):
@@ -36,9 +39,12 @@ class MoeConfig(ctypes.Structure):
 
 
 class MoeWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("dense", "experts")]
+
+
+class MoeDenseSrc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("router", "w_down_latent", "w_up_latent",
-                                                "norm_gamma", "shared_gu", "shared_down",
-                                                "experts")]
+                                                "norm_gamma", "shared_gu", "shared_down")]
 
 
 class MoeExpertSrc(ctypes.Structure):
@@ -72,6 +78,8 @@ def lib():
     L.moe_abi_version.restype = ctypes.c_int
     L.moe_status_str.restype = ctypes.c_char_p
     L.moe_status_str.argtypes = [ctypes.c_int]
+    L.moe_packed_dense_size.argtypes = [P(MoeConfig), P(sz)]
+    L.moe_pack_dense.argtypes = [P(MoeConfig), P(MoeDenseSrc), vp, sz, vp]
     L.moe_packed_experts_size.argtypes = [P(MoeConfig), P(sz)]
     L.moe_pack_experts.argtypes = [P(MoeConfig), P(MoeExpertSrc), ctypes.c_int32, ctypes.c_int32,
                                    vp, sz, vp]
@@ -86,6 +94,9 @@ def lib():
     L.moe_dispatch.argtypes = [P(MoeConfig), vp, i64, vp, vp, vp, vp, vp, sz, vp]
     for f in EXPORTS[2:]:
         getattr(L, f).restype = ctypes.c_int
+    if L.moe_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI {L.moe_abi_version()}, the binding expects "
+                           f"{ABI_VERSION}: rebuild it")
     _lib = L
     return L
 
@@ -124,6 +135,18 @@ def workspace_layout(cfg: MoeConfig, n_tokens: int) -> dict:
     return dict(zip(WS_SLOTS, list(off)))
 
 
+def packed_dense_size(cfg: MoeConfig) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().moe_packed_dense_size(ctypes.byref(cfg), ctypes.byref(n)), "moe_packed_dense_size")
+    return n.value
+
+
+def new_workspace(cfg: MoeConfig, max_tokens: int, device):
+    """A device workspace for up to max_tokens tokens."""
+    import torch
+    return torch.empty(max(workspace_size(cfg, max_tokens), 256), dtype=torch.uint8, device=device)
+
+
 def packed_experts_size(cfg: MoeConfig) -> int:
     n = ctypes.c_size_t()
     _check(lib().moe_packed_experts_size(ctypes.byref(cfg), ctypes.byref(n)),
@@ -151,39 +174,47 @@ def _dev_u8(a, device):
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
-class Layer:
-    """One layer resident on the device: canonical bf16 dense weights, fp32 bias and the
-    routed experts packed by moe_pack_experts.  Tensors are torch device tensors."""
+def pack_dense(cfg: MoeConfig, dense, device="cuda"):
+    """Upload canonical dense weights (numpy, bf16 patterns) and pack them on the device."""
+    import torch
+    t = [_dev_u16(getattr(dense, n), device) if getattr(dense, n) is not None else None
+         for n in ("router", "w_down_latent", "w_up_latent", "norm_gamma", "shared_gu",
+                   "shared_down")]
+    packed = torch.empty(packed_dense_size(cfg), dtype=torch.uint8, device=device)
+    stream = torch.cuda.current_stream(device)
+    src = MoeDenseSrc(*[_ptr(v) for v in t])
+    _check(lib().moe_pack_dense(ctypes.byref(cfg), ctypes.byref(src), packed.data_ptr(),
+                                packed.numel(), stream.cuda_stream), "moe_pack_dense")
+    stream.synchronize()   # the canonical staging tensors are released on return
+    return packed
 
-    def __init__(self, cfg: MoeConfig, router, w_down_latent, w_up_latent, norm_gamma,
-                 shared_gu, shared_down, bias, experts):
+
+class Layer:
+    """One layer resident on the device: the packed dense weights (moe_pack_dense), the
+    fp32 bias and the routed experts packed by moe_pack_experts (torch device tensors)."""
+
+    def __init__(self, cfg: MoeConfig, dense, bias, experts):
         self.cfg = cfg
-        self.router, self.w_down_latent, self.w_up_latent = router, w_down_latent, w_up_latent
-        self.norm_gamma, self.shared_gu, self.shared_down = norm_gamma, shared_gu, shared_down
-        self.bias, self.experts = bias, experts
+        self.dense, self.bias, self.experts = dense, bias, experts
         self._ws = None
 
     @property
     def device(self):
-        return self.router.device
+        return self.dense.device
 
     def weights_struct(self) -> MoeWeights:
-        return MoeWeights(_ptr(self.router), _ptr(self.w_down_latent), _ptr(self.w_up_latent),
-                          _ptr(self.norm_gamma), _ptr(self.shared_gu), _ptr(self.shared_down),
-                          _ptr(self.experts))
+        return MoeWeights(_ptr(self.dense), _ptr(self.experts))
 
     def with_dense(self, dense, device=None) -> "Layer":
         """The same packed experts with another set of dense weights (numpy canonical)."""
         device = self.device if device is None else device
-        return Layer(self.cfg, _dev_u16(dense.router, device), _dev_u16(dense.w_down_latent, device),
-                     _dev_u16(dense.w_up_latent, device), _dev_u16(dense.norm_gamma, device),
-                     _dev_u16(dense.shared_gu, device), _dev_u16(dense.shared_down, device),
-                     self.bias, self.experts)
+        return Layer(self.cfg, pack_dense(self.cfg, dense, device), self.bias, self.experts)
 
     @classmethod
     def upload(cls, cfg: MoeConfig, dense, expert_slice, n_experts: int, device="cuda",
                chunk: int = 64) -> "Layer":
-        """Upload canonical numpy arrays and pack the experts on the device.
+        """Upload canonical numpy arrays and pack the dense weights and the experts on the
+        device.
 
         dense: object with router, w_down_latent, w_up_latent, norm_gamma, shared_gu,
         shared_down (uint16 bf16 patterns) and bias (float32).  expert_slice(e0, e1) returns
@@ -205,16 +236,12 @@ class Layer:
                    "moe_pack_experts")
             stream.synchronize()   # staging tensors are released at the next iteration
         bias = torch.from_numpy(np.ascontiguousarray(dense.bias, dtype=np.float32)).to(device)
-        return cls(cfg, _dev_u16(dense.router, device), _dev_u16(dense.w_down_latent, device),
-                   _dev_u16(dense.w_up_latent, device), _dev_u16(dense.norm_gamma, device),
-                   _dev_u16(dense.shared_gu, device), _dev_u16(dense.shared_down, device),
-                   bias, experts)
+        return cls(cfg, pack_dense(cfg, dense, device), bias, experts)
 
     def workspace(self, n_tokens: int):
-        import torch
         need = workspace_size(self.cfg, n_tokens)
         if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+            self._ws = new_workspace(self.cfg, n_tokens, self.device)
         return self._ws
 
     def forward(self, x, delta=None, idx=None, w=None, workspace=None, stream=None):
@@ -293,13 +320,13 @@ class Layer:
         ws = self.workspace(n_tokens) if workspace is None else workspace
         off = workspace_layout(c, n_tokens)
         T, k = n_tokens, c.top_k
-        shapes = {"xc": (T, c.d_latent), "hs": (T, c.d_shared), "h": (T * k, c.d_expert),
-                  "eo": (T * k, c.d_latent), "u": (T, c.d_latent), "perm": (T * k,),
-                  "inv": (T * k,), "counts": (c.n_experts,), "offsets": (c.n_experts + 1,),
-                  "z": (T, c.n_experts)}
+        shapes = {"ctrl": (64,), "xc": (T, c.d_latent), "hs": (T, c.d_shared),
+                  "h": (T * k, c.d_expert), "eo": (T * k, c.d_latent), "u": (T, c.d_latent),
+                  "perm": (T * k,), "inv": (T * k,), "counts": (c.n_experts,),
+                  "offsets": (c.n_experts + 1,), "z": (T, c.n_experts)}
         out = {}
         for name, shp in shapes.items():
             n = int(np.prod(shp))
-            dt = torch.int32 if name in ("perm", "inv", "counts", "offsets") else torch.float32
+            dt = torch.int32 if name in ("ctrl", "perm", "inv", "counts", "offsets") else torch.float32
             out[name] = ws[off[name]: off[name] + 4 * n].view(dt).view(shp)
         return out

@@ -47,18 +47,29 @@ moe_status make_shape(const moe_config* c, Shape* s) {
   s->beta_lin = c->beta_lin;
   s->act = c->act;
   s->wfmt = c->expert_wfmt;
-  s->j_gu = (int)cdiv64(s->l / 8, moe::kWave);
-  s->j_dn = (int)cdiv64(s->m / 8, moe::kWave);
-  size_t gu, dn;
-  if (s->wfmt == MOE_WFMT_MXFP4) {
-    gu = (size_t)(s->m / 2) * s->j_gu * moe::kFp4StepBytes;
-    dn = (size_t)(s->l / 4) * s->j_dn * moe::kFp4StepBytes;
-  } else {
-    gu = (size_t)2 * s->m * s->l * 2;
-    dn = (size_t)s->l * s->m * 2;
-  }
-  s->gu_bytes = gu;
-  s->expert_bytes = align256(gu + dn);
+  // packed dense weights
+  s->ks_in = moe::cdiv(s->d, moe::kStepK);
+  s->tr_r = moe::cdiv(s->E, moe::kTileRows);
+  s->tr_dn = moe::cdiv(s->l, moe::kTileRows);
+  s->tr_sh = moe::cdiv(s->ms, moe::kTileRows / 2);
+  s->tr_in = s->tr_r + s->tr_dn + s->tr_sh;
+  s->zplanes = moe::clampi(s->ks_in / 7, 1, 8);
+  s->ks_l = moe::cdiv(s->l, moe::kStepK);
+  s->ks_ms = moe::cdiv(s->ms, moe::kStepK);
+  s->ks_out = s->ks_l + s->ks_ms;
+  s->tr_out = moe::cdiv(s->d, moe::kTileRows);
+  s->in_bytes = (size_t)s->tr_in * s->ks_in * moe::kBf16StepBytes;
+  s->out_bytes = (size_t)s->tr_out * s->ks_out * moe::kBf16StepBytes;
+  s->gamma_off = s->in_bytes + s->out_bytes;
+  s->dense_bytes = align256(s->gamma_off + (size_t)s->l * 2);
+  // packed experts
+  s->ks_gu = moe::cdiv(s->l, moe::kStepK);
+  s->tr_gu = moe::cdiv(s->m, moe::kTileRows / 2);
+  s->ks_edn = moe::cdiv(s->m, moe::kStepK);
+  s->tr_edn = moe::cdiv(s->l, moe::kTileRows);
+  s->step_bytes = s->wfmt == MOE_WFMT_MXFP4 ? moe::kFp4StepBytes : moe::kBf16StepBytes;
+  s->gu_bytes = (size_t)s->tr_gu * s->ks_gu * s->step_bytes;
+  s->expert_bytes = align256(s->gu_bytes + (size_t)s->tr_edn * s->ks_edn * s->step_bytes);
   return MOE_OK;
 }
 
@@ -67,17 +78,19 @@ void layout(const Shape& s, int64_t T, size_t off[MOE_WS_NUM_SLOTS], size_t* tot
   const int64_t tk = T * s.k;
   const int64_t nch = cdiv64(T, moe::dispatch_chunk_tokens(s.k));
   const size_t sz[MOE_WS_NUM_SLOTS] = {
-      (size_t)T * s.l * 4,        // x^c
-      (size_t)T * s.ms * 4,       // h_s
-      (size_t)tk * s.m * 4,       // h
-      (size_t)tk * s.l * 4,       // E
-      (size_t)T * s.l * 4,        // u
-      (size_t)tk * 4,             // perm
-      (size_t)tk * 4,             // inv
-      (size_t)s.E * 4,            // counts
-      (size_t)(s.E + 1) * 4,      // offsets
-      (size_t)T * s.E * 4,        // z
-      (size_t)nch * s.E * 4,      // chunk histograms
+      (size_t)moe::kCtrlWords * 4,          // control words (unit count)
+      (size_t)T * s.l * 4,                  // x^c
+      (size_t)T * s.ms * 4,                 // h_s
+      (size_t)tk * s.m * 4,                 // h
+      (size_t)tk * s.l * 4,                 // E
+      (size_t)T * s.l * 4,                  // u
+      (size_t)tk * 4,                       // perm
+      (size_t)tk * 4,                       // inv
+      (size_t)s.E * 4,                      // counts
+      (size_t)(s.E + 1) * 4,                // offsets
+      (size_t)s.zplanes * T * s.E * 4,      // z (partial planes)
+      (size_t)nch * s.E * 4,                // chunk histograms
+      (size_t)moe::max_units(s, T) * 16,    // unit table
   };
   size_t o = 0;
   for (int i = 0; i < MOE_WS_NUM_SLOTS; ++i) {
@@ -90,43 +103,26 @@ void layout(const Shape& s, int64_t T, size_t off[MOE_WS_NUM_SLOTS], size_t* tot
 moe::Work make_work(void* ws, const size_t off[MOE_WS_NUM_SLOTS]) {
   char* b = static_cast<char*>(ws);
   moe::Work w;
-  w.xc = reinterpret_cast<float*>(b + off[0]);
-  w.hs = reinterpret_cast<float*>(b + off[1]);
-  w.h = reinterpret_cast<float*>(b + off[2]);
-  w.eo = reinterpret_cast<float*>(b + off[3]);
-  w.u = reinterpret_cast<float*>(b + off[4]);
-  w.perm = reinterpret_cast<int32_t*>(b + off[5]);
-  w.inv = reinterpret_cast<int32_t*>(b + off[6]);
-  w.counts = reinterpret_cast<int32_t*>(b + off[7]);
-  w.offs = reinterpret_cast<int32_t*>(b + off[8]);
-  w.z = reinterpret_cast<float*>(b + off[9]);
-  w.chunk_hist = reinterpret_cast<int32_t*>(b + off[10]);
+  w.ctrl = reinterpret_cast<int32_t*>(b + off[0]);
+  w.xc = reinterpret_cast<float*>(b + off[1]);
+  w.hs = reinterpret_cast<float*>(b + off[2]);
+  w.h = reinterpret_cast<float*>(b + off[3]);
+  w.eo = reinterpret_cast<float*>(b + off[4]);
+  w.u = reinterpret_cast<float*>(b + off[5]);
+  w.perm = reinterpret_cast<int32_t*>(b + off[6]);
+  w.inv = reinterpret_cast<int32_t*>(b + off[7]);
+  w.counts = reinterpret_cast<int32_t*>(b + off[8]);
+  w.offs = reinterpret_cast<int32_t*>(b + off[9]);
+  w.z = reinterpret_cast<float*>(b + off[10]);
+  w.chunk_hist = reinterpret_cast<int32_t*>(b + off[11]);
+  w.units = reinterpret_cast<int32_t*>(b + off[12]);
   return w;
 }
 
-moe_status check_dense(const Shape& s, const moe_weights* w, bool router_only) {
-  if (!w || !w->router || !aligned(w->router, 16)) return MOE_ERR_INVALID_ARG;
-  if (router_only) return MOE_OK;
-  if (!w->w_down_latent || !w->w_up_latent || !w->experts) return MOE_ERR_INVALID_ARG;
-  if (!aligned(w->w_down_latent, 16) || !aligned(w->w_up_latent, 16) || !aligned(w->experts, 16))
-    return MOE_ERR_INVALID_ARG;
-  if (s.use_norm && (!w->norm_gamma || !aligned(w->norm_gamma, 16))) return MOE_ERR_INVALID_ARG;
-  if (s.ms > 0 && (!w->shared_gu || !w->shared_down || !aligned(w->shared_gu, 16) ||
-                   !aligned(w->shared_down, 16)))
+moe_status check_weights(const moe_weights* w) {
+  if (!w || !w->dense || !w->experts || !aligned(w->dense, 256) || !aligned(w->experts, 256))
     return MOE_ERR_INVALID_ARG;
   return MOE_OK;
-}
-
-moe::DenseW dense_of(const moe_weights* w) {
-  moe::DenseW d;
-  d.router = static_cast<const uint16_t*>(w->router);
-  d.wdn = static_cast<const uint16_t*>(w->w_down_latent);
-  d.wup = static_cast<const uint16_t*>(w->w_up_latent);
-  d.gamma = static_cast<const uint16_t*>(w->norm_gamma);
-  d.sgu = static_cast<const uint16_t*>(w->shared_gu);
-  d.sdn = static_cast<const uint16_t*>(w->shared_down);
-  d.experts = static_cast<const uint8_t*>(w->experts);
-  return d;
 }
 
 inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
@@ -146,6 +142,39 @@ MOE_EXPORT const char* moe_status_str(moe_status s) {
   return "MOE_ERR_UNKNOWN";
 }
 
+MOE_EXPORT moe_status moe_packed_dense_size(const moe_config* cfg, size_t* bytes) {
+  Shape s;
+  moe_status st = make_shape(cfg, &s);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = s.dense_bytes;
+  return MOE_OK;
+}
+
+MOE_EXPORT moe_status moe_pack_dense(const moe_config* cfg, const moe_dense_src* src, void* packed,
+                                     size_t packed_bytes, moe_stream_t stream) {
+  Shape s;
+  moe_status st = make_shape(cfg, &s);
+  if (st != MOE_OK) return st;
+  if (!src || !packed || !src->router || !src->w_down_latent || !src->w_up_latent ||
+      !src->norm_gamma || !aligned(packed, 256))
+    return MOE_ERR_INVALID_ARG;
+  if (s.ms > 0 && (!src->shared_gu || !src->shared_down)) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[6] = {src->router, src->w_down_latent, src->w_up_latent, src->norm_gamma,
+                         src->shared_gu, src->shared_down};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 16)) return MOE_ERR_INVALID_ARG;
+  if (packed_bytes < s.dense_bytes) return MOE_ERR_WORKSPACE;
+  moe::DenseSrc d;
+  d.router = static_cast<const uint16_t*>(src->router);
+  d.wdn = static_cast<const uint16_t*>(src->w_down_latent);
+  d.wup = static_cast<const uint16_t*>(src->w_up_latent);
+  d.gamma = static_cast<const uint16_t*>(src->norm_gamma);
+  d.sgu = static_cast<const uint16_t*>(src->shared_gu);
+  d.sdn = static_cast<const uint16_t*>(src->shared_down);
+  return hip_status(moe::launch_pack_dense(s, d, static_cast<uint8_t*>(packed), (hipStream_t)stream));
+}
+
 MOE_EXPORT moe_status moe_packed_experts_size(const moe_config* cfg, size_t* bytes) {
   Shape s;
   moe_status st = make_shape(cfg, &s);
@@ -161,15 +190,18 @@ MOE_EXPORT moe_status moe_pack_experts(const moe_config* cfg, const moe_expert_s
   Shape s;
   moe_status st = make_shape(cfg, &s);
   if (st != MOE_OK) return st;
-  if (!src || !packed || !src->gu || !src->down || !aligned(packed, 16)) return MOE_ERR_INVALID_ARG;
+  if (!src || !packed || !src->gu || !src->down || !aligned(packed, 256)) return MOE_ERR_INVALID_ARG;
   if (s.wfmt == MOE_WFMT_MXFP4 &&
       (!src->gu_scale || !src->down_scale || !aligned(src->gu, 4) || !aligned(src->down, 4)))
+    return MOE_ERR_INVALID_ARG;
+  if (s.wfmt == MOE_WFMT_BF16 && (!aligned(src->gu, 16) || !aligned(src->down, 16)))
     return MOE_ERR_INVALID_ARG;
   if (e0 < 0 || n < 0 || (int64_t)e0 + n > s.E) return MOE_ERR_INVALID_ARG;
   if (packed_bytes < s.expert_bytes * (size_t)s.E) return MOE_ERR_WORKSPACE;
   if (n == 0) return MOE_OK;
-  return hip_status(moe::launch_pack(s, src->gu, src->gu_scale, src->down, src->down_scale, e0, n,
-                                     static_cast<uint8_t*>(packed), (hipStream_t)stream));
+  return hip_status(moe::launch_pack_experts(s, src->gu, src->gu_scale, src->down, src->down_scale,
+                                             e0, n, static_cast<uint8_t*>(packed),
+                                             (hipStream_t)stream));
 }
 
 MOE_EXPORT moe_status moe_workspace_size(const moe_config* cfg, int64_t max_tokens, size_t* bytes) {
@@ -195,6 +227,19 @@ MOE_EXPORT moe_status moe_workspace_layout(const moe_config* cfg, int64_t n_toke
 
 namespace {
 
+moe_status check_call(const Shape& s, const moe_weights* w, const float* bias, const void* x,
+                      int64_t n_tokens, void* workspace, size_t workspace_bytes,
+                      size_t off[MOE_WS_NUM_SLOTS]) {
+  moe_status st;
+  if ((st = check_weights(w)) != MOE_OK) return st;
+  if (!bias || !x || !workspace) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(workspace, 256) || !aligned(bias, 4)) return MOE_ERR_INVALID_ARG;
+  size_t need;
+  layout(s, n_tokens, off, &need);
+  if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
 moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const float* bias,
                         const void* x, int64_t n_tokens, float* delta, int32_t* topk_idx,
                         float* topk_w, void* workspace, size_t workspace_bytes,
@@ -205,27 +250,24 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const float
   if (n_tokens < 0) return MOE_ERR_INVALID_ARG;
   if (step_begin < 0 || step_end > MOE_NUM_STEPS || step_begin > step_end) return MOE_ERR_INVALID_ARG;
   if (n_tokens == 0) return MOE_OK;  // nothing to read or write: buffers may be empty (null)
-  if ((st = check_dense(s, w, false)) != MOE_OK) return st;
-  if (!bias || !x || !delta || !topk_idx || !topk_w || !workspace) return MOE_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(delta, 16) || !aligned(workspace, 256) || !aligned(bias, 4) ||
-      !aligned(topk_idx, 4) || !aligned(topk_w, 4))
-    return MOE_ERR_INVALID_ARG;
-  size_t off[MOE_WS_NUM_SLOTS], need;
-  layout(s, n_tokens, off, &need);
-  if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  size_t off[MOE_WS_NUM_SLOTS];
+  if ((st = check_call(s, w, bias, x, n_tokens, workspace, workspace_bytes, off)) != MOE_OK) return st;
+  if (!delta || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned(delta, 16) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_ERR_INVALID_ARG;
   const moe::Work ws = make_work(workspace, off);
-  const moe::DenseW dw = dense_of(w);
+  const uint8_t* dense = static_cast<const uint8_t*>(w->dense);
+  const uint8_t* experts = static_cast<const uint8_t*>(w->experts);
   hipStream_t hs = (hipStream_t)stream;
   const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const bool fused = moe::route_fused(s, n_tokens);
   for (int step = step_begin; step < step_end; ++step) {
     if (events && events[step] && hipEventRecord((hipEvent_t)events[step], hs) != hipSuccess)
       return MOE_ERR_HIP;
     hipError_t e = hipSuccess;
-    const bool fused = moe::route_fused(n_tokens, s.k);
     switch (step) {
-      case MOE_STEP_ROUTER: e = moe::launch_router(s, dw, xb, n_tokens, ws, hs); break;
-      case MOE_STEP_DENSE_X:
-        e = moe::launch_dense_x(s, dw, xb, n_tokens, bias, topk_idx, topk_w, ws, hs);
+      case MOE_STEP_ROUTER: e = moe::launch_router(s, dense, xb, n_tokens, ws, hs); break;
+      case MOE_STEP_IN:
+        e = moe::launch_in(s, dense, xb, n_tokens, bias, topk_idx, topk_w, ws, hs);
         break;
       case MOE_STEP_ROUTE:
         if (!fused) e = moe::launch_route(s, bias, n_tokens, ws, topk_idx, topk_w, hs);
@@ -233,12 +275,12 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const float
       case MOE_STEP_DISPATCH:
         if (!fused)
           e = moe::launch_dispatch(s, topk_idx, n_tokens, ws.counts, ws.offs, ws.perm, ws.inv,
-                                   ws.chunk_hist, hs);
+                                   ws.chunk_hist, ws.units, ws.ctrl, hs);
         break;
-      case MOE_STEP_EXPERT_GU: e = moe::launch_expert_gu(s, dw, topk_idx, n_tokens, ws, hs); break;
-      case MOE_STEP_EXPERT_DOWN: e = moe::launch_expert_down(s, dw, topk_idx, n_tokens, ws, hs); break;
+      case MOE_STEP_EXPERT_GU: e = moe::launch_expert(s, experts, true, n_tokens, ws, hs); break;
+      case MOE_STEP_EXPERT_DOWN: e = moe::launch_expert(s, experts, false, n_tokens, ws, hs); break;
       case MOE_STEP_COMBINE: e = moe::launch_combine(s, topk_w, n_tokens, ws, hs); break;
-      case MOE_STEP_OUT: e = moe::launch_out(s, dw, n_tokens, ws, delta, hs); break;
+      case MOE_STEP_OUT: e = moe::launch_out(s, dense, n_tokens, ws, delta, hs); break;
     }
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
@@ -287,16 +329,13 @@ MOE_EXPORT moe_status moe_route(const moe_config* cfg, const moe_weights* w, con
   if (st != MOE_OK) return st;
   if (n_tokens < 0) return MOE_ERR_INVALID_ARG;
   if (n_tokens == 0) return MOE_OK;
-  if ((st = check_dense(s, w, true)) != MOE_OK) return st;
-  if (!bias || !x || !topk_idx || !topk_w || !workspace) return MOE_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARG;
-  size_t off[MOE_WS_NUM_SLOTS], need;
-  layout(s, n_tokens, off, &need);
-  if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  size_t off[MOE_WS_NUM_SLOTS];
+  if ((st = check_call(s, w, bias, x, n_tokens, workspace, workspace_bytes, off)) != MOE_OK) return st;
+  if (!topk_idx || !topk_w || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_ERR_INVALID_ARG;
   const moe::Work ws = make_work(workspace, off);
-  const moe::DenseW dw = dense_of(w);
   hipStream_t hs = (hipStream_t)stream;
-  if (moe::launch_router(s, dw, static_cast<const uint16_t*>(x), n_tokens, ws, hs) != hipSuccess)
+  if (moe::launch_router(s, static_cast<const uint8_t*>(w->dense), static_cast<const uint16_t*>(x),
+                         n_tokens, ws, hs) != hipSuccess)
     return MOE_ERR_HIP;
   return hip_status(moe::launch_route(s, bias, n_tokens, ws, topk_idx, topk_w, hs));
 }
@@ -316,5 +355,5 @@ MOE_EXPORT moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_id
   if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
   const moe::Work ws = make_work(workspace, off);
   return hip_status(moe::launch_dispatch(s, topk_idx, n_tokens, counts, offsets, perm, inv,
-                                         ws.chunk_hist, (hipStream_t)stream));
+                                         ws.chunk_hist, ws.units, ws.ctrl, (hipStream_t)stream));
 }

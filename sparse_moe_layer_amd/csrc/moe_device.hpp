@@ -11,6 +11,8 @@ namespace moe {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -22,6 +24,33 @@ __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) {
 // a.lo*b.lo + a.hi*b.hi + c with bf16 pairs, fp32 accumulate (exact bf16 products).
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(b), c, false);
+}
+
+// Two floats rounded to bf16 (round to nearest even) in one 32-bit word, a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t v;
+  v.x = (__bf16)a;
+  v.y = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// D += A B for one 16x16x32 bf16 block (fp32 accumulation); A rows and B columns are
+// held as 8 consecutive K values per lane (lane l: row / column l % 16, K 8 (l / 16)..).
+__device__ __forceinline__ f32x4_t mfma_bf16(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Eight E2M1 codes (one 32-bit word, low nibble first) times the E8M0 scale, as bf16.
+// E2M1 x 2^(e-127) is exact in bf16 for every code and every scale byte 1..254 whose
+// product stays below the bf16 maximum.
+__device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t codes, float scale) {
+  const bf16x2_t b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+  const bf16x2_t b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+  const bf16x2_t b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+  const bf16x2_t b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+  return make_uint4(__builtin_bit_cast(uint32_t, b0), __builtin_bit_cast(uint32_t, b1),
+                    __builtin_bit_cast(uint32_t, b2), __builtin_bit_cast(uint32_t, b3));
 }
 
 // Streaming (non-temporal) loads for weights that are read once per call.

@@ -8,11 +8,14 @@
 namespace moe {
 
 constexpr int kWave = 64;
+constexpr int kBlock = 256;             // 4 wavefronts per workgroup
+constexpr int kTileRows = 16;           // weight rows per packed tile (MFMA 16x16x32)
+constexpr int kStepK = 128;             // input columns per K-step
+constexpr int kBf16StepBytes = 4096;    // bf16 K-step: 4 sub-tiles of 16 rows x 32 columns
+constexpr int kFp4StepBytes = 1024 + 64;  // MXFP4 K-step: 16 rows x 128 codes + 16 x 4 scales
+constexpr int kCtrlWords = 64;          // control words at the head of the workspace
 
-// One MXFP4 "row group" step: 64 lanes x 16 bytes of codes (four rows' 8-column chunks
-// per lane) followed by 16 x 4 bytes of E8M0 scales (four rows' scale of the 32-column
-// block that each quad of lanes covers).
-constexpr int kFp4StepBytes = 1024 + 64;
+__host__ __device__ inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 // Shape of one layer plus everything derived from it that the launches need.
 struct Shape {
@@ -20,15 +23,23 @@ struct Shape {
   int use_norm;
   float eps, route_scale, beta_gate, beta_lin;
   int act;    // 0 SiTU, 1 SwiGLU
-  int wfmt;   // 0 bf16, 1 MXFP4
-  // MXFP4 packing: steps (of 64 lanes x 8 columns) per row group of the two matrices
-  int j_gu, j_dn;
+  int wfmt;   // 0 bf16, 1 MXFP4 (routed experts)
+  // packed dense weights: IN = [router ; W_down_latent ; shared gate/up] over K = d,
+  // OUT = [W_up_latent | W_shared_down] over K = l (padded) + m_s
+  int ks_in, tr_r, tr_dn, tr_sh, tr_in;
+  int zplanes;   // router K-ranges computed apart (partial logit planes summed by the route)
+  int ks_l, ks_ms, ks_out, tr_out;
+  size_t in_bytes, out_bytes, gamma_off, dense_bytes;
+  // packed experts: gate/up tiles (8 gate + 8 up rows) over K = l, then down tiles over K = m
+  int ks_gu, tr_gu, ks_edn, tr_edn;
+  int step_bytes;       // bytes of one expert K-step (MXFP4 or bf16)
   size_t gu_bytes;      // packed gate/up bytes of one expert
   size_t expert_bytes;  // packed bytes of one expert (256-byte multiple)
 };
 
 // Row-major views of the workspace of one forward call.
 struct Work {
+  int32_t* ctrl;   // [kCtrlWords]: [0] unit count (written by the route or the dispatch)
   float* xc;       // [T][l]
   float* hs;       // [T][ms]
   float* h;        // [T*k][m]   dispatch order
@@ -38,45 +49,63 @@ struct Work {
   int32_t* inv;    // [T*k]
   int32_t* counts; // [E]
   int32_t* offs;   // [E+1]
-  float* z;        // [T][E]
+  float* z;        // [zplanes][T][E] partial logits; plane 0 holds the logits after the route
   int32_t* chunk_hist;  // [n_chunks][E]
+  int32_t* units;  // [max_units][4]: expert, first position, positions, 0
 };
 
-struct DenseW {
+// Tokens per dispatch chunk (so that a chunk holds at most 256 assignments).
+inline int dispatch_chunk_tokens(int k) { return k >= 256 ? 1 : 256 / k; }
+
+inline int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+// Tokens per workgroup of the IN launches (bf16 rows of d columns in LDS, next to the
+// route's own LDS) and of the OUT launch (hi/lo rows of l + m_s columns).
+inline int in_tokens_per_block(const Shape& s) { return clampi(45056 / (s.ks_in * kStepK * 2), 1, 16); }
+inline int out_tokens_per_block(const Shape& s) { return clampi(57344 / (s.ks_out * kStepK * 4), 1, 8); }
+// Positions of one expert per unit of the expert launches (2 hi/lo rows each).
+inline int unit_positions(const Shape& s, int64_t T) {
+  const int ks = s.ks_gu > s.ks_edn ? s.ks_gu : s.ks_edn;
+  const int fit = clampi(57344 / (ks * kStepK * 4), 1, 4);
+  return (int)(T < fit ? (T < 1 ? 1 : T) : fit);
+}
+inline int64_t max_units(const Shape& s, int64_t T) {
+  const int64_t n = T * s.k, nu = unit_positions(s, T);
+  const int64_t b = n / nu + (n < s.E ? n : s.E);
+  return b < n ? b : n;
+}
+// With this few tokens the route and the dispatch run inside the IN launch.
+inline bool route_fused(const Shape& s, int64_t T) {
+  return T <= 4 && T * s.k <= kBlock && T <= in_tokens_per_block(s);
+}
+
+hipError_t launch_router(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,
+                         const Work& ws, hipStream_t st);
+hipError_t launch_in(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,
+                     const float* bias, int32_t* idx, float* gw, const Work& ws, hipStream_t st);
+hipError_t launch_route(const Shape& s, const float* bias, int64_t T, const Work& ws,
+                        int32_t* idx, float* gw, hipStream_t st);
+hipError_t launch_dispatch(const Shape& s, const int32_t* idx, int64_t T, int32_t* counts,
+                           int32_t* offs, int32_t* perm, int32_t* inv, int32_t* chunk_hist,
+                           int32_t* units, int32_t* ctrl, hipStream_t st);
+hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_t T,
+                         const Work& ws, hipStream_t st);
+hipError_t launch_combine(const Shape& s, const float* gw, int64_t T, const Work& ws,
+                          hipStream_t st);
+hipError_t launch_out(const Shape& s, const uint8_t* dense, int64_t T, const Work& ws,
+                      float* delta, hipStream_t st);
+
+// Packing.  Dense: canonical bf16 [rows][K] into the tiles of the IN or OUT matrix.
+struct DenseSrc {
   const uint16_t* router;
   const uint16_t* wdn;
   const uint16_t* wup;
   const uint16_t* gamma;
   const uint16_t* sgu;
   const uint16_t* sdn;
-  const uint8_t* experts;
 };
-
-// Tokens per dispatch chunk (so that a chunk holds at most 256 assignments).
-inline int dispatch_chunk_tokens(int k) { return k >= 256 ? 1 : 256 / k; }
-
-hipError_t launch_router(const Shape& s, const DenseW& w, const uint16_t* x, int64_t T,
-                         const Work& ws, hipStream_t st);
-// latent down + shared gate/up; for route_fused batches also the route and the dispatch
-hipError_t launch_dense_x(const Shape& s, const DenseW& w, const uint16_t* x, int64_t T,
-                          const float* bias, int32_t* idx, float* gw, const Work& ws,
-                          hipStream_t st);
-// The route step in its own launch (no dispatch).
-bool route_fused(int64_t T, int k);
-hipError_t launch_route(const Shape& s, const float* bias, int64_t T, const Work& ws,
-                        int32_t* idx, float* gw, hipStream_t st);
-hipError_t launch_dispatch(const Shape& s, const int32_t* idx, int64_t T, int32_t* counts,
-                           int32_t* offs, int32_t* perm, int32_t* inv, int32_t* chunk_hist,
-                           hipStream_t st);
-hipError_t launch_expert_gu(const Shape& s, const DenseW& w, const int32_t* idx, int64_t T,
-                            const Work& ws, hipStream_t st);
-hipError_t launch_expert_down(const Shape& s, const DenseW& w, const int32_t* idx, int64_t T,
-                              const Work& ws, hipStream_t st);
-hipError_t launch_combine(const Shape& s, const float* gw, int64_t T, const Work& ws,
-                          hipStream_t st);
-hipError_t launch_out(const Shape& s, const DenseW& w, int64_t T, const Work& ws, float* delta,
-                      hipStream_t st);
-hipError_t launch_pack(const Shape& s, const void* gu, const void* gus, const void* dn,
-                       const void* dns, int e0, int n, uint8_t* packed, hipStream_t st);
+hipError_t launch_pack_dense(const Shape& s, const DenseSrc& src, uint8_t* packed,
+                             hipStream_t st);
+hipError_t launch_pack_experts(const Shape& s, const void* gu, const void* gus, const void* dn,
+                               const void* dns, int e0, int n, uint8_t* packed, hipStream_t st);
 
 }  // namespace moe

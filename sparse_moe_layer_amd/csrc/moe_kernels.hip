@@ -2,22 +2,23 @@
 //
 // Step order follows the Kimi K3 latent mixture-of-experts block card ("All 23 steps"
 // and its KimiSparseMoeBlock.forward / moe_infer excerpt):
-//   k_router       router logits z = x W_r
-//   k_dense_x      x^c = x W_down_latent and the shared gate/up with its SiTU epilogue;
-//                  for a few tokens its workgroup 0 meanwhile takes s = sigmoid(z), the
-//                  top_k of s + b, G = s / sum(s) and sorts the assignments by expert
-//   k_route        the same selection in its own launch for larger batches
-//   k_disp_*       per-expert histogram -> scan -> stable permutation for larger batches
-//                  (moe_infer's scatter_/argsort, kept on the device: no host round trip)
-//   k_expert_*     routed gate/up (+ SiTU) and down, MXFP4 or bf16 weights
-//   k_combine      u = sum_j G_j E_j in a fixed order (no atomics)
-//   k_out          RMSNorm(u) W_up_latent + h_s W_shared_down -> Delta, one product over
-//                  the concatenated row [W_up_latent[r] | W_shared_down[r]]
+//   k_in          router logits z = x W_r, latent down x^c = x W_down_latent and the
+//                 shared gate/up with its SiTU epilogue, one launch over one packed
+//                 matrix; for a few tokens its last router workgroup also takes
+//                 s = sigmoid(z), the top_k of s + b, G = s / sum(s) and sorts the
+//                 assignments by expert
+//   k_route       the same selection in its own launch for larger batches
+//   k_disp_*      per-expert histogram -> scan -> stable permutation for larger batches
+//                 (moe_infer's scatter_/argsort, kept on the device: no host round trip)
+//   k_exp         routed gate/up (+ SiTU) and down, MXFP4 or bf16 weights
+//   k_combine     u = sum_j G_j E_j in a fixed order (no atomics)
+//   k_out         RMSNorm(u) W_up_latent + h_s W_shared_down -> Delta, one product over
+//                 the packed [W_up_latent | W_shared_down] matrix
 //
-// The weight products are matrix-vector streams: every weight byte is read once per token
-// through 16-byte non-temporal loads (64 lanes x 16 B = 1 KiB per load instruction), two
-// rows (or row groups) in flight per wavefront, so decode is bound by HBM bandwidth.
-// Activations stay fp32 end to end; the bf16 tokens meet bf16 weights in v_dot2_f32_bf16.
+// The weight products run on the matrix cores (v_mfma_f32_16x16x32_bf16) with the
+// weights streamed once from HBM as the B operand and the activations staged in LDS as
+// the A operand; decode is bound by HBM bandwidth.  Activations are fp32 between the
+// steps; where they meet the matrix cores they are carried as exact bf16 hi/lo pairs.
 #include <climits>
 #include <cmath>
 
@@ -27,90 +28,7 @@
 namespace moe {
 namespace {
 
-constexpr int kBlock = 256;  // 4 wavefronts per workgroup
 constexpr int kWavesPerBlock = kBlock / kWave;
-
-__device__ __forceinline__ int64_t global_wave() {
-  return (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-}
-
-// ------------------------------------------------------------------------------------
-// Row products.  Lane l covers the 8-column chunks l, l+64, l+128, ... of a row; the
-// per-lane sum runs in chunk order and the DPP reduction finishes it (fixed order).
-// ------------------------------------------------------------------------------------
-
-template <int NCH>
-__device__ __forceinline__ void load_row(const uint16_t* row, int k8, int lane, uint4 (&w)[NCH]) {
-  const uint4* r = reinterpret_cast<const uint4*>(row);
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int c = j * kWave + lane;
-    w[j] = (c < k8) ? ld_stream(r + c) : make_uint4(0u, 0u, 0u, 0u);
-  }
-}
-
-// bf16 weights x bf16 activations (packed pairs).
-template <int NCH>
-__device__ __forceinline__ float dot_bb(const uint4 (&w)[NCH], const uint4 (&x)[NCH]) {
-  float acc = 0.f;
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    acc = dot2_bf16(w[j].x, x[j].x, acc);
-    acc = dot2_bf16(w[j].y, x[j].y, acc);
-    acc = dot2_bf16(w[j].z, x[j].z, acc);
-    acc = dot2_bf16(w[j].w, x[j].w, acc);
-  }
-  return acc;
-}
-
-// bf16 weights x fp32 activations held in registers.
-template <int NCH>
-__device__ __forceinline__ float dot_bf(const uint4 (&w)[NCH], const float (&xs)[NCH][8]) {
-  float acc = 0.f;
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const uint32_t q[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc = fmaf(bf16_lo(q[i]), xs[j][2 * i], acc);
-      acc = fmaf(bf16_hi(q[i]), xs[j][2 * i + 1], acc);
-    }
-  }
-  return acc;
-}
-
-template <int NCH>
-__device__ __forceinline__ void load_x_f32(const float* xr, int k8, int lane, float (&xs)[NCH][8]) {
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int c = j * kWave + lane;
-    if (c < k8) {
-      const float4 a = reinterpret_cast<const float4*>(xr)[2 * c];
-      const float4 b = reinterpret_cast<const float4*>(xr)[2 * c + 1];
-      xs[j][0] = a.x; xs[j][1] = a.y; xs[j][2] = a.z; xs[j][3] = a.w;
-      xs[j][4] = b.x; xs[j][5] = b.y; xs[j][6] = b.z; xs[j][7] = b.w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xs[j][i] = 0.f;
-    }
-  }
-}
-
-// An fp32 activation row staged in LDS as two planes: plane 0 holds columns 8c..8c+3 and
-// plane 1 columns 8c+4..8c+7 of chunk c, so that a wavefront reading chunk j*64+lane
-// reads 64 consecutive 16-byte words from each plane (no bank conflicts).
-__device__ __forceinline__ void stage_x(const float* xr, int k8, int n_chunks, float4* p0, float4* p1) {
-  const float4* x4 = reinterpret_cast<const float4*>(xr);
-  for (int c = threadIdx.x; c < n_chunks; c += kBlock) {
-    if (c < k8) {
-      p0[c] = x4[2 * c];
-      p1[c] = x4[2 * c + 1];
-    } else {
-      p0[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-      p1[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
-}
 
 // ------------------------------------------------------------------------------------
 // Step ROUTE: one workgroup (4 wavefronts) per token.  Expert e = (4i + w)*64 + lane
@@ -119,10 +37,13 @@ __device__ __forceinline__ void stage_x(const float* xr, int k8, int n_chunks, f
 // ~e in the low word: larger kappa first, then the lower index); the 4k candidates are
 // then ranked in LDS.  G = route_scale * s / sum(s), the sum in selection order.
 // For at most 4 tokens one workgroup handles all of them and then sorts the T*k
-// assignments by expert (histogram, scan, stable rank) in LDS.
+// assignments by expert (histogram, scan, stable rank) in LDS and writes the unit table
+// of the expert launches.
 // ------------------------------------------------------------------------------------
 struct RouteArgs {
-  const float* z;
+  float* z;         // zplanes partial planes [zplanes][T][E]; the route leaves their sum in plane 0
+  int zplanes;
+  int64_t zplane;   // floats between planes
   const float* bias;
   int64_t T;
   int E, k;
@@ -133,6 +54,9 @@ struct RouteArgs {
   int32_t* offs;
   int32_t* perm;
   int32_t* inv;
+  int32_t* units;   // unit table of the expert launches (dispatch only)
+  int32_t* ctrl;    // ctrl[0] <- number of units (dispatch only)
+  int nu;           // positions per unit
 };
 
 constexpr int kRouteSlots = 4;      // E <= 4 slots x 4 wavefronts x 64 lanes = 1024
@@ -145,12 +69,22 @@ __device__ __forceinline__ void block_route_token(const RouteArgs& a, int64_t t,
   const int wv = threadIdx.x >> 6;
   uint64_t key[kRouteSlots];
   float sv[kRouteSlots];
-  const float* zr = a.z + t * a.E;
+  float* zr = a.z + t * a.E;
+  float zv[kRouteSlots];
+#pragma unroll
+  for (int i = 0; i < kRouteSlots; ++i) {
+    const int e = (i * kWavesPerBlock + wv) * kWave + lane;
+    float v = 0.f;
+    if (e < a.E)
+      for (int p = 0; p < a.zplanes; ++p) v += zr[p * a.zplane + e];
+    zv[i] = v;
+  }
 #pragma unroll
   for (int i = 0; i < kRouteSlots; ++i) {
     const int e = (i * kWavesPerBlock + wv) * kWave + lane;
     if (e < a.E) {
-      const float s = sigmoidf_(zr[e]);
+      if (a.zplanes > 1) zr[e] = zv[i];   // the logits themselves, for inspection
+      const float s = sigmoidf_(zv[i]);
       float kk = s + a.bias[e];
       if (kk != kk) kk = -INFINITY;
       sv[i] = s;
@@ -228,6 +162,7 @@ __device__ void route_block(const RouteArgs& a, int64_t t_begin, int64_t t_end, 
   __shared__ int hist[1024];
   __shared__ int soff[1024];
   __shared__ int part[kBlock];
+  __shared__ int upart[kBlock];
   for (int64_t t = t_begin; t < t_end; ++t)
     block_route_token(a, t, cand_key, cand_s, sel_e, sel_s, dispatch ? sidx : nullptr);
   if (!dispatch) return;
@@ -238,23 +173,28 @@ __device__ void route_block(const RouteArgs& a, int64_t t_begin, int64_t t_end, 
   __syncthreads();
   if (tid < n) atomicAdd(&hist[sidx[tid]], 1);
   __syncthreads();
-  // exclusive scan over experts: 4 consecutive experts per thread, then across threads
-  int loc[4], ps = 0;
+  // exclusive scans over experts (4 consecutive experts per thread, then across threads)
+  // of the counts and of the units (runs of at most nu positions of one expert)
+  int loc[4], ps = 0, pu = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = tid * 4 + i;
     loc[i] = (e < a.E) ? hist[e] : 0;
     ps += loc[i];
+    pu += (loc[i] + a.nu - 1) / a.nu;
   }
   part[tid] = ps;
+  upart[tid] = pu;
   __syncthreads();
   for (int o = 1; o < kBlock; o <<= 1) {
     const int v = (tid >= o) ? part[tid - o] : 0;
+    const int w = (tid >= o) ? upart[tid - o] : 0;
     __syncthreads();
     part[tid] += v;
+    upart[tid] += w;
     __syncthreads();
   }
-  int run = part[tid] - ps;
+  int run = part[tid] - ps, urun = upart[tid] - pu;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = tid * 4 + i;
@@ -262,10 +202,13 @@ __device__ void route_block(const RouteArgs& a, int64_t t_begin, int64_t t_end, 
       soff[e] = run;
       a.offs[e] = run;
       a.counts[e] = loc[i];
+      for (int r0 = 0; r0 < loc[i]; r0 += a.nu, ++urun)
+        *reinterpret_cast<int4*>(a.units + 4 * urun) = make_int4(e, run + r0, min(a.nu, loc[i] - r0), 0);
     }
     run += loc[i];
   }
   if (tid == 0) a.offs[a.E] = n;
+  if (tid == kBlock - 1) a.ctrl[0] = upart[tid];
   __syncthreads();
   if (tid < n) {
     const int e = sidx[tid];
@@ -282,106 +225,12 @@ __global__ __launch_bounds__(kBlock) void k_route(RouteArgs a) {
   route_block(a, blockIdx.x, blockIdx.x + 1, false);
 }
 
-// ------------------------------------------------------------------------------------
-// Step DENSE_X: router logits, latent down-projection, shared gate/up + activation.
-// The token slice stays in registers; rows go two at a time.
-// ------------------------------------------------------------------------------------
-struct DenseXArgs {
-  const uint16_t* x;
-  int64_t T;
-  int d;
-  const uint16_t* wr;
-  int E;
-  float* z;
-  const uint16_t* wdn;
-  int l;
-  float* xc;
-  const uint16_t* sgu;
-  int ms;
-  float* hs;
-  int act;
-  float bg, bl;
-  int rows_per_wave;     // router / latent rows per wavefront (even)
-  int pairs_per_wave;    // shared gate/up row pairs per wavefront
-  int waves_r, waves_dn, waves_sh;  // per token
-  int route;             // 1: workgroup 0 routes and dispatches the (<= 4) tokens
-  RouteArgs ra;
-};
-
-template <int NCH>
-__device__ __forceinline__ void rows_x2(const uint16_t* w, int d, int r0, int r1,
-                                        const uint4 (&xv)[NCH], int d8, int lane, float* out) {
-  for (int r = r0; r < r1; r += 2) {
-    const int rb = min(r + 1, r1 - 1);
-    uint4 wa[NCH], wb[NCH];
-    load_row<NCH>(w + (int64_t)r * d, d8, lane, wa);
-    load_row<NCH>(w + (int64_t)rb * d, d8, lane, wb);
-    const float a = wave_sum(dot_bb<NCH>(wa, xv));
-    const float b = wave_sum(dot_bb<NCH>(wb, xv));
-    if (lane == 0) {
-      out[r] = a;
-      if (rb != r) out[rb] = b;
-    }
-  }
-}
-
-template <int NCH>
-__device__ __forceinline__ void dense_x_body(const DenseXArgs& a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  if (a.route) {
-    // the router logits come from the previous launch; this workgroup's selection runs
-    // while the others stream the latent and shared weights
-    if (blockIdx.x == 0) {
-      route_block(a.ra, 0, a.T, true);
-      return;
-    }
-  }
-  const int64_t gw = global_wave() - (a.route ? kWavesPerBlock : 0);
-  const int per_tok = a.waves_r + a.waves_dn + a.waves_sh;
-  const int64_t t = gw / per_tok;
-  if (t >= a.T) return;
-  int w = (int)(gw - t * per_tok);
-  const int d8 = a.d >> 3;
-  const uint4* xr = reinterpret_cast<const uint4*>(a.x + t * (int64_t)a.d);
-  uint4 xv[NCH];
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int c = j * kWave + lane;
-    xv[j] = (c < d8) ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
-  }
-  if (w < a.waves_r) {
-    const int r0 = w * a.rows_per_wave, r1 = min(a.E, r0 + a.rows_per_wave);
-    rows_x2<NCH>(a.wr, a.d, r0, r1, xv, d8, lane, a.z + t * a.E);
-    return;
-  }
-  w -= a.waves_r;
-  if (w < a.waves_dn) {
-    const int r0 = w * a.rows_per_wave, r1 = min(a.l, r0 + a.rows_per_wave);
-    rows_x2<NCH>(a.wdn, a.d, r0, r1, xv, d8, lane, a.xc + t * a.l);
-    return;
-  }
-  w -= a.waves_dn;
-  const int r0 = w * a.pairs_per_wave, r1 = min(a.ms, r0 + a.pairs_per_wave);
-  for (int r = r0; r < r1; ++r) {
-    uint4 wg[NCH], wu[NCH];
-    load_row<NCH>(a.sgu + (int64_t)r * a.d, d8, lane, wg);
-    load_row<NCH>(a.sgu + (int64_t)(a.ms + r) * a.d, d8, lane, wu);
-    const float g = wave_sum(dot_bb<NCH>(wg, xv));
-    const float u = wave_sum(dot_bb<NCH>(wu, xv));
-    if (lane == 0) a.hs[t * a.ms + r] = glu_act(g, u, a.act, a.bg, a.bl);
-  }
-}
-
-// Two entry points over the same body so that profilers tell the launches apart.
-template <int NCH>
-__global__ __launch_bounds__(kBlock) void k_router(DenseXArgs a) { dense_x_body<NCH>(a); }
-template <int NCH>
-__global__ __launch_bounds__(kBlock) void k_dense_x(DenseXArgs a) { dense_x_body<NCH>(a); }
 
 // ------------------------------------------------------------------------------------
 // Step DISPATCH for larger batches: deterministic counting sort by expert.
 //   count:   per-chunk histograms (integer LDS atomics: exact counts)
-//   scan:    per-expert prefix over chunks, then the exclusive scan over experts
+//   scan:    per-expert prefix over chunks, then the exclusive scan over experts and
+//            the unit table of the expert launches (runs of at most nu positions)
 //   scatter: position = offsets[e] + chunk prefix + rank among the chunk's earlier
 //            assignments of the same expert (stable: increasing t*k+j)
 // ------------------------------------------------------------------------------------
@@ -397,9 +246,12 @@ __global__ __launch_bounds__(kBlock) void k_disp_count(const int32_t* idx, int64
   for (int e = threadIdx.x; e < E; e += kBlock) chunk_hist[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
-__global__ __launch_bounds__(1024) void k_disp_scan(int n_chunks, int E, int32_t* chunk_hist,
-                                                    int32_t* counts, int32_t* offs) {
+__global__ __launch_bounds__(1024) void k_disp_scan(int n_chunks, int E, int nu,
+                                                    int32_t* chunk_hist, int32_t* counts,
+                                                    int32_t* offs, int32_t* units,
+                                                    int32_t* ctrl) {
   __shared__ int sc[1024];
+  __shared__ int su[1024];
   const int e = threadIdx.x;
   int tot = 0;
   if (e < E) {
@@ -410,16 +262,27 @@ __global__ __launch_bounds__(1024) void k_disp_scan(int n_chunks, int E, int32_t
     }
     counts[e] = tot;
   }
+  const int nue = (e < E) ? (tot + nu - 1) / nu : 0;
   sc[e] = (e < E) ? tot : 0;
+  su[e] = nue;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {
     const int v = (e >= o) ? sc[e - o] : 0;
+    const int w = (e >= o) ? su[e - o] : 0;
     __syncthreads();
     sc[e] += v;
+    su[e] += w;
     __syncthreads();
   }
-  if (e < E) offs[e] = sc[e] - tot;
+  if (e < E) {
+    const int off = sc[e] - tot;
+    offs[e] = off;
+    int ub = su[e] - nue;
+    for (int r0 = 0; r0 < tot; r0 += nu, ++ub)
+      *reinterpret_cast<int4*>(units + 4 * ub) = make_int4(e, off + r0, min(nu, tot - r0), 0);
+  }
   if (e == 0) offs[E] = sc[1023];
+  if (e == 1023) ctrl[0] = su[1023];
 }
 
 __global__ __launch_bounds__(kBlock) void k_disp_scatter(const int32_t* idx, int64_t n, int E,
@@ -442,144 +305,6 @@ __global__ __launch_bounds__(kBlock) void k_disp_scatter(const int32_t* idx, int
   }
 }
 
-// ------------------------------------------------------------------------------------
-// Routed experts.  A workgroup serves one dispatch position p and a run of row groups;
-// its input row (x^c of the assignment's token for gate/up, h of position p for down)
-// is staged once in LDS.
-// ------------------------------------------------------------------------------------
-struct ExpArgs {
-  const uint8_t* experts;
-  size_t expert_bytes, region_off;
-  const int32_t* idx;
-  const int32_t* perm;
-  int64_t n_assign;
-  int k;
-  const float* xin;
-  int kin;           // input row length
-  int in_by_token;   // 1: input row = token of the assignment; 0: input row = position
-  float* out;
-  int n_out;         // output row length
-  int n_units;       // row groups (MXFP4) or rows / row pairs (bf16)
-  int units_per_wave;
-  int wgs_per_pos;   // workgroups per position (MXFP4) / waves per position (bf16)
-  int m;             // gate rows of the bf16 gate/up matrix
-  int act;
-  float bg, bl;
-};
-
-// MXFP4 row groups: 4 rows, J steps of (64 lanes x 16 code bytes + 16 x 4 scale bytes).
-template <int J>
-__device__ __forceinline__ void load_fp4_group(const uint8_t* gp, int lane, uint4 (&cw)[J],
-                                               uint32_t (&sw)[J]) {
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    cw[j] = ld_stream(gp + j * kFp4StepBytes + lane * 16);
-    sw[j] = ld_stream32(gp + j * kFp4StepBytes + 1024 + (lane >> 2) * 4);
-  }
-}
-
-template <int J>
-__device__ __forceinline__ void fma_fp4_step(uint4 cw, uint32_t sw, float4 xa, float4 xb,
-                                             float (&acc)[4]) {
-  const uint32_t cq[4] = {cw.x, cw.y, cw.z, cw.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float sc = e8m0_as_f32((sw >> (8 * q)) & 0xFFu);
-    const float2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cq[q], sc, 0);
-    const float2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cq[q], sc, 1);
-    const float2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cq[q], sc, 2);
-    const float2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cq[q], sc, 3);
-    float s = acc[q];
-    s = fmaf(v0.x, xa.x, s);
-    s = fmaf(v0.y, xa.y, s);
-    s = fmaf(v1.x, xa.z, s);
-    s = fmaf(v1.y, xa.w, s);
-    s = fmaf(v2.x, xb.x, s);
-    s = fmaf(v2.y, xb.y, s);
-    s = fmaf(v3.x, xb.z, s);
-    s = fmaf(v3.y, xb.w, s);
-    acc[q] = s;
-  }
-}
-
-template <int J, bool GU>
-__global__ __launch_bounds__(kBlock) void k_expert_fp4(ExpArgs a) {
-  __shared__ float4 xp0[J * kWave], xp1[J * kWave];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x >> 6;
-  const int64_t pos = blockIdx.x / a.wgs_per_pos;
-  if (pos >= a.n_assign) return;
-  const int wg = (int)(blockIdx.x - pos * a.wgs_per_pos);
-  const int asg = a.perm[pos];
-  const int e = a.idx[asg];
-  const int64_t xrow = a.in_by_token ? (int64_t)(asg / a.k) : pos;
-  const uint8_t* base = a.experts + (size_t)e * a.expert_bytes + a.region_off;
-  const int g0 = (wg * kWavesPerBlock + wv) * a.units_per_wave;
-  const int g1 = min(a.n_units, g0 + a.units_per_wave);
-  float* orow = a.out + pos * a.n_out;
-  stage_x(a.xin + xrow * a.kin, a.kin >> 3, J * kWave, xp0, xp1);
-  __syncthreads();
-  for (int g = g0; g < g1; ++g) {
-    // keep the LDS reads inside the loop (see k_out)
-    asm volatile("" ::: "memory");
-    uint4 cw[J];
-    uint32_t sw[J];
-    load_fp4_group<J>(base + (size_t)g * J * kFp4StepBytes, lane, cw, sw);
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < J; ++j)
-      fma_fp4_step<J>(cw[j], sw[j], xp0[j * kWave + lane], xp1[j * kWave + lane], acc);
-    float r[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) r[q] = wave_sum(acc[q]);
-    if (lane == 0) {
-      if (GU) {
-        // row group g: gate rows 2g, 2g+1 and up rows 2g, 2g+1
-        orow[2 * g] = glu_act(r[0], r[2], a.act, a.bg, a.bl);
-        orow[2 * g + 1] = glu_act(r[1], r[3], a.act, a.bg, a.bl);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) orow[4 * g + q] = r[q];
-      }
-    }
-  }
-}
-
-// bf16 experts in canonical row order: gate/up [2m][kin] (unit = row pair i, m+i) and
-// down [n_out][kin] (unit = row); the input row stays in registers.
-template <int NCH, bool GU>
-__global__ __launch_bounds__(kBlock) void k_expert_bf16(ExpArgs a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t gw = global_wave();
-  const int64_t pos = gw / a.wgs_per_pos;
-  if (pos >= a.n_assign) return;
-  const int chunk = (int)(gw - pos * a.wgs_per_pos);
-  const int asg = a.perm[pos];
-  const int e = a.idx[asg];
-  const int64_t xrow = a.in_by_token ? (int64_t)(asg / a.k) : pos;
-  const int k8 = a.kin >> 3;
-  float xs[NCH][8];
-  load_x_f32<NCH>(a.xin + xrow * a.kin, k8, lane, xs);
-  const uint16_t* base =
-      reinterpret_cast<const uint16_t*>(a.experts + (size_t)e * a.expert_bytes + a.region_off);
-  const int u0 = chunk * a.units_per_wave, u1 = min(a.n_units, u0 + a.units_per_wave);
-  float* orow = a.out + pos * a.n_out;
-  for (int r = u0; r < u1; ++r) {
-    if (GU) {
-      uint4 wg[NCH], wu[NCH];
-      load_row<NCH>(base + (int64_t)r * a.kin, k8, lane, wg);
-      load_row<NCH>(base + (int64_t)(a.m + r) * a.kin, k8, lane, wu);
-      const float g = wave_sum(dot_bf<NCH>(wg, xs));
-      const float u = wave_sum(dot_bf<NCH>(wu, xs));
-      if (lane == 0) orow[r] = glu_act(g, u, a.act, a.bg, a.bl);
-    } else {
-      uint4 wr[NCH];
-      load_row<NCH>(base + (int64_t)r * a.kin, k8, lane, wr);
-      const float v = wave_sum(dot_bf<NCH>(wr, xs));
-      if (lane == 0) orow[r] = v;
-    }
-  }
-}
 
 // ------------------------------------------------------------------------------------
 // Step COMBINE: u[t] = sum_j G[t,j] E[inv[t,j]], j = 0..k-1 in order.
@@ -612,273 +337,656 @@ __global__ __launch_bounds__(kBlock) void k_combine(const float* __restrict__ gw
   u[t * l + r] = acc;
 }
 
-// ------------------------------------------------------------------------------------
-// Step OUT: Delta[t, r] = [W_up_latent[r] | W_shared_down[r]] . [u_hat_t ; h_s,t], with
-// u_hat = u / sqrt(mean(u^2) + eps) * gamma computed once per workgroup.  The activation
-// row [u_hat ; h_s] (l + m_s fp32) sits in LDS in the two-plane layout.
-// ------------------------------------------------------------------------------------
-struct OutArgs {
-  const uint16_t* wup;   // [d][l]
-  const uint16_t* sdn;   // [d][ms] (ms may be 0)
-  const uint16_t* gamma;
-  int d, l, ms;
-  int norm;
-  float eps;
-  const float* u;        // [T][l]
-  const float* hs;       // [T][ms]
-  int64_t T;
-  float* delta;          // [T][d]
-  int rows_per_wave;
-  int wgs_per_tok;
-};
 
-// Row r of [W_up_latent | W_shared_down]: chunk c < l/8 from W_up_latent, then W_shared_down.
-template <int NCH>
-__device__ __forceinline__ void load_cat_row(const OutArgs& a, int r, int l8, int k8, int lane,
-                                             uint4 (&w)[NCH]) {
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int c = j * kWave + lane;
-    if (c < l8) w[j] = ld_stream(a.wup + (int64_t)r * a.l + 8 * c);
-    else if (c < k8) w[j] = ld_stream(a.sdn + (int64_t)r * a.ms + 8 * (c - l8));
-    else w[j] = make_uint4(0u, 0u, 0u, 0u);
+// ------------------------------------------------------------------------------------
+// Weight streaming on the matrix cores.
+//
+// Every weight matrix is packed (moe_pack_dense / moe_pack_experts) into tile rows of 16
+// output rows; a tile row is a run of K-steps of 128 input columns.  In a bf16 K-step,
+// sub-tile s (1 KiB) holds columns 32s..32s+31 with lane l's 16 bytes = row l % 16,
+// columns 32s + 8 (l / 16) .. +8: exactly the B operand of v_mfma_f32_16x16x32_bf16, so
+// one wavefront load brings 1 KiB of contiguous bytes and feeds one MFMA.  An MXFP4
+// K-step is 1 KiB of codes (lane l: row l % 16, word s = columns 32s + 8 (l / 16) .. +8)
+// plus the 16 rows' four scale bytes; the codes become bf16 operands through
+// v_cvt_scalef32_pk_bf16_fp4, which is exact.
+//
+// The activations form the A operand: up to 16 rows staged once per workgroup in LDS.
+// bf16 tokens are rows as they are; fp32 activations are split into a bf16 pair
+// hi = bf16(v), lo = bf16(v - hi) in rows 2i, 2i + 1, so that hi + lo carries 16
+// significant bits and both MFMA products are exact: D = A W^T then holds fp32-accurate
+// dot products (row 2i + row 2i+1 of D).  D row r of the 16x16 block depends on A row r
+// alone, so lanes beyond the staged rows read a duplicate row and are ignored.
+//
+// LDS layout of the staged rows: the 16-byte word (q, s, g, r) at ((q*4 + s)*4 + g)*nr + r
+// holds row r, columns 128q + 32s + 8g .. +8 (nr = rows staged).
+// ------------------------------------------------------------------------------------
+
+// Tokens x (bf16, row stride ld) rows r0..r0+nr-1 into LDS; columns >= n are zero.
+__device__ __forceinline__ void stage_bf16(uint4* sm, const uint16_t* x, int64_t ld, int nr,
+                                           int n, int ks) {
+  const int per_row = ks * 16;
+  for (int idx = threadIdx.x; idx < nr * per_row; idx += kBlock) {
+    const int r = idx / per_row, j = idx - r * per_row;
+    const int col = 8 * j;
+    const uint4 v = (col < n) ? *reinterpret_cast<const uint4*>(x + r * ld + col)
+                              : make_uint4(0u, 0u, 0u, 0u);
+    sm[j * nr + r] = v;  // j = (q*4 + s)*4 + g
   }
 }
 
-template <int NCH>
-__global__ __launch_bounds__(kBlock) void k_out(OutArgs a) {
-  __shared__ float4 xp0[NCH * kWave], xp1[NCH * kWave];
-  __shared__ float red[kWavesPerBlock];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x >> 6;
-  const int64_t t = blockIdx.x / a.wgs_per_tok;
-  if (t >= a.T) return;
-  const int wg = (int)(blockIdx.x - t * a.wgs_per_tok);
-  const int l8 = a.l >> 3, s8 = a.ms >> 3, k8 = l8 + s8;
-  const int r0 = (wg * kWavesPerBlock + wv) * a.rows_per_wave;
-  const int r1 = min(a.d, r0 + a.rows_per_wave);
-  // stage u (then scale it) and h_s
-  stage_x(a.u + t * a.l, l8, l8, xp0, xp1);
-  if (s8 > 0) stage_x(a.hs + t * a.ms, s8, NCH * kWave - l8, xp0 + l8, xp1 + l8);
-  else
-    for (int c = l8 + threadIdx.x; c < NCH * kWave; c += kBlock) {
-      xp0[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-      xp1[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  __syncthreads();
-  if (a.norm) {
-    float ss = 0.f;
-    for (int c = threadIdx.x; c < l8; c += kBlock) {
-      const float4 p = xp0[c], q = xp1[c];
-      ss = fmaf(p.x, p.x, ss); ss = fmaf(p.y, p.y, ss); ss = fmaf(p.z, p.z, ss); ss = fmaf(p.w, p.w, ss);
-      ss = fmaf(q.x, q.x, ss); ss = fmaf(q.y, q.y, ss); ss = fmaf(q.z, q.z, ss); ss = fmaf(q.w, q.w, ss);
-    }
-    ss = wave_sum(ss);
-    if (lane == 0) red[wv] = ss;
-    __syncthreads();
-    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
-    const float inv = 1.0f / sqrtf(tot / (float)a.l + a.eps);
-    const uint4* g4 = reinterpret_cast<const uint4*>(a.gamma);
-    for (int c = threadIdx.x; c < l8; c += kBlock) {
-      const uint4 g = g4[c];
-      float4 p = xp0[c], q = xp1[c];
-      p.x = p.x * inv * bf16_lo(g.x); p.y = p.y * inv * bf16_hi(g.x);
-      p.z = p.z * inv * bf16_lo(g.y); p.w = p.w * inv * bf16_hi(g.y);
-      q.x = q.x * inv * bf16_lo(g.z); q.y = q.y * inv * bf16_hi(g.z);
-      q.z = q.z * inv * bf16_lo(g.w); q.w = q.w * inv * bf16_hi(g.w);
-      xp0[c] = p;
-      xp1[c] = q;
-    }
-    __syncthreads();
+// Eight fp32 values into the hi and lo bf16 words.
+__device__ __forceinline__ void split_hilo(const float (&v)[8], uint4& hi, uint4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    const float h0 = bf16_lo(h[i]), h1 = bf16_hi(h[i]);
+    l[i] = pack_bf16x2(v[2 * i] - h0, v[2 * i + 1] - h1);
   }
-  for (int r = r0; r < r1; ++r) {
-    // keep the LDS reads inside the loop: hoisting them would hold the whole row of
-    // activations in registers and drop the occupancy to one wavefront per SIMD
-    asm volatile("" ::: "memory");
-    uint4 wa[NCH];
-    load_cat_row<NCH>(a, r, l8, k8, lane, wa);
-    float sa = 0.f;
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// An fp32 activation row for the hi/lo staging: columns [0, n0) from p0 (optionally
+// times scale * gamma[c]), columns [c1, c1 + n1) from p1, zero elsewhere.
+struct HiloRow {
+  const float* p0;
+  const float* p1;
+  float scale;
+};
+
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// nt fp32 rows (rows[i], resolved by the caller into the per-row pointers) as 2*nt hi/lo
+// rows; gamma (bf16, may be null) multiplies segment 0 with the row's scale.
+__device__ __forceinline__ void stage_hilo(uint4* sm, const HiloRow* rows, int nt, int n0,
+                                           int c1, int n1, const uint16_t* gamma, int ks) {
+  const int per_row = ks * 16;
+  const int nr = 2 * nt;
+  for (int idx = threadIdx.x; idx < nt * per_row; idx += kBlock) {
+    const int i = idx / per_row, j = idx - i * per_row;
+    const int col = 8 * j;
+    float v[8];
+    if (col < n0) {
+      load8(rows[i].p0 + col, v);
+      if (gamma) {
+        const uint4 g = *reinterpret_cast<const uint4*>(gamma + col);
+        const float s = rows[i].scale;
+        v[0] = v[0] * s * bf16_lo(g.x); v[1] = v[1] * s * bf16_hi(g.x);
+        v[2] = v[2] * s * bf16_lo(g.y); v[3] = v[3] * s * bf16_hi(g.y);
+        v[4] = v[4] * s * bf16_lo(g.z); v[5] = v[5] * s * bf16_hi(g.z);
+        v[6] = v[6] * s * bf16_lo(g.w); v[7] = v[7] * s * bf16_hi(g.w);
+      }
+    } else if (col >= c1 && col < c1 + n1) {
+      load8(rows[i].p1 + (col - c1), v);
+    } else {
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const float4 p = xp0[j * kWave + lane], q = xp1[j * kWave + lane];
-      const float xv[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
-      const uint32_t ua[4] = {wa[j].x, wa[j].y, wa[j].z, wa[j].w};
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+    uint4 hi, lo;
+    split_hilo(v, hi, lo);
+    sm[j * nr + 2 * i] = hi;
+    sm[j * nr + 2 * i + 1] = lo;
+  }
+}
+
+// One tile row over K-steps [q0, q0 + n): D += A W^T on the 16 x 16 block (A = staged
+// rows, W = the tile row's 16 weight rows).  WF: 0 bf16 K-steps, 1 MXFP4 K-steps.  P
+// K-steps of weights are in flight per wavefront.  `abase` is the lane's LDS word offset
+// g*nr + (row of this lane), `nr` the staged rows.  N > 0: n == N at compile time, the
+// loop fully unrolled, so every load is unconditional and the waits count exactly the
+// loads in flight; N == 0: any n, with the loads past the end clamped to the last
+// K-step (re-reads that are never used).
+template <int WF>
+struct WeightStep {
+  static constexpr int SB = WF ? kFp4StepBytes : kBf16StepBytes;
+  static constexpr int NW = WF ? 1 : 4;
+  uint4 w[NW];
+  uint32_t sc;
+  __device__ __forceinline__ void load(const uint8_t* trow, int q, int lane) {
+    const uint8_t* p = trow + (size_t)q * SB;
+    if (WF) {
+      w[0] = ld_stream(p + lane * 16);
+      sc = ld_stream32(p + 1024 + (lane & 15) * 4);
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sa = fmaf(bf16_lo(ua[i]), xv[2 * i], sa);
-        sa = fmaf(bf16_hi(ua[i]), xv[2 * i + 1], sa);
+      for (int s = 0; s < NW; ++s) w[s] = ld_stream(p + s * 1024 + lane * 16);
+    }
+  }
+  __device__ __forceinline__ f32x4_t mma(const uint4* ap, int stride, f32x4_t acc) const {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 a = ap[s * stride];
+      uint4 b;
+      if (WF) {
+        const uint32_t cd = s == 0 ? w[0].x : s == 1 ? w[0].y : s == 2 ? w[0].z : w[0].w;
+        b = fp4x8_to_bf16(cd, e8m0_as_f32((sc >> (8 * s)) & 0xFFu));
+      } else {
+        b = w[s];
+      }
+      acc = mfma_bf16(a, b, acc);
+    }
+    return acc;
+  }
+};
+
+// The weight registers of one tile row in flight: P K-steps, filled by prefetch() before
+// the activations are staged (so that the stream starts at once) and consumed by run().
+template <int WF, int P>
+struct TileStream {
+  WeightStep<WF> w[P];
+  // K-steps q0 .. q0 + P - 1 (clamped to the last of the n >= 1 steps of the wavefront)
+  __device__ __forceinline__ void prefetch(const uint8_t* trow, int q0, int n) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int i = 0; i < P; ++i) w[i].load(trow, q0 + min(i, n - 1), lane);
+  }
+};
+
+// One tile row over K-steps [q0, q0 + n) after prefetch(trow, q0, n): D += A W^T on the
+// 16 x 16 block (A = staged rows, W = the tile row's 16 weight rows).  N > 0: n == N at
+// compile time, the loop fully unrolled, so every load is unconditional and the waits
+// count exactly the loads in flight; N == 0: any n, the loads past the end clamped to
+// the last K-step (re-reads that are never used).
+template <int WF, int P, int N>
+__device__ __forceinline__ f32x4_t run_tile_row(TileStream<WF, P>& ts, const uint8_t* trow,
+                                                int q0, int n, const uint4* sm, int abase,
+                                                int nr) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int stride = 4 * nr;
+  const uint4* ap = sm + abase + q0 * 4 * stride;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if (N > 0) {
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      acc = ts.w[q % P].mma(ap + q * 4 * stride, stride, acc);
+      if (q + P < N) {
+        ts.w[q % P].load(trow, q0 + q + P, lane);
+        asm volatile("" ::: "memory");
       }
     }
-    sa = wave_sum(sa);
-    if (lane == 0) a.delta[t * a.d + r] = sa;
+    return acc;
+  }
+  const int ql = q0 + n - 1;
+  for (int j = 0; j < n; j += P) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      if (j + i < n) acc = ts.w[i].mma(ap + (j + i) * 4 * stride, stride, acc);
+      ts.w[i].load(trow, min(q0 + j + i + P, ql), lane);
+    }
+    asm volatile("" ::: "memory");
+  }
+  return acc;
+}
+
+// run_tile_row with the K-step count as a compile-time constant where it is 1..32.
+template <int WF, int P>
+__device__ __forceinline__ f32x4_t run_tile_row_n(TileStream<WF, P>& ts, const uint8_t* trow,
+                                                  int q0, int n, const uint4* sm, int abase,
+                                                  int nr) {
+  if (n <= 0) return f32x4_t{0.f, 0.f, 0.f, 0.f};
+  switch (n) {
+#define MOE_N_CASE(N) \
+  case N: return run_tile_row<WF, P, N>(ts, trow, q0, n, sm, abase, nr);
+    MOE_N_CASE(1) MOE_N_CASE(2) MOE_N_CASE(3) MOE_N_CASE(4) MOE_N_CASE(5) MOE_N_CASE(6)
+    MOE_N_CASE(7) MOE_N_CASE(8) MOE_N_CASE(9) MOE_N_CASE(10) MOE_N_CASE(11) MOE_N_CASE(12)
+    MOE_N_CASE(13) MOE_N_CASE(14) MOE_N_CASE(15) MOE_N_CASE(16) MOE_N_CASE(17) MOE_N_CASE(18)
+    MOE_N_CASE(19) MOE_N_CASE(20) MOE_N_CASE(21) MOE_N_CASE(22) MOE_N_CASE(23) MOE_N_CASE(24)
+    MOE_N_CASE(25) MOE_N_CASE(26) MOE_N_CASE(27) MOE_N_CASE(28) MOE_N_CASE(29) MOE_N_CASE(30)
+    MOE_N_CASE(31) MOE_N_CASE(32)
+#undef MOE_N_CASE
+    default: return run_tile_row<WF, P, 0>(ts, trow, q0, n, sm, abase, nr);
+  }
+}
+
+// Partial blocks of the K-split: waves kp > 0 of a tile row hand theirs to the wave with
+// kp = 0, which adds them in the order kp = 1, 2, ... (a fixed order).
+__device__ __forceinline__ f32x4_t reduce_ksplit(f32x4_t acc, f32x4_t (*part)[kWave], int ksplit,
+                                                 int kp) {
+  if (ksplit == 1) return acc;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (kp > 0) part[wv][lane] = acc;
+  __syncthreads();
+  if (kp == 0)
+    for (int i = 1; i < ksplit; ++i) acc += part[wv + i][lane];
+  return acc;
+}
+
+// Lanes c >= 8 receive the value of lane c - 8 of their 16-lane row (gate -> up lane).
+__device__ __forceinline__ float from_gate_lane(float v) {
+  return __uint_as_float(dpp_u32<kDppRowShr8, 0xF, true>(0u, __float_as_uint(v)));
+}
+
+// ------------------------------------------------------------------------------------
+// Steps ROUTER and IN: the three products with the token as input, over the packed IN
+// matrix [router ; W_down_latent ; shared gate/up]: z = x W_r^T, x^c = x W_down^T and
+// h_s = act(x W_sg^T, x W_su^T).  A workgroup stages up to ntb tokens (bf16 rows).
+//   ROUTER launch: each workgroup one K-range (1/zplanes of K) of one router tile row,
+//     its 4 wavefronts splitting the range, written as a partial plane of z; many small
+//     workgroups spread the 2% of the bytes over the whole chip.
+//   IN launch: W_down_latent and the shared gate/up, 4/ksplit tile rows per workgroup,
+//     K split between ksplit wavefronts; with few tokens workgroup 0 meanwhile sums the
+//     logit planes of the ROUTER launch and takes the route and the dispatch.
+// ------------------------------------------------------------------------------------
+struct InArgs {
+  const uint8_t* w;
+  int ks, tr_r, tr_dn, tr_sh, ksplit, ntb;
+  int router;                 // 1: ROUTER launch, 0: IN launch
+  int wg_per_blk;             // workgroups per token block (route workgroup excluded)
+  int zplanes;
+  const uint16_t* x;
+  int64_t T;
+  int d;
+  float* z;
+  int E;
+  float* xc;
+  int l;
+  float* hs;
+  int ms;
+  int act;
+  float bg, bl;
+  int route;
+  RouteArgs ra;
+};
+
+__device__ __forceinline__ void in_body(const InArgs& a) {
+  extern __shared__ uint4 sm[];
+  __shared__ f32x4_t part[kWavesPerBlock][kWave];
+  if (a.route) {
+    // the logits come from the ROUTER launch; this workgroup's selection runs while the
+    // others stream the latent and shared weights
+    if (blockIdx.x == 0) {
+      route_block(a.ra, 0, a.T, true);
+      return;
+    }
+  }
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int bid = blockIdx.x - a.route;
+  const int blk = bid / a.wg_per_blk, wgi = bid - blk * a.wg_per_blk;
+  const int64_t t0 = (int64_t)blk * a.ntb;
+  const int nt = (int)min((int64_t)a.ntb, a.T - t0);
+  int tr, kp, ksplit, q0, q1;
+  if (a.router) {
+    // tile row wgi / zplanes, K-range plane wgi % zplanes split over the 4 wavefronts
+    tr = wgi / a.zplanes;
+    const int plane = wgi - tr * a.zplanes;
+    const int qpp = cdiv(a.ks, a.zplanes);
+    const int r0 = min(a.ks, plane * qpp), r1 = min(a.ks, r0 + qpp);
+    const int qw = cdiv(r1 - r0, kWavesPerBlock);
+    kp = wv;
+    ksplit = kWavesPerBlock;
+    q0 = min(r1, r0 + wv * qw);
+    q1 = min(r1, q0 + qw);
+  } else {
+    const int slot = wgi * kWavesPerBlock + wv;
+    ksplit = a.ksplit;
+    tr = slot / ksplit;
+    kp = slot - tr * ksplit;
+    tr += a.tr_r;
+    const int qper = cdiv(a.ks, ksplit);
+    q0 = min(a.ks, kp * qper);
+    q1 = min(a.ks, q0 + qper);
+  }
+  const int tr_end = a.router ? a.tr_r : a.tr_r + a.tr_dn + a.tr_sh;
+  const bool live = tr < tr_end && q1 > q0;
+  const uint8_t* trow = a.w + (size_t)tr * a.ks * kBf16StepBytes;
+  TileStream<0, 3> ts;
+  if (live) ts.prefetch(trow, q0, q1 - q0);
+  stage_bf16(sm, a.x + t0 * a.d, a.d, nt, a.d, a.ks);
+  __syncthreads();
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if (live) acc = run_tile_row_n<0, 3>(ts, trow, q0, q1 - q0, sm, g * nt + c % nt, nt);
+  acc = reduce_ksplit(acc, part, ksplit, kp);
+  if (tr < tr_end && kp == 0) {
+    // D row 4g + v = token 4g + v of the block, column c = weight row 16 tr + c
+    if (a.router) {
+      const int e = 16 * tr + c;
+      float* zp = a.z + (int64_t)(wgi - tr * a.zplanes) * a.T * a.E;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (4 * g + v < nt && e < a.E) zp[(t0 + 4 * g + v) * a.E + e] = acc[v];
+    } else if (tr < a.tr_r + a.tr_dn) {
+      const int r = 16 * (tr - a.tr_r) + c;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (4 * g + v < nt && r < a.l) a.xc[(t0 + 4 * g + v) * a.l + r] = acc[v];
+    } else {
+      const int r = 8 * (tr - a.tr_r - a.tr_dn) + (c - 8);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float gate = from_gate_lane(acc[v]);
+        if (c >= 8 && 4 * g + v < nt && r < a.ms)
+          a.hs[(t0 + 4 * g + v) * a.ms + r] = glu_act(gate, acc[v], a.act, a.bg, a.bl);
+      }
+    }
+  }
+}
+
+// Two entry points over the same body so that profilers tell the launches apart.
+__global__ __launch_bounds__(kBlock) void k_router(InArgs a) { in_body(a); }
+__global__ __launch_bounds__(kBlock) void k_in(InArgs a) { in_body(a); }
+
+// ------------------------------------------------------------------------------------
+// Routed experts.  The unit table lists runs of at most nu dispatch positions of one
+// expert; a work item is (unit, group of 4/ksplit tile rows).  Gate/up: the input rows
+// are x^c of the positions' tokens and the output h[p] = act(g, u) (tile rows carry 8
+// gate and the matching 8 up rows); down: the input rows are h[p], the output E[p].
+// The workgroups walk the items with a grid stride (the number of units is known only
+// on the device).
+// ------------------------------------------------------------------------------------
+struct ExpArgs {
+  const uint8_t* experts;
+  size_t expert_bytes, region_off;
+  int ks, n_tr, ksplit, wg_per_unit;
+  const int32_t* units;
+  const int32_t* ctrl;
+  int max_units, nu, E, k;
+  int64_t n_assign;
+  const int32_t* perm;
+  const float* xin;
+  int kin;
+  float* out;
+  int n_out;
+  int act;
+  float bg, bl;
+};
+
+template <int WF, bool GU>
+__global__ __launch_bounds__(kBlock) void k_exp(ExpArgs a) {
+  extern __shared__ uint4 sm[];
+  __shared__ f32x4_t part[kWavesPerBlock][kWave];
+  __shared__ HiloRow rows[8];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int n_units = min(a.ctrl[0], a.max_units);
+  const int64_t items = (int64_t)n_units * a.wg_per_unit;
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    const int u = (int)(item / a.wg_per_unit), wgi = (int)(item - (int64_t)u * a.wg_per_unit);
+    const int4 un = *reinterpret_cast<const int4*>(a.units + 4 * u);
+    const int e = un.x, p0 = un.y, n = un.z;
+    if (e < 0 || e >= a.E || n < 1 || n > a.nu || p0 < 0 || p0 + n > a.n_assign) continue;
+    const int nr = 2 * n;
+    const int slot = wgi * kWavesPerBlock + wv;
+    const int tr = slot / a.ksplit, kp = slot - tr * a.ksplit;
+    const int qper = cdiv(a.ks, a.ksplit);
+    const int q0 = min(a.ks, kp * qper), q1 = min(a.ks, q0 + qper);
+    const bool live = tr < a.n_tr && q1 > q0;
+    const uint8_t* trow = a.experts + (size_t)e * a.expert_bytes + a.region_off +
+                          (size_t)tr * a.ks * (WF ? kFp4StepBytes : kBf16StepBytes);
+    TileStream<WF, WF ? 4 : 3> ts;
+    if (live) ts.prefetch(trow, q0, q1 - q0);
+    __syncthreads();  // the previous item's LDS reads are done
+    if ((int)threadIdx.x < n) {
+      const int p = p0 + threadIdx.x;
+      int64_t src = p;
+      if (GU) {
+        const int asg = a.perm[p];
+        src = (asg >= 0 && asg < a.n_assign) ? asg / a.k : 0;
+      }
+      rows[threadIdx.x] = HiloRow{a.xin + src * a.kin, nullptr, 1.f};
+    }
+    __syncthreads();
+    stage_hilo(sm, rows, n, a.kin, 0, 0, nullptr, a.ks);
+    __syncthreads();
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    if (live) acc = run_tile_row_n<WF, WF ? 4 : 3>(ts, trow, q0, q1 - q0, sm, g * nr + c % nr, nr);
+    acc = reduce_ksplit(acc, part, a.ksplit, kp);
+    if (tr < a.n_tr && kp == 0) {
+      // D rows 4g..4g+3 = (hi, lo) of positions 2g and 2g + 1 of the unit
+      const float y0 = acc[0] + acc[1], y1 = acc[2] + acc[3];
+      const int i0 = 2 * g, i1 = 2 * g + 1;
+      if (GU) {
+        const float g0 = from_gate_lane(y0), g1 = from_gate_lane(y1);
+        const int r = 8 * tr + (c - 8);
+        if (c >= 8 && r < a.n_out) {
+          if (i0 < n) a.out[(int64_t)(p0 + i0) * a.n_out + r] = glu_act(g0, y0, a.act, a.bg, a.bl);
+          if (i1 < n) a.out[(int64_t)(p0 + i1) * a.n_out + r] = glu_act(g1, y1, a.act, a.bg, a.bl);
+        }
+      } else {
+        const int r = 16 * tr + c;
+        if (r < a.n_out) {
+          if (i0 < n) a.out[(int64_t)(p0 + i0) * a.n_out + r] = y0;
+          if (i1 < n) a.out[(int64_t)(p0 + i1) * a.n_out + r] = y1;
+        }
+      }
+    }
   }
 }
 
 // ------------------------------------------------------------------------------------
-// Expert packing (MXFP4): one thread per (expert, row group, step, lane) writes the
-// lane's 16 code bytes (four rows' 8-column chunk) and, for lanes 0..15, the four rows'
-// scale bytes of 32-column block step*16 + lane.
+// Step OUT: Delta[t] = [W_up_latent | W_shared_down] [RMSNorm(u_t) * gamma ; h_s,t], one
+// product over the packed OUT matrix.  The workgroup computes the norm of its tokens'
+// u rows and stages [u_hat ; h_s] as hi/lo pairs.
+// ------------------------------------------------------------------------------------
+struct OutArgs {
+  const uint8_t* w;
+  int ks, ks_l, n_tr, ksplit, wg_per_blk, ntb;
+  const float* u;
+  const float* hs;
+  const uint16_t* gamma;
+  int d, l, ms, norm;
+  float eps;
+  int64_t T;
+  float* delta;
+};
+
+constexpr int kOutMaxTokens = 8;
+
+__global__ __launch_bounds__(kBlock) void k_out(OutArgs a) {
+  extern __shared__ uint4 sm[];
+  __shared__ f32x4_t part[kWavesPerBlock][kWave];
+  __shared__ HiloRow rows[kOutMaxTokens];
+  __shared__ float red[kWavesPerBlock];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int blk = blockIdx.x / a.wg_per_blk, wgi = blockIdx.x - blk * a.wg_per_blk;
+  const int64_t t0 = (int64_t)blk * a.ntb;
+  const int nt = (int)min((int64_t)a.ntb, a.T - t0);
+  const int slot = wgi * kWavesPerBlock + wv;
+  const int tr = slot / a.ksplit, kp = slot - tr * a.ksplit;
+  const int qper = cdiv(a.ks, a.ksplit);
+  const int q0 = min(a.ks, kp * qper), q1 = min(a.ks, q0 + qper);
+  const bool live = tr < a.n_tr && q1 > q0;
+  const uint8_t* trow = a.w + (size_t)tr * a.ks * kBf16StepBytes;
+  TileStream<0, 3> ts;
+  if (live) ts.prefetch(trow, q0, q1 - q0);
+  for (int i = 0; i < nt; ++i) {
+    const float* ur = a.u + (t0 + i) * a.l;
+    float inv = 1.f;
+    if (a.norm) {
+      float ss = 0.f;
+      for (int col = threadIdx.x * 4; col < a.l; col += kBlock * 4) {
+        const float4 p = *reinterpret_cast<const float4*>(ur + col);
+        ss = fmaf(p.x, p.x, ss); ss = fmaf(p.y, p.y, ss);
+        ss = fmaf(p.z, p.z, ss); ss = fmaf(p.w, p.w, ss);
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) red[wv] = ss;
+      __syncthreads();
+      const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+      inv = 1.0f / sqrtf(tot / (float)a.l + a.eps);
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) rows[i] = HiloRow{ur, a.hs + (t0 + i) * a.ms, inv};
+  }
+  __syncthreads();
+  stage_hilo(sm, rows, nt, a.l, a.ks_l * kStepK, a.ms, a.norm ? a.gamma : nullptr, a.ks);
+  __syncthreads();
+  const int nr = 2 * nt;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if (live) acc = run_tile_row_n<0, 3>(ts, trow, q0, q1 - q0, sm, g * nr + c % nr, nr);
+  acc = reduce_ksplit(acc, part, a.ksplit, kp);
+  if (tr < a.n_tr && kp == 0) {
+    const int r = 16 * tr + c;
+    const float y0 = acc[0] + acc[1], y1 = acc[2] + acc[3];
+    if (r < a.d) {
+      if (2 * g < nt) a.delta[(t0 + 2 * g) * a.d + r] = y0;
+      if (2 * g + 1 < nt) a.delta[(t0 + 2 * g + 1) * a.d + r] = y1;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Packing (once per layer).  bf16: one thread per (expert, tile row, K-step, sub-tile,
+// lane) copies the lane's 8 columns of its row (zero for rows / columns past the
+// matrix).  Row maps: plain (tile row t, lane row c -> 16t + c) or gated (c < 8: gate
+// row 8t + c, c >= 8: up row H + 8t + c - 8 of a [gate ; up] matrix with H gate rows).
+// MXFP4: the same tiles with 4-byte code words and the 16 rows' scale words.
 // ------------------------------------------------------------------------------------
 struct PackArgs {
-  const uint8_t* codes;   // [n][rows][cols/2]
-  const uint8_t* scales;  // [n][rows][cols/32]
-  int rows, cols, J, gu, m, n, n_rg;
-  uint8_t* dst;           // first packed expert of the run
-  size_t expert_bytes, region_off;
+  const uint8_t* src;     // canonical rows (bf16 elements or fp4 code bytes)
+  const uint8_t* scales;  // MXFP4 scale bytes [n][rows][cols/32]
+  int64_t src_stride, scale_stride;   // bytes between experts
+  int rows, cols, gated;  // canonical rows (H = rows/2 when gated), columns
+  int n_tr, ks_dst, q_off, ks_src;
+  int n;                  // matrices (experts)
+  uint8_t* dst;           // tile row 0 of the first matrix
+  int64_t dst_stride;     // bytes between experts
 };
+
+__device__ __forceinline__ int packed_row(int t, int c, int rows, int gated) {
+  if (!gated) {
+    const int r = 16 * t + c;
+    return r < rows ? r : -1;
+  }
+  const int H = rows / 2, r = 8 * t + (c & 7);
+  if (r >= H) return -1;
+  return c < 8 ? r : H + r;
+}
+
+__global__ __launch_bounds__(kBlock) void k_pack_bf16(PackArgs a) {
+  const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  const int64_t per_mat = (int64_t)a.n_tr * a.ks_src * 4 * kWave;
+  if (gid >= per_mat * a.n) return;
+  const int64_t ei = gid / per_mat;
+  int64_t r = gid - ei * per_mat;
+  const int lane = (int)(r % kWave); r /= kWave;
+  const int s = (int)(r % 4); r /= 4;
+  const int q = (int)(r % a.ks_src);
+  const int t = (int)(r / a.ks_src);
+  const int c = lane & 15, g = lane >> 4;
+  const int row = packed_row(t, c, a.rows, a.gated);
+  const int col = q * kStepK + 32 * s + 8 * g;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (row >= 0 && col < a.cols)
+    v = *reinterpret_cast<const uint4*>(a.src + ei * a.src_stride + ((int64_t)row * a.cols + col) * 2);
+  uint8_t* dp = a.dst + ei * a.dst_stride + ((int64_t)t * a.ks_dst + a.q_off + q) * kBf16StepBytes +
+                s * 1024 + lane * 16;
+  *reinterpret_cast<uint4*>(dp) = v;
+}
 
 __global__ __launch_bounds__(kBlock) void k_pack_fp4(PackArgs a) {
   const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  const int64_t total = (int64_t)a.n * a.n_rg * a.J * kWave;
-  if (gid >= total) return;
-  const int lane = (int)(gid % kWave);
-  const int j = (int)((gid / kWave) % a.J);
-  const int g = (int)((gid / ((int64_t)kWave * a.J)) % a.n_rg);
-  const int64_t ei = gid / ((int64_t)kWave * a.J * a.n_rg);
-  const int c = j * kWave + lane;
-  const int c8 = a.cols >> 3, nb = a.cols >> 5;
-  uint32_t wd[4], sd = 0;
+  const int64_t per_mat = (int64_t)a.n_tr * a.ks_src * kWave;
+  if (gid >= per_mat * a.n) return;
+  const int64_t ei = gid / per_mat;
+  int64_t r = gid - ei * per_mat;
+  const int lane = (int)(r % kWave); r /= kWave;
+  const int q = (int)(r % a.ks_src);
+  const int t = (int)(r / a.ks_src);
+  const int c = lane & 15, g = lane >> 4;
+  const int row = packed_row(t, c, a.rows, a.gated);
+  const int nb = a.cols / 32;
+  uint32_t wd[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int R = a.gu ? (q < 2 ? 2 * g + q : a.m + 2 * g + (q - 2)) : 4 * g + q;
-    const uint8_t* crow = a.codes + (ei * a.rows + R) * (int64_t)(a.cols / 2);
-    wd[q] = (c < c8) ? *reinterpret_cast<const uint32_t*>(crow + 4 * c) : 0u;
-    if (lane < 16) {
-      const int blk = j * 16 + lane;
-      const uint32_t sb = (blk < nb) ? a.scales[(ei * a.rows + R) * (int64_t)nb + blk] : 127u;
-      sd |= sb << (8 * q);
-    }
+  for (int s = 0; s < 4; ++s) {
+    const int col = q * kStepK + 32 * s + 8 * g;
+    wd[s] = (row >= 0 && col < a.cols)
+                ? *reinterpret_cast<const uint32_t*>(a.src + ei * a.src_stride + (int64_t)row * (a.cols / 2) + col / 2)
+                : 0u;
   }
-  uint8_t* gp = a.dst + ei * (int64_t)a.expert_bytes + a.region_off +
-                ((int64_t)g * a.J + j) * kFp4StepBytes;
-  *reinterpret_cast<uint4*>(gp + lane * 16) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-  if (lane < 16) *reinterpret_cast<uint32_t*>(gp + 1024 + lane * 4) = sd;
+  uint8_t* dp = a.dst + ei * a.dst_stride + ((int64_t)t * a.ks_dst + q) * kFp4StepBytes;
+  *reinterpret_cast<uint4*>(dp + lane * 16) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  if (g == 0) {
+    uint32_t sd = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int blkc = 4 * q + s;
+      const uint32_t sb = (row >= 0 && blkc < nb)
+                              ? a.scales[ei * a.scale_stride + (int64_t)row * nb + blkc] : 127u;
+      sd |= sb << (8 * s);
+    }
+    *reinterpret_cast<uint32_t*>(dp + 1024 + c * 4) = sd;
+  }
 }
-
-inline unsigned blocks_for_waves(int64_t waves) {
-  return (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
-}
-
-inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 }  // namespace
 
-// Template dispatch over the chunks per lane (1..N): widths up to N * 512 columns.
-#define MOE_SWITCH16(N, BODY)                                                            \
-  do {                                                                                   \
-    switch (N) {                                                                         \
-      case 1: { constexpr int NC = 1; BODY; } break;                                     \
-      case 2: { constexpr int NC = 2; BODY; } break;                                     \
-      case 3: { constexpr int NC = 3; BODY; } break;                                     \
-      case 4: { constexpr int NC = 4; BODY; } break;                                     \
-      case 5: { constexpr int NC = 5; BODY; } break;                                     \
-      case 6: { constexpr int NC = 6; BODY; } break;                                     \
-      case 7: { constexpr int NC = 7; BODY; } break;                                     \
-      case 8: { constexpr int NC = 8; BODY; } break;                                     \
-      case 9: { constexpr int NC = 9; BODY; } break;                                     \
-      case 10: { constexpr int NC = 10; BODY; } break;                                   \
-      case 11: { constexpr int NC = 11; BODY; } break;                                   \
-      case 12: { constexpr int NC = 12; BODY; } break;                                   \
-      case 13: { constexpr int NC = 13; BODY; } break;                                   \
-      case 14: { constexpr int NC = 14; BODY; } break;                                   \
-      case 15: { constexpr int NC = 15; BODY; } break;                                   \
-      case 16: { constexpr int NC = 16; BODY; } break;                                   \
-      default: return hipErrorInvalidValue;                                              \
-    }                                                                                    \
-  } while (0)
+// ------------------------------------------------------------------------------------
+// Launches
+// ------------------------------------------------------------------------------------
+namespace {
 
-#define MOE_SWITCH32(N, BODY)                                                          \
-  do {                                                                                 \
-    switch (N) {                                                                       \
-      case 1: { constexpr int NC = 1; BODY; } break;                                   \
-      case 2: { constexpr int NC = 2; BODY; } break;                                   \
-      case 3: { constexpr int NC = 3; BODY; } break;                                   \
-      case 4: { constexpr int NC = 4; BODY; } break;                                   \
-      case 5: { constexpr int NC = 5; BODY; } break;                                   \
-      case 6: { constexpr int NC = 6; BODY; } break;                                   \
-      case 7: { constexpr int NC = 7; BODY; } break;                                   \
-      case 8: { constexpr int NC = 8; BODY; } break;                                   \
-      case 9: { constexpr int NC = 9; BODY; } break;                                   \
-      case 10: { constexpr int NC = 10; BODY; } break;                                 \
-      case 11: { constexpr int NC = 11; BODY; } break;                                 \
-      case 12: { constexpr int NC = 12; BODY; } break;                                 \
-      case 13: { constexpr int NC = 13; BODY; } break;                                 \
-      case 14: { constexpr int NC = 14; BODY; } break;                                 \
-      case 15: { constexpr int NC = 15; BODY; } break;                                 \
-      case 16: { constexpr int NC = 16; BODY; } break;                                 \
-      case 17: { constexpr int NC = 17; BODY; } break;                                 \
-      case 18: { constexpr int NC = 18; BODY; } break;                                 \
-      case 19: { constexpr int NC = 19; BODY; } break;                                 \
-      case 20: { constexpr int NC = 20; BODY; } break;                                 \
-      case 21: { constexpr int NC = 21; BODY; } break;                                 \
-      case 22: { constexpr int NC = 22; BODY; } break;                                 \
-      case 23: { constexpr int NC = 23; BODY; } break;                                 \
-      case 24: { constexpr int NC = 24; BODY; } break;                                 \
-      case 25: { constexpr int NC = 25; BODY; } break;                                 \
-      case 26: { constexpr int NC = 26; BODY; } break;                                 \
-      case 27: { constexpr int NC = 27; BODY; } break;                                 \
-      case 28: { constexpr int NC = 28; BODY; } break;                                 \
-      case 29: { constexpr int NC = 29; BODY; } break;                                 \
-      case 30: { constexpr int NC = 30; BODY; } break;                                 \
-      case 31: { constexpr int NC = 31; BODY; } break;                                 \
-      case 32: { constexpr int NC = 32; BODY; } break;                                 \
-      default: return hipErrorInvalidValue;                                            \
-    }                                                                                  \
-  } while (0)
+RouteArgs route_args(const Shape& s, const float* bias, int64_t T, const Work& ws, int32_t* idx,
+                     float* gw) {
+  return RouteArgs{ws.z, s.zplanes, T * s.E, bias, T, s.E, s.k, s.route_scale, idx, gw,
+                   ws.counts, ws.offs, ws.perm, ws.inv, ws.units, ws.ctrl, unit_positions(s, T)};
+}
 
-static inline int chunks_per_lane(int k) { return cdiv(k / 8, kWave); }
+// Wavefronts per tile row: split K until a single token's launch has enough wavefronts
+// to keep every compute unit streaming (about 16 per CU), keeping at least 8 K-steps per
+// wavefront.  The split depends on the matrix alone, never on the batch, so a token's
+// result has the same bits in every batch (the summation order is fixed per matrix).
+int choose_ksplit(int64_t tile_rows, int ks) {
+  int ksplit = 1;
+  while (ksplit < kWavesPerBlock && tile_rows * ksplit < 4096 && ks / (2 * ksplit) >= 8) ksplit *= 2;
+  return ksplit;
+}
 
-bool route_fused(int64_t T, int k) { return T * k <= kBlock && T <= 4; }
+}  // namespace
 
 namespace {
 
-DenseXArgs dense_x_args(const Shape& s, const DenseW& w, const uint16_t* x, int64_t T,
-                        const Work& ws) {
-  DenseXArgs a;
+InArgs in_args(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T, const Work& ws) {
+  InArgs a;
+  a.w = dense;
+  a.ks = s.ks_in;
+  a.tr_r = s.tr_r; a.tr_dn = s.tr_dn; a.tr_sh = s.tr_sh;
+  a.zplanes = s.zplanes;
+  a.ntb = in_tokens_per_block(s);
+  a.ksplit = choose_ksplit(s.tr_dn + s.tr_sh, s.ks_in);
   a.x = x; a.T = T; a.d = s.d;
-  a.wr = w.router; a.E = s.E; a.z = ws.z;
-  a.wdn = w.wdn; a.l = s.l; a.xc = ws.xc;
-  a.sgu = w.sgu; a.ms = s.ms; a.hs = ws.hs;
+  a.z = ws.z; a.E = s.E;
+  a.xc = ws.xc; a.l = s.l;
+  a.hs = ws.hs; a.ms = s.ms;
   a.act = s.act; a.bg = s.beta_gate; a.bl = s.beta_lin;
-  a.rows_per_wave = 4;
-  a.pairs_per_wave = 2;
-  a.waves_r = a.waves_dn = a.waves_sh = 0;
   a.route = 0;
   return a;
 }
 
-RouteArgs route_args(const Shape& s, const float* bias, int64_t T, const Work& ws, int32_t* idx,
-                     float* gw) {
-  return RouteArgs{ws.z, bias, T, s.E, s.k, s.route_scale, idx, gw, ws.counts, ws.offs,
-                   ws.perm, ws.inv};
-}
-
 }  // namespace
 
-hipError_t launch_router(const Shape& s, const DenseW& w, const uint16_t* x, int64_t T,
+hipError_t launch_router(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,
                          const Work& ws, hipStream_t st) {
-  DenseXArgs a = dense_x_args(s, w, x, T, ws);
-  a.rows_per_wave = 2;   // a small matrix: spread it over more wavefronts
-  a.waves_r = cdiv(s.E, a.rows_per_wave);
-  const int64_t waves = T * a.waves_r;
-  MOE_SWITCH16(chunks_per_lane(s.d),
-               hipLaunchKernelGGL(k_router<NC>, dim3(blocks_for_waves(waves)), dim3(kBlock), 0,
-                                  st, a));
+  InArgs a = in_args(s, dense, x, T, ws);
+  a.router = 1;
+  a.wg_per_blk = s.tr_r * s.zplanes;
+  const int64_t nblk = (T + a.ntb - 1) / a.ntb;
+  const size_t lds = (size_t)(T < a.ntb ? T : a.ntb) * s.ks_in * kStepK * 2;
+  hipLaunchKernelGGL(k_router, dim3((unsigned)(nblk * a.wg_per_blk)), dim3(kBlock), lds, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_dense_x(const Shape& s, const DenseW& w, const uint16_t* x, int64_t T,
-                          const float* bias, int32_t* idx, float* gw, const Work& ws,
-                          hipStream_t st) {
-  DenseXArgs a = dense_x_args(s, w, x, T, ws);
-  a.waves_dn = cdiv(s.l, a.rows_per_wave);
-  a.waves_sh = (s.ms == 0) ? 0 : cdiv(s.ms, a.pairs_per_wave);
-  a.route = route_fused(T, s.k) ? 1 : 0;
+hipError_t launch_in(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,
+                     const float* bias, int32_t* idx, float* gw, const Work& ws, hipStream_t st) {
+  InArgs a = in_args(s, dense, x, T, ws);
+  a.router = 0;
+  a.wg_per_blk = cdiv((int64_t)(s.tr_dn + s.tr_sh) * a.ksplit, kWavesPerBlock);
+  a.route = route_fused(s, T) ? 1 : 0;
   a.ra = route_args(s, bias, T, ws, idx, gw);
-  const int64_t waves = T * (a.waves_dn + a.waves_sh) + (a.route ? kWavesPerBlock : 0);
-  MOE_SWITCH16(chunks_per_lane(s.d),
-               hipLaunchKernelGGL(k_dense_x<NC>, dim3(blocks_for_waves(waves)), dim3(kBlock), 0,
-                                  st, a));
+  const int64_t nblk = (T + a.ntb - 1) / a.ntb;
+  const size_t lds = (size_t)(T < a.ntb ? T : a.ntb) * s.ks_in * kStepK * 2;
+  hipLaunchKernelGGL(k_in, dim3((unsigned)(nblk * a.wg_per_blk + a.route)), dim3(kBlock), lds, st, a);
   return hipGetLastError();
 }
 
@@ -891,89 +999,51 @@ hipError_t launch_route(const Shape& s, const float* bias, int64_t T, const Work
 
 hipError_t launch_dispatch(const Shape& s, const int32_t* idx, int64_t T, int32_t* counts,
                            int32_t* offs, int32_t* perm, int32_t* inv, int32_t* chunk_hist,
-                           hipStream_t st) {
+                           int32_t* units, int32_t* ctrl, hipStream_t st) {
   const int ct = dispatch_chunk_tokens(s.k);
   const int chunk = ct * s.k;
   const int64_t n = T * s.k;
   const int nch = cdiv(T, ct);
   hipLaunchKernelGGL(k_disp_count, dim3(nch), dim3(kBlock), 0, st, idx, n, s.E, chunk, chunk_hist);
-  hipLaunchKernelGGL(k_disp_scan, dim3(1), dim3(1024), 0, st, nch, s.E, chunk_hist, counts, offs);
+  hipLaunchKernelGGL(k_disp_scan, dim3(1), dim3(1024), 0, st, nch, s.E, unit_positions(s, T),
+                     chunk_hist, counts, offs, units, ctrl);
   hipLaunchKernelGGL(k_disp_scatter, dim3(nch), dim3(kBlock), 0, st, idx, n, s.E, chunk,
                      (const int32_t*)chunk_hist, (const int32_t*)offs, perm, inv);
   return hipGetLastError();
 }
 
-namespace {
-
-ExpArgs expert_args(const Shape& s, const DenseW& w, const int32_t* idx, int64_t T,
-                    const Work& ws) {
+hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_t T,
+                         const Work& ws, hipStream_t st) {
   ExpArgs a;
-  a.experts = w.experts;
+  a.experts = experts;
   a.expert_bytes = s.expert_bytes;
-  a.idx = idx;
-  a.perm = ws.perm;
+  a.region_off = gu ? 0 : s.gu_bytes;
+  a.ks = gu ? s.ks_gu : s.ks_edn;
+  a.n_tr = gu ? s.tr_gu : s.tr_edn;
+  a.units = ws.units;
+  a.ctrl = ws.ctrl;
+  a.nu = unit_positions(s, T);
+  a.max_units = (int)max_units(s, T);
+  a.E = s.E; a.k = s.k;
   a.n_assign = T * s.k;
-  a.k = s.k;
-  a.m = s.m;
-  a.act = s.act;
-  a.bg = s.beta_gate;
-  a.bl = s.beta_lin;
-  return a;
-}
-
-hipError_t launch_fp4(ExpArgs a, int J, bool gu, hipStream_t st) {
-  a.units_per_wave = 2;
-  a.wgs_per_pos = cdiv(a.n_units, (int64_t)a.units_per_wave * kWavesPerBlock);
-  const unsigned blocks = (unsigned)(a.n_assign * a.wgs_per_pos);
-  if (gu) {
-    MOE_SWITCH16(J, hipLaunchKernelGGL((k_expert_fp4<NC, true>), dim3(blocks), dim3(kBlock), 0, st, a));
+  a.perm = ws.perm;
+  a.xin = gu ? ws.xc : ws.h;
+  a.kin = gu ? s.l : s.m;
+  a.out = gu ? ws.h : ws.eo;
+  a.n_out = gu ? s.m : s.l;
+  a.act = s.act; a.bg = s.beta_gate; a.bl = s.beta_lin;
+  a.ksplit = choose_ksplit((int64_t)s.k * a.n_tr, a.ks);
+  a.wg_per_unit = cdiv((int64_t)a.n_tr * a.ksplit, kWavesPerBlock);
+  const int64_t items = (int64_t)a.max_units * a.wg_per_unit;
+  const unsigned grid = (unsigned)(items < 8192 ? items : 8192);
+  const size_t lds = (size_t)2 * a.nu * a.ks * kStepK * 2;
+  if (s.wfmt == 1) {
+    if (gu) hipLaunchKernelGGL((k_exp<1, true>), dim3(grid), dim3(kBlock), lds, st, a);
+    else hipLaunchKernelGGL((k_exp<1, false>), dim3(grid), dim3(kBlock), lds, st, a);
   } else {
-    MOE_SWITCH16(J, hipLaunchKernelGGL((k_expert_fp4<NC, false>), dim3(blocks), dim3(kBlock), 0, st, a));
+    if (gu) hipLaunchKernelGGL((k_exp<0, true>), dim3(grid), dim3(kBlock), lds, st, a);
+    else hipLaunchKernelGGL((k_exp<0, false>), dim3(grid), dim3(kBlock), lds, st, a);
   }
-  return hipGetLastError();
-}
-
-}  // namespace
-
-hipError_t launch_expert_gu(const Shape& s, const DenseW& w, const int32_t* idx, int64_t T,
-                            const Work& ws, hipStream_t st) {
-  // x^c of the assignment's token -> h[p], p in dispatch order
-  ExpArgs a = expert_args(s, w, idx, T, ws);
-  a.region_off = 0;
-  a.xin = ws.xc; a.kin = s.l; a.in_by_token = 1;
-  a.out = ws.h; a.n_out = s.m;
-  if (s.wfmt == 1) {
-    a.n_units = s.m / 2;
-    return launch_fp4(a, s.j_gu, true, st);
-  }
-  a.n_units = s.m;
-  a.units_per_wave = 4;
-  a.wgs_per_pos = cdiv(a.n_units, a.units_per_wave);
-  const int64_t waves = a.n_assign * a.wgs_per_pos;
-  MOE_SWITCH16(chunks_per_lane(s.l),
-               hipLaunchKernelGGL((k_expert_bf16<NC, true>), dim3(blocks_for_waves(waves)),
-                                  dim3(kBlock), 0, st, a));
-  return hipGetLastError();
-}
-
-hipError_t launch_expert_down(const Shape& s, const DenseW& w, const int32_t* idx, int64_t T,
-                              const Work& ws, hipStream_t st) {
-  // h[p] -> E[p]
-  ExpArgs a = expert_args(s, w, idx, T, ws);
-  a.region_off = s.gu_bytes;
-  a.xin = ws.h; a.kin = s.m; a.in_by_token = 0;
-  a.out = ws.eo; a.n_out = s.l;
-  if (s.wfmt == 1) {
-    a.n_units = s.l / 4;
-    return launch_fp4(a, s.j_dn, false, st);
-  }
-  a.n_units = s.l;
-  a.units_per_wave = 8;
-  a.wgs_per_pos = cdiv(a.n_units, a.units_per_wave);
-  const int64_t waves = a.n_assign * a.wgs_per_pos;
-  MOE_SWITCH16(chunks_per_lane(s.m),
-               hipLaunchKernelGGL((k_expert_bf16<NC, false>), dim3(blocks_for_waves(waves)),
-                                  dim3(kBlock), 0, st, a));
   return hipGetLastError();
 }
 
@@ -985,44 +1055,94 @@ hipError_t launch_combine(const Shape& s, const float* gw, int64_t T, const Work
   return hipGetLastError();
 }
 
-hipError_t launch_out(const Shape& s, const DenseW& w, int64_t T, const Work& ws, float* delta,
-                      hipStream_t st) {
+hipError_t launch_out(const Shape& s, const uint8_t* dense, int64_t T, const Work& ws,
+                      float* delta, hipStream_t st) {
   OutArgs a;
-  a.wup = w.wup; a.sdn = w.sdn; a.gamma = w.gamma;
-  a.d = s.d; a.l = s.l; a.ms = s.ms;
-  a.norm = s.use_norm; a.eps = s.eps;
-  a.u = ws.u; a.hs = ws.hs; a.T = T; a.delta = delta;
-  a.rows_per_wave = 4;
-  a.wgs_per_tok = cdiv(s.d, (int64_t)a.rows_per_wave * kWavesPerBlock);
-  const unsigned blocks = (unsigned)(T * a.wgs_per_tok);
-  MOE_SWITCH32(cdiv((s.l + s.ms) / 8, kWave),
-               hipLaunchKernelGGL(k_out<NC>, dim3(blocks), dim3(kBlock), 0, st, a));
+  a.w = dense + s.in_bytes;
+  a.ks = s.ks_out; a.ks_l = s.ks_l;
+  a.n_tr = s.tr_out;
+  a.ntb = out_tokens_per_block(s);   // 2 * ntb hi/lo rows: at most one 16-row MFMA block
+  const int64_t nblk = (T + a.ntb - 1) / a.ntb;
+  a.ksplit = choose_ksplit(s.tr_out, s.ks_out);
+  a.wg_per_blk = cdiv((int64_t)a.n_tr * a.ksplit, kWavesPerBlock);
+  a.u = ws.u; a.hs = ws.hs;
+  a.gamma = reinterpret_cast<const uint16_t*>(dense + s.gamma_off);
+  a.d = s.d; a.l = s.l; a.ms = s.ms; a.norm = s.use_norm; a.eps = s.eps;
+  a.T = T; a.delta = delta;
+  const size_t lds = (size_t)2 * (T < a.ntb ? T : a.ntb) * s.ks_out * kStepK * 2;
+  hipLaunchKernelGGL(k_out, dim3((unsigned)(nblk * a.wg_per_blk)), dim3(kBlock), lds, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_pack(const Shape& s, const void* gu, const void* gus, const void* dn,
-                       const void* dns, int e0, int n, uint8_t* packed, hipStream_t st) {
+namespace {
+
+hipError_t pack_bf16(const void* src, int64_t src_stride, int rows, int cols, int gated, int n_tr,
+                     int ks_dst, int q_off, int n, uint8_t* dst, int64_t dst_stride,
+                     hipStream_t st) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  PackArgs a{};
+  a.src = static_cast<const uint8_t*>(src);
+  a.src_stride = src_stride;
+  a.rows = rows; a.cols = cols; a.gated = gated;
+  a.n_tr = n_tr; a.ks_dst = ks_dst; a.q_off = q_off; a.ks_src = cdiv(cols, kStepK);
+  a.n = n; a.dst = dst; a.dst_stride = dst_stride;
+  const int64_t threads = (int64_t)n * n_tr * a.ks_src * 4 * kWave;
+  hipLaunchKernelGGL(k_pack_bf16, dim3((unsigned)cdiv(threads, kBlock)), dim3(kBlock), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pack_dense(const Shape& s, const DenseSrc& src, uint8_t* packed,
+                             hipStream_t st) {
+  hipError_t e;
+  const int64_t row_in = (int64_t)s.ks_in * kBf16StepBytes;
+  // IN: router, W_down_latent, shared gate/up (gated tiles)
+  if ((e = pack_bf16(src.router, 0, s.E, s.d, 0, s.tr_r, s.ks_in, 0, 1, packed, 0, st)) != hipSuccess) return e;
+  if ((e = pack_bf16(src.wdn, 0, s.l, s.d, 0, s.tr_dn, s.ks_in, 0, 1, packed + s.tr_r * row_in, 0,
+                     st)) != hipSuccess) return e;
+  if (s.ms > 0 && (e = pack_bf16(src.sgu, 0, 2 * s.ms, s.d, 1, s.tr_sh, s.ks_in, 0, 1,
+                                 packed + (int64_t)(s.tr_r + s.tr_dn) * row_in, 0, st)) != hipSuccess)
+    return e;
+  // OUT: [W_up_latent | W_shared_down]
+  uint8_t* out = packed + s.in_bytes;
+  if ((e = pack_bf16(src.wup, 0, s.d, s.l, 0, s.tr_out, s.ks_out, 0, 1, out, 0, st)) != hipSuccess) return e;
+  if (s.ms > 0 && (e = pack_bf16(src.sdn, 0, s.d, s.ms, 0, s.tr_out, s.ks_out, s.ks_l, 1, out, 0,
+                                 st)) != hipSuccess)
+    return e;
+  return hipMemcpyAsync(packed + s.gamma_off, src.gamma, (size_t)s.l * 2, hipMemcpyDeviceToDevice, st);
+}
+
+hipError_t launch_pack_experts(const Shape& s, const void* gu, const void* gus, const void* dn,
+                               const void* dns, int e0, int n, uint8_t* packed, hipStream_t st) {
   uint8_t* dst = packed + (size_t)e0 * s.expert_bytes;
   if (s.wfmt == 0) {
-    const size_t gub = (size_t)2 * s.m * s.l * 2, dnb = (size_t)s.l * s.m * 2;
-    hipError_t err = hipMemcpy2DAsync(dst, s.expert_bytes, gu, gub, gub, n, hipMemcpyDeviceToDevice, st);
-    if (err != hipSuccess) return err;
-    return hipMemcpy2DAsync(dst + s.gu_bytes, s.expert_bytes, dn, dnb, dnb, n,
-                            hipMemcpyDeviceToDevice, st);
+    hipError_t e = pack_bf16(gu, (int64_t)2 * s.m * s.l * 2, 2 * s.m, s.l, 1, s.tr_gu, s.ks_gu, 0, n,
+                             dst, s.expert_bytes, st);
+    if (e != hipSuccess) return e;
+    return pack_bf16(dn, (int64_t)s.l * s.m * 2, s.l, s.m, 0, s.tr_edn, s.ks_edn, 0, n,
+                     dst + s.gu_bytes, s.expert_bytes, st);
   }
-  PackArgs a;
-  a.m = s.m; a.n = n; a.dst = dst; a.expert_bytes = s.expert_bytes;
-  // gate/up: [2m][l], row groups of (gate 2g, 2g+1, up 2g, 2g+1)
-  a.codes = static_cast<const uint8_t*>(gu); a.scales = static_cast<const uint8_t*>(gus);
-  a.rows = 2 * s.m; a.cols = s.l; a.J = s.j_gu; a.gu = 1; a.n_rg = s.m / 2; a.region_off = 0;
-  int64_t threads = (int64_t)n * a.n_rg * a.J * kWave;
+  PackArgs a{};
+  a.src = static_cast<const uint8_t*>(gu);
+  a.scales = static_cast<const uint8_t*>(gus);
+  a.src_stride = (int64_t)2 * s.m * (s.l / 2);
+  a.scale_stride = (int64_t)2 * s.m * (s.l / 32);
+  a.rows = 2 * s.m; a.cols = s.l; a.gated = 1;
+  a.n_tr = s.tr_gu; a.ks_dst = s.ks_gu; a.q_off = 0; a.ks_src = s.ks_gu;
+  a.n = n; a.dst = dst; a.dst_stride = s.expert_bytes;
+  int64_t threads = (int64_t)n * a.n_tr * a.ks_src * kWave;
   hipLaunchKernelGGL(k_pack_fp4, dim3((unsigned)cdiv(threads, kBlock)), dim3(kBlock), 0, st, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // down: [l][m], row groups of 4 consecutive rows
-  a.codes = static_cast<const uint8_t*>(dn); a.scales = static_cast<const uint8_t*>(dns);
-  a.rows = s.l; a.cols = s.m; a.J = s.j_dn; a.gu = 0; a.n_rg = s.l / 4; a.region_off = s.gu_bytes;
-  threads = (int64_t)n * a.n_rg * a.J * kWave;
+  a.src = static_cast<const uint8_t*>(dn);
+  a.scales = static_cast<const uint8_t*>(dns);
+  a.src_stride = (int64_t)s.l * (s.m / 2);
+  a.scale_stride = (int64_t)s.l * (s.m / 32);
+  a.rows = s.l; a.cols = s.m; a.gated = 0;
+  a.n_tr = s.tr_edn; a.ks_dst = s.ks_edn; a.ks_src = s.ks_edn;
+  a.dst = dst + s.gu_bytes;
+  threads = (int64_t)n * a.n_tr * a.ks_src * kWave;
   hipLaunchKernelGGL(k_pack_fp4, dim3((unsigned)cdiv(threads, kBlock)), dim3(kBlock), 0, st, a);
   return hipGetLastError();
 }

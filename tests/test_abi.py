@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2 == moe.ABI_VERSION
     assert moe.status_str(0) == "MOE_OK"
     assert moe.status_str(3) == "MOE_ERR_WORKSPACE"
     assert moe.status_str(99) == "MOE_ERR_UNKNOWN"
@@ -46,8 +46,18 @@ def test_packed_expert_bytes_equal_mxfp4_storage(L):
     cfg = moe.config_from(synth.K3_DECODE_B1)
     assert moe.packed_experts_size(cfg) == 896 * 17_547_264
     assert 17_547_264 * 8 == 33_030_144 * 4.25
-    toy = moe.config_from(synth.TOY)    # bf16: 3 * 320 * 256 * 2 bytes per expert
-    assert moe.packed_experts_size(toy) == 64 * 491_520
+    # toy bf16 experts: gate/up input columns 320 padded to 3 K-steps of 128
+    toy = moe.config_from(synth.TOY)
+    assert moe.packed_experts_size(toy) == 64 * (2 * 256 * 384 * 2 + 320 * 256 * 2)
+
+
+def test_packed_dense_bytes_equal_bf16_storage(L):
+    # K3 widths are multiples of 128: the tiles hold exactly the canonical bytes + gamma
+    cfg = moe.config_from(synth.K3_DECODE_B1)
+    d, l, E, ms = 7168, 3584, 896, 6144
+    canonical = (E * d + l * d + 2 * ms * d + d * l + d * ms) * 2
+    assert moe.packed_dense_size(cfg) == canonical + l * 2
+    assert canonical == 379_846_656
 
 
 def test_workspace_layout_is_ordered_and_aligned(L):
@@ -71,7 +81,7 @@ def _bad(**kw):
     ("top_k", 65, moe.MOE_ERR_INVALID_ARG),          # k > E
     ("top_k", 0, moe.MOE_ERR_INVALID_ARG),
     ("d_model", 644, moe.MOE_ERR_INVALID_ARG),       # not a multiple of 8
-    ("d_model", 16384, moe.MOE_ERR_UNSUPPORTED),     # wider than the register-resident slice
+    ("d_model", 16384, moe.MOE_ERR_UNSUPPORTED),     # wider than the shapes built
     ("n_experts", 2048, moe.MOE_ERR_UNSUPPORTED),
     ("act", 7, moe.MOE_ERR_INVALID_ARG),
     ("expert_wfmt", 5, moe.MOE_ERR_INVALID_ARG),
@@ -94,7 +104,7 @@ def test_mxfp4_needs_blocks_of_32(L):
 def test_forward_rejects_bad_arguments_before_launch(L):
     cfg = moe.config_from(synth.TOY)
     A = 1 << 20          # a 256-aligned non-null address; never dereferenced on error paths
-    W = moe.MoeWeights(A, A, A, A, A, A, A)
+    W = moe.MoeWeights(A, A)
     f = L.moe_layer_forward
     ok = dict(bias=A, x=A, T=4, delta=A, idx=A, w=A, ws=A, wsb=1 << 40)
 
@@ -107,7 +117,8 @@ def test_forward_rejects_bad_arguments_before_launch(L):
     assert call(ws=A + 64) == moe.MOE_ERR_INVALID_ARG            # workspace not 256-aligned
     assert call(T=-1) == moe.MOE_ERR_INVALID_ARG
     assert call(wsb=16) == moe.MOE_ERR_WORKSPACE
-    assert call(W=moe.MoeWeights(A, A, A, A, None, A, A)) == moe.MOE_ERR_INVALID_ARG
+    assert call(W=moe.MoeWeights(A, None)) == moe.MOE_ERR_INVALID_ARG
+    assert call(W=moe.MoeWeights(A + 16, A)) == moe.MOE_ERR_INVALID_ARG   # packed: 256-aligned
     assert call(T=0) == moe.MOE_OK                               # nothing to do, no launch
     assert call(T=0, x=None, delta=None, W=moe.MoeWeights()) == moe.MOE_OK
     assert f(None, ctypes.byref(W), A, A, 1, A, A, A, A, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
@@ -121,6 +132,12 @@ def test_pack_and_dispatch_reject_bad_ranges(L):
     assert L.moe_pack_experts(ctypes.byref(cfg), ctypes.byref(src), 60, 5, A, size, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_pack_experts(ctypes.byref(cfg), ctypes.byref(src), 0, 4, A, size - 1, None) == moe.MOE_ERR_WORKSPACE
     assert L.moe_pack_experts(ctypes.byref(cfg), ctypes.byref(src), 3, 0, A, size, None) == moe.MOE_OK
+    dsrc = moe.MoeDenseSrc(A, A, A, A, A, A)
+    dsize = moe.packed_dense_size(cfg)
+    assert L.moe_pack_dense(ctypes.byref(cfg), ctypes.byref(dsrc), A, dsize - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_pack_dense(ctypes.byref(cfg), ctypes.byref(dsrc), A + 16, dsize, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_dense(ctypes.byref(cfg), ctypes.byref(moe.MoeDenseSrc(A, None, A, A, A, A)), A,
+                            dsize, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_dispatch(ctypes.byref(cfg), A, 8, A, A, A, A, A, 8, None) == moe.MOE_ERR_WORKSPACE
     assert L.moe_dispatch(ctypes.byref(cfg), None, 8, A, A, A, A, A, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_dispatch(ctypes.byref(cfg), None, 0, None, None, None, None, None, 0, None) == moe.MOE_OK

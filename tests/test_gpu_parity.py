@@ -165,8 +165,7 @@ def test_dispatch_bit_exact(T, E, k):
     rng = np.random.default_rng(T * 1000 + E)
     idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
     cfg = synth.TOY.with_(E=E, k=k)
-    lay = moe.Layer(moe.config_from(cfg), *([None] * 8))
-    lay.router = torch.empty(1, device=DEV)   # device for the workspace
+    lay = moe.Layer(moe.config_from(cfg), torch.empty(1, device=DEV), None, None)
     got = [t.cpu().numpy() for t in lay.dispatch(torch.from_numpy(idx).to(DEV))]
     want = O.dispatch(idx, E)
     for g, wv, name in zip(got, want, ("counts", "offsets", "perm", "inv")):
