@@ -39,10 +39,11 @@ def algorithmic_bytes(cfg, T, D):
         gu_w, dn_w = 2 * m * l * 2, l * m * 2
     tk = T * k
     small = T <= 3   # the route and the dispatch run inside the IN launch
+    sh_head = 0   # shared gate/up rows in the ROUTER launch
     return {
-        "router": T * d * 2 + E * d * 2 + T * E * 4 * 8,
-        "in": T * d * 2 + (l + 2 * ms) * d * 2 + T * (l + ms) * 4
-              + ((T * E * 4 * 8 + E * 4 + tk * 16 + E * 8) if small else 0),
+        "router": T * d * 2 + (E + l + 2 * sh_head) * d * 2 + T * (E + l + sh_head) * 4,
+        "in": T * d * 2 + 2 * (ms - sh_head) * d * 2 + T * (ms - sh_head) * 4
+              + ((T * E * 4 + E * 4 + tk * 16 + E * 8) if small else 0),
         "route": 0 if small else T * E * 4 + E * 4 + tk * 8,
         "dispatch": 0 if small else tk * 4 * 4 + E * 8,
         "expert_gu": D * gu_w + T * l * 4 + tk * m * 4,
@@ -242,7 +243,7 @@ def main():
     hip.destroy(evs)
     steps_us = {n: round(float(v) * 1e3, 2) for n, v in zip(moe.STEPS, step_ms)}
     log(f"[bench] per step with events at every boundary (us): {steps_us}")
-    dom = max(("in", "expert_gu", "expert_down", "out"),
+    dom = max(("router", "in", "expert_gu", "expert_down", "out"),
               key=lambda n: step_ms[moe.STEPS.index(n)])
     # The dominant step alone, K launches back to back between two events.  Each launch
     # works on the buffers of an earlier full forward; R sets of buffers (different tokens,

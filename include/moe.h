@@ -196,11 +196,11 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const 
 
 /* Steps of the forward, in launch order. */
 typedef enum moe_step {
-  MOE_STEP_ROUTER = 0,      /* router logits z = x W_r (partial planes) */
-  MOE_STEP_IN = 1,          /* x^c = x W_down_latent, shared gate/up + SiTU; with few tokens
-                               (at most 4, fewer for very wide d) one workgroup of the same
-                               launch also takes the top-k, the gate weights and the
-                               dispatch */
+  MOE_STEP_ROUTER = 0,      /* router logits z = x W_r (partial planes), and in the same
+                               launch x^c = x W_down_latent */
+  MOE_STEP_IN = 1,          /* shared gate/up + SiTU; with few tokens (at most 4, fewer for
+                               very wide d) one workgroup of the same launch also takes the
+                               top-k, the gate weights and the dispatch */
   MOE_STEP_ROUTE = 2,       /* sigmoid, top_k(s + b), gate weights (larger batches; launches
                                nothing otherwise) */
   MOE_STEP_DISPATCH = 3,    /* histogram, scan, stable permutation by expert (larger

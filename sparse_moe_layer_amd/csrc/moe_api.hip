@@ -265,7 +265,7 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const float
       return MOE_ERR_HIP;
     hipError_t e = hipSuccess;
     switch (step) {
-      case MOE_STEP_ROUTER: e = moe::launch_router(s, dense, xb, n_tokens, ws, hs); break;
+      case MOE_STEP_ROUTER: e = moe::launch_router(s, dense, xb, n_tokens, false, ws, hs); break;
       case MOE_STEP_IN:
         e = moe::launch_in(s, dense, xb, n_tokens, bias, topk_idx, topk_w, ws, hs);
         break;
@@ -335,7 +335,7 @@ MOE_EXPORT moe_status moe_route(const moe_config* cfg, const moe_weights* w, con
   const moe::Work ws = make_work(workspace, off);
   hipStream_t hs = (hipStream_t)stream;
   if (moe::launch_router(s, static_cast<const uint8_t*>(w->dense), static_cast<const uint16_t*>(x),
-                         n_tokens, ws, hs) != hipSuccess)
+                         n_tokens, true, ws, hs) != hipSuccess)
     return MOE_ERR_HIP;
   return hip_status(moe::launch_route(s, bias, n_tokens, ws, topk_idx, topk_w, hs));
 }

@@ -78,8 +78,9 @@ inline bool route_fused(const Shape& s, int64_t T) {
   return T <= 4 && T * s.k <= kBlock && T <= in_tokens_per_block(s);
 }
 
+// router_only: the router rows alone (otherwise W_down_latent rides in the same launch)
 hipError_t launch_router(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,
-                         const Work& ws, hipStream_t st);
+                         bool router_only, const Work& ws, hipStream_t st);
 hipError_t launch_in(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,
                      const float* bias, int32_t* idx, float* gw, const Work& ws, hipStream_t st);
 hipError_t launch_route(const Shape& s, const float* bias, int64_t T, const Work& ws,

@@ -60,6 +60,7 @@ struct RouteArgs {
 };
 
 constexpr int kRouteSlots = 4;      // E <= 4 slots x 4 wavefronts x 64 lanes = 1024
+constexpr int kMaxZPlanes = 8;      // partial logit planes of the router launch
 constexpr int kMaxK = 64;
 
 __device__ __forceinline__ void block_route_token(const RouteArgs& a, int64_t t, uint64_t* cand_key,
@@ -69,23 +70,28 @@ __device__ __forceinline__ void block_route_token(const RouteArgs& a, int64_t t,
   const int wv = threadIdx.x >> 6;
   uint64_t key[kRouteSlots];
   float sv[kRouteSlots];
+  // every logit plane and bias value of this lane's experts in flight at once
   float* zr = a.z + t * a.E;
-  float zv[kRouteSlots];
+  float zp[kRouteSlots][kMaxZPlanes], bv[kRouteSlots];
 #pragma unroll
   for (int i = 0; i < kRouteSlots; ++i) {
     const int e = (i * kWavesPerBlock + wv) * kWave + lane;
-    float v = 0.f;
-    if (e < a.E)
-      for (int p = 0; p < a.zplanes; ++p) v += zr[p * a.zplane + e];
-    zv[i] = v;
+    const bool ok = e < a.E;
+#pragma unroll
+    for (int p = 0; p < kMaxZPlanes; ++p)
+      zp[i][p] = (ok && p < a.zplanes) ? zr[p * a.zplane + e] : 0.f;
+    bv[i] = ok ? a.bias[e] : 0.f;
   }
 #pragma unroll
   for (int i = 0; i < kRouteSlots; ++i) {
     const int e = (i * kWavesPerBlock + wv) * kWave + lane;
+    float zv = 0.f;
+#pragma unroll
+    for (int p = 0; p < kMaxZPlanes; ++p) zv += zp[i][p];   // plane order; absent planes add 0
     if (e < a.E) {
-      if (a.zplanes > 1) zr[e] = zv[i];   // the logits themselves, for inspection
-      const float s = sigmoidf_(zv[i]);
-      float kk = s + a.bias[e];
+      if (a.zplanes > 1) zr[e] = zv;   // the logits themselves, for inspection
+      const float s = sigmoidf_(zv);
+      float kk = s + bv[i];
       if (kk != kk) kk = -INFINITY;
       sv[i] = s;
       key[i] = ((uint64_t)float_order_key(kk) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
@@ -566,20 +572,20 @@ __device__ __forceinline__ float from_gate_lane(float v) {
 // ------------------------------------------------------------------------------------
 // Steps ROUTER and IN: the three products with the token as input, over the packed IN
 // matrix [router ; W_down_latent ; shared gate/up]: z = x W_r^T, x^c = x W_down^T and
-// h_s = act(x W_sg^T, x W_su^T).  A workgroup stages up to ntb tokens (bf16 rows).
-//   ROUTER launch: each workgroup one K-range (1/zplanes of K) of one router tile row,
-//     its 4 wavefronts splitting the range, written as a partial plane of z; many small
-//     workgroups spread the 2% of the bytes over the whole chip.
-//   IN launch: W_down_latent and the shared gate/up, 4/ksplit tile rows per workgroup,
-//     K split between ksplit wavefronts; with few tokens workgroup 0 meanwhile sums the
-//     logit planes of the ROUTER launch and takes the route and the dispatch.
+// h_s = act(x W_sg^T, x W_su^T).  A launch covers a range of tile rows, 4/ksplit tile
+// rows per workgroup with K split between ksplit wavefronts, a workgroup staging up to
+// ntb tokens (bf16 rows).  The ROUTER launch takes the router (as partial logit planes
+// over ranges of K, see in_body) and W_down_latent; the IN launch the shared gate/up,
+// and with few tokens its workgroup 0 meanwhile takes the route and the dispatch from the
+// logits of the ROUTER launch (hidden behind the stream of the shared weights, which do
+// not depend on the route).
 // ------------------------------------------------------------------------------------
 struct InArgs {
   const uint8_t* w;
   int ks, tr_r, tr_dn, tr_sh, ksplit, ntb;
-  int router;                 // 1: ROUTER launch, 0: IN launch
+  int router_wgs, zplanes;    // router K-range workgroups first (per token block) ...
+  int tr_first, tr_count;     // ... then the tile rows [tr_first, tr_first + tr_count)
   int wg_per_blk;             // workgroups per token block (route workgroup excluded)
-  int zplanes;
   const uint16_t* x;
   int64_t T;
   int d;
@@ -600,7 +606,7 @@ __device__ __forceinline__ void in_body(const InArgs& a) {
   __shared__ f32x4_t part[kWavesPerBlock][kWave];
   if (a.route) {
     // the logits come from the ROUTER launch; this workgroup's selection runs while the
-    // others stream the latent and shared weights
+    // others stream the shared weights
     if (blockIdx.x == 0) {
       route_block(a.ra, 0, a.T, true);
       return;
@@ -613,9 +619,12 @@ __device__ __forceinline__ void in_body(const InArgs& a) {
   const int blk = bid / a.wg_per_blk, wgi = bid - blk * a.wg_per_blk;
   const int64_t t0 = (int64_t)blk * a.ntb;
   const int nt = (int)min((int64_t)a.ntb, a.T - t0);
+  const bool router = wgi < a.router_wgs;
   int tr, kp, ksplit, q0, q1;
-  if (a.router) {
-    // tile row wgi / zplanes, K-range plane wgi % zplanes split over the 4 wavefronts
+  if (router) {
+    // router tile row wgi / zplanes, K-range plane wgi % zplanes split over the 4
+    // wavefronts: many small workgroups, so that the router's 2% of the bytes spread over
+    // the whole chip; the route sums the planes
     tr = wgi / a.zplanes;
     const int plane = wgi - tr * a.zplanes;
     const int qpp = cdiv(a.ks, a.zplanes);
@@ -626,18 +635,17 @@ __device__ __forceinline__ void in_body(const InArgs& a) {
     q0 = min(r1, r0 + wv * qw);
     q1 = min(r1, q0 + qw);
   } else {
-    const int slot = wgi * kWavesPerBlock + wv;
+    const int slot = (wgi - a.router_wgs) * kWavesPerBlock + wv;
     ksplit = a.ksplit;
     tr = slot / ksplit;
     kp = slot - tr * ksplit;
-    tr += a.tr_r;
+    tr = tr < a.tr_count ? a.tr_first + tr : INT_MAX;
     const int qper = cdiv(a.ks, ksplit);
     q0 = min(a.ks, kp * qper);
     q1 = min(a.ks, q0 + qper);
   }
-  const int tr_end = a.router ? a.tr_r : a.tr_r + a.tr_dn + a.tr_sh;
-  const bool live = tr < tr_end && q1 > q0;
-  const uint8_t* trow = a.w + (size_t)tr * a.ks * kBf16StepBytes;
+  const bool live = tr != INT_MAX && q1 > q0;
+  const uint8_t* trow = a.w + (size_t)(live ? tr : 0) * a.ks * kBf16StepBytes;
   TileStream<0, 3> ts;
   if (live) ts.prefetch(trow, q0, q1 - q0);
   stage_bf16(sm, a.x + t0 * a.d, a.d, nt, a.d, a.ks);
@@ -645,9 +653,9 @@ __device__ __forceinline__ void in_body(const InArgs& a) {
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   if (live) acc = run_tile_row_n<0, 3>(ts, trow, q0, q1 - q0, sm, g * nt + c % nt, nt);
   acc = reduce_ksplit(acc, part, ksplit, kp);
-  if (tr < tr_end && kp == 0) {
+  if (tr != INT_MAX && kp == 0) {
     // D row 4g + v = token 4g + v of the block, column c = weight row 16 tr + c
-    if (a.router) {
+    if (router) {
       const int e = 16 * tr + c;
       float* zp = a.z + (int64_t)(wgi - tr * a.zplanes) * a.T * a.E;
 #pragma unroll
@@ -670,7 +678,7 @@ __device__ __forceinline__ void in_body(const InArgs& a) {
   }
 }
 
-// Two entry points over the same body so that profilers tell the launches apart.
+// Entry points over the same body so that profilers tell the launches apart.
 __global__ __launch_bounds__(kBlock) void k_router(InArgs a) { in_body(a); }
 __global__ __launch_bounds__(kBlock) void k_in(InArgs a) { in_body(a); }
 
@@ -947,14 +955,19 @@ int choose_ksplit(int64_t tile_rows, int ks) {
 
 namespace {
 
-InArgs in_args(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T, const Work& ws) {
+InArgs in_args(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T, const Work& ws,
+               int tr_first, int tr_count) {
   InArgs a;
   a.w = dense;
   a.ks = s.ks_in;
   a.tr_r = s.tr_r; a.tr_dn = s.tr_dn; a.tr_sh = s.tr_sh;
-  a.zplanes = s.zplanes;
   a.ntb = in_tokens_per_block(s);
-  a.ksplit = choose_ksplit(s.tr_dn + s.tr_sh, s.ks_in);
+  a.ksplit = choose_ksplit(s.tr_in, s.ks_in);
+  a.router_wgs = 0;
+  a.zplanes = s.zplanes;
+  a.tr_first = tr_first;
+  a.tr_count = tr_count;
+  a.wg_per_blk = cdiv((int64_t)tr_count * a.ksplit, kWavesPerBlock);
   a.x = x; a.T = T; a.d = s.d;
   a.z = ws.z; a.E = s.E;
   a.xc = ws.xc; a.l = s.l;
@@ -964,13 +977,17 @@ InArgs in_args(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t 
   return a;
 }
 
+// Shared gate/up tile rows of the IN launch: all of them, the streaming that hides the
+// route of a few tokens.
+int in_launch_shared_rows(const Shape& s) { return s.tr_sh; }
+
 }  // namespace
 
 hipError_t launch_router(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,
-                         const Work& ws, hipStream_t st) {
-  InArgs a = in_args(s, dense, x, T, ws);
-  a.router = 1;
-  a.wg_per_blk = s.tr_r * s.zplanes;
+                         bool router_only, const Work& ws, hipStream_t st) {
+  InArgs a = in_args(s, dense, x, T, ws, s.tr_r, router_only ? 0 : s.tr_dn);
+  a.router_wgs = s.tr_r * s.zplanes;
+  a.wg_per_blk += a.router_wgs;
   const int64_t nblk = (T + a.ntb - 1) / a.ntb;
   const size_t lds = (size_t)(T < a.ntb ? T : a.ntb) * s.ks_in * kStepK * 2;
   hipLaunchKernelGGL(k_router, dim3((unsigned)(nblk * a.wg_per_blk)), dim3(kBlock), lds, st, a);
@@ -979,14 +996,15 @@ hipError_t launch_router(const Shape& s, const uint8_t* dense, const uint16_t* x
 
 hipError_t launch_in(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,
                      const float* bias, int32_t* idx, float* gw, const Work& ws, hipStream_t st) {
-  InArgs a = in_args(s, dense, x, T, ws);
-  a.router = 0;
-  a.wg_per_blk = cdiv((int64_t)(s.tr_dn + s.tr_sh) * a.ksplit, kWavesPerBlock);
+  const int n_tr = in_launch_shared_rows(s);
+  InArgs a = in_args(s, dense, x, T, ws, s.tr_in - n_tr, n_tr);
   a.route = route_fused(s, T) ? 1 : 0;
   a.ra = route_args(s, bias, T, ws, idx, gw);
   const int64_t nblk = (T + a.ntb - 1) / a.ntb;
+  const int64_t grid = nblk * a.wg_per_blk + a.route;
+  if (grid == 0) return hipSuccess;   // no shared expert and a separate route
   const size_t lds = (size_t)(T < a.ntb ? T : a.ntb) * s.ks_in * kStepK * 2;
-  hipLaunchKernelGGL(k_in, dim3((unsigned)(nblk * a.wg_per_blk + a.route)), dim3(kBlock), lds, st, a);
+  hipLaunchKernelGGL(k_in, dim3((unsigned)grid), dim3(kBlock), lds, st, a);
   return hipGetLastError();
 }
 
@@ -1032,10 +1050,13 @@ hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_
   a.out = gu ? ws.h : ws.eo;
   a.n_out = gu ? s.m : s.l;
   a.act = s.act; a.bg = s.beta_gate; a.bl = s.beta_lin;
-  a.ksplit = choose_ksplit((int64_t)s.k * a.n_tr, a.ks);
-  a.wg_per_unit = cdiv((int64_t)a.n_tr * a.ksplit, kWavesPerBlock);
+  // one wavefront per tile row and its whole K range (the per-item staging and the
+  // cross-wavefront sum cost more than a K-split gains), the workgroups walking the
+  // items with a grid stride over about 4 workgroups per CU
+  a.ksplit = 1;
+  a.wg_per_unit = cdiv(a.n_tr, kWavesPerBlock);
   const int64_t items = (int64_t)a.max_units * a.wg_per_unit;
-  const unsigned grid = (unsigned)(items < 8192 ? items : 8192);
+  const unsigned grid = (unsigned)(items < 1024 ? items : 1024);
   const size_t lds = (size_t)2 * a.nu * a.ks * kStepK * 2;
   if (s.wfmt == 1) {
     if (gu) hipLaunchKernelGGL((k_exp<1, true>), dim3(grid), dim3(kBlock), lds, st, a);
