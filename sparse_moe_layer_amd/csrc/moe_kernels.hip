@@ -569,6 +569,23 @@ __device__ __forceinline__ float from_gate_lane(float v) {
   return __uint_as_float(dpp_u32<kDppRowShr8, 0xF, true>(0u, __float_as_uint(v)));
 }
 
+// Workgroups go round-robin to the 8 XCDs (each with its own L2).  A launch over
+// n_groups x n_blk items (tile-row groups x token blocks) maps workgroup bid to the item
+// so that all token blocks of one group run on one XCD, back to back: the group's
+// weights come from HBM once and from that XCD's L2 for the other blocks.  The launch has
+// 8 * ceil(n_groups / 8) * n_blk workgroups; the padding ones return false.
+constexpr int kXcds = 8;
+__device__ __forceinline__ bool xcd_item(int bid, int n_groups, int n_blk, int& grp, int& blk) {
+  const int x = bid % kXcds, j = bid / kXcds;
+  const int gi = j / n_blk;
+  blk = j - gi * n_blk;
+  grp = x + kXcds * gi;
+  return grp < n_groups;
+}
+inline int64_t xcd_grid(int64_t n_groups, int64_t n_blk) {
+  return kXcds * ((n_groups + kXcds - 1) / kXcds) * n_blk;
+}
+
 // ------------------------------------------------------------------------------------
 // Steps ROUTER and IN: the three products with the token as input, over the packed IN
 // matrix [router ; W_down_latent ; shared gate/up]: z = x W_r^T, x^c = x W_down^T and
@@ -586,6 +603,7 @@ struct InArgs {
   int router_wgs, zplanes;    // router K-range workgroups first (per token block) ...
   int tr_first, tr_count;     // ... then the tile rows [tr_first, tr_first + tr_count)
   int wg_per_blk;             // workgroups per token block (route workgroup excluded)
+  int n_blk;                  // token blocks
   const uint16_t* x;
   int64_t T;
   int d;
@@ -616,7 +634,8 @@ __device__ __forceinline__ void in_body(const InArgs& a) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int bid = blockIdx.x - a.route;
-  const int blk = bid / a.wg_per_blk, wgi = bid - blk * a.wg_per_blk;
+  int wgi, blk;
+  if (!xcd_item(bid, a.wg_per_blk, a.n_blk, wgi, blk)) return;
   const int64_t t0 = (int64_t)blk * a.ntb;
   const int nt = (int)min((int64_t)a.ntb, a.T - t0);
   const bool router = wgi < a.router_wgs;
@@ -715,13 +734,15 @@ __global__ __launch_bounds__(kBlock) void k_exp(ExpArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
+  // one (tile-row group, unit) item per workgroup, the units of a group on one XCD in
+  // unit order (so that the units of one expert reuse its weights from that L2)
   const int n_units = min(a.ctrl[0], a.max_units);
-  const int64_t items = (int64_t)n_units * a.wg_per_unit;
-  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
-    const int u = (int)(item / a.wg_per_unit), wgi = (int)(item - (int64_t)u * a.wg_per_unit);
+  int wgi, u;
+  if (!xcd_item(blockIdx.x, a.wg_per_unit, a.max_units, wgi, u) || u >= n_units) return;
+  {
     const int4 un = *reinterpret_cast<const int4*>(a.units + 4 * u);
     const int e = un.x, p0 = un.y, n = un.z;
-    if (e < 0 || e >= a.E || n < 1 || n > a.nu || p0 < 0 || p0 + n > a.n_assign) continue;
+    if (e < 0 || e >= a.E || n < 1 || n > a.nu || p0 < 0 || p0 + n > a.n_assign) return;
     const int nr = 2 * n;
     const int slot = wgi * kWavesPerBlock + wv;
     const int tr = slot / a.ksplit, kp = slot - tr * a.ksplit;
@@ -732,7 +753,6 @@ __global__ __launch_bounds__(kBlock) void k_exp(ExpArgs a) {
                           (size_t)tr * a.ks * (WF ? kFp4StepBytes : kBf16StepBytes);
     TileStream<WF, WF ? 4 : 3> ts;
     if (live) ts.prefetch(trow, q0, q1 - q0);
-    __syncthreads();  // the previous item's LDS reads are done
     if ((int)threadIdx.x < n) {
       const int p = p0 + threadIdx.x;
       int64_t src = p;
@@ -777,7 +797,7 @@ __global__ __launch_bounds__(kBlock) void k_exp(ExpArgs a) {
 // ------------------------------------------------------------------------------------
 struct OutArgs {
   const uint8_t* w;
-  int ks, ks_l, n_tr, ksplit, wg_per_blk, ntb;
+  int ks, ks_l, n_tr, ksplit, wg_per_blk, ntb, n_blk;
   const float* u;
   const float* hs;
   const uint16_t* gamma;
@@ -797,7 +817,8 @@ __global__ __launch_bounds__(kBlock) void k_out(OutArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
-  const int blk = blockIdx.x / a.wg_per_blk, wgi = blockIdx.x - blk * a.wg_per_blk;
+  int wgi, blk;
+  if (!xcd_item(blockIdx.x, a.wg_per_blk, a.n_blk, wgi, blk)) return;
   const int64_t t0 = (int64_t)blk * a.ntb;
   const int nt = (int)min((int64_t)a.ntb, a.T - t0);
   const int slot = wgi * kWavesPerBlock + wv;
@@ -968,6 +989,7 @@ InArgs in_args(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t 
   a.tr_first = tr_first;
   a.tr_count = tr_count;
   a.wg_per_blk = cdiv((int64_t)tr_count * a.ksplit, kWavesPerBlock);
+  a.n_blk = cdiv(T, a.ntb);
   a.x = x; a.T = T; a.d = s.d;
   a.z = ws.z; a.E = s.E;
   a.xc = ws.xc; a.l = s.l;
@@ -988,9 +1010,9 @@ hipError_t launch_router(const Shape& s, const uint8_t* dense, const uint16_t* x
   InArgs a = in_args(s, dense, x, T, ws, s.tr_r, router_only ? 0 : s.tr_dn);
   a.router_wgs = s.tr_r * s.zplanes;
   a.wg_per_blk += a.router_wgs;
-  const int64_t nblk = (T + a.ntb - 1) / a.ntb;
   const size_t lds = (size_t)(T < a.ntb ? T : a.ntb) * s.ks_in * kStepK * 2;
-  hipLaunchKernelGGL(k_router, dim3((unsigned)(nblk * a.wg_per_blk)), dim3(kBlock), lds, st, a);
+  hipLaunchKernelGGL(k_router, dim3((unsigned)xcd_grid(a.wg_per_blk, a.n_blk)), dim3(kBlock), lds,
+                     st, a);
   return hipGetLastError();
 }
 
@@ -1000,8 +1022,7 @@ hipError_t launch_in(const Shape& s, const uint8_t* dense, const uint16_t* x, in
   InArgs a = in_args(s, dense, x, T, ws, s.tr_in - n_tr, n_tr);
   a.route = route_fused(s, T) ? 1 : 0;
   a.ra = route_args(s, bias, T, ws, idx, gw);
-  const int64_t nblk = (T + a.ntb - 1) / a.ntb;
-  const int64_t grid = nblk * a.wg_per_blk + a.route;
+  const int64_t grid = (a.wg_per_blk > 0 ? xcd_grid(a.wg_per_blk, a.n_blk) : 0) + a.route;
   if (grid == 0) return hipSuccess;   // no shared expert and a separate route
   const size_t lds = (size_t)(T < a.ntb ? T : a.ntb) * s.ks_in * kStepK * 2;
   hipLaunchKernelGGL(k_in, dim3((unsigned)grid), dim3(kBlock), lds, st, a);
@@ -1051,12 +1072,10 @@ hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_
   a.n_out = gu ? s.m : s.l;
   a.act = s.act; a.bg = s.beta_gate; a.bl = s.beta_lin;
   // one wavefront per tile row and its whole K range (the per-item staging and the
-  // cross-wavefront sum cost more than a K-split gains), the workgroups walking the
-  // items with a grid stride over about 4 workgroups per CU
+  // cross-wavefront sum cost more than a K-split gains)
   a.ksplit = 1;
   a.wg_per_unit = cdiv(a.n_tr, kWavesPerBlock);
-  const int64_t items = (int64_t)a.max_units * a.wg_per_unit;
-  const unsigned grid = (unsigned)(items < 1024 ? items : 1024);
+  const unsigned grid = (unsigned)xcd_grid(a.wg_per_unit, a.max_units);
   const size_t lds = (size_t)2 * a.nu * a.ks * kStepK * 2;
   if (s.wfmt == 1) {
     if (gu) hipLaunchKernelGGL((k_exp<1, true>), dim3(grid), dim3(kBlock), lds, st, a);
@@ -1083,7 +1102,7 @@ hipError_t launch_out(const Shape& s, const uint8_t* dense, int64_t T, const Wor
   a.ks = s.ks_out; a.ks_l = s.ks_l;
   a.n_tr = s.tr_out;
   a.ntb = out_tokens_per_block(s);   // 2 * ntb hi/lo rows: at most one 16-row MFMA block
-  const int64_t nblk = (T + a.ntb - 1) / a.ntb;
+  a.n_blk = cdiv(T, a.ntb);
   a.ksplit = choose_ksplit(s.tr_out, s.ks_out);
   a.wg_per_blk = cdiv((int64_t)a.n_tr * a.ksplit, kWavesPerBlock);
   a.u = ws.u; a.hs = ws.hs;
@@ -1091,7 +1110,8 @@ hipError_t launch_out(const Shape& s, const uint8_t* dense, int64_t T, const Wor
   a.d = s.d; a.l = s.l; a.ms = s.ms; a.norm = s.use_norm; a.eps = s.eps;
   a.T = T; a.delta = delta;
   const size_t lds = (size_t)2 * (T < a.ntb ? T : a.ntb) * s.ks_out * kStepK * 2;
-  hipLaunchKernelGGL(k_out, dim3((unsigned)(nblk * a.wg_per_blk)), dim3(kBlock), lds, st, a);
+  hipLaunchKernelGGL(k_out, dim3((unsigned)xcd_grid(a.wg_per_blk, a.n_blk)), dim3(kBlock), lds, st,
+                     a);
   return hipGetLastError();
 }
 

@@ -204,6 +204,27 @@ def test_k3_decode_b64_sampled_tokens():
     assert np.array_equal(i1[0], idx[21]) and np.array_equal(d1[0], delta[21])
 
 
+def test_k3_decode_b64_zipf_layer():
+    """The Zipf-loaded B=64 layer: two experts take every token, so their 64 positions
+    are split over several units of the expert launches, next to many single-token units."""
+    cfg = synth.K3_DECODE_B64_ZIPF
+    lay, _ = device_layer(cfg)
+    x = synth.tokens(cfg, batch=1000)
+    log(f"[k3 zipf] T={x.shape[0]}")
+    delta, idx, w = run(lay, x)
+    OL = oracle_layer(cfg)
+    s = O.router_scores(O.bf16_to_f64(x), OL.router)
+    ridx, G, margin = O.select_and_weight(s, OL.bias, cfg.k)
+    clear = margin >= MARGIN
+    assert np.array_equal(idx[clear], ridx[clear])
+    load = np.bincount(idx.reshape(-1), minlength=cfg.E)
+    assert int((load == x.shape[0]).sum()) == 2
+    log(f"[k3 zipf] distinct experts {int((load > 0).sum())}")
+    check(cfg, x, delta, idx, w, rows=[0, 31, 63])
+    d1, i1, w1 = run(lay, x[31:32])
+    assert np.array_equal(i1[0], idx[31]) and np.array_equal(d1[0], delta[31])
+
+
 def test_step_ranges_and_timed_forward_match_the_forward():
     cfg = TINY.with_(tokens=3)
     lay, _ = device_layer(TINY)
