@@ -168,15 +168,20 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t max_tokens, size_t*
  *   [3] h      [T*k][m] fp32     routed expert hidden, rows in dispatch order
  *   [4] E      [T*k][l] fp32     routed expert outputs, rows in dispatch order
  *   [5] u      [T][l]   fp32     gated latent sum before the norm
- *   [6] perm   [T*k]    int32    dispatch order -> assignment t*k+j
- *   [7] inv    [T*k]    int32    assignment -> dispatch order
- *   [8] counts [E]      int32    assignments per expert
- *   [9] offsets[E+1]    int32    exclusive scan of counts
- *  [10] z      [P][T][E] fp32   router logits as P partial planes over ranges of d (their
+ *   [6] u_hat  [T][l]   fp32     RMSNorm(u) * gamma (written for batches that take the
+ *                                token-tiled launches, see moe_step)
+ *   [7] hi/lo  bf16 row pairs (hi = bf16(v), lo = bf16(v - hi)) of x^c [T][2][l], h_s
+ *                                [T][2][m_s], h [T*k][2][m] and u_hat [T][2][l], each part
+ *                                256-aligned (token-tiled launches; internal)
+ *   [8] perm   [T*k]    int32    dispatch order -> assignment t*k+j
+ *   [9] inv    [T*k]    int32    assignment -> dispatch order
+ *  [10] counts [E]      int32    assignments per expert
+ *  [11] offsets[E+1]    int32    exclusive scan of counts
+ *  [12] z      [P][T][E] fp32   router logits as P partial planes over ranges of d (their
  *                                sum); after the route, plane 0 holds the logits
- *  [11] per-chunk expert histograms of the dispatch (internal)
- *  [12] unit table of the expert launches (internal) */
-#define MOE_WS_NUM_SLOTS 13
+ *  [13] per-chunk expert histograms of the dispatch (internal)
+ *  [14] unit table of the expert launches (internal) */
+#define MOE_WS_NUM_SLOTS 15
 moe_status moe_workspace_layout(const moe_config* cfg, int64_t n_tokens,
                                 size_t offsets[MOE_WS_NUM_SLOTS]);
 
@@ -194,20 +199,24 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const 
                              float* topk_w, void* workspace, size_t workspace_bytes,
                              moe_stream_t stream);
 
-/* Steps of the forward, in launch order. */
+/* Steps of the forward, in launch order.  With few tokens (at most 4, fewer for very
+ * wide d) each product stages all its activation rows at once; larger batches take
+ * token-tiled launches (tiles of up to 64 tokens or 32 assignments of one expert, the
+ * weights read once per tile) whose sums follow the same order, so a token's results
+ * have the same bits in both.  Where the two differ it is said below. */
 typedef enum moe_step {
   MOE_STEP_ROUTER = 0,      /* router logits z = x W_r (partial planes), and in the same
-                               launch x^c = x W_down_latent */
-  MOE_STEP_IN = 1,          /* shared gate/up + SiTU; with few tokens (at most 4, fewer for
-                               very wide d) one workgroup of the same launch also takes the
-                               top-k, the gate weights and the dispatch */
+                               launch x^c = x W_down_latent (larger batches: in IN) */
+  MOE_STEP_IN = 1,          /* shared gate/up + SiTU; with few tokens one workgroup of the
+                               same launch also takes the top-k, the gate weights and the
+                               dispatch */
   MOE_STEP_ROUTE = 2,       /* sigmoid, top_k(s + b), gate weights (larger batches; launches
                                nothing otherwise) */
   MOE_STEP_DISPATCH = 3,    /* histogram, scan, stable permutation by expert (larger
                                batches; launches nothing otherwise) */
   MOE_STEP_EXPERT_GU = 4,   /* routed gate/up + SiTU */
   MOE_STEP_EXPERT_DOWN = 5, /* routed down */
-  MOE_STEP_COMBINE = 6,     /* u = sum_j G_j E_j */
+  MOE_STEP_COMBINE = 6,     /* u = sum_j G_j E_j (larger batches: and u_hat) */
   MOE_STEP_OUT = 7,         /* Delta = RMSNorm(u) W_up_latent + h_s W_shared_down */
   MOE_NUM_STEPS = 8
 } moe_step;

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 ACT = {"situ": 0, "swiglu": 1}
 WFMT = {"bf16": 0, "mxfp4": 1}
-WS_SLOTS = ("ctrl", "xc", "hs", "h", "eo", "u", "perm", "inv", "counts", "offsets", "z",
+WS_SLOTS = ("ctrl", "xc", "hs", "h", "eo", "u", "uh", "hl", "perm", "inv", "counts", "offsets", "z",
             "chunk_hist", "units")
 
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_packed_dense_size", "moe_pack_dense",
@@ -322,6 +322,7 @@ class Layer:
         T, k = n_tokens, c.top_k
         shapes = {"ctrl": (64,), "xc": (T, c.d_latent), "hs": (T, c.d_shared),
                   "h": (T * k, c.d_expert), "eo": (T * k, c.d_latent), "u": (T, c.d_latent),
+                  "uh": (T, c.d_latent),
                   "perm": (T * k,), "inv": (T * k,), "counts": (c.n_experts,),
                   "offsets": (c.n_experts + 1,), "z": (T, c.n_experts)}
         out = {}

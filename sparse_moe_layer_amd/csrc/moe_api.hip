@@ -73,6 +73,18 @@ moe_status make_shape(const moe_config* c, Shape* s) {
   return MOE_OK;
 }
 
+// The hi/lo slot: x^c, h_s, h and u_hat as bf16 row pairs, each part 256-aligned.
+size_t hilo_part(const Shape& s, int64_t T, int part) {
+  const int64_t rows[4] = {T, T, T * s.k, T};
+  const int64_t width[4] = {s.l, s.ms, s.m, s.l};
+  return align256((size_t)rows[part] * 2 * width[part] * 2);
+}
+size_t hilo_bytes(const Shape& s, int64_t T) {
+  size_t n = 0;
+  for (int i = 0; i < 4; ++i) n += hilo_part(s, T, i);
+  return n;
+}
+
 // Workspace slots in the order of moe_workspace_layout.
 void layout(const Shape& s, int64_t T, size_t off[MOE_WS_NUM_SLOTS], size_t* total) {
   const int64_t tk = T * s.k;
@@ -84,6 +96,8 @@ void layout(const Shape& s, int64_t T, size_t off[MOE_WS_NUM_SLOTS], size_t* tot
       (size_t)tk * s.m * 4,                 // h
       (size_t)tk * s.l * 4,                 // E
       (size_t)T * s.l * 4,                  // u
+      (size_t)T * s.l * 4,                  // u_hat
+      hilo_bytes(s, T),                     // hi/lo rows of the token-tiled launches
       (size_t)tk * 4,                       // perm
       (size_t)tk * 4,                       // inv
       (size_t)s.E * 4,                      // counts
@@ -100,7 +114,7 @@ void layout(const Shape& s, int64_t T, size_t off[MOE_WS_NUM_SLOTS], size_t* tot
   *total = o;
 }
 
-moe::Work make_work(void* ws, const size_t off[MOE_WS_NUM_SLOTS]) {
+moe::Work make_work(const Shape& s, int64_t T, void* ws, const size_t off[MOE_WS_NUM_SLOTS]) {
   char* b = static_cast<char*>(ws);
   moe::Work w;
   w.ctrl = reinterpret_cast<int32_t*>(b + off[0]);
@@ -109,13 +123,22 @@ moe::Work make_work(void* ws, const size_t off[MOE_WS_NUM_SLOTS]) {
   w.h = reinterpret_cast<float*>(b + off[3]);
   w.eo = reinterpret_cast<float*>(b + off[4]);
   w.u = reinterpret_cast<float*>(b + off[5]);
-  w.perm = reinterpret_cast<int32_t*>(b + off[6]);
-  w.inv = reinterpret_cast<int32_t*>(b + off[7]);
-  w.counts = reinterpret_cast<int32_t*>(b + off[8]);
-  w.offs = reinterpret_cast<int32_t*>(b + off[9]);
-  w.z = reinterpret_cast<float*>(b + off[10]);
-  w.chunk_hist = reinterpret_cast<int32_t*>(b + off[11]);
-  w.units = reinterpret_cast<int32_t*>(b + off[12]);
+  w.uh = reinterpret_cast<float*>(b + off[6]);
+  {
+    char* p = b + off[7];
+    uint16_t** parts[4] = {&w.xc_hl, &w.hs_hl, &w.h_hl, &w.uh_hl};
+    for (int i = 0; i < 4; ++i) {
+      *parts[i] = reinterpret_cast<uint16_t*>(p);
+      p += hilo_part(s, T, i);
+    }
+  }
+  w.perm = reinterpret_cast<int32_t*>(b + off[8]);
+  w.inv = reinterpret_cast<int32_t*>(b + off[9]);
+  w.counts = reinterpret_cast<int32_t*>(b + off[10]);
+  w.offs = reinterpret_cast<int32_t*>(b + off[11]);
+  w.z = reinterpret_cast<float*>(b + off[12]);
+  w.chunk_hist = reinterpret_cast<int32_t*>(b + off[13]);
+  w.units = reinterpret_cast<int32_t*>(b + off[14]);
   return w;
 }
 
@@ -254,7 +277,7 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const float
   if ((st = check_call(s, w, bias, x, n_tokens, workspace, workspace_bytes, off)) != MOE_OK) return st;
   if (!delta || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
   if (!aligned(delta, 16) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_ERR_INVALID_ARG;
-  const moe::Work ws = make_work(workspace, off);
+  const moe::Work ws = make_work(s, n_tokens, workspace, off);
   const uint8_t* dense = static_cast<const uint8_t*>(w->dense);
   const uint8_t* experts = static_cast<const uint8_t*>(w->experts);
   hipStream_t hs = (hipStream_t)stream;
@@ -279,7 +302,7 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const float
         break;
       case MOE_STEP_EXPERT_GU: e = moe::launch_expert(s, experts, true, n_tokens, ws, hs); break;
       case MOE_STEP_EXPERT_DOWN: e = moe::launch_expert(s, experts, false, n_tokens, ws, hs); break;
-      case MOE_STEP_COMBINE: e = moe::launch_combine(s, topk_w, n_tokens, ws, hs); break;
+      case MOE_STEP_COMBINE: e = moe::launch_combine(s, dense, topk_w, n_tokens, ws, hs); break;
       case MOE_STEP_OUT: e = moe::launch_out(s, dense, n_tokens, ws, delta, hs); break;
     }
     if (e != hipSuccess) return MOE_ERR_HIP;
@@ -332,7 +355,7 @@ MOE_EXPORT moe_status moe_route(const moe_config* cfg, const moe_weights* w, con
   size_t off[MOE_WS_NUM_SLOTS];
   if ((st = check_call(s, w, bias, x, n_tokens, workspace, workspace_bytes, off)) != MOE_OK) return st;
   if (!topk_idx || !topk_w || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_ERR_INVALID_ARG;
-  const moe::Work ws = make_work(workspace, off);
+  const moe::Work ws = make_work(s, n_tokens, workspace, off);
   hipStream_t hs = (hipStream_t)stream;
   if (moe::launch_router(s, static_cast<const uint8_t*>(w->dense), static_cast<const uint16_t*>(x),
                          n_tokens, true, ws, hs) != hipSuccess)
@@ -353,7 +376,7 @@ MOE_EXPORT moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_id
   size_t off[MOE_WS_NUM_SLOTS], need;
   layout(s, n_tokens, off, &need);
   if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
-  const moe::Work ws = make_work(workspace, off);
+  const moe::Work ws = make_work(s, n_tokens, workspace, off);
   return hip_status(moe::launch_dispatch(s, topk_idx, n_tokens, counts, offsets, perm, inv,
                                          ws.chunk_hist, ws.units, ws.ctrl, (hipStream_t)stream));
 }

@@ -45,6 +45,12 @@ struct Work {
   float* h;        // [T*k][m]   dispatch order
   float* eo;       // [T*k][l]   dispatch order
   float* u;        // [T][l]
+  float* uh;       // [T][l]     RMSNorm(u) * gamma (token-tiled launches)
+  // token-tiled launches: fp32 activations as bf16 hi/lo row pairs [rows][2][width]
+  uint16_t* xc_hl; // [T][2][l]
+  uint16_t* hs_hl; // [T][2][ms]
+  uint16_t* h_hl;  // [T*k][2][m]
+  uint16_t* uh_hl; // [T][2][l]
   int32_t* perm;   // [T*k]
   int32_t* inv;    // [T*k]
   int32_t* counts; // [E]
@@ -62,20 +68,23 @@ inline int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v
 // route's own LDS) and of the OUT launch (hi/lo rows of l + m_s columns).
 inline int in_tokens_per_block(const Shape& s) { return clampi(45056 / (s.ks_in * kStepK * 2), 1, 16); }
 inline int out_tokens_per_block(const Shape& s) { return clampi(57344 / (s.ks_out * kStepK * 4), 1, 8); }
+// With this few tokens the route and the dispatch run inside the IN launch, and every
+// product stages all its activation rows at once (the decode launches); larger batches
+// take the token-tiled launches.
+inline bool route_fused(const Shape& s, int64_t T) {
+  return T <= 4 && T * s.k <= kBlock && T <= in_tokens_per_block(s);
+}
+inline bool token_tiled(const Shape& s, int64_t T) { return !route_fused(s, T); }
+constexpr int kTiledUnitPositions = 32;
 // Positions of one expert per unit of the expert launches (2 hi/lo rows each).
 inline int unit_positions(const Shape& s, int64_t T) {
-  const int ks = s.ks_gu > s.ks_edn ? s.ks_gu : s.ks_edn;
-  const int fit = clampi(57344 / (ks * kStepK * 4), 1, 4);
-  return (int)(T < fit ? (T < 1 ? 1 : T) : fit);
+  if (token_tiled(s, T)) return kTiledUnitPositions;
+  return T < 1 ? 1 : (int)T;
 }
 inline int64_t max_units(const Shape& s, int64_t T) {
   const int64_t n = T * s.k, nu = unit_positions(s, T);
   const int64_t b = n / nu + (n < s.E ? n : s.E);
   return b < n ? b : n;
-}
-// With this few tokens the route and the dispatch run inside the IN launch.
-inline bool route_fused(const Shape& s, int64_t T) {
-  return T <= 4 && T * s.k <= kBlock && T <= in_tokens_per_block(s);
 }
 
 // router_only: the router rows alone (otherwise W_down_latent rides in the same launch)
@@ -90,8 +99,9 @@ hipError_t launch_dispatch(const Shape& s, const int32_t* idx, int64_t T, int32_
                            int32_t* units, int32_t* ctrl, hipStream_t st);
 hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_t T,
                          const Work& ws, hipStream_t st);
-hipError_t launch_combine(const Shape& s, const float* gw, int64_t T, const Work& ws,
-                          hipStream_t st);
+// the combine, and for the token-tiled launches the norm
+hipError_t launch_combine(const Shape& s, const uint8_t* dense, const float* gw, int64_t T,
+                          const Work& ws, hipStream_t st);
 hipError_t launch_out(const Shape& s, const uint8_t* dense, int64_t T, const Work& ws,
                       float* delta, hipStream_t st);
 

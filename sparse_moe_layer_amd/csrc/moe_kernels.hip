@@ -393,6 +393,15 @@ __device__ __forceinline__ void split_hilo(const float (&v)[8], uint4& hi, uint4
   lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
+// An fp32 value as the hi/lo bf16 pair the token-tiled launches read: p[0] = hi, p[ld] = lo
+// (the same split as split_hilo).
+__device__ __forceinline__ void store_hilo(uint16_t* p, int64_t ld, float v) {
+  const uint32_t w = pack_bf16x2(v, 0.f);
+  const float h = bf16_lo(w);
+  p[0] = (uint16_t)(w & 0xFFFFu);
+  p[ld] = (uint16_t)(pack_bf16x2(v - h, 0.f) & 0xFFFFu);
+}
+
 // An fp32 activation row for the hi/lo staging: columns [0, n0) from p0 (optionally
 // times scale * gamma[c]), columns [c1, c1 + n1) from p1, zero elsewhere.
 struct HiloRow {
@@ -724,6 +733,10 @@ struct ExpArgs {
   int n_out;
   int act;
   float bg, bl;
+  const uint16_t* xin_hl;   // token-tiled launches: hi/lo input rows [rows][2][kin_ld]
+  int kin_ld;
+  uint16_t* out_hl;         // and the gate/up output's hi/lo rows [T*k][2][out_ld]
+  int out_ld;
 };
 
 template <int WF, bool GU>
@@ -809,6 +822,41 @@ struct OutArgs {
 
 constexpr int kOutMaxTokens = 8;
 
+// 1 / sqrt(mean(row^2) + eps) of an fp32 row, by the whole workgroup (fixed order).
+__device__ __forceinline__ float row_inv_rms(const float* ur, int l, float eps, float* red) {
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x >> 6;
+  float ss = 0.f;
+  for (int col = threadIdx.x * 4; col < l; col += kBlock * 4) {
+    const float4 p = *reinterpret_cast<const float4*>(ur + col);
+    ss = fmaf(p.x, p.x, ss); ss = fmaf(p.y, p.y, ss);
+    ss = fmaf(p.z, p.z, ss); ss = fmaf(p.w, p.w, ss);
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) red[wv] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return 1.0f / sqrtf(tot / (float)l + eps);
+}
+
+// u_hat = u * inv * gamma, one workgroup per token: the same values the OUT launch of a
+// few tokens stages itself (the same reduction and the same products).
+__global__ __launch_bounds__(kBlock) void k_norm(const float* __restrict__ u,
+                                                 const uint16_t* __restrict__ gamma, int l,
+                                                 int norm, float eps, float* __restrict__ uhat,
+                                                 uint16_t* __restrict__ uhat_hl) {
+  __shared__ float red[kWavesPerBlock];
+  const int64_t t = blockIdx.x;
+  const float* ur = u + t * l;
+  const float inv = norm ? row_inv_rms(ur, l, eps, red) : 1.f;
+  for (int col = threadIdx.x; col < l; col += kBlock) {
+    const float gm = norm ? __uint_as_float((uint32_t)gamma[col] << 16) : 1.f;
+    const float v = norm ? ur[col] * inv * gm : ur[col];
+    uhat[t * l + col] = v;
+    store_hilo(uhat_hl + t * 2 * l + col, l, v);
+  }
+}
+
 __global__ __launch_bounds__(kBlock) void k_out(OutArgs a) {
   extern __shared__ uint4 sm[];
   __shared__ f32x4_t part[kWavesPerBlock][kWave];
@@ -831,21 +879,7 @@ __global__ __launch_bounds__(kBlock) void k_out(OutArgs a) {
   if (live) ts.prefetch(trow, q0, q1 - q0);
   for (int i = 0; i < nt; ++i) {
     const float* ur = a.u + (t0 + i) * a.l;
-    float inv = 1.f;
-    if (a.norm) {
-      float ss = 0.f;
-      for (int col = threadIdx.x * 4; col < a.l; col += kBlock * 4) {
-        const float4 p = *reinterpret_cast<const float4*>(ur + col);
-        ss = fmaf(p.x, p.x, ss); ss = fmaf(p.y, p.y, ss);
-        ss = fmaf(p.z, p.z, ss); ss = fmaf(p.w, p.w, ss);
-      }
-      ss = wave_sum(ss);
-      if (lane == 0) red[wv] = ss;
-      __syncthreads();
-      const float tot = (red[0] + red[1]) + (red[2] + red[3]);
-      inv = 1.0f / sqrtf(tot / (float)a.l + a.eps);
-      __syncthreads();
-    }
+    const float inv = a.norm ? row_inv_rms(ur, a.l, a.eps, red) : 1.f;
     if (threadIdx.x == 0) rows[i] = HiloRow{ur, a.hs + (t0 + i) * a.ms, inv};
   }
   __syncthreads();
@@ -863,6 +897,385 @@ __global__ __launch_bounds__(kBlock) void k_out(OutArgs a) {
       if (2 * g + 1 < nt) a.delta[(t0 + 2 * g + 1) * a.d + r] = y1;
     }
   }
+}
+
+// ------------------------------------------------------------------------------------
+// Larger batches: token-tiled products.  A workgroup takes a tile of up to 16*NB
+// activation rows (bf16 tokens, or hi/lo pairs of fp32 rows) and 4 tile rows of weights
+// (one per wavefront) and walks K one K-step at a time: the K-step of the tile's rows is
+// staged in LDS (double buffer, its loads issued a step ahead) and each wavefront
+// multiplies it with its weight K-step, NB MFMA blocks per weight operand, so a weight
+// byte is read once per tile instead of once per token block.  The partial sums follow
+// the K-split of the launches for a few tokens (a running sum over the same K ranges,
+// added in the same order), so a token's result has the same bits in both paths.
+// ------------------------------------------------------------------------------------
+constexpr int kTTMaxSrc = 64;     // activation rows per tile
+
+// The tile's activation rows, bf16 (tokens as they are, fp32 values as hi/lo row pairs
+// written by their producer).  Row r: columns [0, n0) at b0 + 8 o0[r] + col, columns
+// [c1, c1 + n1) at b1 + 8 o1[r] + (col - c1) (offsets in 16-byte words), zero elsewhere
+// and for rows r >= R.
+struct TTRows {
+  uint32_t o0[kTTMaxSrc];
+  uint32_t o1[kTTMaxSrc];
+};
+struct TTSrc {
+  const uint16_t* b0;
+  const uint16_t* b1;
+  int R, n0, c1, n1;
+};
+
+// A ring of P K-steps of the tile's 16 NB rows in registers, each loaded P K-steps ahead
+// of its use and written to the LDS buffer of its K-step one step ahead.  Thread piece i
+// is idx = threadIdx + 256 i: row idx / 16, columns 8 (idx % 16) .. + 8 of the K-step,
+// so that a wavefront reads 4 rows of 256 contiguous bytes.  The rows' offsets are read
+// once; every load is issued (a piece outside the rows reads the first word of b0 and
+// is zeroed when it is committed): no branches, so the waits count the loads in
+// flight exactly.
+template <int P, int NB>
+struct TTStage {
+  uint4 v[P][NB];
+  uint32_t o0[NB], o1[NB];
+  bool rv[NB];
+  __device__ __forceinline__ void init(const TTRows& rows, const TTSrc& src) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int r = (threadIdx.x + i * kBlock) >> 4;
+      rv[i] = r < src.R;
+      o0[i] = rv[i] ? rows.o0[r] : 0u;
+      o1[i] = rv[i] && src.n1 > 0 ? rows.o1[r] : 0u;
+    }
+  }
+  __device__ __forceinline__ bool in0(int i, const TTSrc& src, int col) const {
+    return rv[i] && col < src.n0;
+  }
+  __device__ __forceinline__ bool in1(int i, const TTSrc& src, int col) const {
+    return rv[i] && col >= src.c1 && col < src.c1 + src.n1;
+  }
+  __device__ __forceinline__ int col_of(int i, int q) const {
+    return q * kStepK + 8 * ((threadIdx.x + i * kBlock) & 15);
+  }
+  __device__ __forceinline__ void load(int slot, const TTSrc& src, int q) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int col = col_of(i, q);
+      const bool a0 = in0(i, src, col), a1 = in1(i, src, col);
+      const uint32_t w = a0 ? o0[i] + (col >> 3) : a1 ? o1[i] + ((col - src.c1) >> 3) : 0u;
+      const uint4* base = reinterpret_cast<const uint4*>(a1 ? src.b1 : src.b0);
+#pragma unroll
+      for (int sl = 0; sl < P; ++sl)
+        if (sl == slot) v[sl][i] = base[w];
+    }
+  }
+  // Slot `slot` holds K-step q: the pieces outside the rows are zeroed here, where the
+  // data is needed anyway (a select at the load would wait for it there).  The LDS
+  // buffer holds piece j of row r at word j * 16 NB + (r ^ j): the XOR keeps both these
+  // writes and the MFMA operand reads free of bank conflicts.
+  __device__ __forceinline__ void commit(int slot, uint4* buf, const TTSrc& src, int q) const {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int idx = threadIdx.x + i * kBlock;
+      const int r = idx >> 4, j = idx & 15;
+      const int col = col_of(i, q);
+      const bool z = !(in0(i, src, col) || in1(i, src, col));
+#pragma unroll
+      for (int sl = 0; sl < P; ++sl)
+        if (sl == slot) {
+          const uint4 x = v[sl][i];
+          buf[j * 16 * NB + (r ^ j)] =
+              make_uint4(z ? 0u : x.x, z ? 0u : x.y, z ? 0u : x.z, z ? 0u : x.w);
+        }
+    }
+  }
+};
+
+// The K loop of a tile: D[b] (16 x 16 block b of the tile's rows x this wavefront's tile
+// row) over all ks K-steps.  Sums restart every qper K-steps and the partial sums are
+// added in order (the K-split of the launches for few tokens).  Every wavefront of the
+// workgroup runs it (staging and barriers are shared); trow must be a valid tile row
+// (waves without one pass tile row 0 and drop the result).  The loop runs whole rounds
+// of the P-deep ring: steps past ks re-read the last K-step and are never summed.
+template <int WF, int P, int NB>
+__device__ __forceinline__ void tt_run(const TTRows& rows, const TTSrc& src, const uint8_t* trow,
+                                       int ks, int qper, uint4* lds, f32x4_t (&tot)[NB]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = lane & 15, g = lane >> 4;
+  constexpr int RB = 16 * NB;
+  constexpr int rstride = RB * 16;           // words per buffer (16 pieces x RB rows)
+  TileStream<WF, P> ts;
+  TTStage<P, NB> st;
+  st.init(rows, src);
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    ts.w[i].load(trow, min(i, ks - 1), lane);
+    st.load(i, src, min(i, ks - 1));
+  }
+  asm volatile("" ::: "memory");
+  st.commit(0, lds, src, 0);
+  __syncthreads();
+  f32x4_t cur[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    cur[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    tot[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  bool first = true;
+  int in_part = 0;
+  const int rounds = cdiv(ks, P);
+  for (int j = 0; j < rounds * P; j += P) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int q = j + i;
+      // slot i held K-step q, committed to LDS at the end of the previous step
+      st.load(i, src, min(q + P, ks - 1));
+      const uint4* buf = lds + (q & 1) * rstride;
+      uint4 af[4][NB];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int jj = s4 * 4 + g;
+          af[s4][b] = buf[jj * RB + 16 * b + (c ^ jj)];
+        }
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        uint4 bw;
+        if (WF) {
+          const uint32_t cd = s4 == 0 ? ts.w[i].w[0].x : s4 == 1 ? ts.w[i].w[0].y
+                            : s4 == 2 ? ts.w[i].w[0].z : ts.w[i].w[0].w;
+          bw = fp4x8_to_bf16(cd, e8m0_as_f32((ts.w[i].sc >> (8 * s4)) & 0xFFu));
+        } else {
+          bw = ts.w[i].w[s4];
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) cur[b] = mfma_bf16(af[s4][b], bw, cur[b]);
+      }
+      ts.w[i].load(trow, min(q + P, ks - 1), lane);
+      if (q < ks && (++in_part == qper || q + 1 == ks)) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          tot[b] = first ? cur[b] : tot[b] + cur[b];
+          cur[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        first = false;
+        in_part = 0;
+      }
+      asm volatile("" ::: "memory");
+      st.commit((i + 1) % P, lds + ((q + 1) & 1) * rstride, src, min(q + 1, ks - 1));
+      __syncthreads();
+    }
+  }
+}
+
+// Dense IN matrix rows (W_down_latent and the shared gate/up) for a tile of up to 64
+// tokens: tile rows [tr_first, tr_first + tr_count), 4 per workgroup.
+struct InTTArgs {
+  const uint8_t* w;
+  int ks, qper, tr_r, tr_dn, tr_first, tr_count, n_grp, n_tiles;
+  const uint16_t* x;
+  int64_t T;
+  int d;
+  float* xc;
+  uint16_t* xc_hl;   // [T][2][lp] hi/lo of x^c for the expert launch
+  int l, lp;
+  float* hs;
+  uint16_t* hs_hl;   // [T][2][ms] hi/lo of h_s for the OUT launch
+  int ms;
+  int act;
+  float bg, bl;
+};
+
+constexpr int kInTTBlocks = 4;    // 64 bf16 token rows
+
+__global__ __launch_bounds__(kBlock) void k_in_tt(InTTArgs a) {
+  extern __shared__ uint4 sm[];
+  __shared__ TTRows rows;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  int grp, tile;
+  if (!xcd_item(blockIdx.x, a.n_grp, a.n_tiles, grp, tile)) return;
+  const int64_t t0 = (int64_t)tile * kTTMaxSrc;
+  const int nt = (int)min((int64_t)kTTMaxSrc, a.T - t0);
+  if ((int)threadIdx.x < nt) rows.o0[threadIdx.x] = (uint32_t)((t0 + threadIdx.x) * a.d / 8);
+  __syncthreads();
+  const int tri = grp * kWavesPerBlock + wv;
+  const bool live = tri < a.tr_count;
+  const int tr = a.tr_first + (live ? tri : 0);
+  f32x4_t tot[kInTTBlocks];
+  tt_run<0, 4, kInTTBlocks>(rows, TTSrc{a.x, nullptr, nt, a.d, 0, 0},
+                            a.w + (size_t)tr * a.ks * kBf16StepBytes, a.ks, a.qper, sm, tot);
+  if (!live) return;
+#pragma unroll
+  for (int b = 0; b < kInTTBlocks; ++b) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int ti = 16 * b + 4 * g + v;
+      if (tr < a.tr_r + a.tr_dn) {
+        const int r = 16 * (tr - a.tr_r) + c;
+        if (ti < nt && r < a.l) {
+          a.xc[(t0 + ti) * a.l + r] = tot[b][v];
+          store_hilo(a.xc_hl + (t0 + ti) * 2 * a.lp + r, a.lp, tot[b][v]);
+        }
+      } else {
+        const int r = 8 * (tr - a.tr_r - a.tr_dn) + (c - 8);
+        const float gate = from_gate_lane(tot[b][v]);
+        if (c >= 8 && ti < nt && r < a.ms) {
+          const float h = glu_act(gate, tot[b][v], a.act, a.bg, a.bl);
+          a.hs[(t0 + ti) * a.ms + r] = h;
+          store_hilo(a.hs_hl + (t0 + ti) * 2 * a.ms + r, a.ms, h);
+        }
+      }
+    }
+  }
+}
+
+// OUT matrix for a tile of up to 32 tokens: [u_hat ; h_s] as hi/lo rows.
+struct OutTTArgs {
+  const uint8_t* w;
+  int ks, ks_l, qper, n_tr, n_grp, n_tiles;
+  const uint16_t* uh_hl;   // [T][2][l]
+  const uint16_t* hs_hl;   // [T][2][ms]
+  int d, l, ms;
+  int64_t T;
+  float* delta;
+};
+
+constexpr int kHiloTTBlocks = 4;  // 32 fp32 rows as 64 hi/lo rows
+constexpr int kHiloTTRows = 32;
+
+__global__ __launch_bounds__(kBlock) void k_out_tt(OutTTArgs a) {
+  extern __shared__ uint4 sm[];
+  __shared__ TTRows rows;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  int grp, tile;
+  if (!xcd_item(blockIdx.x, a.n_grp, a.n_tiles, grp, tile)) return;
+  const int64_t t0 = (int64_t)tile * kHiloTTRows;
+  const int nt = (int)min((int64_t)kHiloTTRows, a.T - t0);
+  if ((int)threadIdx.x < 2 * nt) {
+    const int64_t row = 2 * t0 + threadIdx.x;    // hi/lo row of token t0 + threadIdx / 2
+    rows.o0[threadIdx.x] = (uint32_t)(row * a.l / 8);
+    rows.o1[threadIdx.x] = (uint32_t)(row * a.ms / 8);
+  }
+  __syncthreads();
+  const int tr = grp * kWavesPerBlock + wv;
+  const bool live = tr < a.n_tr;
+  f32x4_t tot[kHiloTTBlocks];
+  tt_run<0, 4, kHiloTTBlocks>(rows, TTSrc{a.uh_hl, a.hs_hl, 2 * nt, a.l, a.ks_l * kStepK, a.ms},
+                              a.w + (size_t)(live ? tr : 0) * a.ks * kBf16StepBytes, a.ks, a.qper,
+                              sm, tot);
+  if (!live) return;
+  const int r = 16 * tr + c;
+  if (r >= a.d) return;
+#pragma unroll
+  for (int b = 0; b < kHiloTTBlocks; ++b) {
+    const int i0 = 8 * b + 2 * g;
+    if (i0 < nt) a.delta[(t0 + i0) * a.d + r] = tot[b][0] + tot[b][1];
+    if (i0 + 1 < nt) a.delta[(t0 + i0 + 1) * a.d + r] = tot[b][2] + tot[b][3];
+  }
+}
+
+// Gate/up: h[p] = act(gate, up) (and its hi/lo row for the down launch); down: E[p].
+// y0, y1 are the sums of positions i0 and i0 + 1 of the unit (position offset p0, n used).
+template <bool GU>
+__device__ __forceinline__ void exp_store(const ExpArgs& a, int p0, int n, int tr, int c, int i0,
+                                          float y0, float y1) {
+  const int i1 = i0 + 1;
+  if (GU) {
+    const float g0 = from_gate_lane(y0), g1 = from_gate_lane(y1);
+    const int r = 8 * tr + (c - 8);
+    if (c >= 8 && r < a.n_out) {
+      if (i0 < n) {
+        const float h = glu_act(g0, y0, a.act, a.bg, a.bl);
+        a.out[(int64_t)(p0 + i0) * a.n_out + r] = h;
+        store_hilo(a.out_hl + (int64_t)(p0 + i0) * 2 * a.out_ld + r, a.out_ld, h);
+      }
+      if (i1 < n) {
+        const float h = glu_act(g1, y1, a.act, a.bg, a.bl);
+        a.out[(int64_t)(p0 + i1) * a.n_out + r] = h;
+        store_hilo(a.out_hl + (int64_t)(p0 + i1) * 2 * a.out_ld + r, a.out_ld, h);
+      }
+    }
+  } else {
+    const int r = 16 * tr + c;
+    if (r < a.n_out) {
+      if (i0 < n) a.out[(int64_t)(p0 + i0) * a.n_out + r] = y0;
+      if (i1 < n) a.out[(int64_t)(p0 + i1) * a.n_out + r] = y1;
+    }
+  }
+}
+
+// Positions of a unit up to which the expert launch stages the whole K range at once and
+// streams the weights without barriers (as for a few tokens); larger units take the
+// K-step loop of the token-tiled products.
+constexpr int kExpWholeK = 2;
+
+// The K-step loop for a unit of n > kExpWholeK positions (2n hi/lo rows in NB blocks).
+template <int WF, bool GU, int NB>
+__device__ __forceinline__ void exp_tt_unit(const ExpArgs& a, const TTRows& rows, uint4* sm,
+                                            const uint8_t* trow, bool live, int p0, int n, int tr,
+                                            int c, int g) {
+  f32x4_t tot[NB];
+  tt_run<WF, 4, NB>(rows, TTSrc{a.xin_hl, nullptr, 2 * n, a.kin, 0, 0}, trow, a.ks,
+                             a.ks, sm, tot);
+  if (!live) return;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    exp_store<GU>(a, p0, n, tr, c, 8 * b + 2 * g, tot[b][0] + tot[b][1], tot[b][2] + tot[b][3]);
+}
+
+// Routed experts for units of up to 32 positions.  The input rows are hi/lo bf16 rows
+// written by their producer (x^c by the IN launch, h by the gate/up launch).
+template <int WF, bool GU>
+__global__ __launch_bounds__(kBlock) void k_exp_tt(ExpArgs a) {
+  extern __shared__ uint4 sm[];
+  __shared__ TTRows rows;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int n_units = min(a.ctrl[0], a.max_units);
+  int wgi, u;
+  if (!xcd_item(blockIdx.x, a.wg_per_unit, a.max_units, wgi, u) || u >= n_units) return;
+  const int4 un = *reinterpret_cast<const int4*>(a.units + 4 * u);
+  const int e = un.x, p0 = un.y, n = un.z;
+  if (e < 0 || e >= a.E || n < 1 || n > a.nu || n > kHiloTTRows || p0 < 0 || p0 + n > a.n_assign)
+    return;
+  const int tr = wgi * kWavesPerBlock + wv;
+  const bool live = tr < a.n_tr;
+  const uint8_t* trow = a.experts + (size_t)e * a.expert_bytes + a.region_off +
+                        (size_t)(live ? tr : 0) * a.ks * (WF ? kFp4StepBytes : kBf16StepBytes);
+  constexpr int P = WF ? 4 : 3;
+  TileStream<WF, P> ts;
+  if (n <= kExpWholeK) ts.prefetch(trow, 0, a.ks);
+  if ((int)threadIdx.x < 2 * n) {
+    const int i = threadIdx.x >> 1, hl = threadIdx.x & 1;
+    int64_t src = p0 + i;
+    if (GU) {
+      const int asg = a.perm[p0 + i];
+      src = (asg >= 0 && asg < a.n_assign) ? asg / a.k : 0;
+    }
+    rows.o0[threadIdx.x] = (uint32_t)((src * 2 + hl) * a.kin_ld / 8);
+  }
+  __syncthreads();
+  if (n > kExpWholeK) {
+    if (n <= 8) exp_tt_unit<WF, GU, 1>(a, rows, sm, trow, live, p0, n, tr, c, g);
+    else if (n <= 16) exp_tt_unit<WF, GU, 2>(a, rows, sm, trow, live, p0, n, tr, c, g);
+    else exp_tt_unit<WF, GU, 4>(a, rows, sm, trow, live, p0, n, tr, c, g);
+    return;
+  }
+  // few positions: the whole K range at once, word j * nr + r = row r, columns 8j..8j+7
+  const int nr = 2 * n, per_row = a.ks * 16;
+  const uint4* xin = reinterpret_cast<const uint4*>(a.xin_hl);
+  for (int idx = threadIdx.x; idx < nr * per_row; idx += kBlock) {
+    const int r = idx / per_row, j = idx - r * per_row;
+    sm[j * nr + r] = 8 * j < a.kin ? xin[rows.o0[r] + j] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();
+  if (!live) return;
+  const f32x4_t acc = run_tile_row_n<WF, P>(ts, trow, 0, a.ks, sm, g * nr + c % nr, nr);
+  exp_store<GU>(a, p0, n, tr, c, 2 * g, acc[0] + acc[1], acc[2] + acc[3]);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1007,6 +1420,8 @@ int in_launch_shared_rows(const Shape& s) { return s.tr_sh; }
 
 hipError_t launch_router(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,
                          bool router_only, const Work& ws, hipStream_t st) {
+  // larger batches: the router alone (W_down_latent goes to the token-tiled IN launch)
+  if (token_tiled(s, T)) router_only = true;
   InArgs a = in_args(s, dense, x, T, ws, s.tr_r, router_only ? 0 : s.tr_dn);
   a.router_wgs = s.tr_r * s.zplanes;
   a.wg_per_blk += a.router_wgs;
@@ -1018,6 +1433,25 @@ hipError_t launch_router(const Shape& s, const uint8_t* dense, const uint16_t* x
 
 hipError_t launch_in(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,
                      const float* bias, int32_t* idx, float* gw, const Work& ws, hipStream_t st) {
+  if (token_tiled(s, T)) {
+    // W_down_latent and the shared gate/up over tiles of 64 tokens
+    InTTArgs a;
+    a.w = dense;
+    a.ks = s.ks_in;
+    a.qper = cdiv(s.ks_in, choose_ksplit(s.tr_in, s.ks_in));
+    a.tr_r = s.tr_r; a.tr_dn = s.tr_dn;
+    a.tr_first = s.tr_r; a.tr_count = s.tr_dn + s.tr_sh;
+    a.n_grp = cdiv(a.tr_count, kWavesPerBlock);
+    a.n_tiles = cdiv(T, kTTMaxSrc);
+    a.x = x; a.T = T; a.d = s.d;
+    a.xc = ws.xc; a.xc_hl = ws.xc_hl; a.l = s.l; a.lp = s.l;
+    a.hs = ws.hs; a.hs_hl = ws.hs_hl; a.ms = s.ms;
+    a.act = s.act; a.bg = s.beta_gate; a.bl = s.beta_lin;
+    const size_t lds = (size_t)2 * kInTTBlocks * 16 * 16 * 16;
+    hipLaunchKernelGGL(k_in_tt, dim3((unsigned)xcd_grid(a.n_grp, a.n_tiles)), dim3(kBlock), lds, st,
+                       a);
+    return hipGetLastError();
+  }
   const int n_tr = in_launch_shared_rows(s);
   InArgs a = in_args(s, dense, x, T, ws, s.tr_in - n_tr, n_tr);
   a.route = route_fused(s, T) ? 1 : 0;
@@ -1071,11 +1505,27 @@ hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_
   a.out = gu ? ws.h : ws.eo;
   a.n_out = gu ? s.m : s.l;
   a.act = s.act; a.bg = s.beta_gate; a.bl = s.beta_lin;
+  a.xin_hl = gu ? ws.xc_hl : ws.h_hl;
+  a.kin_ld = gu ? s.l : s.m;
+  a.out_hl = ws.h_hl;
+  a.out_ld = s.m;
   // one wavefront per tile row and its whole K range (the per-item staging and the
   // cross-wavefront sum cost more than a K-split gains)
   a.ksplit = 1;
   a.wg_per_unit = cdiv(a.n_tr, kWavesPerBlock);
   const unsigned grid = (unsigned)xcd_grid(a.wg_per_unit, a.max_units);
+  if (token_tiled(s, T)) {
+    const size_t lds = std::max((size_t)2 * kHiloTTBlocks * 16 * 16 * 16,
+                                (size_t)2 * kExpWholeK * a.ks * kStepK * 2);
+    if (s.wfmt == 1) {
+      if (gu) hipLaunchKernelGGL((k_exp_tt<1, true>), dim3(grid), dim3(kBlock), lds, st, a);
+      else hipLaunchKernelGGL((k_exp_tt<1, false>), dim3(grid), dim3(kBlock), lds, st, a);
+    } else {
+      if (gu) hipLaunchKernelGGL((k_exp_tt<0, true>), dim3(grid), dim3(kBlock), lds, st, a);
+      else hipLaunchKernelGGL((k_exp_tt<0, false>), dim3(grid), dim3(kBlock), lds, st, a);
+    }
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)2 * a.nu * a.ks * kStepK * 2;
   if (s.wfmt == 1) {
     if (gu) hipLaunchKernelGGL((k_exp<1, true>), dim3(grid), dim3(kBlock), lds, st, a);
@@ -1087,16 +1537,37 @@ hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const Shape& s, const float* gw, int64_t T, const Work& ws,
-                          hipStream_t st) {
+hipError_t launch_combine(const Shape& s, const uint8_t* dense, const float* gw, int64_t T,
+                          const Work& ws, hipStream_t st) {
   const int bpt = cdiv(s.l, kBlock);
   hipLaunchKernelGGL(k_combine, dim3((unsigned)(T * bpt)), dim3(kBlock), 0, st, gw,
                      (const int32_t*)ws.inv, (const float*)ws.eo, T, s.k, s.l, bpt, ws.u);
+  if (token_tiled(s, T))
+    hipLaunchKernelGGL(k_norm, dim3((unsigned)T), dim3(kBlock), 0, st, (const float*)ws.u,
+                       reinterpret_cast<const uint16_t*>(dense + s.gamma_off), s.l, s.use_norm,
+                       s.eps, ws.uh, ws.uh_hl);
   return hipGetLastError();
 }
 
 hipError_t launch_out(const Shape& s, const uint8_t* dense, int64_t T, const Work& ws,
                       float* delta, hipStream_t st) {
+  if (token_tiled(s, T)) {
+    // [u_hat ; h_s] hi/lo rows over tiles of 32 tokens
+    OutTTArgs a;
+    a.w = dense + s.in_bytes;
+    a.ks = s.ks_out; a.ks_l = s.ks_l;
+    a.qper = cdiv(s.ks_out, choose_ksplit(s.tr_out, s.ks_out));
+    a.n_tr = s.tr_out;
+    a.n_grp = cdiv(s.tr_out, kWavesPerBlock);
+    a.n_tiles = cdiv(T, kHiloTTRows);
+    a.uh_hl = ws.uh_hl; a.hs_hl = ws.hs_hl;
+    a.d = s.d; a.l = s.l; a.ms = s.ms;
+    a.T = T; a.delta = delta;
+    const size_t lds = (size_t)2 * kHiloTTBlocks * 16 * 16 * 16;
+    hipLaunchKernelGGL(k_out_tt, dim3((unsigned)xcd_grid(a.n_grp, a.n_tiles)), dim3(kBlock), lds,
+                       st, a);
+    return hipGetLastError();
+  }
   OutArgs a;
   a.w = dense + s.in_bytes;
   a.ks = s.ks_out; a.ks_l = s.ks_l;
