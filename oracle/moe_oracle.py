@@ -23,6 +23,14 @@ Precision: every continuous quantity is float64 on exactly dequantised weights
 point decides an integer, the top-k selection, is taken in float32 as the
 kernel takes it: kappa = float32(s) + float32(b).
 
+Precision profiles.  "fp32" (the default) rounds nothing.  "mx8" inserts exactly
+the rounding points that a compute-bound path declares, and nothing else:
+  - the experts' input x^c and their hidden h are converted to MXFP8-E4M3
+    (the walkthrough's deployment recipe: MXFP4 weights with MXFP8 activations),
+    blocks of 32 along the reduction axis, by the OCP MX conversion rule;
+  - the normalised latent u_hat and the shared hidden h_s are rounded to bf16
+    (nearest, ties to even) before their products with W_up and W_shared_down.
+
 Readings of points the pages leave open are listed in the repository's design
 notes; the ones that change arithmetic are stated where they act below.
 """
@@ -36,6 +44,7 @@ import numpy as np
 
 __all__ = [
     "bf16_to_f64", "e2m1_decode", "e8m0_decode", "dequant_mxfp4", "E2M1_GRID",
+    "e4m3_decode", "round_e4m3", "E4M3_MAX", "quantize_mx8", "round_bf16", "PRECISIONS",
     "sigmoid", "select_and_weight", "router_scores", "situ", "swiglu", "glu", "rmsnorm",
     "OracleLayer", "forward", "routed_sum_dense_mask", "Result", "dispatch",
 ]
@@ -92,6 +101,76 @@ def dequant_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
         raise ValueError("scale count does not match the block size of 32")
     q = q.reshape(q.shape[:-1] + (cols // 32, 32)) * s[..., None]
     return q.reshape(q.shape[:-2] + (cols,))
+
+
+# FP8 E4M3 (the OCP 8-bit floating point formats, E4M3 variant; also the element format
+# of MXFP8 in OCP MX v1.0): 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits;
+# exponent field 0 is subnormal (value = mantissa/8 * 2^-6); S.1111.111 is NaN; there is
+# no infinity, so the largest finite magnitude is 1.75 * 2^8 = 448.
+E4M3_MAX = 448.0
+
+#: Where the "mx8" profile rounds (see the module docstring).
+PRECISIONS = ("fp32", "mx8")
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """8-bit E4M3 codes -> float64 from the field definition (NaN for S.1111.111)."""
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    mant = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, mant / 8.0 * 2.0 ** -6, np.ldexp(1.0 + mant / 8.0, (e - 7).astype(np.int64)))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def _binade(a: np.ndarray) -> np.ndarray:
+    """floor(log2(a)) for a > 0 (exact, from the binary exponent); 0 where a == 0."""
+    _, ex = np.frexp(a)
+    return np.where(a > 0, ex - 1, 0).astype(np.int64)
+
+
+def round_e4m3(y: np.ndarray) -> np.ndarray:
+    """The nearest E4M3 value (ties to the even mantissa), saturated to +-448.
+
+    Normal binade 2^e (e >= -6) holds 8 values spaced 2^(e-3); below 2^-6 the subnormals
+    are spaced 2^-9.  Saturation follows the OCP MX conversion rule (values past the
+    largest normal are clamped to it)."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    e = np.maximum(_binade(a), -6)
+    quantum = np.ldexp(1.0, e - 3)
+    r = np.round(a / quantum) * quantum        # numpy rounds halves to even
+    return np.copysign(np.minimum(r, E4M3_MAX), y)
+
+
+def quantize_mx8(v: np.ndarray, block: int = 32):
+    """MXFP8 (E4M3 elements, one E8M0 scale per `block` values along the last axis), by the
+    OCP MX v1.0 conversion: X = floor(log2(max |v|)) - 8 per block (8 is the largest
+    exponent of E4M3), -127 for an all-zero block, clamped to the E8M0 range; elements
+    are v / 2^X rounded to E4M3 (round_e4m3).
+
+    Returns (dequantised values, E4M3 element values, scale bytes X + 127)."""
+    v = np.asarray(v, dtype=np.float64)
+    shp = v.shape
+    if shp[-1] % block:
+        raise ValueError("the last axis must be a multiple of the block size")
+    vb = v.reshape(shp[:-1] + (shp[-1] // block, block))
+    amax = np.max(np.abs(vb), axis=-1)
+    X = np.where(amax > 0, _binade(amax) - 8, -127)
+    X = np.clip(X, -127, 127)
+    q = round_e4m3(vb * np.ldexp(1.0, -X)[..., None])
+    deq = q * np.ldexp(1.0, X)[..., None]
+    return deq.reshape(shp), q.reshape(shp), (X + 127).astype(np.uint8)
+
+
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """The nearest bf16 value (ties to even) of float64 values: 8 significant bits over the
+    fp32 exponent range (bf16 is the upper half of an fp32; subnormals below 2^-126)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    e = np.maximum(_binade(a), -126)
+    quantum = np.ldexp(1.0, e - 7)
+    return np.copysign(np.round(a / quantum) * quantum, v)
 
 
 # ----------------------------------------------------------------------------------------
@@ -173,15 +252,21 @@ def _act(cfg, g, u):
     raise ValueError(cfg.act)
 
 
-def glu(xin: np.ndarray, w_gu: np.ndarray, w_down: np.ndarray, act: Callable) -> np.ndarray:
+def glu(xin: np.ndarray, w_gu: np.ndarray, w_down: np.ndarray, act: Callable,
+        hidden_round: Callable | None = None) -> np.ndarray:
     """Three-matrix gated MLP: h = act(x W_gate, x W_up), out = h W_down.
 
     w_gu is [2m, K] with the gate rows first and the up rows second (the walkthrough's
-    SituAndMul splits the last axis in half, gate then up); w_down is [K_out, m]."""
+    SituAndMul splits the last axis in half, gate then up); w_down is [K_out, m].
+    `hidden_round`, when given, is applied to h before the down product (a declared
+    rounding point of a precision profile)."""
     m = w_gu.shape[0] // 2
     g = xin @ w_gu[:m].T
     u = xin @ w_gu[m:].T
-    return act(g, u) @ w_down.T
+    h = act(g, u)
+    if hidden_round is not None:
+        h = hidden_round(h)
+    return h @ w_down.T
 
 
 def rmsnorm(u: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
@@ -260,20 +345,28 @@ class Result:
     y_shared: np.ndarray   # [T, d]
 
 
-def forward(layer: OracleLayer, x_bf16: np.ndarray, forced_idx: np.ndarray | None = None) -> Result:
+def forward(layer: OracleLayer, x_bf16: np.ndarray, forced_idx: np.ndarray | None = None,
+            precision: str | None = None) -> Result:
     """The layer forward for tokens x [T, d] (bf16 bit patterns or float64 values).
 
     The routed sum is organised as the block card's `moe_infer` does it: assignments are
     grouped by expert, each expert runs once on the tokens that chose it, and each result
     is weighted by its G and added into its token's sum.  `forced_idx` replaces the
-    selection (used for tokens whose top-k margin is a near tie)."""
+    selection (used for tokens whose top-k margin is a near tie).  `precision` is a
+    profile of PRECISIONS (default: the layer config's `precision`, else "fp32")."""
     cfg = layer.cfg
+    precision = precision or getattr(cfg, "precision", "fp32")
+    if precision not in PRECISIONS:
+        raise ValueError(precision)
+    mx8 = precision == "mx8"
+    q8 = (lambda v: quantize_mx8(v)[0]) if mx8 else None  # noqa: E731
     x = bf16_to_f64(x_bf16) if np.asarray(x_bf16).dtype == np.uint16 else np.asarray(x_bf16, np.float64)
     T = x.shape[0]
     s = router_scores(x, layer.router)
     idx, G, margin = select_and_weight(s, layer.bias, cfg.k, cfg.route_scale, forced_idx)
 
     xc = x @ layer.w_down_latent.T if cfg.l else x
+    xe = q8(xc) if mx8 else xc      # the experts' input
     lat = xc.shape[1]
     u = np.zeros((T, lat), np.float64)
     act = lambda g, v: _act(cfg, g, v)  # noqa: E731
@@ -282,16 +375,18 @@ def forward(layer: OracleLayer, x_bf16: np.ndarray, forced_idx: np.ndarray | Non
         tj = np.nonzero(flat == e)[0]
         t_rows, j_cols = tj // cfg.k, tj % cfg.k
         w_gu, w_dn = layer.expert(int(e))
-        out = glu(xc[t_rows], w_gu, w_dn, act)
+        out = glu(xe[t_rows], w_gu, w_dn, act, q8)
         u[t_rows] += G[t_rows, j_cols][:, None] * out   # one (t, e) pair per token at most
 
     if cfg.l:
         u_hat = rmsnorm(u, layer.gamma, cfg.eps) if cfg.use_norm else u
+        if mx8:
+            u_hat = round_bf16(u_hat)
         y_r = u_hat @ layer.w_up_latent.T
     else:
         y_r = u
     if cfg.ms:
-        y_s = glu(x, layer.shared_gu, layer.shared_down, act)
+        y_s = glu(x, layer.shared_gu, layer.shared_down, act, round_bf16 if mx8 else None)
     else:
         y_s = np.zeros_like(y_r)
     return Result(y_r + y_s, idx, G, margin, xc, u, y_r, y_s)

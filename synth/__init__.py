@@ -148,6 +148,7 @@ class LayerConfig:
     bias_file: str = ""
     e8m0_lo: int = 119               # E8M0 scale bytes uniform in [lo, hi]
     e8m0_hi: int = 123
+    precision: str = "fp32"          # rounding profile of the forward: "fp32" | "mx8"
 
     def with_(self, **kw) -> "LayerConfig":
         return replace(self, **kw)
@@ -164,7 +165,9 @@ K3_DECODE_B1 = LayerConfig(name="k3_latent_moe_decode_b1", tokens=1, seed=1002, 
 K3_DECODE_B64_ZIPF = LayerConfig(
     name="k3_latent_moe_decode_b64_zipf1.0", tokens=64, seed=1003,
     **{**_K3, "bias_kind": "file", "bias_file": "k3_zipf1.0_bias.f32"})
-K3_PREFILL_8K = LayerConfig(name="k3_latent_moe_prefill_8192", tokens=8192, seed=1004, **_K3)
+# prefill: MXFP4 weights against MXFP8 activations on the matrix cores ("mx8" profile)
+K3_PREFILL_8K = LayerConfig(name="k3_latent_moe_prefill_8192", tokens=8192, seed=1004,
+                            precision="mx8", **_K3)
 
 PRESETS = {c.name: c for c in (TOY, K3_DECODE_B1, K3_DECODE_B64_ZIPF, K3_PREFILL_8K)}
 
