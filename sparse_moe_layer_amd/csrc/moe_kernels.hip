@@ -352,9 +352,11 @@ __global__ __launch_bounds__(kBlock) void k_combine(const float* __restrict__ gw
 // sub-tile s (1 KiB) holds columns 32s..32s+31 with lane l's 16 bytes = row l % 16,
 // columns 32s + 8 (l / 16) .. +8: exactly the B operand of v_mfma_f32_16x16x32_bf16, so
 // one wavefront load brings 1 KiB of contiguous bytes and feeds one MFMA.  An MXFP4
-// K-step is 1 KiB of codes (lane l: row l % 16, word s = columns 32s + 8 (l / 16) .. +8)
-// plus the 16 rows' four scale bytes; the codes become bf16 operands through
-// v_cvt_scalef32_pk_bf16_fp4, which is exact.
+// K-step is 1 KiB of codes (lane l: the 32 codes of row l % 16, columns 32 (l / 16) ..
+// +32, one MX block, as the checkpoint stores them) plus the 16 rows' four scale bytes.
+// With few tokens the codes become bf16 operands through v_cvt_scalef32_pk_bf16_fp4
+// (exact); on the compute-bound path the same bytes are the B operand of the scaled
+// 16x16x128 FP4 MFMA.
 //
 // The activations form the A operand: up to 16 rows staged once per workgroup in LDS.
 // bf16 tokens are rows as they are; fp32 activations are split into a bf16 pair
@@ -363,8 +365,8 @@ __global__ __launch_bounds__(kBlock) void k_combine(const float* __restrict__ gw
 // dot products (row 2i + row 2i+1 of D).  D row r of the 16x16 block depends on A row r
 // alone, so lanes beyond the staged rows read a duplicate row and are ignored.
 //
-// LDS layout of the staged rows: the 16-byte word (q, s, g, r) at ((q*4 + s)*4 + g)*nr + r
-// holds row r, columns 128q + 32s + 8g .. +8 (nr = rows staged).
+// LDS layout of the staged rows: the 16-byte word (q, j, r) at (16 q + j) nr + r holds
+// row r, columns 128 q + 8 j .. +8 (piece j of K-step q; nr = rows staged).
 // ------------------------------------------------------------------------------------
 
 // Tokens x (bf16, row stride ld) rows r0..r0+nr-1 into LDS; columns >= n are zero.
@@ -376,7 +378,7 @@ __device__ __forceinline__ void stage_bf16(uint4* sm, const uint16_t* x, int64_t
     const int col = 8 * j;
     const uint4 v = (col < n) ? *reinterpret_cast<const uint4*>(x + r * ld + col)
                               : make_uint4(0u, 0u, 0u, 0u);
-    sm[j * nr + r] = v;  // j = (q*4 + s)*4 + g
+    sm[j * nr + r] = v;  // j = 16 q + piece
   }
 }
 
@@ -450,13 +452,14 @@ __device__ __forceinline__ void stage_hilo(uint4* sm, const HiloRow* rows, int n
   }
 }
 
-// One tile row over K-steps [q0, q0 + n): D += A W^T on the 16 x 16 block (A = staged
-// rows, W = the tile row's 16 weight rows).  WF: 0 bf16 K-steps, 1 MXFP4 K-steps.  P
-// K-steps of weights are in flight per wavefront.  `abase` is the lane's LDS word offset
-// g*nr + (row of this lane), `nr` the staged rows.  N > 0: n == N at compile time, the
-// loop fully unrolled, so every load is unconditional and the waits count exactly the
-// loads in flight; N == 0: any n, with the loads past the end clamped to the last
-// K-step (re-reads that are never used).
+// The weight operand of one K-step of one tile row.  WF: 0 bf16 K-steps, 1 MXFP4
+// K-steps.  A bf16 K-step feeds four 16x16x32 MFMAs: sub-tile s (lane l: row l % 16,
+// columns 32s + 8 (l / 16) .. +8).  An MXFP4 K-step gives lane l one whole MX block: the
+// 32 codes of row l % 16, columns 32 (l / 16) .. +32, and its scale (byte l / 16 of the
+// row's scale word); the four MFMAs then take codes 8s .. 8s+7 of every lane, i.e.
+// columns 32 (l / 16) + 8s .. +8, so the activation operand is read with the roles of s
+// and l / 16 swapped (a_word below).  The same bytes are the B operand of the scaled
+// 16x16x128 FP4 MFMA, which takes the whole block of each lane at once.
 template <int WF>
 struct WeightStep {
   static constexpr int SB = WF ? kFp4StepBytes : kBf16StepBytes;
@@ -473,19 +476,22 @@ struct WeightStep {
       for (int s = 0; s < NW; ++s) w[s] = ld_stream(p + s * 1024 + lane * 16);
     }
   }
-  __device__ __forceinline__ f32x4_t mma(const uint4* ap, int stride, f32x4_t acc) const {
+  // the lane's E8M0 scale as an fp32 power of two (MXFP4)
+  __device__ __forceinline__ float scale(int g) const { return e8m0_as_f32((sc >> (8 * g)) & 0xFFu); }
+  // the B operand of MFMA s
+  __device__ __forceinline__ uint4 operand(int s, float scl) const {
+    if (!WF) return w[s];
+    const uint32_t cd = s == 0 ? w[0].x : s == 1 ? w[0].y : s == 2 ? w[0].z : w[0].w;
+    return fp4x8_to_bf16(cd, scl);
+  }
+  // The 8-column piece (0..15) of the K-step that lane group g feeds to MFMA s.
+  static __device__ __forceinline__ int a_piece(int s, int g) { return WF ? 4 * g + s : 4 * s + g; }
+  // D += A W^T over the K-step: ap points at piece 0 of the lane's staged row, pieces
+  // `stride` words apart.
+  __device__ __forceinline__ f32x4_t mma(const uint4* ap, int stride, int g, f32x4_t acc) const {
+    const float scl = WF ? scale(g) : 0.f;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint4 a = ap[s * stride];
-      uint4 b;
-      if (WF) {
-        const uint32_t cd = s == 0 ? w[0].x : s == 1 ? w[0].y : s == 2 ? w[0].z : w[0].w;
-        b = fp4x8_to_bf16(cd, e8m0_as_f32((sc >> (8 * s)) & 0xFFu));
-      } else {
-        b = w[s];
-      }
-      acc = mfma_bf16(a, b, acc);
-    }
+    for (int s = 0; s < 4; ++s) acc = mfma_bf16(ap[a_piece(s, g) * stride], operand(s, scl), acc);
     return acc;
   }
 };
@@ -508,18 +514,19 @@ struct TileStream {
 // compile time, the loop fully unrolled, so every load is unconditional and the waits
 // count exactly the loads in flight; N == 0: any n, the loads past the end clamped to
 // the last K-step (re-reads that are never used).
+// `arow` is the lane's staged row, `nr` the rows staged (word 16 q nr + piece nr + row).
 template <int WF, int P, int N>
 __device__ __forceinline__ f32x4_t run_tile_row(TileStream<WF, P>& ts, const uint8_t* trow,
-                                                int q0, int n, const uint4* sm, int abase,
+                                                int q0, int n, const uint4* sm, int arow,
                                                 int nr) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int stride = 4 * nr;
-  const uint4* ap = sm + abase + q0 * 4 * stride;
+  const int g = lane >> 4;
+  const uint4* ap = sm + arow + q0 * 16 * nr;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   if (N > 0) {
 #pragma unroll
     for (int q = 0; q < N; ++q) {
-      acc = ts.w[q % P].mma(ap + q * 4 * stride, stride, acc);
+      acc = ts.w[q % P].mma(ap + q * 16 * nr, nr, g, acc);
       if (q + P < N) {
         ts.w[q % P].load(trow, q0 + q + P, lane);
         asm volatile("" ::: "memory");
@@ -531,7 +538,7 @@ __device__ __forceinline__ f32x4_t run_tile_row(TileStream<WF, P>& ts, const uin
   for (int j = 0; j < n; j += P) {
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-      if (j + i < n) acc = ts.w[i].mma(ap + (j + i) * 4 * stride, stride, acc);
+      if (j + i < n) acc = ts.w[i].mma(ap + (j + i) * 16 * nr, nr, g, acc);
       ts.w[i].load(trow, min(q0 + j + i + P, ql), lane);
     }
     asm volatile("" ::: "memory");
@@ -542,12 +549,12 @@ __device__ __forceinline__ f32x4_t run_tile_row(TileStream<WF, P>& ts, const uin
 // run_tile_row with the K-step count as a compile-time constant where it is 1..32.
 template <int WF, int P>
 __device__ __forceinline__ f32x4_t run_tile_row_n(TileStream<WF, P>& ts, const uint8_t* trow,
-                                                  int q0, int n, const uint4* sm, int abase,
+                                                  int q0, int n, const uint4* sm, int arow,
                                                   int nr) {
   if (n <= 0) return f32x4_t{0.f, 0.f, 0.f, 0.f};
   switch (n) {
 #define MOE_N_CASE(N) \
-  case N: return run_tile_row<WF, P, N>(ts, trow, q0, n, sm, abase, nr);
+  case N: return run_tile_row<WF, P, N>(ts, trow, q0, n, sm, arow, nr);
     MOE_N_CASE(1) MOE_N_CASE(2) MOE_N_CASE(3) MOE_N_CASE(4) MOE_N_CASE(5) MOE_N_CASE(6)
     MOE_N_CASE(7) MOE_N_CASE(8) MOE_N_CASE(9) MOE_N_CASE(10) MOE_N_CASE(11) MOE_N_CASE(12)
     MOE_N_CASE(13) MOE_N_CASE(14) MOE_N_CASE(15) MOE_N_CASE(16) MOE_N_CASE(17) MOE_N_CASE(18)
@@ -555,7 +562,7 @@ __device__ __forceinline__ f32x4_t run_tile_row_n(TileStream<WF, P>& ts, const u
     MOE_N_CASE(25) MOE_N_CASE(26) MOE_N_CASE(27) MOE_N_CASE(28) MOE_N_CASE(29) MOE_N_CASE(30)
     MOE_N_CASE(31) MOE_N_CASE(32)
 #undef MOE_N_CASE
-    default: return run_tile_row<WF, P, 0>(ts, trow, q0, n, sm, abase, nr);
+    default: return run_tile_row<WF, P, 0>(ts, trow, q0, n, sm, arow, nr);
   }
 }
 
@@ -679,7 +686,7 @@ __device__ __forceinline__ void in_body(const InArgs& a) {
   stage_bf16(sm, a.x + t0 * a.d, a.d, nt, a.d, a.ks);
   __syncthreads();
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  if (live) acc = run_tile_row_n<0, 3>(ts, trow, q0, q1 - q0, sm, g * nt + c % nt, nt);
+  if (live) acc = run_tile_row_n<0, 3>(ts, trow, q0, q1 - q0, sm, c % nt, nt);
   acc = reduce_ksplit(acc, part, ksplit, kp);
   if (tr != INT_MAX && kp == 0) {
     // D row 4g + v = token 4g + v of the block, column c = weight row 16 tr + c
@@ -779,7 +786,7 @@ __global__ __launch_bounds__(kBlock) void k_exp(ExpArgs a) {
     stage_hilo(sm, rows, n, a.kin, 0, 0, nullptr, a.ks);
     __syncthreads();
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    if (live) acc = run_tile_row_n<WF, WF ? 4 : 3>(ts, trow, q0, q1 - q0, sm, g * nr + c % nr, nr);
+    if (live) acc = run_tile_row_n<WF, WF ? 4 : 3>(ts, trow, q0, q1 - q0, sm, c % nr, nr);
     acc = reduce_ksplit(acc, part, a.ksplit, kp);
     if (tr < a.n_tr && kp == 0) {
       // D rows 4g..4g+3 = (hi, lo) of positions 2g and 2g + 1 of the unit
@@ -887,7 +894,7 @@ __global__ __launch_bounds__(kBlock) void k_out(OutArgs a) {
   __syncthreads();
   const int nr = 2 * nt;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  if (live) acc = run_tile_row_n<0, 3>(ts, trow, q0, q1 - q0, sm, g * nr + c % nr, nr);
+  if (live) acc = run_tile_row_n<0, 3>(ts, trow, q0, q1 - q0, sm, c % nr, nr);
   acc = reduce_ksplit(acc, part, a.ksplit, kp);
   if (tr < a.n_tr && kp == 0) {
     const int r = 16 * tr + c;
@@ -1034,19 +1041,13 @@ __device__ __forceinline__ void tt_run(const TTRows& rows, const TTSrc& src, con
       for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          const int jj = s4 * 4 + g;
+          const int jj = WeightStep<WF>::a_piece(s4, g);
           af[s4][b] = buf[jj * RB + 16 * b + (c ^ jj)];
         }
+      const float scl = WF ? ts.w[i].scale(g) : 0.f;
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        uint4 bw;
-        if (WF) {
-          const uint32_t cd = s4 == 0 ? ts.w[i].w[0].x : s4 == 1 ? ts.w[i].w[0].y
-                            : s4 == 2 ? ts.w[i].w[0].z : ts.w[i].w[0].w;
-          bw = fp4x8_to_bf16(cd, e8m0_as_f32((ts.w[i].sc >> (8 * s4)) & 0xFFu));
-        } else {
-          bw = ts.w[i].w[s4];
-        }
+        const uint4 bw = ts.w[i].operand(s4, scl);
 #pragma unroll
         for (int b = 0; b < NB; ++b) cur[b] = mfma_bf16(af[s4][b], bw, cur[b]);
       }
@@ -1274,7 +1275,7 @@ __global__ __launch_bounds__(kBlock) void k_exp_tt(ExpArgs a) {
   }
   __syncthreads();
   if (!live) return;
-  const f32x4_t acc = run_tile_row_n<WF, P>(ts, trow, 0, a.ks, sm, g * nr + c % nr, nr);
+  const f32x4_t acc = run_tile_row_n<WF, P>(ts, trow, 0, a.ks, sm, c % nr, nr);
   exp_store<GU>(a, p0, n, tr, c, 2 * g, acc[0] + acc[1], acc[2] + acc[3]);
 }
 
@@ -1339,14 +1340,14 @@ __global__ __launch_bounds__(kBlock) void k_pack_fp4(PackArgs a) {
   const int c = lane & 15, g = lane >> 4;
   const int row = packed_row(t, c, a.rows, a.gated);
   const int nb = a.cols / 32;
+  // lane l: the MX block of row l % 16, columns 128 q + 32 (l / 16) .. +32 (16 bytes)
   uint32_t wd[4];
+  const int col = q * kStepK + 32 * g;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int col = q * kStepK + 32 * s + 8 * g;
+  for (int s = 0; s < 4; ++s)
     wd[s] = (row >= 0 && col < a.cols)
-                ? *reinterpret_cast<const uint32_t*>(a.src + ei * a.src_stride + (int64_t)row * (a.cols / 2) + col / 2)
+                ? *reinterpret_cast<const uint32_t*>(a.src + ei * a.src_stride + (int64_t)row * (a.cols / 2) + col / 2 + 4 * s)
                 : 0u;
-  }
   uint8_t* dp = a.dst + ei * a.dst_stride + ((int64_t)t * a.ks_dst + q) * kFp4StepBytes;
   *reinterpret_cast<uint4*>(dp + lane * 16) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
   if (g == 0) {
