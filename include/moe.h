@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef struct ihipStream_t* moe_stream_t; /* the same type as hipStream_t */
 
@@ -64,7 +64,15 @@ typedef enum moe_wfmt {
 } moe_wfmt;
 
 typedef enum moe_precision {
-  MOE_PREC_FP32 = 0 /* activations kept in fp32 between all steps; Delta in fp32 */
+  MOE_PREC_FP32 = 0, /* activations kept in fp32 between all steps; Delta in fp32 */
+  MOE_PREC_MX8 = 1   /* the compute-bound profile: the experts' input x^c and hidden h are
+                        converted to MXFP8-E4M3 (blocks of 32 along K; OCP MX conversion:
+                        scale 2^(floor(log2 amax) - 8), elements rounded to nearest even,
+                        saturated at 448) and multiplied with the MXFP4 weights on the
+                        scaled FP8 x FP4 matrix cores; u_hat and h_s are rounded to bf16
+                        before W_up_latent and W_shared_down; everything else as FP32.
+                        The walkthrough's deployment recipe: MXFP4 weights, MXFP8
+                        activations.  Needs MXFP4 experts. */
 } moe_precision;
 
 /* Layer shape and options.  K3: d_model 7168, d_latent 3584, n_experts 896, top_k 16,
@@ -170,9 +178,13 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t max_tokens, size_t*
  *   [5] u      [T][l]   fp32     gated latent sum before the norm
  *   [6] u_hat  [T][l]   fp32     RMSNorm(u) * gamma (written for batches that take the
  *                                token-tiled launches, see moe_step)
- *   [7] hi/lo  bf16 row pairs (hi = bf16(v), lo = bf16(v - hi)) of x^c [T][2][l], h_s
+ *   [7] FP32: bf16 row pairs (hi = bf16(v), lo = bf16(v - hi)) of x^c [T][2][l], h_s
  *                                [T][2][m_s], h [T*k][2][m] and u_hat [T][2][l], each part
  *                                256-aligned (token-tiled launches; internal)
+ *       MX8:  x^c as E4M3 codes [T][128 ceil(l/128)] and E8M0 scales [T][4 ceil(l/128)],
+ *             h as codes [T*k][128 ceil(m/128)] and scales [T*k][4 ceil(m/128)] (dispatch
+ *             order; K-steps past l or m zero), u_hat bf16 [T][l], h_s bf16 [T][m_s],
+ *             each part 256-aligned (internal); the slots [2] h_s and [3] h stay unused
  *   [8] perm   [T*k]    int32    dispatch order -> assignment t*k+j
  *   [9] inv    [T*k]    int32    assignment -> dispatch order
  *  [10] counts [E]      int32    assignments per expert
@@ -203,7 +215,10 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const 
  * wide d) each product stages all its activation rows at once; larger batches take
  * token-tiled launches (tiles of up to 64 tokens or 32 assignments of one expert, the
  * weights read once per tile) whose sums follow the same order, so a token's results
- * have the same bits in both.  Where the two differ it is said below. */
+ * have the same bits in both.  Where the two differ it is said below.  MOE_PREC_MX8
+ * maps the steps onto its own launches: ROUTER computes all products with the token
+ * (router logits, x^c, h_s), IN converts x^c to MXFP8, EXPERT_GU converts h to MXFP8 in
+ * its epilogue, COMBINE also normalises and rounds u_hat to bf16. */
 typedef enum moe_step {
   MOE_STEP_ROUTER = 0,      /* router logits z = x W_r (partial planes), and in the same
                                launch x^c = x W_down_latent (larger batches: in IN) */
@@ -249,7 +264,8 @@ moe_status moe_layer_forward_steps(const moe_config* cfg, const moe_weights* w,
 /* The router step alone (block card: z = x W_r, s = sigmoid(z), top_k(s + b), and G;
  * toy chapter: the bias selects, the raw score weights).  Same arguments and output
  * layout as the corresponding ones of moe_layer_forward; the logits are left in the
- * workspace slot [10]. */
+ * workspace slot [12].  The router runs as in MOE_PREC_FP32 whatever cfg->precision
+ * says (the profiles differ after the route). */
 moe_status moe_route(const moe_config* cfg, const moe_weights* w, const float* bias,
                      const void* x, int64_t n_tokens, int32_t* topk_idx, float* topk_w,
                      void* workspace, size_t workspace_bytes, moe_stream_t stream);

@@ -45,7 +45,7 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "e2m1_decode", "e8m0_decode", "dequant_mxfp4", "E2M1_GRID",
     "e4m3_decode", "round_e4m3", "E4M3_MAX", "quantize_mx8", "round_bf16", "PRECISIONS",
-    "sigmoid", "select_and_weight", "router_scores", "situ", "swiglu", "glu", "rmsnorm",
+    "sigmoid", "select_and_weight", "selection_kappa", "router_scores", "situ", "swiglu", "glu", "rmsnorm",
     "OracleLayer", "forward", "routed_sum_dense_mask", "Result", "dispatch",
 ]
 
@@ -222,6 +222,14 @@ def select_and_weight(s: np.ndarray, bias: np.ndarray, k: int, route_scale: floa
     else:
         margin = np.full(T, np.inf)
     return idx.astype(np.int32), G, margin
+
+
+def selection_kappa(s: np.ndarray, bias: np.ndarray, k: int) -> np.ndarray:
+    """kappa = float32(s) + float32(b) of the k + 1 largest, in selection order [T, k+1]
+    (as select_and_weight forms it), for the gaps between neighbours of the ranking."""
+    kappa = np.asarray(s, dtype=np.float64).astype(np.float32) + np.asarray(bias, dtype=np.float32)[None, :]
+    order = np.argsort(-kappa, axis=1, kind="stable")[:, : k + 1]
+    return np.take_along_axis(kappa, order, axis=1).astype(np.float64)
 
 
 # ----------------------------------------------------------------------------------------

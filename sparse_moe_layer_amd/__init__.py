@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 ACT = {"situ": 0, "swiglu": 1}
 WFMT = {"bf16": 0, "mxfp4": 1}
+PREC = {"fp32": 0, "mx8": 1}
 WS_SLOTS = ("ctrl", "xc", "hs", "h", "eo", "u", "uh", "hl", "perm", "inv", "counts", "offsets", "z",
             "chunk_hist", "units")
 
@@ -25,7 +26,7 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_packed_dense_size", "moe_pa
            "moe_workspace_layout", "moe_layer_forward",
            "moe_layer_forward_timed", "moe_layer_forward_steps", "moe_route", "moe_dispatch")
 STEPS = ("router", "in", "route", "dispatch", "expert_gu", "expert_down", "combine", "out")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class MoeConfig(ctypes.Structure):
@@ -111,15 +112,17 @@ def _check(st: int, what: str):
 
 
 def make_config(d, l, E, k, m, ms, expert_fmt="mxfp4", act="situ", route_scale=1.0,
-                use_norm=True, eps=1e-6, beta_gate=4.0, beta_lin=25.0) -> MoeConfig:
+                use_norm=True, eps=1e-6, beta_gate=4.0, beta_lin=25.0,
+                precision="fp32") -> MoeConfig:
     return MoeConfig(d, l, E, k, m, ms, 1 if use_norm else 0, eps, route_scale, beta_gate,
-                     beta_lin, ACT[act], WFMT[expert_fmt], 0)
+                     beta_lin, ACT[act], WFMT[expert_fmt], PREC[precision])
 
 
 def config_from(c) -> MoeConfig:
     """MoeConfig from any object with the layer-config attribute names."""
     return make_config(c.d, c.l, c.E, c.k, c.m, c.ms, c.expert_fmt, c.act, c.route_scale,
-                       c.use_norm, c.eps, c.beta_gate, c.beta_lin)
+                       c.use_norm, c.eps, c.beta_gate, c.beta_lin,
+                       getattr(c, "precision", "fp32"))
 
 
 def workspace_size(cfg: MoeConfig, max_tokens: int) -> int:

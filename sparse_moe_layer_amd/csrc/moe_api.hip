@@ -29,7 +29,8 @@ moe_status make_shape(const moe_config* c, Shape* s) {
     return MOE_ERR_INVALID_ARG;
   if (c->expert_wfmt == MOE_WFMT_MXFP4 && (c->d_latent % 32 || c->d_expert % 32))
     return MOE_ERR_INVALID_ARG;
-  if (c->precision != MOE_PREC_FP32) return MOE_ERR_UNSUPPORTED;
+  if (c->precision != MOE_PREC_FP32 && c->precision != MOE_PREC_MX8) return MOE_ERR_INVALID_ARG;
+  if (c->precision == MOE_PREC_MX8 && c->expert_wfmt != MOE_WFMT_MXFP4) return MOE_ERR_UNSUPPORTED;
   if (c->d_latent == 0) return MOE_ERR_UNSUPPORTED;  // non-latent blocks: not built yet
   if (c->n_experts > 1024 || c->top_k > 64) return MOE_ERR_UNSUPPORTED;
   if (c->d_model > 8192 || c->d_latent > 8192 || c->d_expert > 8192 || c->d_shared > 8192)
@@ -47,6 +48,7 @@ moe_status make_shape(const moe_config* c, Shape* s) {
   s->beta_lin = c->beta_lin;
   s->act = c->act;
   s->wfmt = c->expert_wfmt;
+  s->prec = c->precision == MOE_PREC_MX8 ? 1 : 0;
   // packed dense weights
   s->ks_in = moe::cdiv(s->d, moe::kStepK);
   s->tr_r = moe::cdiv(s->E, moe::kTileRows);
@@ -73,15 +75,24 @@ moe_status make_shape(const moe_config* c, Shape* s) {
   return MOE_OK;
 }
 
-// The hi/lo slot: x^c, h_s, h and u_hat as bf16 row pairs, each part 256-aligned.
+// Slot [7].  FP32: x^c, h_s, h and u_hat as bf16 row pairs.  MX8: the MXFP8 codes and
+// scales of x^c and h, u_hat and h_s in bf16.  Each part 256-aligned.
+constexpr int kHiloParts = 6;
 size_t hilo_part(const Shape& s, int64_t T, int part) {
+  if (s.prec == 1) {
+    const int64_t rows[6] = {T, T, T * s.k, T * s.k, T, T};
+    const int64_t bytes[6] = {128LL * s.ks_gu, 4LL * s.ks_gu, 128LL * s.ks_edn, 4LL * s.ks_edn,
+                              2LL * s.l, 2LL * s.ms};
+    return align256((size_t)(rows[part] * bytes[part]));
+  }
+  if (part >= 4) return 0;
   const int64_t rows[4] = {T, T, T * s.k, T};
   const int64_t width[4] = {s.l, s.ms, s.m, s.l};
   return align256((size_t)rows[part] * 2 * width[part] * 2);
 }
 size_t hilo_bytes(const Shape& s, int64_t T) {
   size_t n = 0;
-  for (int i = 0; i < 4; ++i) n += hilo_part(s, T, i);
+  for (int i = 0; i < kHiloParts; ++i) n += hilo_part(s, T, i);
   return n;
 }
 
@@ -126,11 +137,21 @@ moe::Work make_work(const Shape& s, int64_t T, void* ws, const size_t off[MOE_WS
   w.uh = reinterpret_cast<float*>(b + off[6]);
   {
     char* p = b + off[7];
-    uint16_t** parts[4] = {&w.xc_hl, &w.hs_hl, &w.h_hl, &w.uh_hl};
-    for (int i = 0; i < 4; ++i) {
-      *parts[i] = reinterpret_cast<uint16_t*>(p);
+    void* parts[kHiloParts];
+    for (int i = 0; i < kHiloParts; ++i) {
+      parts[i] = p;
       p += hilo_part(s, T, i);
     }
+    w.xc_hl = static_cast<uint16_t*>(parts[0]);
+    w.hs_hl = static_cast<uint16_t*>(parts[1]);
+    w.h_hl = static_cast<uint16_t*>(parts[2]);
+    w.uh_hl = static_cast<uint16_t*>(parts[3]);
+    w.pf.xq = static_cast<uint8_t*>(parts[0]);
+    w.pf.xs = static_cast<uint8_t*>(parts[1]);
+    w.pf.hq = static_cast<uint8_t*>(parts[2]);
+    w.pf.hsc = static_cast<uint8_t*>(parts[3]);
+    w.pf.uh = static_cast<uint16_t*>(parts[4]);
+    w.pf.hs = static_cast<uint16_t*>(parts[5]);
   }
   w.perm = reinterpret_cast<int32_t*>(b + off[8]);
   w.inv = reinterpret_cast<int32_t*>(b + off[9]);
@@ -287,6 +308,26 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const float
     if (events && events[step] && hipEventRecord((hipEvent_t)events[step], hs) != hipSuccess)
       return MOE_ERR_HIP;
     hipError_t e = hipSuccess;
+    if (s.prec == 1) {
+      switch (step) {
+        case MOE_STEP_ROUTER: e = moe::launch_pf_in(s, dense, xb, n_tokens, ws.pf, ws.z, ws.xc, hs); break;
+        case MOE_STEP_IN: e = moe::launch_pf_quant(s, ws.xc, n_tokens, ws.pf, hs); break;
+        case MOE_STEP_ROUTE: e = moe::launch_route(s, bias, n_tokens, ws, topk_idx, topk_w, hs); break;
+        case MOE_STEP_DISPATCH:
+          e = moe::launch_dispatch(s, topk_idx, n_tokens, ws.counts, ws.offs, ws.perm, ws.inv,
+                                   ws.chunk_hist, ws.units, ws.ctrl, hs);
+          break;
+        case MOE_STEP_EXPERT_GU: e = moe::launch_pf_expert(s, experts, true, n_tokens, ws, ws.pf, hs); break;
+        case MOE_STEP_EXPERT_DOWN: e = moe::launch_pf_expert(s, experts, false, n_tokens, ws, ws.pf, hs); break;
+        case MOE_STEP_COMBINE:
+          e = moe::launch_combine(s, dense, topk_w, n_tokens, ws, hs);
+          if (e == hipSuccess) e = moe::launch_pf_norm(s, dense, n_tokens, ws, ws.pf, hs);
+          break;
+        case MOE_STEP_OUT: e = moe::launch_pf_out(s, dense, n_tokens, ws.pf, delta, hs); break;
+      }
+      if (e != hipSuccess) return MOE_ERR_HIP;
+      continue;
+    }
     switch (step) {
       case MOE_STEP_ROUTER: e = moe::launch_router(s, dense, xb, n_tokens, false, ws, hs); break;
       case MOE_STEP_IN:
@@ -357,10 +398,12 @@ MOE_EXPORT moe_status moe_route(const moe_config* cfg, const moe_weights* w, con
   if (!topk_idx || !topk_w || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_ERR_INVALID_ARG;
   const moe::Work ws = make_work(s, n_tokens, workspace, off);
   hipStream_t hs = (hipStream_t)stream;
-  if (moe::launch_router(s, static_cast<const uint8_t*>(w->dense), static_cast<const uint16_t*>(x),
+  Shape rs = s;     // the router of the FP32 launches (its logit planes fit the z slot)
+  rs.prec = 0;
+  if (moe::launch_router(rs, static_cast<const uint8_t*>(w->dense), static_cast<const uint16_t*>(x),
                          n_tokens, true, ws, hs) != hipSuccess)
     return MOE_ERR_HIP;
-  return hip_status(moe::launch_route(s, bias, n_tokens, ws, topk_idx, topk_w, hs));
+  return hip_status(moe::launch_route(rs, bias, n_tokens, ws, topk_idx, topk_w, hs));
 }
 
 MOE_EXPORT moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int64_t n_tokens,

@@ -135,4 +135,70 @@ __device__ __forceinline__ float glu_act(float g, float u, int act, float bg, fl
   return g * sigmoidf_(g) * u;
 }
 
+// The weight operand of one K-step of one tile row.  WF: 0 bf16 K-steps, 1 MXFP4
+// K-steps.  A bf16 K-step feeds four 16x16x32 MFMAs: sub-tile s (lane l: row l % 16,
+// columns 32s + 8 (l / 16) .. +8).  An MXFP4 K-step gives lane l one whole MX block: the
+// 32 codes of row l % 16, columns 32 (l / 16) .. +32, and its scale (byte l / 16 of the
+// row's scale word); the four MFMAs then take codes 8s .. 8s+7 of every lane, i.e.
+// columns 32 (l / 16) + 8s .. +8, so the activation operand is read with the roles of s
+// and l / 16 swapped (a_piece below).  The same bytes are the B operand of the scaled
+// 16x16x128 FP4 MFMA, which takes the whole block of each lane at once.
+template <int WF>
+struct WeightStep {
+  static constexpr int SB = WF ? kFp4StepBytes : kBf16StepBytes;
+  static constexpr int NW = WF ? 1 : 4;
+  uint4 w[NW];
+  uint32_t sc;
+  __device__ __forceinline__ void load(const uint8_t* trow, int q, int lane) {
+    const uint8_t* p = trow + (size_t)q * SB;
+    if (WF) {
+      w[0] = ld_stream(p + lane * 16);
+      sc = ld_stream32(p + 1024 + (lane & 15) * 4);
+    } else {
+#pragma unroll
+      for (int s = 0; s < NW; ++s) w[s] = ld_stream(p + s * 1024 + lane * 16);
+    }
+  }
+  // the lane's E8M0 scale as an fp32 power of two (MXFP4)
+  __device__ __forceinline__ float scale(int g) const { return e8m0_as_f32((sc >> (8 * g)) & 0xFFu); }
+  // the B operand of MFMA s
+  __device__ __forceinline__ uint4 operand(int s, float scl) const {
+    if (!WF) return w[s];
+    const uint32_t cd = s == 0 ? w[0].x : s == 1 ? w[0].y : s == 2 ? w[0].z : w[0].w;
+    return fp4x8_to_bf16(cd, scl);
+  }
+  // The 8-column piece (0..15) of the K-step that lane group g feeds to MFMA s.
+  static __device__ __forceinline__ int a_piece(int s, int g) { return WF ? 4 * g + s : 4 * s + g; }
+  // D += A W^T over the K-step: ap points at piece 0 of the lane's staged row, pieces
+  // `stride` words apart.
+  __device__ __forceinline__ f32x4_t mma(const uint4* ap, int stride, int g, f32x4_t acc) const {
+    const float scl = WF ? scale(g) : 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mfma_bf16(ap[a_piece(s, g) * stride], operand(s, scl), acc);
+    return acc;
+  }
+};
+
+// Lanes c >= 8 receive the value of lane c - 8 of their 16-lane row (gate -> up lane).
+__device__ __forceinline__ float from_gate_lane(float v) {
+  return __uint_as_float(dpp_u32<kDppRowShr8, 0xF, true>(0u, __float_as_uint(v)));
+}
+
+// Workgroups go round-robin to the 8 XCDs (each with its own L2).  A launch over
+// n_groups x n_blk items (tile-row groups x token blocks) maps workgroup bid to the item
+// so that all token blocks of one group run on one XCD, back to back: the group's
+// weights come from HBM once and from that XCD's L2 for the other blocks.  The launch has
+// 8 * ceil(n_groups / 8) * n_blk workgroups; the padding ones return false.
+constexpr int kXcds = 8;
+__device__ __forceinline__ bool xcd_item(int bid, int n_groups, int n_blk, int& grp, int& blk) {
+  const int x = bid % kXcds, j = bid / kXcds;
+  const int gi = j / n_blk;
+  blk = j - gi * n_blk;
+  grp = x + kXcds * gi;
+  return grp < n_groups;
+}
+__host__ inline int64_t xcd_grid(int64_t n_groups, int64_t n_blk) {
+  return kXcds * ((n_groups + kXcds - 1) / kXcds) * n_blk;
+}
+
 }  // namespace moe

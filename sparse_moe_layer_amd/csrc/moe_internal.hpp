@@ -24,6 +24,7 @@ struct Shape {
   float eps, route_scale, beta_gate, beta_lin;
   int act;    // 0 SiTU, 1 SwiGLU
   int wfmt;   // 0 bf16, 1 MXFP4 (routed experts)
+  int prec;   // 0 fp32 activations, 1 the mx8 profile (MXFP8 expert inputs, bf16 u_hat / h_s)
   // packed dense weights: IN = [router ; W_down_latent ; shared gate/up] over K = d,
   // OUT = [W_up_latent | W_shared_down] over K = l (padded) + m_s
   int ks_in, tr_r, tr_dn, tr_sh, tr_in;
@@ -35,6 +36,16 @@ struct Shape {
   int step_bytes;       // bytes of one expert K-step (MXFP4 or bf16)
   size_t gu_bytes;      // packed gate/up bytes of one expert
   size_t expert_bytes;  // packed bytes of one expert (256-byte multiple)
+};
+
+// Operands of the mx8 launches (in the hi/lo slot of the workspace).
+struct PfWork {
+  uint8_t* xq;     // [T][128 ks_gu]    x^c as E4M3 codes (K-steps padded with zeros)
+  uint8_t* xs;     // [T][4 ks_gu]      its E8M0 block scales
+  uint8_t* hq;     // [T*k][128 ks_edn] h as E4M3 codes, dispatch order
+  uint8_t* hsc;    // [T*k][4 ks_edn]
+  uint16_t* uh;    // [T][l]            u_hat in bf16
+  uint16_t* hs;    // [T][ms]           h_s in bf16
 };
 
 // Row-major views of the workspace of one forward call.
@@ -58,6 +69,7 @@ struct Work {
   float* z;        // [zplanes][T][E] partial logits; plane 0 holds the logits after the route
   int32_t* chunk_hist;  // [n_chunks][E]
   int32_t* units;  // [max_units][4]: expert, first position, positions, 0
+  PfWork pf;       // the mx8 operands (same memory as the hi/lo rows)
 };
 
 // Tokens per dispatch chunk (so that a chunk holds at most 256 assignments).
@@ -71,13 +83,17 @@ inline int out_tokens_per_block(const Shape& s) { return clampi(57344 / (s.ks_ou
 // With this few tokens the route and the dispatch run inside the IN launch, and every
 // product stages all its activation rows at once (the decode launches); larger batches
 // take the token-tiled launches.
+// The mx8 profile always takes its own launches (moe_prefill.hip).
 inline bool route_fused(const Shape& s, int64_t T) {
-  return T <= 4 && T * s.k <= kBlock && T <= in_tokens_per_block(s);
+  return s.prec == 0 && T <= 4 && T * s.k <= kBlock && T <= in_tokens_per_block(s);
 }
 inline bool token_tiled(const Shape& s, int64_t T) { return !route_fused(s, T); }
 constexpr int kTiledUnitPositions = 32;
-// Positions of one expert per unit of the expert launches (2 hi/lo rows each).
+constexpr int kPfUnitPositions = 64;
+// Positions of one expert per unit of the expert launches (2 hi/lo rows each; one FP8
+// row each in the mx8 launches).
 inline int unit_positions(const Shape& s, int64_t T) {
+  if (s.prec == 1) return kPfUnitPositions;
   if (token_tiled(s, T)) return kTiledUnitPositions;
   return T < 1 ? 1 : (int)T;
 }
@@ -94,16 +110,30 @@ hipError_t launch_in(const Shape& s, const uint8_t* dense, const uint16_t* x, in
                      const float* bias, int32_t* idx, float* gw, const Work& ws, hipStream_t st);
 hipError_t launch_route(const Shape& s, const float* bias, int64_t T, const Work& ws,
                         int32_t* idx, float* gw, hipStream_t st);
+// The logit planes the route sums: the router launch's K-split, or 1 (mx8: plain logits).
+inline int route_planes(const Shape& s) { return s.prec == 1 ? 1 : s.zplanes; }
 hipError_t launch_dispatch(const Shape& s, const int32_t* idx, int64_t T, int32_t* counts,
                            int32_t* offs, int32_t* perm, int32_t* inv, int32_t* chunk_hist,
                            int32_t* units, int32_t* ctrl, hipStream_t st);
 hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_t T,
                          const Work& ws, hipStream_t st);
-// the combine, and for the token-tiled launches the norm
+// the combine, and for the token-tiled launches of the FP32 profile the norm
 hipError_t launch_combine(const Shape& s, const uint8_t* dense, const float* gw, int64_t T,
                           const Work& ws, hipStream_t st);
 hipError_t launch_out(const Shape& s, const uint8_t* dense, int64_t T, const Work& ws,
                       float* delta, hipStream_t st);
+
+// The mx8 launches (moe_prefill.hip).
+hipError_t launch_pf_in(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,
+                        const PfWork& pw, float* z, float* xc, hipStream_t st);
+hipError_t launch_pf_quant(const Shape& s, const float* xc, int64_t T, const PfWork& pw,
+                           hipStream_t st);
+hipError_t launch_pf_expert(const Shape& s, const uint8_t* experts, bool gu, int64_t T,
+                            const Work& ws, const PfWork& pw, hipStream_t st);
+hipError_t launch_pf_norm(const Shape& s, const uint8_t* dense, int64_t T, const Work& ws,
+                          const PfWork& pw, hipStream_t st);
+hipError_t launch_pf_out(const Shape& s, const uint8_t* dense, int64_t T, const PfWork& pw,
+                         float* delta, hipStream_t st);
 
 // Packing.  Dense: canonical bf16 [rows][K] into the tiles of the IN or OUT matrix.
 struct DenseSrc {

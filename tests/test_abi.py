@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 2 == moe.ABI_VERSION
+    assert L.moe_abi_version() == 3 == moe.ABI_VERSION
     assert moe.status_str(0) == "MOE_OK"
     assert moe.status_str(3) == "MOE_ERR_WORKSPACE"
     assert moe.status_str(99) == "MOE_ERR_UNKNOWN"
@@ -60,8 +60,9 @@ def test_packed_dense_bytes_equal_bf16_storage(L):
     assert canonical == 379_846_656
 
 
-def test_workspace_layout_is_ordered_and_aligned(L):
-    cfg = moe.config_from(synth.K3_DECODE_B1)
+@pytest.mark.parametrize("preset", [synth.K3_DECODE_B1, synth.K3_PREFILL_8K])
+def test_workspace_layout_is_ordered_and_aligned(L, preset):
+    cfg = moe.config_from(preset)
     for T in (1, 64, 8192):
         off = moe.workspace_layout(cfg, T)
         vals = [off[k] for k in moe.WS_SLOTS]
@@ -85,7 +86,8 @@ def _bad(**kw):
     ("n_experts", 2048, moe.MOE_ERR_UNSUPPORTED),
     ("act", 7, moe.MOE_ERR_INVALID_ARG),
     ("expert_wfmt", 5, moe.MOE_ERR_INVALID_ARG),
-    ("precision", 1, moe.MOE_ERR_UNSUPPORTED),
+    ("precision", 1, moe.MOE_ERR_UNSUPPORTED),       # mx8 needs MXFP4 experts (toy: bf16)
+    ("precision", 2, moe.MOE_ERR_INVALID_ARG),
     ("d_latent", 0, moe.MOE_ERR_UNSUPPORTED),
     ("rms_eps", float("nan"), moe.MOE_ERR_INVALID_ARG),
     ("beta_gate", 0.0, moe.MOE_ERR_INVALID_ARG),

@@ -1,9 +1,10 @@
 """GPU parity: the HIP path through the C ABI against the float64 CPU oracle.
 
 Bars (restating the layer's acceptance rule):
-  - expert indices identical on every token whose oracle top-k margin
-    kappa_(k) - kappa_(k+1) is >= 1e-5 (near ties are reported, and their Delta is
-    compared with the oracle run on the GPU's own selection);
+  - on every token whose oracle top-k margin kappa_(k) - kappa_(k+1) is >= 1e-5, the
+    oracle's set of experts, in the oracle's order wherever neighbouring kappas are
+    >= 1e-5 apart (near ties are reported, and their Delta is compared with the oracle
+    run on the GPU's own selection);
   - gate weights within 1e-6 of the oracle's G where the indices agree;
   - Delta: relative L2 error <= 2e-3 and max abs error <= 1e-2 * rms(Delta_oracle).
 """
@@ -63,16 +64,45 @@ def run(lay, x):
     return d.cpu().numpy().astype(np.float64), i.cpu().numpy(), w.cpu().numpy().astype(np.float64)
 
 
+def assert_routing(idx, ridx, kap, margin):
+    """The index rule.  On every token whose margin kappa_(k) - kappa_(k+1) is >= MARGIN the
+    GPU selects the oracle's set of experts, and the oracle's expert at every rank whose
+    kappa is at least MARGIN away from both neighbours (experts whose kappas lie closer
+    than that may come out in either order).  Returns the mask of such tokens."""
+    clear = margin >= MARGIN
+    assert np.array_equal(np.sort(idx[clear], 1), np.sort(ridx[clear], 1)), \
+        "expert sets differ on clear margins"
+    k = idx.shape[1]
+    gaps = kap[:, :-1] - kap[:, 1:]                 # rank j to j + 1, j = 0..k-1
+    left = np.concatenate([np.full((len(kap), 1), np.inf), gaps[:, : k - 1]], axis=1)
+    pinned = (left >= MARGIN) & (gaps >= MARGIN)
+    bad = clear[:, None] & pinned & (idx != ridx)
+    assert not bad.any(), f"rank order differs at clear gaps on tokens {np.nonzero(bad.any(1))[0][:8]}"
+    swapped = clear & np.any(idx != ridx, axis=1)
+    if swapped.any():
+        log(f"tokens with near-equal neighbours ranked in the other order: {int(swapped.sum())}")
+    return clear
+
+
+def by_expert(idx, w):
+    """Weights reordered by expert id (for comparing tokens whose ranking differs only
+    between near-equal neighbours)."""
+    o = np.argsort(idx, axis=1)
+    return np.take_along_axis(idx, o, 1), np.take_along_axis(w, o, 1)
+
+
 def check(cfg, x, delta, idx, w, rows=None):
     """Compare GPU outputs for tokens `rows` of x against the oracle; returns error stats."""
     OL = oracle_layer(cfg)
     rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
     ref = O.forward(OL, x[rows])
     near = ref.margin < MARGIN
-    far = ~near
-    assert np.array_equal(idx[rows][far], ref.idx[far]), "expert indices differ on clear margins"
-    same = np.all(idx[rows] == ref.idx, axis=1)
-    assert np.max(np.abs(w[rows][same] - ref.G[same]), initial=0.0) <= 1e-6
+    kap = O.selection_kappa(O.router_scores(O.bf16_to_f64(x[rows]), OL.router), OL.bias, cfg.k)
+    assert_routing(idx[rows], ref.idx, kap, ref.margin)
+    gi, gw = by_expert(idx[rows], w[rows])
+    ri, rg = by_expert(ref.idx, ref.G)
+    same = np.all(gi == ri, axis=1)
+    assert np.max(np.abs(gw[same] - rg[same]), initial=0.0) <= 1e-6
     ref_delta = ref.delta.copy()
     if np.any(~same):   # near ties resolved differently: compare with the GPU's selection
         log(f"near-tie tokens {rows[~same].tolist()} margins {ref.margin[~same].tolist()}")
@@ -195,8 +225,7 @@ def test_k3_decode_b64_sampled_tokens():
     # routing of all 64 tokens from the oracle's router alone
     s = O.router_scores(O.bf16_to_f64(x), OL.router)
     ridx, G, margin = O.select_and_weight(s, OL.bias, cfg.k)
-    clear = margin >= MARGIN
-    assert np.array_equal(idx[clear], ridx[clear])
+    assert_routing(idx, ridx, O.selection_kappa(s, OL.bias, cfg.k), margin)
     # full Delta on a sample of tokens (each costs 16 expert dequantisations on the CPU)
     check(cfg, x, delta, idx, w, rows=[0, 21, 63])
     # per-token independence: the same token alone gives the same Delta bits
@@ -215,8 +244,7 @@ def test_k3_decode_b64_zipf_layer():
     OL = oracle_layer(cfg)
     s = O.router_scores(O.bf16_to_f64(x), OL.router)
     ridx, G, margin = O.select_and_weight(s, OL.bias, cfg.k)
-    clear = margin >= MARGIN
-    assert np.array_equal(idx[clear], ridx[clear])
+    assert_routing(idx, ridx, O.selection_kappa(s, OL.bias, cfg.k), margin)
     load = np.bincount(idx.reshape(-1), minlength=cfg.E)
     assert int((load == x.shape[0]).sum()) == 2
     log(f"[k3 zipf] distinct experts {int((load > 0).sum())}")
@@ -253,3 +281,64 @@ def test_step_ranges_and_timed_forward_match_the_forward():
         assert torch.equal(p, q.cpu())
     for e in evs:
         hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+# ---- the mx8 profile (MXFP8 expert inputs on the scaled FP8 x FP4 matrix cores) --------
+# Compared with the oracle run in the same profile; the kernels and the oracle take each
+# rounding decision on their own fp32 / float64 values, so a value within rounding
+# distance of an E4M3 or bf16 midpoint may round to the neighbour: rare, and far inside
+# the bar.
+
+TINY_MX8 = TINY.with_(name="tiny_mx8", precision="mx8")
+RAGGED_MX8 = RAGGED.with_(name="ragged_mx8", precision="mx8")
+
+
+@pytest.mark.parametrize("T", [1, 5, 33, 100])
+def test_mx8_tiny_token_counts(T):
+    lay, _ = device_layer(TINY_MX8)
+    x = synth.tokens(TINY_MX8, batch=T, T=T)
+    check(TINY_MX8, x, *run(lay, x))
+
+
+def test_mx8_ragged_widths_and_expert_count():
+    lay, _ = device_layer(RAGGED_MX8)
+    x = synth.tokens(RAGGED_MX8)
+    check(RAGGED_MX8, x, *run(lay, x))
+
+
+@pytest.mark.parametrize("variant", ["swiglu", "no_norm", "no_shared"])
+def test_mx8_layer_variants(variant):
+    kw = {"swiglu": dict(act="swiglu"), "no_norm": dict(use_norm=False), "no_shared": dict(ms=0)}[variant]
+    cfg = TINY_MX8.with_(name=f"tiny_mx8_{variant}", tokens=20, **kw)
+    lay, _ = device_layer(cfg)
+    x = synth.tokens(cfg)
+    check(cfg, x, *run(lay, x))
+
+
+def test_mx8_is_deterministic_and_token_independent():
+    lay, _ = device_layer(TINY_MX8)
+    x = to_dev(synth.tokens(TINY_MX8, batch=11, T=70))
+    a = [t.cpu().clone() for t in lay.forward(x)]
+    b = [t.cpu().clone() for t in lay.forward(x)]
+    for p, q in zip(a, b):
+        assert torch.equal(p, q)
+    one = [t.cpu().clone() for t in lay.forward(x[40:41].contiguous())]
+    assert torch.equal(one[1][0], a[1][40]) and torch.equal(one[0][0], a[0][40])
+
+
+def test_k3_prefill_8192_sampled_tokens():
+    """The K3 layer at prefill size in the mx8 profile: every token's indices from the
+    oracle router, Delta of sampled tokens from the oracle."""
+    cfg = synth.K3_PREFILL_8K
+    lay, _ = device_layer(cfg)
+    x = synth.tokens(cfg, batch=0)
+    log(f"[k3 prefill] T={x.shape[0]}")
+    delta, idx, w = run(lay, x)
+    OL = oracle_layer(cfg)
+    s = O.router_scores(O.bf16_to_f64(x), OL.router)
+    ridx, G, margin = O.select_and_weight(s, OL.bias, cfg.k)
+    log(f"[k3 prefill] near-tie tokens {int((margin < MARGIN).sum())}")
+    assert_routing(idx, ridx, O.selection_kappa(s, OL.bias, cfg.k), margin)
+    assert np.all(np.isfinite(delta))
+    rel, mxr, _ = check(cfg, x, delta, idx, w, rows=[0, 4097, 8191])
+    assert rel < 1e-3

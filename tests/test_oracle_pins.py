@@ -431,3 +431,16 @@ def test_dispatch_bookkeeping_brute_force():
         assert [sum(flat == e) for e in range(E)] == list(counts)
         assert offs[0] == 0 and offs[-1] == T * k and np.all(np.diff(offs) == counts)
         assert all(perm[inv[a]] == a for a in range(T * k))
+
+
+def test_selection_kappa_ranks_and_gives_the_margin():
+    rng = np.random.default_rng(4)
+    s = O.sigmoid(rng.standard_normal((40, 30)))
+    b = rng.uniform(-0.1, 0.1, 30).astype(np.float32)
+    idx, G, margin = O.select_and_weight(s, b, 6)
+    kap = O.selection_kappa(s, b, 6)
+    assert kap.shape == (40, 7) and np.all(np.diff(kap, axis=1) <= 0)
+    assert np.array_equal(kap[:, 5] - kap[:, 6], margin)
+    # brute force: the kappas of the selected experts, in selection order
+    want = np.float32(s).astype(np.float64)[np.arange(40)[:, None], idx] + b[idx]
+    assert np.allclose(kap[:, :6], want, rtol=0, atol=1e-7)
