@@ -52,6 +52,19 @@ def algorithmic_bytes(cfg, T, D):
         "out": d * (l + ms) * 2 + l * 2 + T * (l + ms) * 4 + T * d * 4,
     }
 
+def algorithmic_flops(cfg, T):
+    """Multiply-add flops (2 per product) of each step for T tokens."""
+    d, l, E, k, m, ms = cfg.d, cfg.l, cfg.E, cfg.k, cfg.m, cfg.ms
+    tk = T * k
+    return {"router": 2 * T * d * (E + l + 2 * ms), "in": 0, "route": 0, "dispatch": 0,
+            "expert_gu": 2 * tk * l * 2 * m, "expert_down": 2 * tk * m * l, "combine": 2 * tk * l,
+            "out": 2 * T * (l + ms) * d}
+
+
+# matrix-core peaks of MI355X (dense, published), TFLOP/s
+MFMA_PEAK = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
+
+
 def weight_bytes(cfg, D):
     """Weights (and the fp32 bias) one call reads: the layer's algorithmic byte count."""
     d, l, E, m, ms = cfg.d, cfg.l, cfg.E, cfg.m, cfg.ms
@@ -63,6 +76,9 @@ def weight_bytes(cfg, D):
 # rocprofv3 kernel symbol of each step's launch (its template arguments vary with shape)
 STEP_KERNELS = {"router": ("k_router",), "in": ("k_in",), "expert_gu": ("k_exp", "true"),
                 "expert_down": ("k_exp", "false"), "combine": ("k_combine",), "out": ("k_out",)}
+STEP_KERNELS_MX8 = {"router": ("k_pf_dense", "true"), "in": ("k_pf_quant",),
+                    "expert_gu": ("k_pf_exp", "true"), "expert_down": ("k_pf_exp", "false"),
+                    "combine": ("k_pf_norm",), "out": ("k_pf_dense", "false")}
 
 
 def kernel_sources_sha():
@@ -75,7 +91,7 @@ def kernel_sources_sha():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, step):
+def measured_traffic(workload, step, kernels=None):
     """HBM bytes per launch of `step` from the committed rocprofv3 counter summary, or None
     when there is none or the kernel sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.md")
@@ -86,7 +102,7 @@ def measured_traffic(workload, step):
             rec = json.loads(line[len("traffic_json: "):])
             if rec.get("src_sha") != kernel_sources_sha():
                 return None
-            want = STEP_KERNELS.get(step, ())
+            want = (kernels or STEP_KERNELS).get(step, ())
             for name, v in rec["bytes_per_launch"].items():
                 if want and all(w in name for w in want):
                     return v
@@ -123,8 +139,9 @@ class HipEvents:
             self.h.hipEventDestroy(e)
 
 
-def cpu_baseline(cfg, dense, seconds):
-    """The float64 CPU oracle, as it is, on a bounded sample of the same workload."""
+def cpu_baseline(cfg, dense, seconds, sample_tokens=None):
+    """The float64 CPU oracle, as it is, on a bounded sample of the same workload
+    (batches of the workload's size, or of `sample_tokens` tokens for large batches)."""
     import numpy as np
     import oracle
     import synth
@@ -134,18 +151,20 @@ def cpu_baseline(cfg, dense, seconds):
     except Exception:
         cores = 1
     OL = oracle.OracleLayer.from_synth(cfg, dense)
+    tb = cfg.tokens if sample_tokens is None else min(cfg.tokens, sample_tokens)
     n, t0 = 0, time.perf_counter()
     while True:
-        x = synth.tokens(cfg, batch=5000 + n)
+        x = synth.tokens(cfg, batch=5000 + n, T=tb)
         oracle.forward(OL, x)
         n += 1
         el = time.perf_counter() - t0
         if el >= seconds or n >= 64:
             break
-    tps = n * cfg.tokens / el
+    tps = n * tb / el
     return {"value": tps, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n} step(s) of {cfg.tokens} token(s), {el:.1f} s, float64 numpy oracle "
-                      f"(BLAS threads {cores}), experts regenerated and dequantised per token"}
+            "sample": f"{n} batch(es) of {tb} token(s) of the workload, {el:.1f} s, float64 numpy "
+                      f"oracle in the {getattr(cfg, 'precision', 'fp32')} profile (BLAS threads "
+                      f"{cores}), each touched expert regenerated and dequantised per batch"}
 
 
 def main():
@@ -245,6 +264,7 @@ def main():
     log(f"[bench] per step with events at every boundary (us): {steps_us}")
     dom = max(("router", "in", "expert_gu", "expert_down", "out"),
               key=lambda n: step_ms[moe.STEPS.index(n)])
+    mx8 = getattr(cfg, "precision", "fp32") == "mx8"
     # The dominant step alone, K launches back to back between two events.  Each launch
     # works on the buffers of an earlier full forward; R sets of buffers (different tokens,
     # so different experts, and different dense copies) rotate past the last-level cache.
@@ -279,9 +299,28 @@ def main():
 
     Dm = float(np.mean([D[i % args.batches] for i in range(K)]))
     ab = algorithmic_bytes(cfg, T, Dm)
-    achieved = ab[dom] / dom_s / 1e9
+    af = algorithmic_flops(cfg, T)
     layer_bytes = weight_bytes(cfg, Dm)
     layer_gbs = layer_bytes / (ms_step * 1e-3) / 1e9
+    layer_tflops = sum(af.values()) / (ms_step * 1e-3) / 1e12
+    if mx8:
+        # compute-bound: the expert products on the scaled FP8 x FP4 matrix cores (they run
+        # at the FP8 rate), the dense products on bf16 ones
+        dtype_peak = "fp8" if dom.startswith("expert") else "bf16"
+        achieved = af[dom] / dom_s / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved,
+                    "peak": MFMA_PEAK[dtype_peak], "unit": "TFLOP/s",
+                    "frac": achieved / MFMA_PEAK[dtype_peak],
+                    "traffic": measured_traffic(cfg.name, dom, STEP_KERNELS_MX8),
+                    "algorithmic_flops": af[dom], "avg_us": dom_s * 1e6,
+                    "peak_dtype": "fp8 x fp4 (fp8 rate)" if dtype_peak == "fp8" else "bf16",
+                    "frac_of_mxfp4_peak": achieved / MFMA_PEAK["fp4"] if dtype_peak == "fp8" else None}
+    else:
+        achieved = ab[dom] / dom_s / 1e9
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                    "traffic": measured_traffic(cfg.name, dom),
+                    "algorithmic_bytes": ab[dom], "avg_us": dom_s * 1e6}
 
     out = {
         "metric": METRIC,
@@ -294,24 +333,24 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "fp8xfp4+bf16" if mx8 else "f32",
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens_per_step": T, "d": cfg.d, "latent": cfg.l,
                    "experts": cfg.E, "top_k": cfg.k, "expert_hidden": cfg.m,
                    "shared_hidden": cfg.ms, "expert_weights": cfg.expert_fmt,
+                   "precision_profile": getattr(cfg, "precision", "fp32"),
                    "dense_weight_copies": args.rotate, "token_batches": args.batches,
                    "distinct_experts_per_step": Dm},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(cfg.name, dom),
-                     "algorithmic_bytes": ab[dom], "avg_us": dom_s * 1e6},
+        "roofline": roofline,
         "layer": {"algorithmic_bytes": layer_bytes, "achieved_GBps": layer_gbs,
                   "hbm_frac": layer_gbs / HBM_PEAK_GBS,
+                  "algorithmic_flops": sum(af.values()), "achieved_TFLOPs": layer_tflops,
                   "steps_us_with_event_per_boundary": steps_us},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
-        out["cpu_baseline"] = cpu_baseline(cfg, dense0, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(cfg, dense0, args.cpu_seconds,
+                                           sample_tokens=8 if T > 64 else None)
     print(json.dumps(out), flush=True)
 
 

@@ -226,10 +226,14 @@ def select_and_weight(s: np.ndarray, bias: np.ndarray, k: int, route_scale: floa
 
 def selection_kappa(s: np.ndarray, bias: np.ndarray, k: int) -> np.ndarray:
     """kappa = float32(s) + float32(b) of the k + 1 largest, in selection order [T, k+1]
-    (as select_and_weight forms it), for the gaps between neighbours of the ranking."""
+    (as select_and_weight forms it), for the gaps between neighbours of the ranking; the
+    (k+1)-th is -inf when E == k."""
     kappa = np.asarray(s, dtype=np.float64).astype(np.float32) + np.asarray(bias, dtype=np.float32)[None, :]
     order = np.argsort(-kappa, axis=1, kind="stable")[:, : k + 1]
-    return np.take_along_axis(kappa, order, axis=1).astype(np.float64)
+    out = np.take_along_axis(kappa, order, axis=1).astype(np.float64)
+    if out.shape[1] == k:     # E == k: no (k+1)-th expert, the margin is unbounded
+        out = np.concatenate([out, np.full((out.shape[0], 1), -np.inf)], axis=1)
+    return out
 
 
 # ----------------------------------------------------------------------------------------

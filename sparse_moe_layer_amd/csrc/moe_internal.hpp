@@ -89,7 +89,7 @@ inline bool route_fused(const Shape& s, int64_t T) {
 }
 inline bool token_tiled(const Shape& s, int64_t T) { return !route_fused(s, T); }
 constexpr int kTiledUnitPositions = 32;
-constexpr int kPfUnitPositions = 64;
+constexpr int kPfUnitPositions = 64;   // 16 x the expert tile blocks of moe_prefill.hip
 // Positions of one expert per unit of the expert launches (2 hi/lo rows each; one FP8
 // row each in the mx8 launches).
 inline int unit_positions(const Shape& s, int64_t T) {

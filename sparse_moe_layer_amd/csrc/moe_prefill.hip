@@ -14,7 +14,7 @@
 //   k_pf_out     Delta = u_hat W_up_latent + h_s W_shared_down, one product over the packed
 //                OUT matrix (bf16 MFMA)
 //
-// Tiling: a workgroup multiplies a tile of 16 NB activation rows (NB <= 4) with 4 x NT
+// Tiling: a workgroup multiplies a tile of 16 NB activation rows (NB <= 10) with 4 x NT
 // tile rows of weights (NT per wavefront).  K advances one K-step (128 columns) at a
 // time: the activation rows of the next K-steps travel global -> registers -> LDS (two
 // LDS buffers, one barrier per K-step) while every wavefront streams its own weight
@@ -32,9 +32,16 @@ namespace {
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kPfRows = 64;      // activation rows per tile (NB = 4 blocks of 16)
+constexpr int kPfDenseNB = 6;    // dense products: tiles of 96 tokens
+constexpr int kPfExpNB = 4;      // routed experts: units of up to 64 positions
+static_assert(16 * kPfExpNB == kPfUnitPositions, "dispatch units fill one expert tile");
+// the most activation rows of a tile (the row tables hold this many)
+constexpr int kPfRows = 16 * (kPfDenseNB > kPfExpNB ? kPfDenseNB : kPfExpNB);
+static_assert(kPfRows <= kBlock, "one thread per activation row sets the row tables");
 constexpr int kPfNT = 4;         // weight tile rows per wavefront
 constexpr int kPfWaves = kBlock / kWave;
+constexpr int kPfDenseDepth = 2;   // K-steps in flight: bf16 weights (4 KiB per tile row)
+constexpr int kPfExpDepth = 2;     // MXFP4 weights (1 KiB per tile row)
 
 // D += A B^T on one 16x16 block over 128 K: A = 16 rows of FP8-E4M3 (32 bytes per lane,
 // lane l: row l % 16, K 16 (l/16) .. +16 in bytes 0..15 and K 64 + 16 (l/16) .. +16 in
@@ -66,6 +73,45 @@ __device__ __forceinline__ uint32_t mx8_scale_byte(float amax) {
 // 2^-X for the scale byte (X = byte - 127): an fp32 with exponent field 254 - byte.
 __device__ __forceinline__ float mx8_inv_scale(uint32_t sbyte) { return __uint_as_float((254u - sbyte) << 23); }
 
+// tanh of the compute-bound epilogues: the odd series x (1 - x^2/3 + 2 x^4/15) below
+// |x| = 1/16 (relative error < 1e-8 there), else (1 - e^-2|x|) / (1 + e^-2|x|) with the
+// hardware exponential (relative error below 1e-6), sign restored.
+__device__ __forceinline__ float tanh_fast(float x) {
+  const float ax = fabsf(x), x2 = x * x;
+  const float series = x * (1.f + x2 * (-1.f / 3.f + x2 * (2.f / 15.f)));
+  const float e = __expf(-2.f * ax);
+  const float r = __fdividef(1.f - e, 1.f + e);
+  return ax < 0.0625f ? series : copysignf(r, x);
+}
+__device__ __forceinline__ float sigmoid_fast(float g) { return __fdividef(1.f, 1.f + __expf(-g)); }
+
+// SiTU-GLU (act 0) or SwiGLU (act 1) with the fast tanh and sigmoid; rbg, rbl = 1 / beta.
+__device__ __forceinline__ float glu_act_fast(float g, float u, int act, float rbg, float bg,
+                                              float rbl, float bl) {
+  if (act == 0) return (bg * tanh_fast(g * rbg) * sigmoid_fast(g)) * (bl * tanh_fast(u * rbl));
+  return g * sigmoid_fast(g) * u;
+}
+
+// Four fp32 values (already divided by their block scale) as E4M3 bytes, the first in the
+// low byte.
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -448.f), 448.f); b = fminf(fmaxf(b, -448.f), 448.f);
+  c = fminf(fmaxf(c, -448.f), 448.f); d = fminf(fmaxf(d, -448.f), 448.f);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// A value of another lane of the same quad (DPP quad permutation CTRL).
+template <int CTRL>
+__device__ __forceinline__ float quad_perm_f32(float v) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)__float_as_uint(v), CTRL, 0xF, 0xF, false));
+}
+
+// The value of lane c ^ 8 within each 16-lane row (DPP row rotate by 8).
+__device__ __forceinline__ float swap_half_rows(float v) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0x128, 0xF, 0xF, false));
+}
+
 // ------------------------------------------------------------------------------------
 // The activation side of a tile.
 //   AF 0: bf16 rows, 16 pieces of 16 bytes per K-step; columns [0, n0) from segment 0
@@ -90,13 +136,13 @@ struct PfSrc {
   int R, n0, c1, n1;
 };
 
-template <int AF, int NB>
+template <int AF, int NB, int P>
 struct PfStage {
   static constexpr int PR = AF ? 8 : 16;
   static constexpr int RB = 16 * NB;
   static constexpr int NP = (RB * PR + kBlock - 1) / kBlock;
-  uint4 v[2][NP];
-  uint32_t sv[2];
+  uint4 v[P][NP];
+  uint32_t sv[P];
   uint32_t o0[NP], o1[NP];
   bool rv[NP];
   uint32_t so;
@@ -121,8 +167,8 @@ struct PfStage {
     const int col = q * kStepK + 8 * piece_of(i);
     return !AF && rv[i] && col >= src.c1 && col < src.c1 + src.n1;
   }
-  template <int SLOT>
-  __device__ __forceinline__ void load(const PfSrc& src, int q) {
+  // K-step q into register slot `slot` (a constant once the caller's loop is unrolled)
+  __device__ __forceinline__ void load(int slot, const PfSrc& src, int q) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       uint32_t w = 0u;
@@ -135,103 +181,122 @@ struct PfStage {
         w = a0 ? o0[i] + (col >> 3) : a1 ? o1[i] + ((col - src.c1) >> 3) : 0u;
         base = a1 ? src.b1 : src.b0;
       }
-      v[SLOT][i] = base[w];
+      const uint4 x = base[w];
+#pragma unroll
+      for (int sl = 0; sl < P; ++sl)
+        if (sl == slot) v[sl][i] = x;
     }
-    if (AF) sv[SLOT] = src.sc[srv ? so + q : 0u];
+    if (AF) {
+      const uint32_t x = src.sc[srv ? so + q : 0u];
+#pragma unroll
+      for (int sl = 0; sl < P; ++sl)
+        if (sl == slot) sv[sl] = x;
+    }
   }
-  template <int SLOT>
-  __device__ __forceinline__ void commit(uint4* buf, uint32_t* sbuf, const PfSrc& src, int q) const {
+  // Register slot `slot`, holding K-step q, into an LDS buffer (invalid pieces as zeros).
+  __device__ __forceinline__ void commit(int slot, uint4* buf, uint32_t* sbuf, const PfSrc& src,
+                                         int q) const {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int idx = threadIdx.x + i * kBlock;
       if (idx < RB * PR) {
         const int r = idx / PR, j = idx % PR;
         const bool z = !(in0(i, src, q) || in1(i, src, q));
-        const uint4 x = v[SLOT][i];
+        uint4 x = v[0][i];
+#pragma unroll
+        for (int sl = 1; sl < P; ++sl)
+          if (sl == slot) x = v[sl][i];
         buf[j * RB + (r ^ j)] = make_uint4(z ? 0u : x.x, z ? 0u : x.y, z ? 0u : x.z, z ? 0u : x.w);
       }
     }
-    if (AF && (int)threadIdx.x < RB) sbuf[threadIdx.x] = srv ? sv[SLOT] : 0u;
+    if (AF && (int)threadIdx.x < RB) {
+      uint32_t x = sv[0];
+#pragma unroll
+      for (int sl = 1; sl < P; ++sl)
+        if (sl == slot) x = sv[sl];
+      sbuf[threadIdx.x] = srv ? x : 0u;
+    }
   }
 };
 
 // The K loop of a tile: acc[t][b] = D of activation block b x the wavefront's tile row t
 // (trow[t]; waves or tile rows without work pass tile row 0 of the same matrix and drop
-// the result).  AF 0 pairs with bf16 weights (WF 0), AF 1 with MXFP4 weights (WF 1).
-template <int AF, int NB, int NT>
+// the result).  AF 0 pairs with bf16 weights (WF 0), AF 1 with MXFP4 weights (WF 1).  P
+// K-steps of weights and of activation rows are in flight (register rings, slot q % P
+// holds K-step q); the rows of K-step q + 1 go to LDS at the end of step q.
+template <int AF, int NB, int NT, int P>
 __device__ __forceinline__ void pf_run(const PfRows& rows, const PfSrc& src,
                                        const uint8_t* const (&trow)[NT], int ks, uint4* lds,
                                        uint32_t* slds, f32x4_t (&acc)[NT][NB]) {
   constexpr int WF = AF;
   constexpr int RB = 16 * NB;
-  constexpr int PR = PfStage<AF, NB>::PR;
+  constexpr int PR = PfStage<AF, NB, P>::PR;
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane & 15, g = lane >> 4;
-  WeightStep<WF> w[2][NT];
-  PfStage<AF, NB> st;
+  WeightStep<WF> w[P][NT];
+  PfStage<AF, NB, P> st;
   st.init(rows, src);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    w[0][t].load(trow[t], 0, lane);
-    w[1][t].load(trow[t], min(1, ks - 1), lane);
+  for (int i = 0; i < P; ++i) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) w[i][t].load(trow[t], min(i, ks - 1), lane);
+    st.load(i, src, min(i, ks - 1));
   }
-  st.template load<0>(src, 0);
-  st.template load<1>(src, min(1, ks - 1));
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[t][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   asm volatile("" ::: "memory");
-  st.template commit<0>(lds, slds, src, 0);
+  st.commit(0, lds, slds, src, 0);
   __syncthreads();
-  // one K-step with the weights of slot SLOT and LDS buffer q & 1
-  auto step = [&](auto slot_c, int q) {
-    constexpr int SLOT = decltype(slot_c)::value;
-    st.template load<SLOT>(src, min(q + 2, ks - 1));
-    const uint4* buf = lds + (q & 1) * RB * PR;
-    if (AF) {
-      const uint32_t* sb = slds + (q & 1) * RB;
+  for (int q0 = 0; q0 < ks; q0 += P) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int r = 16 * b + c;
-        const uint4 alo = buf[g * RB + (r ^ g)];
-        const uint4 ahi = buf[(4 + g) * RB + (r ^ (4 + g))];
-        const uint32_t sa = (sb[r] >> (8 * g)) & 0xFFu;
+    for (int sl = 0; sl < P; ++sl) {
+      const int q = q0 + sl;
+      if (q >= ks) break;
+      // slot sl held K-step q (already in LDS buffer q & 1): refill it with q + P
+      st.load(sl, src, min(q + P, ks - 1));
+      const uint4* buf = lds + (q & 1) * RB * PR;
+      if (AF) {
+        const uint32_t* sb = slds + (q & 1) * RB;
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          acc[t][b] = mfma_fp8_fp4(alo, ahi, w[SLOT][t].w[0], sa, (w[SLOT][t].sc >> (8 * g)) & 0xFFu,
-                                   acc[t][b]);
-      }
-    } else {
+        for (int b = 0; b < NB; ++b) {
+          const int r = 16 * b + c;
+          const uint4 alo = buf[g * RB + (r ^ g)];
+          const uint4 ahi = buf[(4 + g) * RB + (r ^ (4 + g))];
+          const uint32_t sa = (sb[r] >> (8 * g)) & 0xFFu;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int j = 4 * s + g;
-        uint4 af[NB];
+          for (int t = 0; t < NT; ++t)
+            acc[t][b] = mfma_fp8_fp4(alo, ahi, w[sl][t].w[0], sa, (w[sl][t].sc >> (8 * g)) & 0xFFu,
+                                     acc[t][b]);
+        }
+      } else {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) af[b] = buf[j * RB + ((16 * b + c) ^ j)];
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int j = 4 * s4 + g;
+          uint4 af[NB];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const uint4 bw = w[SLOT][t].operand(s, 0.f);
+          for (int b = 0; b < NB; ++b) af[b] = buf[j * RB + ((16 * b + c) ^ j)];
 #pragma unroll
-          for (int b = 0; b < NB; ++b) acc[t][b] = mfma_bf16(af[b], bw, acc[t][b]);
+          for (int t = 0; t < NT; ++t) {
+            const uint4 bw = w[sl][t].operand(s4, 0.f);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[t][b] = mfma_bf16(af[b], bw, acc[t][b]);
+          }
         }
       }
-    }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) w[SLOT][t].load(trow[t], min(q + 2, ks - 1), lane);
-    asm volatile("" ::: "memory");
-    st.template commit<SLOT ^ 1>(lds + ((q + 1) & 1) * RB * PR, slds + ((q + 1) & 1) * RB, src,
-                                 min(q + 1, ks - 1));
-    __syncthreads();
-  };
-  for (int q = 0; q < ks; q += 2) {
-    step(std::integral_constant<int, 0>{}, q);
-    if (q + 1 < ks) step(std::integral_constant<int, 1>{}, q + 1);
+      for (int t = 0; t < NT; ++t) w[sl][t].load(trow[t], min(q + P, ks - 1), lane);
+      asm volatile("" ::: "memory");
+      st.commit((sl + 1) % P, lds + ((q + 1) & 1) * RB * PR, slds + ((q + 1) & 1) * RB, src,
+                min(q + 1, ks - 1));
+      __syncthreads();
+    }
   }
 }
 
 // ------------------------------------------------------------------------------------
-// Dense products for a tile of up to 64 tokens: k_pf_in over the IN matrix (router
+// Dense products for a tile of up to 16 kPfDenseNB tokens: k_pf_in over the IN matrix (router
 // logits -> z, W_down_latent -> x^c fp32, shared gate/up -> SiTU -> h_s bf16), k_pf_out
 // over the OUT matrix (-> Delta).  Work item (tile-row group, token tile); the tiles of
 // one group run back to back on one XCD so that the group's weights come from its L2.
@@ -252,7 +317,7 @@ struct PfDenseArgs {
   int l;
   uint16_t* hs;
   int ms, act;
-  float bg, bl;
+  float bg, bl, rbg, rbl;
   // OUT epilogue
   float* delta;
   int d;
@@ -267,8 +332,8 @@ __global__ __launch_bounds__(kBlock) void k_pf_dense(PfDenseArgs a) {
   const int c = lane & 15, g = lane >> 4;
   int grp, tile;
   if (!xcd_item(blockIdx.x, a.n_grp, a.n_tiles, grp, tile)) return;
-  const int64_t t0 = (int64_t)tile * kPfRows;
-  const int nt = (int)min((int64_t)kPfRows, a.T - t0);
+  const int64_t t0 = (int64_t)tile * 16 * kPfDenseNB;
+  const int nt = (int)min((int64_t)16 * kPfDenseNB, a.T - t0);
   if ((int)threadIdx.x < nt) {
     rows.o0[threadIdx.x] = (uint32_t)((t0 + threadIdx.x) * a.lda0 / 8);
     rows.o1[threadIdx.x] = (uint32_t)((t0 + threadIdx.x) * a.lda1 / 8);
@@ -281,20 +346,21 @@ __global__ __launch_bounds__(kBlock) void k_pf_dense(PfDenseArgs a) {
     tr[t] = (grp * kPfWaves + wv) * kPfNT + t;
     trow[t] = a.w + (size_t)(tr[t] < a.tr_count ? tr[t] : 0) * a.ks * kBf16StepBytes;
   }
-  f32x4_t acc[kPfNT][4];
-  pf_run<0, 4, kPfNT>(rows, PfSrc{reinterpret_cast<const uint4*>(a.a0), reinterpret_cast<const uint4*>(a.a1),
+  f32x4_t acc[kPfNT][kPfDenseNB];
+  pf_run<0, kPfDenseNB, kPfNT, kPfDenseDepth>(rows, PfSrc{reinterpret_cast<const uint4*>(a.a0), reinterpret_cast<const uint4*>(a.a1),
                                   nullptr, nt, a.n0, a.c1, a.n1},
                       trow, a.ks, sm, nullptr, acc);
+  const bool lo = c < 8;
 #pragma unroll
   for (int t = 0; t < kPfNT; ++t) {
-    if (tr[t] >= a.tr_count) continue;
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < kPfDenseNB; ++b)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int ti = 16 * b + 4 * g + v;
         const int64_t tok = t0 + ti;
         const float y = acc[t][b][v];
+        if (tr[t] >= a.tr_count) continue;
         if (!IN) {
           const int r = 16 * tr[t] + c;
           if (ti < nt && r < a.d) a.delta[tok * a.d + r] = y;
@@ -304,16 +370,31 @@ __global__ __launch_bounds__(kBlock) void k_pf_dense(PfDenseArgs a) {
         } else if (tr[t] < a.tr_r + a.tr_dn) {
           const int r = 16 * (tr[t] - a.tr_r) + c;
           if (ti < nt && r < a.l) a.xc[tok * a.l + r] = y;
-        } else {
-          const int r = 8 * (tr[t] - a.tr_r - a.tr_dn) + (c - 8);
-          const float gate = from_gate_lane(y);
-          if (c >= 8 && ti < nt && r < a.ms) {
-            const float h = glu_act(gate, y, a.act, a.bg, a.bl);
-            a.hs[tok * a.ms + r] = (uint16_t)(pack_bf16x2(h, 0.f) & 0xFFFFu);
-          }
         }
       }
   }
+  if (!IN) return;
+  // shared gate/up rows: tile rows t, t + 1 form a pair; lane c < 8 evaluates the h_s of
+  // tile row t (its gate, the up value of lane c + 8), lane c >= 8 that of tile row t + 1
+  const int sh0 = a.tr_r + a.tr_dn;
+#pragma unroll
+  for (int t = 0; t < kPfNT; t += 2)
+#pragma unroll
+    for (int b = 0; b < kPfDenseNB; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float send = lo ? acc[t + 1][b][v] : acc[t][b][v];
+        const float recv = swap_half_rows(send);
+        const float gate = lo ? acc[t][b][v] : recv;
+        const float up = lo ? recv : acc[t + 1][b][v];
+        const int trm = tr[lo ? t : t + 1];
+        const int ti = 16 * b + 4 * g + v;
+        const int r = 8 * (trm - sh0) + (c & 7);
+        if (trm >= sh0 && trm < a.tr_count && ti < nt && r < a.ms) {
+          const float h = glu_act_fast(gate, up, a.act, a.rbg, a.bg, a.rbl, a.bl);
+          a.hs[(t0 + ti) * a.ms + r] = (uint16_t)(pack_bf16x2(h, 0.f) & 0xFFFFu);
+        }
+      }
 }
 
 // x^c fp32 [T][l] -> MXFP8 rows of ks K-steps: codes [T][128 ks], scales [T][4 ks] (blocks
@@ -357,7 +438,7 @@ __global__ __launch_bounds__(kBlock) void k_pf_quant(const float* __restrict__ x
 
 // ------------------------------------------------------------------------------------
 // Routed experts, FP8 x MXFP4.  Work item (tile-row group, unit); a unit is a run of at
-// most 64 dispatch positions of one expert.  Gate/up: input rows x^c_q of the positions'
+// most 16 kPfExpNB dispatch positions of one expert.  Gate/up: input rows x^c_q of the positions'
 // tokens; each wavefront's 4 tile rows (8 gate + 8 up rows each) give one MX block of 32
 // columns of h = SiTU(gate, up), converted to MXFP8 in the epilogue.  Down: input rows
 // h_q of the positions, output E fp32.
@@ -377,7 +458,7 @@ struct PfExpArgs {
   uint8_t* hq;
   uint8_t* hsc;
   int ks_out, m, act;
-  float bg, bl;
+  float bg, bl, rbg, rbl;
   // down output
   float* out;
   int n_out;
@@ -390,7 +471,7 @@ __device__ __forceinline__ void pf_exp_unit(const PfExpArgs& a, const PfRows& ro
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane & 15, g = lane >> 4;
   f32x4_t acc[kPfNT][NB];
-  pf_run<1, NB, kPfNT>(rows, PfSrc{reinterpret_cast<const uint4*>(a.xq), nullptr,
+  pf_run<1, NB, kPfNT, kPfExpDepth>(rows, PfSrc{reinterpret_cast<const uint4*>(a.xq), nullptr,
                                    reinterpret_cast<const uint32_t*>(a.xs), n, 0, 0, 0},
                        trow, a.ks, sm, ssm, acc);
   if (!GU) {
@@ -408,48 +489,59 @@ __device__ __forceinline__ void pf_exp_unit(const PfExpArgs& a, const PfRows& ro
     }
     return;
   }
-  // h block wblk (columns 32 wblk .. +32) of each position: lanes c >= 8 hold column
-  // 32 wblk + 8 t + (c - 8) of tile row t
-  const bool blk_live = 32 * wblk < a.m;
+  // h block wblk (columns 32 wblk .. +32) of each position, 16 positions (one activation
+  // block) at a time through a wavefront-private LDS tile (fp32, rows of 36 words).  Tile
+  // row t holds the gate of column 8 t + (c % 8) in lane c < 8 and its up value in lane
+  // c + 8; the pair swaps halves so that lane c < 8 evaluates tile rows 0, 1 and lane
+  // c >= 8 tile rows 2, 3.  Then lane l converts row l / 4, columns 8 (l % 4) .. +8: the
+  // block's largest magnitude over the quad of lanes, the E8M0 byte, 8 codes, one 8-byte
+  // store.
   const int nbk = 4 * a.ks_out;
   if (32 * wblk >= 128 * a.ks_out) return;
+  const bool lo = c < 8;
+  float* tile = reinterpret_cast<float*>(sm) + (threadIdx.x >> 6) * 16 * 36;
+  const int rr = lane >> 2, qq = lane & 3;
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+  for (int b = 0; b < NB; ++b) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the previous block's reads are done
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int i = 16 * b + 4 * g + v;
-      float h[kPfNT];
-      float amax = 0.f;
+    for (int v = 0; v < 4; ++v)
 #pragma unroll
-      for (int t = 0; t < kPfNT; ++t) {
-        const float y = acc[t][b][v];
-        const float gate = from_gate_lane(y);
-        const int col = 8 * tr[t] + (c - 8);
-        h[t] = (blk_live && col < a.m) ? glu_act(gate, y, a.act, a.bg, a.bl) : 0.f;
-        if (c < 8) h[t] = 0.f;
-        amax = fmaxf(amax, fabsf(h[t]));
+      for (int tt = 0; tt < 2; ++tt) {
+        // lane c < 8 sends its gate of tile row 2 + tt, lane c + 8 its up of tile row tt
+        const float send = lo ? acc[2 + tt][b][v] : acc[tt][b][v];
+        const float recv = swap_half_rows(send);
+        const float gate = lo ? acc[tt][b][v] : recv;
+        const float up = lo ? recv : acc[2 + tt][b][v];
+        const int t = lo ? tt : 2 + tt;
+        const int col = 8 * tr[t] + (c & 7);
+        const float h = col < a.m ? glu_act_fast(gate, up, a.act, a.rbg, a.bg, a.rbl, a.bl) : 0.f;
+        tile[(4 * g + v) * 36 + 8 * t + (c & 7)] = h;
       }
-      // the block's largest magnitude: lanes 8..15 of the 16-lane row (lanes 0..7 hold 0)
-      amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-      amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
-      amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
-      amax = fmaxf(amax, __shfl_xor(amax, 8, kWave));
-      const uint32_t sb = mx8_scale_byte(amax);
-      const float inv = mx8_inv_scale(sb);
-      if (i < n) {
-        const int64_t p = p0 + i;
-        if (c >= 8) {
-#pragma unroll
-          for (int t = 0; t < kPfNT; ++t)
-            a.hq[p * 128 * a.ks_out + 32 * wblk + 8 * t + (c - 8)] = (uint8_t)to_e4m3(h[t] * inv);
-        }
-        if (c == 8) a.hsc[p * nbk + wblk] = (uint8_t)sb;
-      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile is written
+    const float4 x0 = *reinterpret_cast<const float4*>(tile + rr * 36 + 8 * qq);
+    const float4 x1 = *reinterpret_cast<const float4*>(tile + rr * 36 + 8 * qq + 4);
+    float amax = fmaxf(fmaxf(fmaxf(fabsf(x0.x), fabsf(x0.y)), fmaxf(fabsf(x0.z), fabsf(x0.w))),
+                       fmaxf(fmaxf(fabsf(x1.x), fabsf(x1.y)), fmaxf(fabsf(x1.z), fabsf(x1.w))));
+    amax = fmaxf(amax, quad_perm_f32<0xB1>(amax));   // lanes 1, 0, 3, 2 of the quad
+    amax = fmaxf(amax, quad_perm_f32<0x4E>(amax));   // lanes 2, 3, 0, 1
+    const uint32_t sb = mx8_scale_byte(amax);
+    const float inv = mx8_inv_scale(sb);
+    const int i = 16 * b + rr;
+    if (i < n) {
+      const int64_t p = p0 + i;
+      const uint2 w2 = make_uint2(pack4_e4m3(x0.x * inv, x0.y * inv, x0.z * inv, x0.w * inv),
+                                  pack4_e4m3(x1.x * inv, x1.y * inv, x1.z * inv, x1.w * inv));
+      *reinterpret_cast<uint2*>(a.hq + p * 128 * a.ks_out + 32 * wblk + 8 * qq) = w2;
+      if (qq == 0) a.hsc[p * nbk + wblk] = (uint8_t)sb;
     }
+  }
 }
 
 template <bool GU>
-__global__ __launch_bounds__(kBlock) void k_pf_exp(PfExpArgs a) {
+// two workgroups per compute unit (a register budget of 256 per lane): while one waits at
+// its barrier or for its loads the other issues MFMAs
+__global__ __launch_bounds__(kBlock, 2) void k_pf_exp(PfExpArgs a) {
   extern __shared__ uint4 sm[];
   __shared__ PfRows rows;
   __shared__ uint32_t ssm[2 * kPfRows];
@@ -480,10 +572,11 @@ __global__ __launch_bounds__(kBlock) void k_pf_exp(PfExpArgs a) {
     tr[t] = wblk * kPfNT + t;
     trow[t] = base + (size_t)(tr[t] < a.n_tr ? tr[t] : 0) * a.ks * kFp4StepBytes;
   }
-  if (n <= 16) pf_exp_unit<GU, 1>(a, rows, sm, ssm, trow, tr, wblk, p0, n);
-  else if (n <= 32) pf_exp_unit<GU, 2>(a, rows, sm, ssm, trow, tr, wblk, p0, n);
-  else if (n <= 48) pf_exp_unit<GU, 3>(a, rows, sm, ssm, trow, tr, wblk, p0, n);
-  else pf_exp_unit<GU, 4>(a, rows, sm, ssm, trow, tr, wblk, p0, n);
+  // blocks of 16 positions: the unit's count rounded up to one of the built tile heights
+  const int nb = (n + 15) / 16;
+  if (nb <= 1) pf_exp_unit<GU, 1>(a, rows, sm, ssm, trow, tr, wblk, p0, n);
+  else if (nb <= 2) pf_exp_unit<GU, 2>(a, rows, sm, ssm, trow, tr, wblk, p0, n);
+  else pf_exp_unit<GU, kPfExpNB>(a, rows, sm, ssm, trow, tr, wblk, p0, n);
 }
 
 // u_hat = RMSNorm(u) * gamma rounded to bf16 (the OUT product's input), one workgroup per
@@ -516,8 +609,8 @@ __global__ __launch_bounds__(kBlock) void k_pf_norm(const float* __restrict__ u,
   }
 }
 
-constexpr size_t kPfDenseLds = (size_t)2 * kPfRows * 16 * 16;   // two K-steps of 64 bf16 rows
-constexpr size_t kPfExpLds = (size_t)2 * kPfRows * 8 * 16;      // two K-steps of 64 FP8 rows
+constexpr size_t kPfDenseLds = (size_t)2 * 16 * kPfDenseNB * 16 * 16;   // two K-steps of the bf16 rows
+constexpr size_t kPfExpLds = (size_t)2 * 16 * kPfExpNB * 8 * 16;       // two K-steps of the FP8 rows
 
 }  // namespace
 
@@ -528,7 +621,7 @@ hipError_t launch_pf_in(const Shape& s, const uint8_t* dense, const uint16_t* x,
   a.ks = s.ks_in;
   a.tr_count = s.tr_in;
   a.n_grp = cdiv(s.tr_in, kPfWaves * kPfNT);
-  a.n_tiles = cdiv(T, kPfRows);
+  a.n_tiles = cdiv(T, 16 * kPfDenseNB);
   a.a0 = x; a.lda0 = s.d; a.n0 = s.d;
   a.a1 = x; a.lda1 = 0; a.c1 = 0; a.n1 = 0;
   a.T = T;
@@ -536,6 +629,7 @@ hipError_t launch_pf_in(const Shape& s, const uint8_t* dense, const uint16_t* x,
   a.z = z; a.E = s.E;
   a.xc = xc; a.l = s.l;
   a.hs = pw.hs; a.ms = s.ms; a.act = s.act; a.bg = s.beta_gate; a.bl = s.beta_lin;
+  a.rbg = 1.f / s.beta_gate; a.rbl = 1.f / s.beta_lin;
   hipLaunchKernelGGL(k_pf_dense<true>, dim3((unsigned)xcd_grid(a.n_grp, a.n_tiles)), dim3(kBlock),
                      kPfDenseLds, st, a);
   return hipGetLastError();
@@ -570,6 +664,7 @@ hipError_t launch_pf_expert(const Shape& s, const uint8_t* experts, bool gu, int
   a.hq = pw.hq; a.hsc = pw.hsc;
   a.ks_out = s.ks_edn;
   a.m = s.m; a.act = s.act; a.bg = s.beta_gate; a.bl = s.beta_lin;
+  a.rbg = 1.f / s.beta_gate; a.rbl = 1.f / s.beta_lin;
   a.out = ws.eo;
   a.n_out = s.l;
   const unsigned grid = (unsigned)xcd_grid(a.n_grp, a.max_units);
@@ -593,7 +688,7 @@ hipError_t launch_pf_out(const Shape& s, const uint8_t* dense, int64_t T, const 
   a.ks = s.ks_out;
   a.tr_count = s.tr_out;
   a.n_grp = cdiv(s.tr_out, kPfWaves * kPfNT);
-  a.n_tiles = cdiv(T, kPfRows);
+  a.n_tiles = cdiv(T, 16 * kPfDenseNB);
   a.a0 = pw.uh; a.lda0 = s.l; a.n0 = s.l;
   a.a1 = s.ms > 0 ? pw.hs : pw.uh; a.lda1 = s.ms; a.c1 = s.ks_l * kStepK; a.n1 = s.ms;
   a.T = T;

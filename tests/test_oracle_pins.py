@@ -444,3 +444,5 @@ def test_selection_kappa_ranks_and_gives_the_margin():
     # brute force: the kappas of the selected experts, in selection order
     want = np.float32(s).astype(np.float64)[np.arange(40)[:, None], idx] + b[idx]
     assert np.allclose(kap[:, :6], want, rtol=0, atol=1e-7)
+    full = O.selection_kappa(s[:, :6], b[:6], 6)    # E == k
+    assert full.shape == (40, 7) and np.all(np.isneginf(full[:, 6]))
