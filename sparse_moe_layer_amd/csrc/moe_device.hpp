@@ -149,14 +149,21 @@ struct WeightStep {
   static constexpr int NW = WF ? 1 : 4;
   uint4 w[NW];
   uint32_t sc;
+  // K-step q of the tile row.  Streaming (non-temporal) loads where every weight is read
+  // once per call; cached loads where several workgroups read the same weights in a short
+  // window (the compute-bound launches).
+  template <bool CACHED = false>
   __device__ __forceinline__ void load(const uint8_t* trow, int q, int lane) {
     const uint8_t* p = trow + (size_t)q * SB;
     if (WF) {
-      w[0] = ld_stream(p + lane * 16);
-      sc = ld_stream32(p + 1024 + (lane & 15) * 4);
+      w[0] = CACHED ? *reinterpret_cast<const uint4*>(p + lane * 16) : ld_stream(p + lane * 16);
+      sc = CACHED ? *reinterpret_cast<const uint32_t*>(p + 1024 + (lane & 15) * 4)
+                  : ld_stream32(p + 1024 + (lane & 15) * 4);
     } else {
 #pragma unroll
-      for (int s = 0; s < NW; ++s) w[s] = ld_stream(p + s * 1024 + lane * 16);
+      for (int s = 0; s < NW; ++s)
+        w[s] = CACHED ? *reinterpret_cast<const uint4*>(p + s * 1024 + lane * 16)
+                      : ld_stream(p + s * 1024 + lane * 16);
     }
   }
   // the lane's E8M0 scale as an fp32 power of two (MXFP4)

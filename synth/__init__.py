@@ -158,9 +158,13 @@ TOY = LayerConfig(
     name="toy_latent_moe_d640_l320_e64k2_t16", d=640, l=320, E=64, k=2, m=256, ms=512,
     tokens=16, seed=1001, expert_fmt="bf16", bias_kind="uniform", bias_a=-0.01, bias_b=0.01)
 
-# N(0, 1e-3) for the bias: the second argument is read as the variance, as in N(0, 0.02^2).
+# Router bias N(0, 1e-3): the second argument is read as the standard deviation.  The
+# prefill workload is described as near-uniform routing under this bias, which holds for a
+# spread of 1e-3 (every expert used, per-expert load within about +-11%) but not for a
+# variance of 1e-3 (std 0.032 outweighs the gaps between the top sigmoid scores: a fifth of
+# the experts never chosen, others taking six times the mean).
 _K3 = dict(d=7168, l=3584, E=896, k=16, m=3072, ms=6144, expert_fmt="mxfp4",
-           bias_kind="normal", bias_a=0.0, bias_b=float(np.sqrt(1e-3)))
+           bias_kind="normal", bias_a=0.0, bias_b=1e-3)
 K3_DECODE_B1 = LayerConfig(name="k3_latent_moe_decode_b1", tokens=1, seed=1002, **_K3)
 K3_DECODE_B64_ZIPF = LayerConfig(
     name="k3_latent_moe_decode_b64_zipf1.0", tokens=64, seed=1003,
