@@ -45,6 +45,7 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "e2m1_decode", "e8m0_decode", "dequant_mxfp4", "E2M1_GRID",
     "e4m3_decode", "round_e4m3", "E4M3_MAX", "quantize_mx8", "round_bf16", "PRECISIONS",
+    "dequant_fp8_block128",
     "sigmoid", "select_and_weight", "selection_kappa", "router_scores", "situ", "swiglu", "glu", "rmsnorm",
     "OracleLayer", "forward", "routed_sum_dense_mask", "Result", "dispatch",
 ]
@@ -121,6 +122,17 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     mant = (c & 0x7).astype(np.float64)
     mag = np.where(e == 0, mant / 8.0 * 2.0 ** -6, np.ldexp(1.0 + mant / 8.0, (e - 7).astype(np.int64)))
     return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def dequant_fp8_block128(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """FP8 E4M3 codes [.., rows, cols] with one fp32 scale per 128 x 128 block
+    [.., ceil(rows/128), ceil(cols/128)] -> float64: code value times its block's scale
+    (the K2 block card's expert weights: FP8 with 128 x 128 block scales)."""
+    codes = np.asarray(codes)
+    rows, cols = codes.shape[-2:]
+    s = np.asarray(scales, dtype=np.float64)
+    full = np.repeat(np.repeat(s, 128, axis=-2), 128, axis=-1)[..., :rows, :cols]
+    return e4m3_decode(codes) * full
 
 
 def _binade(a: np.ndarray) -> np.ndarray:
@@ -337,6 +349,8 @@ class OracleLayer:
 def _slice_to_f64(sl):
     if sl.fmt == "bf16":
         return bf16_to_f64(sl.gu), bf16_to_f64(sl.down)
+    if sl.fmt == "fp8b128":
+        return dequant_fp8_block128(sl.gu, sl.gu_scale), dequant_fp8_block128(sl.down, sl.down_scale)
     return dequant_mxfp4(sl.gu, sl.gu_scale), dequant_mxfp4(sl.down, sl.down_scale)
 
 

@@ -18,6 +18,8 @@ Canonical storage (both sides read exactly these arrays):
      MXFP4 layers: codes [E, rows, cols/2] uint8 (low nibble = even column)
                    plus E8M0 scales [E, rows, cols/32] uint8, blocks of 32
                    along the input (reduction) axis.
+     FP8 block-128 layers: E4M3 codes [E, rows, cols] uint8 plus fp32 scales
+                   [E, ceil(rows/128), ceil(cols/128)], one per 128 x 128 block.
   bias          [E]           fp32
   x             [T, d]        bf16
 """
@@ -61,8 +63,10 @@ def _load():
     lib.synth_uniform_f32.argtypes = [u64, u64, u64, u64, ctypes.c_double, ctypes.c_double, vp]
     lib.synth_bytes.argtypes = [u64, u64, u64, u64, vp]
     lib.synth_uniform_int_u8.argtypes = [u64, u64, u64, u64, ctypes.c_uint32, ctypes.c_uint32, vp]
+    lib.synth_fp8_block128.argtypes = [u64, u64, u64, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_double, vp, vp]
     for f in ("synth_normal_bf16", "synth_normal_f32", "synth_uniform_f32", "synth_bytes",
-              "synth_uniform_int_u8"):
+              "synth_uniform_int_u8", "synth_fp8_block128"):
         getattr(lib, f).restype = None
     _lib = lib
     return lib
@@ -115,6 +119,19 @@ def uniform_int_u8(seed, name, start, shape, lo, hi, out=None):
     return out
 
 
+def fp8_block128(seed, name, start, rows, cols, std, codes_out=None, scales_out=None):
+    """One [rows, cols] matrix as FP8 E4M3 codes with an fp32 scale per 128 x 128 block
+    (scale = block max |w| / 448; w = std x a unit-variance Irwin-Hall(4) draw, close to
+    N(0, std^2), from stream `name` at `start`)."""
+    codes = np.empty((rows, cols), np.uint8) if codes_out is None else codes_out
+    scales = (np.empty(((rows + 127) // 128, (cols + 127) // 128), np.float32)
+              if scales_out is None else scales_out)
+    assert codes.flags.c_contiguous and scales.flags.c_contiguous
+    _load().synth_fp8_block128(seed, stream_id(name), start, rows, cols, std, codes.ctypes.data,
+                               scales.ctypes.data)
+    return codes, scales
+
+
 # --------------------------------------------------------------------------------------
 # Layer presets.  Shapes follow the Kimi K3 latent-MoE block card (parameter table) and
 # the toy reproduction chapter (640 -> 320 latent, 64 experts, top-2, merged 2x256 shared).
@@ -135,7 +152,7 @@ class LayerConfig:
     ms: int           # shared hidden width (merged shared experts)
     tokens: int       # tokens per call of the workload
     seed: int
-    expert_fmt: str = "mxfp4"        # "bf16" | "mxfp4"
+    expert_fmt: str = "mxfp4"        # "bf16" | "mxfp4" | "fp8b128"
     act: str = "situ"                # "situ" | "swiglu"
     route_scale: float = 1.0
     use_norm: bool = True
@@ -173,7 +190,16 @@ K3_DECODE_B64_ZIPF = LayerConfig(
 K3_PREFILL_8K = LayerConfig(name="k3_latent_moe_prefill_8192", tokens=8192, seed=1004,
                             precision="mx8", **_K3)
 
-PRESETS = {c.name: c for c in (TOY, K3_DECODE_B1, K3_DECODE_B64_ZIPF, K3_PREFILL_8K)}
+# The K2 block card's non-latent MoE block on the same kernels: 384 SwiGLU experts top-8,
+# gate weights renormalised and scaled by 2.827, one shared 2048-wide expert, FP8 E4M3
+# experts with 128 x 128 fp32 block scales, 1024 tokens with Zipf(1.2)-loaded routing.
+K2_MOE_1024_ZIPF = LayerConfig(
+    name="k2_moe_1024_zipf1.2", d=7168, l=0, E=384, k=8, m=2048, ms=2048, tokens=1024, seed=1005,
+    expert_fmt="fp8b128", act="swiglu", route_scale=2.827, use_norm=False,
+    bias_kind="file", bias_file="k2_zipf1.2_bias.f32")
+
+PRESETS = {c.name: c for c in (TOY, K3_DECODE_B1, K3_DECODE_B64_ZIPF, K3_PREFILL_8K,
+                               K2_MOE_1024_ZIPF)}
 
 
 def param_shapes(cfg: LayerConfig) -> dict:
@@ -242,10 +268,10 @@ class ExpertSlice:
     e0: int
     e1: int
     fmt: str
-    gu: np.ndarray               # bf16 [n, 2m, l] or codes [n, 2m, l/2]
-    down: np.ndarray             # bf16 [n, l, m]  or codes [n, l, m/2]
-    gu_scale: np.ndarray | None = None    # [n, 2m, l/32]
-    down_scale: np.ndarray | None = None  # [n, l, m/32]
+    gu: np.ndarray               # bf16 [n, 2m, l] or codes [n, 2m, l/2] (fp8: [n, 2m, l])
+    down: np.ndarray             # bf16 [n, l, m]  or codes [n, l, m/2] (fp8: [n, l, m])
+    gu_scale: np.ndarray | None = None    # [n, 2m, l/32] (fp8: fp32 [n, 2m/128, l/128])
+    down_scale: np.ndarray | None = None  # [n, l, m/32] (fp8: fp32 [n, l/128, m/128])
 
 
 def expert_slice(cfg: LayerConfig, e0: int, e1: int, out: ExpertSlice | None = None) -> ExpertSlice:
@@ -274,6 +300,18 @@ def expert_slice(cfg: LayerConfig, e0: int, e1: int, out: ExpertSlice | None = N
                              (n, r_dn, c_dn // 32), cfg.e8m0_lo, cfg.e8m0_hi,
                              out=None if out is None else out.down_scale)
         return ExpertSlice(e0, e1, "mxfp4", gu, dn, gus, dns)
+    if cfg.expert_fmt == "fp8b128":
+        gu = np.empty((n, r_gu, c_gu), np.uint8) if out is None else out.gu
+        dn = np.empty((n, r_dn, c_dn), np.uint8) if out is None else out.down
+        gus = (np.empty((n, (r_gu + 127) // 128, (c_gu + 127) // 128), np.float32)
+               if out is None else out.gu_scale)
+        dns = (np.empty((n, (r_dn + 127) // 128, (c_dn + 127) // 128), np.float32)
+               if out is None else out.down_scale)
+        for i in range(n):
+            e = e0 + i
+            fp8_block128(cfg.seed, "expert_gu", e * r_gu * c_gu, r_gu, c_gu, WEIGHT_STD, gu[i], gus[i])
+            fp8_block128(cfg.seed, "expert_down", e * r_dn * c_dn, r_dn, c_dn, WEIGHT_STD, dn[i], dns[i])
+        return ExpertSlice(e0, e1, "fp8b128", gu, dn, gus, dns)
     raise ValueError(cfg.expert_fmt)
 
 

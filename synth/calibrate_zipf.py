@@ -1,9 +1,10 @@
-"""Router bias of the K3 decode B=64 workload: expert load shaped as a capped Zipf(s).
+"""Router biases with expert load shaped as a capped Zipf(s).
 
-Writes synth/data/k3_zipf1.0_bias.f32 (E little-endian float32), the input that the
-preset K3_DECODE_B64_ZIPF loads.  Input tooling, run offline once:
+Writes synth/data/k3_zipf1.0_bias.f32 (the K3 decode B=64 workload, Zipf(1.0)) or, with
+the argument "k2", synth/data/k2_zipf1.2_bias.f32 (the K2-style block, Zipf(1.2)): E
+little-endian float32, the input the presets load.  Input tooling, run offline once:
 
-    python -m synth.calibrate_zipf
+    python -m synth.calibrate_zipf [k2]
 
 It calls the float64 oracle's router for the scores and nothing of the HIP path.
 
@@ -36,6 +37,7 @@ import oracle  # noqa: E402
 import synth  # noqa: E402
 
 ZIPF_S = 1.0
+K2_ZIPF_S = 1.2
 CAL_TOKENS = 16384
 CAL_BATCH = 900_000          # token stream of the calibration batch (never timed)
 PERM_SEED = 20_251           # seeds the expert ranking
@@ -83,12 +85,13 @@ def qb_bias(s: np.ndarray, k: int, q: np.ndarray, saturated: np.ndarray, iters: 
     return -beta, load, it + 1
 
 
-def main():
-    cfg = synth.K3_DECODE_B64_ZIPF
+def main(cfg=None, zipf_s=None):
+    cfg = synth.K3_DECODE_B64_ZIPF if cfg is None else cfg
+    zipf_s = ZIPF_S if zipf_s is None else zipf_s
     dense = synth.dense_weights(cfg.with_(bias_kind="normal", bias_a=0.0, bias_b=0.0))
     w_r = oracle.bf16_to_f64(dense.router)
     rng = np.random.default_rng(PERM_SEED)
-    pi, rank, c = zipf_targets(cfg.E, cfg.k, ZIPF_S, rng)
+    pi, rank, c = zipf_targets(cfg.E, cfg.k, zipf_s, rng)
     saturated = pi >= 1.0
     print(f"c = {c:.4f}, saturated experts {int(saturated.sum())}, sum pi = {pi.sum():.6f}")
     s = np.empty((CAL_TOKENS, cfg.E))
@@ -105,4 +108,8 @@ def main():
 
 
 if __name__ == "__main__":
-    main()
+    # default: the K3 decode B=64 layer, Zipf(1.0); "k2": the K2-style block, Zipf(1.2)
+    if len(sys.argv) > 1 and sys.argv[1] == "k2":
+        main(synth.K2_MOE_1024_ZIPF, K2_ZIPF_S)
+    else:
+        main()

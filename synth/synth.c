@@ -3,7 +3,8 @@
  *
  * This module holds no arithmetic of the layer itself: it only turns
  * (seed, stream, index) triples into bytes, bf16 normals, fp32 normals and
- * uniforms, and E8M0 exponent bytes.  Both the CPU oracle and the HIP path
+ * uniforms, E8M0 exponent bytes, and FP8 E4M3 weight codes with their block
+ * scales (how the synthetic checkpoint stores a block-scaled FP8 matrix).  Both the CPU oracle and the HIP path
  * read what it writes, so neither side ever produces the other's inputs.
  *
  * Every element is a pure function of (seed, stream, index), so any slice of
@@ -128,5 +129,67 @@ void synth_uniform_int_u8(uint64_t seed, uint64_t stream, uint64_t start, uint64
     /* multiply-high of a 32-bit uniform by the span: bias below 2^-24 */
     uint64_t r = ((w >> 32) * span) >> 32;
     out[i] = (uint8_t)(lo + r);
+  }
+}
+
+/* E4M3 code (OCP 8-bit floating point, E4M3 variant: bias 7, 3 mantissa bits, subnormals
+ * below 2^-6, largest finite 448) of an fp32 value with |y| <= 448, rounded to the nearest
+ * representable value, ties to the even mantissa. */
+static inline uint8_t e4m3_code(float y) {
+  uint32_t u;
+  memcpy(&u, &y, 4);
+  const uint8_t sign = (uint8_t)((u >> 24) & 0x80u);
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a < 0x3C800000u) {                    /* below 2^-6: multiples of 2^-9 (code 8 = 2^-6) */
+    float m = rintf(fabsf(y) * 512.0f);
+    return (uint8_t)(sign | (uint8_t)m);
+  }
+  /* keep 3 of the 23 mantissa bits, rounding to nearest even (a carry moves the exponent) */
+  const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) & 0xFFF00000u;
+  const int e = (int)(r >> 23) - 127;
+  return (uint8_t)(sign | (uint8_t)(((e + 7) << 3) | ((r >> 20) & 7u)));
+}
+
+/* Approximately standard normal from one word: the sum of its four 16-bit uniforms,
+ * centred and scaled to unit variance (Irwin-Hall, n = 4; range +-2 sqrt 3).  No
+ * transcendental, for the multi-gigabyte FP8 expert sets. */
+static inline float irwin_hall4(uint64_t w) {
+  const float inv16 = 1.0f / 65536.0f;
+  float sum = 0.f;
+  for (int k = 0; k < 4; ++k) sum += ((float)((w >> (16 * k)) & 0xFFFFu) + 0.5f) * inv16;
+  return (sum - 2.0f) * 1.7320508075688772f;
+}
+
+/* A matrix of FP8 E4M3 weights with one fp32 scale per 128 x 128 block (the K2 block
+ * card's expert format as the synthetic layers store it): w = std * irwin_hall4 of the
+ * word of element r * cols + c (stream index start + r * cols + c); per block
+ * scale = max |w| / 448 in fp32, code = E4M3 of the fp32 quotient w / scale.
+ * codes: rows * cols bytes, row-major; scales: ceil(rows/128) * ceil(cols/128) floats. */
+void synth_fp8_block128(uint64_t seed, uint64_t stream, uint64_t start, int64_t rows, int64_t cols,
+                        double std, uint8_t* codes, float* scales) {
+  uint64_t key = stream_key(seed, stream);
+  const int64_t br = (rows + 127) / 128, bc = (cols + 127) / 128;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < br * bc; ++b) {
+    const int64_t r0 = (b / bc) * 128, c0 = (b % bc) * 128;
+    const int64_t r1 = r0 + 128 < rows ? r0 + 128 : rows, c1 = c0 + 128 < cols ? c0 + 128 : cols;
+    float wb[128 * 128];
+    float amax = 0.f;
+    for (int64_t r = r0; r < r1; ++r)
+      for (int64_t c = c0; c < c1; ++c) {
+        float w = (float)std * irwin_hall4(word_at(key, start + (uint64_t)(r * cols + c)));
+        wb[(r - r0) * 128 + (c - c0)] = w;
+        float aw = fabsf(w);
+        if (aw > amax) amax = aw;
+      }
+    const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+    scales[b] = s;
+    for (int64_t r = r0; r < r1; ++r)
+      for (int64_t c = c0; c < c1; ++c) {
+        float y = wb[(r - r0) * 128 + (c - c0)] / s;
+        if (y > 448.0f) y = 448.0f;
+        if (y < -448.0f) y = -448.0f;
+        codes[r * cols + c] = e4m3_code(y);
+      }
   }
 }
