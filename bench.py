@@ -29,19 +29,27 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def expert_weight_bytes(cfg):
+    """(gate/up, down) bytes of one routed expert in its storage format."""
+    l, m = cfg.l or cfg.d, cfg.m
+    if cfg.expert_fmt == "mxfp4":
+        return 2 * m * (l // 2 + l // 32), l * (m // 2 + m // 32)
+    if cfg.expert_fmt == "fp8b128":
+        cd = lambda a, b: (a + b - 1) // b  # noqa: E731
+        return 2 * m * l + 4 * cd(2 * m, 128) * cd(l, 128), l * m + 4 * cd(l, 128) * cd(m, 128)
+    return 2 * m * l * 2, l * m * 2
+
+
 def algorithmic_bytes(cfg, T, D):
     """Compulsory HBM bytes of each step for T tokens touching D distinct experts."""
-    d, l, E, k, m, ms = cfg.d, cfg.l, cfg.E, cfg.k, cfg.m, cfg.ms
-    if cfg.expert_fmt == "mxfp4":
-        gu_w = 2 * m * (l // 2 + l // 32)
-        dn_w = l * (m // 2 + m // 32)
-    else:
-        gu_w, dn_w = 2 * m * l * 2, l * m * 2
+    d, E, k, m, ms = cfg.d, cfg.E, cfg.k, cfg.m, cfg.ms
+    l = cfg.l or cfg.d           # the experts' width (the token itself without a latent)
+    gu_w, dn_w = expert_weight_bytes(cfg)
     tk = T * k
     small = T <= 3   # the route and the dispatch run inside the IN launch
     sh_head = 0   # shared gate/up rows in the ROUTER launch
     return {
-        "router": T * d * 2 + (E + l + 2 * sh_head) * d * 2 + T * (E + l + sh_head) * 4,
+        "router": T * d * 2 + (E + cfg.l + 2 * sh_head) * d * 2 + T * (E + l + sh_head) * 4,
         "in": T * d * 2 + 2 * (ms - sh_head) * d * 2 + T * (ms - sh_head) * 4
               + ((T * E * 4 + E * 4 + tk * 16 + E * 8) if small else 0),
         "route": 0 if small else T * E * 4 + E * 4 + tk * 8,
@@ -49,15 +57,16 @@ def algorithmic_bytes(cfg, T, D):
         "expert_gu": D * gu_w + T * l * 4 + tk * m * 4,
         "expert_down": D * dn_w + tk * m * 4 + tk * l * 4,
         "combine": tk * l * 4 + tk * 8 + T * l * 4,
-        "out": d * (l + ms) * 2 + l * 2 + T * (l + ms) * 4 + T * d * 4,
+        "out": d * (cfg.l + ms) * 2 + cfg.l * 2 + T * (l + ms) * 4 + T * d * 4,
     }
 
 def algorithmic_flops(cfg, T):
     """Multiply-add flops (2 per product) of each step for T tokens."""
     d, l, E, k, m, ms = cfg.d, cfg.l, cfg.E, cfg.k, cfg.m, cfg.ms
     tk = T * k
+    lx = l or d                  # the experts' width (the token itself without a latent)
     return {"router": 2 * T * d * (E + l + 2 * ms), "in": 0, "route": 0, "dispatch": 0,
-            "expert_gu": 2 * tk * l * 2 * m, "expert_down": 2 * tk * m * l, "combine": 2 * tk * l,
+            "expert_gu": 2 * tk * lx * 2 * m, "expert_down": 2 * tk * m * lx, "combine": 2 * tk * lx,
             "out": 2 * T * (l + ms) * d}
 
 
@@ -67,10 +76,8 @@ MFMA_PEAK = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
 
 def weight_bytes(cfg, D):
     """Weights (and the fp32 bias) one call reads: the layer's algorithmic byte count."""
-    d, l, E, m, ms = cfg.d, cfg.l, cfg.E, cfg.m, cfg.ms
-    per_expert = (2 * m * (l // 2 + l // 32) + l * (m // 2 + m // 32)) if cfg.expert_fmt == "mxfp4" \
-        else 3 * m * l * 2
-    return (E * d + 2 * l * d + l + 3 * ms * d) * 2 + E * 4 + D * per_expert
+    d, l, E, ms = cfg.d, cfg.l, cfg.E, cfg.ms
+    return (E * d + 2 * l * d + l + 3 * ms * d) * 2 + E * 4 + D * sum(expert_weight_bytes(cfg))
 
 
 # rocprofv3 kernel symbol of each step's launch (its template arguments vary with shape)

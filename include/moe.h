@@ -59,8 +59,11 @@ typedef enum moe_act {
 
 typedef enum moe_wfmt {
   MOE_WFMT_BF16 = 0,  /* bf16 expert weights */
-  MOE_WFMT_MXFP4 = 1  /* E2M1 codes, two per byte (low nibble = even column), plus one
+  MOE_WFMT_MXFP4 = 1, /* E2M1 codes, two per byte (low nibble = even column), plus one
                          E8M0 scale byte per 32 consecutive input columns of a row */
+  MOE_WFMT_FP8_B128 = 2 /* FP8 E4M3 codes, one per byte, plus one fp32 scale per block of
+                           128 x 128 weights (the K2 block card's expert format); the
+                           scale multiplies the fp32 partial sums of its block */
 } moe_wfmt;
 
 typedef enum moe_precision {
@@ -78,10 +81,15 @@ typedef enum moe_precision {
 /* Layer shape and options.  K3: d_model 7168, d_latent 3584, n_experts 896, top_k 16,
  * d_expert 3072, d_shared 6144 (two merged 3072-wide shared experts), SiTU with
  * beta_gate 4 and beta_lin 25, route_scale 1, use_latent_norm 1 (block card: parameter
- * table and config fields; walkthrough: SituAndMul and the activation_situ_* fields). */
+ * table and config fields; walkthrough: SituAndMul and the activation_situ_* fields).
+ * A non-latent block (d_latent 0; the K2 block card: 384 SwiGLU experts top-8, gate
+ * scale 2.827, one shared expert) routes the token itself: the experts read x and write
+ * d-wide rows, and Delta = sum_j G_j E_j + the shared path (no W_down_latent, norm or
+ * W_up_latent; it needs a shared expert). */
 typedef struct moe_config {
   int32_t d_model;         /* d: token width; multiple of 8 */
-  int32_t d_latent;        /* l: latent width of the routed experts; multiple of 8 (> 0) */
+  int32_t d_latent;        /* l: latent width of the routed experts; multiple of 8; 0 for a
+                              non-latent block (the experts then take the d-wide token) */
   int32_t n_experts;       /* E: routed experts, 1..1024 */
   int32_t top_k;           /* k: experts per token, 1..min(E, 64) */
   int32_t d_expert;        /* m: routed expert hidden width; multiple of 8 */
@@ -92,11 +100,13 @@ typedef struct moe_config {
   float beta_gate;         /* SiTU gate cap (4) */
   float beta_lin;          /* SiTU up-branch cap (25) */
   int32_t act;             /* moe_act */
-  int32_t expert_wfmt;     /* moe_wfmt; MXFP4 needs d_latent and d_expert divisible by 32 */
+  int32_t expert_wfmt;     /* moe_wfmt; MXFP4 needs the expert widths divisible by 32 */
   int32_t precision;       /* moe_precision */
 } moe_config;
 
-/* Canonical dense weights, bf16 [out, in] (as moe_pack_dense reads them). */
+/* Canonical dense weights, bf16 [out, in] (as moe_pack_dense reads them).  Without a
+ * latent (d_latent 0) w_down_latent, w_up_latent and norm_gamma are not read (may be
+ * null). */
 typedef struct moe_dense_src {
   const void* router;        /* W_r           [E, d]       bf16 */
   const void* w_down_latent; /* W_down_latent [l, d]       bf16 */
@@ -118,7 +128,10 @@ typedef struct moe_weights {
  * rows m..2m-1 up, each row l wide; down is [l, m].
  *   BF16:  gu = [n][2m][l] bf16, down = [n][l][m] bf16, scale pointers unused.
  *   MXFP4: gu = [n][2m][l/2] code bytes, gu_scale = [n][2m][l/32] E8M0 bytes,
- *          down = [n][l][m/2], down_scale = [n][l][m/32]. */
+ *          down = [n][l][m/2], down_scale = [n][l][m/32].
+ *   FP8_B128: gu = [n][2m][l] E4M3 bytes, gu_scale = [n][ceil(2m/128)][ceil(l/128)] fp32,
+ *          down = [n][l][m], down_scale = [n][ceil(l/128)][ceil(m/128)] fp32.
+ * For a non-latent block l is d_model. */
 typedef struct moe_expert_src {
   const void* gu;
   const void* gu_scale;

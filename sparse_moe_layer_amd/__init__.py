@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 ACT = {"situ": 0, "swiglu": 1}
-WFMT = {"bf16": 0, "mxfp4": 1}
+WFMT = {"bf16": 0, "mxfp4": 1, "fp8b128": 2}
 PREC = {"fp32": 0, "mx8": 1}
 WS_SLOTS = ("ctrl", "xc", "hs", "h", "eo", "u", "uh", "hl", "perm", "inv", "counts", "offsets", "z",
             "chunk_hist", "units")
@@ -231,6 +231,9 @@ class Layer:
             if cfg.expert_wfmt == WFMT["mxfp4"]:
                 t = [_dev_u8(sl.gu, device), _dev_u8(sl.gu_scale, device),
                      _dev_u8(sl.down, device), _dev_u8(sl.down_scale, device)]
+            elif cfg.expert_wfmt == WFMT["fp8b128"]:
+                t = [_dev_u8(sl.gu, device), _dev_u8(np.ascontiguousarray(sl.gu_scale, np.float32).view(np.uint8), device),
+                     _dev_u8(sl.down, device), _dev_u8(np.ascontiguousarray(sl.down_scale, np.float32).view(np.uint8), device)]
             else:
                 t = [_dev_u16(sl.gu, device), None, _dev_u16(sl.down, device), None]
             src = MoeExpertSrc(*[_ptr(v) for v in t])

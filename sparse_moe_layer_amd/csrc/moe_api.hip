@@ -22,26 +22,30 @@ moe_status make_shape(const moe_config* c, Shape* s) {
     return MOE_ERR_INVALID_ARG;
   if (c->top_k > c->n_experts) return MOE_ERR_INVALID_ARG;
   if (c->act != MOE_ACT_SITU && c->act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
-  if (c->expert_wfmt != MOE_WFMT_BF16 && c->expert_wfmt != MOE_WFMT_MXFP4) return MOE_ERR_INVALID_ARG;
+  if (c->expert_wfmt != MOE_WFMT_BF16 && c->expert_wfmt != MOE_WFMT_MXFP4 &&
+      c->expert_wfmt != MOE_WFMT_FP8_B128)
+    return MOE_ERR_INVALID_ARG;
   if (!(c->rms_eps >= 0.f) || !(c->route_scale == c->route_scale)) return MOE_ERR_INVALID_ARG;
   if (c->act == MOE_ACT_SITU && !(c->beta_gate > 0.f && c->beta_lin > 0.f)) return MOE_ERR_INVALID_ARG;
   if (c->d_model % 8 || c->d_latent % 8 || c->d_expert % 8 || c->d_shared % 8)
     return MOE_ERR_INVALID_ARG;
-  if (c->expert_wfmt == MOE_WFMT_MXFP4 && (c->d_latent % 32 || c->d_expert % 32))
-    return MOE_ERR_INVALID_ARG;
+  const int32_t lin = c->d_latent > 0 ? c->d_latent : c->d_model;   // the experts' input width
+  if (c->expert_wfmt == MOE_WFMT_MXFP4 && (lin % 32 || c->d_expert % 32)) return MOE_ERR_INVALID_ARG;
   if (c->precision != MOE_PREC_FP32 && c->precision != MOE_PREC_MX8) return MOE_ERR_INVALID_ARG;
   if (c->precision == MOE_PREC_MX8 && c->expert_wfmt != MOE_WFMT_MXFP4) return MOE_ERR_UNSUPPORTED;
-  if (c->d_latent == 0) return MOE_ERR_UNSUPPORTED;  // non-latent blocks: not built yet
+  if (c->d_latent == 0 && c->d_shared == 0) return MOE_ERR_UNSUPPORTED;  // non-latent needs a shared expert
+  if (c->d_latent == 0 && c->precision == MOE_PREC_MX8) return MOE_ERR_UNSUPPORTED;
   if (c->n_experts > 1024 || c->top_k > 64) return MOE_ERR_UNSUPPORTED;
   if (c->d_model > 8192 || c->d_latent > 8192 || c->d_expert > 8192 || c->d_shared > 8192)
     return MOE_ERR_UNSUPPORTED;
   s->d = c->d_model;
-  s->l = c->d_latent;
+  s->latent = c->d_latent > 0 ? 1 : 0;
+  s->l = lin;   // the width the experts read and write (the token itself without a latent)
   s->E = c->n_experts;
   s->k = c->top_k;
   s->m = c->d_expert;
   s->ms = c->d_shared;
-  s->use_norm = c->use_latent_norm ? 1 : 0;
+  s->use_norm = (c->use_latent_norm && s->latent) ? 1 : 0;
   s->eps = c->rms_eps;
   s->route_scale = c->route_scale;
   s->beta_gate = c->beta_gate;
@@ -52,11 +56,11 @@ moe_status make_shape(const moe_config* c, Shape* s) {
   // packed dense weights
   s->ks_in = moe::cdiv(s->d, moe::kStepK);
   s->tr_r = moe::cdiv(s->E, moe::kTileRows);
-  s->tr_dn = moe::cdiv(s->l, moe::kTileRows);
+  s->tr_dn = s->latent ? moe::cdiv(s->l, moe::kTileRows) : 0;
   s->tr_sh = moe::cdiv(s->ms, moe::kTileRows / 2);
   s->tr_in = s->tr_r + s->tr_dn + s->tr_sh;
   s->zplanes = moe::clampi(s->ks_in / 7, 1, 8);
-  s->ks_l = moe::cdiv(s->l, moe::kStepK);
+  s->ks_l = s->latent ? moe::cdiv(s->l, moe::kStepK) : 0;   // OUT's u_hat segment
   s->ks_ms = moe::cdiv(s->ms, moe::kStepK);
   s->ks_out = s->ks_l + s->ks_ms;
   s->tr_out = moe::cdiv(s->d, moe::kTileRows);
@@ -69,7 +73,8 @@ moe_status make_shape(const moe_config* c, Shape* s) {
   s->tr_gu = moe::cdiv(s->m, moe::kTileRows / 2);
   s->ks_edn = moe::cdiv(s->m, moe::kStepK);
   s->tr_edn = moe::cdiv(s->l, moe::kTileRows);
-  s->step_bytes = s->wfmt == MOE_WFMT_MXFP4 ? moe::kFp4StepBytes : moe::kBf16StepBytes;
+  s->step_bytes = s->wfmt == MOE_WFMT_MXFP4 ? moe::kFp4StepBytes
+                : s->wfmt == MOE_WFMT_FP8_B128 ? moe::kFp8StepBytes : moe::kBf16StepBytes;
   s->gu_bytes = (size_t)s->tr_gu * s->ks_gu * s->step_bytes;
   s->expert_bytes = align256(s->gu_bytes + (size_t)s->tr_edn * s->ks_edn * s->step_bytes);
   return MOE_OK;
@@ -200,8 +205,8 @@ MOE_EXPORT moe_status moe_pack_dense(const moe_config* cfg, const moe_dense_src*
   Shape s;
   moe_status st = make_shape(cfg, &s);
   if (st != MOE_OK) return st;
-  if (!src || !packed || !src->router || !src->w_down_latent || !src->w_up_latent ||
-      !src->norm_gamma || !aligned(packed, 256))
+  if (!src || !packed || !src->router || !aligned(packed, 256)) return MOE_ERR_INVALID_ARG;
+  if (s.latent && (!src->w_down_latent || !src->w_up_latent || !src->norm_gamma))
     return MOE_ERR_INVALID_ARG;
   if (s.ms > 0 && (!src->shared_gu || !src->shared_down)) return MOE_ERR_INVALID_ARG;
   const void* ptrs[6] = {src->router, src->w_down_latent, src->w_up_latent, src->norm_gamma,
@@ -239,6 +244,10 @@ MOE_EXPORT moe_status moe_pack_experts(const moe_config* cfg, const moe_expert_s
       (!src->gu_scale || !src->down_scale || !aligned(src->gu, 4) || !aligned(src->down, 4)))
     return MOE_ERR_INVALID_ARG;
   if (s.wfmt == MOE_WFMT_BF16 && (!aligned(src->gu, 16) || !aligned(src->down, 16)))
+    return MOE_ERR_INVALID_ARG;
+  if (s.wfmt == MOE_WFMT_FP8_B128 &&
+      (!src->gu_scale || !src->down_scale || !aligned(src->gu, 8) || !aligned(src->down, 8) ||
+       !aligned(src->gu_scale, 4) || !aligned(src->down_scale, 4)))
     return MOE_ERR_INVALID_ARG;
   if (e0 < 0 || n < 0 || (int64_t)e0 + n > s.E) return MOE_ERR_INVALID_ARG;
   if (packed_bytes < s.expert_bytes * (size_t)s.E) return MOE_ERR_WORKSPACE;

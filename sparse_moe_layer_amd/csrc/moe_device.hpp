@@ -53,6 +53,17 @@ __device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t codes, float scale) {
                     __builtin_bit_cast(uint32_t, b2), __builtin_bit_cast(uint32_t, b3));
 }
 
+// Eight E4M3 codes (two 32-bit words, lowest byte first) as bf16, exactly (every E4M3
+// value has at most 4 significant bits and an exponent within the bf16 range).
+__device__ __forceinline__ uint4 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const bf16x2_t b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2_t b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2_t b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2_t b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, b0), __builtin_bit_cast(uint32_t, b1),
+                    __builtin_bit_cast(uint32_t, b2), __builtin_bit_cast(uint32_t, b3));
+}
+
 // Streaming (non-temporal) loads for weights that are read once per call.
 __device__ __forceinline__ uint4 ld_stream(const void* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
@@ -135,18 +146,25 @@ __device__ __forceinline__ float glu_act(float g, float u, int act, float bg, fl
   return g * sigmoidf_(g) * u;
 }
 
-// The weight operand of one K-step of one tile row.  WF: 0 bf16 K-steps, 1 MXFP4
-// K-steps.  A bf16 K-step feeds four 16x16x32 MFMAs: sub-tile s (lane l: row l % 16,
-// columns 32s + 8 (l / 16) .. +8).  An MXFP4 K-step gives lane l one whole MX block: the
-// 32 codes of row l % 16, columns 32 (l / 16) .. +32, and its scale (byte l / 16 of the
-// row's scale word); the four MFMAs then take codes 8s .. 8s+7 of every lane, i.e.
-// columns 32 (l / 16) + 8s .. +8, so the activation operand is read with the roles of s
-// and l / 16 swapped (a_piece below).  The same bytes are the B operand of the scaled
-// 16x16x128 FP4 MFMA, which takes the whole block of each lane at once.
+// The weight operand of one K-step of one tile row.  WF: 0 bf16, 1 MXFP4, 2 FP8 E4M3 with
+// 128 x 128 block scales.
+//   bf16: four 16x16x32 MFMAs, sub-tile s (1 KiB) with lane l holding row l % 16, columns
+//     32s + 8 (l / 16) .. +8.
+//   MXFP4: lane l holds one whole MX block, the 32 codes of row l % 16, columns 32 (l / 16)
+//     .. +32, and its scale (byte l / 16 of the row's scale word); the four MFMAs take codes
+//     8s .. 8s+7 of every lane, i.e. columns 32 (l / 16) + 8s .. +8, so the activation
+//     operand is read with the roles of s and l / 16 swapped (a_piece).  The same bytes are
+//     the B operand of the scaled 16x16x128 FP4 MFMA, which takes the whole block at once.
+//   FP8: lane l holds 32 codes, 8 per sub-tile in the bf16 order (columns 32s + 8 (l / 16)
+//     .. +8), converted exactly to bf16; a K-step lies in one 128 x 128 block of the rows of
+//     each half of the tile row (gate rows in lanes l % 16 < 8, up rows in the others, or one
+//     block for plain tile rows), so the K-step's partial sum is scaled by its block's fp32
+//     scale and added to the running sum.
 template <int WF>
 struct WeightStep {
-  static constexpr int SB = WF ? kFp4StepBytes : kBf16StepBytes;
-  static constexpr int NW = WF ? 1 : 4;
+  static constexpr bool kFp4 = WF == 1, kFp8 = WF == 2;
+  static constexpr int SB = kFp4 ? kFp4StepBytes : kFp8 ? kFp8StepBytes : kBf16StepBytes;
+  static constexpr int NW = kFp4 ? 1 : kFp8 ? 2 : 4;
   uint4 w[NW];
   uint32_t sc;
   // K-step q of the tile row.  Streaming (non-temporal) loads where every weight is read
@@ -155,10 +173,14 @@ struct WeightStep {
   template <bool CACHED = false>
   __device__ __forceinline__ void load(const uint8_t* trow, int q, int lane) {
     const uint8_t* p = trow + (size_t)q * SB;
-    if (WF) {
+    if (kFp4) {
       w[0] = CACHED ? *reinterpret_cast<const uint4*>(p + lane * 16) : ld_stream(p + lane * 16);
       sc = CACHED ? *reinterpret_cast<const uint32_t*>(p + 1024 + (lane & 15) * 4)
                   : ld_stream32(p + 1024 + (lane & 15) * 4);
+    } else if (kFp8) {
+      w[0] = ld_stream(p + lane * 32);
+      w[1] = ld_stream(p + lane * 32 + 16);
+      sc = ld_stream32(p + 2048 + ((lane & 15) >= 8 ? 4 : 0));
     } else {
 #pragma unroll
       for (int s = 0; s < NW; ++s)
@@ -166,23 +188,38 @@ struct WeightStep {
                       : ld_stream(p + s * 1024 + lane * 16);
     }
   }
-  // the lane's E8M0 scale as an fp32 power of two (MXFP4)
-  __device__ __forceinline__ float scale(int g) const { return e8m0_as_f32((sc >> (8 * g)) & 0xFFu); }
+  // the lane's E8M0 scale as an fp32 power of two (MXFP4), or its fp32 block scale (FP8)
+  __device__ __forceinline__ float scale(int g) const {
+    return kFp8 ? __uint_as_float(sc) : e8m0_as_f32((sc >> (8 * g)) & 0xFFu);
+  }
   // the B operand of MFMA s
   __device__ __forceinline__ uint4 operand(int s, float scl) const {
-    if (!WF) return w[s];
-    const uint32_t cd = s == 0 ? w[0].x : s == 1 ? w[0].y : s == 2 ? w[0].z : w[0].w;
-    return fp4x8_to_bf16(cd, scl);
+    if (kFp4) {
+      const uint32_t cd = s == 0 ? w[0].x : s == 1 ? w[0].y : s == 2 ? w[0].z : w[0].w;
+      return fp4x8_to_bf16(cd, scl);
+    }
+    if (kFp8) {
+      const uint4 v = w[s >> 1];
+      return fp8x8_to_bf16((s & 1) ? v.z : v.x, (s & 1) ? v.w : v.y);
+    }
+    return w[s];
   }
   // The 8-column piece (0..15) of the K-step that lane group g feeds to MFMA s.
-  static __device__ __forceinline__ int a_piece(int s, int g) { return WF ? 4 * g + s : 4 * s + g; }
-  // D += A W^T over the K-step: ap points at piece 0 of the lane's staged row, pieces
+  static __device__ __forceinline__ int a_piece(int s, int g) { return kFp4 ? 4 * g + s : 4 * s + g; }
+  // acc + A W^T over the K-step: ap points at piece 0 of the lane's staged row, pieces
   // `stride` words apart.
   __device__ __forceinline__ f32x4_t mma(const uint4* ap, int stride, int g, f32x4_t acc) const {
-    const float scl = WF ? scale(g) : 0.f;
+    const float scl = kFp4 ? scale(g) : 0.f;
+    f32x4_t part = kFp8 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma_bf16(ap[a_piece(s, g) * stride], operand(s, scl), acc);
-    return acc;
+    for (int s = 0; s < 4; ++s) part = mfma_bf16(ap[a_piece(s, g) * stride], operand(s, scl), part);
+    if (kFp8) return scale_add(part, scale(g), acc);
+    return part;
+  }
+  // acc + scale * part (the FP8 block scale applied to a K-step's partial sums)
+  static __device__ __forceinline__ f32x4_t scale_add(f32x4_t part, float scl, f32x4_t acc) {
+    return f32x4_t{fmaf(scl, part[0], acc[0]), fmaf(scl, part[1], acc[1]),
+                   fmaf(scl, part[2], acc[2]), fmaf(scl, part[3], acc[3])};
   }
 };
 

@@ -13,17 +13,20 @@ constexpr int kTileRows = 16;           // weight rows per packed tile (MFMA 16x
 constexpr int kStepK = 128;             // input columns per K-step
 constexpr int kBf16StepBytes = 4096;    // bf16 K-step: 4 sub-tiles of 16 rows x 32 columns
 constexpr int kFp4StepBytes = 1024 + 64;  // MXFP4 K-step: 16 rows x 128 codes + 16 x 4 scales
+constexpr int kFp8StepBytes = 2048 + 16;  // FP8 block-128 K-step: 16 rows x 128 codes + the
+                                          // gate-half and up-half block scales (fp32), padded
 constexpr int kCtrlWords = 64;          // control words at the head of the workspace
 
 __host__ __device__ inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 // Shape of one layer plus everything derived from it that the launches need.
 struct Shape {
-  int d, l, E, k, m, ms;
+  int d, l, E, k, m, ms;   // l: the experts' input / output width (d when not latent)
+  int latent;              // 1: W_down_latent / norm / W_up_latent around the experts
   int use_norm;
   float eps, route_scale, beta_gate, beta_lin;
   int act;    // 0 SiTU, 1 SwiGLU
-  int wfmt;   // 0 bf16, 1 MXFP4 (routed experts)
+  int wfmt;   // 0 bf16, 1 MXFP4, 2 FP8 E4M3 with 128 x 128 block scales (routed experts)
   int prec;   // 0 fp32 activations, 1 the mx8 profile (MXFP8 expert inputs, bf16 u_hat / h_s)
   // packed dense weights: IN = [router ; W_down_latent ; shared gate/up] over K = d,
   // OUT = [W_up_latent | W_shared_down] over K = l (padded) + m_s
@@ -95,7 +98,12 @@ constexpr int kPfUnitPositions = 64;   // 16 x the expert tile blocks of moe_pre
 inline int unit_positions(const Shape& s, int64_t T) {
   if (s.prec == 1) return kPfUnitPositions;
   if (token_tiled(s, T)) return kTiledUnitPositions;
-  return T < 1 ? 1 : (int)T;
+  // few tokens: all rows of a unit staged at once (2 hi/lo rows of the widest expert
+  // input per position, within 56 KiB of LDS)
+  const int ks = s.ks_gu > s.ks_edn ? s.ks_gu : s.ks_edn;
+  const int fit = clampi(57344 / (ks * kStepK * 4), 1, 4);
+  const int t = T < 1 ? 1 : (int)T;
+  return t < fit ? t : fit;
 }
 inline int64_t max_units(const Shape& s, int64_t T) {
   const int64_t n = T * s.k, nu = unit_positions(s, T);

@@ -704,8 +704,8 @@ __global__ __launch_bounds__(kBlock) void k_exp(ExpArgs a) {
     const int q0 = min(a.ks, kp * qper), q1 = min(a.ks, q0 + qper);
     const bool live = tr < a.n_tr && q1 > q0;
     const uint8_t* trow = a.experts + (size_t)e * a.expert_bytes + a.region_off +
-                          (size_t)tr * a.ks * (WF ? kFp4StepBytes : kBf16StepBytes);
-    TileStream<WF, WF ? 4 : 3> ts;
+                          (size_t)tr * a.ks * WeightStep<WF>::SB;
+    TileStream<WF, WF == 1 ? 4 : 3> ts;
     if (live) ts.prefetch(trow, q0, q1 - q0);
     if ((int)threadIdx.x < n) {
       const int p = p0 + threadIdx.x;
@@ -720,7 +720,7 @@ __global__ __launch_bounds__(kBlock) void k_exp(ExpArgs a) {
     stage_hilo(sm, rows, n, a.kin, 0, 0, nullptr, a.ks);
     __syncthreads();
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    if (live) acc = run_tile_row_n<WF, WF ? 4 : 3>(ts, trow, q0, q1 - q0, sm, c % nr, nr);
+    if (live) acc = run_tile_row_n<WF, WF == 1 ? 4 : 3>(ts, trow, q0, q1 - q0, sm, c % nr, nr);
     acc = reduce_ksplit(acc, part, a.ksplit, kp);
     if (tr < a.n_tr && kp == 0) {
       // D rows 4g..4g+3 = (hi, lo) of positions 2g and 2g + 1 of the unit
@@ -756,9 +756,11 @@ struct OutArgs {
   const float* hs;
   const uint16_t* gamma;
   int d, l, ms, norm;
+  int n0;               // columns of the u_hat segment (0 without a latent)
   float eps;
   int64_t T;
   float* delta;
+  const float* add_u;   // without a latent: Delta = u + the product
 };
 
 constexpr int kOutMaxTokens = 8;
@@ -824,7 +826,7 @@ __global__ __launch_bounds__(kBlock) void k_out(OutArgs a) {
     if (threadIdx.x == 0) rows[i] = HiloRow{ur, a.hs + (t0 + i) * a.ms, inv};
   }
   __syncthreads();
-  stage_hilo(sm, rows, nt, a.l, a.ks_l * kStepK, a.ms, a.norm ? a.gamma : nullptr, a.ks);
+  stage_hilo(sm, rows, nt, a.n0, a.ks_l * kStepK, a.ms, a.norm ? a.gamma : nullptr, a.ks);
   __syncthreads();
   const int nr = 2 * nt;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -834,8 +836,9 @@ __global__ __launch_bounds__(kBlock) void k_out(OutArgs a) {
     const int r = 16 * tr + c;
     const float y0 = acc[0] + acc[1], y1 = acc[2] + acc[3];
     if (r < a.d) {
-      if (2 * g < nt) a.delta[(t0 + 2 * g) * a.d + r] = y0;
-      if (2 * g + 1 < nt) a.delta[(t0 + 2 * g + 1) * a.d + r] = y1;
+      const int64_t i0 = (t0 + 2 * g) * a.d + r, i1 = i0 + a.d;
+      if (2 * g < nt) a.delta[i0] = a.add_u ? a.add_u[i0] + y0 : y0;
+      if (2 * g + 1 < nt) a.delta[i1] = a.add_u ? a.add_u[i1] + y1 : y1;
     }
   }
 }
@@ -978,13 +981,20 @@ __device__ __forceinline__ void tt_run(const TTRows& rows, const TTSrc& src, con
           const int jj = WeightStep<WF>::a_piece(s4, g);
           af[s4][b] = buf[jj * RB + 16 * b + (c ^ jj)];
         }
+      constexpr bool kFp8 = WeightStep<WF>::kFp8;
       const float scl = WF ? ts.w[i].scale(g) : 0.f;
+      f32x4_t part[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) part[b] = kFp8 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : cur[b];
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
         const uint4 bw = ts.w[i].operand(s4, scl);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) cur[b] = mfma_bf16(af[s4][b], bw, cur[b]);
+        for (int b = 0; b < NB; ++b) part[b] = mfma_bf16(af[s4][b], bw, part[b]);
       }
+#pragma unroll
+      for (int b = 0; b < NB; ++b)   // FP8: the K-step's partial sums times its block scale
+        cur[b] = kFp8 ? WeightStep<WF>::scale_add(part[b], scl, cur[b]) : part[b];
       ts.w[i].load(trow, min(q + P, ks - 1), lane);
       if (q < ks && (++in_part == qper || q + 1 == ks)) {
 #pragma unroll
@@ -1071,9 +1081,10 @@ struct OutTTArgs {
   int ks, ks_l, qper, n_tr, n_grp, n_tiles;
   const uint16_t* uh_hl;   // [T][2][l]
   const uint16_t* hs_hl;   // [T][2][ms]
-  int d, l, ms;
+  int d, l, ms, n0;        // n0: columns of the u_hat segment (0 without a latent)
   int64_t T;
   float* delta;
+  const float* add_u;      // without a latent: Delta = u + the product
 };
 
 constexpr int kHiloTTBlocks = 4;  // 32 fp32 rows as 64 hi/lo rows
@@ -1098,7 +1109,7 @@ __global__ __launch_bounds__(kBlock) void k_out_tt(OutTTArgs a) {
   const int tr = grp * kWavesPerBlock + wv;
   const bool live = tr < a.n_tr;
   f32x4_t tot[kHiloTTBlocks];
-  tt_run<0, 4, kHiloTTBlocks>(rows, TTSrc{a.uh_hl, a.hs_hl, 2 * nt, a.l, a.ks_l * kStepK, a.ms},
+  tt_run<0, 4, kHiloTTBlocks>(rows, TTSrc{a.uh_hl, a.hs_hl, 2 * nt, a.n0, a.ks_l * kStepK, a.ms},
                               a.w + (size_t)(live ? tr : 0) * a.ks * kBf16StepBytes, a.ks, a.qper,
                               sm, tot);
   if (!live) return;
@@ -1107,8 +1118,10 @@ __global__ __launch_bounds__(kBlock) void k_out_tt(OutTTArgs a) {
 #pragma unroll
   for (int b = 0; b < kHiloTTBlocks; ++b) {
     const int i0 = 8 * b + 2 * g;
-    if (i0 < nt) a.delta[(t0 + i0) * a.d + r] = tot[b][0] + tot[b][1];
-    if (i0 + 1 < nt) a.delta[(t0 + i0 + 1) * a.d + r] = tot[b][2] + tot[b][3];
+    const int64_t o0 = (t0 + i0) * a.d + r, o1 = o0 + a.d;
+    const float y0 = tot[b][0] + tot[b][1], y1 = tot[b][2] + tot[b][3];
+    if (i0 < nt) a.delta[o0] = a.add_u ? a.add_u[o0] + y0 : y0;
+    if (i0 + 1 < nt) a.delta[o1] = a.add_u ? a.add_u[o1] + y1 : y1;
   }
 }
 
@@ -1180,8 +1193,8 @@ __global__ __launch_bounds__(kBlock) void k_exp_tt(ExpArgs a) {
   const int tr = wgi * kWavesPerBlock + wv;
   const bool live = tr < a.n_tr;
   const uint8_t* trow = a.experts + (size_t)e * a.expert_bytes + a.region_off +
-                        (size_t)(live ? tr : 0) * a.ks * (WF ? kFp4StepBytes : kBf16StepBytes);
-  constexpr int P = WF ? 4 : 3;
+                        (size_t)(live ? tr : 0) * a.ks * WeightStep<WF>::SB;
+  constexpr int P = WF == 1 ? 4 : 3;
   TileStream<WF, P> ts;
   if (n <= kExpWholeK) ts.prefetch(trow, 0, a.ks);
   if ((int)threadIdx.x < 2 * n) {
@@ -1297,6 +1310,41 @@ __global__ __launch_bounds__(kBlock) void k_pack_fp4(PackArgs a) {
   }
 }
 
+// FP8 block-128: lane l's 32 bytes are the codes of row l % 16 at columns 128 q + 32 s +
+// 8 (l / 16) .. +8 for s = 0..3; then the K-step's two fp32 block scales (the rows of
+// lanes 0..7 and of lanes 8..15), padded to 16 bytes.
+__global__ __launch_bounds__(kBlock) void k_pack_fp8(PackArgs a) {
+  const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  const int64_t per_mat = (int64_t)a.n_tr * a.ks_src * kWave;
+  if (gid >= per_mat * a.n) return;
+  const int64_t ei = gid / per_mat;
+  int64_t r = gid - ei * per_mat;
+  const int lane = (int)(r % kWave); r /= kWave;
+  const int q = (int)(r % a.ks_src);
+  const int t = (int)(r / a.ks_src);
+  const int c = lane & 15, g = lane >> 4;
+  const int row = packed_row(t, c, a.rows, a.gated);
+  uint2 v[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int col = q * kStepK + 32 * s + 8 * g;
+    v[s] = (row >= 0 && col < a.cols)
+               ? *reinterpret_cast<const uint2*>(a.src + ei * a.src_stride + (int64_t)row * a.cols + col)
+               : make_uint2(0u, 0u);
+  }
+  uint8_t* dp = a.dst + ei * a.dst_stride + ((int64_t)t * a.ks_dst + q) * kFp8StepBytes;
+  *reinterpret_cast<uint4*>(dp + lane * 32) = make_uint4(v[0].x, v[0].y, v[1].x, v[1].y);
+  *reinterpret_cast<uint4*>(dp + lane * 32 + 16) = make_uint4(v[2].x, v[2].y, v[3].x, v[3].y);
+  if (lane < 2) {
+    const int hrow = packed_row(t, 8 * lane, a.rows, a.gated);
+    const int bc = (a.cols + 127) / 128;
+    const float* sc = reinterpret_cast<const float*>(a.scales) + ei * a.scale_stride;
+    *reinterpret_cast<float*>(dp + 2048 + 4 * lane) = hrow >= 0 ? sc[(hrow / 128) * bc + q] : 0.f;
+  } else if (lane == 2) {
+    *reinterpret_cast<uint2*>(dp + 2056) = make_uint2(0u, 0u);
+  }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------------------
@@ -1353,8 +1401,31 @@ int in_launch_shared_rows(const Shape& s) { return s.tr_sh; }
 
 }  // namespace
 
+namespace {
+// Without a latent the experts read the token itself: x (bf16) as the fp32 rows of the
+// few-token launches and as the hi/lo rows (lo = 0) of the token-tiled ones.
+__global__ __launch_bounds__(kBlock) void k_token_rows(const uint16_t* __restrict__ x, int64_t n,
+                                                       float* __restrict__ xc, uint16_t* __restrict__ xc_hl,
+                                                       int d) {
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i >= n) return;
+  const uint16_t v = x[i];
+  xc[i] = __uint_as_float((uint32_t)v << 16);
+  if (xc_hl) {
+    const int64_t t = i / d, c = i - t * d;
+    xc_hl[t * 2 * d + c] = v;
+    xc_hl[t * 2 * d + d + c] = 0;
+  }
+}
+}  // namespace
+
 hipError_t launch_router(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,
                          bool router_only, const Work& ws, hipStream_t st) {
+  if (!s.latent && !router_only) {
+    const int64_t n = T * s.d;
+    hipLaunchKernelGGL(k_token_rows, dim3((unsigned)cdiv(n, kBlock)), dim3(kBlock), 0, st, x, n,
+                       ws.xc, token_tiled(s, T) ? ws.xc_hl : nullptr, s.d);
+  }
   // larger batches: the router alone (W_down_latent goes to the token-tiled IN launch)
   if (token_tiled(s, T)) router_only = true;
   InArgs a = in_args(s, dense, x, T, ws, s.tr_r, router_only ? 0 : s.tr_dn);
@@ -1455,6 +1526,9 @@ hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_
     if (s.wfmt == 1) {
       if (gu) hipLaunchKernelGGL((k_exp_tt<1, true>), dim3(grid), dim3(kBlock), lds, st, a);
       else hipLaunchKernelGGL((k_exp_tt<1, false>), dim3(grid), dim3(kBlock), lds, st, a);
+    } else if (s.wfmt == 2) {
+      if (gu) hipLaunchKernelGGL((k_exp_tt<2, true>), dim3(grid), dim3(kBlock), lds, st, a);
+      else hipLaunchKernelGGL((k_exp_tt<2, false>), dim3(grid), dim3(kBlock), lds, st, a);
     } else {
       if (gu) hipLaunchKernelGGL((k_exp_tt<0, true>), dim3(grid), dim3(kBlock), lds, st, a);
       else hipLaunchKernelGGL((k_exp_tt<0, false>), dim3(grid), dim3(kBlock), lds, st, a);
@@ -1465,6 +1539,9 @@ hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_
   if (s.wfmt == 1) {
     if (gu) hipLaunchKernelGGL((k_exp<1, true>), dim3(grid), dim3(kBlock), lds, st, a);
     else hipLaunchKernelGGL((k_exp<1, false>), dim3(grid), dim3(kBlock), lds, st, a);
+  } else if (s.wfmt == 2) {
+    if (gu) hipLaunchKernelGGL((k_exp<2, true>), dim3(grid), dim3(kBlock), lds, st, a);
+    else hipLaunchKernelGGL((k_exp<2, false>), dim3(grid), dim3(kBlock), lds, st, a);
   } else {
     if (gu) hipLaunchKernelGGL((k_exp<0, true>), dim3(grid), dim3(kBlock), lds, st, a);
     else hipLaunchKernelGGL((k_exp<0, false>), dim3(grid), dim3(kBlock), lds, st, a);
@@ -1477,7 +1554,7 @@ hipError_t launch_combine(const Shape& s, const uint8_t* dense, const float* gw,
   const int bpt = cdiv(s.l, kBlock);
   hipLaunchKernelGGL(k_combine, dim3((unsigned)(T * bpt)), dim3(kBlock), 0, st, gw,
                      (const int32_t*)ws.inv, (const float*)ws.eo, T, s.k, s.l, bpt, ws.u);
-  if (token_tiled(s, T) && s.prec == 0)   // (the mx8 launches take their own norm)
+  if (token_tiled(s, T) && s.prec == 0 && s.latent)   // (the mx8 launches take their own norm)
     hipLaunchKernelGGL(k_norm, dim3((unsigned)T), dim3(kBlock), 0, st, (const float*)ws.u,
                        reinterpret_cast<const uint16_t*>(dense + s.gamma_off), s.l, s.use_norm,
                        s.eps, ws.uh, ws.uh_hl);
@@ -1496,8 +1573,9 @@ hipError_t launch_out(const Shape& s, const uint8_t* dense, int64_t T, const Wor
     a.n_grp = cdiv(s.tr_out, kWavesPerBlock);
     a.n_tiles = cdiv(T, kHiloTTRows);
     a.uh_hl = ws.uh_hl; a.hs_hl = ws.hs_hl;
-    a.d = s.d; a.l = s.l; a.ms = s.ms;
+    a.d = s.d; a.l = s.l; a.ms = s.ms; a.n0 = s.latent ? s.l : 0;
     a.T = T; a.delta = delta;
+    a.add_u = s.latent ? nullptr : ws.u;
     const size_t lds = (size_t)2 * kHiloTTBlocks * 16 * 16 * 16;
     hipLaunchKernelGGL(k_out_tt, dim3((unsigned)xcd_grid(a.n_grp, a.n_tiles)), dim3(kBlock), lds,
                        st, a);
@@ -1514,7 +1592,9 @@ hipError_t launch_out(const Shape& s, const uint8_t* dense, int64_t T, const Wor
   a.u = ws.u; a.hs = ws.hs;
   a.gamma = reinterpret_cast<const uint16_t*>(dense + s.gamma_off);
   a.d = s.d; a.l = s.l; a.ms = s.ms; a.norm = s.use_norm; a.eps = s.eps;
+  a.n0 = s.latent ? s.l : 0;
   a.T = T; a.delta = delta;
+  a.add_u = s.latent ? nullptr : ws.u;
   const size_t lds = (size_t)2 * (T < a.ntb ? T : a.ntb) * s.ks_out * kStepK * 2;
   hipLaunchKernelGGL(k_out, dim3((unsigned)xcd_grid(a.wg_per_blk, a.n_blk)), dim3(kBlock), lds, st,
                      a);
@@ -1546,17 +1626,20 @@ hipError_t launch_pack_dense(const Shape& s, const DenseSrc& src, uint8_t* packe
   const int64_t row_in = (int64_t)s.ks_in * kBf16StepBytes;
   // IN: router, W_down_latent, shared gate/up (gated tiles)
   if ((e = pack_bf16(src.router, 0, s.E, s.d, 0, s.tr_r, s.ks_in, 0, 1, packed, 0, st)) != hipSuccess) return e;
-  if ((e = pack_bf16(src.wdn, 0, s.l, s.d, 0, s.tr_dn, s.ks_in, 0, 1, packed + s.tr_r * row_in, 0,
-                     st)) != hipSuccess) return e;
+  if (s.latent && (e = pack_bf16(src.wdn, 0, s.l, s.d, 0, s.tr_dn, s.ks_in, 0, 1,
+                                 packed + s.tr_r * row_in, 0, st)) != hipSuccess)
+    return e;
   if (s.ms > 0 && (e = pack_bf16(src.sgu, 0, 2 * s.ms, s.d, 1, s.tr_sh, s.ks_in, 0, 1,
                                  packed + (int64_t)(s.tr_r + s.tr_dn) * row_in, 0, st)) != hipSuccess)
     return e;
   // OUT: [W_up_latent | W_shared_down]
   uint8_t* out = packed + s.in_bytes;
-  if ((e = pack_bf16(src.wup, 0, s.d, s.l, 0, s.tr_out, s.ks_out, 0, 1, out, 0, st)) != hipSuccess) return e;
+  if (s.latent && (e = pack_bf16(src.wup, 0, s.d, s.l, 0, s.tr_out, s.ks_out, 0, 1, out, 0, st)) != hipSuccess)
+    return e;
   if (s.ms > 0 && (e = pack_bf16(src.sdn, 0, s.d, s.ms, 0, s.tr_out, s.ks_out, s.ks_l, 1, out, 0,
                                  st)) != hipSuccess)
     return e;
+  if (!s.latent) return hipSuccess;   // no latent: no norm gain
   return hipMemcpyAsync(packed + s.gamma_off, src.gamma, (size_t)s.l * 2, hipMemcpyDeviceToDevice, st);
 }
 
@@ -1569,6 +1652,32 @@ hipError_t launch_pack_experts(const Shape& s, const void* gu, const void* gus, 
     if (e != hipSuccess) return e;
     return pack_bf16(dn, (int64_t)s.l * s.m * 2, s.l, s.m, 0, s.tr_edn, s.ks_edn, 0, n,
                      dst + s.gu_bytes, s.expert_bytes, st);
+  }
+  if (s.wfmt == 2) {
+    PackArgs a{};
+    const int64_t bgu = (int64_t)((2 * s.m + 127) / 128) * ((s.l + 127) / 128);
+    const int64_t bdn = (int64_t)((s.l + 127) / 128) * ((s.m + 127) / 128);
+    a.src = static_cast<const uint8_t*>(gu);
+    a.scales = static_cast<const uint8_t*>(gus);
+    a.src_stride = (int64_t)2 * s.m * s.l;
+    a.scale_stride = bgu;
+    a.rows = 2 * s.m; a.cols = s.l; a.gated = 1;
+    a.n_tr = s.tr_gu; a.ks_dst = s.ks_gu; a.q_off = 0; a.ks_src = s.ks_gu;
+    a.n = n; a.dst = dst; a.dst_stride = s.expert_bytes;
+    int64_t threads = (int64_t)n * a.n_tr * a.ks_src * kWave;
+    hipLaunchKernelGGL(k_pack_fp8, dim3((unsigned)cdiv(threads, kBlock)), dim3(kBlock), 0, st, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    a.src = static_cast<const uint8_t*>(dn);
+    a.scales = static_cast<const uint8_t*>(dns);
+    a.src_stride = (int64_t)s.l * s.m;
+    a.scale_stride = bdn;
+    a.rows = s.l; a.cols = s.m; a.gated = 0;
+    a.n_tr = s.tr_edn; a.ks_dst = s.ks_edn; a.ks_src = s.ks_edn;
+    a.dst = dst + s.gu_bytes;
+    threads = (int64_t)n * a.n_tr * a.ks_src * kWave;
+    hipLaunchKernelGGL(k_pack_fp8, dim3((unsigned)cdiv(threads, kBlock)), dim3(kBlock), 0, st, a);
+    return hipGetLastError();
   }
   PackArgs a{};
   a.src = static_cast<const uint8_t*>(gu);

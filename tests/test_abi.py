@@ -88,7 +88,8 @@ def _bad(**kw):
     ("expert_wfmt", 5, moe.MOE_ERR_INVALID_ARG),
     ("precision", 1, moe.MOE_ERR_UNSUPPORTED),       # mx8 needs MXFP4 experts (toy: bf16)
     ("precision", 2, moe.MOE_ERR_INVALID_ARG),
-    ("d_latent", 0, moe.MOE_ERR_UNSUPPORTED),
+    ("d_shared", 0, moe.MOE_OK),                      # latent block without shared: fine
+    ("expert_wfmt", 2, moe.MOE_OK),                   # FP8 block-128 experts
     ("rms_eps", float("nan"), moe.MOE_ERR_INVALID_ARG),
     ("beta_gate", 0.0, moe.MOE_ERR_INVALID_ARG),
 ])
@@ -143,3 +144,15 @@ def test_pack_and_dispatch_reject_bad_ranges(L):
     assert L.moe_dispatch(ctypes.byref(cfg), A, 8, A, A, A, A, A, 8, None) == moe.MOE_ERR_WORKSPACE
     assert L.moe_dispatch(ctypes.byref(cfg), None, 8, A, A, A, A, A, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_dispatch(ctypes.byref(cfg), None, 0, None, None, None, None, None, 0, None) == moe.MOE_OK
+
+
+def test_nonlatent_blocks_need_a_shared_expert(L):
+    n = ctypes.c_size_t()
+    ok = _bad(d_latent=0, use_latent_norm=0)
+    assert L.moe_workspace_size(ctypes.byref(ok), 4, ctypes.byref(n)) == moe.MOE_OK
+    no_shared = _bad(d_latent=0, d_shared=0)
+    assert L.moe_workspace_size(ctypes.byref(no_shared), 4, ctypes.byref(n)) == moe.MOE_ERR_UNSUPPORTED
+    k2 = moe.config_from(synth.K2_MOE_1024_ZIPF)
+    assert L.moe_packed_experts_size(ctypes.byref(k2), ctypes.byref(n)) == moe.MOE_OK
+    # 384 experts of 256 + 448 tile rows x (56 / 16 K-steps) x (2048 codes + 16 scale bytes)
+    assert n.value == 384 * (256 * 56 + 448 * 16) * 2064

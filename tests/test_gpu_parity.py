@@ -342,3 +342,44 @@ def test_k3_prefill_8192_sampled_tokens():
     assert np.all(np.isfinite(delta))
     rel, mxr, _ = check(cfg, x, delta, idx, w, rows=[0, 4097, 8191])
     assert rel < 1e-3
+
+
+# ---- the K2-style non-latent block: FP8 E4M3 block-128 experts, SwiGLU, gate scale 2.827 --
+
+TINY_K2 = synth.LayerConfig(name="tiny_k2", d=160, l=0, E=6, k=2, m=48, ms=32, tokens=5,
+                            seed=4242, expert_fmt="fp8b128", act="swiglu", route_scale=2.827,
+                            use_norm=False, bias_kind="uniform", bias_a=-0.01, bias_b=0.01)
+
+
+@pytest.mark.parametrize("T", [1, 3, 5, 33, 100])
+def test_nonlatent_fp8_tiny_token_counts(T):
+    lay, _ = device_layer(TINY_K2)
+    x = synth.tokens(TINY_K2, batch=T, T=T)
+    rel, _, _ = check(TINY_K2, x, *run(lay, x))
+    assert rel < 1e-5
+
+
+def test_latent_layer_with_fp8_block_experts():
+    cfg = TINY.with_(name="tiny_latent_fp8", expert_fmt="fp8b128", d=200, l=136, m=40, tokens=9)
+    lay, _ = device_layer(cfg)
+    x = synth.tokens(cfg)
+    rel, _, _ = check(cfg, x, *run(lay, x))
+    assert rel < 1e-5
+
+
+def test_k2_block_1024_tokens_sampled():
+    cfg = synth.K2_MOE_1024_ZIPF
+    lay, _ = device_layer(cfg)
+    x = synth.tokens(cfg, batch=0)
+    log(f"[k2] T={x.shape[0]}")
+    delta, idx, w = run(lay, x)
+    OL = oracle_layer(cfg)
+    s = O.router_scores(O.bf16_to_f64(x), OL.router)
+    ridx, G, margin = O.select_and_weight(s, OL.bias, cfg.k, cfg.route_scale)
+    assert_routing(idx, ridx, O.selection_kappa(s, OL.bias, cfg.k), margin)
+    assert np.all(np.isfinite(delta))
+    rel, _, _ = check(cfg, x, delta, idx, w, rows=[0, 511, 1023])
+    assert rel < 1e-4
+    # few-token launches on the same layer: the same Delta bits for a token alone
+    d1, i1, w1 = run(lay, x[511:512])
+    assert np.array_equal(i1[0], idx[511]) and np.array_equal(d1[0], delta[511])
