@@ -1075,6 +1075,62 @@ __global__ __launch_bounds__(kBlock) void k_in_tt(InTTArgs a) {
   }
 }
 
+// Router logits for a tile of up to 64 tokens: one workgroup per (4 router tile rows,
+// logit plane, token tile).  Plane p covers the K-steps [p qpp, (p+1) qpp) of the few-token
+// router launch and is summed in its order: runs of qw K-steps (its per-wavefront K-split)
+// added in sequence.  The route adds the planes in order, so a token's logits have the same
+// bits in both launches.
+struct RouterTTArgs {
+  const uint8_t* w;
+  int ks, qpp, tr_r, n_grp, zplanes, n_tiles;
+  const uint16_t* x;
+  int64_t T;
+  int d, E;
+  float* z;          // [zplanes][T][E]
+};
+
+__global__ __launch_bounds__(kBlock) void k_router_tt(RouterTTArgs a) {
+  extern __shared__ uint4 sm[];
+  __shared__ TTRows rows;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  int gp, tile;
+  if (!xcd_item(blockIdx.x, a.n_grp * a.zplanes, a.n_tiles, gp, tile)) return;
+  const int grp = gp / a.zplanes, plane = gp - grp * a.zplanes;
+  const int r0 = min(a.ks, plane * a.qpp), r1 = min(a.ks, r0 + a.qpp);
+  const int qw = cdiv(r1 - r0, kWavesPerBlock);
+  const int64_t t0 = (int64_t)tile * kTTMaxSrc;
+  const int nt = (int)min((int64_t)kTTMaxSrc, a.T - t0);
+  float* zp = a.z + (int64_t)plane * a.T * a.E;
+  if (r1 <= r0) {   // an empty plane holds zeros, as in the few-token launch (uniform branch)
+    for (int i = threadIdx.x; i < nt * 16 * kWavesPerBlock; i += kBlock) {
+      const int e = 16 * grp * kWavesPerBlock + i % (16 * kWavesPerBlock);
+      if (e < a.E) zp[(t0 + i / (16 * kWavesPerBlock)) * a.E + e] = 0.f;
+    }
+    return;
+  }
+  // rows start at the plane's first column
+  if ((int)threadIdx.x < nt) rows.o0[threadIdx.x] = (uint32_t)((t0 + threadIdx.x) * a.d / 8 + r0 * (kStepK / 8));
+  __syncthreads();
+  const int tri = grp * kWavesPerBlock + wv;
+  const bool live = tri < a.tr_r;
+  const uint8_t* trow = a.w + ((size_t)(live ? tri : 0) * a.ks + r0) * kBf16StepBytes;
+  f32x4_t tot[kInTTBlocks];
+  tt_run<0, 4, kInTTBlocks>(rows, TTSrc{a.x, nullptr, nt, a.d - r0 * kStepK, 0, 0}, trow, r1 - r0,
+                            qw, sm, tot);
+  if (!live) return;
+  const int e = 16 * tri + c;
+  if (e >= a.E) return;
+#pragma unroll
+  for (int b = 0; b < kInTTBlocks; ++b)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int ti = 16 * b + 4 * g + v;
+      if (ti < nt) zp[(t0 + ti) * a.E + e] = tot[b][v];
+    }
+}
+
 // OUT matrix for a tile of up to 32 tokens: [u_hat ; h_s] as hi/lo rows.
 struct OutTTArgs {
   const uint8_t* w;
@@ -1426,8 +1482,24 @@ hipError_t launch_router(const Shape& s, const uint8_t* dense, const uint16_t* x
     hipLaunchKernelGGL(k_token_rows, dim3((unsigned)cdiv(n, kBlock)), dim3(kBlock), 0, st, x, n,
                        ws.xc, token_tiled(s, T) ? ws.xc_hl : nullptr, s.d);
   }
-  // larger batches: the router alone (W_down_latent goes to the token-tiled IN launch)
-  if (token_tiled(s, T)) router_only = true;
+  if (token_tiled(s, T)) {
+    // larger batches: the router over tiles of 64 tokens (W_down_latent goes to the
+    // token-tiled IN launch)
+    RouterTTArgs a;
+    a.w = dense;
+    a.ks = s.ks_in;
+    a.qpp = cdiv(s.ks_in, s.zplanes);
+    a.tr_r = s.tr_r;
+    a.n_grp = cdiv(s.tr_r, kWavesPerBlock);
+    a.zplanes = s.zplanes;
+    a.n_tiles = cdiv(T, kTTMaxSrc);
+    a.x = x; a.T = T; a.d = s.d; a.E = s.E;
+    a.z = ws.z;
+    const size_t lds = (size_t)2 * kInTTBlocks * 16 * 16 * 16;
+    hipLaunchKernelGGL(k_router_tt, dim3((unsigned)xcd_grid((int64_t)a.n_grp * a.zplanes, a.n_tiles)),
+                       dim3(kBlock), lds, st, a);
+    return hipGetLastError();
+  }
   InArgs a = in_args(s, dense, x, T, ws, s.tr_r, router_only ? 0 : s.tr_dn);
   a.router_wgs = s.tr_r * s.zplanes;
   a.wg_per_blk += a.router_wgs;
