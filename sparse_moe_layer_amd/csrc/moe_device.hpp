@@ -188,6 +188,18 @@ struct WeightStep {
                       : ld_stream(p + s * 1024 + lane * 16);
     }
   }
+  // An ordering point: the registers count as rewritten here, so nothing derived from
+  // them (the operand conversions) is computed earlier, which would make the wave wait
+  // for this K-step's loads before the step that consumes them.
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int s = 0; s < NW; ++s) {
+      uint32_t a = w[s].x, b = w[s].y, c = w[s].z, d = w[s].w;
+      asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+      w[s] = make_uint4(a, b, c, d);
+    }
+    if (WF) asm volatile("" : "+v"(sc));
+  }
   // the lane's E8M0 scale as an fp32 power of two (MXFP4), or its fp32 block scale (FP8)
   __device__ __forceinline__ float scale(int g) const {
     return kFp8 ? __uint_as_float(sc) : e8m0_as_f32((sc >> (8 * g)) & 0xFFu);
@@ -243,6 +255,27 @@ __device__ __forceinline__ bool xcd_item(int bid, int n_groups, int n_blk, int& 
 }
 __host__ inline int64_t xcd_grid(int64_t n_groups, int64_t n_blk) {
   return kXcds * ((n_groups + kXcds - 1) / kXcds) * n_blk;
+}
+
+// Work order over (unit, tile-row group) items when the number of units is known only on
+// the device: XCD x takes a contiguous range of the units (so of the experts, the unit
+// table being sorted by expert) and walks it in chunks of `chunk` units, each chunk
+// through every tile-row group: a chunk's activation rows stay in that XCD's L2 across
+// the groups, and the units of one expert in a chunk read each weight slice close
+// together in time.  Items past a range return false (they come last on each XCD).
+__device__ __forceinline__ bool chunk_item(int bid, int n_units, int n_grp, int chunk, int& grp,
+                                           int& u) {
+  const int x = bid % kXcds, j = bid / kXcds;
+  const int per_xcd = (n_units + kXcds - 1) / kXcds;
+  const int c = j / (chunk * n_grp), r = j - c * chunk * n_grp;
+  grp = r / chunk;
+  const int ui = c * chunk + (r - grp * chunk);
+  u = x * per_xcd + ui;
+  return ui < per_xcd && u < n_units;
+}
+__host__ inline int64_t chunk_grid(int64_t max_units, int64_t n_grp, int64_t chunk) {
+  const int64_t per_xcd = (max_units + kXcds - 1) / kXcds;
+  return kXcds * ((per_xcd + chunk - 1) / chunk) * chunk * n_grp;
 }
 
 }  // namespace moe

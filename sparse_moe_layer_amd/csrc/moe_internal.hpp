@@ -53,7 +53,7 @@ struct PfWork {
 
 // Row-major views of the workspace of one forward call.
 struct Work {
-  int32_t* ctrl;   // [kCtrlWords]: [0] unit count (written by the route or the dispatch)
+  int32_t* ctrl;   // [kCtrlWords]: [0] unit count, [1] units in the first (short) list
   float* xc;       // [T][l]
   float* hs;       // [T][ms]
   float* h;        // [T*k][m]   dispatch order
@@ -109,6 +109,31 @@ inline int64_t max_units(const Shape& s, int64_t T) {
   const int64_t n = T * s.k, nu = unit_positions(s, T);
   const int64_t b = n / nu + (n < s.E ? n : s.E);
   return b < n ? b : n;
+}
+// Units of at most this many positions form the first list of the unit table and take
+// the expert kernel for few positions (all rows staged at once, no barrier in the K loop);
+// in the token-tiled launches that is within 32 KiB of LDS, so that five workgroups share
+// a compute unit.  The larger units take the token-tiled expert kernel.
+inline int small_unit_positions(const Shape& s, int64_t T) {
+  const int nu = unit_positions(s, T);
+  if (s.prec == 1 || !token_tiled(s, T)) return nu;
+  const int ks = s.ks_gu > s.ks_edn ? s.ks_gu : s.ks_edn;
+  const int w = clampi(32768 / (ks * kStepK * 4), 1, 4);
+  return w < nu ? w : nu;
+}
+// Bounds of the two lists: every expert has at most one unit shorter than nu positions,
+// and a large unit holds more than small_unit_positions of them.
+inline int64_t max_small_units(const Shape& s, int64_t T) {
+  const int64_t n = T * s.k, w = small_unit_positions(s, T);
+  if (w >= unit_positions(s, T)) return max_units(s, T);
+  const int64_t b = n < s.E ? n : s.E;
+  return b < max_units(s, T) ? b : max_units(s, T);
+}
+inline int64_t max_large_units(const Shape& s, int64_t T) {
+  const int64_t n = T * s.k, w = small_unit_positions(s, T);
+  if (w >= unit_positions(s, T)) return 0;
+  const int64_t b = n / (w + 1);
+  return b < max_units(s, T) ? b : max_units(s, T);
 }
 
 // router_only: the router rows alone (otherwise W_down_latent rides in the same launch)

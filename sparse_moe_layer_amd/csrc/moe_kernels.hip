@@ -55,7 +55,7 @@ struct RouteArgs {
   int32_t* perm;
   int32_t* inv;
   int32_t* units;   // unit table of the expert launches (dispatch only)
-  int32_t* ctrl;    // ctrl[0] <- number of units (dispatch only)
+  int32_t* ctrl;    // ctrl[0] <- number of units, ctrl[1] <- the same (dispatch only)
   int nu;           // positions per unit
 };
 
@@ -214,7 +214,7 @@ __device__ void route_block(const RouteArgs& a, int64_t t_begin, int64_t t_end, 
     run += loc[i];
   }
   if (tid == 0) a.offs[a.E] = n;
-  if (tid == kBlock - 1) a.ctrl[0] = upart[tid];
+  if (tid == kBlock - 1) a.ctrl[0] = a.ctrl[1] = upart[tid];
   __syncthreads();
   if (tid < n) {
     const int e = sidx[tid];
@@ -252,12 +252,15 @@ __global__ __launch_bounds__(kBlock) void k_disp_count(const int32_t* idx, int64
   for (int e = threadIdx.x; e < E; e += kBlock) chunk_hist[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
-__global__ __launch_bounds__(1024) void k_disp_scan(int n_chunks, int E, int nu,
+// Units of at most `small` positions come first in the table (ctrl[1] of them), then
+// the larger ones; ctrl[0] = all units.  Each list runs in expert order.
+__global__ __launch_bounds__(1024) void k_disp_scan(int n_chunks, int E, int nu, int small,
                                                     int32_t* chunk_hist, int32_t* counts,
                                                     int32_t* offs, int32_t* units,
                                                     int32_t* ctrl) {
   __shared__ int sc[1024];
   __shared__ int su[1024];
+  __shared__ int sb[1024];
   const int e = threadIdx.x;
   int tot = 0;
   if (e < E) {
@@ -268,27 +271,41 @@ __global__ __launch_bounds__(1024) void k_disp_scan(int n_chunks, int E, int nu,
     }
     counts[e] = tot;
   }
-  const int nue = (e < E) ? (tot + nu - 1) / nu : 0;
+  // this expert's units: tot / nu full ones and a tail of tot % nu positions
+  const int full = tot / nu, tail = tot - full * nu;
+  const bool full_small = nu <= small;
+  const int ns = (e < E) ? (full_small ? full : 0) + (tail > 0 && tail <= small) : 0;
+  const int nb = (e < E) ? (full_small ? 0 : full) + (tail > small) : 0;
   sc[e] = (e < E) ? tot : 0;
-  su[e] = nue;
+  su[e] = ns;
+  sb[e] = nb;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {
     const int v = (e >= o) ? sc[e - o] : 0;
     const int w = (e >= o) ? su[e - o] : 0;
+    const int x = (e >= o) ? sb[e - o] : 0;
     __syncthreads();
     sc[e] += v;
     su[e] += w;
+    sb[e] += x;
     __syncthreads();
   }
+  const int n_small = su[1023];
   if (e < E) {
     const int off = sc[e] - tot;
     offs[e] = off;
-    int ub = su[e] - nue;
-    for (int r0 = 0; r0 < tot; r0 += nu, ++ub)
-      *reinterpret_cast<int4*>(units + 4 * ub) = make_int4(e, off + r0, min(nu, tot - r0), 0);
+    int us = su[e] - ns, ub = n_small + sb[e] - nb;
+    for (int r0 = 0; r0 < tot; r0 += nu) {
+      const int n = min(nu, tot - r0);
+      const int slot = n <= small ? us++ : ub++;
+      *reinterpret_cast<int4*>(units + 4 * slot) = make_int4(e, off + r0, n, 0);
+    }
   }
   if (e == 0) offs[E] = sc[1023];
-  if (e == 1023) ctrl[0] = su[1023];
+  if (e == 1023) {
+    ctrl[0] = n_small + sb[1023];
+    ctrl[1] = n_small;
+  }
 }
 
 __global__ __launch_bounds__(kBlock) void k_disp_scatter(const int32_t* idx, int64_t n, int E,
@@ -487,6 +504,10 @@ __device__ __forceinline__ f32x4_t run_tile_row(TileStream<WF, P>& ts, const uin
         ts.w[q % P].load(trow, q0 + q + P, lane);
         asm volatile("" ::: "memory");
       }
+      // FP8: every K-step's products start from zero and only the scaled sums chain the
+      // steps; pin each step's sum here, or the compiler defers them all to the end and
+      // holds every step's products in registers at once
+      if (WeightStep<WF>::kFp8) asm volatile("" : "+v"(acc));
     }
     return acc;
   }
@@ -666,6 +687,7 @@ struct ExpArgs {
   const int32_t* units;
   const int32_t* ctrl;
   int max_units, nu, E, k;
+  int chunk;                // > 0: chunk_item work order (token-tiled launches), else xcd_item
   int64_t n_assign;
   const int32_t* perm;
   const float* xin;
@@ -680,6 +702,37 @@ struct ExpArgs {
   int out_ld;
 };
 
+// Gate/up: h[p] = act(gate, up) (and, with out_hl, its hi/lo row for the token-tiled down
+// launch); down: E[p].
+// y0, y1 are the sums of positions i0 and i0 + 1 of the unit (position offset p0, n used).
+template <bool GU>
+__device__ __forceinline__ void exp_store(const ExpArgs& a, int p0, int n, int tr, int c, int i0,
+                                          float y0, float y1) {
+  const int i1 = i0 + 1;
+  if (GU) {
+    const float g0 = from_gate_lane(y0), g1 = from_gate_lane(y1);
+    const int r = 8 * tr + (c - 8);
+    if (c >= 8 && r < a.n_out) {
+      if (i0 < n) {
+        const float h = glu_act(g0, y0, a.act, a.bg, a.bl);
+        a.out[(int64_t)(p0 + i0) * a.n_out + r] = h;
+        if (a.out_hl) store_hilo(a.out_hl + (int64_t)(p0 + i0) * 2 * a.out_ld + r, a.out_ld, h);
+      }
+      if (i1 < n) {
+        const float h = glu_act(g1, y1, a.act, a.bg, a.bl);
+        a.out[(int64_t)(p0 + i1) * a.n_out + r] = h;
+        if (a.out_hl) store_hilo(a.out_hl + (int64_t)(p0 + i1) * 2 * a.out_ld + r, a.out_ld, h);
+      }
+    }
+  } else {
+    const int r = 16 * tr + c;
+    if (r < a.n_out) {
+      if (i0 < n) a.out[(int64_t)(p0 + i0) * a.n_out + r] = y0;
+      if (i1 < n) a.out[(int64_t)(p0 + i1) * a.n_out + r] = y1;
+    }
+  }
+}
+
 template <int WF, bool GU>
 __global__ __launch_bounds__(kBlock) void k_exp(ExpArgs a) {
   extern __shared__ uint4 sm[];
@@ -692,7 +745,11 @@ __global__ __launch_bounds__(kBlock) void k_exp(ExpArgs a) {
   // unit order (so that the units of one expert reuse its weights from that L2)
   const int n_units = min(a.ctrl[0], a.max_units);
   int wgi, u;
-  if (!xcd_item(blockIdx.x, a.wg_per_unit, a.max_units, wgi, u) || u >= n_units) return;
+  if (a.chunk > 0) {
+    if (!chunk_item(blockIdx.x, n_units, a.wg_per_unit, a.chunk, wgi, u)) return;
+  } else if (!xcd_item(blockIdx.x, a.wg_per_unit, a.max_units, wgi, u) || u >= n_units) {
+    return;
+  }
   {
     const int4 un = *reinterpret_cast<const int4*>(a.units + 4 * u);
     const int e = un.x, p0 = un.y, n = un.z;
@@ -722,25 +779,8 @@ __global__ __launch_bounds__(kBlock) void k_exp(ExpArgs a) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     if (live) acc = run_tile_row_n<WF, WF == 1 ? 4 : 3>(ts, trow, q0, q1 - q0, sm, c % nr, nr);
     acc = reduce_ksplit(acc, part, a.ksplit, kp);
-    if (tr < a.n_tr && kp == 0) {
-      // D rows 4g..4g+3 = (hi, lo) of positions 2g and 2g + 1 of the unit
-      const float y0 = acc[0] + acc[1], y1 = acc[2] + acc[3];
-      const int i0 = 2 * g, i1 = 2 * g + 1;
-      if (GU) {
-        const float g0 = from_gate_lane(y0), g1 = from_gate_lane(y1);
-        const int r = 8 * tr + (c - 8);
-        if (c >= 8 && r < a.n_out) {
-          if (i0 < n) a.out[(int64_t)(p0 + i0) * a.n_out + r] = glu_act(g0, y0, a.act, a.bg, a.bl);
-          if (i1 < n) a.out[(int64_t)(p0 + i1) * a.n_out + r] = glu_act(g1, y1, a.act, a.bg, a.bl);
-        }
-      } else {
-        const int r = 16 * tr + c;
-        if (r < a.n_out) {
-          if (i0 < n) a.out[(int64_t)(p0 + i0) * a.n_out + r] = y0;
-          if (i1 < n) a.out[(int64_t)(p0 + i1) * a.n_out + r] = y1;
-        }
-      }
-    }
+    // D rows 4g..4g+3 = (hi, lo) of positions 2g and 2g + 1 of the unit
+    if (tr < a.n_tr && kp == 0) exp_store<GU>(a, p0, n, tr, c, 2 * g, acc[0] + acc[1], acc[2] + acc[3]);
   }
 }
 
@@ -934,25 +974,28 @@ struct TTStage {
 };
 
 // The K loop of a tile: D[b] (16 x 16 block b of the tile's rows x this wavefront's tile
-// row) over all ks K-steps.  Sums restart every qper K-steps and the partial sums are
-// added in order (the K-split of the launches for few tokens).  Every wavefront of the
-// workgroup runs it (staging and barriers are shared); trow must be a valid tile row
-// (waves without one pass tile row 0 and drop the result).  The loop runs whole rounds
-// of the P-deep ring: steps past ks re-read the last K-step and are never summed.
-template <int WF, int P, int NB>
+// row) over all ks K-steps.  With PARTS, sums restart every qper K-steps and the partial
+// sums are added in order (the K-split of the launches for few tokens); without, one
+// running sum over all of K (qper is then ks).  Every wavefront of the workgroup runs it
+// (staging and barriers are shared); trow must be a valid tile row (waves without one pass
+// tile row 0 and drop the result).  Weights are loaded P K-steps ahead, activations PA
+// (P a multiple of PA).  The loop runs whole rounds of P steps: steps past ks re-read the
+// last K-step and are never summed.
+template <int WF, int P, int NB, int PA = P, bool PARTS = true>
 __device__ __forceinline__ void tt_run(const TTRows& rows, const TTSrc& src, const uint8_t* trow,
                                        int ks, int qper, uint4* lds, f32x4_t (&tot)[NB]) {
+  static_assert(P % PA == 0, "the weight ring is a multiple of the activation ring");
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane & 15, g = lane >> 4;
   constexpr int RB = 16 * NB;
   constexpr int rstride = RB * 16;           // words per buffer (16 pieces x RB rows)
   TileStream<WF, P> ts;
-  TTStage<P, NB> st;
+  TTStage<PA, NB> st;
   st.init(rows, src);
 #pragma unroll
   for (int i = 0; i < P; ++i) {
     ts.w[i].load(trow, min(i, ks - 1), lane);
-    st.load(i, src, min(i, ks - 1));
+    if (i < PA) st.load(i, src, min(i, ks - 1));
   }
   asm volatile("" ::: "memory");
   st.commit(0, lds, src, 0);
@@ -970,33 +1013,27 @@ __device__ __forceinline__ void tt_run(const TTRows& rows, const TTSrc& src, con
 #pragma unroll
     for (int i = 0; i < P; ++i) {
       const int q = j + i;
-      // slot i held K-step q, committed to LDS at the end of the previous step
-      st.load(i, src, min(q + P, ks - 1));
+      // activation slot i % PA held K-step q, committed to LDS at the end of the previous step
+      st.load(i % PA, src, min(q + PA, ks - 1));
       const uint4* buf = lds + (q & 1) * rstride;
-      uint4 af[4][NB];
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const int jj = WeightStep<WF>::a_piece(s4, g);
-          af[s4][b] = buf[jj * RB + 16 * b + (c ^ jj)];
-        }
       constexpr bool kFp8 = WeightStep<WF>::kFp8;
+      ts.w[i].pin();
       const float scl = WF ? ts.w[i].scale(g) : 0.f;
       f32x4_t part[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b) part[b] = kFp8 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : cur[b];
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
+        const int jj = WeightStep<WF>::a_piece(s4, g);
         const uint4 bw = ts.w[i].operand(s4, scl);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) part[b] = mfma_bf16(af[s4][b], bw, part[b]);
+        for (int b = 0; b < NB; ++b) part[b] = mfma_bf16(buf[jj * RB + 16 * b + (c ^ jj)], bw, part[b]);
       }
 #pragma unroll
       for (int b = 0; b < NB; ++b)   // FP8: the K-step's partial sums times its block scale
         cur[b] = kFp8 ? WeightStep<WF>::scale_add(part[b], scl, cur[b]) : part[b];
       ts.w[i].load(trow, min(q + P, ks - 1), lane);
-      if (q < ks && (++in_part == qper || q + 1 == ks)) {
+      if (PARTS && q < ks && (++in_part == qper || q + 1 == ks)) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           tot[b] = first ? cur[b] : tot[b] + cur[b];
@@ -1005,8 +1042,12 @@ __device__ __forceinline__ void tt_run(const TTRows& rows, const TTSrc& src, con
         first = false;
         in_part = 0;
       }
+      if (!PARTS && q + 1 == ks) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) tot[b] = cur[b];
+      }
       asm volatile("" ::: "memory");
-      st.commit((i + 1) % P, lds + ((q + 1) & 1) * rstride, src, min(q + 1, ks - 1));
+      st.commit((i + 1) % PA, lds + ((q + 1) & 1) * rstride, src, min(q + 1, ks - 1));
       __syncthreads();
     }
   }
@@ -1181,68 +1222,47 @@ __global__ __launch_bounds__(kBlock) void k_out_tt(OutTTArgs a) {
   }
 }
 
-// Gate/up: h[p] = act(gate, up) (and its hi/lo row for the down launch); down: E[p].
-// y0, y1 are the sums of positions i0 and i0 + 1 of the unit (position offset p0, n used).
-template <bool GU>
-__device__ __forceinline__ void exp_store(const ExpArgs& a, int p0, int n, int tr, int c, int i0,
-                                          float y0, float y1) {
-  const int i1 = i0 + 1;
-  if (GU) {
-    const float g0 = from_gate_lane(y0), g1 = from_gate_lane(y1);
-    const int r = 8 * tr + (c - 8);
-    if (c >= 8 && r < a.n_out) {
-      if (i0 < n) {
-        const float h = glu_act(g0, y0, a.act, a.bg, a.bl);
-        a.out[(int64_t)(p0 + i0) * a.n_out + r] = h;
-        store_hilo(a.out_hl + (int64_t)(p0 + i0) * 2 * a.out_ld + r, a.out_ld, h);
-      }
-      if (i1 < n) {
-        const float h = glu_act(g1, y1, a.act, a.bg, a.bl);
-        a.out[(int64_t)(p0 + i1) * a.n_out + r] = h;
-        store_hilo(a.out_hl + (int64_t)(p0 + i1) * 2 * a.out_ld + r, a.out_ld, h);
-      }
-    }
-  } else {
-    const int r = 16 * tr + c;
-    if (r < a.n_out) {
-      if (i0 < n) a.out[(int64_t)(p0 + i0) * a.n_out + r] = y0;
-      if (i1 < n) a.out[(int64_t)(p0 + i1) * a.n_out + r] = y1;
-    }
-  }
-}
+// Work order of the token-tiled expert launches: 0 = xcd_item (every XCD walks one
+// tile-row group through all units: measured faster on the decode batches than the
+// chunks of chunk_item, which keep a chunk's activation rows in L2 but concentrate the
+// XCD's weight reads on a few experts), > 0 = chunk_item with that many units per chunk.
+constexpr int kExpChunk = 0;
 
-// Positions of a unit up to which the expert launch stages the whole K range at once and
-// streams the weights without barriers (as for a few tokens); larger units take the
-// K-step loop of the token-tiled products.
-constexpr int kExpWholeK = 2;
-
-// The K-step loop for a unit of n > kExpWholeK positions (2n hi/lo rows in NB blocks).
+// The K-step loop for a unit of n positions (2n hi/lo rows in NB blocks).
 template <int WF, bool GU, int NB>
 __device__ __forceinline__ void exp_tt_unit(const ExpArgs& a, const TTRows& rows, uint4* sm,
                                             const uint8_t* trow, bool live, int p0, int n, int tr,
                                             int c, int g) {
   f32x4_t tot[NB];
-  tt_run<WF, 4, NB>(rows, TTSrc{a.xin_hl, nullptr, 2 * n, a.kin, 0, 0}, trow, a.ks,
-                             a.ks, sm, tot);
+  // weights about 4 KiB per wavefront ahead (4 MXFP4 K-steps, 2 FP8 or bf16 ones)
+  tt_run<WF, WF == 1 ? 4 : 2, NB, 2, false>(rows, TTSrc{a.xin_hl, nullptr, 2 * n, a.kin, 0, 0},
+                                            trow, a.ks, a.ks, sm, tot);
   if (!live) return;
 #pragma unroll
   for (int b = 0; b < NB; ++b)
     exp_store<GU>(a, p0, n, tr, c, 8 * b + 2 * g, tot[b][0] + tot[b][1], tot[b][2] + tot[b][3]);
 }
 
-// Routed experts for units of up to 32 positions.  The input rows are hi/lo bf16 rows
-// written by their producer (x^c by the IN launch, h by the gate/up launch).
+// Routed experts for the second list of the unit table: units [ctrl[1], ctrl[0]), each of
+// up to 32 positions (the first list, of short units, goes to k_exp).  The input rows are
+// hi/lo bf16 rows written by their producer (x^c by the IN launch, h by the gate/up
+// launches).
 template <int WF, bool GU>
-__global__ __launch_bounds__(kBlock) void k_exp_tt(ExpArgs a) {
+__global__ __launch_bounds__(kBlock, 4) void k_exp_tt(ExpArgs a) {
   extern __shared__ uint4 sm[];
   __shared__ TTRows rows;
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
-  const int n_units = min(a.ctrl[0], a.max_units);
+  const int first = a.ctrl[1];
+  const int n_units = min(a.ctrl[0] - first, a.max_units);
   int wgi, u;
-  if (!xcd_item(blockIdx.x, a.wg_per_unit, a.max_units, wgi, u) || u >= n_units) return;
-  const int4 un = *reinterpret_cast<const int4*>(a.units + 4 * u);
+  if (a.chunk > 0) {
+    if (!chunk_item(blockIdx.x, n_units, a.wg_per_unit, a.chunk, wgi, u)) return;
+  } else if (!xcd_item(blockIdx.x, a.wg_per_unit, a.max_units, wgi, u) || u >= n_units) {
+    return;
+  }
+  const int4 un = *reinterpret_cast<const int4*>(a.units + 4 * (first + u));
   const int e = un.x, p0 = un.y, n = un.z;
   if (e < 0 || e >= a.E || n < 1 || n > a.nu || n > kHiloTTRows || p0 < 0 || p0 + n > a.n_assign)
     return;
@@ -1250,9 +1270,6 @@ __global__ __launch_bounds__(kBlock) void k_exp_tt(ExpArgs a) {
   const bool live = tr < a.n_tr;
   const uint8_t* trow = a.experts + (size_t)e * a.expert_bytes + a.region_off +
                         (size_t)(live ? tr : 0) * a.ks * WeightStep<WF>::SB;
-  constexpr int P = WF == 1 ? 4 : 3;
-  TileStream<WF, P> ts;
-  if (n <= kExpWholeK) ts.prefetch(trow, 0, a.ks);
   if ((int)threadIdx.x < 2 * n) {
     const int i = threadIdx.x >> 1, hl = threadIdx.x & 1;
     int64_t src = p0 + i;
@@ -1263,23 +1280,9 @@ __global__ __launch_bounds__(kBlock) void k_exp_tt(ExpArgs a) {
     rows.o0[threadIdx.x] = (uint32_t)((src * 2 + hl) * a.kin_ld / 8);
   }
   __syncthreads();
-  if (n > kExpWholeK) {
-    if (n <= 8) exp_tt_unit<WF, GU, 1>(a, rows, sm, trow, live, p0, n, tr, c, g);
-    else if (n <= 16) exp_tt_unit<WF, GU, 2>(a, rows, sm, trow, live, p0, n, tr, c, g);
-    else exp_tt_unit<WF, GU, 4>(a, rows, sm, trow, live, p0, n, tr, c, g);
-    return;
-  }
-  // few positions: the whole K range at once, word j * nr + r = row r, columns 8j..8j+7
-  const int nr = 2 * n, per_row = a.ks * 16;
-  const uint4* xin = reinterpret_cast<const uint4*>(a.xin_hl);
-  for (int idx = threadIdx.x; idx < nr * per_row; idx += kBlock) {
-    const int r = idx / per_row, j = idx - r * per_row;
-    sm[j * nr + r] = 8 * j < a.kin ? xin[rows.o0[r] + j] : make_uint4(0u, 0u, 0u, 0u);
-  }
-  __syncthreads();
-  if (!live) return;
-  const f32x4_t acc = run_tile_row_n<WF, P>(ts, trow, 0, a.ks, sm, c % nr, nr);
-  exp_store<GU>(a, p0, n, tr, c, 2 * g, acc[0] + acc[1], acc[2] + acc[3]);
+  if (n <= 8) exp_tt_unit<WF, GU, 1>(a, rows, sm, trow, live, p0, n, tr, c, g);
+  else if (n <= 16) exp_tt_unit<WF, GU, 2>(a, rows, sm, trow, live, p0, n, tr, c, g);
+  else exp_tt_unit<WF, GU, 4>(a, rows, sm, trow, live, p0, n, tr, c, g);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1557,7 +1560,7 @@ hipError_t launch_dispatch(const Shape& s, const int32_t* idx, int64_t T, int32_
   const int nch = cdiv(T, ct);
   hipLaunchKernelGGL(k_disp_count, dim3(nch), dim3(kBlock), 0, st, idx, n, s.E, chunk, chunk_hist);
   hipLaunchKernelGGL(k_disp_scan, dim3(1), dim3(1024), 0, st, nch, s.E, unit_positions(s, T),
-                     chunk_hist, counts, offs, units, ctrl);
+                     small_unit_positions(s, T), chunk_hist, counts, offs, units, ctrl);
   hipLaunchKernelGGL(k_disp_scatter, dim3(nch), dim3(kBlock), 0, st, idx, n, s.E, chunk,
                      (const int32_t*)chunk_hist, (const int32_t*)offs, perm, inv);
   return hipGetLastError();
@@ -1591,22 +1594,39 @@ hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_
   // cross-wavefront sum cost more than a K-split gains)
   a.ksplit = 1;
   a.wg_per_unit = cdiv(a.n_tr, kWavesPerBlock);
-  const unsigned grid = (unsigned)xcd_grid(a.wg_per_unit, a.max_units);
+  a.chunk = 0;
   if (token_tiled(s, T)) {
-    const size_t lds = std::max((size_t)2 * kHiloTTBlocks * 16 * 16 * 16,
-                                (size_t)2 * kExpWholeK * a.ks * kStepK * 2);
-    if (s.wfmt == 1) {
-      if (gu) hipLaunchKernelGGL((k_exp_tt<1, true>), dim3(grid), dim3(kBlock), lds, st, a);
-      else hipLaunchKernelGGL((k_exp_tt<1, false>), dim3(grid), dim3(kBlock), lds, st, a);
-    } else if (s.wfmt == 2) {
-      if (gu) hipLaunchKernelGGL((k_exp_tt<2, true>), dim3(grid), dim3(kBlock), lds, st, a);
-      else hipLaunchKernelGGL((k_exp_tt<2, false>), dim3(grid), dim3(kBlock), lds, st, a);
-    } else {
-      if (gu) hipLaunchKernelGGL((k_exp_tt<0, true>), dim3(grid), dim3(kBlock), lds, st, a);
-      else hipLaunchKernelGGL((k_exp_tt<0, false>), dim3(grid), dim3(kBlock), lds, st, a);
+    // the long units: K-step loop over tiles of their hi/lo rows
+    ExpArgs b = a;
+    b.max_units = (int)max_large_units(s, T);
+    b.chunk = kExpChunk;
+    if (b.max_units > 0) {
+      const unsigned grid = (unsigned)(b.chunk > 0 ? chunk_grid(b.max_units, b.wg_per_unit, b.chunk)
+                                                   : xcd_grid(b.wg_per_unit, b.max_units));
+      const size_t lds = (size_t)2 * kHiloTTBlocks * 16 * 16 * 16;
+      if (s.wfmt == 1) {
+        if (gu) hipLaunchKernelGGL((k_exp_tt<1, true>), dim3(grid), dim3(kBlock), lds, st, b);
+        else hipLaunchKernelGGL((k_exp_tt<1, false>), dim3(grid), dim3(kBlock), lds, st, b);
+      } else if (s.wfmt == 2) {
+        if (gu) hipLaunchKernelGGL((k_exp_tt<2, true>), dim3(grid), dim3(kBlock), lds, st, b);
+        else hipLaunchKernelGGL((k_exp_tt<2, false>), dim3(grid), dim3(kBlock), lds, st, b);
+      } else {
+        if (gu) hipLaunchKernelGGL((k_exp_tt<0, true>), dim3(grid), dim3(kBlock), lds, st, b);
+        else hipLaunchKernelGGL((k_exp_tt<0, false>), dim3(grid), dim3(kBlock), lds, st, b);
+      }
+      const hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
     }
-    return hipGetLastError();
+    // the short ones (the first list: its count is ctrl[1]) as for a few tokens
+    a.ctrl = ws.ctrl + 1;
+    a.nu = small_unit_positions(s, T);
+    a.max_units = (int)max_small_units(s, T);
+    a.chunk = kExpChunk;
+  } else {
+    a.out_hl = nullptr;
   }
+  const unsigned grid = (unsigned)(a.chunk > 0 ? chunk_grid(a.max_units, a.wg_per_unit, a.chunk)
+                                               : xcd_grid(a.wg_per_unit, a.max_units));
   const size_t lds = (size_t)2 * a.nu * a.ks * kStepK * 2;
   if (s.wfmt == 1) {
     if (gu) hipLaunchKernelGGL((k_exp<1, true>), dim3(grid), dim3(kBlock), lds, st, a);

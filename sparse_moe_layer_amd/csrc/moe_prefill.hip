@@ -538,25 +538,9 @@ __device__ __forceinline__ void pf_exp_unit(const PfExpArgs& a, const PfRows& ro
   }
 }
 
-// Work order of the expert launches.  Workgroups go round-robin to the 8 XCDs; XCD x
-// takes a contiguous range of the units (so of the experts: the unit table is sorted by
-// expert) and walks it in chunks of kPfChunk units, each chunk through every tile-row
-// group: a chunk's activation rows stay in that XCD's L2 across the groups, and the few
-// units of one expert read each weight slice close together in time (once from HBM).
+// Work order of the expert launches: chunks of 4 units through every tile-row group
+// (chunk_item).
 constexpr int kPfChunk = 4;
-__device__ __forceinline__ bool pf_exp_item(int bid, int n_units, int n_grp, int& grp, int& u) {
-  const int x = bid % kXcds, j = bid / kXcds;
-  const int per_xcd = (n_units + kXcds - 1) / kXcds;
-  const int chunk = j / (kPfChunk * n_grp), r = j - chunk * kPfChunk * n_grp;
-  grp = r / kPfChunk;
-  const int ui = chunk * kPfChunk + (r - grp * kPfChunk);
-  u = x * per_xcd + ui;
-  return ui < per_xcd && u < n_units;
-}
-__host__ inline int64_t pf_exp_grid(int64_t max_units, int64_t n_grp) {
-  const int64_t per_xcd = (max_units + kXcds - 1) / kXcds;
-  return kXcds * ((per_xcd + kPfChunk - 1) / kPfChunk) * kPfChunk * n_grp;
-}
 
 // Two workgroups per compute unit (a register budget of 256 per lane): while one waits at
 // its barrier or for its loads the other issues MFMAs.
@@ -568,7 +552,7 @@ __global__ __launch_bounds__(kBlock, 2) void k_pf_exp(PfExpArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_units = min(a.ctrl[0], a.max_units);
   int grp, u;
-  if (!pf_exp_item(blockIdx.x, n_units, a.n_grp, grp, u)) return;
+  if (!chunk_item(blockIdx.x, n_units, a.n_grp, kPfChunk, grp, u)) return;
   const int4 un = *reinterpret_cast<const int4*>(a.units + 4 * u);
   const int e = un.x, p0 = un.y, n = un.z;
   if (e < 0 || e >= a.E || n < 1 || n > a.nu || n > kPfRows || p0 < 0 || p0 + n > a.n_assign) return;
@@ -687,7 +671,7 @@ hipError_t launch_pf_expert(const Shape& s, const uint8_t* experts, bool gu, int
   a.rbg = 1.f / s.beta_gate; a.rbl = 1.f / s.beta_lin;
   a.out = ws.eo;
   a.n_out = s.l;
-  const unsigned grid = (unsigned)pf_exp_grid(a.max_units, a.n_grp);
+  const unsigned grid = (unsigned)chunk_grid(a.max_units, a.n_grp, kPfChunk);
   if (gu) hipLaunchKernelGGL(k_pf_exp<true>, dim3(grid), dim3(kBlock), kPfExpLds, st, a);
   else hipLaunchKernelGGL(k_pf_exp<false>, dim3(grid), dim3(kBlock), kPfExpLds, st, a);
   return hipGetLastError();
