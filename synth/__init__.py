@@ -198,8 +198,15 @@ K2_MOE_1024_ZIPF = LayerConfig(
     expert_fmt="fp8b128", act="swiglu", route_scale=2.827, use_norm=False,
     bias_kind="file", bias_file="k2_zipf1.2_bias.f32")
 
+# One GPU's share of an expert-parallel prefill: 65,536 tokens over 8 GPUs send each GPU's
+# 112 experts about 1,170 rows apiece (65,536 x 16 / 896).  The same row count comes from
+# 8192 tokens routed top-16 over 112 experts, the regime where the expert products are
+# bound by the matrix cores rather than by the weight stream.
+K3_EP_SHARE = LayerConfig(name="k3_ep_share_112x1170", tokens=8192, seed=1006, precision="mx8",
+                          **{**_K3, "E": 112})
+
 PRESETS = {c.name: c for c in (TOY, K3_DECODE_B1, K3_DECODE_B64_ZIPF, K3_PREFILL_8K,
-                               K2_MOE_1024_ZIPF)}
+                               K2_MOE_1024_ZIPF, K3_EP_SHARE)}
 
 
 def param_shapes(cfg: LayerConfig) -> dict:

@@ -344,6 +344,26 @@ def test_k3_prefill_8192_sampled_tokens():
     assert rel < 1e-3
 
 
+def test_k3_ep_share_sampled_tokens():
+    """One GPU's expert-parallel share (112 experts, about 1,170 rows each) in the mx8
+    profile: every token's indices from the oracle router, Delta of sampled tokens."""
+    cfg = synth.K3_EP_SHARE
+    lay, _ = device_layer(cfg)
+    x = synth.tokens(cfg, batch=0)
+    log(f"[ep share] T={x.shape[0]} E={cfg.E}")
+    delta, idx, w = run(lay, x)
+    counts = np.bincount(idx.reshape(-1), minlength=cfg.E)
+    log(f"[ep share] rows per expert min {counts.min()} max {counts.max()}")
+    assert counts.sum() == cfg.tokens * cfg.k and counts.min() > 0
+    OL = oracle_layer(cfg)
+    s = O.router_scores(O.bf16_to_f64(x), OL.router)
+    ridx, G, margin = O.select_and_weight(s, OL.bias, cfg.k)
+    assert_routing(idx, ridx, O.selection_kappa(s, OL.bias, cfg.k), margin)
+    assert np.all(np.isfinite(delta))
+    rel, mxr, _ = check(cfg, x, delta, idx, w, rows=[0, 3001, 8191])
+    assert rel < 1e-3
+
+
 # ---- the K2-style non-latent block: FP8 E4M3 block-128 experts, SwiGLU, gate scale 2.827 --
 
 TINY_K2 = synth.LayerConfig(name="tiny_k2", d=160, l=0, E=6, k=2, m=48, ms=32, tokens=5,
