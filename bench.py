@@ -47,17 +47,27 @@ def algorithmic_bytes(cfg, T, D):
     gu_w, dn_w = expert_weight_bytes(cfg)
     tk = T * k
     small = T <= 3   # the route and the dispatch run inside the IN launch
-    sh_head = 0   # shared gate/up rows in the ROUTER launch
+    mx8 = getattr(cfg, "precision", "fp32") == "mx8"
+    ab = 4 if not mx8 else 1 + 1 / 32   # bytes per activation element of the expert inputs
+    if mx8:
+        # one IN product (router logits, x^c fp32, h_s bf16), then x^c to MXFP8
+        router = T * d * 2 + (E + cfg.l + 2 * ms) * d * 2 + T * (E * 4 + cfg.l * 4 + ms * 2)
+        in_ = T * cfg.l * 4 + T * cfg.l * ab
+    else:
+        # W_down_latent rides in the ROUTER launch for a few tokens, in the IN launch otherwise
+        ldn = cfg.l if small else 0
+        router = T * d * 2 + (E + ldn) * d * 2 + T * (E + ldn) * 4
+        in_ = (T * d * 2 + (cfg.l - ldn + 2 * ms) * d * 2 + T * (cfg.l - ldn + ms) * 4
+               + ((T * E * 4 + E * 4 + tk * 16 + E * 8) if small else 0))
     return {
-        "router": T * d * 2 + (E + cfg.l + 2 * sh_head) * d * 2 + T * (E + l + sh_head) * 4,
-        "in": T * d * 2 + 2 * (ms - sh_head) * d * 2 + T * (ms - sh_head) * 4
-              + ((T * E * 4 + E * 4 + tk * 16 + E * 8) if small else 0),
+        "router": router,
+        "in": in_,
         "route": 0 if small else T * E * 4 + E * 4 + tk * 8,
         "dispatch": 0 if small else tk * 4 * 4 + E * 8,
-        "expert_gu": D * gu_w + T * l * 4 + tk * m * 4,
-        "expert_down": D * dn_w + tk * m * 4 + tk * l * 4,
+        "expert_gu": D * gu_w + T * l * ab + tk * m * ab,
+        "expert_down": D * dn_w + tk * m * ab + tk * l * 4,
         "combine": tk * l * 4 + tk * 8 + T * l * 4,
-        "out": d * (cfg.l + ms) * 2 + cfg.l * 2 + T * (l + ms) * 4 + T * d * 4,
+        "out": d * (cfg.l + ms) * 2 + cfg.l * 2 + T * (l + ms) * (2 if mx8 else 4) + T * d * 4,
     }
 
 def algorithmic_flops(cfg, T):
@@ -80,12 +90,24 @@ def weight_bytes(cfg, D):
     return (E * d + 2 * l * d + l + 3 * ms * d) * 2 + E * 4 + D * sum(expert_weight_bytes(cfg))
 
 
-# rocprofv3 kernel symbol of each step's launch (its template arguments vary with shape)
-STEP_KERNELS = {"router": ("k_router",), "in": ("k_in",), "expert_gu": ("k_exp", "true"),
-                "expert_down": ("k_exp", "false"), "combine": ("k_combine",), "out": ("k_out",)}
-STEP_KERNELS_MX8 = {"router": ("k_pf_dense", "true"), "in": ("k_pf_quant",),
-                    "expert_gu": ("k_pf_exp", "true"), "expert_down": ("k_pf_exp", "false"),
-                    "combine": ("k_pf_norm",), "out": ("k_pf_dense", "false")}
+# rocprofv3 kernel symbols of each step's launches (their template arguments vary with
+# shape): a kernel belongs to the step when its name holds all the words of one entry
+STEP_KERNELS = {"router": [("k_router",), ("k_token_rows",)], "in": [("k_in",)],
+                "route": [("k_route",)], "dispatch": [("k_disp",)],
+                "expert_gu": [("k_exp", "true")], "expert_down": [("k_exp", "false")],
+                "combine": [("k_combine",), ("k_norm",)], "out": [("k_out",)]}
+STEP_KERNELS_MX8 = {"router": [("k_pf_dense", "true")], "in": [("k_pf_quant",)],
+                    "route": [("k_route",)], "dispatch": [("k_disp",)],
+                    "expert_gu": [("k_pf_exp", "true")], "expert_down": [("k_pf_exp", "false")],
+                    "combine": [("k_combine",), ("k_pf_norm",)], "out": [("k_pf_dense", "false")]}
+
+
+def step_of_kernel(name, kernels):
+    """The step whose launches include the kernel `name`, or None."""
+    for step, alts in kernels.items():
+        if any(all(w in name for w in words) for words in alts):
+            return step
+    return None
 
 
 def kernel_sources_sha():
@@ -109,10 +131,11 @@ def measured_traffic(workload, step, kernels=None):
             rec = json.loads(line[len("traffic_json: "):])
             if rec.get("src_sha") != kernel_sources_sha():
                 return None
-            want = (kernels or STEP_KERNELS).get(step, ())
-            for name, v in rec["bytes_per_launch"].items():
-                if want and all(w in name for w in want):
-                    return v
+            # a step may take more than one launch (the token-tiled expert steps launch the
+            # kernel for short units and the one for long units): their bytes add up
+            hits = [v for name, v in rec["bytes_per_launch"].items()
+                    if step_of_kernel(name, kernels or STEP_KERNELS) == step]
+            return sum(hits) if hits else None
     return None
 
 

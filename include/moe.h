@@ -183,7 +183,8 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t max_tokens, size_t*
 
 /* Offsets (bytes) of the intermediates inside the workspace of a call with n_tokens,
  * for inspection after moe_layer_forward (host call).  Layouts, all row-major:
- *   [0] control words (internal: [0] = number of units of the expert launches)
+ *   [0] control words (internal: [0] = number of units of the expert launches, [1] = how
+ *       many of them, first in the unit table, are short enough for the few-token kernel)
  *   [1] x^c    [T][l]   fp32     latent down-projection
  *   [2] h_s    [T][m_s] fp32     shared SiTU-GLU hidden
  *   [3] h      [T*k][m] fp32     routed expert hidden, rows in dispatch order
