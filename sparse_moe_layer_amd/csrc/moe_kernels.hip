@@ -700,6 +700,8 @@ struct ExpArgs {
   int kin_ld;
   uint16_t* out_hl;         // and the gate/up output's hi/lo rows [T*k][2][out_ld]
   int out_ld;
+  int single;               // 1: the input is bf16 (lo rows zero): the long units read the
+                            // hi rows alone, one row per position
 };
 
 // Gate/up: h[p] = act(gate, up) (and, with out_hl, its hi/lo row for the token-tiled down
@@ -1243,6 +1245,24 @@ __device__ __forceinline__ void exp_tt_unit(const ExpArgs& a, const TTRows& rows
     exp_store<GU>(a, p0, n, tr, c, 8 * b + 2 * g, tot[b][0] + tot[b][1], tot[b][2] + tot[b][3]);
 }
 
+// The same over one bf16 row per position (an input that is bf16 already, whose lo rows
+// are zero): D row 16 b + 4 g + v is position 16 b + 4 g + v, with the same sum as hi + lo
+// (hi + 0).
+template <int WF, bool GU, int NB>
+__device__ __forceinline__ void exp_tt_unit_single(const ExpArgs& a, const TTRows& rows, uint4* sm,
+                                                   const uint8_t* trow, bool live, int p0, int n,
+                                                   int tr, int c, int g) {
+  f32x4_t tot[NB];
+  tt_run<WF, WF == 1 ? 4 : 2, NB, 2, false>(rows, TTSrc{a.xin_hl, nullptr, n, a.kin, 0, 0},
+                                            trow, a.ks, a.ks, sm, tot);
+  if (!live) return;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    exp_store<GU>(a, p0, n, tr, c, 16 * b + 4 * g, tot[b][0], tot[b][1]);
+    exp_store<GU>(a, p0, n, tr, c, 16 * b + 4 * g + 2, tot[b][2], tot[b][3]);
+  }
+}
+
 // Routed experts for the second list of the unit table: units [ctrl[1], ctrl[0]), each of
 // up to 32 positions (the first list, of short units, goes to k_exp).  The input rows are
 // hi/lo bf16 rows written by their producer (x^c by the IN launch, h by the gate/up
@@ -1270,8 +1290,9 @@ __global__ __launch_bounds__(kBlock, 4) void k_exp_tt(ExpArgs a) {
   const bool live = tr < a.n_tr;
   const uint8_t* trow = a.experts + (size_t)e * a.expert_bytes + a.region_off +
                         (size_t)(live ? tr : 0) * a.ks * WeightStep<WF>::SB;
-  if ((int)threadIdx.x < 2 * n) {
-    const int i = threadIdx.x >> 1, hl = threadIdx.x & 1;
+  const bool single = GU && a.single;
+  if ((int)threadIdx.x < (single ? n : 2 * n)) {
+    const int i = single ? threadIdx.x : threadIdx.x >> 1, hl = single ? 0 : threadIdx.x & 1;
     int64_t src = p0 + i;
     if (GU) {
       const int asg = a.perm[p0 + i];
@@ -1280,6 +1301,11 @@ __global__ __launch_bounds__(kBlock, 4) void k_exp_tt(ExpArgs a) {
     rows.o0[threadIdx.x] = (uint32_t)((src * 2 + hl) * a.kin_ld / 8);
   }
   __syncthreads();
+  if (single) {
+    if (n <= 16) exp_tt_unit_single<WF, GU, 1>(a, rows, sm, trow, live, p0, n, tr, c, g);
+    else exp_tt_unit_single<WF, GU, 2>(a, rows, sm, trow, live, p0, n, tr, c, g);
+    return;
+  }
   if (n <= 8) exp_tt_unit<WF, GU, 1>(a, rows, sm, trow, live, p0, n, tr, c, g);
   else if (n <= 16) exp_tt_unit<WF, GU, 2>(a, rows, sm, trow, live, p0, n, tr, c, g);
   else exp_tt_unit<WF, GU, 4>(a, rows, sm, trow, live, p0, n, tr, c, g);
@@ -1590,6 +1616,7 @@ hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_
   a.kin_ld = gu ? s.l : s.m;
   a.out_hl = ws.h_hl;
   a.out_ld = s.m;
+  a.single = gu && !s.latent ? 1 : 0;   // x itself: bf16, its lo rows zero
   // one wavefront per tile row and its whole K range (the per-item staging and the
   // cross-wavefront sum cost more than a K-split gains)
   a.ksplit = 1;

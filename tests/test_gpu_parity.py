@@ -379,6 +379,20 @@ def test_nonlatent_fp8_tiny_token_counts(T):
     assert rel < 1e-5
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "bf16"])
+def test_nonlatent_mxfp4_and_bf16_experts_long_units(fmt):
+    """Without a latent the token-tiled gate/up reads one bf16 row per position: every
+    weight format, with units long enough for the K-step kernel (T * k / E ~ 33)."""
+    cfg = TINY_K2.with_(name=f"tiny_k2_{fmt}", expert_fmt=fmt, m=64, tokens=100)
+    lay, _ = device_layer(cfg)
+    x = synth.tokens(cfg)
+    rel, _, _ = check(cfg, x, *run(lay, x))
+    assert rel < 1e-5
+    one = [t.cpu().clone() for t in lay.forward(to_dev(x[57:58]))]
+    full = [t.cpu().clone() for t in lay.forward(to_dev(x))]
+    assert torch.equal(one[0][0], full[0][57]) and torch.equal(one[1][0], full[1][57])
+
+
 def test_latent_layer_with_fp8_block_experts():
     cfg = TINY.with_(name="tiny_latent_fp8", expert_fmt="fp8b128", d=200, l=136, m=40, tokens=9)
     lay, _ = device_layer(cfg)
