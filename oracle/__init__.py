@@ -12,3 +12,4 @@ the toy reproduction; the Chinese walkthrough of report section 2.3 and
 Appendix B; the NVFP4 port notes) in float64, on exactly dequantised weights.
 """
 from .moe_oracle import *  # noqa: F401,F403
+from .qb import *  # noqa: F401,F403,E402
