@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef struct ihipStream_t* moe_stream_t; /* the same type as hipStream_t */
 
@@ -294,6 +294,36 @@ moe_status moe_route(const moe_config* cfg, const moe_weights* w, const float* b
 moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int64_t n_tokens,
                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
                         void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* Quantile Balancing statistics of the router (toy chapter "Quantile Balancing: giving
+ * every expert a fair shot"; walkthrough "Stable 之三：Quantile Balancing" and its histogram
+ * estimate).  The training-side step next to S1: it reads the router and the current
+ * biases and leaves the forward untouched.
+ *
+ * moe_qb_histogram: the router of n_tokens tokens x (as in moe_route; the logits are left
+ * in workspace slot [12]), then per token the cutoff alpha = the (k+1)-th largest
+ * s + b (float32) and, for every expert e, r = alpha - s_e (float32: the bias expert e
+ * needs to make the token's top k) counted into hist[e * n_bins + bin], with n_bins
+ * uniform bins over [lo, hi] = [min(bias) - 1, max(bias) + 1] (float32) and bin =
+ * floor((r - lo) * (n_bins / (hi - lo))) clamped to 0 .. n_bins - 1.  hist: device int32
+ * [E][n_bins], ADDED to (the caller zeroes it; calls over several micro-batches with the
+ * same biases accumulate, integer atomics, so the counts do not depend on the order).
+ * Needs top_k < n_experts and top_k <= 63; 1 <= n_bins <= MOE_QB_MAX_BINS.  workspace:
+ * at least moe_workspace_size(cfg, n_tokens) bytes.  n_tokens = 0 does nothing.
+ *
+ * moe_qb_readout: from such counts over n_tokens tokens in all, the new biases
+ * new_bias[E] (device float32): per expert the first bin where the cumulative count
+ * reaches ceil(n_tokens * k / E), at lo + w (t + (ceil(q) - C) / c_t) (w the bin width,
+ * C the count below bin t, c_t the bin's), then the mean over the experts subtracted.
+ * The estimate is within one bin width of the exact order statistic.  bias must be the
+ * biases the counts were taken with (they fix lo and hi).  Asynchronous. */
+#define MOE_QB_MAX_BINS 65536
+moe_status moe_qb_histogram(const moe_config* cfg, const moe_weights* w, const float* bias,
+                            const void* x, int64_t n_tokens, int32_t n_bins, int32_t* hist,
+                            void* workspace, size_t workspace_bytes, moe_stream_t stream);
+moe_status moe_qb_readout(const moe_config* cfg, const float* bias, int32_t n_bins,
+                          const int32_t* hist, int64_t n_tokens, float* new_bias,
+                          moe_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -24,9 +24,10 @@ WS_SLOTS = ("ctrl", "xc", "hs", "h", "eo", "u", "uh", "hl", "perm", "inv", "coun
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_packed_dense_size", "moe_pack_dense",
            "moe_packed_experts_size", "moe_pack_experts", "moe_workspace_size",
            "moe_workspace_layout", "moe_layer_forward",
-           "moe_layer_forward_timed", "moe_layer_forward_steps", "moe_route", "moe_dispatch")
+           "moe_layer_forward_timed", "moe_layer_forward_steps", "moe_route", "moe_dispatch",
+           "moe_qb_histogram", "moe_qb_readout")
 STEPS = ("router", "in", "route", "dispatch", "expert_gu", "expert_down", "combine", "out")
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class MoeConfig(ctypes.Structure):
@@ -93,6 +94,9 @@ def lib():
                                           vp, sz, ctypes.c_int32, ctypes.c_int32, vp]
     L.moe_route.argtypes = [P(MoeConfig), P(MoeWeights), vp, vp, i64, vp, vp, vp, sz, vp]
     L.moe_dispatch.argtypes = [P(MoeConfig), vp, i64, vp, vp, vp, vp, vp, sz, vp]
+    i32 = ctypes.c_int32
+    L.moe_qb_histogram.argtypes = [P(MoeConfig), P(MoeWeights), vp, vp, i64, i32, vp, vp, sz, vp]
+    L.moe_qb_readout.argtypes = [P(MoeConfig), vp, i32, vp, i64, vp, vp]
     for f in EXPORTS[2:]:
         getattr(L, f).restype = ctypes.c_int
     if L.moe_abi_version() != ABI_VERSION:
@@ -303,6 +307,32 @@ class Layer:
                                x.data_ptr(), T, idx.data_ptr(), w.data_ptr(), ws.data_ptr(),
                                ws.numel(), _stream(stream)), "moe_route")
         return idx, w
+
+    def qb_histogram(self, x, n_bins=1000, hist=None, stream=None):
+        """Quantile Balancing counts of the tokens x under the layer's biases, added to
+        hist (int32 [E, n_bins] on the device; a zeroed one when None)."""
+        import torch
+        T = x.shape[0]
+        c = self.cfg
+        if hist is None:
+            hist = torch.zeros((c.n_experts, n_bins), dtype=torch.int32, device=self.device)
+        ws = self.workspace(T)
+        W = self.weights_struct()
+        _check(lib().moe_qb_histogram(ctypes.byref(c), ctypes.byref(W), self.bias.data_ptr(),
+                                      x.data_ptr(), T, n_bins, hist.data_ptr(), ws.data_ptr(),
+                                      ws.numel(), _stream(stream)), "moe_qb_histogram")
+        return hist
+
+    def qb_readout(self, hist, n_tokens, bias=None, stream=None):
+        """The centred Quantile Balancing biases from counts over n_tokens tokens (taken
+        with `bias`, the layer's own by default)."""
+        import torch
+        c = self.cfg
+        b = self.bias if bias is None else bias
+        out = torch.empty(c.n_experts, dtype=torch.float32, device=self.device)
+        _check(lib().moe_qb_readout(ctypes.byref(c), b.data_ptr(), hist.shape[1], hist.data_ptr(),
+                                    n_tokens, out.data_ptr(), _stream(stream)), "moe_qb_readout")
+        return out
 
     def dispatch(self, idx, stream=None):
         import torch

@@ -415,6 +415,42 @@ MOE_EXPORT moe_status moe_route(const moe_config* cfg, const moe_weights* w, con
   return hip_status(moe::launch_route(rs, bias, n_tokens, ws, topk_idx, topk_w, hs));
 }
 
+MOE_EXPORT moe_status moe_qb_histogram(const moe_config* cfg, const moe_weights* w,
+                                       const float* bias, const void* x, int64_t n_tokens,
+                                       int32_t n_bins, int32_t* hist, void* workspace,
+                                       size_t workspace_bytes, moe_stream_t stream) {
+  Shape s;
+  moe_status st = make_shape(cfg, &s);
+  if (st != MOE_OK) return st;
+  if (n_tokens < 0 || n_bins < 1 || n_bins > MOE_QB_MAX_BINS || s.k >= s.E || s.k + 1 > 64)
+    return MOE_ERR_INVALID_ARG;
+  if (!hist || !aligned(hist, 4)) return MOE_ERR_INVALID_ARG;
+  if (n_tokens == 0) return MOE_OK;
+  size_t off[MOE_WS_NUM_SLOTS];
+  if ((st = check_call(s, w, bias, x, n_tokens, workspace, workspace_bytes, off)) != MOE_OK) return st;
+  const moe::Work ws = make_work(s, n_tokens, workspace, off);
+  hipStream_t hs = (hipStream_t)stream;
+  Shape rs = s;     // the router of the FP32 launches, as in moe_route
+  rs.prec = 0;
+  if (moe::launch_router(rs, static_cast<const uint8_t*>(w->dense), static_cast<const uint16_t*>(x),
+                         n_tokens, true, ws, hs) != hipSuccess)
+    return MOE_ERR_HIP;
+  return hip_status(moe::launch_qb_hist(rs, bias, n_tokens, n_bins, hist, ws, hs));
+}
+
+MOE_EXPORT moe_status moe_qb_readout(const moe_config* cfg, const float* bias, int32_t n_bins,
+                                     const int32_t* hist, int64_t n_tokens, float* new_bias,
+                                     moe_stream_t stream) {
+  Shape s;
+  moe_status st = make_shape(cfg, &s);
+  if (st != MOE_OK) return st;
+  if (n_tokens < 1 || n_bins < 1 || n_bins > MOE_QB_MAX_BINS || s.k >= s.E) return MOE_ERR_INVALID_ARG;
+  if (!bias || !hist || !new_bias || !aligned(bias, 4) || !aligned(hist, 4) || !aligned(new_bias, 4))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_qb_readout(s, bias, n_tokens, n_bins, hist, new_bias,
+                                           (hipStream_t)stream));
+}
+
 MOE_EXPORT moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int64_t n_tokens,
                                    int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
                                    void* workspace, size_t workspace_bytes, moe_stream_t stream) {

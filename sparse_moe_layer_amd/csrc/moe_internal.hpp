@@ -141,6 +141,12 @@ hipError_t launch_router(const Shape& s, const uint8_t* dense, const uint16_t* x
                          bool router_only, const Work& ws, hipStream_t st);
 hipError_t launch_in(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,
                      const float* bias, int32_t* idx, float* gw, const Work& ws, hipStream_t st);
+// Quantile Balancing statistics: counts of r = alpha - s into hist [E][bins] (added to
+// what it holds), and the centred biases read from such counts over T tokens.
+hipError_t launch_qb_hist(const Shape& s, const float* bias, int64_t T, int bins, int32_t* hist,
+                          const Work& ws, hipStream_t st);
+hipError_t launch_qb_readout(const Shape& s, const float* bias, int64_t T, int bins,
+                             const int32_t* hist, float* new_bias, hipStream_t st);
 hipError_t launch_route(const Shape& s, const float* bias, int64_t T, const Work& ws,
                         int32_t* idx, float* gw, hipStream_t st);
 // The logit planes the route sums: the router launch's K-split, or 1 (mx8: plain logits).

@@ -330,6 +330,203 @@ __global__ __launch_bounds__(kBlock) void k_disp_scatter(const int32_t* idx, int
 
 
 // ------------------------------------------------------------------------------------
+// Quantile Balancing statistics (the toy chapter's "Quantile Balancing"; the walkthrough's
+// "Stable 之三" and its histogram estimate).  Per token the cutoff alpha = the (k+1)-th
+// largest s + b (route with the top k + 1); per expert e the bias r = alpha - s_e it would
+// need to make the token's top k, counted into hist[e][bins] over [min b - 1, max b + 1]
+// (integer atomics: the counts do not depend on the order).  The readout takes per expert
+// the first bin where the cumulative count reaches ceil(T k / E), interpolates linearly
+// inside it, and removes the mean over the experts.
+// ------------------------------------------------------------------------------------
+struct QbArgs {
+  const float* z;
+  int zplanes;
+  int64_t zplane;
+  const float* bias;
+  int64_t T;
+  int E, k, bins;
+  int32_t* hist;
+  const int32_t* chist;     // readout: the counts
+  float* new_bias;          // readout: the centred biases
+};
+
+// (min b - 1, max b + 1) by the whole workgroup, from the float32 biases (E <= 1024).
+__device__ __forceinline__ void qb_range(const float* bias, int E, float* red, float& lo,
+                                         float& hi) {
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x >> 6;
+  float mn = INFINITY, mx = -INFINITY;
+  for (int e = threadIdx.x; e < E; e += kBlock) {
+    mn = fminf(mn, bias[e]);
+    mx = fmaxf(mx, bias[e]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, o));
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+  }
+  if (lane == 0) {
+    red[wv] = mn;
+    red[kWavesPerBlock + wv] = mx;
+  }
+  __syncthreads();
+  mn = red[0];
+  mx = red[kWavesPerBlock];
+#pragma unroll
+  for (int w = 1; w < kWavesPerBlock; ++w) {
+    mn = fminf(mn, red[w]);
+    mx = fmaxf(mx, red[kWavesPerBlock + w]);
+  }
+  __syncthreads();
+  lo = mn - 1.0f;
+  hi = mx + 1.0f;
+}
+
+__global__ __launch_bounds__(kBlock) void k_qb_hist(QbArgs a) {
+  __shared__ uint64_t cand_key[kWavesPerBlock * kMaxK];
+  __shared__ float cand_v[kWavesPerBlock * kMaxK];
+  __shared__ float red[2 * kWavesPerBlock];
+  __shared__ float alpha_sh;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
+  float lo, hi;
+  qb_range(a.bias, a.E, red, lo, hi);
+  const float inv_w = (float)a.bins / (hi - lo);
+  const int kk = a.k + 1;   // the cutoff is the (k+1)-th largest
+  for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x) {
+    const float* zr = a.z + t * a.E;
+    uint64_t key[kRouteSlots];
+    float sv[kRouteSlots], kv[kRouteSlots];
+#pragma unroll
+    for (int i = 0; i < kRouteSlots; ++i) {
+      const int e = (i * kWavesPerBlock + wv) * kWave + lane;
+      key[i] = 0;
+      sv[i] = 0.f;
+      kv[i] = 0.f;
+      if (e < a.E) {
+        float zv = 0.f;
+        for (int p = 0; p < a.zplanes; ++p) zv += zr[p * a.zplane + e];   // plane order
+        const float sc = sigmoidf_(zv);
+        float kap = sc + a.bias[e];
+        if (kap != kap) kap = -INFINITY;
+        sv[i] = sc;
+        kv[i] = kap;
+        key[i] = ((uint64_t)float_order_key(kap) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+      }
+    }
+    // the wave's k + 1 largest keys, then their rank among all waves' candidates
+    uint64_t head = 0;
+#pragma unroll
+    for (int i = 0; i < kRouteSlots; ++i) head = max_u64(head, key[i]);
+    for (int j = 0; j < kk; ++j) {
+      const uint64_t m = wave_max_u64(head);
+      float v_win = -INFINITY;
+      if (m != 0) {
+        const int e = (int)(0xFFFFFFFFu - (uint32_t)m);
+        const int owner = e & (kWave - 1);
+        const int slot = e >> 8;
+        float mine = 0.f;
+#pragma unroll
+        for (int i = 0; i < kRouteSlots; ++i) mine = (i == slot) ? kv[i] : mine;
+        v_win = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(mine), owner));
+        if (lane == owner) {
+          head = 0;
+#pragma unroll
+          for (int i = 0; i < kRouteSlots; ++i) {
+            if (i == slot) key[i] = 0;
+            head = max_u64(head, key[i]);
+          }
+        }
+      }
+      if (lane == 0) {
+        cand_key[wv * kMaxK + j] = m;
+        cand_v[wv * kMaxK + j] = v_win;
+      }
+    }
+    __syncthreads();
+    {
+      const int c = threadIdx.x;
+      const int j = c & (kMaxK - 1);
+      const uint64_t kc = cand_key[c];
+      if (j < kk && kc != 0) {
+        int rank = 0;
+#pragma unroll
+        for (int w = 0; w < kWavesPerBlock; ++w)
+          for (int q = 0; q < kk; ++q) rank += (cand_key[w * kMaxK + q] > kc);
+        if (rank == a.k) alpha_sh = cand_v[c];
+      }
+    }
+    __syncthreads();
+    const float alpha = alpha_sh;
+#pragma unroll
+    for (int i = 0; i < kRouteSlots; ++i) {
+      const int e = (i * kWavesPerBlock + wv) * kWave + lane;
+      if (e < a.E) {
+        const float r = alpha - sv[i];
+        const float u = (r - lo) * inv_w;
+        int b = (u == u) ? (int)fmaxf(0.f, fminf(floorf(u), (float)(a.bins - 1))) : 0;
+        atomicAdd(a.hist + (int64_t)e * a.bins + b, 1);
+      }
+    }
+    __syncthreads();   // the candidate tables are rewritten by the next token
+  }
+}
+
+// Readout, one workgroup per expert: thread i sums bins [i c, i c + c) (c = ceil(bins /
+// 256)), an exclusive scan of those sums finds the thread whose bins reach ceil(T k / E),
+// and that thread walks them to the bin and interpolates.  The uncentred value goes to
+// new_bias[e]; k_qb_centre removes the mean.
+__global__ __launch_bounds__(kBlock) void k_qb_readout(QbArgs a) {
+  __shared__ float red[2 * kWavesPerBlock];
+  __shared__ int64_t pre[kBlock];
+  __shared__ float found;
+  const int e = blockIdx.x;
+  float lo, hi;
+  qb_range(a.bias, a.E, red, lo, hi);
+  const float w = (hi - lo) / (float)a.bins;
+  const int64_t qc = (a.T * a.k + a.E - 1) / a.E;
+  const int32_t* h = a.chist + (int64_t)e * a.bins;
+  const int per = (a.bins + kBlock - 1) / kBlock;
+  const int t0 = min(a.bins, (int)threadIdx.x * per), t1 = min(a.bins, t0 + per);
+  int64_t mine = 0;
+  for (int t = t0; t < t1; ++t) mine += h[t];
+  pre[threadIdx.x] = mine;
+  if (threadIdx.x == 0) found = hi;   // no bin reaches the target: the top of the range
+  __syncthreads();
+  for (int o = 1; o < kBlock; o <<= 1) {   // inclusive scan
+    const int64_t v = (int)threadIdx.x >= o ? pre[threadIdx.x - o] : 0;
+    __syncthreads();
+    pre[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int64_t cum = pre[threadIdx.x] - mine;
+  if (cum < qc && cum + mine >= qc) {
+    for (int t = t0; t < t1; ++t) {
+      const int64_t c = h[t];
+      if (c > 0 && cum + c >= qc) {
+        found = lo + w * ((float)t + (float)(qc - cum) / (float)c);
+        break;
+      }
+      cum += c;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) a.new_bias[e] = found;
+}
+
+// new_bias -= mean(new_bias) over the experts, one workgroup, a fixed summation order.
+__global__ __launch_bounds__(kBlock) void k_qb_centre(QbArgs a) {
+  __shared__ float red[kWavesPerBlock];
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x >> 6;
+  float part = 0.f;
+  for (int e = threadIdx.x; e < a.E; e += kBlock) part += a.new_bias[e];   // e = tid, tid + 256, ...
+  part = wave_sum(part);
+  if (lane == 0) red[wv] = part;
+  __syncthreads();
+  const float mean = ((red[0] + red[1]) + (red[2] + red[3])) / (float)a.E;
+  for (int e = threadIdx.x; e < a.E; e += kBlock) a.new_bias[e] -= mean;
+}
+
+// ------------------------------------------------------------------------------------
 // Step COMBINE: u[t] = sum_j G[t,j] E[inv[t,j]], j = 0..k-1 in order.
 // ------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kBlock) void k_combine(const float* __restrict__ gw,
@@ -1574,6 +1771,27 @@ hipError_t launch_route(const Shape& s, const float* bias, int64_t T, const Work
                         int32_t* idx, float* gw, hipStream_t st) {
   RouteArgs a = route_args(s, bias, T, ws, idx, gw);
   hipLaunchKernelGGL(k_route, dim3((unsigned)T), dim3(kBlock), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_qb_hist(const Shape& s, const float* bias, int64_t T, int bins, int32_t* hist,
+                          const Work& ws, hipStream_t st) {
+  QbArgs a{};
+  a.z = ws.z; a.zplanes = route_planes(s); a.zplane = T * s.E;
+  a.bias = bias; a.T = T; a.E = s.E; a.k = s.k; a.bins = bins;
+  a.hist = hist;
+  const unsigned grid = (unsigned)(T < 2048 ? T : 2048);
+  hipLaunchKernelGGL(k_qb_hist, dim3(grid), dim3(kBlock), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_qb_readout(const Shape& s, const float* bias, int64_t T, int bins,
+                             const int32_t* hist, float* new_bias, hipStream_t st) {
+  QbArgs a{};
+  a.bias = bias; a.T = T; a.E = s.E; a.k = s.k; a.bins = bins;
+  a.chist = hist; a.new_bias = new_bias;
+  hipLaunchKernelGGL(k_qb_readout, dim3((unsigned)s.E), dim3(kBlock), 0, st, a);
+  hipLaunchKernelGGL(k_qb_centre, dim3(1), dim3(kBlock), 0, st, a);
   return hipGetLastError();
 }
 

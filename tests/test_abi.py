@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 3 == moe.ABI_VERSION
+    assert L.moe_abi_version() == 4 == moe.ABI_VERSION
     assert moe.status_str(0) == "MOE_OK"
     assert moe.status_str(3) == "MOE_ERR_WORKSPACE"
     assert moe.status_str(99) == "MOE_ERR_UNKNOWN"
@@ -125,6 +125,36 @@ def test_forward_rejects_bad_arguments_before_launch(L):
     assert call(T=0) == moe.MOE_OK                               # nothing to do, no launch
     assert call(T=0, x=None, delta=None, W=moe.MoeWeights()) == moe.MOE_OK
     assert f(None, ctypes.byref(W), A, A, 1, A, A, A, A, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_qb_statistics_reject_bad_arguments_before_launch(L):
+    cfg = moe.config_from(synth.TOY)
+    A = 1 << 20
+    W = moe.MoeWeights(A, A)
+    h = L.moe_qb_histogram
+    ok = dict(bias=A, x=A, T=4, bins=1000, hist=A, ws=A, wsb=1 << 40)
+
+    def hist(c=cfg, **kw):
+        a = {**ok, **kw}
+        return h(ctypes.byref(c), ctypes.byref(W), a["bias"], a["x"], a["T"], a["bins"],
+                 a["hist"], a["ws"], a["wsb"], None)
+    assert hist(bins=0) == moe.MOE_ERR_INVALID_ARG
+    assert hist(bins=65537) == moe.MOE_ERR_INVALID_ARG
+    assert hist(hist=None) == moe.MOE_ERR_INVALID_ARG
+    assert hist(hist=A + 2) == moe.MOE_ERR_INVALID_ARG
+    assert hist(T=-1) == moe.MOE_ERR_INVALID_ARG
+    assert hist(x=None) == moe.MOE_ERR_INVALID_ARG
+    assert hist(wsb=16) == moe.MOE_ERR_WORKSPACE
+    assert hist(T=0) == moe.MOE_OK
+    full = moe.config_from(synth.TOY)
+    full.top_k = full.n_experts                 # no (k+1)-th score: no cutoff
+    assert hist(c=full) == moe.MOE_ERR_INVALID_ARG
+    r = L.moe_qb_readout
+    assert r(ctypes.byref(cfg), None, 1000, A, 16, A, None) == moe.MOE_ERR_INVALID_ARG
+    assert r(ctypes.byref(cfg), A, 1000, A, 0, A, None) == moe.MOE_ERR_INVALID_ARG
+    assert r(ctypes.byref(cfg), A, 0, A, 16, A, None) == moe.MOE_ERR_INVALID_ARG
+    assert r(ctypes.byref(cfg), A, 1000, A, 16, A + 2, None) == moe.MOE_ERR_INVALID_ARG
+    assert r(ctypes.byref(full), A, 1000, A, 16, A, None) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_pack_and_dispatch_reject_bad_ranges(L):
