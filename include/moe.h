@@ -300,8 +300,8 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int64_t 
  * estimate).  The training-side step next to S1: it reads the router and the current
  * biases and leaves the forward untouched.
  *
- * moe_qb_histogram: the router of n_tokens tokens x (as in moe_route; the logits are left
- * in workspace slot [12]), then per token the cutoff alpha = the (k+1)-th largest
+ * moe_qb_histogram: the router of n_tokens tokens x (as in moe_route; workspace slot [12]
+ * then holds the scores s = sigmoid(z), [T][E] fp32 in its first plane), then per token the cutoff alpha = the (k+1)-th largest
  * s + b (float32) and, for every expert e, r = alpha - s_e (float32: the bias expert e
  * needs to make the token's top k) counted into hist[e * n_bins + bin], with n_bins
  * uniform bins over [lo, hi] = [min(bias) - 1, max(bias) + 1] (float32) and bin =
@@ -317,7 +317,7 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int64_t 
  * C the count below bin t, c_t the bin's), then the mean over the experts subtracted.
  * The estimate is within one bin width of the exact order statistic.  bias must be the
  * biases the counts were taken with (they fix lo and hi).  Asynchronous. */
-#define MOE_QB_MAX_BINS 65536
+#define MOE_QB_MAX_BINS 16384
 moe_status moe_qb_histogram(const moe_config* cfg, const moe_weights* w, const float* bias,
                             const void* x, int64_t n_tokens, int32_t n_bins, int32_t* hist,
                             void* workspace, size_t workspace_bytes, moe_stream_t stream);

@@ -339,13 +339,15 @@ __global__ __launch_bounds__(kBlock) void k_disp_scatter(const int32_t* idx, int
 // inside it, and removes the mean over the experts.
 // ------------------------------------------------------------------------------------
 struct QbArgs {
-  const float* z;
+  float* z;
   int zplanes;
   int64_t zplane;
   const float* bias;
   int64_t T;
   int E, k, bins;
   int32_t* hist;
+  float* alpha;             // [T] the cutoffs (k_qb_alpha -> k_qb_count)
+  int eb, tc;               // k_qb_count: experts and tokens per workgroup
   const int32_t* chist;     // readout: the counts
   float* new_bias;          // readout: the centred biases
 };
@@ -381,34 +383,36 @@ __device__ __forceinline__ void qb_range(const float* bias, int E, float* red, f
   hi = mx + 1.0f;
 }
 
-__global__ __launch_bounds__(kBlock) void k_qb_hist(QbArgs a) {
+// The logit of expert e for token t: the partial planes added in plane order (as the
+// route adds them), then the float32 sigmoid.
+__device__ __forceinline__ float qb_score(const QbArgs& a, int64_t t, int e) {
+  const float* zr = a.z + t * a.E + e;
+  float zv = 0.f;
+  for (int p = 0; p < a.zplanes; ++p) zv += zr[p * a.zplane];
+  return sigmoidf_(zv);
+}
+
+// alpha[t] = the (k+1)-th largest s + b of token t, one workgroup per token (grid stride);
+// the scores s replace the token's logits in plane 0.
+__global__ __launch_bounds__(kBlock) void k_qb_alpha(QbArgs a) {
   __shared__ uint64_t cand_key[kWavesPerBlock * kMaxK];
   __shared__ float cand_v[kWavesPerBlock * kMaxK];
-  __shared__ float red[2 * kWavesPerBlock];
-  __shared__ float alpha_sh;
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x >> 6;
-  float lo, hi;
-  qb_range(a.bias, a.E, red, lo, hi);
-  const float inv_w = (float)a.bins / (hi - lo);
   const int kk = a.k + 1;   // the cutoff is the (k+1)-th largest
   for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x) {
-    const float* zr = a.z + t * a.E;
     uint64_t key[kRouteSlots];
-    float sv[kRouteSlots], kv[kRouteSlots];
+    float kv[kRouteSlots];
 #pragma unroll
     for (int i = 0; i < kRouteSlots; ++i) {
       const int e = (i * kWavesPerBlock + wv) * kWave + lane;
       key[i] = 0;
-      sv[i] = 0.f;
       kv[i] = 0.f;
       if (e < a.E) {
-        float zv = 0.f;
-        for (int p = 0; p < a.zplanes; ++p) zv += zr[p * a.zplane + e];   // plane order
-        const float sc = sigmoidf_(zv);
+        const float sc = qb_score(a, t, e);
+        a.z[t * a.E + e] = sc;     // plane 0 keeps the score for the counts (read above)
         float kap = sc + a.bias[e];
         if (kap != kap) kap = -INFINITY;
-        sv[i] = sc;
         kv[i] = kap;
         key[i] = ((uint64_t)float_order_key(kap) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
       }
@@ -452,22 +456,45 @@ __global__ __launch_bounds__(kBlock) void k_qb_hist(QbArgs a) {
 #pragma unroll
         for (int w = 0; w < kWavesPerBlock; ++w)
           for (int q = 0; q < kk; ++q) rank += (cand_key[w * kMaxK + q] > kc);
-        if (rank == a.k) alpha_sh = cand_v[c];
-      }
-    }
-    __syncthreads();
-    const float alpha = alpha_sh;
-#pragma unroll
-    for (int i = 0; i < kRouteSlots; ++i) {
-      const int e = (i * kWavesPerBlock + wv) * kWave + lane;
-      if (e < a.E) {
-        const float r = alpha - sv[i];
-        const float u = (r - lo) * inv_w;
-        int b = (u == u) ? (int)fmaxf(0.f, fminf(floorf(u), (float)(a.bins - 1))) : 0;
-        atomicAdd(a.hist + (int64_t)e * a.bins + b, 1);
+        if (rank == a.k) a.alpha[t] = cand_v[c];
       }
     }
     __syncthreads();   // the candidate tables are rewritten by the next token
+  }
+}
+
+// The counts: a workgroup takes eb consecutive experts (their eb x bins counters in LDS)
+// and tc consecutive tokens; thread i walks (token, expert) pairs with the expert fastest
+// so that a wavefront's plane loads are contiguous runs.  r = alpha - s and the bin in
+// float32 (s from plane 0, where k_qb_alpha left it), LDS atomics, then the non-zero
+// counters added to the global histogram.
+__global__ __launch_bounds__(kBlock) void k_qb_count(QbArgs a) {
+  extern __shared__ int32_t cnt[];
+  __shared__ float red[2 * kWavesPerBlock];
+  float lo, hi;
+  qb_range(a.bias, a.E, red, lo, hi);
+  const float inv_w = (float)a.bins / (hi - lo);
+  const int n_eg = (a.E + a.eb - 1) / a.eb;
+  const int eg = blockIdx.x % n_eg;
+  const int64_t tb = blockIdx.x / n_eg;
+  const int e0 = eg * a.eb, ne = min(a.eb, a.E - e0);
+  const int64_t t0 = tb * a.tc;
+  const int64_t nt = min((int64_t)a.tc, a.T - t0);
+  for (int i = threadIdx.x; i < a.eb * a.bins; i += kBlock) cnt[i] = 0;
+  __syncthreads();
+  const int64_t n = nt * ne;
+  for (int64_t i = threadIdx.x; i < n; i += kBlock) {
+    const int64_t t = t0 + i / ne;
+    const int el = (int)(i % ne);
+    const float r = a.alpha[t] - a.z[t * a.E + e0 + el];
+    const float u = (r - lo) * inv_w;
+    const int b = (u == u) ? (int)fmaxf(0.f, fminf(floorf(u), (float)(a.bins - 1))) : 0;
+    atomicAdd(cnt + el * a.bins + b, 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < ne * a.bins; i += kBlock) {
+    const int v = cnt[i];
+    if (v) atomicAdd(a.hist + (int64_t)(e0 + i / a.bins) * a.bins + i % a.bins, v);
   }
 }
 
@@ -1774,14 +1801,23 @@ hipError_t launch_route(const Shape& s, const float* bias, int64_t T, const Work
   return hipGetLastError();
 }
 
+constexpr int kQbLdsBins = 16384;
+
 hipError_t launch_qb_hist(const Shape& s, const float* bias, int64_t T, int bins, int32_t* hist,
                           const Work& ws, hipStream_t st) {
   QbArgs a{};
   a.z = ws.z; a.zplanes = route_planes(s); a.zplane = T * s.E;
   a.bias = bias; a.T = T; a.E = s.E; a.k = s.k; a.bins = bins;
   a.hist = hist;
+  a.alpha = reinterpret_cast<float*>(ws.perm);   // T <= T k floats of the dispatch slot
   const unsigned grid = (unsigned)(T < 2048 ? T : 2048);
-  hipLaunchKernelGGL(k_qb_hist, dim3(grid), dim3(kBlock), 0, st, a);
+  hipLaunchKernelGGL(k_qb_alpha, dim3(grid), dim3(kBlock), 0, st, a);
+  // counters of up to 16 Ki bins per workgroup (64 KiB of LDS), 512 tokens each
+  a.eb = std::max(1, std::min(16, kQbLdsBins / bins));
+  a.tc = 512;
+  const int64_t n_eg = cdiv(s.E, a.eb), n_tb = cdiv(T, a.tc);
+  hipLaunchKernelGGL(k_qb_count, dim3((unsigned)(n_eg * n_tb)), dim3(kBlock),
+                     (size_t)a.eb * bins * 4, st, a);
   return hipGetLastError();
 }
 

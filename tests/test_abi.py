@@ -139,7 +139,7 @@ def test_qb_statistics_reject_bad_arguments_before_launch(L):
         return h(ctypes.byref(c), ctypes.byref(W), a["bias"], a["x"], a["T"], a["bins"],
                  a["hist"], a["ws"], a["wsb"], None)
     assert hist(bins=0) == moe.MOE_ERR_INVALID_ARG
-    assert hist(bins=65537) == moe.MOE_ERR_INVALID_ARG
+    assert hist(bins=16385) == moe.MOE_ERR_INVALID_ARG
     assert hist(hist=None) == moe.MOE_ERR_INVALID_ARG
     assert hist(hist=A + 2) == moe.MOE_ERR_INVALID_ARG
     assert hist(T=-1) == moe.MOE_ERR_INVALID_ARG
