@@ -197,6 +197,31 @@ def cpu_baseline(cfg, dense, seconds, sample_tokens=None):
                       f"{cores}), each touched expert regenerated and dequantised per batch"}
 
 
+def qb_stats(layer, x, cfg, K, dev):
+    """Time the Quantile Balancing statistics of one token batch: moe_qb_histogram (router
+    launch, cutoffs, counts) and moe_qb_readout, K of each back to back between events."""
+    import torch
+    T, bins = x.shape[0], 1000
+    hist = torch.zeros((cfg.E, bins), dtype=torch.int32, device=dev)
+    for _ in range(3):
+        layer.qb_readout(layer.qb_histogram(x, n_bins=bins, hist=hist), T)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for _ in range(K):
+        layer.qb_histogram(x, n_bins=bins, hist=hist)
+    ev[1].record()
+    for _ in range(K):
+        layer.qb_readout(hist, T)
+    ev[2].record()
+    torch.cuda.synchronize()
+    h_us = ev[0].elapsed_time(ev[1]) / K * 1e3
+    r_us = ev[1].elapsed_time(ev[2]) / K * 1e3
+    log(f"[bench] qb statistics: histogram {h_us:.1f} us, readout {r_us:.1f} us per call")
+    return {"tokens": T, "bins": bins, "histogram_us": h_us, "readout_us": r_us,
+            "tokens_per_s": T / ((h_us + r_us) * 1e-6)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +234,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with a 1 GiB device copy (scale for HBM byte counters)")
+    ap.add_argument("--qb-stats", action="store_true",
+                    help="also time the Quantile Balancing statistics step on the workload's "
+                         "token batch (1000 bins): adds a qb_stats object")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -377,6 +405,8 @@ def main():
                   "algorithmic_flops": sum(af.values()), "achieved_TFLOPs": layer_tflops,
                   "steps_us_with_event_per_boundary": steps_us},
     }
+    if args.qb_stats:
+        out["qb_stats"] = qb_stats(layers[0], xs[0], cfg, K, dev)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(cfg, dense0, args.cpu_seconds,
