@@ -262,6 +262,21 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* w,
                                    void* workspace, size_t workspace_bytes,
                                    void* const* step_events, moe_stream_t stream);
 
+/* moe_layer_forward with the residual add after the block fused into its last step: the
+ * K3 block card's block output is Δ_ffn, which the decoder layer adds to its residual
+ * stream (h <- h + Δ).  residual: device fp32 [T][d], read and written, residual += Δ
+ * (one fp32 add per element).  x_next: device bf16 [T][d] or null: the updated residual
+ * rounded to bf16 (nearest, ties to even), the next layer's input; it may be x itself
+ * (x is read only before the last step).  delta: fp32 [T][d] or null (Δ then not
+ * stored).  Layer after layer on one stream this chains a decoder's MoE blocks with no
+ * extra pass over the activations.  Alignment 16 bytes for residual and x_next;
+ * MOE_ERR_INVALID_ARG for a null residual (T > 0); otherwise as moe_layer_forward. */
+moe_status moe_layer_forward_residual(const moe_config* cfg, const moe_weights* w,
+                                      const float* bias, const void* x, int64_t n_tokens,
+                                      float* residual, void* x_next, float* delta,
+                                      int32_t* topk_idx, float* topk_w, void* workspace,
+                                      size_t workspace_bytes, moe_stream_t stream);
+
 /* Steps step_begin..step_end-1 of moe_layer_forward alone (0 <= begin <= end <= 8).
  * Each step reads what the earlier steps left in `workspace`, topk_idx and topk_w, so a
  * range that starts after step 0 is only meaningful on the buffers of an earlier call

@@ -47,7 +47,7 @@ __all__ = [
     "e4m3_decode", "round_e4m3", "E4M3_MAX", "quantize_mx8", "round_bf16", "PRECISIONS",
     "dequant_fp8_block128",
     "sigmoid", "select_and_weight", "selection_kappa", "router_scores", "situ", "swiglu", "glu", "rmsnorm",
-    "OracleLayer", "forward", "routed_sum_dense_mask", "Result", "dispatch",
+    "OracleLayer", "forward", "routed_sum_dense_mask", "Result", "dispatch", "residual_add",
 ]
 
 # ----------------------------------------------------------------------------------------
@@ -443,3 +443,13 @@ def dispatch(idx: np.ndarray, n_experts: int):
     inv = np.empty_like(perm)
     inv[perm] = np.arange(perm.size, dtype=np.int32)
     return counts, offsets, perm, inv
+
+
+def residual_add(residual: np.ndarray, delta: np.ndarray):
+    """The block's output joins the residual stream (the block card: the FFN returns
+    Delta_ffn, the decoder layer adds it to its hidden state, h <- h + Delta): the new
+    residual (float64) and its bf16 rounding, the next layer's input (uint16 patterns)."""
+    new = np.asarray(residual, dtype=np.float64) + np.asarray(delta, dtype=np.float64)
+    xb = round_bf16(new).astype(np.float32).view(np.uint32) >> 16
+    return new, xb.astype(np.uint16)
+

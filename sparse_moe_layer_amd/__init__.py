@@ -25,7 +25,7 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_packed_dense_size", "moe_pa
            "moe_packed_experts_size", "moe_pack_experts", "moe_workspace_size",
            "moe_workspace_layout", "moe_layer_forward",
            "moe_layer_forward_timed", "moe_layer_forward_steps", "moe_route", "moe_dispatch",
-           "moe_qb_histogram", "moe_qb_readout")
+           "moe_qb_histogram", "moe_qb_readout", "moe_layer_forward_residual")
 STEPS = ("router", "in", "route", "dispatch", "expert_gu", "expert_down", "combine", "out")
 ABI_VERSION = 4
 
@@ -97,6 +97,8 @@ def lib():
     i32 = ctypes.c_int32
     L.moe_qb_histogram.argtypes = [P(MoeConfig), P(MoeWeights), vp, vp, i64, i32, vp, vp, sz, vp]
     L.moe_qb_readout.argtypes = [P(MoeConfig), vp, i32, vp, i64, vp, vp]
+    L.moe_layer_forward_residual.argtypes = [P(MoeConfig), P(MoeWeights), vp, vp, i64, vp, vp, vp,
+                                             vp, vp, vp, sz, vp]
     for f in EXPORTS[2:]:
         getattr(L, f).restype = ctypes.c_int
     if L.moe_abi_version() != ABI_VERSION:
@@ -271,6 +273,25 @@ class Layer:
                                        w.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)),
                "moe_layer_forward")
         return delta, idx, w
+
+    def forward_residual(self, x, residual, x_next=None, delta=None, idx=None, w=None,
+                         workspace=None, stream=None):
+        """forward() with residual += Delta fused into the last step (residual fp32 [T, d]
+        on the device, updated in place) and, when x_next is given (bf16 patterns [T, d],
+        may be x itself), the updated residual rounded to bf16.  Returns (idx, w)."""
+        import torch
+        T = x.shape[0]
+        c = self.cfg
+        idx = torch.empty((T, c.top_k), dtype=torch.int32, device=self.device) if idx is None else idx
+        w = torch.empty((T, c.top_k), dtype=torch.float32, device=self.device) if w is None else w
+        ws = self.workspace(T) if workspace is None else workspace
+        W = self.weights_struct()
+        _check(lib().moe_layer_forward_residual(
+            ctypes.byref(c), ctypes.byref(W), self.bias.data_ptr(), x.data_ptr(), T,
+            residual.data_ptr(), None if x_next is None else x_next.data_ptr(),
+            None if delta is None else delta.data_ptr(), idx.data_ptr(), w.data_ptr(),
+            ws.data_ptr(), ws.numel(), _stream(stream)), "moe_layer_forward_residual")
+        return idx, w
 
     def forward_timed(self, x, events, delta, idx, w, workspace=None, stream=None):
         """forward() that also records events[s] (hipEvent_t handles, len(STEPS) + 1) on the

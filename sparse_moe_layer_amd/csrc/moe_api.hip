@@ -296,7 +296,8 @@ moe_status check_call(const Shape& s, const moe_weights* w, const float* bias, c
 moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const float* bias,
                         const void* x, int64_t n_tokens, float* delta, int32_t* topk_idx,
                         float* topk_w, void* workspace, size_t workspace_bytes,
-                        void* const* events, int step_begin, int step_end, moe_stream_t stream) {
+                        void* const* events, int step_begin, int step_end, moe_stream_t stream,
+                        float* residual = nullptr, uint16_t* x_next = nullptr) {
   Shape s;
   moe_status st = make_shape(cfg, &s);
   if (st != MOE_OK) return st;
@@ -305,8 +306,10 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const float
   if (n_tokens == 0) return MOE_OK;  // nothing to read or write: buffers may be empty (null)
   size_t off[MOE_WS_NUM_SLOTS];
   if ((st = check_call(s, w, bias, x, n_tokens, workspace, workspace_bytes, off)) != MOE_OK) return st;
-  if (!delta || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  if ((!delta && !residual) || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
   if (!aligned(delta, 16) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(residual, 16) || !aligned(x_next, 16) || (x_next && !residual)) return MOE_ERR_INVALID_ARG;
+  const moe::OutSink sink{delta, residual, x_next};
   const moe::Work ws = make_work(s, n_tokens, workspace, off);
   const uint8_t* dense = static_cast<const uint8_t*>(w->dense);
   const uint8_t* experts = static_cast<const uint8_t*>(w->experts);
@@ -332,7 +335,7 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const float
           e = moe::launch_combine(s, dense, topk_w, n_tokens, ws, hs);
           if (e == hipSuccess) e = moe::launch_pf_norm(s, dense, n_tokens, ws, ws.pf, hs);
           break;
-        case MOE_STEP_OUT: e = moe::launch_pf_out(s, dense, n_tokens, ws.pf, delta, hs); break;
+        case MOE_STEP_OUT: e = moe::launch_pf_out(s, dense, n_tokens, ws.pf, sink, hs); break;
       }
       if (e != hipSuccess) return MOE_ERR_HIP;
       continue;
@@ -353,7 +356,7 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const float
       case MOE_STEP_EXPERT_GU: e = moe::launch_expert(s, experts, true, n_tokens, ws, hs); break;
       case MOE_STEP_EXPERT_DOWN: e = moe::launch_expert(s, experts, false, n_tokens, ws, hs); break;
       case MOE_STEP_COMBINE: e = moe::launch_combine(s, dense, topk_w, n_tokens, ws, hs); break;
-      case MOE_STEP_OUT: e = moe::launch_out(s, dense, n_tokens, ws, delta, hs); break;
+      case MOE_STEP_OUT: e = moe::launch_out(s, dense, n_tokens, ws, sink, hs); break;
     }
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
@@ -372,6 +375,18 @@ MOE_EXPORT moe_status moe_layer_forward(const moe_config* cfg, const moe_weights
                                         moe_stream_t stream) {
   return forward_impl(cfg, w, bias, x, n_tokens, delta, topk_idx, topk_w, workspace,
                       workspace_bytes, nullptr, 0, MOE_NUM_STEPS, stream);
+}
+
+MOE_EXPORT moe_status moe_layer_forward_residual(const moe_config* cfg, const moe_weights* w,
+                                                 const float* bias, const void* x,
+                                                 int64_t n_tokens, float* residual, void* x_next,
+                                                 float* delta, int32_t* topk_idx, float* topk_w,
+                                                 void* workspace, size_t workspace_bytes,
+                                                 moe_stream_t stream) {
+  if (n_tokens > 0 && !residual) return MOE_ERR_INVALID_ARG;
+  return forward_impl(cfg, w, bias, x, n_tokens, delta, topk_idx, topk_w, workspace,
+                      workspace_bytes, nullptr, 0, MOE_NUM_STEPS, stream, residual,
+                      static_cast<uint16_t*>(x_next));
 }
 
 MOE_EXPORT moe_status moe_layer_forward_steps(const moe_config* cfg, const moe_weights* w,

@@ -34,6 +34,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Delta of element i to where the OUT step puts it (OutSink, moe_internal.hpp).
+__device__ __forceinline__ void store_out(const OutSink& o, int64_t i, float v) {
+  if (o.delta) o.delta[i] = v;
+  if (o.res) {
+    const float r = o.res[i] + v;
+    o.res[i] = r;
+    if (o.xn) o.xn[i] = (uint16_t)(pack_bf16x2(r, 0.f) & 0xFFFFu);
+  }
+}
+
 // D += A B for one 16x16x32 bf16 block (fp32 accumulation); A rows and B columns are
 // held as 8 consecutive K values per lane (lane l: row / column l % 16, K 8 (l / 16)..).
 __device__ __forceinline__ f32x4_t mfma_bf16(uint4 a, uint4 b, f32x4_t c) {

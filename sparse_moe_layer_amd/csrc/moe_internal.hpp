@@ -136,6 +136,15 @@ inline int64_t max_large_units(const Shape& s, int64_t T) {
   return b < max_units(s, T) ? b : max_units(s, T);
 }
 
+// Where the OUT step puts Delta: delta[i] (when not null) and, with a residual stream,
+// res[i] += Delta and xn[i] = the new res[i] rounded to bf16 (the next layer's input;
+// when not null).
+struct OutSink {
+  float* delta;
+  float* res;
+  uint16_t* xn;
+};
+
 // router_only: the router rows alone (otherwise W_down_latent rides in the same launch)
 hipError_t launch_router(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,
                          bool router_only, const Work& ws, hipStream_t st);
@@ -160,7 +169,7 @@ hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_
 hipError_t launch_combine(const Shape& s, const uint8_t* dense, const float* gw, int64_t T,
                           const Work& ws, hipStream_t st);
 hipError_t launch_out(const Shape& s, const uint8_t* dense, int64_t T, const Work& ws,
-                      float* delta, hipStream_t st);
+                      const OutSink& out, hipStream_t st);
 
 // The mx8 launches (moe_prefill.hip).
 hipError_t launch_pf_in(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,
@@ -172,7 +181,7 @@ hipError_t launch_pf_expert(const Shape& s, const uint8_t* experts, bool gu, int
 hipError_t launch_pf_norm(const Shape& s, const uint8_t* dense, int64_t T, const Work& ws,
                           const PfWork& pw, hipStream_t st);
 hipError_t launch_pf_out(const Shape& s, const uint8_t* dense, int64_t T, const PfWork& pw,
-                         float* delta, hipStream_t st);
+                         const OutSink& out, hipStream_t st);
 
 // Packing.  Dense: canonical bf16 [rows][K] into the tiles of the IN or OUT matrix.
 struct DenseSrc {

@@ -1025,7 +1025,7 @@ struct OutArgs {
   int n0;               // columns of the u_hat segment (0 without a latent)
   float eps;
   int64_t T;
-  float* delta;
+  OutSink sink;
   const float* add_u;   // without a latent: Delta = u + the product
 };
 
@@ -1103,8 +1103,8 @@ __global__ __launch_bounds__(kBlock) void k_out(OutArgs a) {
     const float y0 = acc[0] + acc[1], y1 = acc[2] + acc[3];
     if (r < a.d) {
       const int64_t i0 = (t0 + 2 * g) * a.d + r, i1 = i0 + a.d;
-      if (2 * g < nt) a.delta[i0] = a.add_u ? a.add_u[i0] + y0 : y0;
-      if (2 * g + 1 < nt) a.delta[i1] = a.add_u ? a.add_u[i1] + y1 : y1;
+      if (2 * g < nt) store_out(a.sink, i0, a.add_u ? a.add_u[i0] + y0 : y0);
+      if (2 * g + 1 < nt) store_out(a.sink, i1, a.add_u ? a.add_u[i1] + y1 : y1);
     }
   }
 }
@@ -1406,7 +1406,7 @@ struct OutTTArgs {
   const uint16_t* hs_hl;   // [T][2][ms]
   int d, l, ms, n0;        // n0: columns of the u_hat segment (0 without a latent)
   int64_t T;
-  float* delta;
+  OutSink sink;
   const float* add_u;      // without a latent: Delta = u + the product
 };
 
@@ -1443,8 +1443,8 @@ __global__ __launch_bounds__(kBlock) void k_out_tt(OutTTArgs a) {
     const int i0 = 8 * b + 2 * g;
     const int64_t o0 = (t0 + i0) * a.d + r, o1 = o0 + a.d;
     const float y0 = tot[b][0] + tot[b][1], y1 = tot[b][2] + tot[b][3];
-    if (i0 < nt) a.delta[o0] = a.add_u ? a.add_u[o0] + y0 : y0;
-    if (i0 + 1 < nt) a.delta[o1] = a.add_u ? a.add_u[o1] + y1 : y1;
+    if (i0 < nt) store_out(a.sink, o0, a.add_u ? a.add_u[o0] + y0 : y0);
+    if (i0 + 1 < nt) store_out(a.sink, o1, a.add_u ? a.add_u[o1] + y1 : y1);
   }
 }
 
@@ -1935,7 +1935,7 @@ hipError_t launch_combine(const Shape& s, const uint8_t* dense, const float* gw,
 }
 
 hipError_t launch_out(const Shape& s, const uint8_t* dense, int64_t T, const Work& ws,
-                      float* delta, hipStream_t st) {
+                      const OutSink& out, hipStream_t st) {
   if (token_tiled(s, T)) {
     // [u_hat ; h_s] hi/lo rows over tiles of 32 tokens
     OutTTArgs a;
@@ -1947,7 +1947,7 @@ hipError_t launch_out(const Shape& s, const uint8_t* dense, int64_t T, const Wor
     a.n_tiles = cdiv(T, kHiloTTRows);
     a.uh_hl = ws.uh_hl; a.hs_hl = ws.hs_hl;
     a.d = s.d; a.l = s.l; a.ms = s.ms; a.n0 = s.latent ? s.l : 0;
-    a.T = T; a.delta = delta;
+    a.T = T; a.sink = out;
     a.add_u = s.latent ? nullptr : ws.u;
     const size_t lds = (size_t)2 * kHiloTTBlocks * 16 * 16 * 16;
     hipLaunchKernelGGL(k_out_tt, dim3((unsigned)xcd_grid(a.n_grp, a.n_tiles)), dim3(kBlock), lds,
@@ -1966,7 +1966,7 @@ hipError_t launch_out(const Shape& s, const uint8_t* dense, int64_t T, const Wor
   a.gamma = reinterpret_cast<const uint16_t*>(dense + s.gamma_off);
   a.d = s.d; a.l = s.l; a.ms = s.ms; a.norm = s.use_norm; a.eps = s.eps;
   a.n0 = s.latent ? s.l : 0;
-  a.T = T; a.delta = delta;
+  a.T = T; a.sink = out;
   a.add_u = s.latent ? nullptr : ws.u;
   const size_t lds = (size_t)2 * (T < a.ntb ? T : a.ntb) * s.ks_out * kStepK * 2;
   hipLaunchKernelGGL(k_out, dim3((unsigned)xcd_grid(a.wg_per_blk, a.n_blk)), dim3(kBlock), lds, st,

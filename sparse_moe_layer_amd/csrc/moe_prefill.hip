@@ -319,7 +319,7 @@ struct PfDenseArgs {
   int ms, act;
   float bg, bl, rbg, rbl;
   // OUT epilogue
-  float* delta;
+  OutSink sink;
   int d;
 };
 
@@ -363,7 +363,7 @@ __global__ __launch_bounds__(kBlock) void k_pf_dense(PfDenseArgs a) {
         if (tr[t] >= a.tr_count) continue;
         if (!IN) {
           const int r = 16 * tr[t] + c;
-          if (ti < nt && r < a.d) a.delta[tok * a.d + r] = y;
+          if (ti < nt && r < a.d) store_out(a.sink, tok * a.d + r, y);
         } else if (tr[t] < a.tr_r) {
           const int e = 16 * tr[t] + c;
           if (ti < nt && e < a.E) a.z[tok * a.E + e] = y;
@@ -686,7 +686,7 @@ hipError_t launch_pf_norm(const Shape& s, const uint8_t* dense, int64_t T, const
 }
 
 hipError_t launch_pf_out(const Shape& s, const uint8_t* dense, int64_t T, const PfWork& pw,
-                         float* delta, hipStream_t st) {
+                         const OutSink& out, hipStream_t st) {
   PfDenseArgs a{};
   a.w = dense + s.in_bytes;
   a.ks = s.ks_out;
@@ -696,7 +696,7 @@ hipError_t launch_pf_out(const Shape& s, const uint8_t* dense, int64_t T, const 
   a.a0 = pw.uh; a.lda0 = s.l; a.n0 = s.l;
   a.a1 = s.ms > 0 ? pw.hs : pw.uh; a.lda1 = s.ms; a.c1 = s.ks_l * kStepK; a.n1 = s.ms;
   a.T = T;
-  a.delta = delta; a.d = s.d;
+  a.sink = out; a.d = s.d;
   hipLaunchKernelGGL(k_pf_dense<false>, dim3((unsigned)xcd_grid(a.n_grp, a.n_tiles)), dim3(kBlock),
                      kPfDenseLds, st, a);
   return hipGetLastError();

@@ -446,3 +446,19 @@ def test_selection_kappa_ranks_and_gives_the_margin():
     assert np.allclose(kap[:, :6], want, rtol=0, atol=1e-7)
     full = O.selection_kappa(s[:, :6], b[:6], 6)    # E == k
     assert full.shape == (40, 7) and np.all(np.isneginf(full[:, 6]))
+
+
+def test_residual_add_rounds_the_new_stream_to_bf16():
+    """residual_add: the sum, and the next input as the bf16 patterns of that sum (against
+    torch's bfloat16 conversion; a zero Delta returns a bf16 residual unchanged)."""
+    import torch
+    rng = np.random.default_rng(21)
+    res = (rng.standard_normal((6, 40)) * 3).astype(np.float32).astype(np.float64)
+    d = rng.standard_normal((6, 40)) * 1e-2
+    new, xb = O.residual_add(res, d)
+    assert np.array_equal(new, res + d)
+    lib = torch.from_numpy(new.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(xb, lib)
+    x = O.bf16_to_f64(xb)
+    _, again = O.residual_add(x, np.zeros_like(x))
+    assert np.array_equal(again, xb)
