@@ -90,22 +90,34 @@ def weight_bytes(cfg, D):
     return (E * d + 2 * l * d + l + 3 * ms * d) * 2 + E * 4 + D * sum(expert_weight_bytes(cfg))
 
 
-# rocprofv3 kernel symbols of each step's launches (their template arguments vary with
-# shape): a kernel belongs to the step when its name holds all the words of one entry
-STEP_KERNELS = {"router": [("k_router",), ("k_token_rows",)], "in": [("k_in",)],
-                "route": [("k_route",)], "dispatch": [("k_disp",)],
-                "expert_gu": [("k_exp", "true")], "expert_down": [("k_exp", "false")],
-                "combine": [("k_combine",), ("k_norm",)], "out": [("k_out",)]}
-STEP_KERNELS_MX8 = {"router": [("k_pf_dense", "true")], "in": [("k_pf_quant",)],
-                    "route": [("k_route",)], "dispatch": [("k_disp",)],
+# The kernels of each step's launches: (kernel name, a word its template arguments must
+# hold, or None).  Kernels of no step (the one-time packing, the QB statistics) map to None.
+STEP_KERNELS = {"router": [("k_router", None), ("k_router_tt", None), ("k_token_rows", None)],
+                "in": [("k_in", None), ("k_in_tt", None)],
+                "route": [("k_route", None)],
+                "dispatch": [("k_disp_count", None), ("k_disp_scan", None), ("k_disp_scatter", None)],
+                "expert_gu": [("k_exp", "true"), ("k_exp_tt", "true")],
+                "expert_down": [("k_exp", "false"), ("k_exp_tt", "false")],
+                "combine": [("k_combine", None), ("k_norm", None)],
+                "out": [("k_out", None), ("k_out_tt", None)]}
+STEP_KERNELS_MX8 = {"router": [("k_pf_dense", "true")], "in": [("k_pf_quant", None)],
+                    "route": [("k_route", None)],
+                    "dispatch": [("k_disp_count", None), ("k_disp_scan", None), ("k_disp_scatter", None)],
                     "expert_gu": [("k_pf_exp", "true")], "expert_down": [("k_pf_exp", "false")],
-                    "combine": [("k_combine",), ("k_pf_norm",)], "out": [("k_pf_dense", "false")]}
+                    "combine": [("k_combine", None), ("k_pf_norm", None)],
+                    "out": [("k_pf_dense", "false")]}
 
 
 def step_of_kernel(name, kernels):
-    """The step whose launches include the kernel `name`, or None."""
+    """The step whose launches include the kernel `name` (a rocprofv3 symbol or its short
+    form `k_name<args>`), or None."""
+    import re
+    m = re.search(r"(k_\w+)(<[^>]*>)?", name)
+    if not m:
+        return None
+    base, targs = m.group(1), m.group(2) or ""
     for step, alts in kernels.items():
-        if any(all(w in name for w in words) for words in alts):
+        if any(base == b and (w is None or w in targs) for b, w in alts):
             return step
     return None
 
