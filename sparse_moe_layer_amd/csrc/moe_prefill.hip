@@ -15,7 +15,8 @@
 //                OUT matrix (bf16 MFMA)
 //
 // Tiling: a workgroup multiplies a tile of 16 NB activation rows (NB <= 10) with 4 x NT
-// tile rows of weights (NT per wavefront).  K advances one K-step (128 columns) at a
+// tile rows of weights (NT per wavefront: kPfNT for the experts, kPfDenseNT for the dense
+// products).  K advances one K-step (128 columns) at a
 // time: the activation rows of the next K-steps travel global -> registers -> LDS (two
 // LDS buffers, one barrier per K-step) while every wavefront streams its own weight
 // K-steps into registers, two K-steps ahead.  Each activation fragment read from LDS
@@ -38,7 +39,8 @@ static_assert(16 * kPfExpNB == kPfUnitPositions, "dispatch units fill one expert
 // the most activation rows of a tile (the row tables hold this many)
 constexpr int kPfRows = 16 * (kPfDenseNB > kPfExpNB ? kPfDenseNB : kPfExpNB);
 static_assert(kPfRows <= kBlock, "one thread per activation row sets the row tables");
-constexpr int kPfNT = 4;         // weight tile rows per wavefront
+constexpr int kPfNT = 4;         // weight tile rows per wavefront: routed experts
+constexpr int kPfDenseNT = 2;    // dense products (2 workgroups per CU fit 256 registers)
 constexpr int kPfWaves = kBlock / kWave;
 constexpr int kPfDenseDepth = 2;   // K-steps in flight: bf16 weights (4 KiB per tile row)
 constexpr int kPfExpDepth = 2;     // MXFP4 weights (1 KiB per tile row)
@@ -324,7 +326,7 @@ struct PfDenseArgs {
 };
 
 template <bool IN>
-__global__ __launch_bounds__(kBlock) void k_pf_dense(PfDenseArgs a) {
+__global__ __launch_bounds__(kBlock, 2) void k_pf_dense(PfDenseArgs a) {
   extern __shared__ uint4 sm[];
   __shared__ PfRows rows;
   const int lane = threadIdx.x & (kWave - 1);
@@ -339,20 +341,20 @@ __global__ __launch_bounds__(kBlock) void k_pf_dense(PfDenseArgs a) {
     rows.o1[threadIdx.x] = (uint32_t)((t0 + threadIdx.x) * a.lda1 / 8);
   }
   __syncthreads();
-  const uint8_t* trow[kPfNT];
-  int tr[kPfNT];
+  const uint8_t* trow[kPfDenseNT];
+  int tr[kPfDenseNT];
 #pragma unroll
-  for (int t = 0; t < kPfNT; ++t) {
-    tr[t] = (grp * kPfWaves + wv) * kPfNT + t;
+  for (int t = 0; t < kPfDenseNT; ++t) {
+    tr[t] = (grp * kPfWaves + wv) * kPfDenseNT + t;
     trow[t] = a.w + (size_t)(tr[t] < a.tr_count ? tr[t] : 0) * a.ks * kBf16StepBytes;
   }
-  f32x4_t acc[kPfNT][kPfDenseNB];
-  pf_run<0, kPfDenseNB, kPfNT, kPfDenseDepth>(rows, PfSrc{reinterpret_cast<const uint4*>(a.a0), reinterpret_cast<const uint4*>(a.a1),
+  f32x4_t acc[kPfDenseNT][kPfDenseNB];
+  pf_run<0, kPfDenseNB, kPfDenseNT, kPfDenseDepth>(rows, PfSrc{reinterpret_cast<const uint4*>(a.a0), reinterpret_cast<const uint4*>(a.a1),
                                   nullptr, nt, a.n0, a.c1, a.n1},
                       trow, a.ks, sm, nullptr, acc);
   const bool lo = c < 8;
 #pragma unroll
-  for (int t = 0; t < kPfNT; ++t) {
+  for (int t = 0; t < kPfDenseNT; ++t) {
 #pragma unroll
     for (int b = 0; b < kPfDenseNB; ++b)
 #pragma unroll
@@ -378,7 +380,7 @@ __global__ __launch_bounds__(kBlock) void k_pf_dense(PfDenseArgs a) {
   // tile row t (its gate, the up value of lane c + 8), lane c >= 8 that of tile row t + 1
   const int sh0 = a.tr_r + a.tr_dn;
 #pragma unroll
-  for (int t = 0; t < kPfNT; t += 2)
+  for (int t = 0; t < kPfDenseNT; t += 2)
 #pragma unroll
     for (int b = 0; b < kPfDenseNB; ++b)
 #pragma unroll
@@ -624,7 +626,7 @@ hipError_t launch_pf_in(const Shape& s, const uint8_t* dense, const uint16_t* x,
   a.w = dense;
   a.ks = s.ks_in;
   a.tr_count = s.tr_in;
-  a.n_grp = cdiv(s.tr_in, kPfWaves * kPfNT);
+  a.n_grp = cdiv(s.tr_in, kPfWaves * kPfDenseNT);
   a.n_tiles = cdiv(T, 16 * kPfDenseNB);
   a.a0 = x; a.lda0 = s.d; a.n0 = s.d;
   a.a1 = x; a.lda1 = 0; a.c1 = 0; a.n1 = 0;
@@ -691,7 +693,7 @@ hipError_t launch_pf_out(const Shape& s, const uint8_t* dense, int64_t T, const 
   a.w = dense + s.in_bytes;
   a.ks = s.ks_out;
   a.tr_count = s.tr_out;
-  a.n_grp = cdiv(s.tr_out, kPfWaves * kPfNT);
+  a.n_grp = cdiv(s.tr_out, kPfWaves * kPfDenseNT);
   a.n_tiles = cdiv(T, 16 * kPfDenseNB);
   a.a0 = pw.uh; a.lda0 = s.l; a.n0 = s.l;
   a.a1 = s.ms > 0 ? pw.hs : pw.uh; a.lda1 = s.ms; a.c1 = s.ks_l * kStepK; a.n1 = s.ms;
