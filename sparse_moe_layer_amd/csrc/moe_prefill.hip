@@ -540,9 +540,10 @@ __device__ __forceinline__ void pf_exp_unit(const PfExpArgs& a, const PfRows& ro
   }
 }
 
-// Work order of the expert launches: chunks of 4 units through every tile-row group
-// (chunk_item).
-constexpr int kPfChunk = 4;
+// Work order of the expert launches: chunks of 8 units through every tile-row group
+// (chunk_item; measured against 2, 4, 16 and 32: the units of one expert share its weight
+// slices in L2 best at 8 when an expert has many units).
+constexpr int kPfChunk = 8;
 
 // Two workgroups per compute unit (a register budget of 256 per lane): while one waits at
 // its barrier or for its loads the other issues MFMAs.
@@ -616,7 +617,10 @@ __global__ __launch_bounds__(kBlock) void k_pf_norm(const float* __restrict__ u,
 }
 
 constexpr size_t kPfDenseLds = (size_t)2 * 16 * kPfDenseNB * 16 * 16;   // two K-steps of the bf16 rows
-constexpr size_t kPfExpLds = (size_t)2 * 16 * kPfExpNB * 8 * 16;       // two K-steps of the FP8 rows
+// two K-steps of the FP8 rows, and room for the gate/up epilogue's wavefront-private tiles
+constexpr size_t kPfExpEpiLds = (size_t)kPfWaves * 16 * 36 * 4;
+constexpr size_t kPfExpLds = (size_t)2 * 16 * kPfExpNB * 8 * 16 > kPfExpEpiLds
+                                 ? (size_t)2 * 16 * kPfExpNB * 8 * 16 : kPfExpEpiLds;
 
 }  // namespace
 
