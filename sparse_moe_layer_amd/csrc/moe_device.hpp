@@ -198,18 +198,6 @@ struct WeightStep {
                       : ld_stream(p + s * 1024 + lane * 16);
     }
   }
-  // An ordering point: the registers count as rewritten here, so nothing derived from
-  // them (the operand conversions) is computed earlier, which would make the wave wait
-  // for this K-step's loads before the step that consumes them.
-  __device__ __forceinline__ void pin() {
-#pragma unroll
-    for (int s = 0; s < NW; ++s) {
-      uint32_t a = w[s].x, b = w[s].y, c = w[s].z, d = w[s].w;
-      asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
-      w[s] = make_uint4(a, b, c, d);
-    }
-    if (WF) asm volatile("" : "+v"(sc));
-  }
   // the lane's E8M0 scale as an fp32 power of two (MXFP4), or its fp32 block scale (FP8)
   __device__ __forceinline__ float scale(int g) const {
     return kFp8 ? __uint_as_float(sc) : e8m0_as_f32((sc >> (8 * g)) & 0xFFu);

@@ -1243,7 +1243,6 @@ __device__ __forceinline__ void tt_run(const TTRows& rows, const TTSrc& src, con
       st.load(i % PA, src, min(q + PA, ks - 1));
       const uint4* buf = lds + (q & 1) * rstride;
       constexpr bool kFp8 = WeightStep<WF>::kFp8;
-      ts.w[i].pin();
       const float scl = WF ? ts.w[i].scale(g) : 0.f;
       f32x4_t part[NB];
 #pragma unroll
@@ -1258,6 +1257,11 @@ __device__ __forceinline__ void tt_run(const TTRows& rows, const TTSrc& src, con
 #pragma unroll
       for (int b = 0; b < NB; ++b)   // FP8: the K-step's partial sums times its block scale
         cur[b] = kFp8 ? WeightStep<WF>::scale_add(part[b], scl, cur[b]) : part[b];
+      // the K-step's products are issued before its slot is reloaded, so that the slot's old
+      // and new values never overlap and keep one register set across the loop's back edge
+      // (where the compiler would otherwise copy the ring, waiting for every load in flight)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) asm volatile("" : "+v"(cur[b]) :: "memory");
       ts.w[i].load(trow, min(q + P, ks - 1), lane);
       if (PARTS && q < ks && (++in_part == qper || q + 1 == ks)) {
 #pragma unroll
@@ -1492,7 +1496,7 @@ __device__ __forceinline__ void exp_tt_unit_single(const ExpArgs& a, const TTRow
 // hi/lo bf16 rows written by their producer (x^c by the IN launch, h by the gate/up
 // launches).
 template <int WF, bool GU>
-__global__ __launch_bounds__(kBlock, 4) void k_exp_tt(ExpArgs a) {
+__global__ __launch_bounds__(kBlock, WF == 1 ? 4 : 3) void k_exp_tt(ExpArgs a) {
   extern __shared__ uint4 sm[];
   __shared__ TTRows rows;
   const int lane = threadIdx.x & (kWave - 1);

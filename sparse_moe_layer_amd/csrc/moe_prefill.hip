@@ -287,6 +287,13 @@ __device__ __forceinline__ void pf_run(const PfRows& rows, const PfSrc& src,
           }
         }
       }
+      // the K-step's products are issued before its slot is reloaded, so that the slot's old
+      // and new values never overlap and keep one register set across the loop's back edge
+      // (where the compiler would otherwise copy the rings, waiting for every load in flight)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) asm volatile("" : "+v"(acc[t][b]) :: "memory");
 #pragma unroll
       for (int t = 0; t < NT; ++t) w[sl][t].template load<true>(trow[t], min(q + P, ks - 1), lane);
       asm volatile("" ::: "memory");
