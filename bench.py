@@ -181,6 +181,64 @@ class HipEvents:
             self.h.hipEventDestroy(e)
 
 
+def percentiles_us(durations_ms):
+    import numpy as np
+    d = np.asarray(durations_ms, dtype=np.float64) * 1e3
+    return {"median_us": float(np.median(d)), "p10_us": float(np.percentile(d, 10)),
+            "p90_us": float(np.percentile(d, 90))}
+
+
+def graph_replay(layers, xs, bufs, rotate, batches, K, warmup):
+    """The forward captured as HIP graphs, one per (dense copy, token batch) pair of the
+    rotation (at most 16), replayed in turn on torch's current stream.
+
+    Returns the mean over K back-to-back replays, the median / p10 / p90 of single replays
+    (one event between consecutive replays, so each figure carries one event record), the
+    same percentiles for eager forwards, and whether a replay gives the eager bits."""
+    import torch
+    G = max(rotate, min(batches, 16))
+    pairs = [(j % rotate, j % batches) for j in range(G)]
+    graphs = []
+    for li, xi in pairs:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layers[li].forward(xs[xi], *bufs)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(max(G, warmup)):
+        graphs[i % G].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(K):
+        graphs[i % G].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    mean_ms = e0.elapsed_time(e1) / K
+
+    def per_step(run):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        evs[0].record()
+        for i in range(K):
+            run(i)
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        return [evs[i].elapsed_time(evs[i + 1]) for i in range(K)]
+    g_ms = per_step(lambda i: graphs[i % G].replay())
+    e_ms = per_step(lambda i: layers[pairs[i % G][0]].forward(xs[pairs[i % G][1]], *bufs))
+    # bits: a replay against an eager forward of the same pair, on buffers of its own
+    graphs[1 % G].replay()
+    got = [t.clone() for t in bufs[:3]]
+    li, xi = pairs[1 % G]
+    ref = layers[li].forward(xs[xi])
+    torch.cuda.synchronize()
+    same = all(torch.equal(a, b) for a, b in zip(got, ref))
+    del graphs
+    return {"graphs": G, "us_per_step": mean_ms * 1e3, "tokens_per_s": None,
+            **percentiles_us(g_ms), "eager": percentiles_us(e_ms),
+            "bits_equal_eager": same}
+
+
 def cpu_baseline(cfg, dense, seconds, sample_tokens=None):
     """The float64 CPU oracle, as it is, on a bounded sample of the same workload
     (batches of the workload's size, or of `sample_tokens` tokens for large batches)."""
@@ -312,6 +370,13 @@ def main():
     ms_total = e0.elapsed_time(e1)
     ms_step = ms_total / K
     log(f"[bench] {K} steps: {ms_step * 1e3:.1f} us/step")
+    graph = graph_replay(layers, xs, (delta, idx, gw, ws), args.rotate, args.batches, K,
+                         args.warmup)
+    graph["tokens_per_s"] = T / (graph["us_per_step"] * 1e-6)
+    log(f"[bench] hipGraph replay: {graph['us_per_step']:.1f} us/step over {K} replays; single "
+        f"replays median {graph['median_us']:.1f} (p10 {graph['p10_us']:.1f}, p90 "
+        f"{graph['p90_us']:.1f}); eager median {graph['eager']['median_us']:.1f}; "
+        f"bits equal eager: {graph['bits_equal_eager']}")
 
     # per-step durations: the same forwards with in-stream events between the steps.  An
     # event record costs a few microseconds of GPU time, so this pass only ranks the steps;
@@ -412,6 +477,7 @@ def main():
                    "dense_weight_copies": args.rotate, "token_batches": args.batches,
                    "distinct_experts_per_step": Dm},
         "roofline": roofline,
+        "hipgraph": graph,
         "layer": {"algorithmic_bytes": layer_bytes, "achieved_GBps": layer_gbs,
                   "hbm_frac": layer_gbs / HBM_PEAK_GBS,
                   "algorithmic_flops": sum(af.values()), "achieved_TFLOPs": layer_tflops,
