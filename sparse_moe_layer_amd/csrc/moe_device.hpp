@@ -271,6 +271,20 @@ __device__ __forceinline__ bool chunk_item(int bid, int n_units, int n_grp, int 
   u = x * per_xcd + ui;
   return ui < per_xcd && u < n_units;
 }
+// Work order where XCD x owns a contiguous block of the tile-row groups and walks the units
+// in table order, each unit through its block of groups back to back: a unit's activation
+// rows are fetched once per XCD, and the XCD's slice of an expert's weights stays in its L2
+// while the expert's units pass.  Items past the groups or the units return false.
+__device__ __forceinline__ bool xcd_block_item(int bid, int n_grp, int n_units, int& grp, int& u) {
+  const int x = bid % kXcds, j = bid / kXcds;
+  const int gx = (n_grp + kXcds - 1) / kXcds;
+  u = j / gx;
+  grp = x * gx + (j - u * gx);
+  return grp < n_grp && u < n_units;
+}
+__host__ inline int64_t xcd_block_grid(int64_t n_grp, int64_t max_units) {
+  return kXcds * ((n_grp + kXcds - 1) / kXcds) * max_units;
+}
 __host__ inline int64_t chunk_grid(int64_t max_units, int64_t n_grp, int64_t chunk) {
   const int64_t per_xcd = (max_units + kXcds - 1) / kXcds;
   return kXcds * ((per_xcd + chunk - 1) / chunk) * chunk * n_grp;

@@ -1457,6 +1457,11 @@ __global__ __launch_bounds__(kBlock) void k_out_tt(OutTTArgs a) {
 // chunks of chunk_item, which keep a chunk's activation rows in L2 but concentrate the
 // XCD's weight reads on a few experts), > 0 = chunk_item with that many units per chunk.
 constexpr int kExpChunk = 0;
+// Work order of the long units (k_exp_tt), as kExpChunk or -1 = xcd_block_item: every XCD
+// owns a block of tile-row groups and takes each unit through it, so that a unit's rows are
+// fetched once per XCD instead of once per group (the group-major order fetched them again
+// for every group; the expert down products took 8-12% less time in this order).
+constexpr int kExpTTOrder = -1;
 
 // The K-step loop for a unit of n positions (2n hi/lo rows in NB blocks).
 template <int WF, bool GU, int NB>
@@ -1505,7 +1510,9 @@ __global__ __launch_bounds__(kBlock, WF == 1 ? 4 : 3) void k_exp_tt(ExpArgs a) {
   const int first = a.ctrl[1];
   const int n_units = min(a.ctrl[0] - first, a.max_units);
   int wgi, u;
-  if (a.chunk > 0) {
+  if (a.chunk < 0) {
+    if (!xcd_block_item(blockIdx.x, a.wg_per_unit, n_units, wgi, u)) return;
+  } else if (a.chunk > 0) {
     if (!chunk_item(blockIdx.x, n_units, a.wg_per_unit, a.chunk, wgi, u)) return;
   } else if (!xcd_item(blockIdx.x, a.wg_per_unit, a.max_units, wgi, u) || u >= n_units) {
     return;
@@ -1884,10 +1891,11 @@ hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_
     // the long units: K-step loop over tiles of their hi/lo rows
     ExpArgs b = a;
     b.max_units = (int)max_large_units(s, T);
-    b.chunk = kExpChunk;
+    b.chunk = kExpTTOrder;
     if (b.max_units > 0) {
-      const unsigned grid = (unsigned)(b.chunk > 0 ? chunk_grid(b.max_units, b.wg_per_unit, b.chunk)
-                                                   : xcd_grid(b.wg_per_unit, b.max_units));
+      const unsigned grid = (unsigned)(b.chunk > 0   ? chunk_grid(b.max_units, b.wg_per_unit, b.chunk)
+                                       : b.chunk < 0 ? xcd_block_grid(b.wg_per_unit, b.max_units)
+                                                     : xcd_grid(b.wg_per_unit, b.max_units));
       const size_t lds = (size_t)2 * kHiloTTBlocks * 16 * 16 * 16;
       if (s.wfmt == 1) {
         if (gu) hipLaunchKernelGGL((k_exp_tt<1, true>), dim3(grid), dim3(kBlock), lds, st, b);
