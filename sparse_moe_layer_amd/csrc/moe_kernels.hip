@@ -1199,39 +1199,43 @@ struct TTStage {
   }
 };
 
-// The K loop of a tile: D[b] (16 x 16 block b of the tile's rows x this wavefront's tile
-// row) over all ks K-steps.  With PARTS, sums restart every qper K-steps and the partial
-// sums are added in order (the K-split of the launches for few tokens); without, one
+// The K loop of a tile: D[t][b] (16 x 16 block b of the tile's rows x this wavefront's tile
+// row t, trow[t]) over all ks K-steps.  With PARTS, sums restart every qper K-steps and the
+// partial sums are added in order (the K-split of the launches for few tokens); without, one
 // running sum over all of K (qper is then ks).  Every wavefront of the workgroup runs it
-// (staging and barriers are shared); trow must be a valid tile row (waves without one pass
-// tile row 0 and drop the result).  Weights are loaded P K-steps ahead, activations PA
-// (P a multiple of PA).  The loop runs whole rounds of P steps: steps past ks re-read the
-// last K-step and are never summed.
-template <int WF, int P, int NB, int PA = P, bool PARTS = true>
-__device__ __forceinline__ void tt_run(const TTRows& rows, const TTSrc& src, const uint8_t* trow,
-                                       int ks, int qper, uint4* lds, f32x4_t (&tot)[NB]) {
+// (staging and barriers are shared); each trow[t] must be a valid tile row (waves without one
+// pass tile row 0 and drop the result).  Each A operand read from LDS feeds the TR tile rows.
+// Weights are loaded P K-steps ahead, activations PA (P a multiple of PA).  The loop runs
+// whole rounds of P steps: steps past ks re-read the last K-step and are never summed.
+template <int WF, int P, int NB, int PA, bool PARTS, int TR>
+__device__ __forceinline__ void tt_run_tr(const TTRows& rows, const TTSrc& src,
+                                          const uint8_t* const (&trow)[TR], int ks, int qper,
+                                          uint4* lds, f32x4_t (&tot)[TR][NB]) {
   static_assert(P % PA == 0, "the weight ring is a multiple of the activation ring");
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane & 15, g = lane >> 4;
   constexpr int RB = 16 * NB;
   constexpr int rstride = RB * 16;           // words per buffer (16 pieces x RB rows)
-  TileStream<WF, P> ts;
+  TileStream<WF, P> ts[TR];
   TTStage<PA, NB> st;
   st.init(rows, src);
 #pragma unroll
   for (int i = 0; i < P; ++i) {
-    ts.w[i].load(trow, min(i, ks - 1), lane);
+#pragma unroll
+    for (int t = 0; t < TR; ++t) ts[t].w[i].load(trow[t], min(i, ks - 1), lane);
     if (i < PA) st.load(i, src, min(i, ks - 1));
   }
   asm volatile("" ::: "memory");
   st.commit(0, lds, src, 0);
   __syncthreads();
-  f32x4_t cur[NB];
+  f32x4_t cur[TR][NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    cur[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    tot[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int t = 0; t < TR; ++t)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      cur[t][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      tot[t][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
   bool first = true;
   int in_part = 0;
   const int rounds = cdiv(ks, P);
@@ -1243,44 +1247,72 @@ __device__ __forceinline__ void tt_run(const TTRows& rows, const TTSrc& src, con
       st.load(i % PA, src, min(q + PA, ks - 1));
       const uint4* buf = lds + (q & 1) * rstride;
       constexpr bool kFp8 = WeightStep<WF>::kFp8;
-      const float scl = WF ? ts.w[i].scale(g) : 0.f;
-      f32x4_t part[NB];
+      float scl[TR];
+      f32x4_t part[TR][NB];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) part[b] = kFp8 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : cur[b];
+      for (int t = 0; t < TR; ++t) {
+        scl[t] = WF ? ts[t].w[i].scale(g) : 0.f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) part[t][b] = kFp8 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : cur[t][b];
+      }
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
         const int jj = WeightStep<WF>::a_piece(s4, g);
-        const uint4 bw = ts.w[i].operand(s4, scl);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) part[b] = mfma_bf16(buf[jj * RB + 16 * b + (c ^ jj)], bw, part[b]);
+        for (int t = 0; t < TR; ++t) {
+          const uint4 bw = ts[t].w[i].operand(s4, scl[t]);
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            part[t][b] = mfma_bf16(buf[jj * RB + 16 * b + (c ^ jj)], bw, part[t][b]);
+        }
       }
 #pragma unroll
-      for (int b = 0; b < NB; ++b)   // FP8: the K-step's partial sums times its block scale
-        cur[b] = kFp8 ? WeightStep<WF>::scale_add(part[b], scl, cur[b]) : part[b];
+      for (int t = 0; t < TR; ++t)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)   // FP8: the K-step's partial sums times its block scale
+          cur[t][b] = kFp8 ? WeightStep<WF>::scale_add(part[t][b], scl[t], cur[t][b]) : part[t][b];
       // the K-step's products are issued before its slot is reloaded, so that the slot's old
       // and new values never overlap and keep one register set across the loop's back edge
       // (where the compiler would otherwise copy the ring, waiting for every load in flight)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) asm volatile("" : "+v"(cur[b]) :: "memory");
-      ts.w[i].load(trow, min(q + P, ks - 1), lane);
+      for (int t = 0; t < TR; ++t)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) asm volatile("" : "+v"(cur[t][b]) :: "memory");
+#pragma unroll
+      for (int t = 0; t < TR; ++t) ts[t].w[i].load(trow[t], min(q + P, ks - 1), lane);
       if (PARTS && q < ks && (++in_part == qper || q + 1 == ks)) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          tot[b] = first ? cur[b] : tot[b] + cur[b];
-          cur[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int t = 0; t < TR; ++t)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            tot[t][b] = first ? cur[t][b] : tot[t][b] + cur[t][b];
+            cur[t][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
         first = false;
         in_part = 0;
       }
       if (!PARTS && q + 1 == ks) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) tot[b] = cur[b];
+        for (int t = 0; t < TR; ++t)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) tot[t][b] = cur[t][b];
       }
       asm volatile("" ::: "memory");
       st.commit((i + 1) % PA, lds + ((q + 1) & 1) * rstride, src, min(q + 1, ks - 1));
       __syncthreads();
     }
   }
+}
+
+// One tile row per wavefront.
+template <int WF, int P, int NB, int PA = P, bool PARTS = true>
+__device__ __forceinline__ void tt_run(const TTRows& rows, const TTSrc& src, const uint8_t* trow,
+                                       int ks, int qper, uint4* lds, f32x4_t (&tot)[NB]) {
+  const uint8_t* const tr1[1] = {trow};
+  f32x4_t t1[1][NB];
+  tt_run_tr<WF, P, NB, PA, PARTS, 1>(rows, src, tr1, ks, qper, lds, t1);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) tot[b] = t1[0][b];
 }
 
 // Dense IN matrix rows (W_down_latent and the shared gate/up) for a tile of up to 64
@@ -1463,45 +1495,64 @@ constexpr int kExpChunk = 0;
 // for every group; the expert down products took 8-12% less time in this order).
 constexpr int kExpTTOrder = -1;
 
-// The K-step loop for a unit of n positions (2n hi/lo rows in NB blocks).
-template <int WF, bool GU, int NB>
+// Tile rows per wavefront of the long-unit launches: every A operand read from LDS feeds
+// that many weight tiles, and one activation stage (and barrier) serves 4 x that many tile
+// rows of the workgroup.  Two (MXFP4, FP8) take about 200 registers, 2 waves per SIMD:
+// measured 5-9% faster than one at 3-4 waves on the FP8 long units, 1-2% on the MXFP4 ones.
+template <int WF>
+struct ExpTTRows {
+  static constexpr int value = WF == 0 ? 1 : 2;
+};
+
+// The K-step loop for a unit of n positions (2n hi/lo rows in NB blocks), over the TR tile
+// rows trow[t] of this wavefront.
+template <int WF, bool GU, int NB, int TR>
 __device__ __forceinline__ void exp_tt_unit(const ExpArgs& a, const TTRows& rows, uint4* sm,
-                                            const uint8_t* trow, bool live, int p0, int n, int tr,
-                                            int c, int g) {
-  f32x4_t tot[NB];
-  // weights about 4 KiB per wavefront ahead (4 MXFP4 K-steps, 2 FP8 or bf16 ones)
-  tt_run<WF, WF == 1 ? 4 : 2, NB, 2, false>(rows, TTSrc{a.xin_hl, nullptr, 2 * n, a.kin, 0, 0},
-                                            trow, a.ks, a.ks, sm, tot);
-  if (!live) return;
+                                            const uint8_t* const (&trow)[TR], const int (&tr)[TR],
+                                            int p0, int n, int c, int g) {
+  f32x4_t tot[TR][NB];
+  // weights about 4 KiB per tile row ahead (4 MXFP4 K-steps, 2 FP8 or bf16 ones)
+  tt_run_tr<WF, WF == 1 ? 4 : 2, NB, 2, false, TR>(
+      rows, TTSrc{a.xin_hl, nullptr, 2 * n, a.kin, 0, 0}, trow, a.ks, a.ks, sm, tot);
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-    exp_store<GU>(a, p0, n, tr, c, 8 * b + 2 * g, tot[b][0] + tot[b][1], tot[b][2] + tot[b][3]);
+  for (int t = 0; t < TR; ++t) {
+    if (tr[t] >= a.n_tr) continue;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      exp_store<GU>(a, p0, n, tr[t], c, 8 * b + 2 * g, tot[t][b][0] + tot[t][b][1],
+                    tot[t][b][2] + tot[t][b][3]);
+  }
 }
 
 // The same over one bf16 row per position (an input that is bf16 already, whose lo rows
 // are zero): D row 16 b + 4 g + v is position 16 b + 4 g + v, with the same sum as hi + lo
 // (hi + 0).
-template <int WF, bool GU, int NB>
-__device__ __forceinline__ void exp_tt_unit_single(const ExpArgs& a, const TTRows& rows, uint4* sm,
-                                                   const uint8_t* trow, bool live, int p0, int n,
-                                                   int tr, int c, int g) {
-  f32x4_t tot[NB];
-  tt_run<WF, WF == 1 ? 4 : 2, NB, 2, false>(rows, TTSrc{a.xin_hl, nullptr, n, a.kin, 0, 0},
-                                            trow, a.ks, a.ks, sm, tot);
-  if (!live) return;
+template <int WF, bool GU, int NB, int TR>
+__device__ __forceinline__ void exp_tt_unit_single(const ExpArgs& a, const TTRows& rows,
+                                                   uint4* sm, const uint8_t* const (&trow)[TR],
+                                                   const int (&tr)[TR], int p0, int n, int c,
+                                                   int g) {
+  f32x4_t tot[TR][NB];
+  tt_run_tr<WF, WF == 1 ? 4 : 2, NB, 2, false, TR>(
+      rows, TTSrc{a.xin_hl, nullptr, n, a.kin, 0, 0}, trow, a.ks, a.ks, sm, tot);
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    exp_store<GU>(a, p0, n, tr, c, 16 * b + 4 * g, tot[b][0], tot[b][1]);
-    exp_store<GU>(a, p0, n, tr, c, 16 * b + 4 * g + 2, tot[b][2], tot[b][3]);
+  for (int t = 0; t < TR; ++t) {
+    if (tr[t] >= a.n_tr) continue;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      exp_store<GU>(a, p0, n, tr[t], c, 16 * b + 4 * g, tot[t][b][0], tot[t][b][1]);
+      exp_store<GU>(a, p0, n, tr[t], c, 16 * b + 4 * g + 2, tot[t][b][2], tot[t][b][3]);
+    }
   }
 }
 
 // Routed experts for the second list of the unit table: units [ctrl[1], ctrl[0]), each of
 // up to 32 positions (the first list, of short units, goes to k_exp).  The input rows are
 // hi/lo bf16 rows written by their producer (x^c by the IN launch, h by the gate/up
-// launches).
+// launches).  Wavefront wv of tile-row group wgi takes tile rows (4 wgi + wv) TR + t.
 template <int WF, bool GU>
-__global__ __launch_bounds__(kBlock, WF == 1 ? 4 : 3) void k_exp_tt(ExpArgs a) {
+__global__ __launch_bounds__(kBlock, ExpTTRows<WF>::value == 2 ? 2 : WF == 1 ? 4 : 3) void k_exp_tt(ExpArgs a) {
+  constexpr int TR = ExpTTRows<WF>::value;
   extern __shared__ uint4 sm[];
   __shared__ TTRows rows;
   const int lane = threadIdx.x & (kWave - 1);
@@ -1521,10 +1572,14 @@ __global__ __launch_bounds__(kBlock, WF == 1 ? 4 : 3) void k_exp_tt(ExpArgs a) {
   const int e = un.x, p0 = un.y, n = un.z;
   if (e < 0 || e >= a.E || n < 1 || n > a.nu || n > kHiloTTRows || p0 < 0 || p0 + n > a.n_assign)
     return;
-  const int tr = wgi * kWavesPerBlock + wv;
-  const bool live = tr < a.n_tr;
-  const uint8_t* trow = a.experts + (size_t)e * a.expert_bytes + a.region_off +
-                        (size_t)(live ? tr : 0) * a.ks * WeightStep<WF>::SB;
+  int tr[TR];
+  const uint8_t* trow[TR];
+#pragma unroll
+  for (int t = 0; t < TR; ++t) {
+    tr[t] = (wgi * kWavesPerBlock + wv) * TR + t;
+    trow[t] = a.experts + (size_t)e * a.expert_bytes + a.region_off +
+              (size_t)(tr[t] < a.n_tr ? tr[t] : 0) * a.ks * WeightStep<WF>::SB;
+  }
   const bool single = GU && a.single;
   if ((int)threadIdx.x < (single ? n : 2 * n)) {
     const int i = single ? threadIdx.x : threadIdx.x >> 1, hl = single ? 0 : threadIdx.x & 1;
@@ -1537,13 +1592,13 @@ __global__ __launch_bounds__(kBlock, WF == 1 ? 4 : 3) void k_exp_tt(ExpArgs a) {
   }
   __syncthreads();
   if (single) {
-    if (n <= 16) exp_tt_unit_single<WF, GU, 1>(a, rows, sm, trow, live, p0, n, tr, c, g);
-    else exp_tt_unit_single<WF, GU, 2>(a, rows, sm, trow, live, p0, n, tr, c, g);
+    if (n <= 16) exp_tt_unit_single<WF, GU, 1, TR>(a, rows, sm, trow, tr, p0, n, c, g);
+    else exp_tt_unit_single<WF, GU, 2, TR>(a, rows, sm, trow, tr, p0, n, c, g);
     return;
   }
-  if (n <= 8) exp_tt_unit<WF, GU, 1>(a, rows, sm, trow, live, p0, n, tr, c, g);
-  else if (n <= 16) exp_tt_unit<WF, GU, 2>(a, rows, sm, trow, live, p0, n, tr, c, g);
-  else exp_tt_unit<WF, GU, 4>(a, rows, sm, trow, live, p0, n, tr, c, g);
+  if (n <= 8) exp_tt_unit<WF, GU, 1, TR>(a, rows, sm, trow, tr, p0, n, c, g);
+  else if (n <= 16) exp_tt_unit<WF, GU, 2, TR>(a, rows, sm, trow, tr, p0, n, c, g);
+  else exp_tt_unit<WF, GU, 4, TR>(a, rows, sm, trow, tr, p0, n, c, g);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1892,6 +1947,10 @@ hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_
     ExpArgs b = a;
     b.max_units = (int)max_large_units(s, T);
     b.chunk = kExpTTOrder;
+    const int ttr = s.wfmt == 1   ? ExpTTRows<1>::value
+                    : s.wfmt == 2 ? ExpTTRows<2>::value
+                                  : ExpTTRows<0>::value;
+    b.wg_per_unit = cdiv(b.n_tr, kWavesPerBlock * ttr);
     if (b.max_units > 0) {
       const unsigned grid = (unsigned)(b.chunk > 0   ? chunk_grid(b.max_units, b.wg_per_unit, b.chunk)
                                        : b.chunk < 0 ? xcd_block_grid(b.wg_per_unit, b.max_units)
