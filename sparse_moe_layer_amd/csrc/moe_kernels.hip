@@ -1351,8 +1351,9 @@ __global__ __launch_bounds__(kBlock) void k_in_tt(InTTArgs a) {
   const bool live = tri < a.tr_count;
   const int tr = a.tr_first + (live ? tri : 0);
   f32x4_t tot[kInTTBlocks];
-  tt_run<0, 4, kInTTBlocks>(rows, TTSrc{a.x, nullptr, nt, a.d, 0, 0},
-                            a.w + (size_t)tr * a.ks * kBf16StepBytes, a.ks, a.qper, sm, tot);
+  // 4 weight K-steps and 2 activation K-steps in flight (measured against 2/2, 6/2, 8/4, 4/4)
+  tt_run<0, 4, kInTTBlocks, 2>(rows, TTSrc{a.x, nullptr, nt, a.d, 0, 0},
+                               a.w + (size_t)tr * a.ks * kBf16StepBytes, a.ks, a.qper, sm, tot);
   if (!live) return;
 #pragma unroll
   for (int b = 0; b < kInTTBlocks; ++b) {
@@ -1468,9 +1469,11 @@ __global__ __launch_bounds__(kBlock) void k_out_tt(OutTTArgs a) {
   const int tr = grp * kWavesPerBlock + wv;
   const bool live = tr < a.n_tr;
   f32x4_t tot[kHiloTTBlocks];
-  tt_run<0, 4, kHiloTTBlocks>(rows, TTSrc{a.uh_hl, a.hs_hl, 2 * nt, a.n0, a.ks_l * kStepK, a.ms},
-                              a.w + (size_t)(live ? tr : 0) * a.ks * kBf16StepBytes, a.ks, a.qper,
-                              sm, tot);
+  // 2 weight and 2 activation K-steps in flight: 7-8% faster than 4/4 (124 registers, 3 waves
+  // per SIMD)
+  tt_run<0, 2, kHiloTTBlocks, 2>(
+      rows, TTSrc{a.uh_hl, a.hs_hl, 2 * nt, a.n0, a.ks_l * kStepK, a.ms},
+      a.w + (size_t)(live ? tr : 0) * a.ks * kBf16StepBytes, a.ks, a.qper, sm, tot);
   if (!live) return;
   const int r = 16 * tr + c;
   if (r >= a.d) return;
