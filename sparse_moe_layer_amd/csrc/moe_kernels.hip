@@ -264,10 +264,19 @@ __global__ __launch_bounds__(1024) void k_disp_scan(int n_chunks, int E, int nu,
   const int e = threadIdx.x;
   int tot = 0;
   if (e < E) {
-    for (int c = 0; c < n_chunks; ++c) {
-      const int v = chunk_hist[(int64_t)c * E + e];
-      chunk_hist[(int64_t)c * E + e] = tot;
-      tot += v;
+    // the chunks' counts in groups of 32 loads in flight, then their exclusive scan in place
+    // (a load after each store of the scan would wait out its whole latency)
+    constexpr int kGroup = 32;
+    for (int c0 = 0; c0 < n_chunks; c0 += kGroup) {
+      int v[kGroup];
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j)
+        v[j] = c0 + j < n_chunks ? chunk_hist[(int64_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        if (c0 + j < n_chunks) chunk_hist[(int64_t)(c0 + j) * E + e] = tot;
+        tot += v[j];
+      }
     }
     counts[e] = tot;
   }
