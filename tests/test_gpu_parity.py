@@ -190,7 +190,10 @@ def test_zero_tokens_is_a_no_op():
     assert d.shape == (0, TINY.d) and i.shape == (0, TINY.k)
 
 
-@pytest.mark.parametrize("T,E,k", [(1, 896, 16), (37, 896, 16), (100, 64, 2), (300, 70, 5)])
+# 3001 x 16 and 5000 x 8: 188 and 157 dispatch chunks, past the scan's groups of 32 with a
+# ragged last group
+@pytest.mark.parametrize("T,E,k", [(1, 896, 16), (37, 896, 16), (100, 64, 2), (300, 70, 5),
+                                   (3001, 896, 16), (5000, 384, 8)])
 def test_dispatch_bit_exact(T, E, k):
     rng = np.random.default_rng(T * 1000 + E)
     idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
