@@ -181,6 +181,31 @@ class HipEvents:
             self.h.hipEventDestroy(e)
 
 
+def measured_hbm_rates(torch, dev, gib=2, reps=5):
+    """What torch's own generic kernels reach on this GPU's HBM: a sum over `gib` GiB (read)
+    and a copy of `gib` GiB (read + write), best of `reps`, in GB/s.  Context beside the
+    nominal 8 TB/s peak that the roofline fractions use; not an achievable-peak probe."""
+    n = gib << 30
+    src = torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    out = {}
+    for name, fn, nbytes in (("torch_sum_read_GBps", lambda: src.sum(), n),
+                             ("torch_copy_GBps", lambda: dst.copy_(src), 2 * n)):
+        fn()
+        best = None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        out[name] = nbytes / (best * 1e-3) / 1e9
+    del src, dst
+    return out
+
+
 def percentiles_us(durations_ms):
     import numpy as np
     d = np.asarray(durations_ms, dtype=np.float64) * 1e3
@@ -432,6 +457,9 @@ def main():
         torch.cuda.synchronize()
         log("[bench] calibration copy: 1 GiB read + 1 GiB written")
 
+    # (not in the counter runs: their calibration is the last large device copy of the run)
+    measured = None if args.copy_calibration else measured_hbm_rates(torch, dev)
+    log(f"[bench] torch's generic kernels on the same HBM (context): {measured}")
     Dm = float(np.mean([D[i % args.batches] for i in range(K)]))
     ab = algorithmic_bytes(cfg, T, Dm)
     af = algorithmic_flops(cfg, T)
@@ -478,6 +506,7 @@ def main():
                    "distinct_experts_per_step": Dm},
         "roofline": roofline,
         "hipgraph": graph,
+        "measured_hbm": measured,
         "layer": {"algorithmic_bytes": layer_bytes, "achieved_GBps": layer_gbs,
                   "hbm_frac": layer_gbs / HBM_PEAK_GBS,
                   "algorithmic_flops": sum(af.values()), "achieved_TFLOPs": layer_tflops,
