@@ -254,6 +254,22 @@ __device__ __forceinline__ bool xcd_item(int bid, int n_groups, int n_blk, int& 
 __host__ inline int64_t xcd_grid(int64_t n_groups, int64_t n_blk) {
   return kXcds * ((n_groups + kXcds - 1) / kXcds) * n_blk;
 }
+// The same with groups taken G at a time: XCD x walks blocks x, x + 8, ... of G consecutive
+// groups, each block tile by tile, the G groups of a tile back to back, so that workgroups
+// in flight on the XCD share each activation tile G ways while the block's weights stay in
+// its L2.  G = 1 is xcd_item.
+__device__ __forceinline__ bool xcd_gblock_item(int bid, int n_groups, int n_blk, int G, int& grp,
+                                                int& blk) {
+  const int x = bid % kXcds, j = bid / kXcds;
+  const int bi = j / (G * n_blk), r = j - bi * G * n_blk;
+  blk = r / G;
+  grp = (x + kXcds * bi) * G + (r - blk * G);
+  return grp < n_groups;
+}
+__host__ inline int64_t xcd_gblock_grid(int64_t n_groups, int64_t n_blk, int64_t G) {
+  const int64_t nb = (n_groups + G - 1) / G;
+  return kXcds * ((nb + kXcds - 1) / kXcds) * G * n_blk;
+}
 
 // Work order over (unit, tile-row group) items when the number of units is known only on
 // the device: XCD x takes a contiguous range of the units (so of the experts, the unit
