@@ -92,12 +92,16 @@ inline bool route_fused(const Shape& s, int64_t T) {
 }
 inline bool token_tiled(const Shape& s, int64_t T) { return !route_fused(s, T); }
 constexpr int kTiledUnitPositions = 32;
+// Without a latent the gate/up input is the token (one bf16 row per position), so a unit of
+// the token-tiled launches holds up to 64 positions: an expert's weights are read once per 64
+// of its positions.  The launches whose input is hi/lo rows take such a unit in two halves.
+constexpr int kTiledUnitPositionsSingle = 64;
 constexpr int kPfUnitPositions = 64;   // 16 x the expert tile blocks of moe_prefill.hip
 // Positions of one expert per unit of the expert launches (2 hi/lo rows each; one FP8
 // row each in the mx8 launches).
 inline int unit_positions(const Shape& s, int64_t T) {
   if (s.prec == 1) return kPfUnitPositions;
-  if (token_tiled(s, T)) return kTiledUnitPositions;
+  if (token_tiled(s, T)) return s.latent ? kTiledUnitPositions : kTiledUnitPositionsSingle;
   // few tokens: all rows of a unit staged at once (2 hi/lo rows of the widest expert
   // input per position, within 56 KiB of LDS)
   const int ks = s.ks_gu > s.ks_edn ? s.ks_gu : s.ks_edn;

@@ -1563,8 +1563,14 @@ __device__ __forceinline__ void exp_tt_unit_single(const ExpArgs& a, const TTRow
   }
 }
 
+// Work items per unit of the long-unit launch: 2 when its hi/lo input rows of a unit of up to
+// 2 kHiloTTRows positions exceed one tile, else 1.
+__host__ __device__ inline int exp_tt_halves(bool single, int nu) {
+  return !single && nu > kHiloTTRows ? 2 : 1;
+}
+
 // Routed experts for the second list of the unit table: units [ctrl[1], ctrl[0]), each of
-// up to 32 positions (the first list, of short units, goes to k_exp).  The input rows are
+// up to 32 positions (64 with single input rows) (the first list, of short units, goes to k_exp).  The input rows are
 // hi/lo bf16 rows written by their producer (x^c by the IN launch, h by the gate/up
 // launches).  Wavefront wv of tile-row group wgi takes tile rows (4 wgi + wv) TR + t.
 template <int WF, bool GU>
@@ -1575,20 +1581,27 @@ __global__ __launch_bounds__(kBlock, ExpTTRows<WF>::value == 2 ? 2 : WF == 1 ? 4
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
+  const bool single = GU && a.single;
+  // hi/lo input rows with units longer than one tile: each unit in halves of kHiloTTRows
+  const int halves = exp_tt_halves(single, a.nu);
   const int first = a.ctrl[1];
-  const int n_units = min(a.ctrl[0] - first, a.max_units);
-  int wgi, u;
+  const int n_items = min(a.ctrl[0] - first, a.max_units) * halves;
+  int wgi, item;
   if (a.chunk < 0) {
-    if (!xcd_block_item(blockIdx.x, a.wg_per_unit, n_units, wgi, u)) return;
+    if (!xcd_block_item(blockIdx.x, a.wg_per_unit, n_items, wgi, item)) return;
   } else if (a.chunk > 0) {
-    if (!chunk_item(blockIdx.x, n_units, a.wg_per_unit, a.chunk, wgi, u)) return;
-  } else if (!xcd_item(blockIdx.x, a.wg_per_unit, a.max_units, wgi, u) || u >= n_units) {
+    if (!chunk_item(blockIdx.x, n_items, a.wg_per_unit, a.chunk, wgi, item)) return;
+  } else if (!xcd_item(blockIdx.x, a.wg_per_unit, a.max_units * halves, wgi, item) ||
+             item >= n_items) {
     return;
   }
+  const int u = item / halves, half = item - u * halves;
   const int4 un = *reinterpret_cast<const int4*>(a.units + 4 * (first + u));
-  const int e = un.x, p0 = un.y, n = un.z;
-  if (e < 0 || e >= a.E || n < 1 || n > a.nu || n > kHiloTTRows || p0 < 0 || p0 + n > a.n_assign)
-    return;
+  const int e = un.x;
+  if (e < 0 || e >= a.E || un.z < 1 || un.z > a.nu || un.y < 0 || un.y + un.z > a.n_assign) return;
+  const int p0 = un.y + half * kHiloTTRows;
+  const int n = halves > 1 ? min(kHiloTTRows, un.z - half * kHiloTTRows) : un.z;
+  if (n < 1 || n > (single ? kTTMaxSrc : kHiloTTRows)) return;
   int tr[TR];
   const uint8_t* trow[TR];
 #pragma unroll
@@ -1597,7 +1610,6 @@ __global__ __launch_bounds__(kBlock, ExpTTRows<WF>::value == 2 ? 2 : WF == 1 ? 4
     trow[t] = a.experts + (size_t)e * a.expert_bytes + a.region_off +
               (size_t)(tr[t] < a.n_tr ? tr[t] : 0) * a.ks * WeightStep<WF>::SB;
   }
-  const bool single = GU && a.single;
   if ((int)threadIdx.x < (single ? n : 2 * n)) {
     const int i = single ? threadIdx.x : threadIdx.x >> 1, hl = single ? 0 : threadIdx.x & 1;
     int64_t src = p0 + i;
@@ -1610,7 +1622,8 @@ __global__ __launch_bounds__(kBlock, ExpTTRows<WF>::value == 2 ? 2 : WF == 1 ? 4
   __syncthreads();
   if (single) {
     if (n <= 16) exp_tt_unit_single<WF, GU, 1, TR>(a, rows, sm, trow, tr, p0, n, c, g);
-    else exp_tt_unit_single<WF, GU, 2, TR>(a, rows, sm, trow, tr, p0, n, c, g);
+    else if (n <= 32) exp_tt_unit_single<WF, GU, 2, TR>(a, rows, sm, trow, tr, p0, n, c, g);
+    else exp_tt_unit_single<WF, GU, 4, TR>(a, rows, sm, trow, tr, p0, n, c, g);
     return;
   }
   if (n <= 8) exp_tt_unit<WF, GU, 1, TR>(a, rows, sm, trow, tr, p0, n, c, g);
@@ -1964,14 +1977,16 @@ hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_
     ExpArgs b = a;
     b.max_units = (int)max_large_units(s, T);
     b.chunk = kExpTTOrder;
+    const int halves = exp_tt_halves(b.single != 0, b.nu);
     const int ttr = s.wfmt == 1   ? ExpTTRows<1>::value
                     : s.wfmt == 2 ? ExpTTRows<2>::value
                                   : ExpTTRows<0>::value;
     b.wg_per_unit = cdiv(b.n_tr, kWavesPerBlock * ttr);
     if (b.max_units > 0) {
-      const unsigned grid = (unsigned)(b.chunk > 0   ? chunk_grid(b.max_units, b.wg_per_unit, b.chunk)
-                                       : b.chunk < 0 ? xcd_block_grid(b.wg_per_unit, b.max_units)
-                                                     : xcd_grid(b.wg_per_unit, b.max_units));
+      const int64_t items = (int64_t)b.max_units * halves;
+      const unsigned grid = (unsigned)(b.chunk > 0   ? chunk_grid(items, b.wg_per_unit, b.chunk)
+                                       : b.chunk < 0 ? xcd_block_grid(b.wg_per_unit, items)
+                                                     : xcd_grid(b.wg_per_unit, items));
       const size_t lds = (size_t)2 * kHiloTTBlocks * 16 * 16 * 16;
       if (s.wfmt == 1) {
         if (gu) hipLaunchKernelGGL((k_exp_tt<1, true>), dim3(grid), dim3(kBlock), lds, st, b);
