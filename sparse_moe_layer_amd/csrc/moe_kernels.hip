@@ -1393,7 +1393,7 @@ __global__ __launch_bounds__(kBlock) void k_in_tt(InTTArgs a) {
   }
 }
 
-// Router logits for a tile of up to 64 tokens: one workgroup per (4 router tile rows,
+// Router logits for a tile of up to 64 tokens: one workgroup per (4 TR router tile rows,
 // logit plane, token tile).  Plane p covers the K-steps [p qpp, (p+1) qpp) of the few-token
 // router launch and is summed in its order: runs of qw K-steps (its per-wavefront K-split)
 // added in sequence.  The route adds the planes in order, so a token's logits have the same
@@ -1407,6 +1407,12 @@ struct RouterTTArgs {
   float* z;          // [zplanes][T][E]
 };
 
+// Tile rows per wavefront of the token-tiled router (TR): with 2 each A operand feeds both
+// and a token tile is read by half as many workgroups (27% faster at 8192 tokens); below
+// kRouterTTWideTokens tokens, 1 keeps twice the workgroups (faster at 64 tokens).
+constexpr int kRouterTTWideTokens = 512;
+
+template <int TR>
 __global__ __launch_bounds__(kBlock) void k_router_tt(RouterTTArgs a) {
   extern __shared__ uint4 sm[];
   __shared__ TTRows rows;
@@ -1422,31 +1428,38 @@ __global__ __launch_bounds__(kBlock) void k_router_tt(RouterTTArgs a) {
   const int nt = (int)min((int64_t)kTTMaxSrc, a.T - t0);
   float* zp = a.z + (int64_t)plane * a.T * a.E;
   if (r1 <= r0) {   // an empty plane holds zeros, as in the few-token launch (uniform branch)
-    for (int i = threadIdx.x; i < nt * 16 * kWavesPerBlock; i += kBlock) {
-      const int e = 16 * grp * kWavesPerBlock + i % (16 * kWavesPerBlock);
-      if (e < a.E) zp[(t0 + i / (16 * kWavesPerBlock)) * a.E + e] = 0.f;
+    constexpr int kGroupRows = 16 * kWavesPerBlock * TR;   // experts of a group
+    for (int i = threadIdx.x; i < nt * kGroupRows; i += kBlock) {
+      const int e = kGroupRows * grp + i % kGroupRows;
+      if (e < a.E) zp[(t0 + i / kGroupRows) * a.E + e] = 0.f;
     }
     return;
   }
   // rows start at the plane's first column
   if ((int)threadIdx.x < nt) rows.o0[threadIdx.x] = (uint32_t)((t0 + threadIdx.x) * a.d / 8 + r0 * (kStepK / 8));
   __syncthreads();
-  const int tri = grp * kWavesPerBlock + wv;
-  const bool live = tri < a.tr_r;
-  const uint8_t* trow = a.w + ((size_t)(live ? tri : 0) * a.ks + r0) * kBf16StepBytes;
-  f32x4_t tot[kInTTBlocks];
-  tt_run<0, 4, kInTTBlocks>(rows, TTSrc{a.x, nullptr, nt, a.d - r0 * kStepK, 0, 0}, trow, r1 - r0,
-                            qw, sm, tot);
-  if (!live) return;
-  const int e = 16 * tri + c;
-  if (e >= a.E) return;
+  int tri[TR];
+  const uint8_t* trow[TR];
 #pragma unroll
-  for (int b = 0; b < kInTTBlocks; ++b)
+  for (int t = 0; t < TR; ++t) {
+    tri[t] = (grp * kWavesPerBlock + wv) * TR + t;
+    trow[t] = a.w + ((size_t)(tri[t] < a.tr_r ? tri[t] : 0) * a.ks + r0) * kBf16StepBytes;
+  }
+  f32x4_t tot[TR][kInTTBlocks];
+  tt_run_tr<0, 2, kInTTBlocks, 2, true, TR>(rows, TTSrc{a.x, nullptr, nt, a.d - r0 * kStepK, 0, 0},
+                                            trow, r1 - r0, qw, sm, tot);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int ti = 16 * b + 4 * g + v;
-      if (ti < nt) zp[(t0 + ti) * a.E + e] = tot[b][v];
-    }
+  for (int t = 0; t < TR; ++t) {
+    const int e = 16 * tri[t] + c;
+    if (tri[t] >= a.tr_r || e >= a.E) continue;
+#pragma unroll
+    for (int b = 0; b < kInTTBlocks; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int ti = 16 * b + 4 * g + v;
+        if (ti < nt) zp[(t0 + ti) * a.E + e] = tot[t][b][v];
+      }
+  }
 }
 
 // OUT matrix for a tile of up to 32 tokens: [u_hat ; h_s] as hi/lo rows.
@@ -1569,12 +1582,15 @@ __host__ __device__ inline int exp_tt_halves(bool single, int nu) {
   return !single && nu > kHiloTTRows ? 2 : 1;
 }
 
-// Routed experts for the second list of the unit table: units [ctrl[1], ctrl[0]), each of
-// up to 32 positions (64 with single input rows) (the first list, of short units, goes to k_exp).  The input rows are
-// hi/lo bf16 rows written by their producer (x^c by the IN launch, h by the gate/up
-// launches).  Wavefront wv of tile-row group wgi takes tile rows (4 wgi + wv) TR + t.
+// Routed experts for the second list of the unit table: units [ctrl[1], ctrl[0]) (the first
+// list, of short units, goes to k_exp).  A unit holds up to 32 positions, or up to 64 when
+// the input is single bf16 rows (the token, without a latent); hi/lo inputs of such a unit go
+// in parts of 32 positions, one work item each.  The hi/lo rows are written by their producer
+// (x^c by the IN launch, h by the gate/up launches).  Wavefront wv of tile-row group wgi takes
+// tile rows (4 wgi + wv) TR + t.
 template <int WF, bool GU>
-__global__ __launch_bounds__(kBlock, ExpTTRows<WF>::value == 2 ? 2 : WF == 1 ? 4 : 3) void k_exp_tt(ExpArgs a) {
+__global__ __launch_bounds__(kBlock, ExpTTRows<WF>::value == 2 ? 2 : WF == 1 ? 4 : 3)
+void k_exp_tt(ExpArgs a) {
   constexpr int TR = ExpTTRows<WF>::value;
   extern __shared__ uint4 sm[];
   __shared__ TTRows rows;
@@ -1839,14 +1855,16 @@ hipError_t launch_router(const Shape& s, const uint8_t* dense, const uint16_t* x
     a.ks = s.ks_in;
     a.qpp = cdiv(s.ks_in, s.zplanes);
     a.tr_r = s.tr_r;
-    a.n_grp = cdiv(s.tr_r, kWavesPerBlock);
+    const int tr = T >= kRouterTTWideTokens ? 2 : 1;
+    a.n_grp = cdiv(s.tr_r, kWavesPerBlock * tr);
     a.zplanes = s.zplanes;
     a.n_tiles = cdiv(T, kTTMaxSrc);
     a.x = x; a.T = T; a.d = s.d; a.E = s.E;
     a.z = ws.z;
     const size_t lds = (size_t)2 * kInTTBlocks * 16 * 16 * 16;
-    hipLaunchKernelGGL(k_router_tt, dim3((unsigned)xcd_grid((int64_t)a.n_grp * a.zplanes, a.n_tiles)),
-                       dim3(kBlock), lds, st, a);
+    const dim3 grid((unsigned)xcd_grid((int64_t)a.n_grp * a.zplanes, a.n_tiles));
+    if (tr == 2) hipLaunchKernelGGL(k_router_tt<2>, grid, dim3(kBlock), lds, st, a);
+    else hipLaunchKernelGGL(k_router_tt<1>, grid, dim3(kBlock), lds, st, a);
     return hipGetLastError();
   }
   InArgs a = in_args(s, dense, x, T, ws, s.tr_r, router_only ? 0 : s.tr_dn);
