@@ -66,7 +66,8 @@ def algorithmic_bytes(cfg, T, D):
         "dispatch": 0 if small else tk * 4 * 4 + E * 8,
         "expert_gu": D * gu_w + T * l * ab + tk * m * ab,
         "expert_down": D * dn_w + tk * m * ab + tk * l * 4,
-        "combine": tk * l * 4 + tk * 8 + T * l * 4,
+        # (mx8: one pass to u_hat in bf16, u itself is not stored)
+        "combine": tk * l * 4 + tk * 8 + T * l * (2 if mx8 else 4),
         "out": d * (cfg.l + ms) * 2 + cfg.l * 2 + T * (l + ms) * (2 if mx8 else 4) + T * d * 4,
     }
 
@@ -104,7 +105,7 @@ STEP_KERNELS_MX8 = {"router": [("k_pf_dense", "true")], "in": [("k_pf_quant", No
                     "route": [("k_route", None)],
                     "dispatch": [("k_disp_count", None), ("k_disp_scan", None), ("k_disp_scatter", None)],
                     "expert_gu": [("k_pf_exp", "true")], "expert_down": [("k_pf_exp", "false")],
-                    "combine": [("k_combine", None), ("k_pf_norm", None)],
+                    "combine": [("k_pf_combine_norm", None), ("k_combine", None), ("k_pf_norm", None)],
                     "out": [("k_pf_dense", "false")]}
 
 

@@ -332,8 +332,7 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const float
         case MOE_STEP_EXPERT_GU: e = moe::launch_pf_expert(s, experts, true, n_tokens, ws, ws.pf, hs); break;
         case MOE_STEP_EXPERT_DOWN: e = moe::launch_pf_expert(s, experts, false, n_tokens, ws, ws.pf, hs); break;
         case MOE_STEP_COMBINE:
-          e = moe::launch_combine(s, dense, topk_w, n_tokens, ws, hs);
-          if (e == hipSuccess) e = moe::launch_pf_norm(s, dense, n_tokens, ws, ws.pf, hs);
+          e = moe::launch_pf_combine_norm(s, dense, topk_w, n_tokens, ws, ws.pf, hs);
           break;
         case MOE_STEP_OUT: e = moe::launch_pf_out(s, dense, n_tokens, ws.pf, sink, hs); break;
       }

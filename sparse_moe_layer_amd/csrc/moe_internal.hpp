@@ -16,6 +16,7 @@ constexpr int kFp4StepBytes = 1024 + 64;  // MXFP4 K-step: 16 rows x 128 codes +
 constexpr int kFp8StepBytes = 2048 + 16;  // FP8 block-128 K-step: 16 rows x 128 codes + the
                                           // gate-half and up-half block scales (fp32), padded
 constexpr int kCtrlWords = 64;          // control words at the head of the workspace
+constexpr int kMaxK = 64;               // experts per token the kernels are built for
 
 __host__ __device__ inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
@@ -184,6 +185,9 @@ hipError_t launch_pf_expert(const Shape& s, const uint8_t* experts, bool gu, int
                             const Work& ws, const PfWork& pw, hipStream_t st);
 hipError_t launch_pf_norm(const Shape& s, const uint8_t* dense, int64_t T, const Work& ws,
                           const PfWork& pw, hipStream_t st);
+// the combine and the norm of the mx8 launches in one pass (u itself is not stored)
+hipError_t launch_pf_combine_norm(const Shape& s, const uint8_t* dense, const float* gw, int64_t T,
+                                  const Work& ws, const PfWork& pw, hipStream_t st);
 hipError_t launch_pf_out(const Shape& s, const uint8_t* dense, int64_t T, const PfWork& pw,
                          const OutSink& out, hipStream_t st);
 

@@ -61,7 +61,6 @@ struct RouteArgs {
 
 constexpr int kRouteSlots = 4;      // E <= 4 slots x 4 wavefronts x 64 lanes = 1024
 constexpr int kMaxZPlanes = 8;      // partial logit planes of the router launch
-constexpr int kMaxK = 64;
 
 __device__ __forceinline__ void block_route_token(const RouteArgs& a, int64_t t, uint64_t* cand_key,
                                                   float* cand_s, int* sel_e, float* sel_s,

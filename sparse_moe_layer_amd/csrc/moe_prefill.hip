@@ -623,6 +623,88 @@ __global__ __launch_bounds__(kBlock) void k_pf_norm(const float* __restrict__ u,
   }
 }
 
+// The combine and the norm in one pass, one workgroup per token, for the mx8 launches (whose
+// only use of u is u_hat): u_t = sum_j G[t,j] E[inv[t,j]] stays in registers, with the same
+// fmaf chain per element as k_combine, and the sum of squares and u_hat follow k_pf_norm's
+// order (thread i takes the column groups 4 i + 1024 c), so the bits are those of the two
+// kernels.  l <= 4 * kBlock * kPfCnChunks.
+constexpr int kPfCnChunks = 8;
+__global__ __launch_bounds__(kBlock) void k_pf_combine_norm(
+    const float* __restrict__ gw, const int32_t* __restrict__ inv, const float* __restrict__ eo,
+    int k, int l, const uint16_t* __restrict__ gamma, int norm, float eps,
+    uint16_t* __restrict__ uh) {
+  __shared__ float sg[kMaxK];
+  __shared__ int si[kMaxK];
+  __shared__ float red[kPfWaves];
+  const int64_t t = blockIdx.x;
+  if ((int)threadIdx.x < k) {
+    sg[threadIdx.x] = gw[t * k + threadIdx.x];
+    si[threadIdx.x] = inv[t * k + threadIdx.x];
+  }
+  __syncthreads();
+  const int l4 = l / 4;
+  const float4* e4 = reinterpret_cast<const float4*>(eo);
+  float4 u[kPfCnChunks];
+#pragma unroll
+  for (int ch = 0; ch < kPfCnChunks; ++ch) {
+    const int c4 = threadIdx.x + kBlock * ch;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c4 < l4) {
+      for (int j0 = 0; j0 < k; j0 += 16) {
+        float4 v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          v[i] = (j0 + i < k) ? e4[(int64_t)si[j0 + i] * l4 + c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (j0 + i < k) {
+            const float g = sg[j0 + i];
+            acc.x = fmaf(g, v[i].x, acc.x);
+            acc.y = fmaf(g, v[i].y, acc.y);
+            acc.z = fmaf(g, v[i].z, acc.z);
+            acc.w = fmaf(g, v[i].w, acc.w);
+          }
+      }
+    }
+    u[ch] = acc;
+  }
+  float rs = 1.f;
+  if (norm) {
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x >> 6;
+    float ss = 0.f;
+#pragma unroll
+    for (int ch = 0; ch < kPfCnChunks; ++ch)
+      if ((int)threadIdx.x + kBlock * ch < l4) {
+        ss = fmaf(u[ch].x, u[ch].x, ss); ss = fmaf(u[ch].y, u[ch].y, ss);
+        ss = fmaf(u[ch].z, u[ch].z, ss); ss = fmaf(u[ch].w, u[ch].w, ss);
+      }
+    ss = wave_sum(ss);
+    if (lane == 0) red[wv] = ss;
+    __syncthreads();
+    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    rs = 1.0f / sqrtf(tot / (float)l + eps);
+  }
+#pragma unroll
+  for (int ch = 0; ch < kPfCnChunks; ++ch) {
+    const int c4 = threadIdx.x + kBlock * ch;
+    if (c4 >= l4) continue;
+    const float uv[4] = {u[ch].x, u[ch].y, u[ch].z, u[ch].w};
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float o[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int col = 4 * c4 + 2 * h + q;
+        const float gm = norm ? __uint_as_float((uint32_t)gamma[col] << 16) : 1.f;
+        o[q] = norm ? uv[2 * h + q] * rs * gm : uv[2 * h + q];
+      }
+      w[h] = pack_bf16x2(o[0], o[1]);
+    }
+    *reinterpret_cast<uint2*>(uh + t * l + 4 * c4) = make_uint2(w[0], w[1]);
+  }
+}
+
 constexpr size_t kPfDenseLds = (size_t)2 * 16 * kPfDenseNB * 16 * 16;   // two K-steps of the bf16 rows
 // two K-steps of the FP8 rows, and room for the gate/up epilogue's wavefront-private tiles
 constexpr size_t kPfExpEpiLds = (size_t)kPfWaves * 16 * 36 * 4;
@@ -687,6 +769,19 @@ hipError_t launch_pf_expert(const Shape& s, const uint8_t* experts, bool gu, int
   const unsigned grid = (unsigned)chunk_grid(a.max_units, a.n_grp, kPfChunk);
   if (gu) hipLaunchKernelGGL(k_pf_exp<true>, dim3(grid), dim3(kBlock), kPfExpLds, st, a);
   else hipLaunchKernelGGL(k_pf_exp<false>, dim3(grid), dim3(kBlock), kPfExpLds, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pf_combine_norm(const Shape& s, const uint8_t* dense, const float* gw, int64_t T,
+                                  const Work& ws, const PfWork& pw, hipStream_t st) {
+  if (s.l > 4 * kBlock * kPfCnChunks || s.k > kMaxK) {
+    const hipError_t e = launch_combine(s, dense, gw, T, ws, st);
+    return e != hipSuccess ? e : launch_pf_norm(s, dense, T, ws, pw, st);
+  }
+  hipLaunchKernelGGL(k_pf_combine_norm, dim3((unsigned)T), dim3(kBlock), 0, st, gw,
+                     (const int32_t*)ws.inv, (const float*)ws.eo, s.k, s.l,
+                     reinterpret_cast<const uint16_t*>(dense + s.gamma_off), s.use_norm, s.eps,
+                     pw.uh);
   return hipGetLastError();
 }
 
