@@ -37,6 +37,7 @@ notes; the ones that change arithmetic are stated where they act below.
 from __future__ import annotations
 
 import math
+import os
 from dataclasses import dataclass
 from typing import Callable
 
@@ -51,8 +52,9 @@ __all__ = [
 ]
 
 # ----------------------------------------------------------------------------------------
-# Formats.  The card states that routed experts are MXFP4 with one scale per 32 weights and
-# the port notes add "E2M1 with one E8M0 exponent per 32 columns".  The element and scale
+# Formats.  The card states that routed experts are MXFP4 with one scale per 32 weights, and
+# the port notes ("Notes from an NVFP4 port of Kimi K3", paragraph "Architecture facts") name
+# the element as E2M1 and the scale as an E8M0 byte over each run of 32 columns.  The element and scale
 # encodings are those of the OCP Microscaling Formats (MX) v1.0 specification:
 #   E2M1: 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit; exponent field 0 is
 #         subnormal (value = mantissa * 0.5).
@@ -90,7 +92,7 @@ def dequant_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
     Two codes per byte, the low nibble holding the even column (storage convention of
     the synthetic layers); one scale per 32 consecutive columns of a row (the blocks run
-    along the input axis, "one E8M0 exponent per 32 columns")."""
+    along the input axis, as the port notes' "Architecture facts" place them)."""
     codes = np.asarray(codes)
     lut = e2m1_decode(np.arange(16))
     cols = codes.shape[-1] * 2
@@ -359,6 +361,42 @@ def _expert_from_slice(sl, i):
     return gu[i], dn[i]
 
 
+def _workers(layer: OracleLayer, workers: int | None) -> int:
+    if workers is not None:
+        return max(1, int(workers))
+    if layer._experts is not None:      # small, preloaded layers: nothing to gain
+        return 1
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _map_ordered(fn, items, workers: int):
+    """fn over items, results yielded in the order of items.  With several workers the
+    calls run in a thread pool (numpy releases the interpreter lock in its array work) with
+    the BLAS library held to one thread per call."""
+    items = list(items)
+    if workers <= 1 or len(items) <= 1:
+        for it in items:
+            yield fn(it)
+        return
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(workers) as ex:
+        # at most 2 x workers calls submitted ahead of the one being consumed: each holds
+        # one dequantised expert while it runs
+        pending = []
+        it = iter(items)
+        for x in it:
+            pending.append(ex.submit(fn, x))
+            if len(pending) >= 2 * workers:
+                break
+        while pending:
+            res = pending.pop(0).result()
+            nxt = next(it, None)
+            if nxt is not None:
+                pending.append(ex.submit(fn, nxt))
+            yield res
+
+
 @dataclass
 class Result:
     delta: np.ndarray      # [T, d] float64
@@ -372,14 +410,16 @@ class Result:
 
 
 def forward(layer: OracleLayer, x_bf16: np.ndarray, forced_idx: np.ndarray | None = None,
-            precision: str | None = None) -> Result:
+            precision: str | None = None, workers: int | None = None) -> Result:
     """The layer forward for tokens x [T, d] (bf16 bit patterns or float64 values).
 
     The routed sum is organised as the block card's `moe_infer` does it: assignments are
     grouped by expert, each expert runs once on the tokens that chose it, and each result
     is weighted by its G and added into its token's sum.  `forced_idx` replaces the
     selection (used for tokens whose top-k margin is a near tie).  `precision` is a
-    profile of PRECISIONS (default: the layer config's `precision`, else "fp32")."""
+    profile of PRECISIONS (default: the layer config's `precision`, else "fp32").
+    `workers`: threads that evaluate experts side by side (default: one per host core for
+    layers whose experts are dequantised on demand, else 1); the result is the same."""
     cfg = layer.cfg
     precision = precision or getattr(cfg, "precision", "fp32")
     if precision not in PRECISIONS:
@@ -397,11 +437,17 @@ def forward(layer: OracleLayer, x_bf16: np.ndarray, forced_idx: np.ndarray | Non
     u = np.zeros((T, lat), np.float64)
     act = lambda g, v: _act(cfg, g, v)  # noqa: E731
     flat = idx.reshape(-1)
-    for e in np.unique(flat):
+
+    def run_expert(e):
         tj = np.nonzero(flat == e)[0]
         t_rows, j_cols = tj // cfg.k, tj % cfg.k
         w_gu, w_dn = layer.expert(int(e))
-        out = glu(xe[t_rows], w_gu, w_dn, act, q8)
+        return t_rows, j_cols, glu(xe[t_rows], w_gu, w_dn, act, q8)
+
+    # The experts' outputs may be evaluated concurrently (each is a pure function of its
+    # expert and rows); they are added into the sums one expert at a time in increasing
+    # expert order either way, so the result does not depend on `workers`.
+    for t_rows, j_cols, out in _map_ordered(run_expert, np.unique(flat), _workers(layer, workers)):
         u[t_rows] += G[t_rows, j_cols][:, None] * out   # one (t, e) pair per token at most
 
     if cfg.l:

@@ -9,6 +9,7 @@ Bars (restating the layer's acceptance rule):
   - Delta: relative L2 error <= 2e-3 and max abs error <= 1e-2 * rms(Delta_oracle).
 """
 import functools
+import time
 
 import numpy as np
 import pytest
@@ -91,11 +92,16 @@ def by_expert(idx, w):
     return np.take_along_axis(idx, o, 1), np.take_along_axis(w, o, 1)
 
 
-def check(cfg, x, delta, idx, w, rows=None):
-    """Compare GPU outputs for tokens `rows` of x against the oracle; returns error stats."""
+def check(cfg, x, delta, idx, w, rows=None, precision=None, ref=None, bars=True):
+    """Compare GPU outputs for tokens `rows` of x against the oracle in `precision` (the
+    layer's own profile by default; `ref`, when given, is that oracle's result for those
+    rows).  Asserts the index rule, the gate weights and, with `bars`, the Delta bars.
+    Returns (rel-L2, max-abs / rms, the oracle's result)."""
     OL = oracle_layer(cfg)
     rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
-    ref = O.forward(OL, x[rows])
+    t0 = time.perf_counter()
+    if ref is None:
+        ref = O.forward(OL, x[rows], precision=precision)
     near = ref.margin < MARGIN
     kap = O.selection_kappa(O.router_scores(O.bf16_to_f64(x[rows]), OL.router), OL.bias, cfg.k)
     assert_routing(idx[rows], ref.idx, kap, ref.margin)
@@ -105,17 +111,19 @@ def check(cfg, x, delta, idx, w, rows=None):
     assert np.max(np.abs(gw[same] - rg[same]), initial=0.0) <= 1e-6
     ref_delta = ref.delta.copy()
     if np.any(~same):   # near ties resolved differently: compare with the GPU's selection
-        log(f"near-tie tokens {rows[~same].tolist()} margins {ref.margin[~same].tolist()}")
-        forced = O.forward(OL, x[rows][~same], forced_idx=idx[rows][~same])
+        log(f"near-tie tokens {rows[~same].tolist()[:16]} margins {ref.margin[~same].tolist()[:16]}")
+        forced = O.forward(OL, x[rows][~same], forced_idx=idx[rows][~same], precision=precision)
         ref_delta[~same] = forced.delta
     err = delta[rows] - ref_delta
     rel = np.linalg.norm(err) / np.linalg.norm(ref_delta)
     rms = np.sqrt(np.mean(ref_delta ** 2))
     mx = np.max(np.abs(err))
-    log(f"{cfg.name}: tokens {len(rows)} rel-L2 {rel:.3e} max-abs/rms {mx / rms:.3e} "
-        f"near-ties {int(near.sum())}")
-    assert rel <= REL_L2
-    assert mx <= MAX_ABS_RMS * rms
+    log(f"{cfg.name} [oracle {precision or cfg.precision}]: tokens {len(rows)} rel-L2 {rel:.3e} "
+        f"max-abs/rms {mx / rms:.3e} near-ties {int(near.sum())} "
+        f"({time.perf_counter() - t0:.0f} s on the host)")
+    if bars:
+        assert rel <= REL_L2
+        assert mx <= MAX_ABS_RMS * rms
     return rel, mx / rms, ref
 
 
@@ -161,6 +169,23 @@ def test_ragged_widths_and_expert_count():
     lay, _ = device_layer(cfg)
     x = synth.tokens(cfg)
     check(cfg, x, *run(lay, x))
+
+
+def test_ragged_router_tiles_at_600_tokens():
+    """From 512 tokens on, the token-tiled router gives each wavefront two tile rows.  Here
+    70 experts fill 5 of the 8 tile rows of its one group (the dead rows read tile row 0
+    and are not written), and d = 1800 gives two logit planes whose last K-step is partial.
+    Indices of every token through moe_route and through the forward (they must agree),
+    and Delta of every token against the oracle."""
+    cfg = RAGGED.with_(name="ragged_wide_router", d=1800, tokens=600)
+    lay, _ = device_layer(cfg)
+    x = synth.tokens(cfg)
+    ri, rw = lay.route(to_dev(x))
+    torch.cuda.synchronize()
+    delta, idx, w = run(lay, x)
+    assert np.array_equal(ri.cpu().numpy(), idx)
+    assert np.array_equal(rw.cpu().numpy().astype(np.float64), w)
+    check(cfg, x, delta, idx, w)
 
 
 def test_all_experts_selected():
@@ -219,18 +244,16 @@ def test_k3_decode_b1_layer():
         assert rel < 1e-4
 
 
-def test_k3_decode_b64_sampled_tokens():
+def test_k3_decode_b64_all_tokens():
+    """The K3 layer at 64 tokens under near-uniform routing (about 600 distinct experts,
+    units of one or two positions): indices, weights and Delta of every token."""
     cfg = synth.K3_DECODE_B1
     lay, _ = k3_layer()
     x = synth.tokens(cfg, batch=100, T=64)
     delta, idx, w = run(lay, x)
-    OL = oracle_layer(cfg)
-    # routing of all 64 tokens from the oracle's router alone
-    s = O.router_scores(O.bf16_to_f64(x), OL.router)
-    ridx, G, margin = O.select_and_weight(s, OL.bias, cfg.k)
-    assert_routing(idx, ridx, O.selection_kappa(s, OL.bias, cfg.k), margin)
-    # full Delta on a sample of tokens (each costs 16 expert dequantisations on the CPU)
-    check(cfg, x, delta, idx, w, rows=[0, 21, 63])
+    log(f"[k3 b64] distinct experts {len(np.unique(idx))}")
+    rel, _, _ = check(cfg, x, delta, idx, w)
+    assert rel < 1e-4
     # per-token independence: the same token alone gives the same Delta bits
     d1, i1, w1 = run(lay, x[21:22])
     assert np.array_equal(i1[0], idx[21]) and np.array_equal(d1[0], delta[21])
@@ -238,7 +261,8 @@ def test_k3_decode_b64_sampled_tokens():
 
 def test_k3_decode_b64_zipf_layer():
     """The Zipf-loaded B=64 layer: two experts take every token, so their 64 positions
-    are split over several units of the expert launches, next to many single-token units."""
+    are split over several units of the expert launches, next to many single-token units.
+    Indices, weights and Delta of every token."""
     cfg = synth.K3_DECODE_B64_ZIPF
     lay, _ = device_layer(cfg)
     x = synth.tokens(cfg, batch=1000)
@@ -251,7 +275,8 @@ def test_k3_decode_b64_zipf_layer():
     load = np.bincount(idx.reshape(-1), minlength=cfg.E)
     assert int((load == x.shape[0]).sum()) == 2
     log(f"[k3 zipf] distinct experts {int((load > 0).sum())}")
-    check(cfg, x, delta, idx, w, rows=[0, 31, 63])
+    rel, _, _ = check(cfg, x, delta, idx, w)      # every token
+    assert rel < 1e-4
     d1, i1, w1 = run(lay, x[31:32])
     assert np.array_equal(i1[0], idx[31]) and np.array_equal(d1[0], delta[31])
 
@@ -329,27 +354,41 @@ def test_mx8_is_deterministic_and_token_independent():
     assert torch.equal(one[1][0], a[1][40]) and torch.equal(one[0][0], a[0][40])
 
 
-def test_k3_prefill_8192_sampled_tokens():
-    """The K3 layer at prefill size in the mx8 profile: every token's indices from the
-    oracle router, Delta of sampled tokens from the oracle."""
+def test_k3_prefill_8192_all_tokens_both_profiles():
+    """The K3 layer at prefill size, every one of the 8192 tokens (all 86 token tiles of the
+    dense products, every unit of the expert launches):
+      - the mx8 launches against the oracle in the mx8 profile (the bars);
+      - the fp32 launches (token-tiled) on the same packed weights against the plain
+        oracle (the bars, unmodified);
+      - informational: the mx8 Delta against the plain oracle (the cost of the declared
+        MXFP8 / bf16 rounding points)."""
     cfg = synth.K3_PREFILL_8K
     lay, _ = device_layer(cfg)
     x = synth.tokens(cfg, batch=0)
-    log(f"[k3 prefill] T={x.shape[0]}")
+    log(f"[k3 prefill] T={x.shape[0]} mx8 launches")
     delta, idx, w = run(lay, x)
-    OL = oracle_layer(cfg)
-    s = O.router_scores(O.bf16_to_f64(x), OL.router)
-    ridx, G, margin = O.select_and_weight(s, OL.bias, cfg.k)
-    log(f"[k3 prefill] near-tie tokens {int((margin < MARGIN).sum())}")
-    assert_routing(idx, ridx, O.selection_kappa(s, OL.bias, cfg.k), margin)
     assert np.all(np.isfinite(delta))
-    rel, mxr, _ = check(cfg, x, delta, idx, w, rows=[0, 4097, 8191])
+    rel, mxr, _ = check(cfg, x, delta, idx, w)
     assert rel < 1e-3
+    # the same layer through the fp32 launches (only the precision field differs)
+    lay32 = moe.Layer(moe.config_from(cfg.with_(precision="fp32")), lay.dense, lay.bias, lay.experts)
+    log("[k3 prefill] fp32 launches")
+    d32, i32, w32 = run(lay32, x)
+    del lay32
+    rel32, mxr32, ref32 = check(cfg, x, d32, i32, w32, precision="fp32")
+    assert rel32 < 1e-4
+    # informational: the mx8 profile's distance from the plain oracle (near-tie tokens
+    # against the oracle on the mx8 launches' own selection)
+    relq, mxq, _ = check(cfg, x, delta, idx, w, precision="fp32", ref=ref32, bars=False)
+    log(f"[k3 prefill] mx8 launches against the plain (fp32) oracle: rel-L2 {relq:.3e} "
+        f"max-abs/rms {mxq:.3e} (informational; the declared rounding points)")
+    assert relq < 0.1
 
 
-def test_k3_ep_share_sampled_tokens():
+def test_k3_ep_share_all_tokens():
     """One GPU's expert-parallel share (112 experts, about 1,170 rows each) in the mx8
-    profile: every token's indices from the oracle router, Delta of sampled tokens."""
+    profile: indices, weights and Delta of all 8192 tokens (every unit of 64 positions of
+    every expert, every token tile)."""
     cfg = synth.K3_EP_SHARE
     lay, _ = device_layer(cfg)
     x = synth.tokens(cfg, batch=0)
@@ -358,12 +397,8 @@ def test_k3_ep_share_sampled_tokens():
     counts = np.bincount(idx.reshape(-1), minlength=cfg.E)
     log(f"[ep share] rows per expert min {counts.min()} max {counts.max()}")
     assert counts.sum() == cfg.tokens * cfg.k and counts.min() > 0
-    OL = oracle_layer(cfg)
-    s = O.router_scores(O.bf16_to_f64(x), OL.router)
-    ridx, G, margin = O.select_and_weight(s, OL.bias, cfg.k)
-    assert_routing(idx, ridx, O.selection_kappa(s, OL.bias, cfg.k), margin)
     assert np.all(np.isfinite(delta))
-    rel, mxr, _ = check(cfg, x, delta, idx, w, rows=[0, 3001, 8191])
+    rel, mxr, _ = check(cfg, x, delta, idx, w)
     assert rel < 1e-3
 
 
@@ -404,18 +439,19 @@ def test_latent_layer_with_fp8_block_experts():
     assert rel < 1e-5
 
 
-def test_k2_block_1024_tokens_sampled():
+def test_k2_block_1024_all_tokens():
+    """The K2-style block at 1024 tokens under the Zipf(1.2) load: indices, weights and
+    Delta of every token (all 16 token tiles; every token also routes to the saturated
+    expert, whose 1024 positions fill 16 units of 64)."""
     cfg = synth.K2_MOE_1024_ZIPF
     lay, _ = device_layer(cfg)
     x = synth.tokens(cfg, batch=0)
     log(f"[k2] T={x.shape[0]}")
     delta, idx, w = run(lay, x)
-    OL = oracle_layer(cfg)
-    s = O.router_scores(O.bf16_to_f64(x), OL.router)
-    ridx, G, margin = O.select_and_weight(s, OL.bias, cfg.k, cfg.route_scale)
-    assert_routing(idx, ridx, O.selection_kappa(s, OL.bias, cfg.k), margin)
+    load = np.bincount(idx.reshape(-1), minlength=cfg.E)
+    assert int((load == x.shape[0]).sum()) >= 1
     assert np.all(np.isfinite(delta))
-    rel, _, _ = check(cfg, x, delta, idx, w, rows=[0, 511, 1023])
+    rel, _, _ = check(cfg, x, delta, idx, w)
     assert rel < 1e-4
     # few-token launches on the same layer: the same Delta bits for a token alone
     d1, i1, w1 = run(lay, x[511:512])
