@@ -45,7 +45,8 @@ import numpy as np
 
 __all__ = [
     "bf16_to_f64", "e2m1_decode", "e8m0_decode", "dequant_mxfp4", "E2M1_GRID",
-    "e4m3_decode", "round_e4m3", "E4M3_MAX", "quantize_mx8", "round_bf16", "PRECISIONS",
+    "e4m3_decode", "round_e4m3", "E4M3_MAX", "quantize_mx8", "mx8_ambiguous", "round_bf16",
+    "PRECISIONS",
     "dequant_fp8_block128",
     "sigmoid", "select_and_weight", "selection_kappa", "router_scores", "situ", "swiglu", "glu", "rmsnorm",
     "OracleLayer", "forward", "routed_sum_dense_mask", "Result", "dispatch", "residual_add",
@@ -157,11 +158,38 @@ def round_e4m3(y: np.ndarray) -> np.ndarray:
     return np.copysign(np.minimum(r, E4M3_MAX), y)
 
 
-def quantize_mx8(v: np.ndarray, block: int = 32):
+def _mx8_exponent(amax: np.ndarray, scale_flip: np.ndarray | None) -> np.ndarray:
+    """Block exponent X = floor(log2(amax)) - 8 (-127 for amax = 0); where `scale_flip` is set,
+    the exponent of the other side of the power of two nearest amax (see mx8_ambiguous)."""
+    X = np.where(amax > 0, _binade(amax) - 8, -127)
+    if scale_flip is not None:
+        # amax in [2^(X+8), 2^(X+9)): the nearer end decides which side is the other one
+        upper = amax >= np.ldexp(np.sqrt(2.0), (X + 8).astype(np.int64))
+        X = np.where(np.asarray(scale_flip, bool) & (amax > 0), np.where(upper, X + 1, X - 1), X)
+    return np.clip(X, -127, 127)
+
+
+def _e4m3_neighbours(y: np.ndarray):
+    """The two E4M3 magnitudes around |y| (lo <= |y| < hi, spaced by the quantum of |y|'s
+    binade; subnormal spacing 2^-9 below 2^-6)."""
+    a = np.abs(y)
+    quantum = np.ldexp(1.0, np.maximum(_binade(a), -6) - 3)
+    lo = np.floor(a / quantum) * quantum
+    return lo, lo + quantum
+
+
+def quantize_mx8(v: np.ndarray, block: int = 32, flip: np.ndarray | None = None,
+                 scale_flip: np.ndarray | None = None):
     """MXFP8 (E4M3 elements, one E8M0 scale per `block` values along the last axis), by the
     OCP MX v1.0 conversion: X = floor(log2(max |v|)) - 8 per block (8 is the largest
     exponent of E4M3), -127 for an all-zero block, clamped to the E8M0 range; elements
     are v / 2^X rounded to E4M3 (round_e4m3).
+
+    `scale_flip` (bool per block) and `flip` (bool per element) take the other valid decision
+    where a value sits on a decision boundary (mx8_ambiguous): the block exponent of the other
+    side of the nearest power of two, or the other of the element's two E4M3 neighbours
+    (never past 448).  Both are correct conversions of a value known only to the accuracy
+    with which it was computed.
 
     Returns (dequantised values, E4M3 element values, scale bytes X + 127)."""
     v = np.asarray(v, dtype=np.float64)
@@ -170,11 +198,39 @@ def quantize_mx8(v: np.ndarray, block: int = 32):
         raise ValueError("the last axis must be a multiple of the block size")
     vb = v.reshape(shp[:-1] + (shp[-1] // block, block))
     amax = np.max(np.abs(vb), axis=-1)
-    X = np.where(amax > 0, _binade(amax) - 8, -127)
-    X = np.clip(X, -127, 127)
-    q = round_e4m3(vb * np.ldexp(1.0, -X)[..., None])
+    X = _mx8_exponent(amax, scale_flip)
+    y = vb * np.ldexp(1.0, -X)[..., None]
+    q = round_e4m3(y)
+    if flip is not None:
+        lo, hi = _e4m3_neighbours(y)
+        other = np.copysign(np.where(np.abs(q) == lo, hi, lo), y)
+        take = np.asarray(flip, bool).reshape(q.shape) & (hi <= E4M3_MAX)
+        q = np.where(take, other, q)
     deq = q * np.ldexp(1.0, X)[..., None]
     return deq.reshape(shp), q.reshape(shp), (X + 127).astype(np.uint8)
+
+
+def mx8_ambiguous(v: np.ndarray, eta: float, block: int = 32, scale_flip: np.ndarray | None = None):
+    """Where the MXFP8 conversion of v takes a decision on a boundary, to within eta:
+      - blocks whose amax lies within a relative eta of a power of two (the block exponent
+        could fall on either side);
+      - elements whose scaled value lies within eta * (the block's largest scaled magnitude)
+        of the midpoint of its two E4M3 neighbours (it could round either way), with the
+        block exponents of `scale_flip` applied.
+    A value computed with an error below those distances may legitimately convert to either
+    decision.  Returns (element mask, block mask)."""
+    v = np.asarray(v, dtype=np.float64)
+    shp = v.shape
+    vb = v.reshape(shp[:-1] + (shp[-1] // block, block))
+    amax = np.max(np.abs(vb), axis=-1)
+    p2 = np.ldexp(1.0, np.round(np.log2(np.where(amax > 0, amax, 1.0))).astype(np.int64))
+    blk = (amax > 0) & (np.abs(amax / p2 - 1.0) <= eta)
+    X = _mx8_exponent(amax, scale_flip)
+    y = vb * np.ldexp(1.0, -X)[..., None]
+    lo, hi = _e4m3_neighbours(y)
+    ymax = (amax * np.ldexp(1.0, -X))[..., None]
+    el = (np.abs(np.abs(y) - 0.5 * (lo + hi)) <= eta * ymax) & (hi <= E4M3_MAX)
+    return el.reshape(shp), blk
 
 
 def round_bf16(v: np.ndarray) -> np.ndarray:
@@ -410,7 +466,8 @@ class Result:
 
 
 def forward(layer: OracleLayer, x_bf16: np.ndarray, forced_idx: np.ndarray | None = None,
-            precision: str | None = None, workers: int | None = None) -> Result:
+            precision: str | None = None, workers: int | None = None,
+            xc_flip: np.ndarray | None = None, xc_scale_flip: np.ndarray | None = None) -> Result:
     """The layer forward for tokens x [T, d] (bf16 bit patterns or float64 values).
 
     The routed sum is organised as the block card's `moe_infer` does it: assignments are
@@ -419,7 +476,10 @@ def forward(layer: OracleLayer, x_bf16: np.ndarray, forced_idx: np.ndarray | Non
     selection (used for tokens whose top-k margin is a near tie).  `precision` is a
     profile of PRECISIONS (default: the layer config's `precision`, else "fp32").
     `workers`: threads that evaluate experts side by side (default: one per host core for
-    layers whose experts are dequantised on demand, else 1); the result is the same."""
+    layers whose experts are dequantised on demand, else 1); the result is the same.
+    `xc_flip`, `xc_scale_flip` (mx8 profile): take the other valid MXFP8 decision at the
+    marked elements / blocks of x^c (quantize_mx8), for tokens whose x^c has a value on a
+    conversion boundary (mx8_ambiguous), as forced routing does for top-k near ties."""
     cfg = layer.cfg
     precision = precision or getattr(cfg, "precision", "fp32")
     if precision not in PRECISIONS:
@@ -432,7 +492,7 @@ def forward(layer: OracleLayer, x_bf16: np.ndarray, forced_idx: np.ndarray | Non
     idx, G, margin = select_and_weight(s, layer.bias, cfg.k, cfg.route_scale, forced_idx)
 
     xc = x @ layer.w_down_latent.T if cfg.l else x
-    xe = q8(xc) if mx8 else xc      # the experts' input
+    xe = quantize_mx8(xc, flip=xc_flip, scale_flip=xc_scale_flip)[0] if mx8 else xc  # the experts' input
     lat = xc.shape[1]
     u = np.zeros((T, lat), np.float64)
     act = lambda g, v: _act(cfg, g, v)  # noqa: E731

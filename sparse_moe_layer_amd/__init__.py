@@ -387,4 +387,12 @@ class Layer:
             n = int(np.prod(shp))
             dt = torch.int32 if name in ("ctrl", "perm", "inv", "counts", "offsets") else torch.float32
             out[name] = ws[off[name]: off[name] + 4 * n].view(dt).view(shp)
+        if c.precision == PREC["mx8"]:
+            # the experts' input x^c as MXFP8: E4M3 codes [T][128 ks] and E8M0 scale bytes
+            # [T][4 ks] (K-steps of 128 columns, padded), the first parts of slot [7]
+            ks = -(-c.d_latent // 128)
+            o = off["hl"]
+            out["xq"] = ws[o: o + T * 128 * ks].view(T, 128 * ks)
+            o += (T * 128 * ks + 255) & ~255
+            out["xs"] = ws[o: o + T * 4 * ks].view(T, 4 * ks)
         return out

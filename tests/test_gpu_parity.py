@@ -24,6 +24,10 @@ pytestmark = pytest.mark.gpu
 REL_L2 = 2e-3
 MAX_ABS_RMS = 1e-2
 MARGIN = 1e-5
+# MXFP8 decisions on a boundary: the GPU's x^c conversion may differ from the oracle's only
+# where the oracle's value lies within MX8_ETA (relative to the block maximum) of an E4M3
+# midpoint, or its block maximum within MX8_ETA of a power of two (O.mx8_ambiguous)
+MX8_ETA = 1e-4
 DEV = torch.device("cuda:0")
 
 TINY = synth.LayerConfig(name="tiny_mxfp4", d=64, l=32, E=8, k=2, m=32, ms=64, tokens=5,
@@ -92,13 +96,47 @@ def by_expert(idx, w):
     return np.take_along_axis(idx, o, 1), np.take_along_axis(w, o, 1)
 
 
-def check(cfg, x, delta, idx, w, rows=None, precision=None, ref=None, bars=True):
+def gpu_xc_codes(lay, T):
+    """The MXFP8 codes and scale bytes of x^c that the last mx8 forward of `lay` left in its
+    workspace (numpy uint8 [T, 128 ks], [T, 4 ks])."""
+    inter = lay.intermediates(T)
+    return inter["xq"].cpu().numpy(), inter["xs"].cpu().numpy()
+
+
+def mx8_decisions(xc, xq, xs):
+    """The GPU's MXFP8 decisions on x^c against the oracle's (x^c in float64, [T, l]): block
+    exponents and element codes must agree except where the oracle marks the decision as on
+    a boundary; returns (element mask, block mask) of the other decisions the GPU took."""
+    l = xc.shape[1]
+    gq = O.e4m3_decode(xq[:, :l])
+    gs = xs[:, : l // 32]
+    _, _, osb = O.quantize_mx8(xc)
+    _, blk_amb = O.mx8_ambiguous(xc, MX8_ETA)
+    sflip = gs != osb
+    assert not np.any(sflip & ~blk_amb), \
+        f"x^c block exponents differ away from a power of two on tokens {np.nonzero((sflip & ~blk_amb).any(1))[0][:8]}"
+    _, oq, _ = O.quantize_mx8(xc, scale_flip=sflip)
+    el_amb, _ = O.mx8_ambiguous(xc, MX8_ETA, scale_flip=sflip)
+    eflip = gq != oq
+    assert not np.any(eflip & ~el_amb), \
+        f"x^c codes differ away from an E4M3 midpoint on tokens {np.nonzero((eflip & ~el_amb).any(1))[0][:8]}"
+    log(f"x^c MXFP8 decisions on a boundary taken the other way: {int(eflip.sum())} codes, "
+        f"{int(sflip.sum())} block exponents, on {int((eflip.any(1) | sflip.any(1)).sum())} tokens "
+        f"(oracle-marked boundary values: {int(el_amb.sum())} codes, {int(blk_amb.sum())} blocks)")
+    return eflip, sflip
+
+
+def check(cfg, x, delta, idx, w, rows=None, precision=None, ref=None, bars=True, xcq=None):
     """Compare GPU outputs for tokens `rows` of x against the oracle in `precision` (the
     layer's own profile by default; `ref`, when given, is that oracle's result for those
     rows).  Asserts the index rule, the gate weights and, with `bars`, the Delta bars.
+    xcq: the GPU's MXFP8 x^c (codes, scale bytes) for the rows, in the mx8 profile: tokens on
+    which the GPU took the other valid conversion decision at a boundary are compared with
+    the oracle taking that decision too (as near-tie tokens are with forced routing).
     Returns (rel-L2, max-abs / rms, the oracle's result)."""
     OL = oracle_layer(cfg)
     rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
+    prof = precision or cfg.precision
     t0 = time.perf_counter()
     if ref is None:
         ref = O.forward(OL, x[rows], precision=precision)
@@ -110,20 +148,29 @@ def check(cfg, x, delta, idx, w, rows=None, precision=None, ref=None, bars=True)
     same = np.all(gi == ri, axis=1)
     assert np.max(np.abs(gw[same] - rg[same]), initial=0.0) <= 1e-6
     ref_delta = ref.delta.copy()
-    if np.any(~same):   # near ties resolved differently: compare with the GPU's selection
+    redo = ~same
+    eflip = sflip = None
+    if prof == "mx8" and xcq is not None:
+        eflip, sflip = mx8_decisions(ref.xc, xcq[0][rows], xcq[1][rows])
+        redo = redo | eflip.any(1) | sflip.any(1)
+    if np.any(~same):
         log(f"near-tie tokens {rows[~same].tolist()[:16]} margins {ref.margin[~same].tolist()[:16]}")
-        forced = O.forward(OL, x[rows][~same], forced_idx=idx[rows][~same], precision=precision)
-        ref_delta[~same] = forced.delta
+    if np.any(redo):   # the oracle on the GPU's selection and boundary decisions
+        forced = O.forward(OL, x[rows][redo], forced_idx=idx[rows][redo], precision=precision,
+                           xc_flip=None if eflip is None else eflip[redo],
+                           xc_scale_flip=None if sflip is None else sflip[redo])
+        ref_delta[redo] = forced.delta
     err = delta[rows] - ref_delta
     rel = np.linalg.norm(err) / np.linalg.norm(ref_delta)
     rms = np.sqrt(np.mean(ref_delta ** 2))
     mx = np.max(np.abs(err))
-    log(f"{cfg.name} [oracle {precision or cfg.precision}]: tokens {len(rows)} rel-L2 {rel:.3e} "
+    log(f"{cfg.name} [oracle {prof}]: tokens {len(rows)} rel-L2 {rel:.3e} "
         f"max-abs/rms {mx / rms:.3e} near-ties {int(near.sum())} "
         f"({time.perf_counter() - t0:.0f} s on the host)")
     if bars:
         assert rel <= REL_L2
-        assert mx <= MAX_ABS_RMS * rms
+        assert mx <= MAX_ABS_RMS * rms, \
+            f"max-abs/rms {mx / rms:.3e} on token {rows[np.argmax(np.max(np.abs(err), 1))]}"
     return rel, mx / rms, ref
 
 
@@ -325,13 +372,15 @@ RAGGED_MX8 = RAGGED.with_(name="ragged_mx8", precision="mx8")
 def test_mx8_tiny_token_counts(T):
     lay, _ = device_layer(TINY_MX8)
     x = synth.tokens(TINY_MX8, batch=T, T=T)
-    check(TINY_MX8, x, *run(lay, x))
+    out = run(lay, x)
+    check(TINY_MX8, x, *out, xcq=gpu_xc_codes(lay, T))
 
 
 def test_mx8_ragged_widths_and_expert_count():
     lay, _ = device_layer(RAGGED_MX8)
     x = synth.tokens(RAGGED_MX8)
-    check(RAGGED_MX8, x, *run(lay, x))
+    out = run(lay, x)
+    check(RAGGED_MX8, x, *out, xcq=gpu_xc_codes(lay, x.shape[0]))
 
 
 @pytest.mark.parametrize("variant", ["swiglu", "no_norm", "no_shared"])
@@ -340,7 +389,8 @@ def test_mx8_layer_variants(variant):
     cfg = TINY_MX8.with_(name=f"tiny_mx8_{variant}", tokens=20, **kw)
     lay, _ = device_layer(cfg)
     x = synth.tokens(cfg)
-    check(cfg, x, *run(lay, x))
+    out = run(lay, x)
+    check(cfg, x, *out, xcq=gpu_xc_codes(lay, x.shape[0]))
 
 
 def test_mx8_is_deterministic_and_token_independent():
@@ -368,7 +418,8 @@ def test_k3_prefill_8192_all_tokens_both_profiles():
     log(f"[k3 prefill] T={x.shape[0]} mx8 launches")
     delta, idx, w = run(lay, x)
     assert np.all(np.isfinite(delta))
-    rel, mxr, _ = check(cfg, x, delta, idx, w)
+    xcq = gpu_xc_codes(lay, x.shape[0])
+    rel, mxr, _ = check(cfg, x, delta, idx, w, xcq=xcq)
     assert rel < 1e-3
     # the same layer through the fp32 launches (only the precision field differs)
     lay32 = moe.Layer(moe.config_from(cfg.with_(precision="fp32")), lay.dense, lay.bias, lay.experts)
@@ -398,7 +449,7 @@ def test_k3_ep_share_all_tokens():
     log(f"[ep share] rows per expert min {counts.min()} max {counts.max()}")
     assert counts.sum() == cfg.tokens * cfg.k and counts.min() > 0
     assert np.all(np.isfinite(delta))
-    rel, mxr, _ = check(cfg, x, delta, idx, w)
+    rel, mxr, _ = check(cfg, x, delta, idx, w, xcq=gpu_xc_codes(lay, x.shape[0]))
     assert rel < 1e-3
 
 

@@ -105,7 +105,8 @@ def test_mx8_profile_inserts_only_its_declared_points(monkeypatch):
     L = O.OracleLayer.from_synth(cfg)
     x = synth.tokens(cfg)
     ref = O.forward(L, x, precision="fp32")
-    monkeypatch.setattr(OM, "quantize_mx8", lambda v, block=32: (np.asarray(v, np.float64), None, None))
+    monkeypatch.setattr(OM, "quantize_mx8", lambda v, block=32, flip=None, scale_flip=None:
+                        (np.asarray(v, np.float64), None, None))
     monkeypatch.setattr(OM, "round_bf16", lambda v: np.asarray(v, np.float64))
     same = O.forward(L, x, precision="mx8")
     assert np.array_equal(same.delta, ref.delta)
@@ -185,3 +186,73 @@ def test_mx8_moves_delta_by_the_expected_quantisation_noise():
     # E4M3 keeps 4 significant bits: each converted value moves by about 2^-5 relative
     # (uniform rounding error, rms ~ 2^-4 / sqrt(12) x the element), diluted by the sums
     assert 3e-3 < rel < 6e-2, rel
+
+
+# ---- decisions on a conversion boundary (the other valid rounding) ---------------------------
+# A value computed to fp32 accuracy that lies within that accuracy of an MX conversion boundary
+# may convert either way; the oracle can take the other decision where it marks one.
+
+def test_mx8_flips_off_change_nothing():
+    v = np.random.default_rng(7).normal(size=(9, 96)) * 3.0
+    base = O.quantize_mx8(v)
+    off = O.quantize_mx8(v, flip=np.zeros(v.shape, bool), scale_flip=np.zeros((9, 3), bool))
+    for a, b in zip(base, off):
+        assert np.array_equal(a, b)
+
+
+def test_mx8_scale_flip_on_hand_computed_blocks():
+    # amax just above 4 = 2^2: exponent 2 - 8 = -6 (byte 121); the other side is -7 (byte 120),
+    # where 4.000000004 / 2^-7 = 512.0000005 saturates to 448 and 1.0 / 2^-7 = 128 exactly
+    b = np.zeros((1, 32)); b[0, 0] = 4 * (1 + 1e-9); b[0, 1] = 1.0
+    _, q0, s0 = O.quantize_mx8(b)
+    _, q1, s1 = O.quantize_mx8(b, scale_flip=np.array([[True]]))
+    assert s0[0, 0] == 121 and s1[0, 0] == 120
+    assert q0[0, 0] == 256.0 and q0[0, 1] == 64.0
+    assert q1[0, 0] == 448.0 and q1[0, 1] == 128.0
+    # amax just below 8 = 2^3: exponent 2 - 8 = -6; the other side is -5
+    c = np.zeros((1, 32)); c[0, 0] = 8 * (1 - 1e-9)
+    assert O.quantize_mx8(c)[2][0, 0] == 121
+    assert O.quantize_mx8(c, scale_flip=np.array([[True]]))[2][0, 0] == 122
+    # both blocks are marked ambiguous at eta = 1e-6; a block with amax 5 is not
+    d = np.zeros((1, 32)); d[0, 0] = 5.0
+    for blk, want in ((b, True), (c, True), (d, False)):
+        assert O.mx8_ambiguous(blk, 1e-6)[1][0, 0] == want
+
+
+def test_mx8_element_flip_takes_the_other_neighbour():
+    # block amax 300 (exponent 8 - 8 = 0; 300 itself is 4 from the midpoint 304 of 288 and
+    # 320): 1.0625 is the midpoint of 1.0 and 1.125 (quantum 1/8); just above it rounds up,
+    # the other decision is 1.0; 40.5 (quantum 4 in [32, 64)) is 0.375 quanta from the
+    # midpoint 42 and is not marked at eta = 1e-6
+    e = np.zeros((1, 32)); e[0, 0] = 300.0; e[0, 1] = 1.0625 * (1 + 1e-7); e[0, 2] = 40.5
+    flip = np.zeros((1, 32), bool); flip[0, 1] = True
+    assert O.quantize_mx8(e)[1][0, 1] == 1.125
+    assert O.quantize_mx8(e, flip=flip)[1][0, 1] == 1.0
+    el, blk = O.mx8_ambiguous(e, 1e-6)
+    assert el[0, 1] and not el[0, 2] and not el[0, 0] and not blk[0, 0]
+    # a subnormal midpoint: 2.5 * 2^-9 between 2 and 3 * 2^-9 (ties to even: 2 * 2^-9)
+    s = np.zeros((1, 32)); s[0, 0] = 300.0; s[0, 1] = 2.5 * 2.0 ** -9
+    f1 = np.zeros((1, 32), bool); f1[0, 1] = True
+    assert O.quantize_mx8(s)[1][0, 1] == 2 * 2.0 ** -9
+    assert O.quantize_mx8(s, flip=f1)[1][0, 1] == 3 * 2.0 ** -9
+
+
+def test_mx8_every_flip_is_the_other_neighbour_and_never_past_448():
+    rng = np.random.default_rng(11)
+    v = rng.normal(size=(64, 128)) * np.exp(rng.normal(size=(64, 1)))
+    _, q, sb = O.quantize_mx8(v)
+    _, qf, sbf = O.quantize_mx8(v, flip=np.ones(v.shape, bool))
+    assert np.array_equal(sb, sbf)
+    y = (v.reshape(64, 4, 32) * np.ldexp(1.0, 127 - sb.astype(np.int64))[..., None]).reshape(v.shape)
+    # brute force: the two representable E4M3 values bracketing |y|
+    grid = O.e4m3_decode(np.arange(0, 0x7F))
+    hi_i = np.searchsorted(grid, np.abs(y), side="right")
+    lo = grid[hi_i - 1]
+    hi = np.where(hi_i < len(grid), grid[np.minimum(hi_i, len(grid) - 1)], np.inf)
+    aq, aqf = np.abs(q), np.abs(qf)
+    inside = hi <= 448.0
+    assert np.all(np.isin(aq[inside], [0.0]) | (aq[inside] == lo[inside]) | (aq[inside] == hi[inside]))
+    assert np.all((aqf[inside] == lo[inside]) | (aqf[inside] == hi[inside]))
+    assert np.all(aqf[inside] != aq[inside])
+    assert np.all(aqf <= 448.0) and np.array_equal(qf[~inside], q[~inside])
+    assert np.all(np.sign(qf[qf != 0]) == np.sign(y[qf != 0]))
