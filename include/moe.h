@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef struct ihipStream_t* moe_stream_t; /* the same type as hipStream_t */
 
@@ -224,6 +224,26 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const 
                              const void* x, int64_t n_tokens, float* delta, int32_t* topk_idx,
                              float* topk_w, void* workspace, size_t workspace_bytes,
                              moe_stream_t stream);
+
+/* moe_layer_forward for callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops or harnesses that forbid allocation): the same launches and the
+ * same results as moe_layer_forward, with the intermediates in a buffer inside the library
+ * instead of a caller's workspace.  Each GPU the library runs on holds one such buffer of
+ * MOE_STATIC_WORKSPACE_BYTES (zero at load, kept until the process ends); the call
+ * allocates nothing and frees nothing.
+ *   - The buffer's device address is looked up once per device, on the first call with
+ *     that device current; `stream` must belong to the current device.
+ *   - Every call on one GPU shares its buffer and leaves the last call's intermediates in
+ *     it.  Nothing in it has to start at zero (each step writes what a later step reads),
+ *     but calls that overlap on one GPU (other streams, other threads) race on it and give
+ *     undefined results: serialise them.
+ *   - MOE_ERR_WORKSPACE when moe_workspace_size(cfg, n_tokens) exceeds
+ *     MOE_STATIC_WORKSPACE_BYTES (K3 shape: up to 64 tokens fit), before anything runs.
+ * Arguments, layouts and the other errors as moe_layer_forward. */
+#define MOE_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+moe_status moe_layer_forward_noalloc(const moe_config* cfg, const moe_weights* w, const float* bias,
+                                     const void* x, int64_t n_tokens, float* delta,
+                                     int32_t* topk_idx, float* topk_w, moe_stream_t stream);
 
 /* Steps of the forward, in launch order.  With few tokens (at most 4, fewer for very
  * wide d) each product stages all its activation rows at once; larger batches take

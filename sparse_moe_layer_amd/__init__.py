@@ -25,9 +25,11 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_packed_dense_size", "moe_pa
            "moe_packed_experts_size", "moe_pack_experts", "moe_workspace_size",
            "moe_workspace_layout", "moe_layer_forward",
            "moe_layer_forward_timed", "moe_layer_forward_steps", "moe_route", "moe_dispatch",
-           "moe_qb_histogram", "moe_qb_readout", "moe_layer_forward_residual")
+           "moe_qb_histogram", "moe_qb_readout", "moe_layer_forward_residual",
+           "moe_layer_forward_noalloc")
 STEPS = ("router", "in", "route", "dispatch", "expert_gu", "expert_down", "combine", "out")
-ABI_VERSION = 4
+ABI_VERSION = 5
+STATIC_WORKSPACE_BYTES = 64 << 20   # MOE_STATIC_WORKSPACE_BYTES
 
 
 class MoeConfig(ctypes.Structure):
@@ -99,6 +101,7 @@ def lib():
     L.moe_qb_readout.argtypes = [P(MoeConfig), vp, i32, vp, i64, vp, vp]
     L.moe_layer_forward_residual.argtypes = [P(MoeConfig), P(MoeWeights), vp, vp, i64, vp, vp, vp,
                                              vp, vp, vp, sz, vp]
+    L.moe_layer_forward_noalloc.argtypes = [P(MoeConfig), P(MoeWeights), vp, vp, i64, vp, vp, vp, vp]
     for f in EXPORTS[2:]:
         getattr(L, f).restype = ctypes.c_int
     if L.moe_abi_version() != ABI_VERSION:
@@ -272,6 +275,16 @@ class Layer:
                                        x.data_ptr(), T, delta.data_ptr(), idx.data_ptr(),
                                        w.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)),
                "moe_layer_forward")
+        return delta, idx, w
+
+    def forward_noalloc(self, x, delta, idx, w, stream=None):
+        """forward() through moe_layer_forward_noalloc: the intermediates in the library's
+        own per-GPU buffer (no workspace).  delta, idx, w: preallocated outputs."""
+        W = self.weights_struct()
+        _check(lib().moe_layer_forward_noalloc(ctypes.byref(self.cfg), ctypes.byref(W),
+                                               self.bias.data_ptr(), x.data_ptr(), x.shape[0],
+                                               delta.data_ptr(), idx.data_ptr(), w.data_ptr(),
+                                               _stream(stream)), "moe_layer_forward_noalloc")
         return delta, idx, w
 
     def forward_residual(self, x, residual, x_next=None, delta=None, idx=None, w=None,

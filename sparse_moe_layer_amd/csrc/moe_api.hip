@@ -2,6 +2,8 @@
 // the Stable LatentMoE FFN forward.  Declarations and the contract are in include/moe.h.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "moe.h"
 #include "moe_internal.hpp"
 
@@ -374,6 +376,51 @@ MOE_EXPORT moe_status moe_layer_forward(const moe_config* cfg, const moe_weights
                                         moe_stream_t stream) {
   return forward_impl(cfg, w, bias, x, n_tokens, delta, topk_idx, topk_w, workspace,
                       workspace_bytes, nullptr, 0, MOE_NUM_STEPS, stream);
+}
+
+// The workspace of moe_layer_forward_noalloc: one copy per GPU in the library's code object.
+// Host code never passes `scratch` itself to a kernel (on the host the name is a stand-in,
+// not a device address): the address of each device's copy comes from hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];   // device address of `scratch` per device, once looked up
+
+// The device address of `scratch` on the current device (looked up on the first call).
+moe_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_EXPORT moe_status moe_layer_forward_noalloc(const moe_config* cfg, const moe_weights* w,
+                                                const float* bias, const void* x, int64_t n_tokens,
+                                                float* delta, int32_t* topk_idx, float* topk_w,
+                                                moe_stream_t stream) {
+  Shape s;
+  moe_status st = make_shape(cfg, &s);
+  if (st != MOE_OK) return st;
+  if (n_tokens < 0) return MOE_ERR_INVALID_ARG;
+  if (n_tokens == 0) return MOE_OK;
+  size_t off[MOE_WS_NUM_SLOTS], need;
+  layout(s, n_tokens, off, &need);
+  if (need > MOE_STATIC_WORKSPACE_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != MOE_OK) return st;
+  return forward_impl(cfg, w, bias, x, n_tokens, delta, topk_idx, topk_w, ws,
+                      MOE_STATIC_WORKSPACE_BYTES, nullptr, 0, MOE_NUM_STEPS, stream);
 }
 
 MOE_EXPORT moe_status moe_layer_forward_residual(const moe_config* cfg, const moe_weights* w,
