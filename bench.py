@@ -4,10 +4,14 @@
 One step = one moe_layer_forward call (all steps of the layer) over one batch of
 synthetic tokens already resident in HBM.  Prints one JSON line.
 
-Default workload: the K3-shaped layer at decode batch 1 (d 7168, latent 3584, 896 MXFP4
-experts top-16, 3072-wide experts, merged 6144-wide shared expert).  Three copies of the
-dense weights (3 x 380 MB) and 64 distinct token batches rotate so that the 256 MB
-last-level cache cannot hold what a step reads.
+By default it measures the three configurations of the metric, each with its roofline, its
+CPU oracle baseline and a parity sample: the K3-shaped layer (d 7168, latent 3584, 896 MXFP4
+experts top-16, 3072-wide experts, merged 6144-wide shared expert) at decode batch 1 (the
+headline: `value` and the top-level fields), at decode batch 64 under a Zipf(1.0) load, and at
+prefill of 8192 tokens in the mx8 profile and in the fp32 profile (under "workloads").  Three
+copies of the dense weights and distinct token batches rotate at decode so that the 256 MB
+last-level cache cannot hold what a step reads.  Measured peaks (an HBM read stream, loops of
+each matrix-core instruction) are reported beside the published ones.
 """
 from __future__ import annotations
 
@@ -182,31 +186,6 @@ class HipEvents:
             self.h.hipEventDestroy(e)
 
 
-def measured_hbm_rates(torch, dev, gib=2, reps=5):
-    """What torch's own generic kernels reach on this GPU's HBM: a sum over `gib` GiB (read)
-    and a copy of `gib` GiB (read + write), best of `reps`, in GB/s.  Context beside the
-    nominal 8 TB/s peak that the roofline fractions use; not an achievable-peak probe."""
-    n = gib << 30
-    src = torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(1.0)
-    dst = torch.empty_like(src)
-    out = {}
-    for name, fn, nbytes in (("torch_sum_read_GBps", lambda: src.sum(), n),
-                             ("torch_copy_GBps", lambda: dst.copy_(src), 2 * n)):
-        fn()
-        best = None
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1)
-            best = ms if best is None else min(best, ms)
-        out[name] = nbytes / (best * 1e-3) / 1e9
-    del src, dst
-    return out
-
-
 def percentiles_us(durations_ms):
     import numpy as np
     d = np.asarray(durations_ms, dtype=np.float64) * 1e3
@@ -265,32 +244,149 @@ def graph_replay(layers, xs, bufs, rotate, batches, K, warmup):
             "bits_equal_eager": same}
 
 
-def cpu_baseline(cfg, dense, seconds, sample_tokens=None):
-    """The float64 CPU oracle, as it is, on a bounded sample of the same workload
-    (batches of the workload's size, or of `sample_tokens` tokens for large batches)."""
-    import numpy as np
-    import oracle
-    import synth
+# ---- measured peaks -----------------------------------------------------------------------
+
+PEAK_KINDS = {"bf16_16x16x32": 0, "bf16_32x32x16": 1, "fp8_16x16x128": 2, "fp8xfp4_16x16x128": 3,
+              "fp4_16x16x128": 4, "fp8_32x32x64": 5, "fp4_32x32x64": 6}
+
+
+def measured_peaks(torch, dev, reps=3):
+    """What this GPU reaches at all: a non-temporal HBM read stream over 4 GiB (best grid of
+    five) and loops of each matrix-core instruction with register operands (libmoe_peaks.so,
+    include/moe_peaks.h).  The roofline fractions are quoted against these and against the
+    published peaks."""
+    from sparse_moe_layer_amd import peaks as pk
+    L = pk.lib()
+    st = torch.cuda.current_stream(dev)
+    out = torch.empty(16384 * 256, dtype=torch.int32, device=dev)
+    src = torch.zeros(4 << 30, dtype=torch.uint8, device=dev)
+
+    def timed(launch):
+        best = None
+        for _ in range(reps + 1):       # the first launch warms up
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            launch()
+            e1.record(st)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        return best
+
+    read = {}
+    for grid in (1024, 2048, 4096, 8192, 16384):
+        ms = timed(lambda: pk.check(L.moe_peak_read(src.data_ptr(), src.numel(), out.data_ptr(),
+                                                          out.numel(), grid, st.cuda_stream)))
+        read[grid] = src.numel() / (ms * 1e-3) / 1e9
+    del src
+    mfma = {}
+    for name, kind in PEAK_KINDS.items():
+        flops = ctypes.c_double()
+        ms = timed(lambda: pk.check(L.moe_peak_mfma(kind, 2048, 4000, out.data_ptr(), out.numel(),
+                                                          ctypes.byref(flops), st.cuda_stream)))
+        mfma[name] = flops.value / (ms * 1e-3) / 1e12
+    torch.cuda.synchronize()
+    res = {"hbm_read_GBps": max(read.values()),
+           "hbm_read_GBps_by_grid": {str(g): round(v, 1) for g, v in read.items()},
+           "mfma_TFLOPs": {k: round(v, 1) for k, v in mfma.items()},
+           "published": {"hbm_GBps": HBM_PEAK_GBS, **{f"{k}_TFLOPs": v for k, v in MFMA_PEAK.items()}}}
+    res["by_dtype_TFLOPs"] = {"bf16": max(mfma["bf16_16x16x32"], mfma["bf16_32x32x16"]),
+                              "fp8": max(mfma["fp8_16x16x128"], mfma["fp8_32x32x64"]),
+                              "fp8xfp4": mfma["fp8xfp4_16x16x128"],
+                              "fp4": max(mfma["fp4_16x16x128"], mfma["fp4_32x32x64"])}
+    log(f"[bench] measured peaks: HBM read {res['hbm_read_GBps']:.0f} GB/s; matrix cores "
+        f"{ {k: round(v) for k, v in res['by_dtype_TFLOPs'].items()} } TFLOP/s")
+    return res
+
+
+# ---- the CPU oracle beside the GPU -----------------------------------------------------------
+
+def host_info():
+    model = "unknown"
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
-    OL = oracle.OracleLayer.from_synth(cfg, dense)
-    tb = cfg.tokens if sample_tokens is None else min(cfg.tokens, sample_tokens)
-    n, t0 = 0, time.perf_counter()
-    while True:
-        x = synth.tokens(cfg, batch=5000 + n, T=tb)
-        oracle.forward(OL, x)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or n >= 64:
-            break
-    tps = n * tb / el
-    return {"value": tps, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n} batch(es) of {tb} token(s) of the workload, {el:.1f} s, float64 numpy "
-                      f"oracle in the {getattr(cfg, 'precision', 'fp32')} profile (BLAS threads "
-                      f"{cores}), each touched expert regenerated and dequantised per batch"}
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    n = os.cpu_count() or 1
+    try:
+        n_aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n_aff = n
+    return model, n, n_aff
+
+
+def cpu_baseline(cfg, dense, x, rows, gpu, xcq=None, other_precision=None, cache=None):
+    """The float64 CPU oracle as it is, timed on the host on a bounded sample of the workload:
+    tokens `rows` of the batch x (bf16 [T, d]).  The canonical expert bytes those tokens
+    route to are generated before the clock starts; the oracle dequantises them itself inside
+    the timed forward (its own work).  Returns (cpu_baseline object, parity sample object):
+    the GPU outputs gpu = (delta, idx, w) of x against the oracle on the same tokens in the
+    workload's profile (tests/parity.py's rule, the bars reported, not asserted), and, with
+    other_precision, against the oracle in that profile too (informational)."""
+    import numpy as np
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    import parity
+    import synth
+    model, n_cpu, n_aff = host_info()
+    prof = getattr(cfg, "precision", "fp32")
+    xs = x[rows]
+    key = (cfg.seed, cfg.E, tuple(int(r) for r in rows[:4]), len(rows), x.shape[0])
+    OL0 = oracle.OracleLayer.from_synth(cfg, dense)
+    # which experts the sample routes to (the oracle's own router), their bytes generated now
+    s = oracle.router_scores(oracle.bf16_to_f64(xs), OL0.router)
+    idx0, _, _ = oracle.select_and_weight(s, OL0.bias, cfg.k, cfg.route_scale)
+    t0 = time.perf_counter()
+    slices = {int(e): synth.expert_slice(cfg, int(e), int(e) + 1) for e in np.unique(idx0)}
+    gen_s = time.perf_counter() - t0
+    OL = oracle.OracleLayer.from_synth(cfg, dense, preload=False, expert_slice=lambda c, a, b: slices[a])
+    workers = oracle.moe_oracle._workers(OL, None)
+
+    def timed(precision):
+        ck = (key, precision)
+        if cache is not None and ck in cache:
+            return cache[ck]
+        t = time.perf_counter()
+        r = oracle.forward(OL, xs, precision=precision)
+        out = (r, time.perf_counter() - t)
+        if cache is not None:
+            cache[ck] = out
+        return out
+    ref, secs = timed(prof)
+    d, i, w = (a[rows] for a in gpu)
+    qsel = None if xcq is None else (xcq[0][rows], xcq[1][rows])
+    step = int(rows[1] - rows[0]) if len(rows) > 1 else 1
+    par = {"tokens": len(rows), "rows": "every token" if step == 1 else f"one token in every {step}"}
+    try:
+        r = parity.compare(OL, xs, d, i, w, precision=prof, ref=ref, xcq=qsel, bars=False, log=log)
+        par["vs_oracle_" + prof] = {"rel_l2": r["rel_l2"], "max_abs_over_rms": r["max_abs_over_rms"],
+                                    "near_tie_tokens": r["near_tie_tokens"],
+                                    "recomputed_tokens": r["recomputed_tokens"],
+                                    "within_bars": r["rel_l2"] <= parity.REL_L2 and
+                                    r["max_abs_over_rms"] <= parity.MAX_ABS_RMS}
+    except parity.ParityError as e:
+        par["vs_oracle_" + prof] = {"error": str(e)}
+    if other_precision:
+        ref2, secs2 = timed(other_precision)
+        try:
+            r2 = parity.compare(OL, xs, d, i, w, precision=other_precision, ref=ref2, bars=False, log=log)
+            par["vs_oracle_" + other_precision] = {"rel_l2": r2["rel_l2"],
+                                                   "max_abs_over_rms": r2["max_abs_over_rms"],
+                                                   "informational": True}
+        except parity.ParityError as e:
+            par["vs_oracle_" + other_precision] = {"error": str(e)}
+    base = {"value": len(rows) / secs, "unit": "tokens/s", "cores": int(workers), "kind": "oracle",
+            "sample": f"{len(rows)} token(s) of the workload's first timed batches ({par['rows']}), "
+                      f"{secs:.1f} s: the float64 numpy oracle in the {prof} profile, experts "
+                      f"evaluated by {workers} threads (BLAS 1 thread each; the dense products "
+                      f"with BLAS on all cores); the {len(slices)} touched experts' canonical bytes "
+                      f"generated before the clock ({gen_s:.1f} s), dequantised inside it",
+            "host": {"cpu_model": model, "nproc": n_cpu, "affinity_cpus": n_aff}}
+    log(f"[bench] cpu oracle: {base['value']:.3f} tokens/s ({secs:.1f} s for {len(rows)} tokens)")
+    return base, par
 
 
 def qb_stats(layer, x, cfg, K, dev):
@@ -318,71 +414,78 @@ def qb_stats(layer, x, cfg, K, dev):
             "tokens_per_s": T / ((h_us + r_us) * 1e-6)}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="k3_latent_moe_decode_b1")
-    ap.add_argument("--rotate", type=int, default=3, help="dense weight copies rotated")
-    ap.add_argument("--batches", type=int, default=64, help="distinct token batches rotated")
-    ap.add_argument("--cpu-seconds", type=float, default=20.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="end with a 1 GiB device copy (scale for HBM byte counters)")
-    ap.add_argument("--qb-stats", action="store_true",
-                    help="also time the Quantile Balancing statistics step on the workload's "
-                         "token batch (1000 bins): adds a qb_stats object")
-    args = ap.parse_args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
-        sys.exit(2)
+DEFAULT_WORKLOADS = ("k3_latent_moe_decode_b1", "k3_latent_moe_decode_b64_zipf1.0",
+                     "k3_latent_moe_prefill_8192", "k3_latent_moe_prefill_8192_fp32")
+# per workload: (dense weight copies rotated, distinct token batches rotated, CPU-baseline sample
+# as (batches of the rotation, tokens per batch taken one every `stride`))
+ROTATION = {"k3_latent_moe_decode_b1": (3, 64), "k3_latent_moe_decode_b64_zipf1.0": (3, 16),
+            "k3_latent_moe_prefill_8192": (1, 2), "k3_latent_moe_prefill_8192_fp32": (1, 2),
+            "k2_moe_1024_zipf1.2": (3, 8), "k3_ep_share_112x1170": (1, 2)}
+CPU_SAMPLE = {"k3_latent_moe_decode_b1": (16, 1), "k3_latent_moe_decode_b64_zipf1.0": (1, 1),
+              "k3_latent_moe_prefill_8192": (1, 128), "k3_latent_moe_prefill_8192_fp32": (1, 128),
+              "k2_moe_1024_zipf1.2": (1, 16), "k3_ep_share_112x1170": (1, 128)}
 
+
+def layer_key(cfg):
+    """Workloads that differ only in name, tokens and profile share one uploaded layer."""
+    return cfg.with_(name="", tokens=0, precision="fp32")
+
+
+def run_workload(cfg, args, peaks, store, cpu_cache):
     import numpy as np
     import torch
 
     import sparse_moe_layer_amd as moe
     import synth
 
-    cfg = synth.PRESETS[args.workload]
     dev = torch.device("cuda:0")
     T = cfg.tokens
     mcfg = moe.config_from(cfg)
-    log(f"[bench] workload {cfg.name}: generating and uploading the layer")
-    t0 = time.perf_counter()
-    dense0 = synth.dense_weights(cfg)
-    chunk = 64
-    staging = {}
+    rot, nb = ROTATION.get(cfg.name, (3, 16))
+    rotate = args.rotate if args.rotate is not None else rot
+    batches = args.batches if args.batches is not None else nb
+    key = layer_key(cfg)
+    if store.get("key") != key or len(store.get("layers", [])) < rotate:
+        store.clear()
+        torch.cuda.empty_cache()
+        log(f"[bench] workload {cfg.name}: generating and uploading the layer")
+        t0 = time.perf_counter()
+        dense0 = synth.dense_weights(cfg)
+        chunk, staging = 64, {}
 
-    def slice_fn(a, b):
-        if b - a == chunk and "s" in staging:
-            return synth.expert_slice(cfg, a, b, out=staging["s"])
-        sl = synth.expert_slice(cfg, a, b)
-        if b - a == chunk:
-            staging["s"] = sl
-        return sl
-    layer0 = moe.Layer.upload(mcfg, dense0, slice_fn, cfg.E, device=dev, chunk=chunk)
-    staging.clear()
-    layers = [layer0] + [layer0.with_dense(synth.dense_weights(cfg, copy=c)) for c in range(1, args.rotate)]
-    xs = [torch.from_numpy(synth.tokens(cfg, batch=1000 + b).view(np.int16)).to(dev)
-          for b in range(args.batches)]
-    torch.cuda.synchronize()
-    log(f"[bench] layer ready in {time.perf_counter() - t0:.1f} s")
-
+        def slice_fn(a, b):
+            if b - a == chunk and "s" in staging:
+                return synth.expert_slice(cfg, a, b, out=staging["s"])
+            sl = synth.expert_slice(cfg, a, b)
+            if b - a == chunk:
+                staging["s"] = sl
+            return sl
+        l0 = moe.Layer.upload(mcfg, dense0, slice_fn, cfg.E, device=dev, chunk=chunk)
+        staging.clear()
+        store.update(key=key, dense0=dense0,
+                     layers=[l0] + [l0.with_dense(synth.dense_weights(cfg, copy=c)) for c in range(1, rotate)])
+        torch.cuda.synchronize()
+        log(f"[bench] layer ready in {time.perf_counter() - t0:.1f} s")
+    else:
+        log(f"[bench] workload {cfg.name}: the layer of the previous workload, profile "
+            f"{getattr(cfg, 'precision', 'fp32')}")
+    dense0 = store["dense0"]
+    # the uploaded weights under this workload's config (the profile may differ)
+    layers = [moe.Layer(mcfg, L.dense, L.bias, L.experts) for L in store["layers"][:rotate]]
+    xs_h = [synth.tokens(cfg, batch=1000 + b) for b in range(batches)]
+    xs = [torch.from_numpy(x.view(np.int16)).to(dev) for x in xs_h]
     delta = torch.empty((T, cfg.d), dtype=torch.float32, device=dev)
     idx = torch.empty((T, cfg.k), dtype=torch.int32, device=dev)
     gw = torch.empty((T, cfg.k), dtype=torch.float32, device=dev)
-    ws = layer0.workspace(T)
+    ws = layers[0].workspace(T)
 
     # distinct experts per batch (for the byte count of the timed steps)
     D = []
-    for b in range(args.batches):
+    for b in range(batches):
         layers[0].forward(xs[b], delta, idx, gw, ws)
         D.append(len(np.unique(idx.cpu().numpy())))
     for i in range(args.warmup):
-        layers[i % args.rotate].forward(xs[i % args.batches], delta, idx, gw, ws)
+        layers[i % rotate].forward(xs[i % batches], delta, idx, gw, ws)
     torch.cuda.synchronize()
 
     # timed region: K whole forwards back to back
@@ -390,29 +493,28 @@ def main():
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(K):
-        layers[i % args.rotate].forward(xs[i % args.batches], delta, idx, gw, ws)
+        layers[i % rotate].forward(xs[i % batches], delta, idx, gw, ws)
     e1.record()
     torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / K
-    log(f"[bench] {K} steps: {ms_step * 1e3:.1f} us/step")
-    graph = graph_replay(layers, xs, (delta, idx, gw, ws), args.rotate, args.batches, K,
-                         args.warmup)
-    graph["tokens_per_s"] = T / (graph["us_per_step"] * 1e-6)
-    log(f"[bench] hipGraph replay: {graph['us_per_step']:.1f} us/step over {K} replays; single "
-        f"replays median {graph['median_us']:.1f} (p10 {graph['p10_us']:.1f}, p90 "
-        f"{graph['p90_us']:.1f}); eager median {graph['eager']['median_us']:.1f}; "
-        f"bits equal eager: {graph['bits_equal_eager']}")
+    ms_step = e0.elapsed_time(e1) / K
+    log(f"[bench] {cfg.name}: {K} steps, {ms_step * 1e3:.1f} us/step, {T / (ms_step * 1e-3):.0f} tokens/s")
+    graph = None
+    if T <= 64:     # decode: the captured forward as a serving loop would replay it
+        graph = graph_replay(layers, xs, (delta, idx, gw, ws), rotate, batches, K, args.warmup)
+        graph["tokens_per_s"] = T / (graph["us_per_step"] * 1e-6)
+        log(f"[bench] hipGraph replay: {graph['us_per_step']:.1f} us/step over {K} replays; single "
+            f"replays median {graph['median_us']:.1f} (p10 {graph['p10_us']:.1f}, p90 "
+            f"{graph['p90_us']:.1f}); eager median {graph['eager']['median_us']:.1f}; "
+            f"bits equal eager: {graph['bits_equal_eager']}")
 
-    # per-step durations: the same forwards with in-stream events between the steps.  An
-    # event record costs a few microseconds of GPU time, so this pass only ranks the steps;
-    # the dominant step is then timed with events around it alone.
+    # per-step durations: the same forwards with in-stream events between the steps (an event
+    # record costs a few microseconds of GPU time, so this pass only ranks the steps)
     hip = HipEvents()
     nst = len(moe.STEPS)
     evs = hip.create(K * (nst + 1))
     for i in range(K):
-        layers[i % args.rotate].forward_timed(xs[i % args.batches], evs[i * (nst + 1):(i + 1) * (nst + 1)],
-                                              delta, idx, gw, ws)
+        layers[i % rotate].forward_timed(xs[i % batches], evs[i * (nst + 1):(i + 1) * (nst + 1)],
+                                         delta, idx, gw, ws)
     torch.cuda.synchronize()
     step_ms = np.zeros(nst)
     for i in range(K):
@@ -426,30 +528,148 @@ def main():
     dom = max(("router", "in", "expert_gu", "expert_down", "out"),
               key=lambda n: step_ms[moe.STEPS.index(n)])
     mx8 = getattr(cfg, "precision", "fp32") == "mx8"
-    # The dominant step alone, K launches back to back between two events.  Each launch
-    # works on the buffers of an earlier full forward; R sets of buffers (different tokens,
-    # so different experts, and different dense copies) rotate past the last-level cache.
+    # The dominant step alone, K launches back to back between two events, each on the
+    # buffers of an earlier full forward; R sets of buffers (different tokens, so different
+    # experts, and different dense copies) rotate past the last-level cache.
     si = moe.STEPS.index(dom)
-    R = 8
+    R = 8 if T <= 64 else 2
     sets = []
     for r in range(R):
         bufs = (torch.empty_like(delta), torch.empty_like(idx), torch.empty_like(gw),
                 moe.new_workspace(mcfg, T, dev))
-        layers[r % args.rotate].forward(xs[r % args.batches], *bufs[:3], workspace=bufs[3])
+        layers[r % rotate].forward(xs[r % batches], *bufs[:3], workspace=bufs[3])
         sets.append(bufs)
     for r in range(R):
-        layers[r % args.rotate].forward_steps(xs[r % args.batches], si, si + 1, *sets[r])
+        layers[r % rotate].forward_steps(xs[r % batches], si, si + 1, *sets[r])
     torch.cuda.synchronize()
     e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e2.record()
     for i in range(K):
         r = i % R
-        layers[r % args.rotate].forward_steps(xs[r % args.batches], si, si + 1, *sets[r])
+        layers[r % rotate].forward_steps(xs[r % batches], si, si + 1, *sets[r])
     e3.record()
     torch.cuda.synchronize()
     dom_s = e2.elapsed_time(e3) / K * 1e-3
     del sets
     log(f"[bench] {dom}: {dom_s * 1e6:.2f} us per launch ({K} launches back to back)")
+
+    Dm = float(np.mean([D[i % batches] for i in range(K)]))
+    ab = algorithmic_bytes(cfg, T, Dm)
+    af = algorithmic_flops(cfg, T)
+    layer_bytes = weight_bytes(cfg, Dm)
+    layer_gbs = layer_bytes / (ms_step * 1e-3) / 1e9
+    layer_tflops = sum(af.values()) / (ms_step * 1e-3) / 1e12
+    kernels = STEP_KERNELS_MX8 if mx8 else STEP_KERNELS
+    traffic = measured_traffic(cfg.name, dom, kernels)
+    # the bound of the dominant step: its algorithmic bytes at the HBM peak against its flops
+    # at the matrix-core rate of its operands (mx8 experts: the FP8 x FP4 instruction runs at
+    # the FP8 rate; everything else: bf16 operands, fp32 activations as bf16 pairs)
+    dtype_peak = "fp8" if (mx8 and dom.startswith("expert")) else "bf16"
+    t_mem = ab[dom] / (HBM_PEAK_GBS * 1e9)
+    t_mma = af[dom] / (MFMA_PEAK[dtype_peak] * 1e12)
+    meas = peaks or {}
+    if t_mma > t_mem:
+        achieved = af[dom] / dom_s / 1e12
+        mpk = meas.get("by_dtype_TFLOPs", {}).get("fp8xfp4" if dtype_peak == "fp8" else "bf16")
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved,
+                    "peak": MFMA_PEAK[dtype_peak], "unit": "TFLOP/s",
+                    "frac": achieved / MFMA_PEAK[dtype_peak],
+                    "traffic": traffic, "traffic_over_algorithmic": (traffic / ab[dom]) if traffic else None,
+                    "algorithmic_flops": af[dom], "algorithmic_bytes": ab[dom], "avg_us": dom_s * 1e6,
+                    "peak_dtype": "fp8 x fp4 (fp8 rate)" if dtype_peak == "fp8" else "bf16",
+                    "measured_peak": mpk, "frac_of_measured": (achieved / mpk) if mpk else None,
+                    "frac_of_mxfp4_peak": achieved / MFMA_PEAK["fp4"] if dtype_peak == "fp8" else None}
+    else:
+        achieved = ab[dom] / dom_s / 1e9
+        mpk = meas.get("hbm_read_GBps")
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                    "traffic": traffic, "traffic_over_algorithmic": (traffic / ab[dom]) if traffic else None,
+                    "algorithmic_bytes": ab[dom], "avg_us": dom_s * 1e6,
+                    "measured_peak": mpk, "frac_of_measured": (achieved / mpk) if mpk else None}
+    res = {
+        "value": T / (ms_step * 1e-3), "unit": "tokens/s", "ms_per_step": ms_step, "steps": K,
+        "warmup": args.warmup,
+        "dtype": "fp8xfp4+bf16" if mx8 else "f32",
+        "config": {"workload": cfg.name, "tokens_per_step": T, "d": cfg.d, "latent": cfg.l,
+                   "experts": cfg.E, "top_k": cfg.k, "expert_hidden": cfg.m,
+                   "shared_hidden": cfg.ms, "expert_weights": cfg.expert_fmt,
+                   "precision_profile": getattr(cfg, "precision", "fp32"),
+                   "dense_weight_copies": rotate, "token_batches": batches,
+                   "distinct_experts_per_step": Dm},
+        "roofline": roofline,
+        "layer": {"algorithmic_bytes": layer_bytes, "achieved_GBps": layer_gbs,
+                  "hbm_frac": layer_gbs / HBM_PEAK_GBS,
+                  "hbm_frac_of_measured": (layer_gbs / meas["hbm_read_GBps"]) if meas else None,
+                  "algorithmic_flops": sum(af.values()), "achieved_TFLOPs": layer_tflops,
+                  "steps_us_with_event_per_boundary": steps_us},
+    }
+    if graph is not None:
+        res["hipgraph"] = graph
+    if args.qb_stats:
+        res["qb_stats"] = qb_stats(layers[0], xs[0], cfg, K, dev)
+    if not args.no_cpu_baseline:
+        log(f"[bench] {cfg.name}: the CPU oracle on a sample of the workload")
+        nbat, stride = CPU_SAMPLE.get(cfg.name, (1, max(1, T // 64)))
+        # the sample's batches, each once more through the GPU (their outputs for the parity
+        # sample; the last forward's workspace holds the mx8 x^c codes)
+        xh = np.concatenate([xs_h[b] for b in range(min(nbat, batches))])
+        outs = []
+        for b in range(min(nbat, batches)):
+            d_, i_, w_ = layers[0].forward(xs[b])
+            outs.append((d_.cpu().numpy().astype(np.float64), i_.cpu().numpy(),
+                         w_.cpu().numpy().astype(np.float64)))
+        torch.cuda.synchronize()
+        gpu = tuple(np.concatenate([o[j] for o in outs]) for j in range(3))
+        xcq = None
+        if mx8 and nbat == 1:
+            inter = layers[0].intermediates(T)
+            xcq = (inter["xq"].cpu().numpy(), inter["xs"].cpu().numpy())
+        rows = np.arange(0, xh.shape[0], stride)
+        res["cpu_baseline"], res["parity_sample"] = cpu_baseline(
+            cfg, dense0, xh, rows, gpu, xcq=xcq, other_precision="fp32" if mx8 else None,
+            cache=cpu_cache)
+    del layers, xs, ws
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None,
+                    help="one workload (synth preset) instead of the default set: K3 decode B=1 "
+                         "(the headline), decode B=64 Zipf(1.0), prefill 8192 in the mx8 and "
+                         "the fp32 profiles")
+    ap.add_argument("--rotate", type=int, default=None, help="dense weight copies rotated")
+    ap.add_argument("--batches", type=int, default=None, help="distinct token batches rotated")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak probes")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with a 1 GiB device copy (scale for HBM byte counters)")
+    ap.add_argument("--qb-stats", action="store_true",
+                    help="also time the Quantile Balancing statistics step on the workload's "
+                         "token batch (1000 bins): adds a qb_stats object")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+
+    dev = torch.device("cuda:0")
+    names = [args.workload] if args.workload else list(DEFAULT_WORKLOADS)
+    peaks = None if (args.no_peaks or args.copy_calibration) else measured_peaks(torch, dev)
+    store, cpu_cache, results = {}, {}, {}
+    for name in names:
+        results[name] = run_workload(synth.PRESETS[name], args, peaks, store, cpu_cache)
+    store.clear()
+    torch.cuda.empty_cache()
     if args.copy_calibration:
         # a plain device copy of known size, for scaling HBM byte counters
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -458,67 +678,30 @@ def main():
         torch.cuda.synchronize()
         log("[bench] calibration copy: 1 GiB read + 1 GiB written")
 
-    # (not in the counter runs: their calibration is the last large device copy of the run)
-    measured = None if args.copy_calibration else measured_hbm_rates(torch, dev)
-    log(f"[bench] torch's generic kernels on the same HBM (context): {measured}")
-    Dm = float(np.mean([D[i % args.batches] for i in range(K)]))
-    ab = algorithmic_bytes(cfg, T, Dm)
-    af = algorithmic_flops(cfg, T)
-    layer_bytes = weight_bytes(cfg, Dm)
-    layer_gbs = layer_bytes / (ms_step * 1e-3) / 1e9
-    layer_tflops = sum(af.values()) / (ms_step * 1e-3) / 1e12
-    if mx8:
-        # compute-bound: the expert products on the scaled FP8 x FP4 matrix cores (they run
-        # at the FP8 rate), the dense products on bf16 ones
-        dtype_peak = "fp8" if dom.startswith("expert") else "bf16"
-        achieved = af[dom] / dom_s / 1e12
-        roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved,
-                    "peak": MFMA_PEAK[dtype_peak], "unit": "TFLOP/s",
-                    "frac": achieved / MFMA_PEAK[dtype_peak],
-                    "traffic": measured_traffic(cfg.name, dom, STEP_KERNELS_MX8),
-                    "algorithmic_flops": af[dom], "avg_us": dom_s * 1e6,
-                    "peak_dtype": "fp8 x fp4 (fp8 rate)" if dtype_peak == "fp8" else "bf16",
-                    "frac_of_mxfp4_peak": achieved / MFMA_PEAK["fp4"] if dtype_peak == "fp8" else None}
-    else:
-        achieved = ab[dom] / dom_s / 1e9
-        roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                    "traffic": measured_traffic(cfg.name, dom),
-                    "algorithmic_bytes": ab[dom], "avg_us": dom_s * 1e6}
-
+    head = results[names[0]]
     out = {
         "metric": METRIC,
-        "value": T / (ms_step * 1e-3),
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8xfp4+bf16" if mx8 else "f32",
+        "dtype": head["dtype"],
         "data": "synthetic",
-        "config": {"workload": cfg.name, "tokens_per_step": T, "d": cfg.d, "latent": cfg.l,
-                   "experts": cfg.E, "top_k": cfg.k, "expert_hidden": cfg.m,
-                   "shared_hidden": cfg.ms, "expert_weights": cfg.expert_fmt,
-                   "precision_profile": getattr(cfg, "precision", "fp32"),
-                   "dense_weight_copies": args.rotate, "token_batches": args.batches,
-                   "distinct_experts_per_step": Dm},
-        "roofline": roofline,
-        "hipgraph": graph,
-        "measured_hbm": measured,
-        "layer": {"algorithmic_bytes": layer_bytes, "achieved_GBps": layer_gbs,
-                  "hbm_frac": layer_gbs / HBM_PEAK_GBS,
-                  "algorithmic_flops": sum(af.values()), "achieved_TFLOPs": layer_tflops,
-                  "steps_us_with_event_per_boundary": steps_us},
+        "config": head["config"],
+        "roofline": head["roofline"],
     }
-    if args.qb_stats:
-        out["qb_stats"] = qb_stats(layers[0], xs[0], cfg, K, dev)
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle")
-        out["cpu_baseline"] = cpu_baseline(cfg, dense0, args.cpu_seconds,
-                                           sample_tokens=8 if T > 64 else None)
+    for k in ("cpu_baseline", "parity_sample", "hipgraph", "layer", "qb_stats"):
+        if k in head:
+            out[k] = head[k]
+    if peaks is not None:
+        out["measured_peaks"] = peaks
+    if len(names) > 1:
+        out["workloads"] = {n: results[n] for n in names[1:]}
     print(json.dumps(out), flush=True)
 
 

@@ -381,18 +381,22 @@ class OracleLayer:
         self._experts = experts   # optional fully materialised (w_gu [E,2m,K], w_down [E,K,m])
 
     @classmethod
-    def from_synth(cls, cfg, dense=None, preload: bool | None = None):
+    def from_synth(cls, cfg, dense=None, preload: bool | None = None, expert_slice=None):
+        """The layer of a `synth` config.  expert_slice(cfg, e0, e1): where the canonical
+        expert bytes come from (synth.expert_slice by default; a caller may hand over bytes
+        it generated beforehand).  The oracle dequantises them itself."""
         import synth
         dense = synth.dense_weights(cfg) if dense is None else dense
         small = cfg.E * 3 * cfg.m * (cfg.l or cfg.d) <= 64 * 1024 * 1024
         preload = small if preload is None else preload
+        source = synth.expert_slice if expert_slice is None else expert_slice
 
         def expert_fn(e):
-            return _expert_from_slice(synth.expert_slice(cfg, e, e + 1), 0)
+            return _expert_from_slice(source(cfg, e, e + 1), 0)
 
         experts = None
         if preload:
-            sl = synth.expert_slice(cfg, 0, cfg.E)
+            sl = source(cfg, 0, cfg.E)
             gu, dn = _slice_to_f64(sl)
             experts = (gu, dn)
         return cls(cfg, dense, expert_fn, experts)

@@ -17,15 +17,28 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
-    tmp = LIB + ".tmp"
+PEAKS_LIB = os.path.join(HERE, "peaks", "libmoe_peaks.so")
+
+
+def _hipcc(srcs, out, verbose):
+    tmp = out + ".tmp"
     cmd = ["/opt/rocm/bin/hipcc", *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
            "-I", os.path.join(HERE, "csrc"), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    return subprocess.Popen(cmd), tmp
+
+
+def build(verbose: bool = False) -> str:
+    """libmoe.so (the layer, csrc/*.hip) and libmoe_peaks.so (the benchmark's peak-rate
+    probes, peaks/*.hip), compiled side by side."""
+    jobs = [(_hipcc(sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip"))), LIB, verbose), LIB),
+            (_hipcc(sorted(glob.glob(os.path.join(HERE, "peaks", "*.hip"))), PEAKS_LIB, verbose),
+             PEAKS_LIB)]
+    for (proc, tmp), out in jobs:
+        if proc.wait() != 0:
+            raise subprocess.CalledProcessError(proc.returncode, "hipcc " + out)
+        os.replace(tmp, out)
     return LIB
 
 

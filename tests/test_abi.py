@@ -34,6 +34,27 @@ def test_every_declared_symbol_is_exported(L):
         assert hasattr(L, n), n
 
 
+def test_peak_probe_library_exports_its_header():
+    from sparse_moe_layer_amd import peaks
+    if not os.path.exists(peaks.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    src = open(os.path.join(ROOT, "include", "moe_peaks.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    assert names == sorted(peaks.EXPORTS)
+    P = peaks.lib()
+    for n in names:
+        assert hasattr(P, n), n
+    # argument checks happen before any launch (no GPU needed for these)
+    import ctypes
+    f = ctypes.c_double()
+    assert P.moe_peak_mfma(99, 1, 1, 16, 4096, ctypes.byref(f), None) == 1
+    assert P.moe_peak_mfma(0, 4, 1, 16, 256, ctypes.byref(f), None) == 1     # out too small
+    assert P.moe_peak_read(None, 1024, 16, 4096, 1, None) == 1
+    assert P.moe_peak_read(32, 1000, 16, 4096, 1, None) == 1                  # not 16-byte sized
+
+
 def test_version_and_status_strings(L):
     assert L.moe_abi_version() == 5 == moe.ABI_VERSION
     assert moe.status_str(0) == "MOE_OK"

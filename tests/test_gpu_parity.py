@@ -1,12 +1,8 @@
 """GPU parity: the HIP path through the C ABI against the float64 CPU oracle.
 
-Bars (restating the layer's acceptance rule):
-  - on every token whose oracle top-k margin kappa_(k) - kappa_(k+1) is >= 1e-5, the
-    oracle's set of experts, in the oracle's order wherever neighbouring kappas are
-    >= 1e-5 apart (near ties are reported, and their Delta is compared with the oracle
-    run on the GPU's own selection);
-  - gate weights within 1e-6 of the oracle's G where the indices agree;
-  - Delta: relative L2 error <= 2e-3 and max abs error <= 1e-2 * rms(Delta_oracle).
+The rule (indices on clear margins, gate weights to 1e-6, Delta within rel-L2 2e-3 and
+max-abs 1e-2 rms, near ties and MXFP8 boundary decisions compared with the oracle taking the
+GPU's choice) is implemented once in tests/parity.py.
 """
 import functools
 import time
@@ -16,18 +12,13 @@ import pytest
 import torch
 
 import oracle as O
+import parity as P
 import sparse_moe_layer_amd as moe
 import synth
 
 pytestmark = pytest.mark.gpu
 
-REL_L2 = 2e-3
-MAX_ABS_RMS = 1e-2
-MARGIN = 1e-5
-# MXFP8 decisions on a boundary: the GPU's x^c conversion may differ from the oracle's only
-# where the oracle's value lies within MX8_ETA (relative to the block maximum) of an E4M3
-# midpoint, or its block maximum within MX8_ETA of a power of two (O.mx8_ambiguous)
-MX8_ETA = 1e-4
+MARGIN = P.MARGIN
 DEV = torch.device("cuda:0")
 
 TINY = synth.LayerConfig(name="tiny_mxfp4", d=64, l=32, E=8, k=2, m=32, ms=64, tokens=5,
@@ -70,30 +61,7 @@ def run(lay, x):
 
 
 def assert_routing(idx, ridx, kap, margin):
-    """The index rule.  On every token whose margin kappa_(k) - kappa_(k+1) is >= MARGIN the
-    GPU selects the oracle's set of experts, and the oracle's expert at every rank whose
-    kappa is at least MARGIN away from both neighbours (experts whose kappas lie closer
-    than that may come out in either order).  Returns the mask of such tokens."""
-    clear = margin >= MARGIN
-    assert np.array_equal(np.sort(idx[clear], 1), np.sort(ridx[clear], 1)), \
-        "expert sets differ on clear margins"
-    k = idx.shape[1]
-    gaps = kap[:, :-1] - kap[:, 1:]                 # rank j to j + 1, j = 0..k-1
-    left = np.concatenate([np.full((len(kap), 1), np.inf), gaps[:, : k - 1]], axis=1)
-    pinned = (left >= MARGIN) & (gaps >= MARGIN)
-    bad = clear[:, None] & pinned & (idx != ridx)
-    assert not bad.any(), f"rank order differs at clear gaps on tokens {np.nonzero(bad.any(1))[0][:8]}"
-    swapped = clear & np.any(idx != ridx, axis=1)
-    if swapped.any():
-        log(f"tokens with near-equal neighbours ranked in the other order: {int(swapped.sum())}")
-    return clear
-
-
-def by_expert(idx, w):
-    """Weights reordered by expert id (for comparing tokens whose ranking differs only
-    between near-equal neighbours)."""
-    o = np.argsort(idx, axis=1)
-    return np.take_along_axis(idx, o, 1), np.take_along_axis(w, o, 1)
+    return P.routing(idx, ridx, kap, margin, log)
 
 
 def gpu_xc_codes(lay, T):
@@ -103,75 +71,16 @@ def gpu_xc_codes(lay, T):
     return inter["xq"].cpu().numpy(), inter["xs"].cpu().numpy()
 
 
-def mx8_decisions(xc, xq, xs):
-    """The GPU's MXFP8 decisions on x^c against the oracle's (x^c in float64, [T, l]): block
-    exponents and element codes must agree except where the oracle marks the decision as on
-    a boundary; returns (element mask, block mask) of the other decisions the GPU took."""
-    l = xc.shape[1]
-    gq = O.e4m3_decode(xq[:, :l])
-    gs = xs[:, : l // 32]
-    _, _, osb = O.quantize_mx8(xc)
-    _, blk_amb = O.mx8_ambiguous(xc, MX8_ETA)
-    sflip = gs != osb
-    assert not np.any(sflip & ~blk_amb), \
-        f"x^c block exponents differ away from a power of two on tokens {np.nonzero((sflip & ~blk_amb).any(1))[0][:8]}"
-    _, oq, _ = O.quantize_mx8(xc, scale_flip=sflip)
-    el_amb, _ = O.mx8_ambiguous(xc, MX8_ETA, scale_flip=sflip)
-    eflip = gq != oq
-    assert not np.any(eflip & ~el_amb), \
-        f"x^c codes differ away from an E4M3 midpoint on tokens {np.nonzero((eflip & ~el_amb).any(1))[0][:8]}"
-    log(f"x^c MXFP8 decisions on a boundary taken the other way: {int(eflip.sum())} codes, "
-        f"{int(sflip.sum())} block exponents, on {int((eflip.any(1) | sflip.any(1)).sum())} tokens "
-        f"(oracle-marked boundary values: {int(el_amb.sum())} codes, {int(blk_amb.sum())} blocks)")
-    return eflip, sflip
-
-
 def check(cfg, x, delta, idx, w, rows=None, precision=None, ref=None, bars=True, xcq=None):
     """Compare GPU outputs for tokens `rows` of x against the oracle in `precision` (the
-    layer's own profile by default; `ref`, when given, is that oracle's result for those
-    rows).  Asserts the index rule, the gate weights and, with `bars`, the Delta bars.
-    xcq: the GPU's MXFP8 x^c (codes, scale bytes) for the rows, in the mx8 profile: tokens on
-    which the GPU took the other valid conversion decision at a boundary are compared with
-    the oracle taking that decision too (as near-tie tokens are with forced routing).
-    Returns (rel-L2, max-abs / rms, the oracle's result)."""
-    OL = oracle_layer(cfg)
+    layer's own profile by default; `ref`: that oracle's result for those rows) by the rule
+    of tests/parity.py.  xcq: the GPU's MXFP8 x^c (codes, scale bytes) of all of x, in the
+    mx8 profile.  Returns (rel-L2, max-abs / rms, the oracle's result)."""
     rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
-    prof = precision or cfg.precision
-    t0 = time.perf_counter()
-    if ref is None:
-        ref = O.forward(OL, x[rows], precision=precision)
-    near = ref.margin < MARGIN
-    kap = O.selection_kappa(O.router_scores(O.bf16_to_f64(x[rows]), OL.router), OL.bias, cfg.k)
-    assert_routing(idx[rows], ref.idx, kap, ref.margin)
-    gi, gw = by_expert(idx[rows], w[rows])
-    ri, rg = by_expert(ref.idx, ref.G)
-    same = np.all(gi == ri, axis=1)
-    assert np.max(np.abs(gw[same] - rg[same]), initial=0.0) <= 1e-6
-    ref_delta = ref.delta.copy()
-    redo = ~same
-    eflip = sflip = None
-    if prof == "mx8" and xcq is not None:
-        eflip, sflip = mx8_decisions(ref.xc, xcq[0][rows], xcq[1][rows])
-        redo = redo | eflip.any(1) | sflip.any(1)
-    if np.any(~same):
-        log(f"near-tie tokens {rows[~same].tolist()[:16]} margins {ref.margin[~same].tolist()[:16]}")
-    if np.any(redo):   # the oracle on the GPU's selection and boundary decisions
-        forced = O.forward(OL, x[rows][redo], forced_idx=idx[rows][redo], precision=precision,
-                           xc_flip=None if eflip is None else eflip[redo],
-                           xc_scale_flip=None if sflip is None else sflip[redo])
-        ref_delta[redo] = forced.delta
-    err = delta[rows] - ref_delta
-    rel = np.linalg.norm(err) / np.linalg.norm(ref_delta)
-    rms = np.sqrt(np.mean(ref_delta ** 2))
-    mx = np.max(np.abs(err))
-    log(f"{cfg.name} [oracle {prof}]: tokens {len(rows)} rel-L2 {rel:.3e} "
-        f"max-abs/rms {mx / rms:.3e} near-ties {int(near.sum())} "
-        f"({time.perf_counter() - t0:.0f} s on the host)")
-    if bars:
-        assert rel <= REL_L2
-        assert mx <= MAX_ABS_RMS * rms, \
-            f"max-abs/rms {mx / rms:.3e} on token {rows[np.argmax(np.max(np.abs(err), 1))]}"
-    return rel, mx / rms, ref
+    r = P.compare(oracle_layer(cfg), x[rows], delta[rows], idx[rows], w[rows], precision=precision,
+                  ref=ref, xcq=None if xcq is None else (xcq[0][rows], xcq[1][rows]), bars=bars,
+                  log=log)
+    return r["rel_l2"], r["max_abs_over_rms"], r["ref"]
 
 
 def test_toy_layer_full():
