@@ -186,6 +186,52 @@ class HipEvents:
             self.h.hipEventDestroy(e)
 
 
+def chain_timing(layers, xs, K, warmup):
+    """Decode through a chain of decoder MoE blocks: the layers in turn on one token, each
+    adding its Delta into the residual stream and handing the bf16 residual to the next
+    (moe_layer_forward_residual), against the same chain where each call's last launch also
+    reads the next layer's first-launch weights (moe_layer_forward_residual_prefetch).  The two
+    variants alternate in rounds of K calls; returns microseconds per layer of each (median of
+    the rounds)."""
+    import numpy as np
+    import torch
+    L = len(layers)
+    T, d = xs[0].shape
+    x = xs[0].clone()
+    res = torch.zeros((T, d), dtype=torch.float32, device=x.device)
+    k = layers[0].cfg.top_k
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    ws = layers[0].workspace(T)
+
+    def run(n, prefetch):
+        for i in range(n):
+            j = i % L
+            if prefetch:
+                layers[j].forward_residual_prefetch(x, res, layers[(j + 1) % L], x_next=x, idx=idx,
+                                                    w=w, workspace=ws)
+            else:
+                layers[j].forward_residual(x, res, x_next=x, idx=idx, w=w, workspace=ws)
+    run(warmup * L, False)
+    run(warmup * L, True)
+    torch.cuda.synchronize()
+    times = {False: [], True: []}
+    n = max(L, (K // L) * L)
+    for _ in range(5):
+        for pf in (False, True):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run(n, pf)
+            e1.record()
+            torch.cuda.synchronize()
+            times[pf].append(e0.elapsed_time(e1) * 1e3 / n)
+    plain, pref = float(np.median(times[False])), float(np.median(times[True]))
+    log(f"[bench] chain of {L} layers at batch {T}: {plain:.1f} us per layer, {pref:.1f} with the "
+        f"next layer's router and W_down_latent prefetched in the tail")
+    return {"layers": L, "calls_per_round": n, "rounds": 5, "us_per_layer": plain,
+            "us_per_layer_prefetch": pref, "rounds_us": {"plain": times[False], "prefetch": times[True]}}
+
+
 def percentiles_us(durations_ms):
     import numpy as np
     d = np.asarray(durations_ms, dtype=np.float64) * 1e3
@@ -507,6 +553,8 @@ def run_workload(cfg, args, peaks, store, cpu_cache):
             f"{graph['p90_us']:.1f}); eager median {graph['eager']['median_us']:.1f}; "
             f"bits equal eager: {graph['bits_equal_eager']}")
 
+    chain = chain_timing(layers, xs, K, args.warmup) if (T <= 4 and rotate > 1) else None
+
     # per-step durations: the same forwards with in-stream events between the steps (an event
     # record costs a few microseconds of GPU time, so this pass only ranks the steps)
     hip = HipEvents()
@@ -606,6 +654,8 @@ def run_workload(cfg, args, peaks, store, cpu_cache):
     }
     if graph is not None:
         res["hipgraph"] = graph
+    if chain is not None:
+        res["chain"] = chain
     if args.qb_stats:
         res["qb_stats"] = qb_stats(layers[0], xs[0], cfg, K, dev)
     if not args.no_cpu_baseline:
@@ -695,7 +745,7 @@ def main():
         "config": head["config"],
         "roofline": head["roofline"],
     }
-    for k in ("cpu_baseline", "parity_sample", "hipgraph", "layer", "qb_stats"):
+    for k in ("cpu_baseline", "parity_sample", "hipgraph", "chain", "layer", "qb_stats"):
         if k in head:
             out[k] = head[k]
     if peaks is not None:

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 typedef struct ihipStream_t* moe_stream_t; /* the same type as hipStream_t */
 
@@ -244,6 +244,23 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const 
 moe_status moe_layer_forward_noalloc(const moe_config* cfg, const moe_weights* w, const float* bias,
                                      const void* x, int64_t n_tokens, float* delta,
                                      int32_t* topk_idx, float* topk_w, moe_stream_t stream);
+
+/* moe_layer_forward_residual that also starts streaming the next layer's weights during this
+ * layer's tail (the chain of decoder blocks of the K3 model, the port notes' "Measured" and
+ * "Not measured (and why)": decode streams every layer's weights in turn).  With few tokens
+ * (the decode launches) the last launch of this call also reads the bytes of `next` that the
+ * next call's first launch will read (its router and W_down_latent rows, about 64 MB at the K3
+ * shape), in workgroups after those of its own product, so that the read fills that launch's
+ * drain and leaves them in the GPU's caches.  `next`: the next layer's weights (same config),
+ * or null for none; results are those of moe_layer_forward_residual, bit for bit.  Larger
+ * batches ignore `next`.  Errors as moe_layer_forward_residual, MOE_ERR_INVALID_ARG for a
+ * null or misaligned buffer in `next`. */
+moe_status moe_layer_forward_residual_prefetch(const moe_config* cfg, const moe_weights* w,
+                                               const float* bias, const void* x, int64_t n_tokens,
+                                               float* residual, void* x_next, float* delta,
+                                               int32_t* topk_idx, float* topk_w, void* workspace,
+                                               size_t workspace_bytes, const moe_weights* next,
+                                               moe_stream_t stream);
 
 /* Steps of the forward, in launch order.  With few tokens (at most 4, fewer for very
  * wide d) each product stages all its activation rows at once; larger batches take

@@ -26,9 +26,9 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_packed_dense_size", "moe_pa
            "moe_workspace_layout", "moe_layer_forward",
            "moe_layer_forward_timed", "moe_layer_forward_steps", "moe_route", "moe_dispatch",
            "moe_qb_histogram", "moe_qb_readout", "moe_layer_forward_residual",
-           "moe_layer_forward_noalloc")
+           "moe_layer_forward_noalloc", "moe_layer_forward_residual_prefetch")
 STEPS = ("router", "in", "route", "dispatch", "expert_gu", "expert_down", "combine", "out")
-ABI_VERSION = 5
+ABI_VERSION = 6
 STATIC_WORKSPACE_BYTES = 64 << 20   # MOE_STATIC_WORKSPACE_BYTES
 
 
@@ -102,6 +102,8 @@ def lib():
     L.moe_layer_forward_residual.argtypes = [P(MoeConfig), P(MoeWeights), vp, vp, i64, vp, vp, vp,
                                              vp, vp, vp, sz, vp]
     L.moe_layer_forward_noalloc.argtypes = [P(MoeConfig), P(MoeWeights), vp, vp, i64, vp, vp, vp, vp]
+    L.moe_layer_forward_residual_prefetch.argtypes = [P(MoeConfig), P(MoeWeights), vp, vp, i64, vp,
+                                                      vp, vp, vp, vp, vp, sz, P(MoeWeights), vp]
     for f in EXPORTS[2:]:
         getattr(L, f).restype = ctypes.c_int
     if L.moe_abi_version() != ABI_VERSION:
@@ -304,6 +306,25 @@ class Layer:
             residual.data_ptr(), None if x_next is None else x_next.data_ptr(),
             None if delta is None else delta.data_ptr(), idx.data_ptr(), w.data_ptr(),
             ws.data_ptr(), ws.numel(), _stream(stream)), "moe_layer_forward_residual")
+        return idx, w
+
+    def forward_residual_prefetch(self, x, residual, next_layer, x_next=None, delta=None, idx=None,
+                                  w=None, workspace=None, stream=None):
+        """forward_residual() that also reads, in its last launch, the weight bytes the next
+        layer's first launch reads (next_layer: a Layer of the same config, or None)."""
+        import torch
+        T = x.shape[0]
+        c = self.cfg
+        idx = torch.empty((T, c.top_k), dtype=torch.int32, device=self.device) if idx is None else idx
+        w = torch.empty((T, c.top_k), dtype=torch.float32, device=self.device) if w is None else w
+        ws = self.workspace(T) if workspace is None else workspace
+        W = self.weights_struct()
+        N = None if next_layer is None else ctypes.byref(next_layer.weights_struct())
+        _check(lib().moe_layer_forward_residual_prefetch(
+            ctypes.byref(c), ctypes.byref(W), self.bias.data_ptr(), x.data_ptr(), T,
+            residual.data_ptr(), None if x_next is None else x_next.data_ptr(),
+            None if delta is None else delta.data_ptr(), idx.data_ptr(), w.data_ptr(),
+            ws.data_ptr(), ws.numel(), N, _stream(stream)), "moe_layer_forward_residual_prefetch")
         return idx, w
 
     def forward_timed(self, x, events, delta, idx, w, workspace=None, stream=None):

@@ -299,7 +299,8 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const float
                         const void* x, int64_t n_tokens, float* delta, int32_t* topk_idx,
                         float* topk_w, void* workspace, size_t workspace_bytes,
                         void* const* events, int step_begin, int step_end, moe_stream_t stream,
-                        float* residual = nullptr, uint16_t* x_next = nullptr) {
+                        float* residual = nullptr, uint16_t* x_next = nullptr,
+                        const moe_weights* next = nullptr) {
   Shape s;
   moe_status st = make_shape(cfg, &s);
   if (st != MOE_OK) return st;
@@ -357,7 +358,16 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const float
       case MOE_STEP_EXPERT_GU: e = moe::launch_expert(s, experts, true, n_tokens, ws, hs); break;
       case MOE_STEP_EXPERT_DOWN: e = moe::launch_expert(s, experts, false, n_tokens, ws, hs); break;
       case MOE_STEP_COMBINE: e = moe::launch_combine(s, dense, topk_w, n_tokens, ws, hs); break;
-      case MOE_STEP_OUT: e = moe::launch_out(s, dense, n_tokens, ws, sink, hs); break;
+      case MOE_STEP_OUT: {
+        moe::Prefetch pf{};
+        if (next && fused) {   // the next layer's first launch reads these bytes
+          pf.p = static_cast<const uint8_t*>(next->dense);
+          pf.bytes = moe::first_launch_dense_bytes(s);
+          pf.sink = reinterpret_cast<uint32_t*>(ws.units);
+        }
+        e = moe::launch_out(s, dense, n_tokens, ws, sink, hs, pf);
+        break;
+      }
     }
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
@@ -433,6 +443,17 @@ MOE_EXPORT moe_status moe_layer_forward_residual(const moe_config* cfg, const mo
   return forward_impl(cfg, w, bias, x, n_tokens, delta, topk_idx, topk_w, workspace,
                       workspace_bytes, nullptr, 0, MOE_NUM_STEPS, stream, residual,
                       static_cast<uint16_t*>(x_next));
+}
+
+MOE_EXPORT moe_status moe_layer_forward_residual_prefetch(
+    const moe_config* cfg, const moe_weights* w, const float* bias, const void* x, int64_t n_tokens,
+    float* residual, void* x_next, float* delta, int32_t* topk_idx, float* topk_w, void* workspace,
+    size_t workspace_bytes, const moe_weights* next, moe_stream_t stream) {
+  if (n_tokens > 0 && !residual) return MOE_ERR_INVALID_ARG;
+  if (next && check_weights(next) != MOE_OK) return MOE_ERR_INVALID_ARG;
+  return forward_impl(cfg, w, bias, x, n_tokens, delta, topk_idx, topk_w, workspace,
+                      workspace_bytes, nullptr, 0, MOE_NUM_STEPS, stream, residual,
+                      static_cast<uint16_t*>(x_next), next);
 }
 
 MOE_EXPORT moe_status moe_layer_forward_steps(const moe_config* cfg, const moe_weights* w,

@@ -150,6 +150,16 @@ struct OutSink {
   uint16_t* xn;
 };
 
+// Bytes that the OUT launch of a few tokens also reads, in workgroups after those of its
+// product, so that they sit in the caches when the next call starts (the next layer's router
+// and W_down_latent rows); `flag` is always 0 (the value read is kept, never stored).
+struct Prefetch {
+  const uint8_t* p;
+  size_t bytes;
+  uint32_t* sink;
+  int flag;
+};
+
 // router_only: the router rows alone (otherwise W_down_latent rides in the same launch)
 hipError_t launch_router(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,
                          bool router_only, const Work& ws, hipStream_t st);
@@ -174,7 +184,12 @@ hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_
 hipError_t launch_combine(const Shape& s, const uint8_t* dense, const float* gw, int64_t T,
                           const Work& ws, hipStream_t st);
 hipError_t launch_out(const Shape& s, const uint8_t* dense, int64_t T, const Work& ws,
-                      const OutSink& out, hipStream_t st);
+                      const OutSink& out, hipStream_t st, const Prefetch& pf = Prefetch{});
+// Bytes of the packed dense weights that the first launch of a few-token forward reads (the
+// router and W_down_latent tile rows at the start of the IN matrix).
+inline size_t first_launch_dense_bytes(const Shape& s) {
+  return (size_t)(s.tr_r + s.tr_dn) * s.ks_in * kBf16StepBytes;
+}
 
 // The mx8 launches (moe_prefill.hip).
 hipError_t launch_pf_in(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,

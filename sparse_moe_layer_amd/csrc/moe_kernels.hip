@@ -1035,9 +1035,31 @@ struct OutArgs {
   int64_t T;
   OutSink sink;
   const float* add_u;   // without a latent: Delta = u + the product
+  int prod_wgs;         // workgroups of the product; the ones after them prefetch
+  Prefetch pf;
+  int pf_wgs;
 };
 
 constexpr int kOutMaxTokens = 8;
+constexpr size_t kPrefetchWgBytes = 64 * 1024;   // bytes read by one prefetch workgroup
+
+// A prefetch workgroup: 16-byte cached loads of its 64 KiB slice of pf, four in flight per
+// lane; the XOR of what it read is stored only under a flag the host never sets.
+__device__ __forceinline__ void prefetch_slice(const Prefetch& pf, int w) {
+  const uint4* p = reinterpret_cast<const uint4*>(pf.p);
+  const int64_t n16 = (int64_t)(pf.bytes / 16);
+  const int64_t b0 = (int64_t)w * (kPrefetchWgBytes / 16);
+  const int64_t b1 = min(n16, b0 + (int64_t)(kPrefetchWgBytes / 16));
+  uint32_t acc = 0;
+  for (int64_t i = b0 + threadIdx.x; i < b1; i += 4 * kBlock) {
+    uint4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = i + j * kBlock < b1 ? p[i + j * kBlock] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  }
+  if (pf.flag) pf.sink[threadIdx.x] = acc;
+}
 
 // 1 / sqrt(mean(row^2) + eps) of an fp32 row, by the whole workgroup (fixed order).
 __device__ __forceinline__ float row_inv_rms(const float* ur, int l, float eps, float* red) {
@@ -1082,6 +1104,10 @@ __global__ __launch_bounds__(kBlock) void k_out(OutArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
+  if ((int)blockIdx.x >= a.prod_wgs) {   // after the product's workgroups: the prefetch
+    prefetch_slice(a.pf, blockIdx.x - a.prod_wgs);
+    return;
+  }
   int wgi, blk;
   if (!xcd_item(blockIdx.x, a.wg_per_blk, a.n_blk, wgi, blk)) return;
   const int64_t t0 = (int64_t)blk * a.ntb;
@@ -2055,7 +2081,7 @@ hipError_t launch_combine(const Shape& s, const uint8_t* dense, const float* gw,
 }
 
 hipError_t launch_out(const Shape& s, const uint8_t* dense, int64_t T, const Work& ws,
-                      const OutSink& out, hipStream_t st) {
+                      const OutSink& out, hipStream_t st, const Prefetch& pf) {
   if (token_tiled(s, T)) {
     // [u_hat ; h_s] hi/lo rows over tiles of 32 tokens
     OutTTArgs a;
@@ -2088,9 +2114,11 @@ hipError_t launch_out(const Shape& s, const uint8_t* dense, int64_t T, const Wor
   a.n0 = s.latent ? s.l : 0;
   a.T = T; a.sink = out;
   a.add_u = s.latent ? nullptr : ws.u;
+  a.prod_wgs = (int)xcd_grid(a.wg_per_blk, a.n_blk);
+  a.pf = pf;
+  a.pf_wgs = pf.p && pf.bytes >= 16 ? (int)((pf.bytes + kPrefetchWgBytes - 1) / kPrefetchWgBytes) : 0;
   const size_t lds = (size_t)2 * (T < a.ntb ? T : a.ntb) * s.ks_out * kStepK * 2;
-  hipLaunchKernelGGL(k_out, dim3((unsigned)xcd_grid(a.wg_per_blk, a.n_blk)), dim3(kBlock), lds, st,
-                     a);
+  hipLaunchKernelGGL(k_out, dim3((unsigned)(a.prod_wgs + a.pf_wgs)), dim3(kBlock), lds, st, a);
   return hipGetLastError();
 }
 

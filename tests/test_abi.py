@@ -56,7 +56,7 @@ def test_peak_probe_library_exports_its_header():
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 5 == moe.ABI_VERSION
+    assert L.moe_abi_version() == 6 == moe.ABI_VERSION
     assert moe.status_str(0) == "MOE_OK"
     assert moe.status_str(3) == "MOE_ERR_WORKSPACE"
     assert moe.status_str(99) == "MOE_ERR_UNKNOWN"

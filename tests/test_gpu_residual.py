@@ -105,3 +105,25 @@ def test_three_layer_chain_against_the_oracle():
     xo_np = O.bf16_to_f64(xo)
     diff = xg_np != xo_np
     assert diff.mean() < 1e-2, diff.mean()
+
+
+@pytest.mark.parametrize("T", [1, 3, 40])
+def test_residual_with_next_layer_prefetch_gives_the_same_bits(T):
+    """moe_layer_forward_residual_prefetch: with few tokens the last launch also reads the next
+    layer's first-launch weight bytes; the results are those of the plain residual forward
+    (larger batches ignore the next layer)."""
+    cfg = TINY
+    lay, _ = device_layer(cfg)
+    nxt, _ = device_layer(cfg.with_(name="tiny_res_next", seed=642))
+    x = to_dev(synth.tokens(cfg, batch=50 + T, T=T))
+    res0 = torch.randn((T, cfg.d), dtype=torch.float32, device=DEV,
+                       generator=torch.Generator(device=DEV).manual_seed(7 + T))
+    r1, r2 = res0.clone(), res0.clone()
+    xn1 = torch.empty_like(x)
+    xn2 = torch.empty_like(x)
+    i1, w1 = lay.forward_residual(x, r1, x_next=xn1)
+    i2, w2 = lay.forward_residual_prefetch(x, r2, nxt, x_next=xn2)
+    i3, w3 = lay.forward_residual_prefetch(x, res0.clone(), None)
+    torch.cuda.synchronize()
+    assert torch.equal(r1, r2) and torch.equal(xn1, xn2)
+    assert torch.equal(i1, i2) and torch.equal(w1, w2) and torch.equal(i1, i3)
