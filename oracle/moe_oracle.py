@@ -30,6 +30,10 @@ the rounding points that a compute-bound path declares, and nothing else:
     blocks of 32 along the reduction axis, by the OCP MX conversion rule;
   - the normalised latent u_hat and the shared hidden h_s are rounded to bf16
     (nearest, ties to even) before their products with W_up and W_shared_down.
+"mx4" is "mx8" with MXFP4-E2M1 in place of MXFP8-E4M3 for x^c and h (the same OCP MX
+rule with the E2M1 element: scale exponent floor(log2 amax) - 2, saturation at 6): both
+operands of the expert products in the walkthrough's MXFP4 weight format.  It is a
+reported variant, not a default: its error against "fp32" is about ten times mx8's.
 
 Readings of points the pages leave open are listed in the repository's design
 notes; the ones that change arithmetic are stated where they act below.
@@ -46,7 +50,8 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "e2m1_decode", "e8m0_decode", "dequant_mxfp4", "E2M1_GRID",
     "e4m3_decode", "round_e4m3", "E4M3_MAX", "quantize_mx8", "mx8_ambiguous", "round_bf16",
-    "PRECISIONS",
+    "round_e2m1", "E2M1_MAX", "round_elem", "quantize_mx", "quantize_mx4", "mx_ambiguous",
+    "MX_ELEMENTS", "MX_PROFILE_ELEMENT", "PRECISIONS",
     "dequant_fp8_block128",
     "sigmoid", "select_and_weight", "selection_kappa", "router_scores", "situ", "swiglu", "glu", "rmsnorm",
     "OracleLayer", "forward", "routed_sum_dense_mask", "Result", "dispatch", "residual_add",
@@ -112,9 +117,19 @@ def dequant_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
 # exponent field 0 is subnormal (value = mantissa/8 * 2^-6); S.1111.111 is NaN; there is
 # no infinity, so the largest finite magnitude is 1.75 * 2^8 = 448.
 E4M3_MAX = 448.0
+#: Largest E2M1 magnitude (1.5 * 2^2).
+E2M1_MAX = 6.0
 
-#: Where the "mx8" profile rounds (see the module docstring).
-PRECISIONS = ("fp32", "mx8")
+#: Where the "mx8" and "mx4" profiles round (see the module docstring).
+PRECISIONS = ("fp32", "mx8", "mx4")
+
+#: Element formats of the MX conversions, from their field layouts: (largest exponent of a
+#: normal value emax, largest magnitude, mantissa bits, exponent of the smallest normal).
+#:   E4M3: normals 2^-6 .. 1.75 * 2^8, 3 mantissa bits;
+#:   E2M1: normals 2^0 .. 1.5 * 2^2, 1 mantissa bit (0.5 is its one subnormal).
+MX_ELEMENTS = {"e4m3": (8, E4M3_MAX, 3, -6), "e2m1": (2, E2M1_MAX, 1, 0)}
+#: The element format of each MX profile.
+MX_PROFILE_ELEMENT = {"mx8": "e4m3", "mx4": "e2m1"}
 
 
 def e4m3_decode(codes: np.ndarray) -> np.ndarray:
@@ -144,93 +159,130 @@ def _binade(a: np.ndarray) -> np.ndarray:
     return np.where(a > 0, ex - 1, 0).astype(np.int64)
 
 
-def round_e4m3(y: np.ndarray) -> np.ndarray:
-    """The nearest E4M3 value (ties to the even mantissa), saturated to +-448.
+def _quantum(a: np.ndarray, elem: str) -> np.ndarray:
+    """Spacing of the element format's values around magnitude a: 2^(e - mantissa bits)
+    in binade e, the subnormal spacing below the smallest normal."""
+    _, _, mbits, emin = MX_ELEMENTS[elem]
+    return np.ldexp(1.0, np.maximum(_binade(a), emin) - mbits)
 
-    Normal binade 2^e (e >= -6) holds 8 values spaced 2^(e-3); below 2^-6 the subnormals
-    are spaced 2^-9.  Saturation follows the OCP MX conversion rule (values past the
-    largest normal are clamped to it)."""
+
+def round_elem(y: np.ndarray, elem: str) -> np.ndarray:
+    """The nearest value of the element format (ties to the even mantissa), saturated to
+    its largest magnitude (the OCP MX conversion clamps values past the largest normal)."""
     y = np.asarray(y, dtype=np.float64)
     a = np.abs(y)
-    e = np.maximum(_binade(a), -6)
-    quantum = np.ldexp(1.0, e - 3)
+    quantum = _quantum(a, elem)
     r = np.round(a / quantum) * quantum        # numpy rounds halves to even
-    return np.copysign(np.minimum(r, E4M3_MAX), y)
+    return np.copysign(np.minimum(r, MX_ELEMENTS[elem][1]), y)
 
 
-def _mx8_exponent(amax: np.ndarray, scale_flip: np.ndarray | None) -> np.ndarray:
-    """Block exponent X = floor(log2(amax)) - 8 (-127 for amax = 0); where `scale_flip` is set,
-    the exponent of the other side of the power of two nearest amax (see mx8_ambiguous)."""
-    X = np.where(amax > 0, _binade(amax) - 8, -127)
+def round_e4m3(y: np.ndarray) -> np.ndarray:
+    """The nearest E4M3 value (ties to the even mantissa), saturated to +-448: normal binade
+    2^e (e >= -6) holds 8 values spaced 2^(e-3); below 2^-6 the subnormals are spaced 2^-9."""
+    return round_elem(y, "e4m3")
+
+
+def round_e2m1(y: np.ndarray) -> np.ndarray:
+    """The nearest E2M1 value (ties to the even mantissa), saturated to +-6: binade 2^e
+    (e >= 0) holds 2 values spaced 2^(e-1); below 1 the values 0 and 0.5."""
+    return round_elem(y, "e2m1")
+
+
+def _mx_exponent(amax: np.ndarray, emax: int, scale_flip: np.ndarray | None) -> np.ndarray:
+    """Block exponent X = floor(log2(amax)) - emax (-127 for amax = 0); where `scale_flip` is
+    set, the exponent of the other side of the power of two nearest amax (mx_ambiguous)."""
+    X = np.where(amax > 0, _binade(amax) - emax, -127)
     if scale_flip is not None:
-        # amax in [2^(X+8), 2^(X+9)): the nearer end decides which side is the other one
-        upper = amax >= np.ldexp(np.sqrt(2.0), (X + 8).astype(np.int64))
+        # amax in [2^(X+emax), 2^(X+emax+1)): the nearer end decides which side is the other one
+        upper = amax >= np.ldexp(np.sqrt(2.0), (X + emax).astype(np.int64))
         X = np.where(np.asarray(scale_flip, bool) & (amax > 0), np.where(upper, X + 1, X - 1), X)
     return np.clip(X, -127, 127)
 
 
-def _e4m3_neighbours(y: np.ndarray):
-    """The two E4M3 magnitudes around |y| (lo <= |y| < hi, spaced by the quantum of |y|'s
-    binade; subnormal spacing 2^-9 below 2^-6)."""
+def _neighbours(y: np.ndarray, elem: str):
+    """The two element-format magnitudes around |y| (lo <= |y| < hi, spaced by the quantum
+    of |y|'s binade)."""
     a = np.abs(y)
-    quantum = np.ldexp(1.0, np.maximum(_binade(a), -6) - 3)
+    quantum = _quantum(a, elem)
     lo = np.floor(a / quantum) * quantum
     return lo, lo + quantum
 
 
-def quantize_mx8(v: np.ndarray, block: int = 32, flip: np.ndarray | None = None,
-                 scale_flip: np.ndarray | None = None):
-    """MXFP8 (E4M3 elements, one E8M0 scale per `block` values along the last axis), by the
-    OCP MX v1.0 conversion: X = floor(log2(max |v|)) - 8 per block (8 is the largest
-    exponent of E4M3), -127 for an all-zero block, clamped to the E8M0 range; elements
-    are v / 2^X rounded to E4M3 (round_e4m3).
+def quantize_mx(v: np.ndarray, elem: str, block: int = 32, flip: np.ndarray | None = None,
+                scale_flip: np.ndarray | None = None):
+    """MX conversion (one E8M0 scale per `block` values along the last axis) to element format
+    `elem` ("e4m3": MXFP8, "e2m1": MXFP4), by the OCP MX v1.0 rule: X = floor(log2(max |v|))
+    - emax per block (emax: the element format's largest normal exponent), -127 for an
+    all-zero block, clamped to the E8M0 range; elements are v / 2^X rounded to the element
+    format (round_elem).
 
     `scale_flip` (bool per block) and `flip` (bool per element) take the other valid decision
-    where a value sits on a decision boundary (mx8_ambiguous): the block exponent of the other
-    side of the nearest power of two, or the other of the element's two E4M3 neighbours
-    (never past 448).  Both are correct conversions of a value known only to the accuracy
-    with which it was computed.
+    where a value sits on a decision boundary (mx_ambiguous): the block exponent of the other
+    side of the nearest power of two, or the other of the element's two neighbours (never
+    past the largest magnitude).  Both are correct conversions of a value known only to the
+    accuracy with which it was computed.
 
-    Returns (dequantised values, E4M3 element values, scale bytes X + 127)."""
+    Returns (dequantised values, element values, scale bytes X + 127)."""
+    emax, vmax = MX_ELEMENTS[elem][:2]
     v = np.asarray(v, dtype=np.float64)
     shp = v.shape
     if shp[-1] % block:
         raise ValueError("the last axis must be a multiple of the block size")
     vb = v.reshape(shp[:-1] + (shp[-1] // block, block))
     amax = np.max(np.abs(vb), axis=-1)
-    X = _mx8_exponent(amax, scale_flip)
+    X = _mx_exponent(amax, emax, scale_flip)
     y = vb * np.ldexp(1.0, -X)[..., None]
-    q = round_e4m3(y)
+    q = round_elem(y, elem)
     if flip is not None:
-        lo, hi = _e4m3_neighbours(y)
+        lo, hi = _neighbours(y, elem)
         other = np.copysign(np.where(np.abs(q) == lo, hi, lo), y)
-        take = np.asarray(flip, bool).reshape(q.shape) & (hi <= E4M3_MAX)
+        take = np.asarray(flip, bool).reshape(q.shape) & (hi <= vmax)
         q = np.where(take, other, q)
     deq = q * np.ldexp(1.0, X)[..., None]
     return deq.reshape(shp), q.reshape(shp), (X + 127).astype(np.uint8)
 
 
-def mx8_ambiguous(v: np.ndarray, eta: float, block: int = 32, scale_flip: np.ndarray | None = None):
-    """Where the MXFP8 conversion of v takes a decision on a boundary, to within eta:
+def quantize_mx8(v: np.ndarray, block: int = 32, flip: np.ndarray | None = None,
+                 scale_flip: np.ndarray | None = None):
+    """MXFP8: quantize_mx with E4M3 elements (X = floor(log2 amax) - 8, saturation at 448)."""
+    return quantize_mx(v, "e4m3", block, flip, scale_flip)
+
+
+def quantize_mx4(v: np.ndarray, block: int = 32, flip: np.ndarray | None = None,
+                 scale_flip: np.ndarray | None = None):
+    """MXFP4: quantize_mx with E2M1 elements (X = floor(log2 amax) - 2, saturation at 6)."""
+    return quantize_mx(v, "e2m1", block, flip, scale_flip)
+
+
+def mx_ambiguous(v: np.ndarray, elem: str, eta: float, block: int = 32,
+                 scale_flip: np.ndarray | None = None):
+    """Where the MX conversion of v to `elem` takes a decision on a boundary, to within eta:
       - blocks whose amax lies within a relative eta of a power of two (the block exponent
         could fall on either side);
       - elements whose scaled value lies within eta * (the block's largest scaled magnitude)
-        of the midpoint of its two E4M3 neighbours (it could round either way), with the
-        block exponents of `scale_flip` applied.
+        of the midpoint of its two neighbours (it could round either way), with the block
+        exponents of `scale_flip` applied; midpoints past the largest magnitude are none
+        (everything there saturates).
     A value computed with an error below those distances may legitimately convert to either
     decision.  Returns (element mask, block mask)."""
+    emax, vmax = MX_ELEMENTS[elem][:2]
     v = np.asarray(v, dtype=np.float64)
     shp = v.shape
     vb = v.reshape(shp[:-1] + (shp[-1] // block, block))
     amax = np.max(np.abs(vb), axis=-1)
     p2 = np.ldexp(1.0, np.round(np.log2(np.where(amax > 0, amax, 1.0))).astype(np.int64))
     blk = (amax > 0) & (np.abs(amax / p2 - 1.0) <= eta)
-    X = _mx8_exponent(amax, scale_flip)
+    X = _mx_exponent(amax, emax, scale_flip)
     y = vb * np.ldexp(1.0, -X)[..., None]
-    lo, hi = _e4m3_neighbours(y)
+    lo, hi = _neighbours(y, elem)
     ymax = (amax * np.ldexp(1.0, -X))[..., None]
-    el = (np.abs(np.abs(y) - 0.5 * (lo + hi)) <= eta * ymax) & (hi <= E4M3_MAX)
+    el = (np.abs(np.abs(y) - 0.5 * (lo + hi)) <= eta * ymax) & (hi <= vmax)
     return el.reshape(shp), blk
+
+
+def mx8_ambiguous(v: np.ndarray, eta: float, block: int = 32, scale_flip: np.ndarray | None = None):
+    """mx_ambiguous for the MXFP8 conversion."""
+    return mx_ambiguous(v, "e4m3", eta, block, scale_flip)
 
 
 def round_bf16(v: np.ndarray) -> np.ndarray:
@@ -481,22 +533,23 @@ def forward(layer: OracleLayer, x_bf16: np.ndarray, forced_idx: np.ndarray | Non
     profile of PRECISIONS (default: the layer config's `precision`, else "fp32").
     `workers`: threads that evaluate experts side by side (default: one per host core for
     layers whose experts are dequantised on demand, else 1); the result is the same.
-    `xc_flip`, `xc_scale_flip` (mx8 profile): take the other valid MXFP8 decision at the
-    marked elements / blocks of x^c (quantize_mx8), for tokens whose x^c has a value on a
-    conversion boundary (mx8_ambiguous), as forced routing does for top-k near ties."""
+    `xc_flip`, `xc_scale_flip` (mx profiles): take the other valid MX decision at the
+    marked elements / blocks of x^c (quantize_mx), for tokens whose x^c has a value on a
+    conversion boundary (mx_ambiguous), as forced routing does for top-k near ties."""
     cfg = layer.cfg
     precision = precision or getattr(cfg, "precision", "fp32")
     if precision not in PRECISIONS:
         raise ValueError(precision)
-    mx8 = precision == "mx8"
-    q8 = (lambda v: quantize_mx8(v)[0]) if mx8 else None  # noqa: E731
+    elem = MX_PROFILE_ELEMENT.get(precision)          # None in "fp32"
+    mx = elem is not None                             # the mx profiles' rounding points
+    qmx = (lambda v: quantize_mx(v, elem)[0]) if mx else None  # noqa: E731
     x = bf16_to_f64(x_bf16) if np.asarray(x_bf16).dtype == np.uint16 else np.asarray(x_bf16, np.float64)
     T = x.shape[0]
     s = router_scores(x, layer.router)
     idx, G, margin = select_and_weight(s, layer.bias, cfg.k, cfg.route_scale, forced_idx)
 
     xc = x @ layer.w_down_latent.T if cfg.l else x
-    xe = quantize_mx8(xc, flip=xc_flip, scale_flip=xc_scale_flip)[0] if mx8 else xc  # the experts' input
+    xe = quantize_mx(xc, elem, flip=xc_flip, scale_flip=xc_scale_flip)[0] if mx else xc  # the experts' input
     lat = xc.shape[1]
     u = np.zeros((T, lat), np.float64)
     act = lambda g, v: _act(cfg, g, v)  # noqa: E731
@@ -506,7 +559,7 @@ def forward(layer: OracleLayer, x_bf16: np.ndarray, forced_idx: np.ndarray | Non
         tj = np.nonzero(flat == e)[0]
         t_rows, j_cols = tj // cfg.k, tj % cfg.k
         w_gu, w_dn = layer.expert(int(e))
-        return t_rows, j_cols, glu(xe[t_rows], w_gu, w_dn, act, q8)
+        return t_rows, j_cols, glu(xe[t_rows], w_gu, w_dn, act, qmx)
 
     # The experts' outputs may be evaluated concurrently (each is a pure function of its
     # expert and rows); they are added into the sums one expert at a time in increasing
@@ -516,13 +569,13 @@ def forward(layer: OracleLayer, x_bf16: np.ndarray, forced_idx: np.ndarray | Non
 
     if cfg.l:
         u_hat = rmsnorm(u, layer.gamma, cfg.eps) if cfg.use_norm else u
-        if mx8:
+        if mx:
             u_hat = round_bf16(u_hat)
         y_r = u_hat @ layer.w_up_latent.T
     else:
         y_r = u
     if cfg.ms:
-        y_s = glu(x, layer.shared_gu, layer.shared_down, act, round_bf16 if mx8 else None)
+        y_s = glu(x, layer.shared_gu, layer.shared_down, act, round_bf16 if mx else None)
     else:
         y_s = np.zeros_like(y_r)
     return Result(y_r + y_s, idx, G, margin, xc, u, y_r, y_s)
