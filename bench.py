@@ -8,7 +8,9 @@ By default it measures the three configurations of the metric, each with its roo
 CPU oracle baseline and a parity sample: the K3-shaped layer (d 7168, latent 3584, 896 MXFP4
 experts top-16, 3072-wide experts, merged 6144-wide shared expert) at decode batch 1 (the
 headline: `value` and the top-level fields), at decode batch 64 under a Zipf(1.0) load, and at
-prefill of 8192 tokens in the mx8 profile and in the fp32 profile (under "workloads").  Three
+prefill of 8192 tokens in the mx8 profile and in the fp32 profile (under "workloads"), with the
+mx4 variant of the prefill (MXFP4 activations on the FP4 x FP4 matrix cores) reported beside
+them.  Three
 copies of the dense weights and distinct token batches rotate at decode so that the 256 MB
 last-level cache cannot hold what a step reads.  Measured peaks (an HBM read stream, loops of
 each matrix-core instruction) are reported beside the published ones.
@@ -51,10 +53,12 @@ def algorithmic_bytes(cfg, T, D):
     gu_w, dn_w = expert_weight_bytes(cfg)
     tk = T * k
     small = T <= 3   # the route and the dispatch run inside the IN launch
-    mx8 = getattr(cfg, "precision", "fp32") == "mx8"
-    ab = 4 if not mx8 else 1 + 1 / 32   # bytes per activation element of the expert inputs
-    if mx8:
-        # one IN product (router logits, x^c fp32, h_s bf16), then x^c to MXFP8
+    prof = getattr(cfg, "precision", "fp32")
+    mx = prof in ("mx8", "mx4")        # the mx launches
+    # bytes per activation element of the expert inputs (MX: codes plus one scale byte per 32)
+    ab = {"mx8": 1 + 1 / 32, "mx4": 0.5 + 1 / 32}.get(prof, 4)
+    if mx:
+        # one IN product (router logits, x^c fp32, h_s bf16), then x^c to MX
         router = T * d * 2 + (E + cfg.l + 2 * ms) * d * 2 + T * (E * 4 + cfg.l * 4 + ms * 2)
         in_ = T * cfg.l * 4 + T * cfg.l * ab
     else:
@@ -70,9 +74,9 @@ def algorithmic_bytes(cfg, T, D):
         "dispatch": 0 if small else tk * 4 * 4 + E * 8,
         "expert_gu": D * gu_w + T * l * ab + tk * m * ab,
         "expert_down": D * dn_w + tk * m * ab + tk * l * 4,
-        # (mx8: one pass to u_hat in bf16, u itself is not stored)
-        "combine": tk * l * 4 + tk * 8 + T * l * (2 if mx8 else 4),
-        "out": d * (cfg.l + ms) * 2 + cfg.l * 2 + T * (l + ms) * (2 if mx8 else 4) + T * d * 4,
+        # (mx: one pass to u_hat in bf16, u itself is not stored)
+        "combine": tk * l * 4 + tk * 8 + T * l * (2 if mx else 4),
+        "out": d * (cfg.l + ms) * 2 + cfg.l * 2 + T * (l + ms) * (2 if mx else 4) + T * d * 4,
     }
 
 def algorithmic_flops(cfg, T):
@@ -105,7 +109,7 @@ STEP_KERNELS = {"router": [("k_router", None), ("k_router_tt", None), ("k_token_
                 "expert_down": [("k_exp", "false"), ("k_exp_tt", "false")],
                 "combine": [("k_combine", None), ("k_norm", None)],
                 "out": [("k_out", None), ("k_out_tt", None)]}
-STEP_KERNELS_MX8 = {"router": [("k_pf_dense", "true")], "in": [("k_pf_quant", None)],
+STEP_KERNELS_MX = {"router": [("k_pf_dense", "true")], "in": [("k_pf_quant", None)],
                     "route": [("k_route", None)],
                     "dispatch": [("k_disp_count", None), ("k_disp_scan", None), ("k_disp_scatter", None)],
                     "expert_gu": [("k_pf_exp", "true")], "expert_down": [("k_pf_exp", "false")],
@@ -461,14 +465,17 @@ def qb_stats(layer, x, cfg, K, dev):
 
 
 DEFAULT_WORKLOADS = ("k3_latent_moe_decode_b1", "k3_latent_moe_decode_b64_zipf1.0",
-                     "k3_latent_moe_prefill_8192", "k3_latent_moe_prefill_8192_fp32")
+                     "k3_latent_moe_prefill_8192", "k3_latent_moe_prefill_8192_fp32",
+                     "k3_latent_moe_prefill_8192_mx4")
 # per workload: (dense weight copies rotated, distinct token batches rotated, CPU-baseline sample
 # as (batches of the rotation, tokens per batch taken one every `stride`))
 ROTATION = {"k3_latent_moe_decode_b1": (3, 64), "k3_latent_moe_decode_b64_zipf1.0": (3, 16),
             "k3_latent_moe_prefill_8192": (1, 2), "k3_latent_moe_prefill_8192_fp32": (1, 2),
+            "k3_latent_moe_prefill_8192_mx4": (1, 2),
             "k2_moe_1024_zipf1.2": (3, 8), "k3_ep_share_112x1170": (1, 2)}
 CPU_SAMPLE = {"k3_latent_moe_decode_b1": (16, 1), "k3_latent_moe_decode_b64_zipf1.0": (1, 1),
               "k3_latent_moe_prefill_8192": (1, 128), "k3_latent_moe_prefill_8192_fp32": (1, 128),
+              "k3_latent_moe_prefill_8192_mx4": (1, 128),
               "k2_moe_1024_zipf1.2": (1, 16), "k3_ep_share_112x1170": (1, 128)}
 
 
@@ -575,7 +582,8 @@ def run_workload(cfg, args, peaks, store, cpu_cache):
     log(f"[bench] per step with events at every boundary (us): {steps_us}")
     dom = max(("router", "in", "expert_gu", "expert_down", "out"),
               key=lambda n: step_ms[moe.STEPS.index(n)])
-    mx8 = getattr(cfg, "precision", "fp32") == "mx8"
+    prof = getattr(cfg, "precision", "fp32")
+    mx = prof in ("mx8", "mx4")     # the mx launches
     # The dominant step alone, K launches back to back between two events, each on the
     # buffers of an earlier full forward; R sets of buffers (different tokens, so different
     # experts, and different dense copies) rotate past the last-level cache.
@@ -607,26 +615,28 @@ def run_workload(cfg, args, peaks, store, cpu_cache):
     layer_bytes = weight_bytes(cfg, Dm)
     layer_gbs = layer_bytes / (ms_step * 1e-3) / 1e9
     layer_tflops = sum(af.values()) / (ms_step * 1e-3) / 1e12
-    kernels = STEP_KERNELS_MX8 if mx8 else STEP_KERNELS
+    kernels = STEP_KERNELS_MX if mx else STEP_KERNELS
     traffic = measured_traffic(cfg.name, dom, kernels)
     # the bound of the dominant step: its algorithmic bytes at the HBM peak against its flops
     # at the matrix-core rate of its operands (mx8 experts: the FP8 x FP4 instruction runs at
-    # the FP8 rate; everything else: bf16 operands, fp32 activations as bf16 pairs)
-    dtype_peak = "fp8" if (mx8 and dom.startswith("expert")) else "bf16"
+    # the FP8 rate; mx4 experts: FP4 x FP4; everything else: bf16 operands, fp32 activations
+    # as bf16 pairs)
+    dtype_peak = ({"mx8": "fp8", "mx4": "fp4"}[prof] if (mx and dom.startswith("expert"))
+                  else "bf16")
     t_mem = ab[dom] / (HBM_PEAK_GBS * 1e9)
     t_mma = af[dom] / (MFMA_PEAK[dtype_peak] * 1e12)
     meas = peaks or {}
     if t_mma > t_mem:
         achieved = af[dom] / dom_s / 1e12
-        mpk = meas.get("by_dtype_TFLOPs", {}).get("fp8xfp4" if dtype_peak == "fp8" else "bf16")
+        mpk = meas.get("by_dtype_TFLOPs", {}).get({"fp8": "fp8xfp4"}.get(dtype_peak, dtype_peak))
         roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved,
                     "peak": MFMA_PEAK[dtype_peak], "unit": "TFLOP/s",
                     "frac": achieved / MFMA_PEAK[dtype_peak],
                     "traffic": traffic, "traffic_over_algorithmic": (traffic / ab[dom]) if traffic else None,
                     "algorithmic_flops": af[dom], "algorithmic_bytes": ab[dom], "avg_us": dom_s * 1e6,
-                    "peak_dtype": "fp8 x fp4 (fp8 rate)" if dtype_peak == "fp8" else "bf16",
+                    "peak_dtype": {"fp8": "fp8 x fp4 (fp8 rate)", "fp4": "fp4 x fp4"}.get(dtype_peak, "bf16"),
                     "measured_peak": mpk, "frac_of_measured": (achieved / mpk) if mpk else None,
-                    "frac_of_mxfp4_peak": achieved / MFMA_PEAK["fp4"] if dtype_peak == "fp8" else None}
+                    "frac_of_mxfp4_peak": achieved / MFMA_PEAK["fp4"] if dtype_peak != "bf16" else None}
     else:
         achieved = ab[dom] / dom_s / 1e9
         mpk = meas.get("hbm_read_GBps")
@@ -638,7 +648,7 @@ def run_workload(cfg, args, peaks, store, cpu_cache):
     res = {
         "value": T / (ms_step * 1e-3), "unit": "tokens/s", "ms_per_step": ms_step, "steps": K,
         "warmup": args.warmup,
-        "dtype": "fp8xfp4+bf16" if mx8 else "f32",
+        "dtype": {"mx8": "fp8xfp4+bf16", "mx4": "fp4xfp4+bf16"}.get(prof, "f32"),
         "config": {"workload": cfg.name, "tokens_per_step": T, "d": cfg.d, "latent": cfg.l,
                    "experts": cfg.E, "top_k": cfg.k, "expert_hidden": cfg.m,
                    "shared_hidden": cfg.ms, "expert_weights": cfg.expert_fmt,
@@ -662,7 +672,7 @@ def run_workload(cfg, args, peaks, store, cpu_cache):
         log(f"[bench] {cfg.name}: the CPU oracle on a sample of the workload")
         nbat, stride = CPU_SAMPLE.get(cfg.name, (1, max(1, T // 64)))
         # the sample's batches, each once more through the GPU (their outputs for the parity
-        # sample; the last forward's workspace holds the mx8 x^c codes)
+        # sample; the last forward's workspace holds the mx x^c codes)
         xh = np.concatenate([xs_h[b] for b in range(min(nbat, batches))])
         outs = []
         for b in range(min(nbat, batches)):
@@ -672,12 +682,12 @@ def run_workload(cfg, args, peaks, store, cpu_cache):
         torch.cuda.synchronize()
         gpu = tuple(np.concatenate([o[j] for o in outs]) for j in range(3))
         xcq = None
-        if mx8 and nbat == 1:
+        if mx and nbat == 1:
             inter = layers[0].intermediates(T)
             xcq = (inter["xq"].cpu().numpy(), inter["xs"].cpu().numpy())
         rows = np.arange(0, xh.shape[0], stride)
         res["cpu_baseline"], res["parity_sample"] = cpu_baseline(
-            cfg, dense0, xh, rows, gpu, xcq=xcq, other_precision="fp32" if mx8 else None,
+            cfg, dense0, xh, rows, gpu, xcq=xcq, other_precision="fp32" if mx else None,
             cache=cpu_cache)
     del layers, xs, ws
     return res
@@ -690,8 +700,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None,
                     help="one workload (synth preset) instead of the default set: K3 decode B=1 "
-                         "(the headline), decode B=64 Zipf(1.0), prefill 8192 in the mx8 and "
-                         "the fp32 profiles")
+                         "(the headline), decode B=64 Zipf(1.0), prefill 8192 in the mx8, "
+                         "fp32 and mx4 profiles")
     ap.add_argument("--rotate", type=int, default=None, help="dense weight copies rotated")
     ap.add_argument("--batches", type=int, default=None, help="distinct token batches rotated")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 typedef struct ihipStream_t* moe_stream_t; /* the same type as hipStream_t */
 
@@ -68,7 +68,7 @@ typedef enum moe_wfmt {
 
 typedef enum moe_precision {
   MOE_PREC_FP32 = 0, /* activations kept in fp32 between all steps; Delta in fp32 */
-  MOE_PREC_MX8 = 1   /* the compute-bound profile: the experts' input x^c and hidden h are
+  MOE_PREC_MX8 = 1,  /* the compute-bound profile: the experts' input x^c and hidden h are
                         converted to MXFP8-E4M3 (blocks of 32 along K; OCP MX conversion:
                         scale 2^(floor(log2 amax) - 8), elements rounded to nearest even,
                         saturated at 448) and multiplied with the MXFP4 weights on the
@@ -76,6 +76,13 @@ typedef enum moe_precision {
                         before W_up_latent and W_shared_down; everything else as FP32.
                         The walkthrough's deployment recipe: MXFP4 weights, MXFP8
                         activations.  Needs MXFP4 experts. */
+  MOE_PREC_MX4 = 2   /* MX8 with MXFP4-E2M1 in place of MXFP8-E4M3 for x^c and h (the same
+                        OCP MX rule with the E2M1 element: scale 2^(floor(log2 amax) - 2),
+                        elements rounded to nearest even, saturated at 6), multiplied with
+                        the MXFP4 weights on the scaled FP4 x FP4 matrix cores: both
+                        operands in the walkthrough's weight format.  A reported variant,
+                        not a default: its error against FP32 is about ten times MX8's.
+                        Needs MXFP4 experts. */
 } moe_precision;
 
 /* Layer shape and options.  K3: d_model 7168, d_latent 3584, n_experts 896, top_k 16,
@@ -199,6 +206,8 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t max_tokens, size_t*
  *             h as codes [T*k][128 ceil(m/128)] and scales [T*k][4 ceil(m/128)] (dispatch
  *             order; K-steps past l or m zero), u_hat bf16 [T][l], h_s bf16 [T][m_s],
  *             each part 256-aligned (internal); the slots [2] h_s and [3] h stay unused
+ *       MX4:  as MX8 with rows of 64 bytes of E2M1 code pairs (low nibble first) per
+ *             K-step of 128 in place of 128 E4M3 bytes, in the same parts
  *   [8] perm   [T*k]    int32    dispatch order -> assignment t*k+j
  *   [9] inv    [T*k]    int32    assignment -> dispatch order
  *  [10] counts [E]      int32    assignments per expert

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 ACT = {"situ": 0, "swiglu": 1}
 WFMT = {"bf16": 0, "mxfp4": 1, "fp8b128": 2}
-PREC = {"fp32": 0, "mx8": 1}
+PREC = {"fp32": 0, "mx8": 1, "mx4": 2}
 WS_SLOTS = ("ctrl", "xc", "hs", "h", "eo", "u", "uh", "hl", "perm", "inv", "counts", "offsets", "z",
             "chunk_hist", "units")
 
@@ -28,7 +28,7 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_packed_dense_size", "moe_pa
            "moe_qb_histogram", "moe_qb_readout", "moe_layer_forward_residual",
            "moe_layer_forward_noalloc", "moe_layer_forward_residual_prefetch")
 STEPS = ("router", "in", "route", "dispatch", "expert_gu", "expert_down", "combine", "out")
-ABI_VERSION = 6
+ABI_VERSION = 7
 STATIC_WORKSPACE_BYTES = 64 << 20   # MOE_STATIC_WORKSPACE_BYTES
 
 
@@ -421,12 +421,14 @@ class Layer:
             n = int(np.prod(shp))
             dt = torch.int32 if name in ("ctrl", "perm", "inv", "counts", "offsets") else torch.float32
             out[name] = ws[off[name]: off[name] + 4 * n].view(dt).view(shp)
-        if c.precision == PREC["mx8"]:
-            # the experts' input x^c as MXFP8: E4M3 codes [T][128 ks] and E8M0 scale bytes
-            # [T][4 ks] (K-steps of 128 columns, padded), the first parts of slot [7]
+        if c.precision in (PREC["mx8"], PREC["mx4"]):
+            # the experts' input x^c in MX form: code rows of 128 E4M3 bytes (mx8) or 64 bytes of
+            # E2M1 pairs (mx4) per K-step of 128 columns (padded) and E8M0 scale bytes [T][4 ks],
+            # the first parts of slot [7] (whose code part is sized for E4M3)
             ks = -(-c.d_latent // 128)
+            row = (128 if c.precision == PREC["mx8"] else 64) * ks
             o = off["hl"]
-            out["xq"] = ws[o: o + T * 128 * ks].view(T, 128 * ks)
+            out["xq"] = ws[o: o + T * row].view(T, row)
             o += (T * 128 * ks + 255) & ~255
             out["xs"] = ws[o: o + T * 4 * ks].view(T, 4 * ks)
         return out

@@ -33,10 +33,12 @@ moe_status make_shape(const moe_config* c, Shape* s) {
     return MOE_ERR_INVALID_ARG;
   const int32_t lin = c->d_latent > 0 ? c->d_latent : c->d_model;   // the experts' input width
   if (c->expert_wfmt == MOE_WFMT_MXFP4 && (lin % 32 || c->d_expert % 32)) return MOE_ERR_INVALID_ARG;
-  if (c->precision != MOE_PREC_FP32 && c->precision != MOE_PREC_MX8) return MOE_ERR_INVALID_ARG;
-  if (c->precision == MOE_PREC_MX8 && c->expert_wfmt != MOE_WFMT_MXFP4) return MOE_ERR_UNSUPPORTED;
+  if (c->precision != MOE_PREC_FP32 && c->precision != MOE_PREC_MX8 && c->precision != MOE_PREC_MX4)
+    return MOE_ERR_INVALID_ARG;
+  const bool mx = c->precision != MOE_PREC_FP32;
+  if (mx && c->expert_wfmt != MOE_WFMT_MXFP4) return MOE_ERR_UNSUPPORTED;
   if (c->d_latent == 0 && c->d_shared == 0) return MOE_ERR_UNSUPPORTED;  // non-latent needs a shared expert
-  if (c->d_latent == 0 && c->precision == MOE_PREC_MX8) return MOE_ERR_UNSUPPORTED;
+  if (c->d_latent == 0 && mx) return MOE_ERR_UNSUPPORTED;
   if (c->n_experts > 1024 || c->top_k > 64) return MOE_ERR_UNSUPPORTED;
   if (c->d_model > 8192 || c->d_latent > 8192 || c->d_expert > 8192 || c->d_shared > 8192)
     return MOE_ERR_UNSUPPORTED;
@@ -54,7 +56,7 @@ moe_status make_shape(const moe_config* c, Shape* s) {
   s->beta_lin = c->beta_lin;
   s->act = c->act;
   s->wfmt = c->expert_wfmt;
-  s->prec = c->precision == MOE_PREC_MX8 ? 1 : 0;
+  s->prec = c->precision == MOE_PREC_MX8 ? 1 : c->precision == MOE_PREC_MX4 ? 2 : 0;
   // packed dense weights
   s->ks_in = moe::cdiv(s->d, moe::kStepK);
   s->tr_r = moe::cdiv(s->E, moe::kTileRows);
@@ -82,11 +84,12 @@ moe_status make_shape(const moe_config* c, Shape* s) {
   return MOE_OK;
 }
 
-// Slot [7].  FP32: x^c, h_s, h and u_hat as bf16 row pairs.  MX8: the MXFP8 codes and
-// scales of x^c and h, u_hat and h_s in bf16.  Each part 256-aligned.
+// Slot [7].  FP32: x^c, h_s, h and u_hat as bf16 row pairs.  MX8 / MX4: the MX codes and
+// scales of x^c and h (MX4 uses the first half of each code row), u_hat and h_s in bf16.
+// Each part 256-aligned.
 constexpr int kHiloParts = 6;
 size_t hilo_part(const Shape& s, int64_t T, int part) {
-  if (s.prec == 1) {
+  if (moe::mx_profile(s)) {
     const int64_t rows[6] = {T, T, T * s.k, T * s.k, T, T};
     const int64_t bytes[6] = {128LL * s.ks_gu, 4LL * s.ks_gu, 128LL * s.ks_edn, 4LL * s.ks_edn,
                               2LL * s.l, 2LL * s.ms};
@@ -323,7 +326,7 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const float
     if (events && events[step] && hipEventRecord((hipEvent_t)events[step], hs) != hipSuccess)
       return MOE_ERR_HIP;
     hipError_t e = hipSuccess;
-    if (s.prec == 1) {
+    if (moe::mx_profile(s)) {
       switch (step) {
         case MOE_STEP_ROUTER: e = moe::launch_pf_in(s, dense, xb, n_tokens, ws.pf, ws.z, ws.xc, hs); break;
         case MOE_STEP_IN: e = moe::launch_pf_quant(s, ws.xc, n_tokens, ws.pf, hs); break;

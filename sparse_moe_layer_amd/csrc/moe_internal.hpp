@@ -28,7 +28,8 @@ struct Shape {
   float eps, route_scale, beta_gate, beta_lin;
   int act;    // 0 SiTU, 1 SwiGLU
   int wfmt;   // 0 bf16, 1 MXFP4, 2 FP8 E4M3 with 128 x 128 block scales (routed experts)
-  int prec;   // 0 fp32 activations, 1 the mx8 profile (MXFP8 expert inputs, bf16 u_hat / h_s)
+  int prec;   // 0 fp32 activations; the mx profiles (bf16 u_hat / h_s, MX expert inputs):
+              // 1 mx8 (MXFP8-E4M3), 2 mx4 (MXFP4-E2M1)
   // packed dense weights: IN = [router ; W_down_latent ; shared gate/up] over K = d,
   // OUT = [W_up_latent | W_shared_down] over K = l (padded) + m_s
   int ks_in, tr_r, tr_dn, tr_sh, tr_in;
@@ -42,11 +43,12 @@ struct Shape {
   size_t expert_bytes;  // packed bytes of one expert (256-byte multiple)
 };
 
-// Operands of the mx8 launches (in the hi/lo slot of the workspace).
+// Operands of the mx launches (in the hi/lo slot of the workspace).  Code rows hold 128
+// E4M3 bytes (mx8) or 64 bytes of two E2M1 codes (mx4, low nibble first) per K-step.
 struct PfWork {
-  uint8_t* xq;     // [T][128 ks_gu]    x^c as E4M3 codes (K-steps padded with zeros)
+  uint8_t* xq;     // [T][128 ks_gu]    x^c codes (K-steps padded with zeros)
   uint8_t* xs;     // [T][4 ks_gu]      its E8M0 block scales
-  uint8_t* hq;     // [T*k][128 ks_edn] h as E4M3 codes, dispatch order
+  uint8_t* hq;     // [T*k][128 ks_edn] h codes, dispatch order
   uint8_t* hsc;    // [T*k][4 ks_edn]
   uint16_t* uh;    // [T][l]            u_hat in bf16
   uint16_t* hs;    // [T][ms]           h_s in bf16
@@ -87,7 +89,8 @@ inline int out_tokens_per_block(const Shape& s) { return clampi(57344 / (s.ks_ou
 // With this few tokens the route and the dispatch run inside the IN launch, and every
 // product stages all its activation rows at once (the decode launches); larger batches
 // take the token-tiled launches.
-// The mx8 profile always takes its own launches (moe_prefill.hip).
+// The mx profiles always take their own launches (moe_prefill.hip).
+inline bool mx_profile(const Shape& s) { return s.prec != 0; }
 inline bool route_fused(const Shape& s, int64_t T) {
   return s.prec == 0 && T <= 4 && T * s.k <= kBlock && T <= in_tokens_per_block(s);
 }
@@ -99,9 +102,9 @@ constexpr int kTiledUnitPositions = 32;
 constexpr int kTiledUnitPositionsSingle = 64;
 constexpr int kPfUnitPositions = 64;   // 16 x the expert tile blocks of moe_prefill.hip
 // Positions of one expert per unit of the expert launches (2 hi/lo rows each; one FP8
-// row each in the mx8 launches).
+// row each in the mx launches).
 inline int unit_positions(const Shape& s, int64_t T) {
-  if (s.prec == 1) return kPfUnitPositions;
+  if (mx_profile(s)) return kPfUnitPositions;
   if (token_tiled(s, T)) return s.latent ? kTiledUnitPositions : kTiledUnitPositionsSingle;
   // few tokens: all rows of a unit staged at once (2 hi/lo rows of the widest expert
   // input per position, within 56 KiB of LDS)
@@ -121,7 +124,7 @@ inline int64_t max_units(const Shape& s, int64_t T) {
 // a compute unit.  The larger units take the token-tiled expert kernel.
 inline int small_unit_positions(const Shape& s, int64_t T) {
   const int nu = unit_positions(s, T);
-  if (s.prec == 1 || !token_tiled(s, T)) return nu;
+  if (mx_profile(s) || !token_tiled(s, T)) return nu;
   const int ks = s.ks_gu > s.ks_edn ? s.ks_gu : s.ks_edn;
   const int w = clampi(32768 / (ks * kStepK * 4), 1, 4);
   return w < nu ? w : nu;
@@ -173,8 +176,9 @@ hipError_t launch_qb_readout(const Shape& s, const float* bias, int64_t T, int b
                              const int32_t* hist, float* new_bias, hipStream_t st);
 hipError_t launch_route(const Shape& s, const float* bias, int64_t T, const Work& ws,
                         int32_t* idx, float* gw, hipStream_t st);
-// The logit planes the route sums: the router launch's K-split, or 1 (mx8: plain logits).
-inline int route_planes(const Shape& s) { return s.prec == 1 ? 1 : s.zplanes; }
+// The logit planes the route sums: the router launch's K-split, or 1 (mx profiles: plain
+// logits).
+inline int route_planes(const Shape& s) { return mx_profile(s) ? 1 : s.zplanes; }
 hipError_t launch_dispatch(const Shape& s, const int32_t* idx, int64_t T, int32_t* counts,
                            int32_t* offs, int32_t* perm, int32_t* inv, int32_t* chunk_hist,
                            int32_t* units, int32_t* ctrl, hipStream_t st);
@@ -191,7 +195,7 @@ inline size_t first_launch_dense_bytes(const Shape& s) {
   return (size_t)(s.tr_r + s.tr_dn) * s.ks_in * kBf16StepBytes;
 }
 
-// The mx8 launches (moe_prefill.hip).
+// The mx launches (moe_prefill.hip).
 hipError_t launch_pf_in(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,
                         const PfWork& pw, float* z, float* xc, hipStream_t st);
 hipError_t launch_pf_quant(const Shape& s, const float* xc, int64_t T, const PfWork& pw,
@@ -200,7 +204,7 @@ hipError_t launch_pf_expert(const Shape& s, const uint8_t* experts, bool gu, int
                             const Work& ws, const PfWork& pw, hipStream_t st);
 hipError_t launch_pf_norm(const Shape& s, const uint8_t* dense, int64_t T, const Work& ws,
                           const PfWork& pw, hipStream_t st);
-// the combine and the norm of the mx8 launches in one pass (u itself is not stored)
+// the combine and the norm of the mx launches in one pass (u itself is not stored)
 hipError_t launch_pf_combine_norm(const Shape& s, const uint8_t* dense, const float* gw, int64_t T,
                                   const Work& ws, const PfWork& pw, hipStream_t st);
 hipError_t launch_pf_out(const Shape& s, const uint8_t* dense, int64_t T, const PfWork& pw,

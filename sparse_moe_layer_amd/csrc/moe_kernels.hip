@@ -2073,7 +2073,7 @@ hipError_t launch_combine(const Shape& s, const uint8_t* dense, const float* gw,
   const int bpt = cdiv(s.l, kBlock);
   hipLaunchKernelGGL(k_combine, dim3((unsigned)(T * bpt)), dim3(kBlock), 0, st, gw,
                      (const int32_t*)ws.inv, (const float*)ws.eo, T, s.k, s.l, bpt, ws.u);
-  if (token_tiled(s, T) && s.prec == 0 && s.latent)   // (the mx8 launches take their own norm)
+  if (token_tiled(s, T) && !mx_profile(s) && s.latent)   // (the mx launches take their own norm)
     hipLaunchKernelGGL(k_norm, dim3((unsigned)T), dim3(kBlock), 0, st, (const float*)ws.u,
                        reinterpret_cast<const uint16_t*>(dense + s.gamma_off), s.l, s.use_norm,
                        s.eps, ws.uh, ws.uh_hl);

@@ -1,15 +1,15 @@
-// gfx950 kernels of the compute-bound forward (the "mx8" precision profile).
+// gfx950 kernels of the compute-bound forward (the "mx8" and "mx4" precision profiles).
 //
 // The same steps as the weight-streaming launches, in the order of the Kimi K3 latent
 // mixture-of-experts block card, with the rounding points of the profile:
 //   k_pf_in      z = x W_r, x^c = x W_down_latent, h_s = SiTU(x W_sg, x W_su) -> bf16,
 //                one product over the packed IN matrix (bf16 MFMA)
-//   k_pf_quant   x^c -> MXFP8-E4M3 (the experts' input)
+//   k_pf_quant   x^c -> MXFP8-E4M3 (mx8) or MXFP4-E2M1 (mx4), the experts' input
 //   (route and dispatch: the launches of the token-tiled path)
-//   k_pf_exp     routed gate/up with SiTU and the MXFP8 conversion of h fused in its
-//                epilogue, then routed down: FP8 activations x MXFP4 weights on the scaled
-//                16x16x128 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4), the E8M0 scales of both
-//                operands applied by the matrix core
+//   k_pf_exp     routed gate/up with SiTU and the MX conversion of h fused in its
+//                epilogue, then routed down: MX activations x MXFP4 weights on the scaled
+//                16x16x128 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4; FP8 x FP4 in mx8, FP4 x
+//                FP4 in mx4), the E8M0 scales of both operands applied by the matrix core
 //   (combine and the RMSNorm, u_hat rounded to bf16)
 //   k_pf_out     Delta = u_hat W_up_latent + h_s W_shared_down, one product over the packed
 //                OUT matrix (bf16 MFMA)
@@ -59,6 +59,16 @@ __device__ __forceinline__ f32x4_t mfma_fp8_fp4(uint4 alo, uint4 ahi, uint4 b, u
                                                           0, (int)sa, 0, (int)sb);
 }
 
+// The same over one 16x16 block with both operands FP4-E2M1: A laid out as B (16 bytes per
+// lane: row l % 16, K 32 (l/16) .. +32, low nibble first).
+__device__ __forceinline__ f32x4_t mfma_fp4_fp4(uint4 a, uint4 b, uint32_t sa, uint32_t sb,
+                                                f32x4_t acc) {
+  const i32x8_t av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const i32x8_t bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4 /*A: E2M1*/, 4 /*B: E2M1*/,
+                                                          0, (int)sa, 0, (int)sb);
+}
+
 // An fp32 value (already divided by its block scale, |y| < 512) to E4M3: the nearest value,
 // ties to even, saturated at 448 (the conversion itself turns values past 464 into NaN).
 __device__ __forceinline__ uint32_t to_e4m3(float y) {
@@ -66,14 +76,34 @@ __device__ __forceinline__ uint32_t to_e4m3(float y) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false) & 0xFFu;
 }
 
-// E8M0 byte of an MX block from its largest magnitude: 2^X with X = floor(log2 amax) - 8
-// (8: the largest E4M3 exponent), the byte X + 127, clamped at 0 (amax of 0 or below 2^-119).
-__device__ __forceinline__ uint32_t mx8_scale_byte(float amax) {
+// E8M0 byte of an MX block from its largest magnitude: 2^X with X = floor(log2 amax) - EMAX
+// (the element format's largest exponent: 8 for E4M3, 2 for E2M1), the byte X + 127, clamped
+// at 0 (amax of 0 or below 2^(EMAX - 127)).
+template <uint32_t EMAX>
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
   const uint32_t ef = (__float_as_uint(amax) >> 23) & 0xFFu;
-  return ef > 8u ? ef - 8u : 0u;
+  return ef > EMAX ? ef - EMAX : 0u;
 }
 // 2^-X for the scale byte (X = byte - 127): an fp32 with exponent field 254 - byte.
-__device__ __forceinline__ float mx8_inv_scale(uint32_t sbyte) { return __uint_as_float((254u - sbyte) << 23); }
+__device__ __forceinline__ float mx_inv_scale(uint32_t sbyte) { return __uint_as_float((254u - sbyte) << 23); }
+
+// An fp32 value (already divided by its block scale, |y| < 8) to its E2M1 code: the nearest
+// of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with halfway cases to the even code (0.25 -> 0, 0.75 -> 1,
+// 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4), saturated at 6, as the count of
+// thresholds below |y|; the sign bit only on a non-zero magnitude.
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+  const float a = fabsf(y);
+  const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.f);
+  return m | (y < 0.f && m != 0u ? 8u : 0u);
+}
+// Eight fp32 values times inv as E2M1 codes, the first in the low nibble.
+__device__ __forceinline__ uint32_t pack8_e2m1(float4 x0, float4 x1, float inv) {
+  return e2m1_code(x0.x * inv) | (e2m1_code(x0.y * inv) << 4) | (e2m1_code(x0.z * inv) << 8) |
+         (e2m1_code(x0.w * inv) << 12) | (e2m1_code(x1.x * inv) << 16) |
+         (e2m1_code(x1.y * inv) << 20) | (e2m1_code(x1.z * inv) << 24) | (e2m1_code(x1.w * inv) << 28);
+}
 
 // tanh of the compute-bound epilogues: the odd series x (1 - x^2/3 + 2 x^4/15) below
 // |x| = 1/16 (relative error < 1e-8 there), else (1 - e^-2|x|) / (1 + e^-2|x|) with the
@@ -120,6 +150,7 @@ __device__ __forceinline__ float swap_half_rows(float v) {
 //         (row r at word o0[r]), [c1, c1 + n1) from segment 1 (word o1[r]), zero elsewhere.
 //   AF 1: MXFP8 rows padded to whole K-steps (128 code bytes and 4 scale bytes per
 //         K-step): 8 pieces per K-step at word o0[r] + 8 q, the scale word at s0[r] + q.
+//   AF 2: MXFP4 rows, likewise with 64 code bytes per K-step: 4 pieces at word o0[r] + 4 q.
 // Rows r >= R are zero.  Thread piece i is idx = threadIdx + 256 i: row idx / PR, piece
 // idx % PR, so that consecutive threads read consecutive bytes of a row.  Every load is
 // issued (invalid pieces read word 0 of segment 0 and are zeroed when committed).  LDS
@@ -140,7 +171,7 @@ struct PfSrc {
 
 template <int AF, int NB, int P>
 struct PfStage {
-  static constexpr int PR = AF ? 8 : 16;
+  static constexpr int PR = AF == 2 ? 4 : AF == 1 ? 8 : 16;
   static constexpr int RB = 16 * NB;
   static constexpr int NP = (RB * PR + kBlock - 1) / kBlock;
   uint4 v[P][NP];
@@ -176,7 +207,7 @@ struct PfStage {
       uint32_t w = 0u;
       const uint4* base = src.b0;
       if (AF) {
-        w = rv[i] ? o0[i] + 8u * q + piece_of(i) : 0u;
+        w = rv[i] ? o0[i] + (uint32_t)PR * q + piece_of(i) : 0u;
       } else {
         const int col = q * kStepK + 8 * piece_of(i);
         const bool a0 = in0(i, src, q), a1 = in1(i, src, q);
@@ -223,14 +254,14 @@ struct PfStage {
 
 // The K loop of a tile: acc[t][b] = D of activation block b x the wavefront's tile row t
 // (trow[t]; waves or tile rows without work pass tile row 0 of the same matrix and drop
-// the result).  AF 0 pairs with bf16 weights (WF 0), AF 1 with MXFP4 weights (WF 1).  P
+// the result).  AF 0 pairs with bf16 weights (WF 0), AF 1 and 2 with MXFP4 weights (WF 1).  P
 // K-steps of weights and of activation rows are in flight (register rings, slot q % P
 // holds K-step q); the rows of K-step q + 1 go to LDS at the end of step q.
 template <int AF, int NB, int NT, int P>
 __device__ __forceinline__ void pf_run(const PfRows& rows, const PfSrc& src,
                                        const uint8_t* const (&trow)[NT], int ks, uint4* lds,
                                        uint32_t* slds, f32x4_t (&acc)[NT][NB]) {
-  constexpr int WF = AF;
+  constexpr int WF = AF ? 1 : 0;
   constexpr int RB = 16 * NB;
   constexpr int PR = PfStage<AF, NB, P>::PR;
   const int lane = threadIdx.x & (kWave - 1);
@@ -259,7 +290,18 @@ __device__ __forceinline__ void pf_run(const PfRows& rows, const PfSrc& src,
       // slot sl held K-step q (already in LDS buffer q & 1): refill it with q + P
       st.load(sl, src, min(q + P, ks - 1));
       const uint4* buf = lds + (q & 1) * RB * PR;
-      if (AF) {
+      if (AF == 2) {
+        const uint32_t* sb = slds + (q & 1) * RB;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int r = 16 * b + c;
+          const uint4 af = buf[g * RB + (r ^ g)];
+          const uint32_t sa = (sb[r] >> (8 * g)) & 0xFFu;
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            acc[t][b] = mfma_fp4_fp4(af, w[sl][t].w[0], sa, (w[sl][t].sc >> (8 * g)) & 0xFFu, acc[t][b]);
+        }
+      } else if (AF) {
         const uint32_t* sb = slds + (q & 1) * RB;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -406,8 +448,10 @@ __global__ __launch_bounds__(kBlock, 2) void k_pf_dense(PfDenseArgs a) {
       }
 }
 
-// x^c fp32 [T][l] -> MXFP8 rows of ks K-steps: codes [T][128 ks], scales [T][4 ks] (blocks
-// past l are zero).  One thread per (token, block of 32).
+// x^c fp32 [T][l] -> MX rows of ks K-steps: codes [T][128 ks] E4M3 bytes (FP4 false) or
+// [T][64 ks] bytes of E2M1 pairs (FP4 true), scales [T][4 ks] (blocks past l are zero).
+// One thread per (token, block of 32).
+template <bool FP4>
 __global__ __launch_bounds__(kBlock) void k_pf_quant(const float* __restrict__ xc, int64_t T, int l,
                                                      int ks, uint8_t* __restrict__ codes,
                                                      uint8_t* __restrict__ scales) {
@@ -416,10 +460,11 @@ __global__ __launch_bounds__(kBlock) void k_pf_quant(const float* __restrict__ x
   if (gid >= T * nbk) return;
   const int64_t t = gid / nbk;
   const int blk = (int)(gid - t * nbk);
-  uint4* dst = reinterpret_cast<uint4*>(codes + t * 128 * ks + 32 * blk);
+  constexpr int kBlkBytes = FP4 ? 16 : 32;
+  uint4* dst = reinterpret_cast<uint4*>(codes + t * 4 * kBlkBytes * ks + kBlkBytes * blk);
   if (32 * blk >= l) {
     dst[0] = make_uint4(0u, 0u, 0u, 0u);
-    dst[1] = make_uint4(0u, 0u, 0u, 0u);
+    if (!FP4) dst[1] = make_uint4(0u, 0u, 0u, 0u);
     scales[t * nbk + blk] = 0;
     return;
   }
@@ -433,8 +478,20 @@ __global__ __launch_bounds__(kBlock) void k_pf_quant(const float* __restrict__ x
   }
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const uint32_t sb = mx8_scale_byte(amax);
-  const float inv = mx8_inv_scale(sb);
+  if (FP4) {
+    const uint32_t sb = mx_scale_byte<2>(amax);
+    const float inv = mx_inv_scale(sb);
+    uint32_t wd[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      wd[i] = pack8_e2m1(make_float4(v[8 * i], v[8 * i + 1], v[8 * i + 2], v[8 * i + 3]),
+                         make_float4(v[8 * i + 4], v[8 * i + 5], v[8 * i + 6], v[8 * i + 7]), inv);
+    dst[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    scales[t * nbk + blk] = (uint8_t)sb;
+    return;
+  }
+  const uint32_t sb = mx_scale_byte<8>(amax);
+  const float inv = mx_inv_scale(sb);
   uint32_t wd[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -446,11 +503,12 @@ __global__ __launch_bounds__(kBlock) void k_pf_quant(const float* __restrict__ x
 }
 
 // ------------------------------------------------------------------------------------
-// Routed experts, FP8 x MXFP4.  Work item (tile-row group, unit); a unit is a run of at
-// most 16 kPfExpNB dispatch positions of one expert.  Gate/up: input rows x^c_q of the positions'
-// tokens; each wavefront's 4 tile rows (8 gate + 8 up rows each) give one MX block of 32
-// columns of h = SiTU(gate, up), converted to MXFP8 in the epilogue.  Down: input rows
-// h_q of the positions, output E fp32.
+// Routed experts, MX activations (AF 1: MXFP8, AF 2: MXFP4) x MXFP4 weights.  Work item
+// (tile-row group, unit); a unit is a run of at most 16 kPfExpNB dispatch positions of one
+// expert.  Gate/up: input rows x^c_q of the positions' tokens; each wavefront's 4 tile rows
+// (8 gate + 8 up rows each) give one MX block of 32 columns of h = SiTU(gate, up), converted
+// to the same MX format in the epilogue.  Down: input rows h_q of the positions, output E
+// fp32.
 // ------------------------------------------------------------------------------------
 struct PfExpArgs {
   const uint8_t* experts;
@@ -461,9 +519,9 @@ struct PfExpArgs {
   int max_units, nu, E, k;
   int64_t n_assign;
   const int32_t* perm;
-  const uint8_t* xq;        // input codes, rows of 128 ks bytes
+  const uint8_t* xq;        // input codes, rows of 128 ks (AF 1) or 64 ks (AF 2) bytes
   const uint8_t* xs;        // input scales, rows of 4 ks bytes
-  // gate/up output: h as MXFP8 rows of ks_out K-steps
+  // gate/up output: h as MX rows of ks_out K-steps
   uint8_t* hq;
   uint8_t* hsc;
   int ks_out, m, act;
@@ -473,14 +531,14 @@ struct PfExpArgs {
   int n_out;
 };
 
-template <bool GU, int NB>
+template <bool GU, int NB, int AF>
 __device__ __forceinline__ void pf_exp_unit(const PfExpArgs& a, const PfRows& rows, uint4* sm,
                                             uint32_t* ssm, const uint8_t* const (&trow)[kPfNT],
                                             const int (&tr)[kPfNT], int wblk, int p0, int n) {
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane & 15, g = lane >> 4;
   f32x4_t acc[kPfNT][NB];
-  pf_run<1, NB, kPfNT, kPfExpDepth>(rows, PfSrc{reinterpret_cast<const uint4*>(a.xq), nullptr,
+  pf_run<AF, NB, kPfNT, kPfExpDepth>(rows, PfSrc{reinterpret_cast<const uint4*>(a.xq), nullptr,
                                    reinterpret_cast<const uint32_t*>(a.xs), n, 0, 0, 0},
                        trow, a.ks, sm, ssm, acc);
   if (!GU) {
@@ -504,7 +562,7 @@ __device__ __forceinline__ void pf_exp_unit(const PfExpArgs& a, const PfRows& ro
   // c + 8; the pair swaps halves so that lane c < 8 evaluates tile rows 0, 1 and lane
   // c >= 8 tile rows 2, 3.  Then lane l converts row l / 4, columns 8 (l % 4) .. +8: the
   // block's largest magnitude over the quad of lanes, the E8M0 byte, 8 codes, one 8-byte
-  // store.
+  // (E4M3) or 4-byte (E2M1) store.
   const int nbk = 4 * a.ks_out;
   if (32 * wblk >= 128 * a.ks_out) return;
   const bool lo = c < 8;
@@ -534,10 +592,14 @@ __device__ __forceinline__ void pf_exp_unit(const PfExpArgs& a, const PfRows& ro
                        fmaxf(fmaxf(fabsf(x1.x), fabsf(x1.y)), fmaxf(fabsf(x1.z), fabsf(x1.w))));
     amax = fmaxf(amax, quad_perm_f32<0xB1>(amax));   // lanes 1, 0, 3, 2 of the quad
     amax = fmaxf(amax, quad_perm_f32<0x4E>(amax));   // lanes 2, 3, 0, 1
-    const uint32_t sb = mx8_scale_byte(amax);
-    const float inv = mx8_inv_scale(sb);
+    const uint32_t sb = AF == 2 ? mx_scale_byte<2>(amax) : mx_scale_byte<8>(amax);
+    const float inv = mx_inv_scale(sb);
     const int i = 16 * b + rr;
-    if (i < n) {
+    if (AF == 2 && i < n) {
+      const int64_t p = p0 + i;
+      *reinterpret_cast<uint32_t*>(a.hq + p * 64 * a.ks_out + 16 * wblk + 4 * qq) = pack8_e2m1(x0, x1, inv);
+      if (qq == 0) a.hsc[p * nbk + wblk] = (uint8_t)sb;
+    } else if (i < n) {
       const int64_t p = p0 + i;
       const uint2 w2 = make_uint2(pack4_e4m3(x0.x * inv, x0.y * inv, x0.z * inv, x0.w * inv),
                                   pack4_e4m3(x1.x * inv, x1.y * inv, x1.z * inv, x1.w * inv));
@@ -554,7 +616,7 @@ constexpr int kPfChunk = 8;
 
 // Two workgroups per compute unit (a register budget of 256 per lane): while one waits at
 // its barrier or for its loads the other issues MFMAs.
-template <bool GU>
+template <bool GU, int AF>
 __global__ __launch_bounds__(kBlock, 2) void k_pf_exp(PfExpArgs a) {
   extern __shared__ uint4 sm[];
   __shared__ PfRows rows;
@@ -573,7 +635,7 @@ __global__ __launch_bounds__(kBlock, 2) void k_pf_exp(PfExpArgs a) {
       const int asg = a.perm[p];
       src = (asg >= 0 && asg < a.n_assign) ? asg / a.k : 0;
     }
-    rows.o0[threadIdx.x] = (uint32_t)(src * 8 * a.ks);     // 16-byte words (128 ks bytes per row)
+    rows.o0[threadIdx.x] = (uint32_t)(src * (AF == 2 ? 4 : 8) * a.ks);   // 16-byte words of the row
     rows.s0[threadIdx.x] = (uint32_t)(src * a.ks);         // scale words (4 ks bytes per row)
   }
   __syncthreads();
@@ -588,9 +650,9 @@ __global__ __launch_bounds__(kBlock, 2) void k_pf_exp(PfExpArgs a) {
   }
   // blocks of 16 positions: the unit's count rounded up to one of the built tile heights
   const int nb = (n + 15) / 16;
-  if (nb <= 1) pf_exp_unit<GU, 1>(a, rows, sm, ssm, trow, tr, wblk, p0, n);
-  else if (nb <= 2) pf_exp_unit<GU, 2>(a, rows, sm, ssm, trow, tr, wblk, p0, n);
-  else pf_exp_unit<GU, kPfExpNB>(a, rows, sm, ssm, trow, tr, wblk, p0, n);
+  if (nb <= 1) pf_exp_unit<GU, 1, AF>(a, rows, sm, ssm, trow, tr, wblk, p0, n);
+  else if (nb <= 2) pf_exp_unit<GU, 2, AF>(a, rows, sm, ssm, trow, tr, wblk, p0, n);
+  else pf_exp_unit<GU, kPfExpNB, AF>(a, rows, sm, ssm, trow, tr, wblk, p0, n);
 }
 
 // u_hat = RMSNorm(u) * gamma rounded to bf16 (the OUT product's input), one workgroup per
@@ -623,7 +685,7 @@ __global__ __launch_bounds__(kBlock) void k_pf_norm(const float* __restrict__ u,
   }
 }
 
-// The combine and the norm in one pass, one workgroup per token, for the mx8 launches (whose
+// The combine and the norm in one pass, one workgroup per token, for the mx launches (whose
 // only use of u is u_hat): u_t = sum_j G[t,j] E[inv[t,j]] stays in registers, with the same
 // fmaf chain per element as k_combine, and the sum of squares and u_hat follow k_pf_norm's
 // order (thread i takes the column groups 4 i + 1024 c), so the bits are those of the two
@@ -737,8 +799,12 @@ hipError_t launch_pf_in(const Shape& s, const uint8_t* dense, const uint16_t* x,
 hipError_t launch_pf_quant(const Shape& s, const float* xc, int64_t T, const PfWork& pw,
                            hipStream_t st) {
   const int64_t n = T * 4 * s.ks_gu;
-  hipLaunchKernelGGL(k_pf_quant, dim3((unsigned)cdiv(n, kBlock)), dim3(kBlock), 0, st, xc, T, s.l,
-                     s.ks_gu, pw.xq, pw.xs);
+  if (s.prec == 2)
+    hipLaunchKernelGGL(k_pf_quant<true>, dim3((unsigned)cdiv(n, kBlock)), dim3(kBlock), 0, st, xc, T,
+                       s.l, s.ks_gu, pw.xq, pw.xs);
+  else
+    hipLaunchKernelGGL(k_pf_quant<false>, dim3((unsigned)cdiv(n, kBlock)), dim3(kBlock), 0, st, xc, T,
+                       s.l, s.ks_gu, pw.xq, pw.xs);
   return hipGetLastError();
 }
 
@@ -767,8 +833,13 @@ hipError_t launch_pf_expert(const Shape& s, const uint8_t* experts, bool gu, int
   a.out = ws.eo;
   a.n_out = s.l;
   const unsigned grid = (unsigned)chunk_grid(a.max_units, a.n_grp, kPfChunk);
-  if (gu) hipLaunchKernelGGL(k_pf_exp<true>, dim3(grid), dim3(kBlock), kPfExpLds, st, a);
-  else hipLaunchKernelGGL(k_pf_exp<false>, dim3(grid), dim3(kBlock), kPfExpLds, st, a);
+  if (s.prec == 2) {
+    if (gu) hipLaunchKernelGGL((k_pf_exp<true, 2>), dim3(grid), dim3(kBlock), kPfExpLds, st, a);
+    else hipLaunchKernelGGL((k_pf_exp<false, 2>), dim3(grid), dim3(kBlock), kPfExpLds, st, a);
+  } else {
+    if (gu) hipLaunchKernelGGL((k_pf_exp<true, 1>), dim3(grid), dim3(kBlock), kPfExpLds, st, a);
+    else hipLaunchKernelGGL((k_pf_exp<false, 1>), dim3(grid), dim3(kBlock), kPfExpLds, st, a);
+  }
   return hipGetLastError();
 }
 

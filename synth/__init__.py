@@ -165,7 +165,7 @@ class LayerConfig:
     bias_file: str = ""
     e8m0_lo: int = 119               # E8M0 scale bytes uniform in [lo, hi]
     e8m0_hi: int = 123
-    precision: str = "fp32"          # rounding profile of the forward: "fp32" | "mx8"
+    precision: str = "fp32"          # rounding profile of the forward: "fp32" | "mx8" | "mx4"
 
     def with_(self, **kw) -> "LayerConfig":
         return replace(self, **kw)
@@ -191,6 +191,8 @@ K3_PREFILL_8K = LayerConfig(name="k3_latent_moe_prefill_8192", tokens=8192, seed
                             precision="mx8", **_K3)
 # the same layer and tokens through the fp32-activation launches (no declared rounding)
 K3_PREFILL_8K_FP32 = K3_PREFILL_8K.with_(name="k3_latent_moe_prefill_8192_fp32", precision="fp32")
+# the same layer with MXFP4 activations too (FP4 x FP4 matrix cores; a reported variant)
+K3_PREFILL_8K_MX4 = K3_PREFILL_8K.with_(name="k3_latent_moe_prefill_8192_mx4", precision="mx4")
 
 # The K2 block card's non-latent MoE block on the same kernels: 384 SwiGLU experts top-8,
 # gate weights renormalised and scaled by 2.827, one shared 2048-wide expert, FP8 E4M3
@@ -208,7 +210,7 @@ K3_EP_SHARE = LayerConfig(name="k3_ep_share_112x1170", tokens=8192, seed=1006, p
                           **{**_K3, "E": 112})
 
 PRESETS = {c.name: c for c in (TOY, K3_DECODE_B1, K3_DECODE_B64_ZIPF, K3_PREFILL_8K,
-                               K3_PREFILL_8K_FP32, K2_MOE_1024_ZIPF, K3_EP_SHARE)}
+                               K3_PREFILL_8K_FP32, K3_PREFILL_8K_MX4, K2_MOE_1024_ZIPF, K3_EP_SHARE)}
 
 
 def param_shapes(cfg: LayerConfig) -> dict:

@@ -8,10 +8,11 @@ Bars (restating the layer's acceptance rule):
     run on the GPU's own selection);
   - gate weights within 1e-6 of the oracle's G where the indices agree;
   - Delta: relative L2 error <= REL_L2 and max abs error <= MAX_ABS_RMS * rms(Delta_oracle).
-In the mx8 profile the MXFP8 conversion of x^c takes integer decisions (block exponents,
-E4M3 codes) on computed values: the GPU's decisions must equal the oracle's except where
-the oracle marks one as on a boundary (within MX8_ETA), and tokens where the GPU took the
-other valid decision are compared with the oracle taking it too.
+In the mx profiles the MX conversion of x^c (MXFP8-E4M3 in mx8, MXFP4-E2M1 in mx4) takes
+integer decisions (block exponents, element codes) on computed values: the GPU's decisions
+must equal the oracle's except where the oracle marks one as on a boundary (within MX8_ETA),
+and tokens where the GPU took the other valid decision are compared with the oracle taking
+it too.
 """
 from __future__ import annotations
 
@@ -24,7 +25,7 @@ import oracle as O
 REL_L2 = 2e-3
 MAX_ABS_RMS = 1e-2
 MARGIN = 1e-5
-MX8_ETA = 1e-4   # relative to the block's largest magnitude (O.mx8_ambiguous)
+MX8_ETA = 1e-4   # relative to the block's largest magnitude (O.mx_ambiguous), both mx profiles
 
 
 class ParityError(AssertionError):
@@ -63,26 +64,39 @@ def by_expert(idx, w):
     return np.take_along_axis(idx, o, 1), np.take_along_axis(w, o, 1)
 
 
-def mx8_decisions(xc, xq, xs, log=print):
-    """The GPU's MXFP8 decisions on x^c (codes [T, >= l] uint8, scale bytes [T, >= l/32])
-    against the oracle's (x^c float64 [T, l]): they must agree except where the oracle marks
-    a boundary.  Returns (element mask, block mask) of the other decisions the GPU took."""
+def gpu_codes(xq, elem):
+    """Element values of GPU code rows: E4M3 bytes, or bytes of two E2M1 codes (the low
+    nibble holding the even column)."""
+    xq = np.asarray(xq)
+    if elem == "e4m3":
+        return O.e4m3_decode(xq)
+    nib = np.empty(xq.shape[:-1] + (2 * xq.shape[-1],), np.uint8)
+    nib[..., 0::2] = xq & 0xF
+    nib[..., 1::2] = xq >> 4
+    return O.e2m1_decode(nib)
+
+
+def mx_decisions(xc, xq, xs, elem="e4m3", log=print):
+    """The GPU's MX decisions on x^c (code rows [T, ...] uint8, scale bytes [T, >= l/32])
+    against the oracle's (x^c float64 [T, l]) for element format `elem`: they must agree
+    except where the oracle marks a boundary.  Returns (element mask, block mask) of the
+    other decisions the GPU took."""
     l = xc.shape[1]
-    gq = O.e4m3_decode(xq[:, :l])
+    gq = gpu_codes(xq, elem)[:, :l]
     gs = xs[:, : l // 32]
-    _, _, osb = O.quantize_mx8(xc)
-    _, blk_amb = O.mx8_ambiguous(xc, MX8_ETA)
+    _, _, osb = O.quantize_mx(xc, elem)
+    _, blk_amb = O.mx_ambiguous(xc, elem, MX8_ETA)
     sflip = gs != osb
     _need(not np.any(sflip & ~blk_amb),
           f"x^c block exponents differ away from a power of two on tokens "
           f"{np.nonzero((sflip & ~blk_amb).any(1))[0][:8]}")
-    _, oq, _ = O.quantize_mx8(xc, scale_flip=sflip)
-    el_amb, _ = O.mx8_ambiguous(xc, MX8_ETA, scale_flip=sflip)
+    _, oq, _ = O.quantize_mx(xc, elem, scale_flip=sflip)
+    el_amb, _ = O.mx_ambiguous(xc, elem, MX8_ETA, scale_flip=sflip)
     eflip = gq != oq
     _need(not np.any(eflip & ~el_amb),
-          f"x^c codes differ away from an E4M3 midpoint on tokens "
+          f"x^c codes differ away from an {elem.upper()} midpoint on tokens "
           f"{np.nonzero((eflip & ~el_amb).any(1))[0][:8]}")
-    log(f"x^c MXFP8 decisions on a boundary taken the other way: {int(eflip.sum())} codes, "
+    log(f"x^c MX ({elem}) decisions on a boundary taken the other way: {int(eflip.sum())} codes, "
         f"{int(sflip.sum())} block exponents, on {int((eflip.any(1) | sflip.any(1)).sum())} tokens "
         f"(oracle-marked boundary values: {int(el_amb.sum())} codes, {int(blk_amb.sum())} blocks)")
     return eflip, sflip
@@ -91,8 +105,8 @@ def mx8_decisions(xc, xq, xs, log=print):
 def compare(OL, x, delta, idx, w, precision=None, ref=None, xcq=None, bars=True, log=print):
     """Compare GPU outputs (delta [T, d], idx and w [T, k], numpy) for the tokens x [T, d]
     (bf16 patterns) with the oracle layer OL in `precision` (the layer's own profile by
-    default; `ref`: that oracle's result for x, when already computed).  xcq: the GPU's MXFP8
-    x^c (codes, scale bytes) in the mx8 profile.  Raises ParityError when the index rule,
+    default; `ref`: that oracle's result for x, when already computed).  xcq: the GPU's MX
+    x^c (code rows, scale bytes) in an mx profile.  Raises ParityError when the index rule,
     the gate weights or (with `bars`) the Delta bars fail.  Returns a dict of the errors and
     the oracle's result under "ref"."""
     cfg = OL.cfg
@@ -110,8 +124,8 @@ def compare(OL, x, delta, idx, w, precision=None, ref=None, xcq=None, bars=True,
     ref_delta = ref.delta.copy()
     redo = ~same
     eflip = sflip = None
-    if prof == "mx8" and xcq is not None:
-        eflip, sflip = mx8_decisions(ref.xc, xcq[0], xcq[1], log)
+    if prof in O.MX_PROFILE_ELEMENT and xcq is not None:
+        eflip, sflip = mx_decisions(ref.xc, xcq[0], xcq[1], O.MX_PROFILE_ELEMENT[prof], log)
         redo = redo | eflip.any(1) | sflip.any(1)
     if np.any(~same):
         log(f"near-tie tokens {np.nonzero(~same)[0].tolist()[:16]} margins {ref.margin[~same].tolist()[:16]}")

@@ -56,7 +56,7 @@ def test_peak_probe_library_exports_its_header():
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 6 == moe.ABI_VERSION
+    assert L.moe_abi_version() == 7 == moe.ABI_VERSION
     assert moe.status_str(0) == "MOE_OK"
     assert moe.status_str(3) == "MOE_ERR_WORKSPACE"
     assert moe.status_str(99) == "MOE_ERR_UNKNOWN"
@@ -108,7 +108,8 @@ def _bad(**kw):
     ("act", 7, moe.MOE_ERR_INVALID_ARG),
     ("expert_wfmt", 5, moe.MOE_ERR_INVALID_ARG),
     ("precision", 1, moe.MOE_ERR_UNSUPPORTED),       # mx8 needs MXFP4 experts (toy: bf16)
-    ("precision", 2, moe.MOE_ERR_INVALID_ARG),
+    ("precision", 2, moe.MOE_ERR_UNSUPPORTED),       # so does mx4
+    ("precision", 3, moe.MOE_ERR_INVALID_ARG),
     ("d_shared", 0, moe.MOE_OK),                      # latent block without shared: fine
     ("expert_wfmt", 2, moe.MOE_OK),                   # FP8 block-128 experts
     ("rms_eps", float("nan"), moe.MOE_ERR_INVALID_ARG),

@@ -65,8 +65,8 @@ def assert_routing(idx, ridx, kap, margin):
 
 
 def gpu_xc_codes(lay, T):
-    """The MXFP8 codes and scale bytes of x^c that the last mx8 forward of `lay` left in its
-    workspace (numpy uint8 [T, 128 ks], [T, 4 ks])."""
+    """The MX code rows and scale bytes of x^c that the last mx forward of `lay` left in its
+    workspace (numpy uint8 [T, 128 ks] in mx8 or [T, 64 ks] in mx4, and [T, 4 ks])."""
     inter = lay.intermediates(T)
     return inter["xq"].cpu().numpy(), inter["xs"].cpu().numpy()
 
@@ -74,8 +74,8 @@ def gpu_xc_codes(lay, T):
 def check(cfg, x, delta, idx, w, rows=None, precision=None, ref=None, bars=True, xcq=None):
     """Compare GPU outputs for tokens `rows` of x against the oracle in `precision` (the
     layer's own profile by default; `ref`: that oracle's result for those rows) by the rule
-    of tests/parity.py.  xcq: the GPU's MXFP8 x^c (codes, scale bytes) of all of x, in the
-    mx8 profile.  Returns (rel-L2, max-abs / rms, the oracle's result)."""
+    of tests/parity.py.  xcq: the GPU's MX x^c (code rows, scale bytes) of all of x, in an
+    mx profile.  Returns (rel-L2, max-abs / rms, the oracle's result)."""
     rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
     r = P.compare(oracle_layer(cfg), x[rows], delta[rows], idx[rows], w[rows], precision=precision,
                   ref=ref, xcq=None if xcq is None else (xcq[0][rows], xcq[1][rows]), bars=bars,
@@ -360,6 +360,69 @@ def test_k3_ep_share_all_tokens():
     assert np.all(np.isfinite(delta))
     rel, mxr, _ = check(cfg, x, delta, idx, w, xcq=gpu_xc_codes(lay, x.shape[0]))
     assert rel < 1e-3
+
+
+# ---- the mx4 profile (MXFP4 expert inputs on the scaled FP4 x FP4 matrix cores) ---------
+# The same rule against the oracle in the mx4 profile.  E2M1 keeps two significant bits, so a
+# value of h that the GPU rounds to the other neighbour moves its product by up to a quarter
+# of the block's largest value: rare (h agrees to about 1e-6), and inside the bar.
+
+TINY_MX4 = TINY.with_(name="tiny_mx4", precision="mx4")
+RAGGED_MX4 = RAGGED.with_(name="ragged_mx4", precision="mx4")
+
+
+@pytest.mark.parametrize("T", [1, 5, 33, 100])
+def test_mx4_tiny_token_counts(T):
+    lay, _ = device_layer(TINY_MX4)
+    x = synth.tokens(TINY_MX4, batch=T, T=T)
+    out = run(lay, x)
+    check(TINY_MX4, x, *out, xcq=gpu_xc_codes(lay, T))
+
+
+@pytest.mark.parametrize("variant", ["ragged", "swiglu", "no_norm", "no_shared"])
+def test_mx4_widths_and_layer_variants(variant):
+    if variant == "ragged":
+        cfg = RAGGED_MX4
+    else:
+        kw = {"swiglu": dict(act="swiglu"), "no_norm": dict(use_norm=False), "no_shared": dict(ms=0)}[variant]
+        cfg = TINY_MX4.with_(name=f"tiny_mx4_{variant}", tokens=20, **kw)
+    lay, _ = device_layer(cfg)
+    x = synth.tokens(cfg)
+    out = run(lay, x)
+    check(cfg, x, *out, xcq=gpu_xc_codes(lay, x.shape[0]))
+
+
+def test_mx4_is_deterministic_and_token_independent():
+    lay, _ = device_layer(TINY_MX4)
+    x = to_dev(synth.tokens(TINY_MX4, batch=11, T=70))
+    a = [t.cpu().clone() for t in lay.forward(x)]
+    b = [t.cpu().clone() for t in lay.forward(x)]
+    for p, q in zip(a, b):
+        assert torch.equal(p, q)
+    one = [t.cpu().clone() for t in lay.forward(x[40:41].contiguous())]
+    assert torch.equal(one[1][0], a[1][40]) and torch.equal(one[0][0], a[0][40])
+
+
+def test_k3_prefill_8192_mx4_sampled_tokens():
+    """The K3 layer at prefill size in the mx4 profile: all 8192 tokens through the launches,
+    every 8th token (12 of each 96-token tile of the dense products) against the oracle in
+    the mx4 profile (the bars), and, informational, against the plain oracle."""
+    cfg = synth.K3_PREFILL_8K
+    lay8, _ = device_layer(cfg)
+    # the same packed weights through the mx4 launches (only the precision field differs)
+    lay = moe.Layer(moe.config_from(synth.K3_PREFILL_8K_MX4), lay8.dense, lay8.bias, lay8.experts)
+    x = synth.tokens(cfg, batch=0)
+    log(f"[k3 prefill mx4] T={x.shape[0]}")
+    delta, idx, w = run(lay, x)
+    assert np.all(np.isfinite(delta))
+    xcq = gpu_xc_codes(lay, x.shape[0])
+    del lay
+    rows = np.arange(0, x.shape[0], 8)
+    check(cfg, x, delta, idx, w, rows=rows, precision="mx4", xcq=xcq)
+    relq, mxq, _ = check(cfg, x, delta, idx, w, rows=rows, precision="fp32", bars=False)
+    log(f"[k3 prefill mx4] against the plain (fp32) oracle: rel-L2 {relq:.3e} max-abs/rms "
+        f"{mxq:.3e} (informational; the declared rounding points)")
+    assert relq < 0.3
 
 
 # ---- the K2-style non-latent block: FP8 E4M3 block-128 experts, SwiGLU, gate scale 2.827 --
