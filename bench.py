@@ -109,12 +109,12 @@ STEP_KERNELS = {"router": [("k_router", None), ("k_router_tt", None), ("k_token_
                 "expert_down": [("k_exp", "false"), ("k_exp_tt", "false")],
                 "combine": [("k_combine", None), ("k_norm", None)],
                 "out": [("k_out", None), ("k_out_tt", None)]}
-STEP_KERNELS_MX = {"router": [("k_pf_dense", "true")], "in": [("k_pf_quant", None)],
+STEP_KERNELS_MX = {"router": [("k_pf_pack_x", None), ("k_pf_gemm", "true")], "in": [("k_pf_quant", None)],
                     "route": [("k_route", None)],
                     "dispatch": [("k_disp_count", None), ("k_disp_scan", None), ("k_disp_scatter", None)],
                     "expert_gu": [("k_pf_exp", "true")], "expert_down": [("k_pf_exp", "false")],
                     "combine": [("k_pf_combine_norm", None), ("k_combine", None), ("k_pf_norm", None)],
-                    "out": [("k_pf_dense", "false")]}
+                    "out": [("k_pf_gemm", "false")]}
 
 
 def step_of_kernel(name, kernels):

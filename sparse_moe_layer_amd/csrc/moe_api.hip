@@ -91,8 +91,9 @@ constexpr int kHiloParts = 6;
 size_t hilo_part(const Shape& s, int64_t T, int part) {
   if (moe::mx_profile(s)) {
     const int64_t rows[6] = {T, T, T * s.k, T * s.k, T, T};
-    const int64_t bytes[6] = {128LL * s.ks_gu, 4LL * s.ks_gu, 128LL * s.ks_edn, 4LL * s.ks_edn,
-                              2LL * s.l, 2LL * s.ms};
+    if (part == 4) return align256(moe::pf_packed_bytes(s, T, true));
+    if (part == 5) return align256(moe::pf_packed_bytes(s, T, false));
+    const int64_t bytes[4] = {128LL * s.ks_gu, 4LL * s.ks_gu, 128LL * s.ks_edn, 4LL * s.ks_edn};
     return align256((size_t)(rows[part] * bytes[part]));
   }
   if (part >= 4) return 0;
@@ -160,8 +161,8 @@ moe::Work make_work(const Shape& s, int64_t T, void* ws, const size_t off[MOE_WS
     w.pf.xs = static_cast<uint8_t*>(parts[1]);
     w.pf.hq = static_cast<uint8_t*>(parts[2]);
     w.pf.hsc = static_cast<uint8_t*>(parts[3]);
-    w.pf.uh = static_cast<uint16_t*>(parts[4]);
-    w.pf.hs = static_cast<uint16_t*>(parts[5]);
+    w.pf.ao = static_cast<uint8_t*>(parts[4]);
+    w.pf.ax = static_cast<uint8_t*>(parts[5]);
   }
   w.perm = reinterpret_cast<int32_t*>(b + off[8]);
   w.inv = reinterpret_cast<int32_t*>(b + off[9]);

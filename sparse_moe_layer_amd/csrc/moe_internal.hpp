@@ -50,9 +50,13 @@ struct PfWork {
   uint8_t* xs;     // [T][4 ks_gu]      its E8M0 block scales
   uint8_t* hq;     // [T*k][128 ks_edn] h codes, dispatch order
   uint8_t* hsc;    // [T*k][4 ks_edn]
-  uint16_t* uh;    // [T][l]            u_hat in bf16
-  uint16_t* hs;    // [T][ms]           h_s in bf16
+  uint8_t* ao;     // the OUT product's input [u_hat | h_s] in bf16, packed rows of ks_out
+                   // K-steps (tiles of 16 rows, the packed weights' layout)
+  uint8_t* ax;     // the tokens x, packed rows of ks_in K-steps
 };
+// Bytes of the packed rows of T tokens (rounded up to whole 256-row tiles) for the OUT
+// product (out) or the IN product.
+size_t pf_packed_bytes(const Shape& s, int64_t T, bool out);
 
 // Row-major views of the workspace of one forward call.
 struct Work {

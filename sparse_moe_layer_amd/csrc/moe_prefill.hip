@@ -13,14 +13,13 @@
 //   (combine and the RMSNorm, u_hat rounded to bf16)
 //   k_pf_out     Delta = u_hat W_up_latent + h_s W_shared_down, one product over the packed
 //                OUT matrix (bf16 MFMA)
-//
-// Tiling: a workgroup multiplies a tile of 16 NB activation rows (NB <= 10) with 4 x NT
-// tile rows of weights (NT per wavefront: kPfNT for the experts, kPfDenseNT for the dense
-// products).  K advances one K-step (128 columns) at a
-// time: the activation rows of the next K-steps travel global -> registers -> LDS (two
-// LDS buffers, one barrier per K-step) while every wavefront streams its own weight
-// K-steps into registers, two K-steps ahead.  Each activation fragment read from LDS
-// feeds NT MFMAs and each weight fragment NB MFMAs.
+// The dense products (k_pf_gemm, below) take tiles of 256 x 256 with both operands staged
+// in LDS.  The experts: a workgroup multiplies a tile of 16 NB activation rows (NB <= 4)
+// with 4 x kPfNT tile rows of weights.  K advances one K-step (128 columns) at a time: the
+// activation rows of the next K-steps travel global -> registers -> LDS (two LDS buffers,
+// one barrier per K-step) while every wavefront streams its own weight K-steps into
+// registers, two K-steps ahead.  Each activation fragment read from LDS feeds kPfNT MFMAs
+// and each weight fragment NB MFMAs.
 #include <climits>
 #include <cmath>
 #include <type_traits>
@@ -33,16 +32,13 @@ namespace {
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kPfDenseNB = 6;    // dense products: tiles of 96 tokens
 constexpr int kPfExpNB = 4;      // routed experts: units of up to 64 positions
 static_assert(16 * kPfExpNB == kPfUnitPositions, "dispatch units fill one expert tile");
 // the most activation rows of a tile (the row tables hold this many)
-constexpr int kPfRows = 16 * (kPfDenseNB > kPfExpNB ? kPfDenseNB : kPfExpNB);
+constexpr int kPfRows = 16 * kPfExpNB;
 static_assert(kPfRows <= kBlock, "one thread per activation row sets the row tables");
 constexpr int kPfNT = 4;         // weight tile rows per wavefront: routed experts
-constexpr int kPfDenseNT = 2;    // dense products (2 workgroups per CU fit 256 registers)
 constexpr int kPfWaves = kBlock / kWave;
-constexpr int kPfDenseDepth = 2;   // K-steps in flight: bf16 weights (4 KiB per tile row)
 constexpr int kPfExpDepth = 2;     // MXFP4 weights (1 KiB per tile row)
 
 // D += A B^T on one 16x16 block over 128 K: A = 16 rows of FP8-E4M3 (32 bytes per lane,
@@ -145,38 +141,35 @@ __device__ __forceinline__ float swap_half_rows(float v) {
 }
 
 // ------------------------------------------------------------------------------------
-// The activation side of a tile.
-//   AF 0: bf16 rows, 16 pieces of 16 bytes per K-step; columns [0, n0) from segment 0
-//         (row r at word o0[r]), [c1, c1 + n1) from segment 1 (word o1[r]), zero elsewhere.
+// The activation side of an expert tile.
 //   AF 1: MXFP8 rows padded to whole K-steps (128 code bytes and 4 scale bytes per
 //         K-step): 8 pieces per K-step at word o0[r] + 8 q, the scale word at s0[r] + q.
 //   AF 2: MXFP4 rows, likewise with 64 code bytes per K-step: 4 pieces at word o0[r] + 4 q.
 // Rows r >= R are zero.  Thread piece i is idx = threadIdx + 256 i: row idx / PR, piece
 // idx % PR, so that consecutive threads read consecutive bytes of a row.  Every load is
-// issued (invalid pieces read word 0 of segment 0 and are zeroed when committed).  LDS
-// word of (piece j, row r): j * RB + (r ^ j), conflict-free for the writes of a row's
-// pieces and for the MFMA reads (16 lanes, one piece, 16 consecutive rows).
+// issued (invalid pieces read word 0 and are zeroed when committed).  LDS word of (piece
+// j, row r): j * RB + (r ^ j), conflict-free for the writes of a row's pieces and for the
+// MFMA reads (16 lanes, one piece, 16 consecutive rows).
 // ------------------------------------------------------------------------------------
 struct PfRows {
   uint32_t o0[kPfRows];
-  uint32_t o1[kPfRows];
   uint32_t s0[kPfRows];
 };
 struct PfSrc {
-  const uint4* b0;
-  const uint4* b1;
-  const uint32_t* sc;    // AF 1: scale words
-  int R, n0, c1, n1;
+  const uint4* b0;       // code words
+  const uint32_t* sc;    // scale words
+  int R;
 };
 
 template <int AF, int NB, int P>
 struct PfStage {
-  static constexpr int PR = AF == 2 ? 4 : AF == 1 ? 8 : 16;
+  static_assert(AF == 1 || AF == 2, "MX activations");
+  static constexpr int PR = AF == 2 ? 4 : 8;
   static constexpr int RB = 16 * NB;
   static constexpr int NP = (RB * PR + kBlock - 1) / kBlock;
   uint4 v[P][NP];
   uint32_t sv[P];
-  uint32_t o0[NP], o1[NP];
+  uint32_t o0[NP];
   bool rv[NP];
   uint32_t so;
   bool srv;
@@ -188,53 +181,32 @@ struct PfStage {
       const int r = row_of(i);
       rv[i] = r < RB && r < src.R;
       o0[i] = rv[i] ? rows.o0[r] : 0u;
-      o1[i] = rv[i] && !AF && src.n1 > 0 ? rows.o1[r] : 0u;
     }
-    srv = AF && (int)threadIdx.x < src.R && (int)threadIdx.x < RB;
+    srv = (int)threadIdx.x < src.R && (int)threadIdx.x < RB;
     so = srv ? rows.s0[threadIdx.x] : 0u;
-  }
-  __device__ __forceinline__ bool in0(int i, const PfSrc& src, int q) const {
-    return rv[i] && (AF || q * kStepK + 8 * piece_of(i) < src.n0);
-  }
-  __device__ __forceinline__ bool in1(int i, const PfSrc& src, int q) const {
-    const int col = q * kStepK + 8 * piece_of(i);
-    return !AF && rv[i] && col >= src.c1 && col < src.c1 + src.n1;
   }
   // K-step q into register slot `slot` (a constant once the caller's loop is unrolled)
   __device__ __forceinline__ void load(int slot, const PfSrc& src, int q) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      uint32_t w = 0u;
-      const uint4* base = src.b0;
-      if (AF) {
-        w = rv[i] ? o0[i] + (uint32_t)PR * q + piece_of(i) : 0u;
-      } else {
-        const int col = q * kStepK + 8 * piece_of(i);
-        const bool a0 = in0(i, src, q), a1 = in1(i, src, q);
-        w = a0 ? o0[i] + (col >> 3) : a1 ? o1[i] + ((col - src.c1) >> 3) : 0u;
-        base = a1 ? src.b1 : src.b0;
-      }
-      const uint4 x = base[w];
+      const uint4 x = src.b0[rv[i] ? o0[i] + (uint32_t)PR * q + piece_of(i) : 0u];
 #pragma unroll
       for (int sl = 0; sl < P; ++sl)
         if (sl == slot) v[sl][i] = x;
     }
-    if (AF) {
-      const uint32_t x = src.sc[srv ? so + q : 0u];
+    const uint32_t x = src.sc[srv ? so + q : 0u];
 #pragma unroll
-      for (int sl = 0; sl < P; ++sl)
-        if (sl == slot) sv[sl] = x;
-    }
+    for (int sl = 0; sl < P; ++sl)
+      if (sl == slot) sv[sl] = x;
   }
   // Register slot `slot`, holding K-step q, into an LDS buffer (invalid pieces as zeros).
-  __device__ __forceinline__ void commit(int slot, uint4* buf, uint32_t* sbuf, const PfSrc& src,
-                                         int q) const {
+  __device__ __forceinline__ void commit(int slot, uint4* buf, uint32_t* sbuf) const {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int idx = threadIdx.x + i * kBlock;
       if (idx < RB * PR) {
         const int r = idx / PR, j = idx % PR;
-        const bool z = !(in0(i, src, q) || in1(i, src, q));
+        const bool z = !rv[i];
         uint4 x = v[0][i];
 #pragma unroll
         for (int sl = 1; sl < P; ++sl)
@@ -242,7 +214,7 @@ struct PfStage {
         buf[j * RB + (r ^ j)] = make_uint4(z ? 0u : x.x, z ? 0u : x.y, z ? 0u : x.z, z ? 0u : x.w);
       }
     }
-    if (AF && (int)threadIdx.x < RB) {
+    if ((int)threadIdx.x < RB) {
       uint32_t x = sv[0];
 #pragma unroll
       for (int sl = 1; sl < P; ++sl)
@@ -252,16 +224,16 @@ struct PfStage {
   }
 };
 
-// The K loop of a tile: acc[t][b] = D of activation block b x the wavefront's tile row t
-// (trow[t]; waves or tile rows without work pass tile row 0 of the same matrix and drop
-// the result).  AF 0 pairs with bf16 weights (WF 0), AF 1 and 2 with MXFP4 weights (WF 1).  P
-// K-steps of weights and of activation rows are in flight (register rings, slot q % P
-// holds K-step q); the rows of K-step q + 1 go to LDS at the end of step q.
+// The K loop of an expert tile: acc[t][b] = D of activation block b x the wavefront's tile
+// row t (trow[t]; waves or tile rows without work pass tile row 0 of the same matrix and
+// drop the result), MX activations (AF 1, 2) against MXFP4 weights.  P K-steps of weights
+// and of activation rows are in flight (register rings, slot q % P holds K-step q); the
+// rows of K-step q + 1 go to LDS at the end of step q.
 template <int AF, int NB, int NT, int P>
 __device__ __forceinline__ void pf_run(const PfRows& rows, const PfSrc& src,
                                        const uint8_t* const (&trow)[NT], int ks, uint4* lds,
                                        uint32_t* slds, f32x4_t (&acc)[NT][NB]) {
-  constexpr int WF = AF ? 1 : 0;
+  constexpr int WF = 1;
   constexpr int RB = 16 * NB;
   constexpr int PR = PfStage<AF, NB, P>::PR;
   const int lane = threadIdx.x & (kWave - 1);
@@ -280,7 +252,7 @@ __device__ __forceinline__ void pf_run(const PfRows& rows, const PfSrc& src,
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[t][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   asm volatile("" ::: "memory");
-  st.commit(0, lds, slds, src, 0);
+  st.commit(0, lds, slds);
   __syncthreads();
   for (int q0 = 0; q0 < ks; q0 += P) {
 #pragma unroll
@@ -301,7 +273,7 @@ __device__ __forceinline__ void pf_run(const PfRows& rows, const PfSrc& src,
           for (int t = 0; t < NT; ++t)
             acc[t][b] = mfma_fp4_fp4(af, w[sl][t].w[0], sa, (w[sl][t].sc >> (8 * g)) & 0xFFu, acc[t][b]);
         }
-      } else if (AF) {
+      } else {
         const uint32_t* sb = slds + (q & 1) * RB;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -314,20 +286,6 @@ __device__ __forceinline__ void pf_run(const PfRows& rows, const PfSrc& src,
             acc[t][b] = mfma_fp8_fp4(alo, ahi, w[sl][t].w[0], sa, (w[sl][t].sc >> (8 * g)) & 0xFFu,
                                      acc[t][b]);
         }
-      } else {
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const int j = 4 * s4 + g;
-          uint4 af[NB];
-#pragma unroll
-          for (int b = 0; b < NB; ++b) af[b] = buf[j * RB + ((16 * b + c) ^ j)];
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const uint4 bw = w[sl][t].operand(s4, 0.f);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) acc[t][b] = mfma_bf16(af[b], bw, acc[t][b]);
-          }
-        }
       }
       // the K-step's products are issued before its slot is reloaded, so that the slot's old
       // and new values never overlap and keep one register set across the loop's back edge
@@ -339,26 +297,91 @@ __device__ __forceinline__ void pf_run(const PfRows& rows, const PfSrc& src,
 #pragma unroll
       for (int t = 0; t < NT; ++t) w[sl][t].template load<true>(trow[t], min(q + P, ks - 1), lane);
       asm volatile("" ::: "memory");
-      st.commit((sl + 1) % P, lds + ((q + 1) & 1) * RB * PR, slds + ((q + 1) & 1) * RB, src,
-                min(q + 1, ks - 1));
+      st.commit((sl + 1) % P, lds + ((q + 1) & 1) * RB * PR, slds + ((q + 1) & 1) * RB);
       __syncthreads();
     }
   }
 }
 
 // ------------------------------------------------------------------------------------
-// Dense products for a tile of up to 16 kPfDenseNB tokens: k_pf_in over the IN matrix (router
-// logits -> z, W_down_latent -> x^c fp32, shared gate/up -> SiTU -> h_s bf16), k_pf_out
-// over the OUT matrix (-> Delta).  Work item (tile-row group, token tile); the tiles of
-// one group run back to back on one XCD so that the group's weights come from its L2.
+// Dense products (bf16 MFMA 32x32x16): k_pf_gemm<true> over the IN matrix (router logits ->
+// z, W_down_latent -> x^c fp32, shared gate/up -> SiTU -> h_s bf16), k_pf_gemm<false> over
+// the OUT matrix (-> Delta).
+//
+// Both operands are packed rows: tiles of 16 rows, each a run of K-steps of 4 KiB in the
+// layout of the packed weights (sub-tile s of 32 columns: lane chunk 16 g + j holds row j,
+// columns 32 s + 8 g .. +8).  A 32-row MFMA operand of a 16-column slice then reads 4 runs
+// of 256 contiguous bytes (lanes 0-15 and 32-47 from one tile, 16-31 and 48-63 from the
+// next): no LDS bank conflicts, and the LDS copy of a tile's K-range is a straight copy of
+// its global bytes.
+//
+// A workgroup computes 256 rows x 256 weight rows (4 wavefronts of 128 x 128 in a 2 x 2
+// grid, 16 accumulator blocks of 32 x 32 each in the AGPRs, one wavefront per SIMD), K in
+// stages of 32 columns: the stage's 32 KiB (both operands) is copied global -> LDS directly
+// three stages ahead (a ring of five buffers, one barrier per stage; no staging registers),
+// and its operands are read into registers while the previous stage is multiplied.
+// Each wavefront reads 16 KiB of operands per stage for 32 products: 64 KiB of LDS reads
+// and 32 KiB of copies per CU against 1024 cycles of the matrix core, within LDS bandwidth
+// while the reads overlap the products.  XCD x runs groups of 4 row tiles x 8 weight tiles
+// together, so that its 32 workgroups in flight read each row tile 8 times and each weight
+// tile 4 times from its L2 at about the same K.
 // ------------------------------------------------------------------------------------
-struct PfDenseArgs {
-  const uint8_t* w;
-  int ks, tr_count, n_grp, n_tiles;
-  const uint16_t* a0;    // segment 0 rows (x, or u_hat bf16)
-  int lda0, n0;
-  const uint16_t* a1;    // segment 1 rows (h_s bf16) from column c1
-  int lda1, c1, n1;
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kGemmTile = 256;                 // rows and weight rows of a workgroup
+constexpr int kGemmTiles16 = kGemmTile / 16;   // 16-row tiles per operand
+constexpr int kGemmStageK = 32;                // columns per stage (one sub-tile)
+constexpr int kGemmStageWords = 2 * kGemmTiles16 * 64;   // 16-byte words of a stage: 32 KiB
+constexpr int kGemmThreads = 256;              // 4 wavefronts, one per SIMD
+static_assert(kGemmStageWords == 8 * kGemmThreads, "8 copies per thread and stage");
+constexpr int kGemmRing = 5;                   // stage buffers (160 KiB of LDS)
+static_assert(32 * 132 * 4 <= kGemmStageWords * 16, "an epilogue slab fits a stage buffer");
+constexpr int kGemmGroupM = 4, kGemmGroupN = 8;
+
+// Byte offset of (row r, column c) in packed rows of ks K-steps.
+__host__ __device__ __forceinline__ size_t packed_off(int64_t r, int c, int ks) {
+  return ((size_t)(r >> 4) * ks + (c >> 7)) * 4096 + (size_t)((c >> 5) & 3) * 1024 +
+         (size_t)((((c >> 3) & 3) << 4) + (int)(r & 15)) * 16 + (size_t)(c & 7) * 2;
+}
+// Rows of a packed activation buffer: the rows rounded up to whole workgroup tiles.
+__host__ __device__ inline int64_t packed_rows(int64_t T) { return (T + kGemmTile - 1) / kGemmTile * kGemmTile; }
+
+// x bf16 [T][d] -> packed rows of ks K-steps (rows T .. packed_rows(T) and columns past d
+// zero).  One thread per 8 columns of a row (reads follow the row).
+__global__ __launch_bounds__(kBlock) void k_pf_pack_x(const uint16_t* __restrict__ x, int64_t T, int d,
+                                                      int ks, int64_t rows, uint8_t* __restrict__ out) {
+  const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  const int cpr = ks * 16;                       // 8-column chunks per packed row
+  if (gid >= rows * cpr) return;
+  const int64_t r = gid / cpr;
+  const int c = (int)(gid - r * cpr) * 8;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (r < T && c < d) v = *reinterpret_cast<const uint4*>(x + r * d + c);
+  *reinterpret_cast<uint4*>(out + packed_off(r, c, ks)) = v;
+}
+
+// Work item of workgroup `bid`: (row tile mt, weight tile nt).  Groups of 4 x 8 tiles go
+// round-robin to the XCDs (bid % 8), the 32 workgroups of a group back to back on one XCD.
+__device__ __forceinline__ bool gemm_item(int bid, int n_m, int n_n, int& mt, int& nt) {
+  constexpr int per = kGemmGroupM * kGemmGroupN;
+  const int x = bid % kXcds, j = bid / kXcds;
+  const int g = (j / per) * kXcds + x, r = j % per;
+  const int gm = (n_m + kGemmGroupM - 1) / kGemmGroupM, gn = (n_n + kGemmGroupN - 1) / kGemmGroupN;
+  if (g >= gm * gn) return false;
+  mt = (g % gm) * kGemmGroupM + r % kGemmGroupM;
+  nt = (g / gm) * kGemmGroupN + r / kGemmGroupM;
+  return mt < n_m && nt < n_n;
+}
+__host__ inline int64_t gemm_grid(int64_t n_m, int64_t n_n) {
+  const int64_t per = kGemmGroupM * kGemmGroupN;
+  const int64_t groups = ((n_m + kGemmGroupM - 1) / kGemmGroupM) * ((n_n + kGemmGroupN - 1) / kGemmGroupN);
+  return ((groups + kXcds - 1) / kXcds) * kXcds * per;
+}
+
+struct PfGemmArgs {
+  const uint8_t* w;      // packed weights: tr_count tile rows of ks K-steps
+  const uint8_t* a;      // packed activation rows of ks K-steps (packed_rows(T) of them)
+  int ks, tr_count, n_m, n_n;
   int64_t T;
   // IN epilogue
   int tr_r, tr_dn;
@@ -366,86 +389,194 @@ struct PfDenseArgs {
   int E;
   float* xc;
   int l;
-  uint16_t* hs;
-  int ms, act;
+  uint8_t* ao;           // the OUT launch's packed rows: h_s from column hs_col0
+  int ks_out, hs_col0, ms, act;
   float bg, bl, rbg, rbl;
   // OUT epilogue
   OutSink sink;
   int d;
 };
 
+// One direct global -> LDS copy of 16 bytes per lane: lane l's bytes at `src` land at LDS
+// address lds + 16 l (lds wavefront-uniform).  Written as inline assembly so that the
+// compiler does not see an LDS write in flight and make every later LDS read wait for all
+// copies (the ring below waits for exactly the stage it reads); the instruction writes no
+// register.
+__device__ __forceinline__ void copy_to_lds(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+}
+
 template <bool IN>
-__global__ __launch_bounds__(kBlock, 2) void k_pf_dense(PfDenseArgs a) {
-  extern __shared__ uint4 sm[];
-  __shared__ PfRows rows;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = lane & 15, g = lane >> 4;
-  int grp, tile;
-  if (!xcd_item(blockIdx.x, a.n_grp, a.n_tiles, grp, tile)) return;
-  const int64_t t0 = (int64_t)tile * 16 * kPfDenseNB;
-  const int nt = (int)min((int64_t)16 * kPfDenseNB, a.T - t0);
-  if ((int)threadIdx.x < nt) {
-    rows.o0[threadIdx.x] = (uint32_t)((t0 + threadIdx.x) * a.lda0 / 8);
-    rows.o1[threadIdx.x] = (uint32_t)((t0 + threadIdx.x) * a.lda1 / 8);
-  }
+__global__ __launch_bounds__(kGemmThreads, 1) void k_pf_gemm(PfGemmArgs a) {
+  // the ring of stage buffers (16 row tiles, then 16 weight tiles, 1 KiB each): 160 KiB
+  __shared__ uint4 lds[kGemmRing * kGemmStageWords];
+  int mt, nt;
+  if (!gemm_item(blockIdx.x, a.n_m, a.n_n, mt, nt)) return;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv & 1, wn = wv >> 1;     // the wave's 128 rows and 128 weight rows
+  // Thread chunk i (0..7) of a stage: LDS word i * 256 + tid: operand i / 4 (row tiles, then
+  // weight tiles), tile 4 (i % 4) + wave, 16-byte piece lane of the tile's 1 KiB (one sub-tile
+  // of 32 columns).
+  const size_t tile_bytes = (size_t)a.ks * 4096;
+  const uint8_t* src_a = a.a + (size_t)(mt * kGemmTiles16 + wv) * tile_bytes + lane * 16;
+  const uint8_t* src_w = a.w + lane * 16;
+  const int tr0 = nt * kGemmTiles16 + wv;   // weight tile of chunk 4 + i: tr0 + 4 i (tile row 0 past the end)
+  const int nk = a.ks * (kStepK / kGemmStageK);
+  auto dma_stage = [&](const uint4* dst, int k) {
+    const uint32_t base = (uint32_t)(uintptr_t)dst + 1024u * wv;   // (low 32 bits: the LDS address)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      copy_to_lds(src_a + (size_t)(4 * i) * tile_bytes + (size_t)k * 1024,
+                  __builtin_amdgcn_readfirstlane(base + 4096u * i));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tr = tr0 + 4 * i;
+      copy_to_lds(src_w + (size_t)(tr < a.tr_count ? tr : 0) * tile_bytes + (size_t)k * 1024,
+                  __builtin_amdgcn_readfirstlane(base + 4096u * (4 + i)));
+    }
+  };
+  auto dma_clamped = [&](const uint4* dst, int k) { dma_stage(dst, k < nk ? k : nk - 1); };
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x16_t{};
+  // Operands: lane l takes row l % 32 of a 32-row block, columns 8 (l / 32) .. +8 of a
+  // 16-column slice h of the stage (lane chunk 16 (2 h + l / 32) + row of the sub-tile); row
+  // block mb = tiles 8 wm + 2 mb, +1; weight block nb = tiles 8 wn + 2 nb, +1.
+  const int lrow = lane & 31, lk = lane >> 5;
+  const int a_word = (8 * wm + (lrow >> 4)) * 64 + lk * 16 + (lrow & 15);
+  const int w_word = kGemmTiles16 * 64 + (8 * wn + (lrow >> 4)) * 64 + lk * 16 + (lrow & 15);
+  // Operands of one stage (both 16-column slices: 8 row pieces, 8 weight pieces) from LDS
+  // into registers, and the stage's 32 products from registers.
+  auto read_stage = [&](const uint4* L, uint4 (&af)[2][4], uint4 (&bw)[2][4]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) af[h][b] = L[a_word + 2 * b * 64 + 32 * h];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) bw[h][b] = L[w_word + 2 * b * 64 + 32 * h];
+    }
+  };
+  auto mma_slice = [&](const uint4 (&af)[2][4], const uint4 (&bw)[2][4], int h) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[h][mb]),
+                                                             __builtin_bit_cast(bf16x8_t, bw[h][nb]),
+                                                             acc[mb][nb], 0, 0, 0);
+  };
+  // Stage k lives in buffer k % 5.  Its copies are issued three stages ahead, its operands
+  // read into registers one stage ahead (while stage k - 1 is multiplied), so the matrix
+  // core never waits for LDS.  Iteration k: wait until this thread's copies of stage k + 1
+  // have landed (those of k + 2 and k + 3 may still fly: 16 instructions) and its reads of
+  // stage k - 1 are done (those of stage k, the last 16 LDS operations, may still fly but for
+  // the first: the wait counter holds 15 at most),
+  // barrier (the same for everyone), issue stage k + 4 into the buffer of stage k - 1, read
+  // stage k + 1 while multiplying stage k.  Past the last stage the copies and reads repeat
+  // it, unused.  (A bare s_barrier: __syncthreads() would also wait for every LDS read in
+  // flight.)
+  auto buf = [&](int k) -> const uint4* { return lds + (k % kGemmRing) * kGemmStageWords; };
+  auto wait_stage = [&]() {
+    asm volatile("s_waitcnt vmcnt(16) lgkmcnt(15)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  uint4 o0a[2][4], o0b[2][4], o1a[2][4], o1b[2][4];   // two register sets of operands
+  dma_stage(buf(0), 0);
+  dma_clamped(buf(1), 1);
+  dma_clamped(buf(2), 2);
+  dma_clamped(buf(3), 3);
+  asm volatile("s_waitcnt vmcnt(24)" ::: "memory");   // stage 0 has landed
   __syncthreads();
-  const uint8_t* trow[kPfDenseNT];
-  int tr[kPfDenseNT];
-#pragma unroll
-  for (int t = 0; t < kPfDenseNT; ++t) {
-    tr[t] = (grp * kPfWaves + wv) * kPfDenseNT + t;
-    trow[t] = a.w + (size_t)(tr[t] < a.tr_count ? tr[t] : 0) * a.ks * kBf16StepBytes;
+  read_stage(buf(0), o0a, o0b);
+  // Within an iteration: the first slice's 16 products, the next stage's 16 reads, the
+  // second slice's 16 products, pinned in that order (the wait counter for LDS holds 15
+  // operations, so each read that a product or the barrier waits for is 16 products old).
+  for (int k = 0; k < nk; k += 2) {
+    wait_stage();
+    dma_clamped(buf(k + 4), k + 4);
+    mma_slice(o0a, o0b, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_stage(buf(k + 1), o1a, o1b);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_slice(o0a, o0b, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_stage();
+    dma_clamped(buf(k + 5), k + 5);
+    mma_slice(o1a, o1b, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_stage(buf(k + 2), o0a, o0b);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_slice(o1a, o1b, 1);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  f32x4_t acc[kPfDenseNT][kPfDenseNB];
-  pf_run<0, kPfDenseNB, kPfDenseNT, kPfDenseDepth>(rows, PfSrc{reinterpret_cast<const uint4*>(a.a0), reinterpret_cast<const uint4*>(a.a1),
-                                  nullptr, nt, a.n0, a.c1, a.n1},
-                      trow, a.ks, sm, nullptr, acc);
-  const bool lo = c < 8;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the repeated reads
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the repeated copies, before LDS is reused
+  // Epilogue through LDS, 32 rows of the wavefront's 128 x 128 at a time: the accumulators
+  // (accumulator i of block (mb, nb): row 32 mb + 8 (i / 4) + 4 (l / 32) + i % 4, column
+  // 32 nb + l % 32 of the wave's tile) go to a wavefront-private fp32 slab of 32 rows x 128
+  // columns (row stride 132 words), then each lane takes 4 consecutive columns of a row:
+  // 16-byte stores, and a shared gate value meets its up value 8 columns further on.
+  __syncthreads();   // every wavefront is done with the last stage's operands
+  float* slab = reinterpret_cast<float*>(lds + wv * kGemmStageWords);
+  const int64_t rbase = (int64_t)mt * kGemmTile + 128 * wm;
+  const int nbase = nt * kGemmTile + 128 * wn;
 #pragma unroll
-  for (int t = 0; t < kPfDenseNT; ++t) {
+  for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
-    for (int b = 0; b < kPfDenseNB; ++b)
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int ti = 16 * b + 4 * g + v;
-        const int64_t tok = t0 + ti;
-        const float y = acc[t][b][v];
-        if (tr[t] >= a.tr_count) continue;
-        if (!IN) {
-          const int r = 16 * tr[t] + c;
-          if (ti < nt && r < a.d) store_out(a.sink, tok * a.d + r, y);
-        } else if (tr[t] < a.tr_r) {
-          const int e = 16 * tr[t] + c;
-          if (ti < nt && e < a.E) a.z[tok * a.E + e] = y;
-        } else if (tr[t] < a.tr_r + a.tr_dn) {
-          const int r = 16 * (tr[t] - a.tr_r) + c;
-          if (ti < nt && r < a.l) a.xc[tok * a.l + r] = y;
+      for (int i = 0; i < 16; ++i)
+        slab[(8 * (i >> 2) + 4 * lk + (i & 3)) * 132 + 32 * nb + lrow] = acc[mb][nb][i];
+    // (one wavefront writes and reads its own slab: its LDS operations complete in order)
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+      const int r = 2 * it + lk, c4 = 4 * lrow;        // row of the slab, first column
+      const int64_t row = rbase + 32 * mb + r;
+      const int n = nbase + c4;                        // first weight row of the four
+      const float4 y = *reinterpret_cast<const float4*>(slab + r * 132 + c4);
+      if (row >= a.T) continue;
+      if (!IN) {
+        if (n < a.d) {
+          const int64_t o = row * a.d + n;
+          store_out(a.sink, o, y.x); store_out(a.sink, o + 1, y.y);
+          store_out(a.sink, o + 2, y.z); store_out(a.sink, o + 3, y.w);
+        }
+        continue;
+      }
+      const int tr = n >> 4, cc = n & 15;              // tile row and its columns cc .. cc + 3
+      if (tr >= a.tr_count) continue;
+      if (tr < a.tr_r) {
+        const int e = 16 * tr + cc;
+        float* z = a.z + row * a.E + e;
+        if (e + 3 < a.E && (a.E & 3) == 0) *reinterpret_cast<float4*>(z) = y;
+        else {
+          if (e < a.E) z[0] = y.x;
+          if (e + 1 < a.E) z[1] = y.y;
+          if (e + 2 < a.E) z[2] = y.z;
+          if (e + 3 < a.E) z[3] = y.w;
+        }
+      } else if (tr < a.tr_r + a.tr_dn) {
+        const int r2 = 16 * (tr - a.tr_r) + cc;       // l is a multiple of 8
+        if (r2 < a.l) *reinterpret_cast<float4*>(a.xc + row * a.l + r2) = y;
+      } else if (cc < 8) {
+        // gate columns cc .. cc + 3, their up values at cc + 8: h_s columns hc .. hc + 3
+        const int hc = 8 * (tr - a.tr_r - a.tr_dn) + cc;
+        const float4 u = *reinterpret_cast<const float4*>(slab + r * 132 + c4 + 8);
+        if (hc < a.ms) {   // ms is a multiple of 8: all four columns
+          const float h0 = glu_act_fast(y.x, u.x, a.act, a.rbg, a.bg, a.rbl, a.bl);
+          const float h1 = glu_act_fast(y.y, u.y, a.act, a.rbg, a.bg, a.rbl, a.bl);
+          const float h2 = glu_act_fast(y.z, u.z, a.act, a.rbg, a.bg, a.rbl, a.bl);
+          const float h3 = glu_act_fast(y.w, u.w, a.act, a.rbg, a.bg, a.rbl, a.bl);
+          *reinterpret_cast<uint2*>(a.ao + packed_off(row, a.hs_col0 + hc, a.ks_out)) =
+              make_uint2(pack_bf16x2(h0, h1), pack_bf16x2(h2, h3));
         }
       }
+    }
   }
-  if (!IN) return;
-  // shared gate/up rows: tile rows t, t + 1 form a pair; lane c < 8 evaluates the h_s of
-  // tile row t (its gate, the up value of lane c + 8), lane c >= 8 that of tile row t + 1
-  const int sh0 = a.tr_r + a.tr_dn;
-#pragma unroll
-  for (int t = 0; t < kPfDenseNT; t += 2)
-#pragma unroll
-    for (int b = 0; b < kPfDenseNB; ++b)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float send = lo ? acc[t + 1][b][v] : acc[t][b][v];
-        const float recv = swap_half_rows(send);
-        const float gate = lo ? acc[t][b][v] : recv;
-        const float up = lo ? recv : acc[t + 1][b][v];
-        const int trm = tr[lo ? t : t + 1];
-        const int ti = 16 * b + 4 * g + v;
-        const int r = 8 * (trm - sh0) + (c & 7);
-        if (trm >= sh0 && trm < a.tr_count && ti < nt && r < a.ms) {
-          const float h = glu_act_fast(gate, up, a.act, a.rbg, a.bg, a.rbl, a.bl);
-          a.hs[(t0 + ti) * a.ms + r] = (uint16_t)(pack_bf16x2(h, 0.f) & 0xFFFFu);
-        }
-      }
 }
 
 // x^c fp32 [T][l] -> MX rows of ks K-steps: codes [T][128 ks] E4M3 bytes (FP4 false) or
@@ -538,9 +669,9 @@ __device__ __forceinline__ void pf_exp_unit(const PfExpArgs& a, const PfRows& ro
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane & 15, g = lane >> 4;
   f32x4_t acc[kPfNT][NB];
-  pf_run<AF, NB, kPfNT, kPfExpDepth>(rows, PfSrc{reinterpret_cast<const uint4*>(a.xq), nullptr,
-                                   reinterpret_cast<const uint32_t*>(a.xs), n, 0, 0, 0},
-                       trow, a.ks, sm, ssm, acc);
+  pf_run<AF, NB, kPfNT, kPfExpDepth>(rows, PfSrc{reinterpret_cast<const uint4*>(a.xq),
+                                                  reinterpret_cast<const uint32_t*>(a.xs), n},
+                                     trow, a.ks, sm, ssm, acc);
   if (!GU) {
 #pragma unroll
     for (int t = 0; t < kPfNT; ++t) {
@@ -655,11 +786,22 @@ __global__ __launch_bounds__(kBlock, 2) void k_pf_exp(PfExpArgs a) {
   else pf_exp_unit<GU, kPfExpNB, AF>(a, rows, sm, ssm, trow, tr, wblk, p0, n);
 }
 
-// u_hat = RMSNorm(u) * gamma rounded to bf16 (the OUT product's input), one workgroup per
-// token, in the fixed reduction order of the other paths.
+// Zero the padding columns of a token's packed OUT row: u_hat columns l .. 128 ks_l and
+// h_s columns ms .. 128 ks_ms (the padded weights there are zero, but 0 x a stale NaN is not).
+__device__ __forceinline__ void zero_out_pads(uint8_t* ao, int64_t t, int l, int ks_l, int ms,
+                                              int ks_ms, int ks_out) {
+  for (int c = l + (int)threadIdx.x; c < 128 * ks_l; c += kBlock)
+    *reinterpret_cast<uint16_t*>(ao + packed_off(t, c, ks_out)) = 0;
+  for (int c = ms + (int)threadIdx.x; c < 128 * ks_ms; c += kBlock)
+    *reinterpret_cast<uint16_t*>(ao + packed_off(t, 128 * ks_l + c, ks_out)) = 0;
+}
+
+// u_hat = RMSNorm(u) * gamma rounded to bf16 into the OUT product's packed rows, one
+// workgroup per token, in the fixed reduction order of the other paths.
 __global__ __launch_bounds__(kBlock) void k_pf_norm(const float* __restrict__ u,
                                                     const uint16_t* __restrict__ gamma, int l,
-                                                    int norm, float eps, uint16_t* __restrict__ uh) {
+                                                    int norm, float eps, uint8_t* __restrict__ ao,
+                                                    int ks_l, int ms, int ks_ms, int ks_out) {
   __shared__ float red[kPfWaves];
   const int64_t t = blockIdx.x;
   const float* ur = u + t * l;
@@ -681,8 +823,9 @@ __global__ __launch_bounds__(kBlock) void k_pf_norm(const float* __restrict__ u,
   for (int col = threadIdx.x; col < l; col += kBlock) {
     const float gm = norm ? __uint_as_float((uint32_t)gamma[col] << 16) : 1.f;
     const float v = norm ? ur[col] * inv * gm : ur[col];
-    uh[t * l + col] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
+    *reinterpret_cast<uint16_t*>(ao + packed_off(t, col, ks_out)) = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
   }
+  zero_out_pads(ao, t, l, ks_l, ms, ks_ms, ks_out);
 }
 
 // The combine and the norm in one pass, one workgroup per token, for the mx launches (whose
@@ -694,7 +837,7 @@ constexpr int kPfCnChunks = 8;
 __global__ __launch_bounds__(kBlock) void k_pf_combine_norm(
     const float* __restrict__ gw, const int32_t* __restrict__ inv, const float* __restrict__ eo,
     int k, int l, const uint16_t* __restrict__ gamma, int norm, float eps,
-    uint16_t* __restrict__ uh) {
+    uint8_t* __restrict__ ao, int ks_l, int ms, int ks_ms, int ks_out) {
   __shared__ float sg[kMaxK];
   __shared__ int si[kMaxK];
   __shared__ float red[kPfWaves];
@@ -763,11 +906,12 @@ __global__ __launch_bounds__(kBlock) void k_pf_combine_norm(
       }
       w[h] = pack_bf16x2(o[0], o[1]);
     }
-    *reinterpret_cast<uint2*>(uh + t * l + 4 * c4) = make_uint2(w[0], w[1]);
+    // columns 4 c4 .. +4 lie in one 8-column piece of the packed row
+    *reinterpret_cast<uint2*>(ao + packed_off(t, 4 * c4, ks_out)) = make_uint2(w[0], w[1]);
   }
+  zero_out_pads(ao, t, l, ks_l, ms, ks_ms, ks_out);
 }
 
-constexpr size_t kPfDenseLds = (size_t)2 * 16 * kPfDenseNB * 16 * 16;   // two K-steps of the bf16 rows
 // two K-steps of the FP8 rows, and room for the gate/up epilogue's wavefront-private tiles
 constexpr size_t kPfExpEpiLds = (size_t)kPfWaves * 16 * 36 * 4;
 constexpr size_t kPfExpLds = (size_t)2 * 16 * kPfExpNB * 8 * 16 > kPfExpEpiLds
@@ -777,22 +921,24 @@ constexpr size_t kPfExpLds = (size_t)2 * 16 * kPfExpNB * 8 * 16 > kPfExpEpiLds
 
 hipError_t launch_pf_in(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,
                         const PfWork& pw, float* z, float* xc, hipStream_t st) {
-  PfDenseArgs a{};
+  const int64_t rows = packed_rows(T);
+  hipLaunchKernelGGL(k_pf_pack_x, dim3((unsigned)cdiv(rows * s.ks_in * 16, kBlock)), dim3(kBlock), 0, st,
+                     x, T, s.d, s.ks_in, rows, pw.ax);
+  PfGemmArgs a{};
   a.w = dense;
+  a.a = pw.ax;
   a.ks = s.ks_in;
   a.tr_count = s.tr_in;
-  a.n_grp = cdiv(s.tr_in, kPfWaves * kPfDenseNT);
-  a.n_tiles = cdiv(T, 16 * kPfDenseNB);
-  a.a0 = x; a.lda0 = s.d; a.n0 = s.d;
-  a.a1 = x; a.lda1 = 0; a.c1 = 0; a.n1 = 0;
+  a.n_m = cdiv(T, kGemmTile);
+  a.n_n = cdiv(s.tr_in, kGemmTiles16);
   a.T = T;
   a.tr_r = s.tr_r; a.tr_dn = s.tr_dn;
   a.z = z; a.E = s.E;
   a.xc = xc; a.l = s.l;
-  a.hs = pw.hs; a.ms = s.ms; a.act = s.act; a.bg = s.beta_gate; a.bl = s.beta_lin;
+  a.ao = pw.ao; a.ks_out = s.ks_out; a.hs_col0 = s.ks_l * kStepK;
+  a.ms = s.ms; a.act = s.act; a.bg = s.beta_gate; a.bl = s.beta_lin;
   a.rbg = 1.f / s.beta_gate; a.rbl = 1.f / s.beta_lin;
-  hipLaunchKernelGGL(k_pf_dense<true>, dim3((unsigned)xcd_grid(a.n_grp, a.n_tiles)), dim3(kBlock),
-                     kPfDenseLds, st, a);
+  hipLaunchKernelGGL(k_pf_gemm<true>, dim3((unsigned)gemm_grid(a.n_m, a.n_n)), dim3(kGemmThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -852,7 +998,7 @@ hipError_t launch_pf_combine_norm(const Shape& s, const uint8_t* dense, const fl
   hipLaunchKernelGGL(k_pf_combine_norm, dim3((unsigned)T), dim3(kBlock), 0, st, gw,
                      (const int32_t*)ws.inv, (const float*)ws.eo, s.k, s.l,
                      reinterpret_cast<const uint16_t*>(dense + s.gamma_off), s.use_norm, s.eps,
-                     pw.uh);
+                     pw.ao, s.ks_l, s.ms, s.ks_ms, s.ks_out);
   return hipGetLastError();
 }
 
@@ -860,25 +1006,27 @@ hipError_t launch_pf_norm(const Shape& s, const uint8_t* dense, int64_t T, const
                           const PfWork& pw, hipStream_t st) {
   hipLaunchKernelGGL(k_pf_norm, dim3((unsigned)T), dim3(kBlock), 0, st, (const float*)ws.u,
                      reinterpret_cast<const uint16_t*>(dense + s.gamma_off), s.l, s.use_norm, s.eps,
-                     pw.uh);
+                     pw.ao, s.ks_l, s.ms, s.ks_ms, s.ks_out);
   return hipGetLastError();
 }
 
 hipError_t launch_pf_out(const Shape& s, const uint8_t* dense, int64_t T, const PfWork& pw,
                          const OutSink& out, hipStream_t st) {
-  PfDenseArgs a{};
+  PfGemmArgs a{};
   a.w = dense + s.in_bytes;
+  a.a = pw.ao;
   a.ks = s.ks_out;
   a.tr_count = s.tr_out;
-  a.n_grp = cdiv(s.tr_out, kPfWaves * kPfDenseNT);
-  a.n_tiles = cdiv(T, 16 * kPfDenseNB);
-  a.a0 = pw.uh; a.lda0 = s.l; a.n0 = s.l;
-  a.a1 = s.ms > 0 ? pw.hs : pw.uh; a.lda1 = s.ms; a.c1 = s.ks_l * kStepK; a.n1 = s.ms;
+  a.n_m = cdiv(T, kGemmTile);
+  a.n_n = cdiv(s.tr_out, kGemmTiles16);
   a.T = T;
   a.sink = out; a.d = s.d;
-  hipLaunchKernelGGL(k_pf_dense<false>, dim3((unsigned)xcd_grid(a.n_grp, a.n_tiles)), dim3(kBlock),
-                     kPfDenseLds, st, a);
+  hipLaunchKernelGGL(k_pf_gemm<false>, dim3((unsigned)gemm_grid(a.n_m, a.n_n)), dim3(kGemmThreads), 0, st, a);
   return hipGetLastError();
+}
+
+size_t pf_packed_bytes(const Shape& s, int64_t T, bool out) {
+  return (size_t)packed_rows(T) * (out ? s.ks_out : s.ks_in) * kStepK * 2;
 }
 
 }  // namespace moe
