@@ -347,17 +347,21 @@ __host__ __device__ __forceinline__ size_t packed_off(int64_t r, int c, int ks) 
 __host__ __device__ inline int64_t packed_rows(int64_t T) { return (T + kGemmTile - 1) / kGemmTile * kGemmTile; }
 
 // x bf16 [T][d] -> packed rows of ks K-steps (rows T .. packed_rows(T) and columns past d
-// zero).  One thread per 8 columns of a row (reads follow the row).
+// zero).  One thread per 16-byte piece of the packed buffer, in its order: the writes are
+// contiguous, and the 64 lanes of a wavefront read 64 contiguous bytes of each of 16 rows.
 __global__ __launch_bounds__(kBlock) void k_pf_pack_x(const uint16_t* __restrict__ x, int64_t T, int d,
                                                       int ks, int64_t rows, uint8_t* __restrict__ out) {
-  const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  const int cpr = ks * 16;                       // 8-column chunks per packed row
-  if (gid >= rows * cpr) return;
-  const int64_t r = gid / cpr;
-  const int c = (int)(gid - r * cpr) * 8;
+  const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;   // piece of the packed buffer
+  if (gid >= rows * ks * 16) return;
+  const int64_t tq = gid >> 8;                   // (16-row tile, K-step)
+  const int p = (int)(gid & 255);                // lane chunk of the K-step: 64 s + 16 g + j
+  const int64_t t = tq / ks;
+  const int q = (int)(tq - t * ks);
+  const int64_t r = 16 * t + (p & 15);
+  const int c = 128 * q + 32 * (p >> 6) + 8 * ((p >> 4) & 3);
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
   if (r < T && c < d) v = *reinterpret_cast<const uint4*>(x + r * d + c);
-  *reinterpret_cast<uint4*>(out + packed_off(r, c, ks)) = v;
+  reinterpret_cast<uint4*>(out)[gid] = v;
 }
 
 // Work item of workgroup `bid`: (row tile mt, weight tile nt).  Groups of 4 x 8 tiles go
