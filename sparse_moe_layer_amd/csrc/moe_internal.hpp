@@ -104,7 +104,9 @@ constexpr int kTiledUnitPositions = 32;
 // the token-tiled launches holds up to 64 positions: an expert's weights are read once per 64
 // of its positions.  The launches whose input is hi/lo rows take such a unit in two halves.
 constexpr int kTiledUnitPositionsSingle = 64;
-constexpr int kPfUnitPositions = 64;   // 16 x the expert tile blocks of moe_prefill.hip
+// Positions per unit of the mx launches (10 blocks of 16 rows in the expert tile); an
+// expert's positions split into near-equal runs (even_units).
+constexpr int kPfUnitPositions = 160;
 // Positions of one expert per unit of the expert launches (2 hi/lo rows each; one FP8
 // row each in the mx launches).
 inline int unit_positions(const Shape& s, int64_t T) {
@@ -117,6 +119,9 @@ inline int unit_positions(const Shape& s, int64_t T) {
   const int t = T < 1 ? 1 : (int)T;
   return t < fit ? t : fit;
 }
+// Whether an expert's positions split into near-equal units (the mx launches, whose tile
+// height follows the unit) or into full units and a tail.
+inline bool even_units(const Shape& s) { return mx_profile(s); }
 inline int64_t max_units(const Shape& s, int64_t T) {
   const int64_t n = T * s.k, nu = unit_positions(s, T);
   const int64_t b = n / nu + (n < s.E ? n : s.E);

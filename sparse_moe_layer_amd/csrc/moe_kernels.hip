@@ -57,6 +57,7 @@ struct RouteArgs {
   int32_t* units;   // unit table of the expert launches (dispatch only)
   int32_t* ctrl;    // ctrl[0] <- number of units, ctrl[1] <- the same (dispatch only)
   int nu;           // positions per unit
+  int even;         // units of an expert near-equal (unit_run)
 };
 
 constexpr int kRouteSlots = 4;      // E <= 4 slots x 4 wavefronts x 64 lanes = 1024
@@ -156,6 +157,20 @@ __device__ __forceinline__ void block_route_token(const RouteArgs& a, int64_t t,
   __syncthreads();
 }
 
+// Unit i of the ceil(tot / nu) units of an expert's tot positions: first position r0 and
+// count n.  Full units of nu and a shorter last one, or (even) near-equal runs whose
+// counts differ by at most one.
+__device__ __forceinline__ void unit_run(int tot, int nu, int even, int i, int& r0, int& n) {
+  if (even) {
+    const int nun = (tot + nu - 1) / nu, base = tot / nun, rem = tot - base * nun;
+    r0 = i * base + min(i, rem);
+    n = base + (i < rem ? 1 : 0);
+  } else {
+    r0 = i * nu;
+    n = min(nu, tot - r0);
+  }
+}
+
 // The route of tokens t_begin..t_end-1 by one workgroup; with `dispatch`, also the
 // counting sort of their (at most 256) assignments by expert.
 __device__ void route_block(const RouteArgs& a, int64_t t_begin, int64_t t_end, bool dispatch) {
@@ -207,8 +222,12 @@ __device__ void route_block(const RouteArgs& a, int64_t t_begin, int64_t t_end, 
       soff[e] = run;
       a.offs[e] = run;
       a.counts[e] = loc[i];
-      for (int r0 = 0; r0 < loc[i]; r0 += a.nu, ++urun)
-        *reinterpret_cast<int4*>(a.units + 4 * urun) = make_int4(e, run + r0, min(a.nu, loc[i] - r0), 0);
+      const int nun = (loc[i] + a.nu - 1) / a.nu;
+      for (int j = 0; j < nun; ++j, ++urun) {
+        int r0, cnt;
+        unit_run(loc[i], a.nu, a.even, j, r0, cnt);
+        *reinterpret_cast<int4*>(a.units + 4 * urun) = make_int4(e, run + r0, cnt, 0);
+      }
     }
     run += loc[i];
   }
@@ -252,8 +271,9 @@ __global__ __launch_bounds__(kBlock) void k_disp_count(const int32_t* idx, int64
 }
 
 // Units of at most `small` positions come first in the table (ctrl[1] of them), then
-// the larger ones; ctrl[0] = all units.  Each list runs in expert order.
-__global__ __launch_bounds__(1024) void k_disp_scan(int n_chunks, int E, int nu, int small,
+// the larger ones; ctrl[0] = all units.  Each list runs in expert order.  (With `even`
+// the units of an expert are near-equal, unit_run, and small >= nu: one list.)
+__global__ __launch_bounds__(1024) void k_disp_scan(int n_chunks, int E, int nu, int small, int even,
                                                     int32_t* chunk_hist, int32_t* counts,
                                                     int32_t* offs, int32_t* units,
                                                     int32_t* ctrl) {
@@ -279,11 +299,12 @@ __global__ __launch_bounds__(1024) void k_disp_scan(int n_chunks, int E, int nu,
     }
     counts[e] = tot;
   }
-  // this expert's units: tot / nu full ones and a tail of tot % nu positions
+  // this expert's units: tot / nu full ones and a tail of tot % nu positions (or, even,
+  // ceil(tot / nu) units of at most nu <= small positions)
   const int full = tot / nu, tail = tot - full * nu;
   const bool full_small = nu <= small;
-  const int ns = (e < E) ? (full_small ? full : 0) + (tail > 0 && tail <= small) : 0;
-  const int nb = (e < E) ? (full_small ? 0 : full) + (tail > small) : 0;
+  const int ns = (e < E) ? (even ? (tot + nu - 1) / nu : (full_small ? full : 0) + (tail > 0 && tail <= small)) : 0;
+  const int nb = (e < E && !even) ? (full_small ? 0 : full) + (tail > small) : 0;
   sc[e] = (e < E) ? tot : 0;
   su[e] = ns;
   sb[e] = nb;
@@ -303,9 +324,11 @@ __global__ __launch_bounds__(1024) void k_disp_scan(int n_chunks, int E, int nu,
     const int off = sc[e] - tot;
     offs[e] = off;
     int us = su[e] - ns, ub = n_small + sb[e] - nb;
-    for (int r0 = 0; r0 < tot; r0 += nu) {
-      const int n = min(nu, tot - r0);
-      const int slot = n <= small ? us++ : ub++;
+    const int nun = (tot + nu - 1) / nu;
+    for (int j = 0; j < nun; ++j) {
+      int r0, n;
+      unit_run(tot, nu, even, j, r0, n);
+      const int slot = (even || n <= small) ? us++ : ub++;
       *reinterpret_cast<int4*>(units + 4 * slot) = make_int4(e, off + r0, n, 0);
     }
   }
@@ -1801,7 +1824,8 @@ namespace {
 RouteArgs route_args(const Shape& s, const float* bias, int64_t T, const Work& ws, int32_t* idx,
                      float* gw) {
   return RouteArgs{ws.z, route_planes(s), T * s.E, bias, T, s.E, s.k, s.route_scale, idx, gw,
-                   ws.counts, ws.offs, ws.perm, ws.inv, ws.units, ws.ctrl, unit_positions(s, T)};
+                   ws.counts, ws.offs, ws.perm, ws.inv, ws.units, ws.ctrl, unit_positions(s, T),
+                   (int)even_units(s)};
 }
 
 // Wavefronts per tile row: split K until a single token's launch has enough wavefronts
@@ -1979,7 +2003,8 @@ hipError_t launch_dispatch(const Shape& s, const int32_t* idx, int64_t T, int32_
   const int nch = cdiv(T, ct);
   hipLaunchKernelGGL(k_disp_count, dim3(nch), dim3(kBlock), 0, st, idx, n, s.E, chunk, chunk_hist);
   hipLaunchKernelGGL(k_disp_scan, dim3(1), dim3(1024), 0, st, nch, s.E, unit_positions(s, T),
-                     small_unit_positions(s, T), chunk_hist, counts, offs, units, ctrl);
+                     small_unit_positions(s, T), (int)even_units(s), chunk_hist, counts, offs,
+                     units, ctrl);
   hipLaunchKernelGGL(k_disp_scatter, dim3(nch), dim3(kBlock), 0, st, idx, n, s.E, chunk,
                      (const int32_t*)chunk_hist, (const int32_t*)offs, perm, inv);
   return hipGetLastError();

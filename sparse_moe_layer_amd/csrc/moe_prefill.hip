@@ -13,13 +13,9 @@
 //   (combine and the RMSNorm, u_hat rounded to bf16)
 //   k_pf_out     Delta = u_hat W_up_latent + h_s W_shared_down, one product over the packed
 //                OUT matrix (bf16 MFMA)
-// The dense products (k_pf_gemm, below) take tiles of 256 x 256 with both operands staged
-// in LDS.  The experts: a workgroup multiplies a tile of 16 NB activation rows (NB <= 4)
-// with 4 x kPfNT tile rows of weights.  K advances one K-step (128 columns) at a time: the
-// activation rows of the next K-steps travel global -> registers -> LDS (two LDS buffers,
-// one barrier per K-step) while every wavefront streams its own weight K-steps into
-// registers, two K-steps ahead.  Each activation fragment read from LDS feeds kPfNT MFMAs
-// and each weight fragment NB MFMAs.
+// The dense products (k_pf_gemm) take tiles of 256 x 256, the experts (k_pf_exp) tiles of
+// one unit's rows (up to 160) x 256 weight rows; both copy their operands global -> LDS
+// directly into a ring of K stages, one workgroup per compute unit.
 #include <climits>
 #include <cmath>
 #include <type_traits>
@@ -32,14 +28,7 @@ namespace {
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kPfExpNB = 4;      // routed experts: units of up to 64 positions
-static_assert(16 * kPfExpNB == kPfUnitPositions, "dispatch units fill one expert tile");
-// the most activation rows of a tile (the row tables hold this many)
-constexpr int kPfRows = 16 * kPfExpNB;
-static_assert(kPfRows <= kBlock, "one thread per activation row sets the row tables");
-constexpr int kPfNT = 4;         // weight tile rows per wavefront: routed experts
 constexpr int kPfWaves = kBlock / kWave;
-constexpr int kPfExpDepth = 2;     // MXFP4 weights (1 KiB per tile row)
 
 // D += A B^T on one 16x16 block over 128 K: A = 16 rows of FP8-E4M3 (32 bytes per lane,
 // lane l: row l % 16, K 16 (l/16) .. +16 in bytes 0..15 and K 64 + 16 (l/16) .. +16 in
@@ -103,15 +92,21 @@ __device__ __forceinline__ uint32_t pack8_e2m1(float4 x0, float4 x1, float inv) 
 
 // tanh of the compute-bound epilogues: the odd series x (1 - x^2/3 + 2 x^4/15) below
 // |x| = 1/16 (relative error < 1e-8 there), else (1 - e^-2|x|) / (1 + e^-2|x|) with the
-// hardware exponential (relative error below 1e-6), sign restored.
+// hardware exponential and reciprocal (v_exp_f32, v_rcp_f32: about 1 ulp each; relative
+// error below 1e-6), sign restored.  (A plain division compiles to the IEEE sequence of
+// about ten instructions.)
+constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float tanh_fast(float x) {
   const float ax = fabsf(x), x2 = x * x;
   const float series = x * (1.f + x2 * (-1.f / 3.f + x2 * (2.f / 15.f)));
-  const float e = __expf(-2.f * ax);
-  const float r = __fdividef(1.f - e, 1.f + e);
+  const float e = __builtin_amdgcn_exp2f(-2.f * kLog2e * ax);
+  const float r = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
   return ax < 0.0625f ? series : copysignf(r, x);
 }
-__device__ __forceinline__ float sigmoid_fast(float g) { return __fdividef(1.f, 1.f + __expf(-g)); }
+// (e^-g past the fp32 range: the reciprocal of infinity is 0)
+__device__ __forceinline__ float sigmoid_fast(float g) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * g));
+}
 
 // SiTU-GLU (act 0) or SwiGLU (act 1) with the fast tanh and sigmoid; rbg, rbl = 1 / beta.
 __device__ __forceinline__ float glu_act_fast(float g, float u, int act, float rbg, float bg,
@@ -138,169 +133,6 @@ __device__ __forceinline__ float quad_perm_f32(float v) {
 // The value of lane c ^ 8 within each 16-lane row (DPP row rotate by 8).
 __device__ __forceinline__ float swap_half_rows(float v) {
   return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0x128, 0xF, 0xF, false));
-}
-
-// ------------------------------------------------------------------------------------
-// The activation side of an expert tile.
-//   AF 1: MXFP8 rows padded to whole K-steps (128 code bytes and 4 scale bytes per
-//         K-step): 8 pieces per K-step at word o0[r] + 8 q, the scale word at s0[r] + q.
-//   AF 2: MXFP4 rows, likewise with 64 code bytes per K-step: 4 pieces at word o0[r] + 4 q.
-// Rows r >= R are zero.  Thread piece i is idx = threadIdx + 256 i: row idx / PR, piece
-// idx % PR, so that consecutive threads read consecutive bytes of a row.  Every load is
-// issued (invalid pieces read word 0 and are zeroed when committed).  LDS word of (piece
-// j, row r): j * RB + (r ^ j), conflict-free for the writes of a row's pieces and for the
-// MFMA reads (16 lanes, one piece, 16 consecutive rows).
-// ------------------------------------------------------------------------------------
-struct PfRows {
-  uint32_t o0[kPfRows];
-  uint32_t s0[kPfRows];
-};
-struct PfSrc {
-  const uint4* b0;       // code words
-  const uint32_t* sc;    // scale words
-  int R;
-};
-
-template <int AF, int NB, int P>
-struct PfStage {
-  static_assert(AF == 1 || AF == 2, "MX activations");
-  static constexpr int PR = AF == 2 ? 4 : 8;
-  static constexpr int RB = 16 * NB;
-  static constexpr int NP = (RB * PR + kBlock - 1) / kBlock;
-  uint4 v[P][NP];
-  uint32_t sv[P];
-  uint32_t o0[NP];
-  bool rv[NP];
-  uint32_t so;
-  bool srv;
-  __device__ __forceinline__ int row_of(int i) const { return (threadIdx.x + i * kBlock) / PR; }
-  __device__ __forceinline__ int piece_of(int i) const { return (threadIdx.x + i * kBlock) % PR; }
-  __device__ __forceinline__ void init(const PfRows& rows, const PfSrc& src) {
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int r = row_of(i);
-      rv[i] = r < RB && r < src.R;
-      o0[i] = rv[i] ? rows.o0[r] : 0u;
-    }
-    srv = (int)threadIdx.x < src.R && (int)threadIdx.x < RB;
-    so = srv ? rows.s0[threadIdx.x] : 0u;
-  }
-  // K-step q into register slot `slot` (a constant once the caller's loop is unrolled)
-  __device__ __forceinline__ void load(int slot, const PfSrc& src, int q) {
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const uint4 x = src.b0[rv[i] ? o0[i] + (uint32_t)PR * q + piece_of(i) : 0u];
-#pragma unroll
-      for (int sl = 0; sl < P; ++sl)
-        if (sl == slot) v[sl][i] = x;
-    }
-    const uint32_t x = src.sc[srv ? so + q : 0u];
-#pragma unroll
-    for (int sl = 0; sl < P; ++sl)
-      if (sl == slot) sv[sl] = x;
-  }
-  // Register slot `slot`, holding K-step q, into an LDS buffer (invalid pieces as zeros).
-  __device__ __forceinline__ void commit(int slot, uint4* buf, uint32_t* sbuf) const {
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int idx = threadIdx.x + i * kBlock;
-      if (idx < RB * PR) {
-        const int r = idx / PR, j = idx % PR;
-        const bool z = !rv[i];
-        uint4 x = v[0][i];
-#pragma unroll
-        for (int sl = 1; sl < P; ++sl)
-          if (sl == slot) x = v[sl][i];
-        buf[j * RB + (r ^ j)] = make_uint4(z ? 0u : x.x, z ? 0u : x.y, z ? 0u : x.z, z ? 0u : x.w);
-      }
-    }
-    if ((int)threadIdx.x < RB) {
-      uint32_t x = sv[0];
-#pragma unroll
-      for (int sl = 1; sl < P; ++sl)
-        if (sl == slot) x = sv[sl];
-      sbuf[threadIdx.x] = srv ? x : 0u;
-    }
-  }
-};
-
-// The K loop of an expert tile: acc[t][b] = D of activation block b x the wavefront's tile
-// row t (trow[t]; waves or tile rows without work pass tile row 0 of the same matrix and
-// drop the result), MX activations (AF 1, 2) against MXFP4 weights.  P K-steps of weights
-// and of activation rows are in flight (register rings, slot q % P holds K-step q); the
-// rows of K-step q + 1 go to LDS at the end of step q.
-template <int AF, int NB, int NT, int P>
-__device__ __forceinline__ void pf_run(const PfRows& rows, const PfSrc& src,
-                                       const uint8_t* const (&trow)[NT], int ks, uint4* lds,
-                                       uint32_t* slds, f32x4_t (&acc)[NT][NB]) {
-  constexpr int WF = 1;
-  constexpr int RB = 16 * NB;
-  constexpr int PR = PfStage<AF, NB, P>::PR;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int c = lane & 15, g = lane >> 4;
-  WeightStep<WF> w[P][NT];
-  PfStage<AF, NB, P> st;
-  st.init(rows, src);
-#pragma unroll
-  for (int i = 0; i < P; ++i) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) w[i][t].template load<true>(trow[t], min(i, ks - 1), lane);
-    st.load(i, src, min(i, ks - 1));
-  }
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[t][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  asm volatile("" ::: "memory");
-  st.commit(0, lds, slds);
-  __syncthreads();
-  for (int q0 = 0; q0 < ks; q0 += P) {
-#pragma unroll
-    for (int sl = 0; sl < P; ++sl) {
-      const int q = q0 + sl;
-      if (q >= ks) break;
-      // slot sl held K-step q (already in LDS buffer q & 1): refill it with q + P
-      st.load(sl, src, min(q + P, ks - 1));
-      const uint4* buf = lds + (q & 1) * RB * PR;
-      if (AF == 2) {
-        const uint32_t* sb = slds + (q & 1) * RB;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const int r = 16 * b + c;
-          const uint4 af = buf[g * RB + (r ^ g)];
-          const uint32_t sa = (sb[r] >> (8 * g)) & 0xFFu;
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-            acc[t][b] = mfma_fp4_fp4(af, w[sl][t].w[0], sa, (w[sl][t].sc >> (8 * g)) & 0xFFu, acc[t][b]);
-        }
-      } else {
-        const uint32_t* sb = slds + (q & 1) * RB;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const int r = 16 * b + c;
-          const uint4 alo = buf[g * RB + (r ^ g)];
-          const uint4 ahi = buf[(4 + g) * RB + (r ^ (4 + g))];
-          const uint32_t sa = (sb[r] >> (8 * g)) & 0xFFu;
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-            acc[t][b] = mfma_fp8_fp4(alo, ahi, w[sl][t].w[0], sa, (w[sl][t].sc >> (8 * g)) & 0xFFu,
-                                     acc[t][b]);
-        }
-      }
-      // the K-step's products are issued before its slot is reloaded, so that the slot's old
-      // and new values never overlap and keep one register set across the loop's back edge
-      // (where the compiler would otherwise copy the rings, waiting for every load in flight)
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) asm volatile("" : "+v"(acc[t][b]) :: "memory");
-#pragma unroll
-      for (int t = 0; t < NT; ++t) w[sl][t].template load<true>(trow[t], min(q + P, ks - 1), lane);
-      asm volatile("" ::: "memory");
-      st.commit((sl + 1) % P, lds + ((q + 1) & 1) * RB * PR, slds + ((q + 1) & 1) * RB);
-      __syncthreads();
-    }
-  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -410,6 +242,12 @@ __device__ __forceinline__ void copy_to_lds(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
 }
 
+// The LDS read that follows product i of a stage's 32 (-1: none): reads 0-11 after every
+// second product of the first 24, reads 12-15 after products 24-27, none after the last 4.
+__host__ __device__ constexpr int gemm_read_after(int i) {
+  return i < 24 ? ((i & 1) ? i >> 1 : -1) : (i < 28 ? i - 12 : -1);
+}
+
 template <bool IN>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_pf_gemm(PfGemmArgs a) {
   // the ring of stage buffers (16 row tiles, then 16 weight tiles, 1 KiB each): 160 KiB
@@ -463,14 +301,35 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_pf_gemm(PfGemmArgs a) {
       for (int b = 0; b < 4; ++b) bw[h][b] = L[w_word + 2 * b * 64 + 32 * h];
     }
   };
-  auto mma_slice = [&](const uint4 (&af)[2][4], const uint4 (&bw)[2][4], int h) {
+  // The 32 products of a stage held in (af, bw), with the 16 reads of the next stage's
+  // operands (from L into naf, nbw) spread among them (read_after: the read, if any, that
+  // follows product i), in the order the next stage's products take them (per slice: row
+  // piece 0, the four weight pieces, row pieces 1-3).  Issued in bursts, the reads of four
+  // wavefronts that leave a barrier together queue at the LDS for hundreds of cycles, and
+  // each matrix core stands idle until its wavefront has issued all 16; spread out, the LDS
+  // serves them while the products run.  The last products follow the last read, so that
+  // the wait for all reads that the compiler puts at the loop's head finds them done.
+  auto mma_read = [&](const uint4 (&af)[2][4], const uint4 (&bw)[2][4], const uint4* L,
+                      uint4 (&naf)[2][4], uint4 (&nbw)[2][4]) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int i = 0; i < 32; ++i) {
+      const int h = i >> 4, mb = (i >> 2) & 3, nb = i & 3;
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[h][mb]),
+                                                           __builtin_bit_cast(bf16x8_t, bw[h][nb]),
+                                                           acc[mb][nb], 0, 0, 0);
+      const int r = gemm_read_after(i);
+      if (r >= 0) {
+        const int rh = r >> 3, j = r & 7;
+        if (j == 0) naf[rh][0] = L[a_word + 32 * rh];
+        else if (j <= 4) nbw[rh][j - 1] = L[w_word + 2 * (j - 1) * 64 + 32 * rh];
+        else naf[rh][j - 4] = L[a_word + 2 * (j - 4) * 64 + 32 * rh];
+      }
+    }
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[h][mb]),
-                                                             __builtin_bit_cast(bf16x8_t, bw[h][nb]),
-                                                             acc[mb][nb], 0, 0, 0);
+    for (int i = 0; i < 32; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // a product
+      if (gemm_read_after(i) >= 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // an LDS read
+    }
   };
   // Stage k lives in buffer k % 5.  Its copies are issued three stages ahead, its operands
   // read into registers one stage ahead (while stage k - 1 is multiplied), so the matrix
@@ -496,25 +355,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_pf_gemm(PfGemmArgs a) {
   asm volatile("s_waitcnt vmcnt(24)" ::: "memory");   // stage 0 has landed
   __syncthreads();
   read_stage(buf(0), o0a, o0b);
-  // Within an iteration: the first slice's 16 products, the next stage's 16 reads, the
-  // second slice's 16 products, pinned in that order (the wait counter for LDS holds 15
-  // operations, so each read that a product or the barrier waits for is 16 products old).
   for (int k = 0; k < nk; k += 2) {
     wait_stage();
     dma_clamped(buf(k + 4), k + 4);
-    mma_slice(o0a, o0b, 0);
     __builtin_amdgcn_sched_barrier(0);
-    read_stage(buf(k + 1), o1a, o1b);
-    __builtin_amdgcn_sched_barrier(0);
-    mma_slice(o0a, o0b, 1);
+    mma_read(o0a, o0b, buf(k + 1), o1a, o1b);
     __builtin_amdgcn_sched_barrier(0);
     wait_stage();
     dma_clamped(buf(k + 5), k + 5);
-    mma_slice(o1a, o1b, 0);
     __builtin_amdgcn_sched_barrier(0);
-    read_stage(buf(k + 2), o0a, o0b);
-    __builtin_amdgcn_sched_barrier(0);
-    mma_slice(o1a, o1b, 1);
+    mma_read(o1a, o1b, buf(k + 2), o0a, o0b);
     __builtin_amdgcn_sched_barrier(0);
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the repeated reads
@@ -639,16 +489,25 @@ __global__ __launch_bounds__(kBlock) void k_pf_quant(const float* __restrict__ x
 
 // ------------------------------------------------------------------------------------
 // Routed experts, MX activations (AF 1: MXFP8, AF 2: MXFP4) x MXFP4 weights.  Work item
-// (tile-row group, unit); a unit is a run of at most 16 kPfExpNB dispatch positions of one
-// expert.  Gate/up: input rows x^c_q of the positions' tokens; each wavefront's 4 tile rows
-// (8 gate + 8 up rows each) give one MX block of 32 columns of h = SiTU(gate, up), converted
-// to the same MX format in the epilogue.  Down: input rows h_q of the positions, output E
-// fp32.
+// (tile-row group, unit); a unit is a run of at most kPfUnitPositions dispatch positions
+// of one expert (an expert's positions split into near-equal runs).  Gate/up: input rows
+// x^c_q of the positions' tokens; each wavefront's 4 tile rows (8 gate + 8 up rows each)
+// give one MX block of 32 columns of h = SiTU(gate, up), converted to the same MX format in
+// the epilogue.  Down: input rows h_q of the positions, output E fp32.
+//
+// One workgroup per compute unit: 4 wavefronts, each multiplying the unit's 16 NB rows
+// (NB <= 10) with its own 4 tile rows (64 weight rows), so that a tile row's weights are
+// read once per unit, and an expert's once per step when it has at most 160 positions.
+// Both operands of a K-step (the unit's activation rows with their scale words, the
+// workgroup's 16 weight tile rows with theirs) are copied global -> LDS directly, into two
+// rings of K-step stages; every wavefront issues the same number of copies per stage, so
+// one counted wait and one barrier per K-step order both rings.  The activation rows are
+// gathered: each lane of a copy names its own row.
 // ------------------------------------------------------------------------------------
 struct PfExpArgs {
   const uint8_t* experts;
   size_t expert_bytes, region_off;
-  int ks, n_tr, n_grp;
+  int ks, n_tr, n_grp, chunk;
   const int32_t* units;
   const int32_t* ctrl;
   int max_units, nu, E, k;
@@ -666,19 +525,222 @@ struct PfExpArgs {
   int n_out;
 };
 
-template <bool GU, int NB, int AF>
-__device__ __forceinline__ void pf_exp_unit(const PfExpArgs& a, const PfRows& rows, uint4* sm,
-                                            uint32_t* ssm, const uint8_t* const (&trow)[kPfNT],
-                                            const int (&tr)[kPfNT], int wblk, int p0, int n) {
+constexpr int kPxNT = 4;                       // weight tile rows per wavefront
+constexpr int kPxWaves = kBlock / kWave;       // 4
+constexpr int kPxTR = kPxWaves * kPxNT;        // weight tile rows per workgroup
+constexpr int kPxMaxNB = kPfUnitPositions / 16;
+static_assert(16 * kPxMaxNB == kPfUnitPositions && kPfUnitPositions <= kBlock,
+              "a unit fills at most kPxMaxNB blocks; one thread per row sets the row table");
+constexpr int kPxRingBytes = 159744;           // 156 KiB of LDS for the rings
+// Ring depths (weight stages of 17 KiB; as many activation stages as fit, at most 6):
+// 3 / 5, 4 / 4 and 5 / 3 for 160-row tiles measured within 2% of one another.
+constexpr int kPxWDepth = 4;
+constexpr int kPxMaxADepth = 6;
+
+// One direct global -> LDS copy of 4 bytes per lane (lane l's word lands at lds + 4 l).
+__device__ __forceinline__ void copy4_to_lds(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory");
+}
+// s_waitcnt immediate that waits for vector memory operations alone (at most n in flight)
+__host__ __device__ constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// Two rings of K-step stages.  Activation stage: codes (row-major, piece j of row r at
+// 16-byte word PR r + (j ^ swz(r)); padded to whole copies of every wavefront), then the
+// scale words (256 rows: one copy of 64 per wavefront).  Row-major, a copy of 64 lanes takes
+// 8 (AF 1) or 16 (AF 2) whole rows, 8 or 16 cache lines; the swizzle makes the 16 rows of an
+// MFMA operand's piece land in 16 different bank groups.  Weight stage: codes (tile row t at
+// words 64 t .. +64, in the order of the packed weights), then the scale words (tile row t,
+// row c at word 16 t + c).  The weights come from HBM once per unit and their ring runs
+// DW - 1 K-steps ahead, the activation rows (read by all of the unit's tile-row groups)
+// DA - 1 K-steps ahead.
+template <int AF, int NB>
+struct PxLayout {
+  static constexpr int RB = 16 * NB;
+  static constexpr int PR = AF == 2 ? 4 : 8;                    // 16-byte pieces per K-step row
+  __device__ static int swz(int r) { return AF == 2 ? (r >> 2) & 3 : (r >> 1) & 7; }
+  __device__ static int word(int r, int j) { return PR * r + (j ^ swz(r)); }
+  static constexpr int A_WORDS = RB * PR;
+  static constexpr int A_COPIES = (A_WORDS + 4 * kWave - 1) / (4 * kWave);   // per wavefront
+  static constexpr int AS_OFF = A_COPIES * 4 * kWave * 16;
+  static constexpr int A_BYTES = AS_OFF + 4 * kWave * 4;
+  static constexpr int WS_OFF = kPxTR * 1024;
+  static constexpr int W_BYTES = WS_OFF + kPxTR * 64;
+  static constexpr int DW = kPxWDepth;
+  static constexpr int A_RING = DW * W_BYTES;                    // the activation ring's offset
+  static constexpr int DA_FIT = (kPxRingBytes - A_RING) / A_BYTES;
+  static constexpr int DA = DA_FIT < kPxMaxADepth ? DA_FIT : kPxMaxADepth;
+  static constexpr int AC = A_COPIES + 1, WC = kPxNT + 1;        // copies per wavefront and stage
+  // Copies in flight after the later of K-step k's two stages: turn j issues weight stage
+  // j + DW - 1, then activation stage j + DA - 1, so with DA <= DW activation stage k comes
+  // last (turn k - DA + 1, DA - 2 turns after it), else weight stage k (turn k - DW + 1,
+  // its activation stage and DW - 2 turns after it).
+  static constexpr int WAIT = DA <= DW ? (DA - 2) * (AC + WC) : AC + (DW - 2) * (AC + WC);
+  static_assert(DA >= 3 && DW >= 3, "two K-steps in flight in each ring");
+  static_assert(WAIT <= 63, "the wait counter holds the copies in flight");
+  static_assert(kPxWaves * kWave >= RB, "the scale copies cover the rows");
+  static_assert(NB % 2 == 0, "block 0 of a K-step takes register set 0");
+};
+
+template <bool GU, int AF, int NB>
+__device__ __forceinline__ void px_unit(const PfExpArgs& a, uint8_t* ring, const int32_t* srcrow,
+                                        const uint8_t* const (&trow)[kPxNT], const int (&tr)[kPxNT],
+                                        int wblk, int p0, int n) {
+  using Lay = PxLayout<AF, NB>;
+  constexpr int PR = Lay::PR, DA = Lay::DA, DW = Lay::DW;
   const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
-  f32x4_t acc[kPfNT][NB];
-  pf_run<AF, NB, kPfNT, kPfExpDepth>(rows, PfSrc{reinterpret_cast<const uint4*>(a.xq),
-                                                  reinterpret_cast<const uint32_t*>(a.xs), n},
-                                     trow, a.ks, sm, ssm, acc);
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;   // (low 32 bits: the LDS address)
+  // This lane's sources at K-step 0.  Activation copy i of the wavefront fills words
+  // (4 i + wv) 64 .. +64 of the stage: word wd holds row wd / PR, piece (wd % PR) ^ swz
+  // (rows past the unit, and the padding, read the unit's first row: in bounds, never used).
+  const size_t row_bytes = (size_t)16 * PR * a.ks;
+  const uint8_t* asrc[Lay::A_COPIES];
+#pragma unroll
+  for (int i = 0; i < Lay::A_COPIES; ++i) {
+    const int wd = (4 * i + wv) * kWave + lane;
+    const int r = wd < Lay::A_WORDS ? wd / PR : 0;
+    const int j = wd < Lay::A_WORDS ? (wd % PR) ^ Lay::swz(r) : 0;
+    asrc[i] = a.xq + (size_t)srcrow[r < n ? r : 0] * row_bytes + 16 * j;
+  }
+  const int sr = kWave * wv + lane;
+  const uint8_t* ssrc = a.xs + (size_t)srcrow[sr < n ? sr : 0] * 4 * a.ks;
+  const int tl = lane >> 4;
+  const uint8_t* wsrc_s = (tl == 0 ? trow[0] : tl == 1 ? trow[1] : tl == 2 ? trow[2] : trow[3]) + 1024 + 4 * c;
+  // activation stage j (K-step min(j, ks - 1)) into its ring slot j % DA; weight stage j likewise
+  auto issue_a = [&](int j) {
+    const int q = j < a.ks ? j : a.ks - 1;
+    const uint32_t base = ring_lds + (uint32_t)(Lay::A_RING + (j % DA) * Lay::A_BYTES);
+#pragma unroll
+    for (int i = 0; i < Lay::A_COPIES; ++i)
+      copy_to_lds(asrc[i] + (size_t)q * 16 * PR, __builtin_amdgcn_readfirstlane(base + (4 * i + wv) * 1024));
+    copy4_to_lds(ssrc + 4 * q, __builtin_amdgcn_readfirstlane(base + Lay::AS_OFF + 256 * wv));
+  };
+  auto issue_w = [&](int j) {
+    const int q = j < a.ks ? j : a.ks - 1;
+    const uint32_t base = ring_lds + (uint32_t)((j % DW) * Lay::W_BYTES);
+#pragma unroll
+    for (int t = 0; t < kPxNT; ++t)
+      copy_to_lds(trow[t] + (size_t)q * kFp4StepBytes + 16 * lane,
+                  __builtin_amdgcn_readfirstlane(base + (kPxNT * wv + t) * 1024));
+    copy4_to_lds(wsrc_s + (size_t)q * kFp4StepBytes, __builtin_amdgcn_readfirstlane(base + Lay::WS_OFF + 256 * wv));
+  };
+  auto a_stage = [&](int q) { return ring + Lay::A_RING + (q % DA) * Lay::A_BYTES; };
+  auto w_stage = [&](int q) { return ring + (q % DW) * Lay::W_BYTES; };
+  f32x4_t acc[kPxNT][NB];
+#pragma unroll
+  for (int t = 0; t < kPxNT; ++t)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[t][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int ks = a.ks;
+  // Operands in registers: the weight fragments of a K-step (two sets: this K-step's and the
+  // next one's) and the activation fragments of a 16-row block (two sets: block b in set
+  // b % 2; NB is even, so block 0 of the next K-step takes set 0).
+  uint4 bw0[kPxNT], bw1[kPxNT], al[2], ah[2];
+  uint32_t bs0[kPxNT], bs1[kPxNT], sa[2];
+  auto read_w = [&](const uint8_t* st, uint4 (&bw)[kPxNT], uint32_t (&bs)[kPxNT]) {
+    const uint4* W = reinterpret_cast<const uint4*>(st);
+    const uint8_t* WS = st + Lay::WS_OFF;
+#pragma unroll
+    for (int t = 0; t < kPxNT; ++t) {
+      bw[t] = W[(kPxNT * wv + t) * kWave + lane];
+      bs[t] = WS[((kPxNT * wv + t) * 16 + c) * 4 + g];   // byte g of row c's scale word
+    }
+  };
+  auto read_a = [&](const uint8_t* st, int b, int set) {
+    const uint4* A = reinterpret_cast<const uint4*>(st);
+    const int r = 16 * b + c;
+    al[set] = A[Lay::word(r, g)];
+    if (AF != 2) ah[set] = A[Lay::word(r, 4 + g)];
+    sa[set] = st[Lay::AS_OFF + 4 * r + g];   // byte g of row r's scale word (no shift after the read)
+  };
+  auto mma_block = [&](int b, int set, const uint4 (&bw)[kPxNT], const uint32_t (&bs)[kPxNT]) {
+#pragma unroll
+    for (int t = 0; t < kPxNT; ++t)
+      acc[t][b] = AF == 2 ? mfma_fp4_fp4(al[set], bw[t], sa[set], bs[t], acc[t][b])
+                          : mfma_fp8_fp4(al[set], ah[set], bw[t], sa[set], bs[t], acc[t][b]);
+  };
+  // Turn k (before K-step k's products): this wavefront's copies of both stages of K-step k
+  // have landed (the copies complete in order: WAIT counts those issued after the later
+  // one) and its LDS reads are done; after the barrier everyone's have, and the slots just
+  // read take weight stage k + DW - 1 and activation stage k + DA - 1.  (Past the last
+  // K-step the copies repeat it, unused.)
+  auto turn = [&](int k) {
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(Lay::WAIT) & ~(15 << 8));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w(k + DW - 1);
+    issue_a(k + DA - 1);
+  };
+  // K-step q with weight fragments (bw, bs); the next K-step's go to (nbw, nbs).  Each block's
+  // 4 products run while the next block's fragments are read (two products, a read, ...);
+  // the barrier comes before the last block, whose products cover the reads of the next
+  // K-step's weight fragments and first block.
+  // (keep: all ones, or zero for a K-step past the last, whose products then add exact
+  // zeros; a mask at the first use, not a branch around the loads)
+  auto kstep = [&](int q, const uint4 (&bwr)[kPxNT], const uint32_t (&bs)[kPxNT], uint4 (&nbw)[kPxNT],
+                   uint32_t (&nbs)[kPxNT], uint32_t keep) {
+    const uint8_t* st = a_stage(q);
+    uint4 bw[kPxNT];
+#pragma unroll
+    for (int t = 0; t < kPxNT; ++t)
+      bw[t] = make_uint4(bwr[t].x & keep, bwr[t].y & keep, bwr[t].z & keep, bwr[t].w & keep);
+#pragma unroll
+    for (int b = 0; b + 1 < NB; ++b) {
+      __builtin_amdgcn_sched_barrier(0);
+      read_a(st, b + 1, (b + 1) & 1);
+      mma_block(b, b & 1, bw, bs);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, AF == 2 ? 0 : 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    turn(q + 1);
+    read_w(w_stage(q + 1), nbw, nbs);
+    read_a(a_stage(q + 1), 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_block(NB - 1, 1, bw, bs);
+    // each accumulator keeps one register set across the K-steps (the allocator otherwise
+    // moves them between sets every iteration)
+#pragma unroll
+    for (int t = 0; t < kPxNT; ++t)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) asm volatile("" : "+a"(acc[t][b]));
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The prologue issues what turns -1, -2, ... would have (in the same order), so that the
+  // same count of copies follows every stage.
+  constexpr int D = DA > DW ? DA : DW;
+#pragma unroll
+  for (int j = 1 - D; j < 0; ++j) {
+    if (j + DW - 1 >= 0) issue_w(j + DW - 1);
+    if (j + DA - 1 >= 0) issue_a(j + DA - 1);
+  }
+  turn(0);
+  read_w(w_stage(0), bw0, bs0);
+  read_a(a_stage(0), 0, 0);
+  // two K-steps per iteration; with an odd count the last iteration's second K-step has
+  // zero weights (a branch or a K-step outside the loop makes the register allocator move
+  // the accumulators between register sets every iteration)
+  for (int q = 0; q < ks; q += 2) {
+    kstep(q, bw0, bs0, bw1, bs1, ~0u);
+    kstep(q + 1, bw1, bs1, bw0, bs0, q + 1 < ks ? ~0u : 0u);
+  }
+  // (the accumulators leave the loop in their registers: the epilogue reads them from there)
+#pragma unroll
+  for (int t = 0; t < kPxNT; ++t)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) asm volatile("" : "+a"(acc[t][b]));
+  // the repeated copies land before the ring is reused
+  __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+  __syncthreads();
   if (!GU) {
 #pragma unroll
-    for (int t = 0; t < kPfNT; ++t) {
+    for (int t = 0; t < kPxNT; ++t) {
       const int r = 16 * tr[t] + c;
       if (tr[t] >= a.n_tr || r >= a.n_out) continue;
 #pragma unroll
@@ -701,7 +763,7 @@ __device__ __forceinline__ void pf_exp_unit(const PfExpArgs& a, const PfRows& ro
   const int nbk = 4 * a.ks_out;
   if (32 * wblk >= 128 * a.ks_out) return;
   const bool lo = c < 8;
-  float* tile = reinterpret_cast<float*>(sm) + (threadIdx.x >> 6) * 16 * 36;
+  float* tile = reinterpret_cast<float*>(ring) + wv * 16 * 36;
   const int rr = lane >> 2, qq = lane & 3;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -744,50 +806,45 @@ __device__ __forceinline__ void pf_exp_unit(const PfExpArgs& a, const PfRows& ro
   }
 }
 
-// Work order of the expert launches: chunks of 8 units through every tile-row group
-// (chunk_item; measured against 2, 4, 16 and 32: the units of one expert share its weight
-// slices in L2 best at 8 when an expert has many units).
-constexpr int kPfChunk = 8;
-
-// Two workgroups per compute unit (a register budget of 256 per lane): while one waits at
-// its barrier or for its loads the other issues MFMAs.
 template <bool GU, int AF>
-__global__ __launch_bounds__(kBlock, 2) void k_pf_exp(PfExpArgs a) {
-  extern __shared__ uint4 sm[];
-  __shared__ PfRows rows;
-  __shared__ uint32_t ssm[2 * kPfRows];
+__global__ __launch_bounds__(kBlock, 1) void k_pf_exp(PfExpArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kPxRingBytes];
+  __shared__ int32_t srcrow[kPfUnitPositions];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_units = min(a.ctrl[0], a.max_units);
   int grp, u;
-  if (!chunk_item(blockIdx.x, n_units, a.n_grp, kPfChunk, grp, u)) return;
+  if (!chunk_item(blockIdx.x, n_units, a.n_grp, a.chunk, grp, u)) return;
   const int4 un = *reinterpret_cast<const int4*>(a.units + 4 * u);
   const int e = un.x, p0 = un.y, n = un.z;
-  if (e < 0 || e >= a.E || n < 1 || n > a.nu || n > kPfRows || p0 < 0 || p0 + n > a.n_assign) return;
+  if (e < 0 || e >= a.E || n < 1 || n > a.nu || n > kPfUnitPositions || p0 < 0 || p0 + n > a.n_assign)
+    return;
+  // the input row of each position: the token's x^c_q row (gate/up) or the position's h_q row
   if ((int)threadIdx.x < n) {
     const int p = p0 + threadIdx.x;
-    int64_t src = p;
+    int src = p;
     if (GU) {
       const int asg = a.perm[p];
       src = (asg >= 0 && asg < a.n_assign) ? asg / a.k : 0;
     }
-    rows.o0[threadIdx.x] = (uint32_t)(src * (AF == 2 ? 4 : 8) * a.ks);   // 16-byte words of the row
-    rows.s0[threadIdx.x] = (uint32_t)(src * a.ks);         // scale words (4 ks bytes per row)
+    srcrow[threadIdx.x] = src;
   }
   __syncthreads();
-  const int wblk = grp * kPfWaves + wv;    // this wavefront's tile rows 4 wblk .. 4 wblk + 3
+  const int wblk = grp * kPxWaves + wv;    // this wavefront's tile rows 4 wblk .. 4 wblk + 3
   const uint8_t* base = a.experts + (size_t)e * a.expert_bytes + a.region_off;
-  const uint8_t* trow[kPfNT];
-  int tr[kPfNT];
+  const uint8_t* trow[kPxNT];
+  int tr[kPxNT];
 #pragma unroll
-  for (int t = 0; t < kPfNT; ++t) {
-    tr[t] = wblk * kPfNT + t;
+  for (int t = 0; t < kPxNT; ++t) {
+    tr[t] = wblk * kPxNT + t;
     trow[t] = base + (size_t)(tr[t] < a.n_tr ? tr[t] : 0) * a.ks * kFp4StepBytes;
   }
   // blocks of 16 positions: the unit's count rounded up to one of the built tile heights
   const int nb = (n + 15) / 16;
-  if (nb <= 1) pf_exp_unit<GU, 1, AF>(a, rows, sm, ssm, trow, tr, wblk, p0, n);
-  else if (nb <= 2) pf_exp_unit<GU, 2, AF>(a, rows, sm, ssm, trow, tr, wblk, p0, n);
-  else pf_exp_unit<GU, kPfExpNB, AF>(a, rows, sm, ssm, trow, tr, wblk, p0, n);
+  if (nb <= 2) px_unit<GU, AF, 2>(a, ring, srcrow, trow, tr, wblk, p0, n);
+  else if (nb <= 4) px_unit<GU, AF, 4>(a, ring, srcrow, trow, tr, wblk, p0, n);
+  else if (nb <= 6) px_unit<GU, AF, 6>(a, ring, srcrow, trow, tr, wblk, p0, n);
+  else if (nb <= 8) px_unit<GU, AF, 8>(a, ring, srcrow, trow, tr, wblk, p0, n);
+  else px_unit<GU, AF, kPxMaxNB>(a, ring, srcrow, trow, tr, wblk, p0, n);
 }
 
 // Zero the padding columns of a token's packed OUT row: u_hat columns l .. 128 ks_l and
@@ -916,11 +973,6 @@ __global__ __launch_bounds__(kBlock) void k_pf_combine_norm(
   zero_out_pads(ao, t, l, ks_l, ms, ks_ms, ks_out);
 }
 
-// two K-steps of the FP8 rows, and room for the gate/up epilogue's wavefront-private tiles
-constexpr size_t kPfExpEpiLds = (size_t)kPfWaves * 16 * 36 * 4;
-constexpr size_t kPfExpLds = (size_t)2 * 16 * kPfExpNB * 8 * 16 > kPfExpEpiLds
-                                 ? (size_t)2 * 16 * kPfExpNB * 8 * 16 : kPfExpEpiLds;
-
 }  // namespace
 
 hipError_t launch_pf_in(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t T,
@@ -966,7 +1018,7 @@ hipError_t launch_pf_expert(const Shape& s, const uint8_t* experts, bool gu, int
   a.region_off = gu ? 0 : s.gu_bytes;
   a.ks = gu ? s.ks_gu : s.ks_edn;
   a.n_tr = gu ? s.tr_gu : s.tr_edn;
-  a.n_grp = cdiv(a.n_tr, kPfWaves * kPfNT);
+  a.n_grp = cdiv(a.n_tr, kPxTR);
   a.units = ws.units;
   a.ctrl = ws.ctrl;
   a.nu = unit_positions(s, T);
@@ -982,13 +1034,19 @@ hipError_t launch_pf_expert(const Shape& s, const uint8_t* experts, bool gu, int
   a.rbg = 1.f / s.beta_gate; a.rbl = 1.f / s.beta_lin;
   a.out = ws.eo;
   a.n_out = s.l;
-  const unsigned grid = (unsigned)chunk_grid(a.max_units, a.n_grp, kPfChunk);
+  // Work order: XCD x walks its share of the unit table in chunks of `chunk` units, each
+  // chunk through every tile-row group (chunk_item).  With about one unit per expert (chunk
+  // 1) a unit's groups run back to back and its activation rows stay in the XCD's L2; with
+  // many units per expert the chunk spans them, so that the units of one expert read each
+  // weight slice at about the same time.
+  a.chunk = clampi((int)cdiv(a.n_assign, (int64_t)s.E * a.nu), 1, 8);
+  const unsigned grid = (unsigned)chunk_grid(a.max_units, a.n_grp, a.chunk);
   if (s.prec == 2) {
-    if (gu) hipLaunchKernelGGL((k_pf_exp<true, 2>), dim3(grid), dim3(kBlock), kPfExpLds, st, a);
-    else hipLaunchKernelGGL((k_pf_exp<false, 2>), dim3(grid), dim3(kBlock), kPfExpLds, st, a);
+    if (gu) hipLaunchKernelGGL((k_pf_exp<true, 2>), dim3(grid), dim3(kBlock), 0, st, a);
+    else hipLaunchKernelGGL((k_pf_exp<false, 2>), dim3(grid), dim3(kBlock), 0, st, a);
   } else {
-    if (gu) hipLaunchKernelGGL((k_pf_exp<true, 1>), dim3(grid), dim3(kBlock), kPfExpLds, st, a);
-    else hipLaunchKernelGGL((k_pf_exp<false, 1>), dim3(grid), dim3(kBlock), kPfExpLds, st, a);
+    if (gu) hipLaunchKernelGGL((k_pf_exp<true, 1>), dim3(grid), dim3(kBlock), 0, st, a);
+    else hipLaunchKernelGGL((k_pf_exp<false, 1>), dim3(grid), dim3(kBlock), 0, st, a);
   }
   return hipGetLastError();
 }
