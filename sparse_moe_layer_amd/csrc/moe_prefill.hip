@@ -495,9 +495,11 @@ __global__ __launch_bounds__(kBlock) void k_pf_quant(const float* __restrict__ x
 // give one MX block of 32 columns of h = SiTU(gate, up), converted to the same MX format in
 // the epilogue.  Down: input rows h_q of the positions, output E fp32.
 //
-// One workgroup per compute unit: 4 wavefronts, each multiplying the unit's 16 NB rows
-// (NB <= 10) with its own 4 tile rows (64 weight rows), so that a tile row's weights are
-// read once per unit, and an expert's once per step when it has at most 160 positions.
+// Two workgroups per compute unit (78 KiB of LDS and 256 registers each, so that one's
+// epilogue and prologue run beside the other's products), of 4 wavefronts, each
+// multiplying the unit's 16 NB rows (NB <= 10) with its own 4 tile rows (64 weight rows):
+// a tile row's weights are read once per unit, and an expert's once per step when it has
+// at most 160 positions.
 // Both operands of a K-step (the unit's activation rows with their scale words, the
 // workgroup's 16 weight tile rows with theirs) are copied global -> LDS directly, into two
 // rings of K-step stages; every wavefront issues the same number of copies per stage, so
@@ -531,15 +533,19 @@ constexpr int kPxTR = kPxWaves * kPxNT;        // weight tile rows per workgroup
 constexpr int kPxMaxNB = kPfUnitPositions / 16;
 static_assert(16 * kPxMaxNB == kPfUnitPositions && kPfUnitPositions <= kBlock,
               "a unit fills at most kPxMaxNB blocks; one thread per row sets the row table");
-constexpr int kPxRingBytes = 159744;           // 156 KiB of LDS for the rings
-// Ring depths (weight stages of 17 KiB; as many activation stages as fit, at most 6):
-// 3 / 5, 4 / 4 and 5 / 3 for 160-row tiles measured within 2% of one another.
-constexpr int kPxWDepth = 4;
+constexpr int kPxRingBytes = 79872;            // 78 KiB of LDS for the rings (two workgroups per CU)
+// Ring depths: 2 weight stages of 17 KiB, as many activation stages as fit (2 for 160-row
+// tiles), at most 6.
+constexpr int kPxWDepth = 2;
 constexpr int kPxMaxADepth = 6;
 
-// One direct global -> LDS copy of 4 bytes per lane (lane l's word lands at lds + 4 l).
-__device__ __forceinline__ void copy4_to_lds(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory");
+// Direct global -> LDS copies from a wavefront-uniform base and a 32-bit lane offset: 16
+// bytes (lane l's at lds + 16 l) or 4 bytes (at lds + 4 l) per lane.
+__device__ __forceinline__ void copy_to_lds_at(uint32_t off, const void* base, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void copy4_to_lds_at(uint32_t off, const void* base, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory");
 }
 // s_waitcnt immediate that waits for vector memory operations alone (at most n in flight)
 __host__ __device__ constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
@@ -575,7 +581,7 @@ struct PxLayout {
   // last (turn k - DA + 1, DA - 2 turns after it), else weight stage k (turn k - DW + 1,
   // its activation stage and DW - 2 turns after it).
   static constexpr int WAIT = DA <= DW ? (DA - 2) * (AC + WC) : AC + (DW - 2) * (AC + WC);
-  static_assert(DA >= 3 && DW >= 3, "two K-steps in flight in each ring");
+  static_assert(DA >= 2 && DW >= 2, "a K-step in flight in each ring");
   static_assert(WAIT <= 63, "the wait counter holds the copies in flight");
   static_assert(kPxWaves * kWave >= RB, "the scale copies cover the rows");
   static_assert(NB % 2 == 0, "block 0 of a K-step takes register set 0");
@@ -583,47 +589,55 @@ struct PxLayout {
 
 template <bool GU, int AF, int NB>
 __device__ __forceinline__ void px_unit(const PfExpArgs& a, uint8_t* ring, const int32_t* srcrow,
-                                        const uint8_t* const (&trow)[kPxNT], const int (&tr)[kPxNT],
-                                        int wblk, int p0, int n) {
+                                        const uint8_t* ebase, const uint8_t* const (&trow)[kPxNT],
+                                        const int (&tr)[kPxNT], int wblk, int p0, int n) {
   using Lay = PxLayout<AF, NB>;
   constexpr int PR = Lay::PR, DA = Lay::DA, DW = Lay::DW;
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;   // (low 32 bits: the LDS address)
-  // This lane's sources at K-step 0.  Activation copy i of the wavefront fills words
-  // (4 i + wv) 64 .. +64 of the stage: word wd holds row wd / PR, piece (wd % PR) ^ swz
-  // (rows past the unit, and the padding, read the unit's first row: in bounds, never used).
-  const size_t row_bytes = (size_t)16 * PR * a.ks;
-  const uint8_t* asrc[Lay::A_COPIES];
+  // This lane's sources: a wavefront-uniform base (per K-step) and a 32-bit lane offset.
+  // The input rows are the unit's own (down: rows p0 .. of h; srcrow relative to p0) or
+  // gathered tokens (gate/up: the launch checks that the T rows span less than 4 GiB).
+  // Activation copy i of the wavefront fills words (4 i + wv) 64 .. +64 of the stage: word
+  // wd holds row wd / PR, piece (wd % PR) ^ swz (rows past the unit, and the padding, read
+  // the unit's first row: in bounds, never used).
+  const uint32_t row_bytes = 16u * PR * (uint32_t)a.ks;
+  const uint8_t* xq = a.xq + (GU ? 0 : (size_t)p0 * row_bytes);
+  const uint8_t* xs = a.xs + (GU ? 0 : (size_t)p0 * 4 * a.ks);
+  uint32_t aoff[Lay::A_COPIES];
 #pragma unroll
   for (int i = 0; i < Lay::A_COPIES; ++i) {
     const int wd = (4 * i + wv) * kWave + lane;
     const int r = wd < Lay::A_WORDS ? wd / PR : 0;
     const int j = wd < Lay::A_WORDS ? (wd % PR) ^ Lay::swz(r) : 0;
-    asrc[i] = a.xq + (size_t)srcrow[r < n ? r : 0] * row_bytes + 16 * j;
+    aoff[i] = (uint32_t)srcrow[r < n ? r : 0] * row_bytes + 16u * j;
   }
   const int sr = kWave * wv + lane;
-  const uint8_t* ssrc = a.xs + (size_t)srcrow[sr < n ? sr : 0] * 4 * a.ks;
+  const uint32_t soff = (uint32_t)srcrow[sr < n ? sr : 0] * 4u * (uint32_t)a.ks;
   const int tl = lane >> 4;
-  const uint8_t* wsrc_s = (tl == 0 ? trow[0] : tl == 1 ? trow[1] : tl == 2 ? trow[2] : trow[3]) + 1024 + 4 * c;
+  const uint32_t wsoff =
+      (uint32_t)((tl == 0 ? trow[0] : tl == 1 ? trow[1] : tl == 2 ? trow[2] : trow[3]) - ebase) + 1024u + 4u * c;
   // activation stage j (K-step min(j, ks - 1)) into its ring slot j % DA; weight stage j likewise
   auto issue_a = [&](int j) {
     const int q = j < a.ks ? j : a.ks - 1;
     const uint32_t base = ring_lds + (uint32_t)(Lay::A_RING + (j % DA) * Lay::A_BYTES);
+    const uint8_t* src = xq + (size_t)q * 16 * PR;
 #pragma unroll
     for (int i = 0; i < Lay::A_COPIES; ++i)
-      copy_to_lds(asrc[i] + (size_t)q * 16 * PR, __builtin_amdgcn_readfirstlane(base + (4 * i + wv) * 1024));
-    copy4_to_lds(ssrc + 4 * q, __builtin_amdgcn_readfirstlane(base + Lay::AS_OFF + 256 * wv));
+      copy_to_lds_at(aoff[i], src, __builtin_amdgcn_readfirstlane(base + (4 * i + wv) * 1024));
+    copy4_to_lds_at(soff, xs + 4 * q, __builtin_amdgcn_readfirstlane(base + Lay::AS_OFF + 256 * wv));
   };
   auto issue_w = [&](int j) {
     const int q = j < a.ks ? j : a.ks - 1;
     const uint32_t base = ring_lds + (uint32_t)((j % DW) * Lay::W_BYTES);
 #pragma unroll
     for (int t = 0; t < kPxNT; ++t)
-      copy_to_lds(trow[t] + (size_t)q * kFp4StepBytes + 16 * lane,
-                  __builtin_amdgcn_readfirstlane(base + (kPxNT * wv + t) * 1024));
-    copy4_to_lds(wsrc_s + (size_t)q * kFp4StepBytes, __builtin_amdgcn_readfirstlane(base + Lay::WS_OFF + 256 * wv));
+      copy_to_lds_at(16u * lane, trow[t] + (size_t)q * kFp4StepBytes,
+                     __builtin_amdgcn_readfirstlane(base + (kPxNT * wv + t) * 1024));
+    copy4_to_lds_at(wsoff, ebase + (size_t)q * kFp4StepBytes,
+                    __builtin_amdgcn_readfirstlane(base + Lay::WS_OFF + 256 * wv));
   };
   auto a_stage = [&](int q) { return ring + Lay::A_RING + (q % DA) * Lay::A_BYTES; };
   auto w_stage = [&](int q) { return ring + (q % DW) * Lay::W_BYTES; };
@@ -633,12 +647,12 @@ __device__ __forceinline__ void px_unit(const PfExpArgs& a, uint8_t* ring, const
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[t][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int ks = a.ks;
-  // Operands in registers: the weight fragments of a K-step (two sets: this K-step's and the
-  // next one's) and the activation fragments of a 16-row block (two sets: block b in set
-  // b % 2; NB is even, so block 0 of the next K-step takes set 0).
-  uint4 bw0[kPxNT], bw1[kPxNT], al[2], ah[2];
-  uint32_t bs0[kPxNT], bs1[kPxNT], sa[2];
-  auto read_w = [&](const uint8_t* st, uint4 (&bw)[kPxNT], uint32_t (&bs)[kPxNT]) {
+  // Operands in registers: the weight fragments of a K-step and the activation fragments of
+  // a 16-row block (two sets: block b in set b % 2; NB is even, so block 0 of the next K-step
+  // takes set 0).
+  uint4 bw[kPxNT], al[2], ah[2];
+  uint32_t bs[kPxNT], sa[2];
+  auto read_w = [&](const uint8_t* st) {
     const uint4* W = reinterpret_cast<const uint4*>(st);
     const uint8_t* WS = st + Lay::WS_OFF;
 #pragma unroll
@@ -654,7 +668,7 @@ __device__ __forceinline__ void px_unit(const PfExpArgs& a, uint8_t* ring, const
     if (AF != 2) ah[set] = A[Lay::word(r, 4 + g)];
     sa[set] = st[Lay::AS_OFF + 4 * r + g];   // byte g of row r's scale word (no shift after the read)
   };
-  auto mma_block = [&](int b, int set, const uint4 (&bw)[kPxNT], const uint32_t (&bs)[kPxNT]) {
+  auto mma_block = [&](int b, int set) {
 #pragma unroll
     for (int t = 0; t < kPxNT; ++t)
       acc[t][b] = AF == 2 ? mfma_fp4_fp4(al[set], bw[t], sa[set], bs[t], acc[t][b])
@@ -672,24 +686,17 @@ __device__ __forceinline__ void px_unit(const PfExpArgs& a, uint8_t* ring, const
     issue_w(k + DW - 1);
     issue_a(k + DA - 1);
   };
-  // K-step q with weight fragments (bw, bs); the next K-step's go to (nbw, nbs).  Each block's
-  // 4 products run while the next block's fragments are read (two products, a read, ...);
-  // the barrier comes before the last block, whose products cover the reads of the next
-  // K-step's weight fragments and first block.
-  // (keep: all ones, or zero for a K-step past the last, whose products then add exact
-  // zeros; a mask at the first use, not a branch around the loads)
-  auto kstep = [&](int q, const uint4 (&bwr)[kPxNT], const uint32_t (&bs)[kPxNT], uint4 (&nbw)[kPxNT],
-                   uint32_t (&nbs)[kPxNT], uint32_t keep) {
+  // K-step q.  Each block's 4 products run while the next block's fragments are read (a
+  // product, a read, ...); the barrier comes before the last block, whose products cover the
+  // read of the next K-step's first block; the next K-step's weight fragments are read once
+  // the last products are issued (the other workgroup on the compute unit fills the wait).
+  auto kstep = [&](int q) {
     const uint8_t* st = a_stage(q);
-    uint4 bw[kPxNT];
-#pragma unroll
-    for (int t = 0; t < kPxNT; ++t)
-      bw[t] = make_uint4(bwr[t].x & keep, bwr[t].y & keep, bwr[t].z & keep, bwr[t].w & keep);
 #pragma unroll
     for (int b = 0; b + 1 < NB; ++b) {
       __builtin_amdgcn_sched_barrier(0);
       read_a(st, b + 1, (b + 1) & 1);
-      mma_block(b, b & 1, bw, bs);
+      mma_block(b, b & 1);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -700,16 +707,11 @@ __device__ __forceinline__ void px_unit(const PfExpArgs& a, uint8_t* ring, const
     }
     __builtin_amdgcn_sched_barrier(0);
     turn(q + 1);
-    read_w(w_stage(q + 1), nbw, nbs);
     read_a(a_stage(q + 1), 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    mma_block(NB - 1, 1, bw, bs);
-    // each accumulator keeps one register set across the K-steps (the allocator otherwise
-    // moves them between sets every iteration)
-#pragma unroll
-    for (int t = 0; t < kPxNT; ++t)
-#pragma unroll
-      for (int b = 0; b < NB; ++b) asm volatile("" : "+a"(acc[t][b]));
+    mma_block(NB - 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_w(w_stage(q + 1));
     __builtin_amdgcn_sched_barrier(0);
   };
   // The prologue issues what turns -1, -2, ... would have (in the same order), so that the
@@ -721,20 +723,9 @@ __device__ __forceinline__ void px_unit(const PfExpArgs& a, uint8_t* ring, const
     if (j + DA - 1 >= 0) issue_a(j + DA - 1);
   }
   turn(0);
-  read_w(w_stage(0), bw0, bs0);
+  read_w(w_stage(0));
   read_a(a_stage(0), 0, 0);
-  // two K-steps per iteration; with an odd count the last iteration's second K-step has
-  // zero weights (a branch or a K-step outside the loop makes the register allocator move
-  // the accumulators between register sets every iteration)
-  for (int q = 0; q < ks; q += 2) {
-    kstep(q, bw0, bs0, bw1, bs1, ~0u);
-    kstep(q + 1, bw1, bs1, bw0, bs0, q + 1 < ks ? ~0u : 0u);
-  }
-  // (the accumulators leave the loop in their registers: the epilogue reads them from there)
-#pragma unroll
-  for (int t = 0; t < kPxNT; ++t)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) asm volatile("" : "+a"(acc[t][b]));
+  for (int q = 0; q < ks; ++q) kstep(q);
   // the repeated copies land before the ring is reused
   __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
   __syncthreads();
@@ -807,7 +798,7 @@ __device__ __forceinline__ void px_unit(const PfExpArgs& a, uint8_t* ring, const
 }
 
 template <bool GU, int AF>
-__global__ __launch_bounds__(kBlock, 1) void k_pf_exp(PfExpArgs a) {
+__global__ __launch_bounds__(kBlock, 2) void k_pf_exp(PfExpArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[kPxRingBytes];
   __shared__ int32_t srcrow[kPfUnitPositions];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -818,12 +809,12 @@ __global__ __launch_bounds__(kBlock, 1) void k_pf_exp(PfExpArgs a) {
   const int e = un.x, p0 = un.y, n = un.z;
   if (e < 0 || e >= a.E || n < 1 || n > a.nu || n > kPfUnitPositions || p0 < 0 || p0 + n > a.n_assign)
     return;
-  // the input row of each position: the token's x^c_q row (gate/up) or the position's h_q row
+  // the input row of each position: the token's x^c_q row (gate/up) or the position's h_q
+  // row, counted from the unit's first (down)
   if ((int)threadIdx.x < n) {
-    const int p = p0 + threadIdx.x;
-    int src = p;
+    int src = threadIdx.x;
     if (GU) {
-      const int asg = a.perm[p];
+      const int asg = a.perm[p0 + threadIdx.x];
       src = (asg >= 0 && asg < a.n_assign) ? asg / a.k : 0;
     }
     srcrow[threadIdx.x] = src;
@@ -840,11 +831,11 @@ __global__ __launch_bounds__(kBlock, 1) void k_pf_exp(PfExpArgs a) {
   }
   // blocks of 16 positions: the unit's count rounded up to one of the built tile heights
   const int nb = (n + 15) / 16;
-  if (nb <= 2) px_unit<GU, AF, 2>(a, ring, srcrow, trow, tr, wblk, p0, n);
-  else if (nb <= 4) px_unit<GU, AF, 4>(a, ring, srcrow, trow, tr, wblk, p0, n);
-  else if (nb <= 6) px_unit<GU, AF, 6>(a, ring, srcrow, trow, tr, wblk, p0, n);
-  else if (nb <= 8) px_unit<GU, AF, 8>(a, ring, srcrow, trow, tr, wblk, p0, n);
-  else px_unit<GU, AF, kPxMaxNB>(a, ring, srcrow, trow, tr, wblk, p0, n);
+  if (nb <= 2) px_unit<GU, AF, 2>(a, ring, srcrow, base, trow, tr, wblk, p0, n);
+  else if (nb <= 4) px_unit<GU, AF, 4>(a, ring, srcrow, base, trow, tr, wblk, p0, n);
+  else if (nb <= 6) px_unit<GU, AF, 6>(a, ring, srcrow, base, trow, tr, wblk, p0, n);
+  else if (nb <= 8) px_unit<GU, AF, 8>(a, ring, srcrow, base, trow, tr, wblk, p0, n);
+  else px_unit<GU, AF, kPxMaxNB>(a, ring, srcrow, base, trow, tr, wblk, p0, n);
 }
 
 // Zero the padding columns of a token's packed OUT row: u_hat columns l .. 128 ks_l and
@@ -1019,6 +1010,8 @@ hipError_t launch_pf_expert(const Shape& s, const uint8_t* experts, bool gu, int
   a.ks = gu ? s.ks_gu : s.ks_edn;
   a.n_tr = gu ? s.tr_gu : s.tr_edn;
   a.n_grp = cdiv(a.n_tr, kPxTR);
+  // the gathered gate/up input is addressed by 32-bit offsets from its start
+  if (gu && T * (int64_t)(s.prec == 2 ? 64 : 128) * a.ks > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
   a.units = ws.units;
   a.ctrl = ws.ctrl;
   a.nu = unit_positions(s, T);
