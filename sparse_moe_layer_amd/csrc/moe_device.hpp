@@ -43,6 +43,16 @@ __device__ __forceinline__ void store_out(const OutSink& o, int64_t i, float v) 
     if (o.xn) o.xn[i] = (uint16_t)(pack_bf16x2(r, 0.f) & 0xFFFFu);
   }
 }
+// The same for four consecutive columns i .. i + 3 (i a multiple of 4: 16-byte stores).
+__device__ __forceinline__ void store_out4(const OutSink& o, int64_t i, float4 v) {
+  if (o.delta) *reinterpret_cast<float4*>(o.delta + i) = v;
+  if (o.res) {
+    float4 r = *reinterpret_cast<const float4*>(o.res + i);
+    r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
+    *reinterpret_cast<float4*>(o.res + i) = r;
+    if (o.xn) *reinterpret_cast<uint2*>(o.xn + i) = make_uint2(pack_bf16x2(r.x, r.y), pack_bf16x2(r.z, r.w));
+  }
+}
 
 // D += A B for one 16x16x32 bf16 block (fp32 accumulation); A rows and B columns are
 // held as 8 consecutive K values per lane (lane l: row / column l % 16, K 8 (l / 16)..).

@@ -304,31 +304,47 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_pf_gemm(PfGemmArgs a) {
   // The 32 products of a stage held in (af, bw), with the 16 reads of the next stage's
   // operands (from L into naf, nbw) spread among them (read_after: the read, if any, that
   // follows product i), in the order the next stage's products take them (per slice: row
-  // piece 0, the four weight pieces, row pieces 1-3).  Issued in bursts, the reads of four
+  // piece 0, the four weight pieces, row pieces 1-3), and the 8 copies of stage kd into
+  // buffer D, one before every fourth product (issued together they hold the wavefront at
+  // the memory unit, behind the other wavefronts' copies, while its matrix core waits).  Issued in bursts, the reads of four
   // wavefronts that leave a barrier together queue at the LDS for hundreds of cycles, and
   // each matrix core stands idle until its wavefront has issued all 16; spread out, the LDS
   // serves them while the products run.  The last products follow the last read, so that
   // the wait for all reads that the compiler puts at the loop's head finds them done.
   auto mma_read = [&](const uint4 (&af)[2][4], const uint4 (&bw)[2][4], const uint4* L,
-                      uint4 (&naf)[2][4], uint4 (&nbw)[2][4]) {
+                      uint4 (&naf)[2][4], uint4 (&nbw)[2][4], const uint4* D, int kd) {
+    const int kc = kd < nk ? kd : nk - 1;
+    const uint32_t dbase = (uint32_t)(uintptr_t)D + 1024u * wv;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int h = i >> 4, mb = (i >> 2) & 3, nb = i & 3;
-      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[h][mb]),
-                                                           __builtin_bit_cast(bf16x8_t, bw[h][nb]),
-                                                           acc[mb][nb], 0, 0, 0);
-      const int r = gemm_read_after(i);
-      if (r >= 0) {
-        const int rh = r >> 3, j = r & 7;
-        if (j == 0) naf[rh][0] = L[a_word + 32 * rh];
-        else if (j <= 4) nbw[rh][j - 1] = L[w_word + 2 * (j - 1) * 64 + 32 * rh];
-        else naf[rh][j - 4] = L[a_word + 2 * (j - 4) * 64 + 32 * rh];
+    for (int s8 = 0; s8 < 8; ++s8) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (s8 < 4) copy_to_lds(src_a + (size_t)(4 * s8) * tile_bytes + (size_t)kc * 1024,
+                              __builtin_amdgcn_readfirstlane(dbase + 4096u * s8));
+      else {
+        const int tr = tr0 + 4 * (s8 - 4);
+        copy_to_lds(src_w + (size_t)(tr < a.tr_count ? tr : 0) * tile_bytes + (size_t)kc * 1024,
+                    __builtin_amdgcn_readfirstlane(dbase + 4096u * s8));
       }
-    }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // a product
-      if (gemm_read_after(i) >= 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // an LDS read
+      for (int i = 4 * s8; i < 4 * s8 + 4; ++i) {
+        const int h = i >> 4, mb = (i >> 2) & 3, nb = i & 3;
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[h][mb]),
+                                                             __builtin_bit_cast(bf16x8_t, bw[h][nb]),
+                                                             acc[mb][nb], 0, 0, 0);
+        const int r = gemm_read_after(i);
+        if (r >= 0) {
+          const int rh = r >> 3, j = r & 7;
+          if (j == 0) naf[rh][0] = L[a_word + 32 * rh];
+          else if (j <= 4) nbw[rh][j - 1] = L[w_word + 2 * (j - 1) * 64 + 32 * rh];
+          else naf[rh][j - 4] = L[a_word + 2 * (j - 4) * 64 + 32 * rh];
+        }
+      }
+#pragma unroll
+      for (int i = 4 * s8; i < 4 * s8 + 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // a product
+        if (gemm_read_after(i) >= 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // an LDS read
+      }
     }
   };
   // Stage k lives in buffer k % 5.  Its copies are issued three stages ahead, its operands
@@ -357,14 +373,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_pf_gemm(PfGemmArgs a) {
   read_stage(buf(0), o0a, o0b);
   for (int k = 0; k < nk; k += 2) {
     wait_stage();
-    dma_clamped(buf(k + 4), k + 4);
-    __builtin_amdgcn_sched_barrier(0);
-    mma_read(o0a, o0b, buf(k + 1), o1a, o1b);
+    mma_read(o0a, o0b, buf(k + 1), o1a, o1b, buf(k + 4), k + 4);
     __builtin_amdgcn_sched_barrier(0);
     wait_stage();
-    dma_clamped(buf(k + 5), k + 5);
-    __builtin_amdgcn_sched_barrier(0);
-    mma_read(o1a, o1b, buf(k + 2), o0a, o0b);
+    mma_read(o1a, o1b, buf(k + 2), o0a, o0b, buf(k + 5), k + 5);
     __builtin_amdgcn_sched_barrier(0);
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the repeated reads
@@ -372,8 +384,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_pf_gemm(PfGemmArgs a) {
   // Epilogue through LDS, 32 rows of the wavefront's 128 x 128 at a time: the accumulators
   // (accumulator i of block (mb, nb): row 32 mb + 8 (i / 4) + 4 (l / 32) + i % 4, column
   // 32 nb + l % 32 of the wave's tile) go to a wavefront-private fp32 slab of 32 rows x 128
-  // columns (row stride 132 words), then each lane takes 4 consecutive columns of a row:
-  // 16-byte stores, and a shared gate value meets its up value 8 columns further on.
+  // columns (row stride 132 words), then each lane takes 4 consecutive columns of a row
+  // (16-byte stores), or in the shared expert's tile rows 2 gate columns and their up
+  // values 8 columns further on.
   __syncthreads();   // every wavefront is done with the last stage's operands
   float* slab = reinterpret_cast<float*>(lds + wv * kGemmStageWords);
   const int64_t rbase = (int64_t)mt * kGemmTile + 128 * wm;
@@ -394,11 +407,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_pf_gemm(PfGemmArgs a) {
       const float4 y = *reinterpret_cast<const float4*>(slab + r * 132 + c4);
       if (row >= a.T) continue;
       if (!IN) {
-        if (n < a.d) {
-          const int64_t o = row * a.d + n;
-          store_out(a.sink, o, y.x); store_out(a.sink, o + 1, y.y);
-          store_out(a.sink, o + 2, y.z); store_out(a.sink, o + 3, y.w);
-        }
+        if (n < a.d) store_out4(a.sink, row * a.d + n, y);   // (d is a multiple of 8)
         continue;
       }
       const int tr = n >> 4, cc = n & 15;              // tile row and its columns cc .. cc + 3
@@ -416,17 +425,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_pf_gemm(PfGemmArgs a) {
       } else if (tr < a.tr_r + a.tr_dn) {
         const int r2 = 16 * (tr - a.tr_r) + cc;       // l is a multiple of 8
         if (r2 < a.l) *reinterpret_cast<float4*>(a.xc + row * a.l + r2) = y;
-      } else if (cc < 8) {
-        // gate columns cc .. cc + 3, their up values at cc + 8: h_s columns hc .. hc + 3
-        const int hc = 8 * (tr - a.tr_r - a.tr_dn) + cc;
-        const float4 u = *reinterpret_cast<const float4*>(slab + r * 132 + c4 + 8);
-        if (hc < a.ms) {   // ms is a multiple of 8: all four columns
-          const float h0 = glu_act_fast(y.x, u.x, a.act, a.rbg, a.bg, a.rbl, a.bl);
-          const float h1 = glu_act_fast(y.y, u.y, a.act, a.rbg, a.bg, a.rbl, a.bl);
-          const float h2 = glu_act_fast(y.z, u.z, a.act, a.rbg, a.bg, a.rbl, a.bl);
-          const float h3 = glu_act_fast(y.w, u.w, a.act, a.rbg, a.bg, a.rbl, a.bl);
-          *reinterpret_cast<uint2*>(a.ao + packed_off(row, a.hs_col0 + hc, a.ks_out)) =
-              make_uint2(pack_bf16x2(h0, h1), pack_bf16x2(h2, h3));
+      } else {
+        // the lane's tile row holds 8 gate and 8 up columns: the lane takes gate columns
+        // 2 (lane % 4), +1 and their up values 8 further on (every lane evaluates two SiTU
+        // values): h_s columns hc, hc + 1
+        const int g0 = 16 * (lrow >> 2) + 2 * (lrow & 3);
+        const float2 gv = *reinterpret_cast<const float2*>(slab + r * 132 + g0);
+        const float2 uv = *reinterpret_cast<const float2*>(slab + r * 132 + g0 + 8);
+        const int hc = 8 * (tr - a.tr_r - a.tr_dn) + 2 * (lrow & 3);
+        if (hc < a.ms) {   // ms is a multiple of 8: both columns
+          const float h0 = glu_act_fast(gv.x, uv.x, a.act, a.rbg, a.bg, a.rbl, a.bl);
+          const float h1 = glu_act_fast(gv.y, uv.y, a.act, a.rbg, a.bg, a.rbl, a.bl);
+          *reinterpret_cast<uint32_t*>(a.ao + packed_off(row, a.hs_col0 + hc, a.ks_out)) = pack_bf16x2(h0, h1);
         }
       }
     }
