@@ -104,13 +104,18 @@ constexpr int kTiledUnitPositions = 32;
 // the token-tiled launches holds up to 64 positions: an expert's weights are read once per 64
 // of its positions.  The launches whose input is hi/lo rows take such a unit in two halves.
 constexpr int kTiledUnitPositionsSingle = 64;
-// Positions per unit of the mx launches (10 blocks of 16 rows in the expert tile); an
-// expert's positions split into near-equal runs (even_units).
+// Positions per unit of the mx launches (at most 10 blocks of 16 rows in the expert tile);
+// an expert's positions split into near-equal runs (even_units).  With more than two such
+// units per expert on average the units hold at most 128 (8 blocks: the compiled loop of
+// the 10-block tile moves accumulators between register files every K-step; with many
+// units per expert the weights are read once per unit either way).
 constexpr int kPfUnitPositions = 160;
+constexpr int kPfUnitPositionsMany = 128;
 // Positions of one expert per unit of the expert launches (2 hi/lo rows each; one FP8
 // row each in the mx launches).
 inline int unit_positions(const Shape& s, int64_t T) {
-  if (mx_profile(s)) return kPfUnitPositions;
+  if (mx_profile(s))
+    return T * s.k > (int64_t)2 * kPfUnitPositions * s.E ? kPfUnitPositionsMany : kPfUnitPositions;
   if (token_tiled(s, T)) return s.latent ? kTiledUnitPositions : kTiledUnitPositionsSingle;
   // few tokens: all rows of a unit staged at once (2 hi/lo rows of the widest expert
   // input per position, within 56 KiB of LDS)
