@@ -208,6 +208,8 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t max_tokens, size_t*
  *             each part 256-aligned (internal); the slots [2] h_s and [3] h stay unused
  *       MX4:  as MX8 with rows of 64 bytes of E2M1 code pairs (low nibble first) per
  *             K-step of 128 in place of 128 E4M3 bytes, in the same parts
+ *       FP32 with at most 4 tokens of a latent layer: partial sums of h_s W_shared_down
+ *             over 4 ranges of m_s, float pairs (hi-row, lo-row sums) [4][T][d] (internal)
  *   [8] perm   [T*k]    int32    dispatch order -> assignment t*k+j
  *   [9] inv    [T*k]    int32    assignment -> dispatch order
  *  [10] counts [E]      int32    assignments per expert
@@ -290,7 +292,8 @@ typedef enum moe_step {
   MOE_STEP_DISPATCH = 3,    /* histogram, scan, stable permutation by expert (larger
                                batches; launches nothing otherwise) */
   MOE_STEP_EXPERT_GU = 4,   /* routed gate/up + SiTU */
-  MOE_STEP_EXPERT_DOWN = 5, /* routed down */
+  MOE_STEP_EXPERT_DOWN = 5, /* routed down; with few tokens of a latent layer (FP32) also the
+                               partial sums of h_s W_shared_down, which OUT adds */
   MOE_STEP_COMBINE = 6,     /* u = sum_j G_j E_j (larger batches: and u_hat) */
   MOE_STEP_OUT = 7,         /* Delta = RMSNorm(u) W_up_latent + h_s W_shared_down */
   MOE_NUM_STEPS = 8

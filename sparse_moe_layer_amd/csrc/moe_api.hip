@@ -106,6 +106,11 @@ size_t hilo_bytes(const Shape& s, int64_t T) {
   for (int i = 0; i < kHiloParts; ++i) n += hilo_part(s, T, i);
   return n;
 }
+// The few-token launches use slot [7] for the shared down-projection's partial sums.
+size_t slot7_bytes(const Shape& s, int64_t T) {
+  const size_t h = hilo_bytes(s, T), y = moe::sd_partial_bytes(s, T);
+  return h > y ? h : y;
+}
 
 // Workspace slots in the order of moe_workspace_layout.
 void layout(const Shape& s, int64_t T, size_t off[MOE_WS_NUM_SLOTS], size_t* total) {
@@ -119,7 +124,7 @@ void layout(const Shape& s, int64_t T, size_t off[MOE_WS_NUM_SLOTS], size_t* tot
       (size_t)tk * s.l * 4,                 // E
       (size_t)T * s.l * 4,                  // u
       (size_t)T * s.l * 4,                  // u_hat
-      hilo_bytes(s, T),                     // hi/lo rows of the token-tiled launches
+      slot7_bytes(s, T),                    // hi/lo rows of the token-tiled launches
       (size_t)tk * 4,                       // perm
       (size_t)tk * 4,                       // inv
       (size_t)s.E * 4,                      // counts
@@ -163,6 +168,7 @@ moe::Work make_work(const Shape& s, int64_t T, void* ws, const size_t off[MOE_WS
     w.pf.hsc = static_cast<uint8_t*>(parts[3]);
     w.pf.ao = static_cast<uint8_t*>(parts[4]);
     w.pf.ax = static_cast<uint8_t*>(parts[5]);
+    w.ys = reinterpret_cast<float2*>(b + off[7]);
   }
   w.perm = reinterpret_cast<int32_t*>(b + off[8]);
   w.inv = reinterpret_cast<int32_t*>(b + off[9]);
@@ -359,8 +365,8 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const float
           e = moe::launch_dispatch(s, topk_idx, n_tokens, ws.counts, ws.offs, ws.perm, ws.inv,
                                    ws.chunk_hist, ws.units, ws.ctrl, hs);
         break;
-      case MOE_STEP_EXPERT_GU: e = moe::launch_expert(s, experts, true, n_tokens, ws, hs); break;
-      case MOE_STEP_EXPERT_DOWN: e = moe::launch_expert(s, experts, false, n_tokens, ws, hs); break;
+      case MOE_STEP_EXPERT_GU: e = moe::launch_expert(s, experts, dense, true, n_tokens, ws, hs); break;
+      case MOE_STEP_EXPERT_DOWN: e = moe::launch_expert(s, experts, dense, false, n_tokens, ws, hs); break;
       case MOE_STEP_COMBINE: e = moe::launch_combine(s, dense, topk_w, n_tokens, ws, hs); break;
       case MOE_STEP_OUT: {
         moe::Prefetch pf{};

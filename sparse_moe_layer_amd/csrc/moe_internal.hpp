@@ -80,6 +80,7 @@ struct Work {
   int32_t* chunk_hist;  // [n_chunks][E]
   int32_t* units;  // [max_units][4]: expert, first position, positions, 0
   PfWork pf;       // the mx8 operands (same memory as the hi/lo rows)
+  float2* ys;      // few tokens: W_sd h_s partial sums [parts][T][d] (hi/lo rows' memory)
 };
 
 // Tokens per dispatch chunk (so that a chunk holds at most 256 assignments).
@@ -87,9 +88,8 @@ inline int dispatch_chunk_tokens(int k) { return k >= 256 ? 1 : 256 / k; }
 
 inline int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 // Tokens per workgroup of the IN launches (bf16 rows of d columns in LDS, next to the
-// route's own LDS) and of the OUT launch (hi/lo rows of l + m_s columns).
+// route's own LDS).
 inline int in_tokens_per_block(const Shape& s) { return clampi(45056 / (s.ks_in * kStepK * 2), 1, 16); }
-inline int out_tokens_per_block(const Shape& s) { return clampi(57344 / (s.ks_out * kStepK * 4), 1, 8); }
 // With this few tokens the route and the dispatch run inside the IN launch, and every
 // product stages all its activation rows at once (the decode launches); larger batches
 // take the token-tiled launches.
@@ -99,6 +99,55 @@ inline bool route_fused(const Shape& s, int64_t T) {
   return s.prec == 0 && T <= 4 && T * s.k <= kBlock && T <= in_tokens_per_block(s);
 }
 inline bool token_tiled(const Shape& s, int64_t T) { return !route_fused(s, T); }
+// Largest batch of the few-token launches.
+constexpr int kFewTokens = 4;
+
+// Wavefronts per tile row: split K until a single token's launch has enough wavefronts
+// to keep every compute unit streaming (about 16 per CU), keeping at least 8 K-steps per
+// wavefront.  The split depends on the matrix alone, never on the batch, so a token's
+// result has the same bits in every batch (the summation order is fixed per matrix).
+inline int choose_ksplit(int64_t tile_rows, int ks) {
+  int ksplit = 1;
+  while (ksplit < 4 && tile_rows * ksplit < 4096 && ks / (2 * ksplit) >= 8) ksplit *= 2;
+  return ksplit;
+}
+// The OUT product's partial sums, added in order.  Without a latent or a shared expert: ks_a
+// = all K-steps in parts of qper.  A latent layer with a shared expert (FP32 profile): the
+// u_hat segment's ks_a = ks_l K-steps in parts of qper (its K-split), then the h_s segment in
+// nsd parts of qper2; with few tokens the expert down launch forms those (h_s is ready after
+// the IN launch) and the OUT launch adds them, the token-tiled OUT launch forms the same.
+constexpr int kSdParts = 4;
+struct OutParts {
+  int ks_a, ksplit, qper, nsd, qper2;   // qper = cdiv(ks_a, ksplit)
+};
+inline OutParts out_parts(const Shape& s) {
+  OutParts o;
+  if (s.latent && s.ms > 0 && s.prec == 0) {
+    // the u_hat segment alone is short: split while each part keeps 4 K-steps
+    o.ks_a = s.ks_l;
+    o.ksplit = 1;
+    while (o.ksplit < 4 && s.tr_out * o.ksplit < 4096 && s.ks_l / (2 * o.ksplit) >= 4) o.ksplit *= 2;
+    o.qper = cdiv(s.ks_l, o.ksplit);
+    o.qper2 = cdiv(s.ks_ms, s.ks_ms < kSdParts ? s.ks_ms : kSdParts);
+    o.nsd = cdiv(s.ks_ms, o.qper2);
+  } else {
+    o.ks_a = s.ks_out;
+    o.ksplit = choose_ksplit(s.tr_out, s.ks_out);
+    o.qper = cdiv(s.ks_out, o.ksplit);
+    o.nsd = 0;
+    o.qper2 = 0;
+  }
+  return o;
+}
+// Tokens per workgroup of the OUT launch of a few tokens (hi/lo rows of the K-steps it stages).
+inline int out_tokens_per_block(const Shape& s) {
+  return clampi(57344 / (out_parts(s).ks_a * kStepK * 4), 1, 8);
+}
+// Bytes of Work::ys for a call of T tokens (kept monotonic in T).
+inline size_t sd_partial_bytes(const Shape& s, int64_t T) {
+  const int64_t t = T < kFewTokens ? T : kFewTokens;
+  return (size_t)out_parts(s).nsd * t * s.d * 8;
+}
 constexpr int kTiledUnitPositions = 32;
 // Without a latent the gate/up input is the token (one bf16 row per position), so a unit of
 // the token-tiled launches holds up to 64 positions: an expert's weights are read once per 64
@@ -106,9 +155,9 @@ constexpr int kTiledUnitPositions = 32;
 constexpr int kTiledUnitPositionsSingle = 64;
 // Positions per unit of the mx launches (at most 10 blocks of 16 rows in the expert tile);
 // an expert's positions split into near-equal runs (even_units).  With more than two such
-// units per expert on average the units hold at most 128 (8 blocks: the compiled loop of
-// the 10-block tile moves accumulators between register files every K-step; with many
-// units per expert the weights are read once per unit either way).
+// units per expert on average the units hold at most 128 (8 blocks): an expert's weights
+// are then read several times either way, and the shorter units measured faster there
+// (1.3% on a share of 112 experts at 8192 tokens, where an expert averages 1170 positions).
 constexpr int kPfUnitPositions = 160;
 constexpr int kPfUnitPositionsMany = 128;
 // Positions of one expert per unit of the expert launches (2 hi/lo rows each; one FP8
@@ -196,8 +245,9 @@ inline int route_planes(const Shape& s) { return mx_profile(s) ? 1 : s.zplanes; 
 hipError_t launch_dispatch(const Shape& s, const int32_t* idx, int64_t T, int32_t* counts,
                            int32_t* offs, int32_t* perm, int32_t* inv, int32_t* chunk_hist,
                            int32_t* units, int32_t* ctrl, hipStream_t st);
-hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_t T,
-                         const Work& ws, hipStream_t st);
+// dense: the packed dense weights (the down launch of a few tokens also takes W_sd h_s)
+hipError_t launch_expert(const Shape& s, const uint8_t* experts, const uint8_t* dense, bool gu,
+                         int64_t T, const Work& ws, hipStream_t st);
 // the combine, and for the token-tiled launches of the FP32 profile the norm
 hipError_t launch_combine(const Shape& s, const uint8_t* dense, const float* gw, int64_t T,
                           const Work& ws, hipStream_t st);

@@ -798,6 +798,29 @@ __device__ __forceinline__ f32x4_t run_tile_row_n(TileStream<WF, P>& ts, const u
   }
 }
 
+// run_tile_row for a wavefront whose whole range of n <= P K-steps is in the ring (loaded
+// before it stages its activations), unrolled per count (run_tile_row_n's counts above P
+// would hold two generations of the ring in registers); P = 3 is run_tile_row_n.
+template <int WF, int P>
+__device__ __forceinline__ f32x4_t run_tile_row_upto(TileStream<WF, P>& ts, const uint8_t* trow,
+                                                     int q0, int n, const uint4* sm, int arow,
+                                                     int nr) {
+  if constexpr (P == 3) {
+    return run_tile_row_n<WF, 3>(ts, trow, q0, n, sm, arow, nr);
+  } else {
+    static_assert(P <= 8, "counts up to 8");
+    switch (n) {
+#define MOE_N_CASE(N) \
+  case N: if constexpr (N <= P) return run_tile_row<WF, P, N>(ts, trow, q0, n, sm, arow, nr); else break;
+      MOE_N_CASE(1) MOE_N_CASE(2) MOE_N_CASE(3) MOE_N_CASE(4) MOE_N_CASE(5) MOE_N_CASE(6)
+      MOE_N_CASE(7) MOE_N_CASE(8)
+#undef MOE_N_CASE
+      default: break;
+    }
+    return f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
 // Partial blocks of the K-split: waves kp > 0 of a tile row hand theirs to the wave with
 // kp = 0, which adds them in the order kp = 1, 2, ... (a fixed order).
 __device__ __forceinline__ f32x4_t reduce_ksplit(f32x4_t acc, f32x4_t (*part)[kWave], int ksplit,
@@ -957,6 +980,15 @@ struct ExpArgs {
   int out_ld;
   int single;               // 1: the input is bf16 (lo rows zero): the long units read the
                             // hi rows alone, one row per position
+  // The down launch of a few tokens of a latent layer also takes the shared down-projection
+  // W_sd h_s, in its first sd_wgs workgroups: sd_parts partial products over ranges of
+  // sd_qper of the sd_ks K-steps that W_sd's tile rows hold from K-step sd_q0 of the OUT
+  // matrix (rows of sd_row K-steps), each written as (hi, lo) row sums [part][T][d].
+  const uint8_t* sd_w;
+  int sd_wgs, sd_parts, sd_q0, sd_qper, sd_ks, sd_row, sd_ntr;
+  const float* sd_hs;
+  int sd_ms, sd_T, sd_d;
+  float2* sd_out;
 };
 
 // Gate/up: h[p] = act(gate, up) (and, with out_hl, its hi/lo row for the token-tiled down
@@ -990,6 +1022,42 @@ __device__ __forceinline__ void exp_store(const ExpArgs& a, int p0, int n, int t
   }
 }
 
+constexpr int kSdDepth = 3;   // bf16 K-steps in flight per wavefront
+
+// Item bid of the shared down-projection in the down launch: (group of 4 tile rows, K-range
+// part), one tile row per wavefront.  The part's h_s columns of the T tokens are staged as
+// hi/lo rows, and the partial sums are those the OUT launch would form over the same
+// K-steps (run_tile_row from zero; its loop for any count, which keeps the launch's register
+// budget that of the expert items).
+__device__ __forceinline__ void sd_partial(const ExpArgs& a, int bid, uint4* sm, HiloRow* rows) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int grp = bid / a.sd_parts, kp = bid - grp * a.sd_parts;
+  const int tr = grp * kWavesPerBlock + wv;
+  const int qa = kp * a.sd_qper, n = min(a.sd_ks, qa + a.sd_qper) - qa;
+  const bool live = tr < a.sd_ntr && n > 0;
+  const uint8_t* trow =
+      a.sd_w + ((size_t)(live ? tr : 0) * a.sd_row + a.sd_q0 + (n > 0 ? qa : 0)) * kBf16StepBytes;
+  TileStream<0, kSdDepth> ts;
+  if (live) ts.prefetch(trow, 0, n);
+  const int nt = a.sd_T;
+  if ((int)threadIdx.x < nt)
+    rows[threadIdx.x] = HiloRow{a.sd_hs + (int64_t)threadIdx.x * a.sd_ms + qa * kStepK, nullptr, 1.f};
+  __syncthreads();
+  if (n > 0) stage_hilo(sm, rows, nt, min(n * kStepK, a.sd_ms - qa * kStepK), 0, 0, nullptr, n);
+  __syncthreads();
+  if (!live) return;
+  const int nr = 2 * nt;
+  const f32x4_t acc = run_tile_row<0, kSdDepth, 0>(ts, trow, 0, n, sm, c % nr, nr);
+  const int r = 16 * tr + c;
+  if (r >= a.sd_d) return;
+  // D rows 4g .. 4g + 3 = (hi, lo) of tokens 2g and 2g + 1
+  float2* o = a.sd_out + (int64_t)kp * nt * a.sd_d + r;
+  if (2 * g < nt) o[(int64_t)(2 * g) * a.sd_d] = make_float2(acc[0], acc[1]);
+  if (2 * g + 1 < nt) o[(int64_t)(2 * g + 1) * a.sd_d] = make_float2(acc[2], acc[3]);
+}
+
 template <int WF, bool GU>
 __global__ __launch_bounds__(kBlock) void k_exp(ExpArgs a) {
   extern __shared__ uint4 sm[];
@@ -998,13 +1066,20 @@ __global__ __launch_bounds__(kBlock) void k_exp(ExpArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
+  // the shared down-projection's workgroups first (their items are the longest); sd_wgs is
+  // a multiple of the XCD count, so the expert items keep their XCDs
+  if (!GU && (int)blockIdx.x < a.sd_wgs) {
+    sd_partial(a, blockIdx.x, sm, rows);
+    return;
+  }
+  const int bid = (int)blockIdx.x - (GU ? 0 : a.sd_wgs);
   // one (tile-row group, unit) item per workgroup, the units of a group on one XCD in
   // unit order (so that the units of one expert reuse its weights from that L2)
   const int n_units = min(a.ctrl[0], a.max_units);
   int wgi, u;
   if (a.chunk > 0) {
-    if (!chunk_item(blockIdx.x, n_units, a.wg_per_unit, a.chunk, wgi, u)) return;
-  } else if (!xcd_item(blockIdx.x, a.wg_per_unit, a.max_units, wgi, u) || u >= n_units) {
+    if (!chunk_item(bid, n_units, a.wg_per_unit, a.chunk, wgi, u)) return;
+  } else if (!xcd_item(bid, a.wg_per_unit, a.max_units, wgi, u) || u >= n_units) {
     return;
   }
   {
@@ -1044,16 +1119,22 @@ __global__ __launch_bounds__(kBlock) void k_exp(ExpArgs a) {
 // ------------------------------------------------------------------------------------
 // Step OUT: Delta[t] = [W_up_latent | W_shared_down] [RMSNorm(u_t) * gamma ; h_s,t], one
 // product over the packed OUT matrix.  The workgroup computes the norm of its tokens'
-// u rows and stages [u_hat ; h_s] as hi/lo pairs.
+// u rows and stages [u_hat ; h_s] as hi/lo pairs.  With few tokens of a latent layer the
+// h_s segment's partial sums come from the expert down launch (which streams W_shared_down
+// beside the experts' down weights), and this launch multiplies the u_hat segment alone.
 // ------------------------------------------------------------------------------------
 struct OutArgs {
   const uint8_t* w;
   int ks, ks_l, n_tr, ksplit, wg_per_blk, ntb, n_blk;
+  int ks_row;           // K-steps of a tile row (ks: those this launch multiplies, from 0)
   const float* u;
   const float* hs;
   const uint16_t* gamma;
   int d, l, ms, norm;
   int n0;               // columns of the u_hat segment (0 without a latent)
+  int n1;               // columns of the h_s segment staged (0: its products come from ys)
+  const float2* ys;     // [nsd][T][d] (hi, lo) partial sums of W_sd h_s, added in order
+  int nsd;
   float eps;
   int64_t T;
   OutSink sink;
@@ -1119,6 +1200,11 @@ __global__ __launch_bounds__(kBlock) void k_norm(const float* __restrict__ u,
   }
 }
 
+constexpr int kOutDeepRing = 7;
+
+// P: bf16 K-steps in the ring; 7 when every wavefront's range fits it (the whole range is
+// then in flight while the workgroup stages its activations), else 3.
+template <int P>
 __global__ __launch_bounds__(kBlock) void k_out(OutArgs a) {
   extern __shared__ uint4 sm[];
   __shared__ f32x4_t part[kWavesPerBlock][kWave];
@@ -1140,8 +1226,8 @@ __global__ __launch_bounds__(kBlock) void k_out(OutArgs a) {
   const int qper = cdiv(a.ks, a.ksplit);
   const int q0 = min(a.ks, kp * qper), q1 = min(a.ks, q0 + qper);
   const bool live = tr < a.n_tr && q1 > q0;
-  const uint8_t* trow = a.w + (size_t)tr * a.ks * kBf16StepBytes;
-  TileStream<0, 3> ts;
+  const uint8_t* trow = a.w + (size_t)tr * a.ks_row * kBf16StepBytes;
+  TileStream<0, P> ts;
   if (live) ts.prefetch(trow, q0, q1 - q0);
   for (int i = 0; i < nt; ++i) {
     const float* ur = a.u + (t0 + i) * a.l;
@@ -1149,14 +1235,30 @@ __global__ __launch_bounds__(kBlock) void k_out(OutArgs a) {
     if (threadIdx.x == 0) rows[i] = HiloRow{ur, a.hs + (t0 + i) * a.ms, inv};
   }
   __syncthreads();
-  stage_hilo(sm, rows, nt, a.n0, a.ks_l * kStepK, a.ms, a.norm ? a.gamma : nullptr, a.ks);
+  stage_hilo(sm, rows, nt, a.n0, a.ks_l * kStepK, a.n1, a.norm ? a.gamma : nullptr, a.ks);
   __syncthreads();
   const int nr = 2 * nt;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  if (live) acc = run_tile_row_n<0, 3>(ts, trow, q0, q1 - q0, sm, c % nr, nr);
+  if (live) acc = run_tile_row_upto<0, P>(ts, trow, q0, q1 - q0, sm, c % nr, nr);
   acc = reduce_ksplit(acc, part, a.ksplit, kp);
   if (tr < a.n_tr && kp == 0) {
     const int r = 16 * tr + c;
+    if (r < a.d) {
+      // the shared down-projection's parts after the K-split's, in part order
+      for (int p = 0; p < a.nsd; ++p) {
+        const float2* yp = a.ys + ((int64_t)p * a.T + t0 + 2 * g) * a.d + r;
+        if (2 * g < nt) {
+          const float2 v = yp[0];
+          acc[0] += v.x;
+          acc[1] += v.y;
+        }
+        if (2 * g + 1 < nt) {
+          const float2 v = yp[a.d];
+          acc[2] += v.x;
+          acc[3] += v.y;
+        }
+      }
+    }
     const float y0 = acc[0] + acc[1], y1 = acc[2] + acc[3];
     if (r < a.d) {
       const int64_t i0 = (t0 + 2 * g) * a.d + r, i1 = i0 + a.d;
@@ -1267,7 +1369,8 @@ struct TTStage {
 template <int WF, int P, int NB, int PA, bool PARTS, int TR>
 __device__ __forceinline__ void tt_run_tr(const TTRows& rows, const TTSrc& src,
                                           const uint8_t* const (&trow)[TR], int ks, int qper,
-                                          uint4* lds, f32x4_t (&tot)[TR][NB]) {
+                                          uint4* lds, f32x4_t (&tot)[TR][NB], int kb = -1,
+                                          int qper2 = 0) {
   static_assert(P % PA == 0, "the weight ring is a multiple of the activation ring");
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane & 15, g = lane >> 4;
@@ -1337,7 +1440,9 @@ __device__ __forceinline__ void tt_run_tr(const TTRows& rows, const TTSrc& src,
         for (int b = 0; b < NB; ++b) asm volatile("" : "+v"(cur[t][b]) :: "memory");
 #pragma unroll
       for (int t = 0; t < TR; ++t) ts[t].w[i].load(trow[t], min(q + P, ks - 1), lane);
-      if (PARTS && q < ks && (++in_part == qper || q + 1 == ks)) {
+      // parts of qper K-steps, or with kb >= 0 of qper up to K-step kb and qper2 after it
+      if (PARTS && q < ks &&
+          (++in_part == (kb < 0 || q < kb ? qper : qper2) || q + 1 == kb || q + 1 == ks)) {
 #pragma unroll
         for (int t = 0; t < TR; ++t)
 #pragma unroll
@@ -1364,10 +1469,11 @@ __device__ __forceinline__ void tt_run_tr(const TTRows& rows, const TTSrc& src,
 // One tile row per wavefront.
 template <int WF, int P, int NB, int PA = P, bool PARTS = true>
 __device__ __forceinline__ void tt_run(const TTRows& rows, const TTSrc& src, const uint8_t* trow,
-                                       int ks, int qper, uint4* lds, f32x4_t (&tot)[NB]) {
+                                       int ks, int qper, uint4* lds, f32x4_t (&tot)[NB],
+                                       int kb = -1, int qper2 = 0) {
   const uint8_t* const tr1[1] = {trow};
   f32x4_t t1[1][NB];
-  tt_run_tr<WF, P, NB, PA, PARTS, 1>(rows, src, tr1, ks, qper, lds, t1);
+  tt_run_tr<WF, P, NB, PA, PARTS, 1>(rows, src, tr1, ks, qper, lds, t1, kb, qper2);
 #pragma unroll
   for (int b = 0; b < NB; ++b) tot[b] = t1[0][b];
 }
@@ -1514,6 +1620,7 @@ __global__ __launch_bounds__(kBlock) void k_router_tt(RouterTTArgs a) {
 struct OutTTArgs {
   const uint8_t* w;
   int ks, ks_l, qper, n_tr, n_grp, n_tiles;
+  int kb, qper2;           // parts of qper K-steps up to K-step kb, of qper2 after it
   const uint16_t* uh_hl;   // [T][2][l]
   const uint16_t* hs_hl;   // [T][2][ms]
   int d, l, ms, n0;        // n0: columns of the u_hat segment (0 without a latent)
@@ -1548,7 +1655,8 @@ __global__ __launch_bounds__(kBlock) void k_out_tt(OutTTArgs a) {
   // per SIMD)
   tt_run<0, 2, kHiloTTBlocks, 2>(
       rows, TTSrc{a.uh_hl, a.hs_hl, 2 * nt, a.n0, a.ks_l * kStepK, a.ms},
-      a.w + (size_t)(live ? tr : 0) * a.ks * kBf16StepBytes, a.ks, a.qper, sm, tot);
+      a.w + (size_t)(live ? tr : 0) * a.ks * kBf16StepBytes, a.ks, a.qper, sm, tot, a.kb,
+      a.qper2);
   if (!live) return;
   const int r = 16 * tr + c;
   if (r >= a.d) return;
@@ -1828,16 +1936,6 @@ RouteArgs route_args(const Shape& s, const float* bias, int64_t T, const Work& w
                    (int)even_units(s)};
 }
 
-// Wavefronts per tile row: split K until a single token's launch has enough wavefronts
-// to keep every compute unit streaming (about 16 per CU), keeping at least 8 K-steps per
-// wavefront.  The split depends on the matrix alone, never on the batch, so a token's
-// result has the same bits in every batch (the summation order is fixed per matrix).
-int choose_ksplit(int64_t tile_rows, int ks) {
-  int ksplit = 1;
-  while (ksplit < kWavesPerBlock && tile_rows * ksplit < 4096 && ks / (2 * ksplit) >= 8) ksplit *= 2;
-  return ksplit;
-}
-
 }  // namespace
 
 namespace {
@@ -2010,9 +2108,9 @@ hipError_t launch_dispatch(const Shape& s, const int32_t* idx, int64_t T, int32_
   return hipGetLastError();
 }
 
-hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_t T,
-                         const Work& ws, hipStream_t st) {
-  ExpArgs a;
+hipError_t launch_expert(const Shape& s, const uint8_t* experts, const uint8_t* dense, bool gu,
+                         int64_t T, const Work& ws, hipStream_t st) {
+  ExpArgs a{};
   a.experts = experts;
   a.expert_bytes = s.expert_bytes;
   a.region_off = gu ? 0 : s.gu_bytes;
@@ -2076,10 +2174,29 @@ hipError_t launch_expert(const Shape& s, const uint8_t* experts, bool gu, int64_
     a.chunk = kExpChunk;
   } else {
     a.out_hl = nullptr;
+    const OutParts op = out_parts(s);
+    if (!gu && op.nsd > 0) {
+      if (!dense || T > kFewTokens) return hipErrorInvalidValue;
+      a.sd_w = dense + s.in_bytes;
+      a.sd_parts = op.nsd;
+      a.sd_q0 = s.ks_l;
+      a.sd_qper = op.qper2;
+      a.sd_ks = s.ks_ms;
+      a.sd_row = s.ks_out;
+      a.sd_ntr = s.tr_out;
+      a.sd_wgs = (int)(kXcds * cdiv((int64_t)cdiv(s.tr_out, kWavesPerBlock) * op.nsd, kXcds));
+      a.sd_hs = ws.hs;
+      a.sd_ms = s.ms;
+      a.sd_T = (int)T;
+      a.sd_d = s.d;
+      a.sd_out = ws.ys;
+    }
   }
-  const unsigned grid = (unsigned)(a.chunk > 0 ? chunk_grid(a.max_units, a.wg_per_unit, a.chunk)
-                                               : xcd_grid(a.wg_per_unit, a.max_units));
-  const size_t lds = (size_t)2 * a.nu * a.ks * kStepK * 2;
+  const unsigned grid = (unsigned)(a.sd_wgs + (a.chunk > 0 ? chunk_grid(a.max_units, a.wg_per_unit, a.chunk)
+                                                           : xcd_grid(a.wg_per_unit, a.max_units)));
+  size_t lds = (size_t)2 * a.nu * a.ks * kStepK * 2;
+  const size_t sd_lds = (size_t)2 * T * a.sd_qper * kStepK * 2;
+  if (a.sd_wgs > 0 && sd_lds > lds) lds = sd_lds;
   if (s.wfmt == 1) {
     if (gu) hipLaunchKernelGGL((k_exp<1, true>), dim3(grid), dim3(kBlock), lds, st, a);
     else hipLaunchKernelGGL((k_exp<1, false>), dim3(grid), dim3(kBlock), lds, st, a);
@@ -2112,7 +2229,10 @@ hipError_t launch_out(const Shape& s, const uint8_t* dense, int64_t T, const Wor
     OutTTArgs a;
     a.w = dense + s.in_bytes;
     a.ks = s.ks_out; a.ks_l = s.ks_l;
-    a.qper = cdiv(s.ks_out, choose_ksplit(s.tr_out, s.ks_out));
+    const OutParts op = out_parts(s);   // the parts of the few-token launches
+    a.qper = op.qper;
+    a.kb = op.nsd > 0 ? op.ks_a : -1;
+    a.qper2 = op.qper2;
     a.n_tr = s.tr_out;
     a.n_grp = cdiv(s.tr_out, kWavesPerBlock);
     a.n_tiles = cdiv(T, kHiloTTRows);
@@ -2126,24 +2246,34 @@ hipError_t launch_out(const Shape& s, const uint8_t* dense, int64_t T, const Wor
     return hipGetLastError();
   }
   OutArgs a;
+  const OutParts op = out_parts(s);
   a.w = dense + s.in_bytes;
-  a.ks = s.ks_out; a.ks_l = s.ks_l;
+  a.ks_row = s.ks_out; a.ks_l = s.ks_l;
+  a.ks = op.ks_a;                    // with nsd > 0 the u_hat segment alone
   a.n_tr = s.tr_out;
   a.ntb = out_tokens_per_block(s);   // 2 * ntb hi/lo rows: at most one 16-row MFMA block
   a.n_blk = cdiv(T, a.ntb);
-  a.ksplit = choose_ksplit(s.tr_out, s.ks_out);
+  a.ksplit = op.ksplit;
   a.wg_per_blk = cdiv((int64_t)a.n_tr * a.ksplit, kWavesPerBlock);
   a.u = ws.u; a.hs = ws.hs;
   a.gamma = reinterpret_cast<const uint16_t*>(dense + s.gamma_off);
   a.d = s.d; a.l = s.l; a.ms = s.ms; a.norm = s.use_norm; a.eps = s.eps;
   a.n0 = s.latent ? s.l : 0;
+  a.n1 = op.nsd > 0 ? 0 : s.ms;
+  a.ys = ws.ys;
+  a.nsd = op.nsd;
+  if (op.nsd > 0 && T > kFewTokens) return hipErrorInvalidValue;
   a.T = T; a.sink = out;
   a.add_u = s.latent ? nullptr : ws.u;
   a.prod_wgs = (int)xcd_grid(a.wg_per_blk, a.n_blk);
   a.pf = pf;
   a.pf_wgs = pf.p && pf.bytes >= 16 ? (int)((pf.bytes + kPrefetchWgBytes - 1) / kPrefetchWgBytes) : 0;
-  const size_t lds = (size_t)2 * (T < a.ntb ? T : a.ntb) * s.ks_out * kStepK * 2;
-  hipLaunchKernelGGL(k_out, dim3((unsigned)(a.prod_wgs + a.pf_wgs)), dim3(kBlock), lds, st, a);
+  const size_t lds = (size_t)2 * (T < a.ntb ? T : a.ntb) * a.ks * kStepK * 2;
+  const dim3 grid((unsigned)(a.prod_wgs + a.pf_wgs));
+  if (cdiv(a.ks, a.ksplit) <= kOutDeepRing)
+    hipLaunchKernelGGL((k_out<kOutDeepRing>), grid, dim3(kBlock), lds, st, a);
+  else
+    hipLaunchKernelGGL((k_out<3>), grid, dim3(kBlock), lds, st, a);
   return hipGetLastError();
 }
 
