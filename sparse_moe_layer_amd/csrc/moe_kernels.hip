@@ -654,6 +654,30 @@ __device__ __forceinline__ void stage_bf16(uint4* sm, const uint16_t* x, int64_t
   }
 }
 
+// One activation row staged from loads issued before the weight stream of the launch (the
+// loads complete in issue order, so staging loads issued after the stream would wait for
+// it).  Bf16RowPre: stage_bf16 of one row (nr = 1), up to 4 pieces of 8 columns per thread.
+constexpr int kPreBf16 = 4;
+struct Bf16RowPre {
+  uint4 v[kPreBf16];
+  static __device__ __forceinline__ bool fits(int ks) { return ks * 16 <= kBlock * kPreBf16; }
+  __device__ __forceinline__ void load(const uint16_t* x, int n, int ks) {
+#pragma unroll
+    for (int m = 0; m < kPreBf16; ++m) {
+      const int j = threadIdx.x + kBlock * m;
+      if (j < ks * 16)
+        v[m] = 8 * j < n ? *reinterpret_cast<const uint4*>(x + 8 * j) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  __device__ __forceinline__ void commit(uint4* sm, int ks) const {
+#pragma unroll
+    for (int m = 0; m < kPreBf16; ++m) {
+      const int j = threadIdx.x + kBlock * m;
+      if (j < ks * 16) sm[j] = v[m];
+    }
+  }
+};
+
 // Eight fp32 values into the hi and lo bf16 words.
 __device__ __forceinline__ void split_hilo(const float (&v)[8], uint4& hi, uint4& lo) {
   uint32_t h[4], l[4];
@@ -723,6 +747,43 @@ __device__ __forceinline__ void stage_hilo(uint4* sm, const HiloRow* rows, int n
     sm[j * nr + 2 * i + 1] = lo;
   }
 }
+
+// stage_hilo of one fp32 row (nt = 1, segment 0 of n0 columns, no gamma) from loads issued
+// before the weight stream, up to 2 pieces of 8 columns per thread.
+constexpr int kPreHilo = 2;
+struct HiloRowPre {
+  float4 v[kPreHilo][2];
+  static __device__ __forceinline__ bool fits(int ks) { return ks * 16 <= kBlock * kPreHilo; }
+  __device__ __forceinline__ void load(const float* p, int n0, int ks) {
+#pragma unroll
+    for (int m = 0; m < kPreHilo; ++m) {
+      const int j = threadIdx.x + kBlock * m;
+      if (j < ks * 16 && 8 * j < n0) {
+        v[m][0] = reinterpret_cast<const float4*>(p + 8 * j)[0];
+        v[m][1] = reinterpret_cast<const float4*>(p + 8 * j)[1];
+      }
+    }
+  }
+  __device__ __forceinline__ void commit(uint4* sm, int n0, int ks) const {
+#pragma unroll
+    for (int m = 0; m < kPreHilo; ++m) {
+      const int j = threadIdx.x + kBlock * m;
+      if (j >= ks * 16) continue;
+      float e[8];
+      if (8 * j < n0) {
+        e[0] = v[m][0].x; e[1] = v[m][0].y; e[2] = v[m][0].z; e[3] = v[m][0].w;
+        e[4] = v[m][1].x; e[5] = v[m][1].y; e[6] = v[m][1].z; e[7] = v[m][1].w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = 0.f;
+      }
+      uint4 hi, lo;
+      split_hilo(e, hi, lo);
+      sm[2 * j] = hi;
+      sm[2 * j + 1] = lo;
+    }
+  }
+};
 
 // The weight registers of one tile row in flight: P K-steps, filled by prefetch() before
 // the activations are staged (so that the stream starts at once) and consumed by run().
@@ -915,8 +976,15 @@ __device__ __forceinline__ void in_body(const InArgs& a) {
   const bool live = tr != INT_MAX && q1 > q0;
   const uint8_t* trow = a.w + (size_t)(live ? tr : 0) * a.ks * kBf16StepBytes;
   TileStream<0, 3> ts;
-  if (live) ts.prefetch(trow, q0, q1 - q0);
-  stage_bf16(sm, a.x + t0 * a.d, a.d, nt, a.d, a.ks);
+  if (nt == 1 && Bf16RowPre::fits(a.ks)) {   // one token: its row first, then the stream
+    Bf16RowPre pre;
+    pre.load(a.x + t0 * a.d, a.d, a.ks);
+    ts.prefetch(trow, live ? q0 : 0, live ? q1 - q0 : 1);   // unconditional: see k_out
+    pre.commit(sm, a.ks);
+  } else {
+    if (live) ts.prefetch(trow, q0, q1 - q0);
+    stage_bf16(sm, a.x + t0 * a.d, a.d, nt, a.d, a.ks);
+  }
   __syncthreads();
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   if (live) acc = run_tile_row_n<0, 3>(ts, trow, q0, q1 - q0, sm, c % nt, nt);
@@ -1040,12 +1108,20 @@ __device__ __forceinline__ void sd_partial(const ExpArgs& a, int bid, uint4* sm,
   const uint8_t* trow =
       a.sd_w + ((size_t)(live ? tr : 0) * a.sd_row + a.sd_q0 + (n > 0 ? qa : 0)) * kBf16StepBytes;
   TileStream<0, kSdDepth> ts;
-  if (live) ts.prefetch(trow, 0, n);
   const int nt = a.sd_T;
-  if ((int)threadIdx.x < nt)
-    rows[threadIdx.x] = HiloRow{a.sd_hs + (int64_t)threadIdx.x * a.sd_ms + qa * kStepK, nullptr, 1.f};
-  __syncthreads();
-  if (n > 0) stage_hilo(sm, rows, nt, min(n * kStepK, a.sd_ms - qa * kStepK), 0, 0, nullptr, n);
+  const int n0 = min(n * kStepK, a.sd_ms - qa * kStepK);
+  if (nt == 1 && n > 0 && HiloRowPre::fits(n)) {   // one token: its row first, then the stream
+    HiloRowPre pre;
+    pre.load(a.sd_hs + qa * kStepK, n0, n);
+    ts.prefetch(trow, 0, n);   // unconditional (tile row 0 without work): see k_out
+    pre.commit(sm, n0, n);
+  } else {
+    if (live) ts.prefetch(trow, 0, n);
+    if ((int)threadIdx.x < nt)
+      rows[threadIdx.x] = HiloRow{a.sd_hs + (int64_t)threadIdx.x * a.sd_ms + qa * kStepK, nullptr, 1.f};
+    __syncthreads();
+    if (n > 0) stage_hilo(sm, rows, nt, n0, 0, 0, nullptr, n);
+  }
   __syncthreads();
   if (!live) return;
   const int nr = 2 * nt;
@@ -1095,18 +1171,29 @@ __global__ __launch_bounds__(kBlock) void k_exp(ExpArgs a) {
     const uint8_t* trow = a.experts + (size_t)e * a.expert_bytes + a.region_off +
                           (size_t)tr * a.ks * WeightStep<WF>::SB;
     TileStream<WF, WF == 1 ? 4 : 3> ts;
-    if (live) ts.prefetch(trow, q0, q1 - q0);
-    if ((int)threadIdx.x < n) {
-      const int p = p0 + threadIdx.x;
-      int64_t src = p;
-      if (GU) {
-        const int asg = a.perm[p];
-        src = (asg >= 0 && asg < a.n_assign) ? asg / a.k : 0;
+    // one position whose row is known without a load (down: its own row; gate/up with a
+    // single token: token 0): the row first, then the stream
+    if (n == 1 && (!GU || a.n_assign == a.k) && HiloRowPre::fits(a.ks)) {
+      HiloRowPre pre;
+      pre.load(a.xin + (GU ? 0 : (int64_t)p0 * a.kin), a.kin, a.ks);
+      // unconditional: see k_out
+      ts.prefetch(live ? trow : a.experts + (size_t)e * a.expert_bytes + a.region_off,
+                  live ? q0 : 0, live ? q1 - q0 : 1);
+      pre.commit(sm, a.kin, a.ks);
+    } else {
+      if (live) ts.prefetch(trow, q0, q1 - q0);
+      if ((int)threadIdx.x < n) {
+        const int p = p0 + threadIdx.x;
+        int64_t src = p;
+        if (GU) {
+          const int asg = a.perm[p];
+          src = (asg >= 0 && asg < a.n_assign) ? asg / a.k : 0;
+        }
+        rows[threadIdx.x] = HiloRow{a.xin + src * a.kin, nullptr, 1.f};
       }
-      rows[threadIdx.x] = HiloRow{a.xin + src * a.kin, nullptr, 1.f};
+      __syncthreads();
+      stage_hilo(sm, rows, n, a.kin, 0, 0, nullptr, a.ks);
     }
-    __syncthreads();
-    stage_hilo(sm, rows, n, a.kin, 0, 0, nullptr, a.ks);
     __syncthreads();
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     if (live) acc = run_tile_row_n<WF, WF == 1 ? 4 : 3>(ts, trow, q0, q1 - q0, sm, c % nr, nr);
@@ -1182,6 +1269,71 @@ __device__ __forceinline__ float row_inv_rms(const float* ur, int l, float eps, 
   return 1.0f / sqrtf(tot / (float)l + eps);
 }
 
+// One token's u row and gamma, loaded by the OUT launch before its weight stream (the loads
+// complete in issue order, so a load issued after the stream would wait for it): thread i
+// holds columns 4 i + 1024 c, c < kOutRow4, the order row_inv_rms sums them in.
+constexpr int kOutRow4 = 4;   // l <= 4096
+struct OutRow {
+  float4 u[kOutRow4];
+  uint2 g[kOutRow4];
+  __device__ __forceinline__ void load(const float* ur, const uint16_t* gamma, int l) {
+#pragma unroll
+    for (int c = 0; c < kOutRow4; ++c) {
+      const int col = 4 * ((int)threadIdx.x + kBlock * c);
+      if (col < l) {
+        u[c] = *reinterpret_cast<const float4*>(ur + col);
+        if (gamma) g[c] = *reinterpret_cast<const uint2*>(gamma + col);
+      }
+    }
+  }
+  // row_inv_rms of the row (the same sums in the same order)
+  __device__ __forceinline__ float inv_rms(int l, float eps, float* red) const {
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x >> 6;
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < kOutRow4; ++c) {
+      if (4 * ((int)threadIdx.x + kBlock * c) < l) {
+        ss = fmaf(u[c].x, u[c].x, ss); ss = fmaf(u[c].y, u[c].y, ss);
+        ss = fmaf(u[c].z, u[c].z, ss); ss = fmaf(u[c].w, u[c].w, ss);
+      }
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) red[wv] = ss;
+    __syncthreads();
+    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+    return 1.0f / sqrtf(tot / (float)l + eps);
+  }
+  // The hi/lo rows 0 and 1 (nr = 2) of stage_hilo with segment 0 = the row (times scale and
+  // gamma when gamma is set), ks K-steps, no segment 1: the same words.
+  __device__ __forceinline__ void stage(uint4* sm, int l, float scale, bool gamma, int ks) const {
+    uint2* s2 = reinterpret_cast<uint2*>(sm);
+#pragma unroll
+    for (int c = 0; c < kOutRow4; ++c) {
+      const int col = 4 * ((int)threadIdx.x + kBlock * c);
+      if (col >= ks * kStepK) continue;
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (col < l) {
+        v[0] = u[c].x; v[1] = u[c].y; v[2] = u[c].z; v[3] = u[c].w;
+        if (gamma) {
+          v[0] = v[0] * scale * bf16_lo(g[c].x); v[1] = v[1] * scale * bf16_hi(g[c].x);
+          v[2] = v[2] * scale * bf16_lo(g[c].y); v[3] = v[3] * scale * bf16_hi(g[c].y);
+        }
+      }
+      uint32_t h[2], lo[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        h[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+        lo[i] = pack_bf16x2(v[2 * i] - bf16_lo(h[i]), v[2 * i + 1] - bf16_hi(h[i]));
+      }
+      // piece j = col / 8 holds words 2 j (hi) and 2 j + 1 (lo); this half is (col / 4) % 2
+      const int w = 2 * (col >> 3), half = (col >> 2) & 1;
+      s2[2 * w + half] = make_uint2(h[0], h[1]);
+      s2[2 * (w + 1) + half] = make_uint2(lo[0], lo[1]);
+    }
+  }
+};
+
 // u_hat = u * inv * gamma, one workgroup per token: the same values the OUT launch of a
 // few tokens stages itself (the same reduction and the same products).
 __global__ __launch_bounds__(kBlock) void k_norm(const float* __restrict__ u,
@@ -1228,14 +1380,27 @@ __global__ __launch_bounds__(kBlock) void k_out(OutArgs a) {
   const bool live = tr < a.n_tr && q1 > q0;
   const uint8_t* trow = a.w + (size_t)tr * a.ks_row * kBf16StepBytes;
   TileStream<0, P> ts;
-  if (live) ts.prefetch(trow, q0, q1 - q0);
-  for (int i = 0; i < nt; ++i) {
-    const float* ur = a.u + (t0 + i) * a.l;
-    const float inv = a.norm ? row_inv_rms(ur, a.l, a.eps, red) : 1.f;
-    if (threadIdx.x == 0) rows[i] = HiloRow{ur, a.hs + (t0 + i) * a.ms, inv};
+  // one token, the u_hat segment alone: its row first, then the weight stream
+  const bool one = nt == 1 && a.n1 == 0 && a.n0 == a.l && a.l % 4 == 0 &&
+                   a.l <= 4 * kBlock * kOutRow4;
+  if (one) {
+    OutRow row;
+    row.load(a.u + t0 * a.l, a.norm ? a.gamma : nullptr, a.l);
+    // unconditional (a wavefront without work re-reads K-step 0 of tile row 0), so that the
+    // wait for the row counts the stream's loads as still in flight
+    ts.prefetch(live ? trow : a.w, live ? q0 : 0, live ? q1 - q0 : 1);
+    const float inv = a.norm ? row.inv_rms(a.l, a.eps, red) : 1.f;
+    row.stage(sm, a.l, inv, a.norm != 0, a.ks);
+  } else {
+    if (live) ts.prefetch(trow, q0, q1 - q0);
+    for (int i = 0; i < nt; ++i) {
+      const float* ur = a.u + (t0 + i) * a.l;
+      const float inv = a.norm ? row_inv_rms(ur, a.l, a.eps, red) : 1.f;
+      if (threadIdx.x == 0) rows[i] = HiloRow{ur, a.hs + (t0 + i) * a.ms, inv};
+    }
+    __syncthreads();
+    stage_hilo(sm, rows, nt, a.n0, a.ks_l * kStepK, a.n1, a.norm ? a.gamma : nullptr, a.ks);
   }
-  __syncthreads();
-  stage_hilo(sm, rows, nt, a.n0, a.ks_l * kStepK, a.n1, a.norm ? a.gamma : nullptr, a.ks);
   __syncthreads();
   const int nr = 2 * nt;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
