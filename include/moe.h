@@ -185,7 +185,11 @@ moe_status moe_packed_experts_size(const moe_config* cfg, size_t* bytes);
 moe_status moe_pack_experts(const moe_config* cfg, const moe_expert_src* src, int32_t e0,
                             int32_t n, void* packed, size_t packed_bytes, moe_stream_t stream);
 
-/* Bytes of workspace that moe_layer_forward needs for up to max_tokens tokens. */
+/* Bytes of workspace that moe_layer_forward needs for up to max_tokens tokens.  A workspace
+ * starts with its first 256 bytes (the control words, slot [0]) zero, e.g. cleared once after
+ * it is allocated; every call leaves them that way.  (With at most 4 tokens of a latent layer
+ * in MOE_PREC_FP32, one word counts the router workgroups that have stored their logits, and
+ * the route waits for all of them.) */
 moe_status moe_workspace_size(const moe_config* cfg, int64_t max_tokens, size_t* bytes);
 
 /* Offsets (bytes) of the intermediates inside the workspace of a call with n_tokens,
@@ -283,7 +287,9 @@ moe_status moe_layer_forward_residual_prefetch(const moe_config* cfg, const moe_
  * its epilogue, COMBINE also normalises and rounds u_hat to bf16. */
 typedef enum moe_step {
   MOE_STEP_ROUTER = 0,      /* router logits z = x W_r (partial planes), and in the same
-                               launch x^c = x W_down_latent (larger batches: in IN) */
+                               launch x^c = x W_down_latent (larger batches: in IN; at most
+                               4 tokens of a latent layer in MOE_PREC_FP32: nothing, IN
+                               takes both) */
   MOE_STEP_IN = 1,          /* shared gate/up + SiTU; with few tokens one workgroup of the
                                same launch also takes the top-k, the gate weights and the
                                dispatch */

@@ -156,9 +156,12 @@ def packed_dense_size(cfg: MoeConfig) -> int:
 
 
 def new_workspace(cfg: MoeConfig, max_tokens: int, device):
-    """A device workspace for up to max_tokens tokens."""
+    """A device workspace for up to max_tokens tokens, its control words zeroed (as a
+    workspace must start; the calls leave them so)."""
     import torch
-    return torch.empty(max(workspace_size(cfg, max_tokens), 256), dtype=torch.uint8, device=device)
+    ws = torch.empty(max(workspace_size(cfg, max_tokens), 256), dtype=torch.uint8, device=device)
+    ws[:256].zero_()
+    return ws
 
 
 def packed_experts_size(cfg: MoeConfig) -> int:

@@ -16,6 +16,11 @@ constexpr int kFp4StepBytes = 1024 + 64;  // MXFP4 K-step: 16 rows x 128 codes +
 constexpr int kFp8StepBytes = 2048 + 16;  // FP8 block-128 K-step: 16 rows x 128 codes + the
                                           // gate-half and up-half block scales (fp32), padded
 constexpr int kCtrlWords = 64;          // control words at the head of the workspace
+// Control word kCtrlArrive (its own 128-byte line): the router workgroups of the IN launch of
+// a few tokens that have stored their logits; zero between calls (the route zeroes it once
+// all have arrived; a workspace starts with its control words zero).  The next word counts
+// waits that ended at the spin limit.
+constexpr int kCtrlArrive = 32;
 constexpr int kMaxK = 64;               // experts per token the kernels are built for
 
 __host__ __device__ inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
@@ -101,6 +106,11 @@ inline bool route_fused(const Shape& s, int64_t T) {
 inline bool token_tiled(const Shape& s, int64_t T) { return !route_fused(s, T); }
 // Largest batch of the few-token launches.
 constexpr int kFewTokens = 4;
+// With few tokens of a latent layer (FP32 profile) the IN launch also takes the router rows
+// and W_down_latent: its route workgroup waits for the router workgroups' arrivals.
+inline bool in_takes_router(const Shape& s, int64_t T) {
+  return s.prec == 0 && s.latent && route_fused(s, T);
+}
 
 // Wavefronts per tile row: split K until a single token's launch has enough wavefronts
 // to keep every compute unit streaming (about 16 per CU), keeping at least 8 K-steps per

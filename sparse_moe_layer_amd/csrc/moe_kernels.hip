@@ -63,6 +63,9 @@ struct RouteArgs {
 constexpr int kRouteSlots = 4;      // E <= 4 slots x 4 wavefronts x 64 lanes = 1024
 constexpr int kMaxZPlanes = 8;      // partial logit planes of the router launch
 
+// AGENT: the logit planes come from other workgroups of the same launch (agent-scope loads:
+// the XCDs' L2 caches are not coherent with each other within a launch).
+template <bool AGENT>
 __device__ __forceinline__ void block_route_token(const RouteArgs& a, int64_t t, uint64_t* cand_key,
                                                   float* cand_s, int* sel_e, float* sel_s,
                                                   int* sidx) {
@@ -79,7 +82,9 @@ __device__ __forceinline__ void block_route_token(const RouteArgs& a, int64_t t,
     const bool ok = e < a.E;
 #pragma unroll
     for (int p = 0; p < kMaxZPlanes; ++p)
-      zp[i][p] = (ok && p < a.zplanes) ? zr[p * a.zplane + e] : 0.f;
+      zp[i][p] = !(ok && p < a.zplanes) ? 0.f
+                 : AGENT ? __hip_atomic_load(zr + p * a.zplane + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : zr[p * a.zplane + e];
     bv[i] = ok ? a.bias[e] : 0.f;
   }
 #pragma unroll
@@ -173,6 +178,7 @@ __device__ __forceinline__ void unit_run(int tot, int nu, int even, int i, int& 
 
 // The route of tokens t_begin..t_end-1 by one workgroup; with `dispatch`, also the
 // counting sort of their (at most 256) assignments by expert.
+template <bool AGENT = false>
 __device__ void route_block(const RouteArgs& a, int64_t t_begin, int64_t t_end, bool dispatch) {
   __shared__ uint64_t cand_key[kWavesPerBlock * kMaxK];
   __shared__ float cand_s[kWavesPerBlock * kMaxK];
@@ -184,7 +190,7 @@ __device__ void route_block(const RouteArgs& a, int64_t t_begin, int64_t t_end, 
   __shared__ int part[kBlock];
   __shared__ int upart[kBlock];
   for (int64_t t = t_begin; t < t_end; ++t)
-    block_route_token(a, t, cand_key, cand_s, sel_e, sel_s, dispatch ? sidx : nullptr);
+    block_route_token<AGENT>(a, t, cand_key, cand_s, sel_e, sel_s, dispatch ? sidx : nullptr);
   if (!dispatch) return;
   // dispatch of the n = T*k <= 256 assignments
   const int n = (int)(a.T * a.k);
@@ -927,7 +933,17 @@ struct InArgs {
   float bg, bl;
   int route;
   RouteArgs ra;
+  // n_arrive > 0: the router rows run in this launch too.  Their workgroups store their
+  // logits with agent-scope stores and then count themselves in *arrive; workgroup 0 waits
+  // for all n_arrive of them (after which it zeroes the counter) before the route.
+  int32_t* arrive;
+  int n_arrive;
 };
+
+// Spin limit of the route's wait for the router workgroups of its launch (each try sleeps
+// about 0.1 us); a wait that reaches it goes on (and counts itself in the word after the
+// counter) rather than hold the GPU.
+constexpr int kRouteSpinLimit = 1 << 22;
 
 __device__ __forceinline__ void in_body(const InArgs& a) {
   extern __shared__ uint4 sm[];
@@ -936,7 +952,21 @@ __device__ __forceinline__ void in_body(const InArgs& a) {
     // the logits come from the ROUTER launch; this workgroup's selection runs while the
     // others stream the shared weights
     if (blockIdx.x == 0) {
-      route_block(a.ra, 0, a.T, true);
+      if (a.n_arrive > 0) {
+        if (threadIdx.x == 0) {
+          int n = 0;
+          while (__hip_atomic_load(a.arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.n_arrive &&
+                 ++n < kRouteSpinLimit)
+            __builtin_amdgcn_s_sleep(2);
+          if (n == kRouteSpinLimit)
+            __hip_atomic_fetch_add(a.arrive + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(a.arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        route_block<true>(a.ra, 0, a.T, true);
+      } else {
+        route_block(a.ra, 0, a.T, true);
+      }
       return;
     }
   }
@@ -996,7 +1026,11 @@ __device__ __forceinline__ void in_body(const InArgs& a) {
       float* zp = a.z + (int64_t)(wgi - tr * a.zplanes) * a.T * a.E;
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        if (4 * g + v < nt && e < a.E) zp[(t0 + 4 * g + v) * a.E + e] = acc[v];
+        if (4 * g + v < nt && e < a.E) {
+          float* o = zp + (t0 + 4 * g + v) * a.E + e;
+          if (a.n_arrive > 0) __hip_atomic_store(o, acc[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else *o = acc[v];
+        }
     } else if (tr < a.tr_r + a.tr_dn) {
       const int r = 16 * (tr - a.tr_r) + c;
 #pragma unroll
@@ -1011,6 +1045,12 @@ __device__ __forceinline__ void in_body(const InArgs& a) {
           a.hs[(t0 + 4 * g + v) * a.ms + r] = glu_act(gate, acc[v], a.act, a.bg, a.bl);
       }
     }
+  }
+  if (router && a.n_arrive > 0) {
+    // every logit of the workgroup stored before its arrival is counted
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(a.arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -2125,6 +2165,8 @@ InArgs in_args(const Shape& s, const uint8_t* dense, const uint16_t* x, int64_t 
   a.hs = ws.hs; a.ms = s.ms;
   a.act = s.act; a.bg = s.beta_gate; a.bl = s.beta_lin;
   a.route = 0;
+  a.arrive = nullptr;
+  a.n_arrive = 0;
   return a;
 }
 
@@ -2179,6 +2221,7 @@ hipError_t launch_router(const Shape& s, const uint8_t* dense, const uint16_t* x
     else hipLaunchKernelGGL(k_router_tt<1>, grid, dim3(kBlock), lds, st, a);
     return hipGetLastError();
   }
+  if (!router_only && in_takes_router(s, T)) return hipSuccess;   // the IN launch takes them
   InArgs a = in_args(s, dense, x, T, ws, s.tr_r, router_only ? 0 : s.tr_dn);
   a.router_wgs = s.tr_r * s.zplanes;
   a.wg_per_blk += a.router_wgs;
@@ -2209,10 +2252,19 @@ hipError_t launch_in(const Shape& s, const uint8_t* dense, const uint16_t* x, in
                        a);
     return hipGetLastError();
   }
-  const int n_tr = in_launch_shared_rows(s);
+  const bool all = in_takes_router(s, T);
+  const int n_tr = all ? s.tr_dn + s.tr_sh : in_launch_shared_rows(s);
   InArgs a = in_args(s, dense, x, T, ws, s.tr_in - n_tr, n_tr);
   a.route = route_fused(s, T) ? 1 : 0;
   a.ra = route_args(s, bias, T, ws, idx, gw);
+  if (all) {
+    // the router rows first (the lowest workgroup numbers after the route's: dispatched
+    // before the others, they wait for nothing), then W_down_latent and the shared gate/up
+    a.router_wgs = s.tr_r * s.zplanes;
+    a.wg_per_blk += a.router_wgs;
+    a.arrive = ws.ctrl + kCtrlArrive;
+    a.n_arrive = a.router_wgs * a.n_blk;
+  }
   const int64_t grid = (a.wg_per_blk > 0 ? xcd_grid(a.wg_per_blk, a.n_blk) : 0) + a.route;
   if (grid == 0) return hipSuccess;   // no shared expert and a separate route
   const size_t lds = (size_t)(T < a.ntb ? T : a.ntb) * s.ks_in * kStepK * 2;
