@@ -63,7 +63,11 @@ moe_status make_shape(const moe_config* c, Shape* s) {
   s->tr_dn = s->latent ? moe::cdiv(s->l, moe::kTileRows) : 0;
   s->tr_sh = moe::cdiv(s->ms, moe::kTileRows / 2);
   s->tr_in = s->tr_r + s->tr_dn + s->tr_sh;
-  s->zplanes = moe::clampi(s->ks_in / 7, 1, 8);
+  // Router logits as partial planes over K-ranges of at least 28 K-steps (2 at d = 7168):
+  // with few tokens the router workgroups of the IN launch then finish well before its
+  // stream does (so the route that waits for them is hidden) without crowding the
+  // launch's first wave (8 planes: 2.5 us per token slower at B = 1, 0.6% faster at 64).
+  s->zplanes = moe::clampi(s->ks_in / 28, 1, 8);
   s->ks_l = s->latent ? moe::cdiv(s->l, moe::kStepK) : 0;   // OUT's u_hat segment
   s->ks_ms = moe::cdiv(s->ms, moe::kStepK);
   s->ks_out = s->ks_l + s->ks_ms;
