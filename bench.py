@@ -61,22 +61,36 @@ def algorithmic_bytes(cfg, T, D):
         # one IN product (router logits, x^c fp32, h_s bf16), then x^c to MX
         router = T * d * 2 + (E + cfg.l + 2 * ms) * d * 2 + T * (E * 4 + cfg.l * 4 + ms * 2)
         in_ = T * cfg.l * 4 + T * cfg.l * ab
+    elif small and cfg.l:
+        # a few tokens of a latent layer: one IN launch takes the router, W_down_latent and the
+        # shared gate/up (and the route); W_shared_down rides in the expert down launch
+        router = 0
+        in_ = (T * d * 2 + (E + cfg.l + 2 * ms) * d * 2 + T * (E + cfg.l + ms) * 4
+               + T * E * 4 + E * 4 + tk * 16 + E * 8)
     else:
         # W_down_latent rides in the ROUTER launch for a few tokens, in the IN launch otherwise
         ldn = cfg.l if small else 0
         router = T * d * 2 + (E + ldn) * d * 2 + T * (E + ldn) * 4
         in_ = (T * d * 2 + (cfg.l - ldn + 2 * ms) * d * 2 + T * (cfg.l - ldn + ms) * 4
                + ((T * E * 4 + E * 4 + tk * 16 + E * 8) if small else 0))
+    if not mx and small and cfg.l and ms:
+        # the four partial sums of h_s W_shared_down, written by the down launch, read by OUT
+        sd = ms * d * 2 + T * ms * 4 + 4 * T * d * 8
+        down = D * dn_w + tk * m * ab + tk * l * 4 + sd
+        out = d * cfg.l * 2 + cfg.l * 2 + T * l * 4 + 4 * T * d * 8 + T * d * 4
+    else:
+        down = D * dn_w + tk * m * ab + tk * l * 4
+        out = d * (cfg.l + ms) * 2 + cfg.l * 2 + T * (l + ms) * (2 if mx else 4) + T * d * 4
     return {
         "router": router,
         "in": in_,
         "route": 0 if small else T * E * 4 + E * 4 + tk * 8,
         "dispatch": 0 if small else tk * 4 * 4 + E * 8,
         "expert_gu": D * gu_w + T * l * ab + tk * m * ab,
-        "expert_down": D * dn_w + tk * m * ab + tk * l * 4,
+        "expert_down": down,
         # (mx: one pass to u_hat in bf16, u itself is not stored)
         "combine": tk * l * 4 + tk * 8 + T * l * (2 if mx else 4),
-        "out": d * (cfg.l + ms) * 2 + cfg.l * 2 + T * (l + ms) * (2 if mx else 4) + T * d * 4,
+        "out": out,
     }
 
 def algorithmic_flops(cfg, T):
