@@ -210,9 +210,16 @@ def test_k3_decode_b64_all_tokens():
     log(f"[k3 b64] distinct experts {len(np.unique(idx))}")
     rel, _, _ = check(cfg, x, delta, idx, w)
     assert rel < 1e-4
-    # per-token independence: the same token alone gives the same Delta bits
-    d1, i1, w1 = run(lay, x[21:22])
-    assert np.array_equal(i1[0], idx[21]) and np.array_equal(d1[0], delta[21])
+    # per-token independence: the same tokens alone or in twos and threes (the few-token
+    # launches: router rows in the IN launch, W_shared_down partial sums in the down launch)
+    # give the same Delta bits as in the token-tiled batch
+    for lo, hi in ((21, 22), (10, 12), (40, 43)):
+        d1, i1, w1 = run(lay, x[lo:hi])
+        assert np.array_equal(i1, idx[lo:hi]) and np.array_equal(d1, delta[lo:hi]), (lo, hi)
+    # the route's wait for the router workgroups ended by their arrivals (the counter is back
+    # at zero, and no wait reached its spin limit)
+    ctrl = lay.workspace(1)[:256].view(torch.int32).cpu().numpy()
+    assert ctrl[32] == 0 and ctrl[33] == 0, ctrl[32:34]
 
 
 def test_k3_decode_b64_zipf_layer():
