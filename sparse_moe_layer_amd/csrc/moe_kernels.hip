@@ -1423,9 +1423,19 @@ __global__ __launch_bounds__(kBlock) void k_out(OutArgs a) {
   // one token, the u_hat segment alone: its row first, then the weight stream
   const bool one = nt == 1 && a.n1 == 0 && a.n0 == a.l && a.l % 4 == 0 &&
                    a.l <= 4 * kBlock * kOutRow4;
+  // with one token, the W_sd partial sums this lane adds (token 0: lanes g = 0 of the
+  // wavefront with kp = 0) are loaded with the row too
+  float2 ysv[kSdParts];
+  const bool ys_lane = one && a.nsd > 0 && a.nsd <= kSdParts && kp == 0 && tr < a.n_tr &&
+                       16 * tr + c < a.d && g == 0;
   if (one) {
     OutRow row;
     row.load(a.u + t0 * a.l, a.norm ? a.gamma : nullptr, a.l);
+    if (ys_lane) {
+#pragma unroll
+      for (int p = 0; p < kSdParts; ++p)
+        if (p < a.nsd) ysv[p] = a.ys[((int64_t)p * a.T + t0) * a.d + 16 * tr + c];
+    }
     // unconditional (a wavefront without work re-reads K-step 0 of tile row 0), so that the
     // wait for the row counts the stream's loads as still in flight
     ts.prefetch(live ? trow : a.w, live ? q0 : 0, live ? q1 - q0 : 1);
@@ -1450,7 +1460,15 @@ __global__ __launch_bounds__(kBlock) void k_out(OutArgs a) {
     const int r = 16 * tr + c;
     if (r < a.d) {
       // the shared down-projection's parts after the K-split's, in part order
-      for (int p = 0; p < a.nsd; ++p) {
+      if (ys_lane) {
+#pragma unroll
+        for (int p = 0; p < kSdParts; ++p)
+          if (p < a.nsd) {
+            acc[0] += ysv[p].x;
+            acc[1] += ysv[p].y;
+          }
+      }
+      for (int p = 0; p < (one ? 0 : a.nsd); ++p) {
         const float2* yp = a.ys + ((int64_t)p * a.T + t0 + 2 * g) * a.d + r;
         if (2 * g < nt) {
           const float2 v = yp[0];
