@@ -219,7 +219,8 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t max_tokens, size_t*
  *  [10] counts [E]      int32    assignments per expert
  *  [11] offsets[E+1]    int32    exclusive scan of counts
  *  [12] z      [P][T][E] fp32   router logits as P partial planes over ranges of d (their
- *                                sum); after the route, plane 0 holds the logits
+ *                                sum, added four at a time and then in order; P = 8 at
+ *                                d = 7168); after the route, plane 0 holds the logits
  *  [13] per-chunk expert histograms of the dispatch (internal)
  *  [14] unit table of the expert launches (internal) */
 #define MOE_WS_NUM_SLOTS 15

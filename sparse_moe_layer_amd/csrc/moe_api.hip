@@ -133,7 +133,7 @@ void layout(const Shape& s, int64_t T, size_t off[MOE_WS_NUM_SLOTS], size_t* tot
       (size_t)tk * 4,                       // inv
       (size_t)s.E * 4,                      // counts
       (size_t)(s.E + 1) * 4,                // offsets
-      (size_t)s.zplanes * T * s.E * 4,      // z (partial planes)
+      (size_t)s.zplanes * moe::kZSub * T * s.E * 4,   // z (partial planes, their parts)
       (size_t)nch * s.E * 4,                // chunk histograms
       (size_t)moe::max_units(s, T) * 16,    // unit table
   };

@@ -38,7 +38,8 @@ struct Shape {
   // packed dense weights: IN = [router ; W_down_latent ; shared gate/up] over K = d,
   // OUT = [W_up_latent | W_shared_down] over K = l (padded) + m_s
   int ks_in, tr_r, tr_dn, tr_sh, tr_in;
-  int zplanes;   // router K-ranges computed apart (partial logit planes summed by the route)
+  int zplanes;   // router K-ranges computed apart (partial logit planes summed by the route),
+                 // each held as kZSub sub-planes (its K-range split in kZSub parts)
   int ks_l, ks_ms, ks_out, tr_out;
   size_t in_bytes, out_bytes, gamma_off, dense_bytes;
   // packed experts: gate/up tiles (8 gate + 8 up rows) over K = l, then down tiles over K = m
@@ -81,7 +82,8 @@ struct Work {
   int32_t* inv;    // [T*k]
   int32_t* counts; // [E]
   int32_t* offs;   // [E+1]
-  float* z;        // [zplanes][T][E] partial logits; plane 0 holds the logits after the route
+  float* z;        // [zplanes * kZSub][T][E] partial logits; plane 0 holds the logits after
+                   // the route
   int32_t* chunk_hist;  // [n_chunks][E]
   int32_t* units;  // [max_units][4]: expert, first position, positions, 0
   PfWork pf;       // the mx8 operands (same memory as the hi/lo rows)
@@ -252,6 +254,12 @@ hipError_t launch_route(const Shape& s, const float* bias, int64_t T, const Work
 // The logit planes the route sums: the router launch's K-split, or 1 (mx profiles: plain
 // logits).
 inline int route_planes(const Shape& s) { return mx_profile(s) ? 1 : s.zplanes; }
+// Sub-planes per logit plane: a plane's K-range in kZSub parts, stored apart and added in
+// order by the route, ((z0 + z1) + z2) + z3 (the order in which the four wavefronts of a
+// few-token router workgroup would add them), so that the token-tiled router can take each
+// part in a workgroup of its own.
+constexpr int kZSub = 4;
+inline int route_subplanes(const Shape& s) { return mx_profile(s) ? 1 : kZSub; }
 hipError_t launch_dispatch(const Shape& s, const int32_t* idx, int64_t T, int32_t* counts,
                            int32_t* offs, int32_t* perm, int32_t* inv, int32_t* chunk_hist,
                            int32_t* units, int32_t* ctrl, hipStream_t st);

@@ -41,9 +41,10 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 // of the expert launches.
 // ------------------------------------------------------------------------------------
 struct RouteArgs {
-  float* z;         // zplanes partial planes [zplanes][T][E]; the route leaves their sum in plane 0
-  int zplanes;
-  int64_t zplane;   // floats between planes
+  float* z;         // zplanes partial planes of zsub parts each [zplanes * zsub][T][E]; the
+                    // route leaves their sum in plane 0
+  int zplanes, zsub;
+  int64_t zplane;   // floats between (sub-)planes
   const float* bias;
   int64_t T;
   int E, k;
@@ -61,7 +62,23 @@ struct RouteArgs {
 };
 
 constexpr int kRouteSlots = 4;      // E <= 4 slots x 4 wavefronts x 64 lanes = 1024
-constexpr int kMaxZPlanes = 8;      // partial logit planes of the router launch
+constexpr int kMaxZPlanes = 8;      // partial logit (sub-)planes of the router launch
+
+// The logit from its partial planes: each plane's parts added in order, then the planes in
+// plane order from zero (absent planes add nothing).
+// (Compile-time indices only: a register array indexed at run time would live in scratch.)
+__device__ __forceinline__ float plane_sum(const float (&zp)[kMaxZPlanes], int planes, int sub) {
+  float zv = 0.f, pv = 0.f;
+#pragma unroll
+  for (int q = 0; q < kMaxZPlanes; ++q) {
+    if (q < planes * sub) {
+      const int r = q % sub;
+      pv = r == 0 ? zp[q] : pv + zp[q];
+      if (r == sub - 1) zv += pv;
+    }
+  }
+  return zv;
+}
 
 // AGENT: the logit planes come from other workgroups of the same launch (agent-scope loads:
 // the XCDs' L2 caches are not coherent with each other within a launch).
@@ -76,13 +93,14 @@ __device__ __forceinline__ void block_route_token(const RouteArgs& a, int64_t t,
   // every logit plane and bias value of this lane's experts in flight at once
   float* zr = a.z + t * a.E;
   float zp[kRouteSlots][kMaxZPlanes], bv[kRouteSlots];
+  const int np = a.zplanes * a.zsub;
 #pragma unroll
   for (int i = 0; i < kRouteSlots; ++i) {
     const int e = (i * kWavesPerBlock + wv) * kWave + lane;
     const bool ok = e < a.E;
 #pragma unroll
     for (int p = 0; p < kMaxZPlanes; ++p)
-      zp[i][p] = !(ok && p < a.zplanes) ? 0.f
+      zp[i][p] = !(ok && p < np) ? 0.f
                  : AGENT ? __hip_atomic_load(zr + p * a.zplane + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                          : zr[p * a.zplane + e];
     bv[i] = ok ? a.bias[e] : 0.f;
@@ -90,11 +108,9 @@ __device__ __forceinline__ void block_route_token(const RouteArgs& a, int64_t t,
 #pragma unroll
   for (int i = 0; i < kRouteSlots; ++i) {
     const int e = (i * kWavesPerBlock + wv) * kWave + lane;
-    float zv = 0.f;
-#pragma unroll
-    for (int p = 0; p < kMaxZPlanes; ++p) zv += zp[i][p];   // plane order; absent planes add 0
+    const float zv = plane_sum(zp[i], a.zplanes, a.zsub);
     if (e < a.E) {
-      if (a.zplanes > 1) zr[e] = zv;   // the logits themselves, for inspection
+      if (np > 1) zr[e] = zv;   // the logits themselves, for inspection
       const float s = sigmoidf_(zv);
       float kk = s + bv[i];
       if (kk != kk) kk = -INFINITY;
@@ -377,7 +393,7 @@ __global__ __launch_bounds__(kBlock) void k_disp_scatter(const int32_t* idx, int
 // ------------------------------------------------------------------------------------
 struct QbArgs {
   float* z;
-  int zplanes;
+  int zplanes, zsub;
   int64_t zplane;
   const float* bias;
   int64_t T;
@@ -424,9 +440,10 @@ __device__ __forceinline__ void qb_range(const float* bias, int E, float* red, f
 // route adds them), then the float32 sigmoid.
 __device__ __forceinline__ float qb_score(const QbArgs& a, int64_t t, int e) {
   const float* zr = a.z + t * a.E + e;
-  float zv = 0.f;
-  for (int p = 0; p < a.zplanes; ++p) zv += zr[p * a.zplane];
-  return sigmoidf_(zv);
+  float zp[kMaxZPlanes];
+#pragma unroll
+  for (int p = 0; p < kMaxZPlanes; ++p) zp[p] = p < a.zplanes * a.zsub ? zr[p * a.zplane] : 0.f;
+  return sigmoidf_(plane_sum(zp, a.zplanes, a.zsub));
 }
 
 // alpha[t] = the (k+1)-th largest s + b of token t, one workgroup per token (grid stride);
@@ -982,8 +999,8 @@ __device__ __forceinline__ void in_body(const InArgs& a) {
   int tr, kp, ksplit, q0, q1;
   if (router) {
     // router tile row wgi / zplanes, K-range plane wgi % zplanes split over the 4
-    // wavefronts: many small workgroups, so that the router's 2% of the bytes spread over
-    // the whole chip; the route sums the planes
+    // wavefronts, each of which stores its part as a sub-plane (kZSub = 4); the route adds
+    // them
     tr = wgi / a.zplanes;
     const int plane = wgi - tr * a.zplanes;
     const int qpp = cdiv(a.ks, a.zplanes);
@@ -1018,12 +1035,13 @@ __device__ __forceinline__ void in_body(const InArgs& a) {
   __syncthreads();
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   if (live) acc = run_tile_row_n<0, 3>(ts, trow, q0, q1 - q0, sm, c % nt, nt);
-  acc = reduce_ksplit(acc, part, ksplit, kp);
-  if (tr != INT_MAX && kp == 0) {
+  static_assert(kZSub == kWavesPerBlock, "a router wavefront per sub-plane");
+  if (!router) acc = reduce_ksplit(acc, part, ksplit, kp);
+  if (tr != INT_MAX && (router || kp == 0)) {
     // D row 4g + v = token 4g + v of the block, column c = weight row 16 tr + c
     if (router) {
       const int e = 16 * tr + c;
-      float* zp = a.z + (int64_t)(wgi - tr * a.zplanes) * a.T * a.E;
+      float* zp = a.z + (int64_t)((wgi - tr * a.zplanes) * kZSub + kp) * a.T * a.E;
 #pragma unroll
       for (int v = 0; v < 4; ++v)
         if (4 * g + v < nt && e < a.E) {
@@ -1771,10 +1789,10 @@ __global__ __launch_bounds__(kBlock) void k_in_tt(InTTArgs a) {
 }
 
 // Router logits for a tile of up to 64 tokens: one workgroup per (4 TR router tile rows,
-// logit plane, token tile).  Plane p covers the K-steps [p qpp, (p+1) qpp) of the few-token
-// router launch and is summed in its order: runs of qw K-steps (its per-wavefront K-split)
-// added in sequence.  The route adds the planes in order, so a token's logits have the same
-// bits in both launches.
+// logit sub-plane, token tile).  Plane p covers the K-steps [p qpp, (p+1) qpp) of the
+// few-token router launch, its sub-plane q the run of qw K-steps that wavefront q of that
+// launch's workgroup takes; the route adds sub-planes and planes in the same order for both
+// launches, so a token's logits have the same bits in both.
 struct RouterTTArgs {
   const uint8_t* w;
   int ks, qpp, tr_r, n_grp, zplanes, n_tiles;
@@ -1797,14 +1815,19 @@ __global__ __launch_bounds__(kBlock) void k_router_tt(RouterTTArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
   int gp, tile;
-  if (!xcd_item(blockIdx.x, a.n_grp * a.zplanes, a.n_tiles, gp, tile)) return;
-  const int grp = gp / a.zplanes, plane = gp - grp * a.zplanes;
-  const int r0 = min(a.ks, plane * a.qpp), r1 = min(a.ks, r0 + a.qpp);
-  const int qw = cdiv(r1 - r0, kWavesPerBlock);
+  if (!xcd_item(blockIdx.x, a.n_grp * a.zplanes * kZSub, a.n_tiles, gp, tile)) return;
+  const int np = a.zplanes * kZSub;
+  const int grp = gp / np, sp = gp - grp * np;    // (tile-row group, sub-plane)
+  // sub-plane sp = part sp % kZSub of plane sp / kZSub: the K-steps a wavefront of the
+  // few-token router workgroup takes
+  const int plane = sp / kZSub, part = sp - plane * kZSub;
+  const int pr0 = min(a.ks, plane * a.qpp), pr1 = min(a.ks, pr0 + a.qpp);
+  const int qw = cdiv(pr1 - pr0, kZSub);
+  const int r0 = min(pr1, pr0 + part * qw), r1 = min(pr1, r0 + qw);
   const int64_t t0 = (int64_t)tile * kTTMaxSrc;
   const int nt = (int)min((int64_t)kTTMaxSrc, a.T - t0);
-  float* zp = a.z + (int64_t)plane * a.T * a.E;
-  if (r1 <= r0) {   // an empty plane holds zeros, as in the few-token launch (uniform branch)
+  float* zp = a.z + (int64_t)sp * a.T * a.E;
+  if (r1 <= r0) {   // an empty part holds zeros, as in the few-token launch (uniform branch)
     constexpr int kGroupRows = 16 * kWavesPerBlock * TR;   // experts of a group
     for (int i = threadIdx.x; i < nt * kGroupRows; i += kBlock) {
       const int e = kGroupRows * grp + i % kGroupRows;
@@ -1823,8 +1846,8 @@ __global__ __launch_bounds__(kBlock) void k_router_tt(RouterTTArgs a) {
     trow[t] = a.w + ((size_t)(tri[t] < a.tr_r ? tri[t] : 0) * a.ks + r0) * kBf16StepBytes;
   }
   f32x4_t tot[TR][kInTTBlocks];
-  tt_run_tr<0, 2, kInTTBlocks, 2, true, TR>(rows, TTSrc{a.x, nullptr, nt, a.d - r0 * kStepK, 0, 0},
-                                            trow, r1 - r0, qw, sm, tot);
+  tt_run_tr<0, 2, kInTTBlocks, 2, false, TR>(rows, TTSrc{a.x, nullptr, nt, a.d - r0 * kStepK, 0, 0},
+                                             trow, r1 - r0, r1 - r0, sm, tot);
 #pragma unroll
   for (int t = 0; t < TR; ++t) {
     const int e = 16 * tri[t] + c;
@@ -2154,7 +2177,7 @@ namespace {
 
 RouteArgs route_args(const Shape& s, const float* bias, int64_t T, const Work& ws, int32_t* idx,
                      float* gw) {
-  return RouteArgs{ws.z, route_planes(s), T * s.E, bias, T, s.E, s.k, s.route_scale, idx, gw,
+  return RouteArgs{ws.z, route_planes(s), route_subplanes(s), T * s.E, bias, T, s.E, s.k, s.route_scale, idx, gw,
                    ws.counts, ws.offs, ws.perm, ws.inv, ws.units, ws.ctrl, unit_positions(s, T),
                    (int)even_units(s)};
 }
@@ -2234,7 +2257,7 @@ hipError_t launch_router(const Shape& s, const uint8_t* dense, const uint16_t* x
     a.x = x; a.T = T; a.d = s.d; a.E = s.E;
     a.z = ws.z;
     const size_t lds = (size_t)2 * kInTTBlocks * 16 * 16 * 16;
-    const dim3 grid((unsigned)xcd_grid((int64_t)a.n_grp * a.zplanes, a.n_tiles));
+    const dim3 grid((unsigned)xcd_grid((int64_t)a.n_grp * a.zplanes * kZSub, a.n_tiles));
     if (tr == 2) hipLaunchKernelGGL(k_router_tt<2>, grid, dim3(kBlock), lds, st, a);
     else hipLaunchKernelGGL(k_router_tt<1>, grid, dim3(kBlock), lds, st, a);
     return hipGetLastError();
@@ -2302,7 +2325,7 @@ constexpr int kQbLdsBins = 16384;
 hipError_t launch_qb_hist(const Shape& s, const float* bias, int64_t T, int bins, int32_t* hist,
                           const Work& ws, hipStream_t st) {
   QbArgs a{};
-  a.z = ws.z; a.zplanes = route_planes(s); a.zplane = T * s.E;
+  a.z = ws.z; a.zplanes = route_planes(s); a.zsub = route_subplanes(s); a.zplane = T * s.E;
   a.bias = bias; a.T = T; a.E = s.E; a.k = s.k; a.bins = bins;
   a.hist = hist;
   a.alpha = reinterpret_cast<float*>(ws.perm);   // T <= T k floats of the dispatch slot
